@@ -1,0 +1,358 @@
+"""fp64 CPU oracle for group-affine int4 GEMV / multi-GEMV / MoE / prefill GEMM.
+
+TEST INFRASTRUCTURE ONLY.  This package is the checker for the HIP library:
+only the tests, the smoke check and the CPU-baseline leg of the benchmark may
+import it.  It shares no code with the HIP path; the seeded generators in
+``synth`` are the only thing both sides use.
+
+Sources, cited by page title and passage:
+
+* [FFAI #14]  thewafflehaus/FFAI pull 14, "feat(everything-bagel): clean
+  migration of PR #9 + #10 onto updated dev".
+* [FFAI #9]   thewafflehaus/FFAI pull 9, "Everything Bagel".
+* [ds4 #844]  antirez/ds4 pull 844, "Ornith 1.5 + Qwen 3.8 27B hybrid runtime +
+  DFlash speculative decoding on Metal".
+
+The integer and product arithmetic lives in ``oracle.c`` (plain double loops);
+this module widens stored values exactly to float64, and composes the steps
+the pages describe (SwiGLU, router top-K, expert gather, weighted combine) in
+plain float64 numpy.
+
+Pinning: every function here is checked in ``tests/test_oracle_pins.py``
+against closed forms, exact rational brute force, library routines or the
+worked router example the pages print.  No function is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+F32 = "f32"
+BF16 = "bf16"
+
+
+# --------------------------------------------------------------------------
+# build / load
+# --------------------------------------------------------------------------
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (-O2, OpenMP, no fast-math) into liboracle.so."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-shared",
+               "-fPIC", "-std=c11", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        lib.orc_unpack.argtypes = [P, I64, I64, P]
+        lib.orc_dequant.argtypes = [P, P, P, I64, I64, I64, P]
+        lib.orc_gemv.argtypes = [P, P, P, I64, I64, I64, P, P, P, ctypes.c_int]
+        lib.orc_gemv_absw.argtypes = [P, P, P, I64, I64, I64, P, P, ctypes.c_int]
+        lib.orc_round_bf16.argtypes = [ctypes.c_double]
+        lib.orc_round_bf16.restype = ctypes.c_double
+        lib.orc_round_bf16_array.argtypes = [P, I64, P]
+        lib.orc_gemm_entries.argtypes = [P, P, P, I64, I64, I64, P, I64, P, P, I64,
+                                         ctypes.c_int, P, P, ctypes.c_int]
+        lib.orc_gemm.argtypes = [P, P, P, I64, I64, I64, P, I64, ctypes.c_int, P, P,
+                                 ctypes.c_int]
+        lib.orc_max_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def max_threads() -> int:
+    return int(_load().orc_max_threads())
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+# --------------------------------------------------------------------------
+# exact widening of stored values
+# --------------------------------------------------------------------------
+
+def widen(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Stored values -> float64, exactly.
+
+    bfloat16 is the upper half of an IEEE binary32 word, so its bit pattern
+    shifted left by 16 is the float32 of the same value; float32 -> float64 is
+    exact.
+    """
+    if dtype == BF16:
+        a = np.asarray(a)
+        if a.dtype != np.uint16:
+            raise TypeError("bf16 arrays are passed as uint16 bit patterns")
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if dtype == F32:
+        return np.asarray(a, dtype=np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+def _slab(w, expert: Optional[int]):
+    """(codes, scales, biases) of one matrix, or of expert ``expert`` of a stack."""
+    if w.n_experts > 1 or expert is not None:
+        e = 0 if expert is None else int(expert)
+        if w.n_experts > 1:
+            return w.codes[e], w.scales[e], w.biases[e]
+        if e != 0:
+            raise IndexError("plain matrix has only expert 0")
+    return w.codes, w.scales, w.biases
+
+
+# --------------------------------------------------------------------------
+# unpack / dequant / GEMV
+# --------------------------------------------------------------------------
+
+def unpack(codes: np.ndarray, k_in: int) -> np.ndarray:
+    """Codes uint32 [..., rows, k_in/8] -> uint8 [..., rows, k_in] (word k//8, nibble k%8)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint32)
+    lead = codes.shape[:-1]
+    rows = int(np.prod(lead)) if lead else 1
+    q = np.empty(lead + (k_in,), dtype=np.uint8)
+    _load().orc_unpack(_p(codes), rows, k_in, _p(q))
+    return q
+
+
+def dequant(w, expert: Optional[int] = None) -> np.ndarray:
+    """float64 [n_out, k_in] weights w = s * q + b of one matrix / expert."""
+    c, s, b = _slab(w, expert)
+    c = np.ascontiguousarray(c, dtype=np.uint32)
+    sd = np.ascontiguousarray(widen(s, w.sb_dtype))
+    bd = np.ascontiguousarray(widen(b, w.sb_dtype))
+    out = np.empty((w.n_out, w.k_in), dtype=np.float64)
+    _load().orc_dequant(_p(c), _p(sd), _p(bd), w.n_out, w.k_in, w.group_size, _p(out))
+    return out
+
+
+def gemv_f64(w, x64: np.ndarray, expert: Optional[int] = None,
+             threads: int = 1) -> Tuple[np.ndarray, np.ndarray]:
+    """y = W x and a = sum |w x| in float64, x already float64 [k_in]."""
+    c, s, b = _slab(w, expert)
+    c = np.ascontiguousarray(c, dtype=np.uint32)
+    sd = np.ascontiguousarray(widen(s, w.sb_dtype))
+    bd = np.ascontiguousarray(widen(b, w.sb_dtype))
+    x64 = np.ascontiguousarray(x64, dtype=np.float64)
+    if x64.shape != (w.k_in,):
+        raise ValueError("x must have shape (k_in,)")
+    y = np.empty(w.n_out, dtype=np.float64)
+    a = np.empty(w.n_out, dtype=np.float64)
+    _load().orc_gemv(_p(c), _p(sd), _p(bd), w.n_out, w.k_in, w.group_size, _p(x64),
+                     _p(y), _p(a), int(threads))
+    return y, a
+
+
+def gemv(w, x: np.ndarray, x_dtype: str, expert: Optional[int] = None,
+         threads: int = 1) -> Tuple[np.ndarray, np.ndarray]:
+    """Single int4 GEMV on stored x (float32 or bf16 bits)."""
+    return gemv_f64(w, widen(x, x_dtype), expert=expert, threads=threads)
+
+
+def multi(ws: Sequence, x: np.ndarray, x_dtype: str, threads: int = 1):
+    """Several projections of one shared input ([FFAI #14], batched QKV / 4-way
+    qgemv commits: one input, N outputs).  Returns a list of (y, a)."""
+    x64 = widen(x, x_dtype)
+    return [gemv_f64(w, x64, threads=threads) for w in ws]
+
+
+# --------------------------------------------------------------------------
+# SwiGLU, dense FFN, router, MoE
+# --------------------------------------------------------------------------
+
+def silu(g: np.ndarray) -> np.ndarray:
+    """silu(g) = g / (1 + exp(-g)) in float64; exp overflow for g << 0 gives -0."""
+    g = np.asarray(g, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """h = silu(gate) * up ([FFAI #9], commit fusing silu and mul into one swiglu)."""
+    return silu(g) * np.asarray(u, dtype=np.float64)
+
+
+def swiglu_pair(gate, up, x: np.ndarray, x_dtype: str, threads: int = 1):
+    """Gate and up projections of one input followed by SwiGLU.
+
+    Returns (h, a_h) where a_h bounds |h| error propagation:
+    |dh| <= |silu'(g)| |u| |dg| + |silu(g)| |du| is reported through
+    a_h = |u| a_g + |silu(g)| a_u (silu' is bounded by 1.1).
+    """
+    x64 = widen(x, x_dtype)
+    g, ag = gemv_f64(gate, x64, threads=threads)
+    u, au = gemv_f64(up, x64, threads=threads)
+    h = swiglu(g, u)
+    a_h = 1.1 * np.abs(u) * ag + np.abs(silu(g)) * au
+    return h, a_h
+
+
+def gemv_absw(w, v64: np.ndarray, expert: Optional[int] = None, threads: int = 1) -> np.ndarray:
+    """m = |W| v for a non-negative float64 vector v (error propagation bound)."""
+    c, s, b = _slab(w, expert)
+    c = np.ascontiguousarray(c, dtype=np.uint32)
+    sd = np.ascontiguousarray(widen(s, w.sb_dtype))
+    bd = np.ascontiguousarray(widen(b, w.sb_dtype))
+    v64 = np.ascontiguousarray(v64, dtype=np.float64)
+    m = np.empty(w.n_out, dtype=np.float64)
+    _load().orc_gemv_absw(_p(c), _p(sd), _p(bd), w.n_out, w.k_in, w.group_size, _p(v64),
+                          _p(m), int(threads))
+    return m
+
+
+def dense_ffn(gate, up, down, x: np.ndarray, x_dtype: str, threads: int = 1):
+    """down( silu(gate x) * (up x) ) in float64.
+
+    Returns (y, a_y, h, a_h): a_y = sum|w_down h| + |W_down| a_h, the magnitude
+    against which a float32 implementation's rounding noise is measured
+    (including what its float32 h carries into the down projection).
+    """
+    h, a_h = swiglu_pair(gate, up, x, x_dtype, threads=threads)
+    y, a = gemv_f64(down, h, threads=threads)
+    a_y = a + gemv_absw(down, a_h, threads=threads)
+    return y, a_y, h, a_h
+
+
+def router_topk(logits: np.ndarray, k: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Router: softmax over all experts, keep the top-k, renormalise.
+
+    Ordering is by probability descending, ties by expert index ascending
+    ([FFAI #9], commit replacing the full sort in MoERouter.topKIndices with a
+    k-heap while keeping the (value desc, index asc) tie-break).  Returns
+    (ids int64 [k], weights float64 [k]) in that order.
+    """
+    z = np.asarray(logits, dtype=np.float64)
+    p = np.exp(z - z.max())
+    p = p / p.sum()
+    order = np.lexsort((np.arange(z.size), -p))  # primary key -p, secondary index
+    ids = order[:k].astype(np.int64)
+    kept = p[ids]
+    return ids, kept / kept.sum()
+
+
+def combine(residual64: Optional[np.ndarray], scalars: Sequence[float],
+            values: Sequence[np.ndarray]) -> np.ndarray:
+    """Weighted accumulate: out = residual + sum_k scalars[k] * values[k].
+
+    The scalar-broadcast FMA chain of [FFAI #14] (commit adding scalarFMA,
+    scalarFMAMany and the 8-way scalarFMAChain8: out[i] = base[i] +
+    scalar * value[i], applied once per kept expert).
+    """
+    out = np.zeros_like(np.asarray(values[0], dtype=np.float64))
+    if residual64 is not None:
+        out = out + residual64
+    for a, v in zip(scalars, values):
+        out = out + float(a) * np.asarray(v, dtype=np.float64)
+    return out
+
+
+def moe(gate, up, down, x: np.ndarray, ids: Sequence[int], wts: Sequence[float],
+        residual: Optional[np.ndarray], x_dtype: str, threads: int = 1):
+    """Top-K MoE decode step on stacked experts.
+
+    For each kept slot k with expert e = ids[k] ([FFAI #14], expert-indexed GEMV
+    commit: e selects a slab of the stacked [nExperts, outDim, inDim/8] tensor):
+      h_k = silu(W_gate[e] x) * (W_up[e] x);  d_k = W_down[e] h_k;
+    then out = residual + sum_k wts[k] * d_k ([FFAI #14], chain8 down+SwiGLU+
+    accumulate commit).  Expert ids outside [0, n_experts) contribute nothing
+    (the library's documented contract for untrusted device ids).
+
+    Returns (out, a_out) where a_out = |residual| + sum_k |wts_k| a_k bounds
+    the accumulation noise.
+    """
+    x64 = widen(x, x_dtype)
+    res64 = None if residual is None else widen(residual, x_dtype)
+    ds, scal, mags = [], [], []
+    for e, a_k in zip(ids, wts):
+        e = int(e)
+        if e < 0 or e >= gate.n_experts:
+            continue
+        g, ag = gemv_f64(gate, x64, expert=e, threads=threads)
+        u, au = gemv_f64(up, x64, expert=e, threads=threads)
+        h = swiglu(g, u)
+        a_h = 1.1 * np.abs(u) * ag + np.abs(silu(g)) * au
+        d, ad = gemv_f64(down, h, expert=e, threads=threads)
+        ad = ad + gemv_absw(down, a_h, expert=e, threads=threads)
+        ds.append(d)
+        scal.append(float(a_k))
+        mags.append(abs(float(a_k)) * ad)
+    if not ds:
+        zero = np.zeros(down.n_out, dtype=np.float64)
+        return (zero if res64 is None else res64.copy()), (np.zeros_like(zero) if res64 is None
+                                                             else np.abs(res64))
+    out = combine(res64, scal, ds)
+    a_out = np.sum(mags, axis=0) + (0.0 if res64 is None else np.abs(res64))
+    return out, a_out
+
+
+# --------------------------------------------------------------------------
+# prefill GEMM
+# --------------------------------------------------------------------------
+
+def round_bf16(v: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 value (ties to even)."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty_like(v)
+    _load().orc_round_bf16_array(_p(v), v.size, _p(out))
+    return out
+
+
+def gemm(w, X: np.ndarray, x_dtype: str = BF16, round_w: bool = True,
+         threads: int = 1) -> Tuple[np.ndarray, np.ndarray]:
+    """Full Y[t][o] = sum_k w'[o][k] X[t][k] for all T rows (small sizes).
+
+    Padding T up to a multiple of 32 appends zero rows whose outputs are sliced
+    away ([FFAI #9], dequantGemmDynamicM T-padding driver), so the result for
+    the T real rows is this plain product; w' = bf16(w) when round_w.
+    """
+    c = np.ascontiguousarray(w.codes, dtype=np.uint32)
+    sd = np.ascontiguousarray(widen(w.scales, w.sb_dtype))
+    bd = np.ascontiguousarray(widen(w.biases, w.sb_dtype))
+    X64 = np.ascontiguousarray(widen(X, x_dtype))
+    T = X64.shape[0]
+    Y = np.empty((T, w.n_out), dtype=np.float64)
+    A = np.empty((T, w.n_out), dtype=np.float64)
+    _load().orc_gemm(_p(c), _p(sd), _p(bd), w.n_out, w.k_in, w.group_size, _p(X64), T,
+                     int(bool(round_w)), _p(Y), _p(A), int(threads))
+    return Y, A
+
+
+def gemm_entries(w, X: np.ndarray, t_idx: np.ndarray, o_idx: np.ndarray,
+                 x_dtype: str = BF16, round_w: bool = True,
+                 threads: int = 1) -> Tuple[np.ndarray, np.ndarray]:
+    """Selected entries Y[t_idx[i]][o_idx[i]] of the prefill GEMM."""
+    c = np.ascontiguousarray(w.codes, dtype=np.uint32)
+    sd = np.ascontiguousarray(widen(w.scales, w.sb_dtype))
+    bd = np.ascontiguousarray(widen(w.biases, w.sb_dtype))
+    X64 = np.ascontiguousarray(widen(X, x_dtype))
+    t_idx = np.ascontiguousarray(t_idx, dtype=np.int64)
+    o_idx = np.ascontiguousarray(o_idx, dtype=np.int64)
+    if t_idx.shape != o_idx.shape:
+        raise ValueError("index arrays must match")
+    if t_idx.size and (t_idx.min() < 0 or t_idx.max() >= X64.shape[0]
+                       or o_idx.min() < 0 or o_idx.max() >= w.n_out):
+        raise IndexError("entry index out of range")
+    y = np.empty(t_idx.size, dtype=np.float64)
+    a = np.empty(t_idx.size, dtype=np.float64)
+    _load().orc_gemm_entries(_p(c), _p(sd), _p(bd), w.n_out, w.k_in, w.group_size, _p(X64),
+                             X64.shape[1], _p(t_idx), _p(o_idx), t_idx.size,
+                             int(bool(round_w)), _p(y), _p(a), int(threads))
+    return y, a
