@@ -1,0 +1,234 @@
+"""Python binding of libqint4.so: int4 group-affine GEMV/GEMM for MI355X (gfx950).
+
+Argument marshalling only: every computation runs in the HIP kernels of
+``libqint4.so`` through its C ABI (``include/qint4.h``).  PyTorch provides
+device memory and the current stream; nothing here computes on the CPU and
+there is no fallback path -- if the library is missing, importing the
+functions raises.
+
+The names and arguments mirror the C entry points:
+
+* :func:`qgemv_int4`                 -- y = W x (T = 1)
+* :func:`qgemv_int4_multi`           -- several projections of one input, one launch;
+                                        optional SwiGLU pairing (gate, up -> h)
+* :func:`moe_gather_qgemv_int4`      -- top-K expert gather + SwiGLU + down +
+                                        weighted 8-way combine + residual
+* :func:`qgemm_int4_padT`            -- prefill GEMM with virtual T padding, bf16 MFMA
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch  # must load before libqint4.so so both share torch's HIP runtime
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqint4.so")
+
+F32 = 0
+BF16 = 1
+EPI_NONE = 0
+EPI_SWIGLU_PAIR = 1
+MULTI_MAX = 8
+TOPK_MAX = 8
+
+STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_DTYPE", 4: "ERR_ALIGN",
+          5: "ERR_ALIAS", 6: "ERR_WORKSPACE", 7: "ERR_DEVICE", 8: "ERR_LAUNCH"}
+
+
+class Int4Error(RuntimeError):
+    """A non-OK qint4_status; ``status`` is its name, the message the library's detail."""
+
+    def __init__(self, code: int, message: str):
+        self.code = int(code)
+        self.status = STATUS.get(int(code), str(code))
+        super().__init__("%s: %s" % (self.status, message))
+
+
+class CMatrix(ctypes.Structure):
+    """Mirror of ``qint4_matrix``."""
+
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("biases", ctypes.c_void_p), ("n_out", ctypes.c_int64),
+                ("k_in", ctypes.c_int64), ("group_size", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("sb_dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+_lib = None
+
+# (name, restype, argtypes) of every symbol include/qint4.h declares
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+SIGNATURES = [
+    ("qgemv_int4", _I32, [ctypes.POINTER(CMatrix), _P, _I32, _P, _I32, _P]),
+    ("qgemv_int4_multi", _I32, [_I32, ctypes.POINTER(CMatrix), _P, _I32,
+                                ctypes.POINTER(ctypes.c_void_p), _I32, _I32, _P]),
+    ("moe_gather_qgemv_int4_workspace_bytes", ctypes.c_size_t, [_I64, _I32]),
+    ("moe_gather_qgemv_int4", _I32, [ctypes.POINTER(CMatrix), ctypes.POINTER(CMatrix),
+                                     ctypes.POINTER(CMatrix), _P, _P, _P, _I32, _P, _P, _I32,
+                                     _P, ctypes.c_size_t, _P]),
+    ("qgemm_int4_padT", _I32, [ctypes.POINTER(CMatrix), _P, _I64, _I64, _P, _I64, _I32, _P]),
+    ("qint4_status_string", ctypes.c_char_p, [_I32]),
+    ("qint4_last_error", ctypes.c_char_p, []),
+    ("qint4_abi_version", _I32, []),
+]
+
+
+def load(path: Optional[str] = None):
+    """Load libqint4.so (built in-tree by ``build.py``) and declare its prototypes."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError("libqint4.so is not built (%s); run python -m dequant_matmul_int4_amd.build" % p)
+    lib = ctypes.CDLL(p)
+    for name, res, args in SIGNATURES:
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(code: int):
+    if code != 0:
+        msg = load().qint4_last_error()
+        raise Int4Error(code, msg.decode() if msg else "")
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError("unsupported dtype %s (float32 or bfloat16)" % t.dtype)
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+class QInt4Matrix:
+    """Packed int4 matrix (or expert stack) in device memory.
+
+    codes:  int32 tensor [E?][n_out][k_in/8] (the u32 words' bits)
+    scales, biases: float32 or bfloat16 tensors [E?][n_out][k_in/group_size]
+    """
+
+    def __init__(self, codes: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor,
+                 group_size: int):
+        if codes.dtype not in (torch.int32, torch.uint32):
+            raise TypeError("codes must be int32 (u32 bit patterns)")
+        if scales.dtype != biases.dtype or scales.shape != biases.shape:
+            raise ValueError("scales and biases must share dtype and shape")
+        if codes.dim() not in (2, 3) or scales.dim() != codes.dim():
+            raise ValueError("codes/scales must be [n_out, *] or [E, n_out, *]")
+        self.codes, self.scales, self.biases = codes, scales, biases
+        self.group_size = int(group_size)
+        self.n_experts = codes.shape[0] if codes.dim() == 3 else 1
+        self.n_out = codes.shape[-2]
+        self.k_in = codes.shape[-1] * 8
+        self.sb_dtype = _dt(scales)
+
+    @property
+    def weight_bytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in (self.codes, self.scales, self.biases))
+
+    def c(self) -> CMatrix:
+        return CMatrix(_dev(self.codes, "codes"), _dev(self.scales, "scales"),
+                       _dev(self.biases, "biases"), self.n_out, self.k_in, self.group_size,
+                       self.n_experts, self.sb_dtype, 0)
+
+
+def qgemv_int4(w: QInt4Matrix, x: torch.Tensor, y: torch.Tensor, stream=None) -> None:
+    """y = W x.  x: [k_in] float32/bfloat16; y: [n_out] float32/bfloat16."""
+    cm = w.c()
+    _check(load().qgemv_int4(ctypes.byref(cm), _dev(x, "x"), _dt(x), _dev(y, "y"), _dt(y),
+                             _stream(stream)))
+
+
+def qgemv_int4_multi(ws: Sequence[QInt4Matrix], x: torch.Tensor, ys: Sequence[torch.Tensor],
+                     epilogue: int = EPI_NONE, stream=None) -> None:
+    """ys[i] = W_i x in one launch; with EPI_SWIGLU_PAIR, ys[0] = silu(W_0 x) * (W_1 x)."""
+    n = len(ws)
+    arr = (CMatrix * max(n, 1))(*[w.c() for w in ws])
+    if len(ys) < 1:
+        raise ValueError("need at least one output")
+    ptrs = (ctypes.c_void_p * max(len(ys), n))(*[_dev(y, "ys[%d]" % i) for i, y in enumerate(ys)])
+    y_dt = _dt(ys[0])
+    if any(_dt(y) != y_dt for y in ys):
+        raise TypeError("all outputs must share one dtype")
+    _check(load().qgemv_int4_multi(n, arr, _dev(x, "x"), _dt(x), ptrs, y_dt, int(epilogue),
+                                   _stream(stream)))
+
+
+def moe_gather_qgemv_int4_workspace_bytes(inter: int, top_k: int) -> int:
+    return int(load().moe_gather_qgemv_int4_workspace_bytes(int(inter), int(top_k)))
+
+
+def moe_gather_qgemv_int4(gate: QInt4Matrix, up: QInt4Matrix, down: QInt4Matrix,
+                          x: torch.Tensor, ids: torch.Tensor, wts: torch.Tensor,
+                          out: torch.Tensor, workspace: torch.Tensor,
+                          residual: Optional[torch.Tensor] = None, stream=None) -> None:
+    """out = residual + sum_k wts[k] * down[ids[k]] (silu(gate[ids[k]] x) * up[ids[k]] x).
+
+    ids: int32/uint32 [top_k] on the device; wts: float32 [top_k]; workspace: any
+    device tensor of at least moe_gather_qgemv_int4_workspace_bytes(inter, top_k) bytes.
+    """
+    if ids.dtype not in (torch.int32, torch.uint32):
+        raise TypeError("ids must be int32/uint32")
+    if wts.dtype != torch.float32:
+        raise TypeError("wts must be float32")
+    if ids.numel() != wts.numel():
+        raise ValueError("ids and wts must have the same length")
+    g, u, d = gate.c(), up.c(), down.c()
+    res_p = _dev(residual, "residual") if residual is not None else None
+    if residual is not None and residual.dtype != out.dtype:
+        raise TypeError("residual and out must share a dtype")
+    if x.dtype != out.dtype:
+        raise TypeError("x and out must share a dtype")
+    _check(load().moe_gather_qgemv_int4(
+        ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), _dev(x, "x"), _dev(ids, "ids"),
+        _dev(wts, "wts"), ids.numel(), res_p, _dev(out, "out"), _dt(out),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+
+
+def qgemm_int4_padT(w: QInt4Matrix, x: torch.Tensor, y: torch.Tensor, stream=None) -> None:
+    """Y[t] = bf16(W) X[t] for t < T.  x: bfloat16 [T][ldx] (row stride may exceed k_in);
+    y: [T][ldy] float32/bfloat16."""
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    if x.dim() != 2 or y.dim() != 2 or x.shape[0] != y.shape[0]:
+        raise ValueError("x and y must be 2-D with the same number of rows")
+    if x.stride(1) != 1 or y.stride(1) != 1:
+        raise ValueError("rows of x and y must be contiguous")
+    if x.device.type != "cuda" or y.device.type != "cuda":
+        raise ValueError("x and y must be device tensors")
+    cm = w.c()
+    _check(load().qgemm_int4_padT(ctypes.byref(cm), x.data_ptr(), x.shape[0], x.stride(0),
+                                  y.data_ptr(), y.stride(0), _dt(y), _stream(stream)))
+
+
+__all__ = ["QInt4Matrix", "Int4Error", "qgemv_int4", "qgemv_int4_multi",
+           "moe_gather_qgemv_int4", "moe_gather_qgemv_int4_workspace_bytes", "qgemm_int4_padT",
+           "load", "F32", "BF16", "EPI_NONE", "EPI_SWIGLU_PAIR", "LIB_PATH", "SIGNATURES"]

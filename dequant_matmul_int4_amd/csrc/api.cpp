@@ -1,0 +1,562 @@
+// api.cpp -- the extern "C" entry points of libqint4.so: argument validation,
+// launch planning and dispatch to the gfx950 kernels.  Semantics, layouts and
+// error behaviour are specified in include/qint4.h.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "kernels.h"
+#include "qint4.h"
+
+using namespace qint4;
+
+namespace {
+
+thread_local char g_last_error[768] = "";
+
+qint4_status fail(qint4_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+// Re-raise a status from a helper with the entry point's name in front.
+qint4_status prefixed(qint4_status st, const char *fn) {
+  char tmp[sizeof(g_last_error)];
+  std::memcpy(tmp, g_last_error, sizeof(tmp));
+  snprintf(g_last_error, sizeof(g_last_error), "%s: %s", fn, tmp);
+  return st;
+}
+
+qint4_status ok() {
+  g_last_error[0] = '\0';
+  return QINT4_OK;
+}
+
+inline size_t elem_bytes(int32_t dt) { return dt == QINT4_BF16 ? 2 : 4; }
+inline bool valid_dtype(int32_t dt) { return dt == QINT4_F32 || dt == QINT4_BF16; }
+inline bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int ilog2(int64_t v) {
+  int l = 0;
+  while ((int64_t)1 << (l + 1) <= v) ++l;
+  return l;
+}
+
+// Address range [p, p + n) of one buffer, for overlap checks.
+struct Range {
+  uintptr_t lo = 0, hi = 0;
+  const char *name = "";
+};
+
+Range range(const void *p, size_t n, const char *name) {
+  Range r;
+  r.lo = reinterpret_cast<uintptr_t>(p);
+  r.hi = r.lo + n;
+  r.name = name;
+  return r;
+}
+
+bool overlap(const Range &a, const Range &b) {
+  return a.lo != 0 && b.lo != 0 && a.lo < b.hi && b.lo < a.hi;
+}
+
+qint4_status check_no_overlap(const Range *outs, int n_out, const Range *ins, int n_in) {
+  for (int i = 0; i < n_out; ++i) {
+    for (int j = 0; j < n_in; ++j)
+      if (overlap(outs[i], ins[j]))
+        return fail(QINT4_ERR_ALIAS, "output %s overlaps input %s", outs[i].name, ins[j].name);
+    for (int j = i + 1; j < n_out; ++j)
+      if (overlap(outs[i], outs[j]))
+        return fail(QINT4_ERR_ALIAS, "output %s overlaps output %s", outs[i].name, outs[j].name);
+  }
+  return QINT4_OK;
+}
+
+constexpr int64_t kMaxK = 1 << 20;
+constexpr int64_t kMaxRows = (int64_t)1 << 30;
+
+qint4_status check_matrix(const qint4_matrix *w, const char *name, bool experts_ok) {
+  if (!w) return fail(QINT4_ERR_NULL, "%s: matrix descriptor is NULL", name);
+  if (!w->codes || !w->scales || !w->biases)
+    return fail(QINT4_ERR_NULL, "%s: codes/scales/biases pointer is NULL", name);
+  if (w->reserved != 0) return fail(QINT4_ERR_SHAPE, "%s: reserved field must be 0", name);
+  if (w->group_size != 32 && w->group_size != 64 && w->group_size != 128)
+    return fail(QINT4_ERR_SHAPE, "%s: group_size %d not in {32, 64, 128}", name, w->group_size);
+  if (w->n_out < 1 || w->n_out > kMaxRows)
+    return fail(QINT4_ERR_SHAPE, "%s: n_out %lld out of range [1, 2^30]", name, (long long)w->n_out);
+  if (w->k_in < w->group_size || w->k_in > kMaxK || w->k_in % w->group_size != 0)
+    return fail(QINT4_ERR_SHAPE, "%s: k_in %lld must be a multiple of group_size %d in [%d, 2^20]",
+                name, (long long)w->k_in, w->group_size, w->group_size);
+  if (w->n_experts < 1) return fail(QINT4_ERR_SHAPE, "%s: n_experts %d < 1", name, w->n_experts);
+  if (!experts_ok && w->n_experts != 1)
+    return fail(QINT4_ERR_SHAPE, "%s: n_experts must be 1 here, got %d", name, w->n_experts);
+  if (!valid_dtype(w->sb_dtype)) return fail(QINT4_ERR_DTYPE, "%s: sb_dtype %d invalid", name, w->sb_dtype);
+  if (!aligned(w->codes, 16)) return fail(QINT4_ERR_ALIGN, "%s: codes not 16-byte aligned", name);
+  const size_t sb = elem_bytes(w->sb_dtype);
+  if (!aligned(w->scales, sb) || !aligned(w->biases, sb))
+    return fail(QINT4_ERR_ALIGN, "%s: scales/biases not aligned to %zu bytes", name, sb);
+  return QINT4_OK;
+}
+
+size_t code_bytes(const qint4_matrix *w) {
+  return (size_t)w->n_experts * (size_t)w->n_out * (size_t)(w->k_in / 2);
+}
+size_t sb_bytes(const qint4_matrix *w) {
+  return (size_t)w->n_experts * (size_t)w->n_out * (size_t)(w->k_in / w->group_size) *
+         elem_bytes(w->sb_dtype);
+}
+
+int add_matrix_ranges(const qint4_matrix *w, const char *names[3], Range *out) {
+  out[0] = range(w->codes, code_bytes(w), names[0]);
+  out[1] = range(w->scales, sb_bytes(w), names[1]);
+  out[2] = range(w->biases, sb_bytes(w), names[2]);
+  return 3;
+}
+
+// Device properties, cached per device ordinal.
+struct DevInfo {
+  int state = 0;  // 0 unknown, 1 gfx950, 2 other
+  int cus = 0;
+};
+DevInfo g_dev[64];
+
+qint4_status check_device(int *n_cu) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return fail(QINT4_ERR_DEVICE, "no current HIP device");
+  }
+  if (dev >= 64) return fail(QINT4_ERR_DEVICE, "device ordinal %d not supported", dev);
+  DevInfo &d = g_dev[dev];
+  if (d.state == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(QINT4_ERR_DEVICE, "hipGetDeviceProperties failed for device %d", dev);
+    }
+    d.cus = prop.multiProcessorCount;
+    d.state = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+  }
+  if (d.state != 1) return fail(QINT4_ERR_DEVICE, "device %d is not gfx950", dev);
+  if (n_cu) *n_cu = d.cus;
+  return QINT4_OK;
+}
+
+// ---------------------------------------------------------------------------
+// GEMV planning
+// ---------------------------------------------------------------------------
+
+// Lanes per row: the largest power of two <= 64 dividing the chunk count.
+int lanes_for(int chunks) {
+  int l = 1;
+  while (l < 64 && chunks % (l * 2) == 0) l *= 2;
+  return l;
+}
+
+// Choose waves per workgroup and lanes per row for a row of `nc` chunks.
+void choose_split(int nc, int *waves, int *lpr) {
+  for (int w : {4, 2, 1}) {
+    if (w == 2) continue;  // only 4- and 1-wave kernels are instantiated
+    if (nc % w) continue;
+    const int l = lanes_for(nc / w);
+    if (l >= 8 || w == 1) {
+      *waves = w;
+      *lpr = l;
+      return;
+    }
+  }
+  *waves = 1;
+  *lpr = lanes_for(nc);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *qint4_status_string(int32_t status) {
+  switch (status) {
+    case QINT4_OK: return "ok";
+    case QINT4_ERR_NULL: return "null pointer";
+    case QINT4_ERR_SHAPE: return "invalid shape";
+    case QINT4_ERR_DTYPE: return "invalid dtype";
+    case QINT4_ERR_ALIGN: return "misaligned pointer";
+    case QINT4_ERR_ALIAS: return "output overlaps input";
+    case QINT4_ERR_WORKSPACE: return "workspace missing or too small";
+    case QINT4_ERR_DEVICE: return "no gfx950 device";
+    case QINT4_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char *qint4_last_error(void) { return g_last_error; }
+
+int32_t qint4_abi_version(void) { return QINT4_ABI_VERSION; }
+
+}  // extern "C"
+
+namespace {
+
+// Shared body of qgemv_int4 and qgemv_int4_multi.
+qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t x_dtype,
+                       void *const *ys, int32_t y_dtype, int32_t epilogue, hipStream_t stream,
+                       const char *fn) {
+  if (n < 1 || n > QINT4_MULTI_MAX)
+    return fail(QINT4_ERR_SHAPE, "%s: n = %d not in [1, %d]", fn, n, QINT4_MULTI_MAX);
+  if (!ws) return fail(QINT4_ERR_NULL, "%s: matrix array is NULL", fn);
+  if (!ys) return fail(QINT4_ERR_NULL, "%s: output array is NULL", fn);
+  if (!x) return fail(QINT4_ERR_NULL, "%s: x is NULL", fn);
+  if (!valid_dtype(x_dtype)) return fail(QINT4_ERR_DTYPE, "%s: x_dtype %d invalid", fn, x_dtype);
+  if (!valid_dtype(y_dtype)) return fail(QINT4_ERR_DTYPE, "%s: y_dtype %d invalid", fn, y_dtype);
+  if (epilogue != QINT4_EPI_NONE && epilogue != QINT4_EPI_SWIGLU_PAIR)
+    return fail(QINT4_ERR_SHAPE, "%s: epilogue %d invalid", fn, epilogue);
+  char name[32];
+  for (int i = 0; i < n; ++i) {
+    snprintf(name, sizeof(name), "ws[%d]", i);
+    qint4_status st = check_matrix(&ws[i], name, false);
+    if (st != QINT4_OK) return st;
+  }
+  for (int i = 1; i < n; ++i) {
+    if (ws[i].k_in != ws[0].k_in)
+      return fail(QINT4_ERR_SHAPE,
+                  "%s: packed width mismatch: ws[%d].k_in = %lld (%lld words) but ws[0].k_in = %lld "
+                  "(%lld words)",
+                  fn, i, (long long)ws[i].k_in, (long long)ws[i].k_in / 8, (long long)ws[0].k_in,
+                  (long long)ws[0].k_in / 8);
+    if (ws[i].group_size != ws[0].group_size)
+      return fail(QINT4_ERR_SHAPE, "%s: ws[%d].group_size %d != ws[0].group_size %d", fn, i,
+                  ws[i].group_size, ws[0].group_size);
+    if (ws[i].sb_dtype != ws[0].sb_dtype)
+      return fail(QINT4_ERR_DTYPE, "%s: ws[%d].sb_dtype differs from ws[0]", fn, i);
+  }
+  const bool swiglu = epilogue == QINT4_EPI_SWIGLU_PAIR;
+  if (swiglu) {
+    if (n != 2) return fail(QINT4_ERR_SHAPE, "%s: SWIGLU_PAIR needs n == 2, got %d", fn, n);
+    if (ws[0].n_out != ws[1].n_out)
+      return fail(QINT4_ERR_SHAPE, "%s: SWIGLU_PAIR gate n_out %lld != up n_out %lld", fn,
+                  (long long)ws[0].n_out, (long long)ws[1].n_out);
+    if (!ys[0]) return fail(QINT4_ERR_NULL, "%s: ys[0] is NULL", fn);
+  } else {
+    for (int i = 0; i < n; ++i)
+      if (!ys[i]) return fail(QINT4_ERR_NULL, "%s: ys[%d] is NULL", fn, i);
+  }
+  if (!aligned(x, 16)) return fail(QINT4_ERR_ALIGN, "%s: x not 16-byte aligned", fn);
+  const int n_outs = swiglu ? 1 : n;
+  for (int i = 0; i < n_outs; ++i)
+    if (!aligned(ys[i], elem_bytes(y_dtype)))
+      return fail(QINT4_ERR_ALIGN, "%s: ys[%d] not aligned to its element size", fn, i);
+
+  // overlap checks
+  Range ins[3 * QINT4_MULTI_MAX + 1], outs[QINT4_MULTI_MAX];
+  int ni = 0;
+  static const char *mnames[3] = {"codes", "scales", "biases"};
+  for (int i = 0; i < n; ++i) ni += add_matrix_ranges(&ws[i], mnames, ins + ni);
+  const int64_t k_in = ws[0].k_in;
+  ins[ni++] = range(x, (size_t)k_in * elem_bytes(x_dtype), "x");
+  static const char *ynames[QINT4_MULTI_MAX] = {"ys[0]", "ys[1]", "ys[2]", "ys[3]",
+                                                  "ys[4]", "ys[5]", "ys[6]", "ys[7]"};
+  for (int i = 0; i < n_outs; ++i)
+    outs[i] = range(ys[i], (size_t)ws[i].n_out * elem_bytes(y_dtype), ynames[i]);
+  qint4_status st = check_no_overlap(outs, n_outs, ins, ni);
+  if (st != QINT4_OK) return prefixed(st, fn);
+
+  // plan
+  const int nc = (int)(k_in / 32);
+  int waves = 1, lpr = 1;
+  choose_split(nc, &waves, &lpr);
+  const int xmode = x_dtype == QINT4_BF16 ? XM_BF16 : XM_F32;
+  const int epi = swiglu ? EPI_SWIGLU : EPI_STORE;
+  const int rpi = 64 / lpr;
+  int n_cu = 256;
+  st = check_device(&n_cu);
+  if (st != QINT4_OK) return prefixed(st, fn);
+
+  auto blocks_for = [&](int rt) {
+    int64_t b = 0;
+    for (int i = 0; i < n_outs; ++i) b += (ws[i].n_out + rt * rpi - 1) / (rt * rpi);
+    return b;
+  };
+  int rt = 1;
+  for (int cand : {4, 2, 1}) {
+    if (swiglu && cand > 2) continue;
+    if (blocks_for(cand) >= 2 * (int64_t)n_cu || cand == 1) {
+      rt = cand;
+      break;
+    }
+  }
+
+  GemvPlan plan;
+  plan.waves = waves;
+  plan.rt = rt;
+  plan.log2_lpr = ilog2(lpr);
+  plan.chunks_per_wave = nc / waves;
+  plan.n_blocks = blocks_for(rt);
+  plan.lds_bytes = gemv_lds_bytes(xmode, nc, waves, rt, plan.log2_lpr, epi);
+  if (plan.lds_bytes > (size_t)kMaxLds)
+    return fail(QINT4_ERR_SHAPE, "%s: k_in %lld needs %zu bytes of LDS (max %d)", fn,
+                (long long)k_in, plan.lds_bytes, kMaxLds);
+
+  GemvParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.n_mats = swiglu ? 2 : n;
+  int64_t b0 = 0;
+  for (int i = 0; i < n; ++i) {
+    p.m[i].codes = ws[i].codes;
+    p.m[i].scales = ws[i].scales;
+    p.m[i].biases = ws[i].biases;
+    p.m[i].y = swiglu ? ys[0] : ys[i];
+    p.m[i].n_out = ws[i].n_out;
+    p.m[i].block0 = b0;
+    if (!swiglu) b0 += (ws[i].n_out + rt * rpi - 1) / (rt * rpi);
+  }
+  p.log2_lpr = plan.log2_lpr;
+  p.log2_group = ilog2(ws[0].group_size);
+  p.chunks_per_row = nc;
+  p.chunks_per_wave = plan.chunks_per_wave;
+  p.n_chunks_x = nc;
+  p.y_bf16 = y_dtype == QINT4_BF16;
+  p.blocks_per_slot = (int32_t)((ws[0].n_out + rt * rpi - 1) / (rt * rpi));
+  p.n_blocks = plan.n_blocks;
+  p.x = x;
+  p.ids = nullptr;
+  p.top_k = 1;
+  p.n_experts = 1;
+
+  hipError_t e = launch_gemv(p, plan, xmode, ws[0].sb_dtype == QINT4_BF16, epi, stream);
+  if (e != hipSuccess) return fail(QINT4_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+qint4_status qgemv_int4(const qint4_matrix *w, const void *x, int32_t x_dtype, void *y,
+                        int32_t y_dtype, void *stream) {
+  if (!w) return fail(QINT4_ERR_NULL, "qgemv_int4: matrix descriptor is NULL");
+  void *ys[1] = {y};
+  if (!y) return fail(QINT4_ERR_NULL, "qgemv_int4: y is NULL");
+  return run_multi(1, w, x, x_dtype, ys, y_dtype, QINT4_EPI_NONE,
+                   reinterpret_cast<hipStream_t>(stream), "qgemv_int4");
+}
+
+qint4_status qgemv_int4_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t x_dtype,
+                              void *const *ys, int32_t y_dtype, int32_t epilogue, void *stream) {
+  return run_multi(n, ws, x, x_dtype, ys, y_dtype, epilogue, reinterpret_cast<hipStream_t>(stream),
+                   "qgemv_int4_multi");
+}
+
+size_t moe_gather_qgemv_int4_workspace_bytes(int64_t inter, int32_t top_k) {
+  if (inter < 1 || inter > kMaxK || top_k < 1 || top_k > QINT4_TOPK_MAX) return 0;
+  return (size_t)top_k * (size_t)inter * sizeof(float);
+}
+
+qint4_status moe_gather_qgemv_int4(const qint4_matrix *gate, const qint4_matrix *up,
+                                   const qint4_matrix *down, const void *x, const uint32_t *ids,
+                                   const float *wts, int32_t top_k, const void *residual, void *out,
+                                   int32_t act_dtype, void *workspace, size_t workspace_bytes,
+                                   void *stream_) {
+  const char *fn = "moe_gather_qgemv_int4";
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  qint4_status st;
+  if ((st = check_matrix(gate, "gate", true)) != QINT4_OK) return st;
+  if ((st = check_matrix(up, "up", true)) != QINT4_OK) return st;
+  if ((st = check_matrix(down, "down", true)) != QINT4_OK) return st;
+  if (!x || !ids || !wts || !out) return fail(QINT4_ERR_NULL, "%s: x/ids/wts/out is NULL", fn);
+  if (!valid_dtype(act_dtype)) return fail(QINT4_ERR_DTYPE, "%s: act_dtype %d invalid", fn, act_dtype);
+  if (top_k < 1 || top_k > QINT4_TOPK_MAX)
+    return fail(QINT4_ERR_SHAPE, "%s: top_k %d not in [1, %d]", fn, top_k, QINT4_TOPK_MAX);
+  if (gate->n_experts != up->n_experts || gate->n_experts != down->n_experts)
+    return fail(QINT4_ERR_SHAPE, "%s: n_experts differ (gate %d, up %d, down %d)", fn,
+                gate->n_experts, up->n_experts, down->n_experts);
+  if (gate->group_size != up->group_size || gate->group_size != down->group_size ||
+      gate->sb_dtype != up->sb_dtype || gate->sb_dtype != down->sb_dtype)
+    return fail(QINT4_ERR_SHAPE, "%s: gate/up/down must share group_size and sb_dtype", fn);
+  const int64_t hidden = gate->k_in, inter = gate->n_out;
+  if (up->k_in != hidden || up->n_out != inter)
+    return fail(QINT4_ERR_SHAPE, "%s: up is %lldx%lld, gate is %lldx%lld", fn, (long long)up->n_out,
+                (long long)up->k_in, (long long)inter, (long long)hidden);
+  if (down->k_in != inter || down->n_out != hidden)
+    return fail(QINT4_ERR_SHAPE, "%s: down is %lldx%lld, expected %lldx%lld", fn,
+                (long long)down->n_out, (long long)down->k_in, (long long)hidden, (long long)inter);
+  if (!aligned(x, 16)) return fail(QINT4_ERR_ALIGN, "%s: x not 16-byte aligned", fn);
+  if (!aligned(ids, 4) || !aligned(wts, 4)) return fail(QINT4_ERR_ALIGN, "%s: ids/wts misaligned", fn);
+  const size_t ab = elem_bytes(act_dtype);
+  if (!aligned(out, ab) || (residual && !aligned(residual, ab)))
+    return fail(QINT4_ERR_ALIGN, "%s: out/residual not aligned to element size", fn);
+  const size_t need = moe_gather_qgemv_int4_workspace_bytes(inter, top_k);
+  if (!workspace || workspace_bytes < need)
+    return fail(QINT4_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn,
+                workspace ? workspace_bytes : (size_t)0, need);
+  if (!aligned(workspace, 16)) return fail(QINT4_ERR_ALIGN, "%s: workspace not 16-byte aligned", fn);
+
+  Range ins[13], outs[2];
+  int ni = 0;
+  static const char *gn[3] = {"gate.codes", "gate.scales", "gate.biases"};
+  static const char *un[3] = {"up.codes", "up.scales", "up.biases"};
+  static const char *dn[3] = {"down.codes", "down.scales", "down.biases"};
+  ni += add_matrix_ranges(gate, gn, ins + ni);
+  ni += add_matrix_ranges(up, un, ins + ni);
+  ni += add_matrix_ranges(down, dn, ins + ni);
+  ins[ni++] = range(x, (size_t)hidden * ab, "x");
+  ins[ni++] = range(ids, (size_t)top_k * 4, "ids");
+  ins[ni++] = range(wts, (size_t)top_k * 4, "wts");
+  if (residual) ins[ni++] = range(residual, (size_t)hidden * ab, "residual");
+  outs[0] = range(out, (size_t)hidden * ab, "out");
+  outs[1] = range(workspace, need, "workspace");
+  if ((st = check_no_overlap(outs, 2, ins, ni)) != QINT4_OK) return prefixed(st, fn);
+
+  int n_cu = 256;
+  if ((st = check_device(&n_cu)) != QINT4_OK) return prefixed(st, fn);
+
+  const int sb_bf16 = gate->sb_dtype == QINT4_BF16;
+  const int xmode_a = act_dtype == QINT4_BF16 ? XM_BF16 : XM_F32;
+  float *h = reinterpret_cast<float *>(workspace);
+
+  // ---- launch A: gate/up of every kept expert, SwiGLU -> h[top_k][inter] (f32) ----
+  {
+    const int nc = (int)(hidden / 32);
+    int waves = 1, lpr = 1;
+    choose_split(nc, &waves, &lpr);
+    const int rpi = 64 / lpr;
+    int rt = 1;
+    for (int cand : {2, 1}) {
+      const int64_t b = (int64_t)top_k * ((inter + cand * rpi - 1) / (cand * rpi));
+      if (b >= 2 * (int64_t)n_cu || cand == 1) {
+        rt = cand;
+        break;
+      }
+    }
+    GemvPlan plan;
+    plan.waves = waves;
+    plan.rt = rt;
+    plan.log2_lpr = ilog2(lpr);
+    plan.chunks_per_wave = nc / waves;
+    const int64_t bps = (inter + rt * rpi - 1) / (rt * rpi);
+    plan.n_blocks = bps * top_k;
+    plan.lds_bytes = gemv_lds_bytes(xmode_a, nc, waves, rt, plan.log2_lpr, EPI_SWIGLU);
+    if (plan.lds_bytes > (size_t)kMaxLds)
+      return fail(QINT4_ERR_SHAPE, "%s: hidden %lld needs too much LDS", fn, (long long)hidden);
+    GemvParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.n_mats = 2;
+    p.m[0] = {gate->codes, gate->scales, gate->biases, h, inter, 0};
+    p.m[1] = {up->codes, up->scales, up->biases, h, inter, 0};
+    p.log2_lpr = plan.log2_lpr;
+    p.log2_group = ilog2(gate->group_size);
+    p.chunks_per_row = nc;
+    p.chunks_per_wave = plan.chunks_per_wave;
+    p.n_chunks_x = nc;
+    p.y_bf16 = 0;
+    p.blocks_per_slot = (int32_t)bps;
+    p.n_blocks = plan.n_blocks;
+    p.x = x;
+    p.ids = ids;
+    p.top_k = top_k;
+    p.n_experts = gate->n_experts;
+    p.expert_code_stride = inter * (hidden / 8);
+    p.expert_sb_stride = inter * (hidden / gate->group_size);
+    hipError_t e = launch_gemv(p, plan, xmode_a, sb_bf16, EPI_SWIGLU, stream);
+    if (e != hipSuccess) return fail(QINT4_ERR_LAUNCH, "%s: gate/up launch failed: %s", fn, hipGetErrorString(e));
+  }
+  // ---- launch B: down projection of every slot + weighted combine + residual ----
+  {
+    const int ncl = (int)(inter / 32);
+    const int lpr = lanes_for(ncl);
+    const int rpi = 64 / lpr;
+    int rt = 1;
+    for (int cand : {2, 1}) {
+      const int64_t b = (hidden + cand * rpi - 1) / (cand * rpi);
+      if (b >= 2 * (int64_t)n_cu || cand == 1) {
+        rt = cand;
+        break;
+      }
+    }
+    GemvPlan plan;
+    plan.waves = 8;
+    plan.rt = rt;
+    plan.log2_lpr = ilog2(lpr);
+    plan.chunks_per_wave = ncl;
+    plan.n_blocks = (hidden + rt * rpi - 1) / (rt * rpi);
+    plan.lds_bytes = gemv_lds_bytes(XM_F32, ncl * top_k, 8, rt, plan.log2_lpr, EPI_MOE_DOWN);
+    if (plan.lds_bytes > (size_t)kMaxLds)
+      return fail(QINT4_ERR_SHAPE, "%s: top_k * inter = %lld needs too much LDS", fn,
+                  (long long)(top_k * inter));
+    GemvParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.n_mats = 1;
+    p.m[0] = {down->codes, down->scales, down->biases, out, hidden, 0};
+    p.log2_lpr = plan.log2_lpr;
+    p.log2_group = ilog2(down->group_size);
+    p.chunks_per_row = ncl;
+    p.chunks_per_wave = ncl;
+    p.n_chunks_x = ncl * top_k;
+    p.y_bf16 = act_dtype == QINT4_BF16;
+    p.n_blocks = plan.n_blocks;
+    p.x = h;
+    p.ids = ids;
+    p.wts = wts;
+    p.residual = residual;
+    p.top_k = top_k;
+    p.n_experts = down->n_experts;
+    p.expert_code_stride = hidden * (inter / 8);
+    p.expert_sb_stride = hidden * (inter / down->group_size);
+    hipError_t e = launch_gemv(p, plan, XM_F32, sb_bf16, EPI_MOE_DOWN, stream);
+    if (e != hipSuccess) return fail(QINT4_ERR_LAUNCH, "%s: down launch failed: %s", fn, hipGetErrorString(e));
+  }
+  return ok();
+}
+
+qint4_status qgemm_int4_padT(const qint4_matrix *w, const void *x, int64_t T, int64_t ldx, void *y,
+                             int64_t ldy, int32_t y_dtype, void *stream) {
+  const char *fn = "qgemm_int4_padT";
+  qint4_status st;
+  if ((st = check_matrix(w, "w", false)) != QINT4_OK) return st;
+  if (!x || !y) return fail(QINT4_ERR_NULL, "%s: x or y is NULL", fn);
+  if (!valid_dtype(y_dtype)) return fail(QINT4_ERR_DTYPE, "%s: y_dtype %d invalid", fn, y_dtype);
+  if (w->n_out % 32 != 0)
+    return fail(QINT4_ERR_SHAPE, "%s: n_out (%lld) must be a multiple of 32 (GEMM tile)", fn,
+                (long long)w->n_out);
+  if (T < 1 || T > ((int64_t)1 << 31)) return fail(QINT4_ERR_SHAPE, "%s: T = %lld invalid", fn, (long long)T);
+  if (ldx < w->k_in || ldx % 8 != 0)
+    return fail(QINT4_ERR_SHAPE, "%s: ldx %lld must be >= k_in %lld and a multiple of 8", fn,
+                (long long)ldx, (long long)w->k_in);
+  if (ldy < w->n_out) return fail(QINT4_ERR_SHAPE, "%s: ldy %lld < n_out %lld", fn, (long long)ldy, (long long)w->n_out);
+  if (!aligned(x, 16)) return fail(QINT4_ERR_ALIGN, "%s: x not 16-byte aligned", fn);
+  if (!aligned(y, elem_bytes(y_dtype))) return fail(QINT4_ERR_ALIGN, "%s: y misaligned", fn);
+  if (w->n_out > INT32_MAX || w->k_in > INT32_MAX) return fail(QINT4_ERR_SHAPE, "%s: too large", fn);
+
+  Range ins[4], outs[1];
+  static const char *mn[3] = {"codes", "scales", "biases"};
+  int ni = add_matrix_ranges(w, mn, ins);
+  ins[ni++] = range(x, (size_t)((T - 1) * ldx + w->k_in) * 2, "x");
+  outs[0] = range(y, (size_t)((T - 1) * ldy + w->n_out) * elem_bytes(y_dtype), "y");
+  if ((st = check_no_overlap(outs, 1, ins, ni)) != QINT4_OK) return prefixed(st, fn);
+  if ((st = check_device(nullptr)) != QINT4_OK) return prefixed(st, fn);
+
+  GemmParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.codes = w->codes;
+  p.scales = w->scales;
+  p.biases = w->biases;
+  p.x = reinterpret_cast<const uint16_t *>(x);
+  p.y = y;
+  p.T = T;
+  p.ldx = ldx;
+  p.ldy = ldy;
+  p.n_out = (int32_t)w->n_out;
+  p.k_in = (int32_t)w->k_in;
+  p.log2_group = ilog2(w->group_size);
+  p.y_bf16 = y_dtype == QINT4_BF16;
+  p.sb_bf16 = w->sb_dtype == QINT4_BF16;
+  hipError_t e = launch_gemm(p, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(QINT4_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

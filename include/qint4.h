@@ -1,0 +1,224 @@
+/*
+ * qint4.h -- C ABI of libqint4.so: group-affine 4-bit weight dequantisation
+ * fused into matrix-vector and small-M matrix products, for AMD MI355X
+ * (gfx950, CDNA4).
+ *
+ * Sources, cited by page title and passage:
+ *   [FFAI #14] thewafflehaus/FFAI pull 14, "feat(everything-bagel): clean
+ *              migration of PR #9 + #10 onto updated dev".
+ *   [FFAI #9]  thewafflehaus/FFAI pull 9, "Everything Bagel".
+ *
+ * ---------------------------------------------------------------------------
+ * Weight format (shared by every entry point)
+ * ---------------------------------------------------------------------------
+ * A matrix W has n_out rows and k_in input columns.  Each weight is a 4-bit
+ * code q in 0..15 with an affine map per group of `group_size` consecutive
+ * input columns of a row:
+ *
+ *     w[o][k] = scale[o][k / group_size] * q[o][k] + bias[o][k / group_size]
+ *
+ * ([FFAI #14], commit "dequantGemvInt4Two/Three/Four": the int4 GEMV takes
+ * a packed weight with its scales and biases, in_dim and group_size.)
+ *
+ *   codes   uint32 [n_experts][n_out][k_in/8], row-major, eight codes per
+ *           word along k_in ([FFAI #14], commit adding the packed-width
+ *           precondition: in_dim = packed width * 8).  Code k of a row is
+ *           (codes[k/8] >> (4*(k%8))) & 15, least significant nibble first.
+ *   scales  [n_experts][n_out][k_in/group_size], float32 or bfloat16
+ *   biases  same shape and dtype as scales
+ *
+ * A stack of experts ([FFAI #14], expert-indexed GEMV commit: a stacked
+ * [nExperts, outDim, inDim/8] u32 tensor) is the same layout with
+ * n_experts > 1; expert e starts at codes + e*n_out*k_in/8 and
+ * scales/biases + e*n_out*(k_in/group_size).
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions
+ * ---------------------------------------------------------------------------
+ * - Every data pointer is DEVICE memory of the current HIP device, owned by
+ *   the caller.  The library never allocates, frees or keeps a pointer.
+ * - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *   enqueues work on it and returns; there is no host synchronisation.
+ * - Arguments are validated before anything is enqueued.  On failure the
+ *   call returns a non-zero qint4_status, writes nothing to device memory,
+ *   and qint4_last_error() names the offending values.  No call aborts.
+ * - Faults inside a kernel surface at the caller's next synchronisation.
+ * - Requirements common to all entry points:
+ *     group_size in {32, 64, 128};  k_in % group_size == 0;
+ *     n_out >= 1;  k_in >= group_size;
+ *     codes 16-byte aligned; activations 16-byte aligned;
+ *     scales/biases aligned to their element size;
+ *     the current device is a gfx950 GPU.
+ * - Outputs must not overlap any input (checked on the address ranges).
+ * - Calls are reentrant; concurrent calls on different streams need
+ *   separate outputs and workspaces.
+ */
+#ifndef QINT4_H
+#define QINT4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QINT4_ABI_VERSION 1
+#define QINT4_MULTI_MAX 8   /* most projections one qgemv_int4_multi call takes */
+#define QINT4_TOPK_MAX 8    /* most experts one moe_gather_qgemv_int4 call combines */
+
+/* Element types (passed as int32_t). */
+enum { QINT4_F32 = 0, QINT4_BF16 = 1 };
+
+/* Epilogues of qgemv_int4_multi (passed as int32_t). */
+enum {
+  QINT4_EPI_NONE = 0,        /* ys[i] = W_i x                                  */
+  QINT4_EPI_SWIGLU_PAIR = 1  /* n == 2: ys[0] = silu(W_0 x) * (W_1 x)          */
+};
+
+/* Status codes. */
+typedef enum qint4_status {
+  QINT4_OK = 0,
+  QINT4_ERR_NULL = 1,       /* a required pointer is NULL                      */
+  QINT4_ERR_SHAPE = 2,      /* sizes inconsistent or outside the supported set */
+  QINT4_ERR_DTYPE = 3,      /* unsupported element-type combination            */
+  QINT4_ERR_ALIGN = 4,      /* a pointer or leading dimension is misaligned    */
+  QINT4_ERR_ALIAS = 5,      /* an output overlaps an input                     */
+  QINT4_ERR_WORKSPACE = 6,  /* workspace NULL or smaller than required         */
+  QINT4_ERR_DEVICE = 7,     /* no current gfx950 device                        */
+  QINT4_ERR_LAUNCH = 8      /* the HIP runtime rejected a kernel launch        */
+} qint4_status;
+
+/* One packed matrix, or a stack of n_experts matrices of the same shape. */
+typedef struct qint4_matrix {
+  const uint32_t *codes;    /* device, [n_experts][n_out][k_in/8]                */
+  const void *scales;       /* device, [n_experts][n_out][k_in/group_size]       */
+  const void *biases;       /* device, same shape/dtype as scales                */
+  int64_t n_out;            /* rows (outputs)                                    */
+  int64_t k_in;             /* input columns                                     */
+  int32_t group_size;       /* 32, 64 or 128                                     */
+  int32_t n_experts;        /* 1 for a plain matrix                              */
+  int32_t sb_dtype;         /* QINT4_F32 or QINT4_BF16                           */
+  int32_t reserved;         /* must be 0                                         */
+} qint4_matrix;
+
+/*
+ * qgemv_int4 -- y = W x, one decode token (T = 1).
+ *
+ * [FFAI #14], commits on the dequant_gemv_int4 family: one output per row of
+ * the packed matrix, the input vector shared by all rows.
+ *
+ *   w       matrix (n_experts must be 1)
+ *   x       device [k_in], dtype x_dtype (QINT4_F32 or QINT4_BF16)
+ *   y       device [n_out], dtype y_dtype (QINT4_F32 or QINT4_BF16);
+ *           every element is overwritten (bf16: round to nearest even from
+ *           the float32 accumulator)
+ * Accumulation is float32.  Returns QINT4_OK or an error status.
+ */
+qint4_status qgemv_int4(const qint4_matrix *w, const void *x, int32_t x_dtype,
+                        void *y, int32_t y_dtype, void *stream);
+
+/*
+ * qgemv_int4_multi -- n projections of ONE shared input in ONE launch.
+ *
+ * [FFAI #14], batched QKV / batched-4 qgemv commits: the q, k, v (or four
+ * GDN input) projections share one input and run as one kernel launch that
+ * reads the input once; all packed widths must match the leading matrix
+ * (the precondition added in the packed-width commit, whose error names the
+ * mismatched widths).  SwiGLU pairing: [FFAI #9], commit fusing silu(gate) *
+ * up into one swiglu step.
+ *
+ *   n        1..QINT4_MULTI_MAX matrices; all share k_in, group_size and
+ *            sb_dtype; each has n_experts == 1
+ *   ws       host array [n] of matrix descriptors
+ *   x        device [k_in], dtype x_dtype
+ *   ys       host array of device output pointers:
+ *              QINT4_EPI_NONE:        [n], ys[i] is [ws[i].n_out]
+ *              QINT4_EPI_SWIGLU_PAIR: n == 2, ws[0] (gate) and ws[1] (up)
+ *                                     have equal n_out, ys[0] is
+ *                                     h = silu(gate x) * (up x), [n_out],
+ *                                     computed in float32
+ *   y_dtype  element type of every output
+ *   epilogue QINT4_EPI_NONE or QINT4_EPI_SWIGLU_PAIR
+ */
+qint4_status qgemv_int4_multi(int32_t n, const qint4_matrix *ws, const void *x,
+                              int32_t x_dtype, void *const *ys, int32_t y_dtype,
+                              int32_t epilogue, void *stream);
+
+/*
+ * Bytes of device workspace one moe_gather_qgemv_int4 call needs for an
+ * expert intermediate width `inter` and `top_k` kept experts (the float32
+ * SwiGLU intermediates, one row per kept expert).  0 for invalid sizes.
+ */
+size_t moe_gather_qgemv_int4_workspace_bytes(int64_t inter, int32_t top_k);
+
+/*
+ * moe_gather_qgemv_int4 -- one token through a top-K mixture of experts.
+ *
+ *   out = residual + sum_{k < top_k} wts[k] * W_down[ids[k]] h_k,
+ *   h_k = silu(W_gate[ids[k]] x) * (W_up[ids[k]] x)
+ *
+ * [FFAI #14]: the expert-indexed GEMV reads the expert id on the device and
+ * selects that slab of the stacked tensor (no host readback); the router
+ * writes [k] u32 ids and [k] weights; the chain8 commit fuses SwiGLU, the
+ * expert-indexed down GEMV and the weighted accumulate
+ * acc[i] = sum_k w_k out_k[i]; the scalar-FMA commit defines the 8-way
+ * scalar FMA chain out[i] = base[i] + sum_k scalar_k value_k[i].
+ *
+ *   gate, up  stacks [E][inter][hidden]; down stack [E][hidden][inter];
+ *             all three with the same n_experts E, group_size and sb_dtype
+ *   x         device [hidden], dtype act_dtype
+ *   ids       device uint32 [top_k]; an id >= E contributes nothing (ids are
+ *             device data and are not checked on the host)
+ *   wts       device float32 [top_k]
+ *   top_k     1..QINT4_TOPK_MAX
+ *   residual  device [hidden], dtype act_dtype, or NULL for none
+ *   out       device [hidden], dtype act_dtype; every element overwritten
+ *   act_dtype QINT4_F32 or QINT4_BF16
+ *   workspace device scratch of at least
+ *             moe_gather_qgemv_int4_workspace_bytes(inter, top_k) bytes,
+ *             16-byte aligned; contents on entry are ignored, contents on
+ *             return are unspecified.  One workspace per concurrent call.
+ * Two kernel launches on `stream` (gate/up + SwiGLU, then down + combine).
+ */
+qint4_status moe_gather_qgemv_int4(const qint4_matrix *gate, const qint4_matrix *up,
+                                   const qint4_matrix *down, const void *x,
+                                   const uint32_t *ids, const float *wts, int32_t top_k,
+                                   const void *residual, void *out, int32_t act_dtype,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * qgemm_int4_padT -- prefill: Y[t][o] = sum_k bf16(w[o][k]) * X[t][k], t < T.
+ *
+ * [FFAI #9], dequantGemmDynamicM commit: T is padded up to a multiple of 32
+ * with zero rows, the dequant GEMM runs on the padded block, and the first T
+ * rows are kept.  Here the padding is virtual: rows t >= T are read as zero
+ * inside the kernel and never written, so X and Y need only T rows.  The
+ * weights are dequantised in float32 and rounded to bfloat16 (nearest even)
+ * in LDS, then multiplied on bf16 MFMA with float32 accumulation.
+ * [FFAI #14], commit adding the outDim guard: the GEMM tile needs
+ * n_out % 32 == 0.
+ *
+ *   w     matrix (n_experts == 1), n_out % 32 == 0
+ *   x     device bf16 [T][ldx], ldx >= k_in, ldx % 8 == 0
+ *   T     rows of x and y, T >= 1
+ *   y     device [T][ldy], dtype y_dtype (QINT4_F32 or QINT4_BF16),
+ *         ldy >= n_out; rows < T fully overwritten, nothing else written
+ */
+qint4_status qgemm_int4_padT(const qint4_matrix *w, const void *x, int64_t T, int64_t ldx,
+                             void *y, int64_t ldy, int32_t y_dtype, void *stream);
+
+/* Static description of a status code. */
+const char *qint4_status_string(int32_t status);
+
+/* Detail of the calling thread's last failed call ("" if none). */
+const char *qint4_last_error(void);
+
+/* QINT4_ABI_VERSION of the loaded library. */
+int32_t qint4_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QINT4_H */

@@ -211,3 +211,32 @@ def torch_matrix(n_out: int, k_in: int, group_size: int, sb_dtype: str, n_expert
     else:
         b = -8.0 * s + noise
     return {"codes": codes, "scales": s.contiguous(), "biases": b.contiguous()}
+
+
+# --------------------------------------------------------------------------
+# numpy -> torch marshalling (device placement only, values unchanged)
+# --------------------------------------------------------------------------
+
+def to_torch(a: np.ndarray, dtype: str, device: str = "cuda"):
+    """float32 array, or uint16 bf16 bit patterns, as a torch tensor on ``device``."""
+    import torch
+
+    a = np.ascontiguousarray(a)
+    if dtype == BF16:
+        if a.dtype != np.uint16:
+            raise TypeError("bf16 data must be uint16 bit patterns")
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    elif dtype == F32:
+        t = torch.from_numpy(a.astype(np.float32, copy=False))
+    else:
+        raise ValueError(dtype)
+    return t.to(device)
+
+
+def matrix_to_torch(w: QMatrix, device: str = "cuda") -> dict:
+    """Codes (as int32 bit patterns), scales and biases of ``w`` on ``device``."""
+    import torch
+
+    codes = torch.from_numpy(np.ascontiguousarray(w.codes).view(np.int32)).to(device)
+    return {"codes": codes, "scales": to_torch(w.scales, w.sb_dtype, device),
+            "biases": to_torch(w.biases, w.sb_dtype, device), "group_size": w.group_size}

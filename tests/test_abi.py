@@ -1,0 +1,144 @@
+"""The C ABI loads, exports every declared symbol, and rejects bad arguments (CPU only).
+
+Every call here fails validation before anything is enqueued, so no kernel is
+launched even when a GPU is present; pointers are fake addresses that are
+never dereferenced.  The one case that passes validation (and would need a
+device) runs only where no GPU exists.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dequant_matmul_int4_amd as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qint4.h")
+
+A = 0x7F0000000000  # fake, 256-byte aligned device-looking addresses
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([A-Za-z_0-9]+)\s*\(", text)) - {"if", "sizeof"})
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(q.LIB_PATH):
+        pytest.skip("libqint4.so not built")
+    return q.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert set(names) == {n for n, _, _ in q.SIGNATURES}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.qint4_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for code in range(9):
+        assert lib.qint4_status_string(code)
+    assert lib.qint4_status_string(99) == b"unknown status"
+
+
+def _m(codes=A, scales=A + 0x100000, biases=A + 0x200000, n_out=64, k_in=256, g=64, e=1, sb=1):
+    return q.CMatrix(codes, scales, biases, n_out, k_in, g, e, sb, 0)
+
+
+def _gemv(lib, m, x=A + 0x300000, y=A + 0x400000, xdt=1, ydt=1):
+    return lib.qgemv_int4(ctypes.byref(m) if m is not None else None, x, xdt, y, ydt, None)
+
+
+def _err(lib):
+    return lib.qint4_last_error().decode()
+
+
+def test_gemv_validation(lib):
+    assert _gemv(lib, None) == 1
+    assert _gemv(lib, _m(codes=0)) == 1
+    assert _gemv(lib, _m(), x=0) == 1
+    assert _gemv(lib, _m(g=48)) == 2 and "group_size 48" in _err(lib)
+    assert _gemv(lib, _m(k_in=96, g=64)) == 2
+    assert _gemv(lib, _m(n_out=0)) == 2
+    assert _gemv(lib, _m(e=2)) == 2
+    assert _gemv(lib, _m(sb=5)) == 3
+    assert _gemv(lib, _m(), xdt=7) == 3
+    assert _gemv(lib, _m(codes=A + 4)) == 4
+    assert _gemv(lib, _m(), x=A + 0x300002) == 4
+    assert _gemv(lib, _m(scales=A + 0x100001)) == 4
+    m = _m()
+    m.reserved = 1
+    assert _gemv(lib, m) == 2
+    # y overlapping the codes
+    assert _gemv(lib, _m(), y=A + 16) == 5 and "overlaps" in _err(lib)
+
+
+def test_multi_validation(lib):
+    ms = (q.CMatrix * 3)(_m(), _m(k_in=512, codes=A + 0x500000), _m(codes=A + 0x600000))
+    ys = (ctypes.c_void_p * 3)(A + 0x700000, A + 0x710000, A + 0x720000)
+    rc = lib.qgemv_int4_multi(3, ms, A + 0x300000, 1, ys, 1, 0, None)
+    assert rc == 2
+    msg = _err(lib)
+    assert "ws[1].k_in = 512" in msg and "ws[0].k_in = 256" in msg and "64 words" in msg
+    assert lib.qgemv_int4_multi(0, ms, A + 0x300000, 1, ys, 1, 0, None) == 2
+    assert lib.qgemv_int4_multi(9, ms, A + 0x300000, 1, ys, 1, 0, None) == 2
+    ms2 = (q.CMatrix * 2)(_m(), _m(n_out=32, codes=A + 0x500000))
+    assert lib.qgemv_int4_multi(2, ms2, A + 0x300000, 1, ys, 1, 1, None) == 2  # swiglu n_out mismatch
+    assert lib.qgemv_int4_multi(3, ms, A + 0x300000, 1, ys, 1, 1, None) == 2  # swiglu needs n == 2
+    assert lib.qgemv_int4_multi(2, ms2, A + 0x300000, 1, ys, 1, 5, None) == 2  # bad epilogue
+    ms3 = (q.CMatrix * 2)(_m(), _m(codes=A + 0x500000))
+    ys_alias = (ctypes.c_void_p * 2)(A + 0x700000, A + 0x700010)
+    assert lib.qgemv_int4_multi(2, ms3, A + 0x300000, 1, ys_alias, 1, 0, None) == 5
+
+
+def _moe(lib, top_k=8, ws_bytes=None, ws=A + 0x900000, e=(16, 16, 16), out=A + 0x800000,
+         residual=A + 0x880000):
+    hidden, inter = 512, 128
+    gate = _m(A, A + 0x10000, A + 0x20000, inter, hidden, 64, e[0], 1)
+    up = _m(A + 0x100000, A + 0x110000, A + 0x120000, inter, hidden, 64, e[1], 1)
+    down = _m(A + 0x200000, A + 0x210000, A + 0x220000, hidden, inter, 64, e[2], 1)
+    need = lib.moe_gather_qgemv_int4_workspace_bytes(inter, max(1, min(top_k, 8)))
+    return lib.moe_gather_qgemv_int4(ctypes.byref(gate), ctypes.byref(up), ctypes.byref(down),
+                                     A + 0x300000, A + 0x310000, A + 0x320000, top_k, residual, out,
+                                     1, ws, need if ws_bytes is None else ws_bytes, None)
+
+
+def test_moe_validation(lib):
+    assert lib.moe_gather_qgemv_int4_workspace_bytes(768, 8) == 8 * 768 * 4
+    assert lib.moe_gather_qgemv_int4_workspace_bytes(768, 9) == 0
+    assert _moe(lib, top_k=0) == 2
+    assert _moe(lib, top_k=9) == 2
+    assert _moe(lib, e=(16, 16, 8)) == 2
+    assert _moe(lib, ws_bytes=16) == 6
+    assert _moe(lib, ws=0) == 6
+    assert _moe(lib, ws=A + 0x900004) == 4
+    assert _moe(lib, out=A + 0x300000 + 64) == 5          # out overlaps x
+    assert _moe(lib, ws=A + 0x800000 + 64) == 5           # workspace overlaps out
+
+
+def _gemm(lib, m, T=32, ldx=256, ldy=64, x=A + 0x300000, y=A + 0x400000, ydt=1):
+    return lib.qgemm_int4_padT(ctypes.byref(m), x, T, ldx, y, ldy, ydt, None)
+
+
+def test_gemm_validation(lib):
+    assert _gemm(lib, _m(n_out=48)) == 2 and "multiple of 32" in _err(lib)
+    assert _gemm(lib, _m(), T=0) == 2
+    assert _gemm(lib, _m(), ldx=128) == 2
+    assert _gemm(lib, _m(), ldx=260) == 2
+    assert _gemm(lib, _m(), ldy=32) == 2
+    assert _gemm(lib, _m(), x=A + 0x300008) == 4
+    assert _gemm(lib, _m(), y=A + 0x300000 + 128) == 5
+
+
+def test_valid_call_without_device_reports_device_error(lib):
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; fake pointers must never reach a launch")
+    assert _gemv(lib, _m()) == 7
+    assert "device" in _err(lib)
