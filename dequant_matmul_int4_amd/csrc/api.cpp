@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 
 #include "kernels.h"
 #include "qint4.h"
@@ -78,6 +79,19 @@ qint4_status check_no_overlap(const Range *outs, int n_out, const Range *ins, in
   return QINT4_OK;
 }
 
+size_t code_bytes(const qint4_matrix *w);
+size_t sb_bytes(const qint4_matrix *w);
+
+// Kernels address a matrix (or expert stack) through 32-bit byte offsets.
+constexpr size_t kMaxMatrixBytes = (size_t)1 << 31;
+
+qint4_status check_matrix_size(const qint4_matrix *w, const char *name) {
+  if (code_bytes(w) >= kMaxMatrixBytes || sb_bytes(w) >= kMaxMatrixBytes)
+    return fail(QINT4_ERR_SHAPE, "%s: %zu code bytes / %zu scale bytes exceed the 2 GiB limit", name,
+                code_bytes(w), sb_bytes(w));
+  return QINT4_OK;
+}
+
 constexpr int64_t kMaxK = 1 << 20;
 constexpr int64_t kMaxRows = (int64_t)1 << 30;
 
@@ -101,7 +115,7 @@ qint4_status check_matrix(const qint4_matrix *w, const char *name, bool experts_
   const size_t sb = elem_bytes(w->sb_dtype);
   if (!aligned(w->scales, sb) || !aligned(w->biases, sb))
     return fail(QINT4_ERR_ALIGN, "%s: scales/biases not aligned to %zu bytes", name, sb);
-  return QINT4_OK;
+  return check_matrix_size(w, name);
 }
 
 size_t code_bytes(const qint4_matrix *w) {
@@ -159,20 +173,31 @@ int lanes_for(int chunks) {
   return l;
 }
 
-// Choose waves per workgroup and lanes per row for a row of `nc` chunks.
-void choose_split(int nc, int *waves, int *lpr) {
-  for (int w : {4, 2, 1}) {
-    if (w == 2) continue;  // only 4- and 1-wave kernels are instantiated
-    if (nc % w) continue;
-    const int l = lanes_for(nc / w);
-    if (l >= 8 || w == 1) {
-      *waves = w;
-      *lpr = l;
-      return;
-    }
-  }
-  *waves = 1;
-  *lpr = lanes_for(nc);
+// Plan a GEMV-family launch over rows of `ncv` (virtual) chunks.
+// tasks_for(rows_per_task) returns the task count for a task height.
+template <class TasksFor>
+GemvPlan plan_gemv(int ncv, int n_cu, int xmode, int n_chunks_x, int64_t residual_rows,
+                   int sb_bf16, int epi, TasksFor tasks_for) {
+  GemvPlan plan;
+  const int lpr = lanes_for(ncv);
+  const int rpi = 64 / lpr;
+  plan.log2_lpr = ilog2(lpr);
+  // two rows per lane when that still leaves >= 8 waves of work per CU
+  plan.rt = tasks_for(2 * rpi) >= 8 * (int64_t)n_cu ? 2 : 1;
+  plan.n_tasks = tasks_for(plan.rt * rpi);
+  plan.lds_bytes = gemv_lds_bytes(xmode, n_chunks_x, residual_rows);
+  // about two persistent workgroups per CU, each staging the activation once
+  int k = (int)std::min<size_t>(2, std::max<size_t>(1, (size_t)kMaxLds / plan.lds_bytes));
+  auto shape = [&](int kk) {
+    int64_t w = (plan.n_tasks + (int64_t)n_cu * kk - 1) / ((int64_t)n_cu * kk);
+    plan.waves = (int)std::max<int64_t>(1, std::min<int64_t>(8, w));
+    plan.grid = std::min<int64_t>((plan.n_tasks + plan.waves - 1) / plan.waves, (int64_t)n_cu * kk);
+  };
+  shape(k);
+  const int bpc = gemv_blocks_per_cu(plan, xmode, sb_bf16, epi);
+  if (bpc >= 1 && bpc < k) shape(bpc);
+  if (plan.grid < 1) plan.grid = 1;
+  return plan;
 }
 
 }  // namespace
@@ -267,67 +292,53 @@ qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t
 
   // plan
   const int nc = (int)(k_in / 32);
-  int waves = 1, lpr = 1;
-  choose_split(nc, &waves, &lpr);
   const int xmode = x_dtype == QINT4_BF16 ? XM_BF16 : XM_F32;
   const int epi = swiglu ? EPI_SWIGLU : EPI_STORE;
-  const int rpi = 64 / lpr;
+  const int sb_bf16 = ws[0].sb_dtype == QINT4_BF16;
   int n_cu = 256;
   st = check_device(&n_cu);
   if (st != QINT4_OK) return prefixed(st, fn);
-
-  auto blocks_for = [&](int rt) {
-    int64_t b = 0;
-    for (int i = 0; i < n_outs; ++i) b += (ws[i].n_out + rt * rpi - 1) / (rt * rpi);
-    return b;
-  };
-  int rt = 1;
-  for (int cand : {4, 2, 1}) {
-    if (swiglu && cand > 2) continue;
-    if (blocks_for(cand) >= 2 * (int64_t)n_cu || cand == 1) {
-      rt = cand;
-      break;
-    }
-  }
-
-  GemvPlan plan;
-  plan.waves = waves;
-  plan.rt = rt;
-  plan.log2_lpr = ilog2(lpr);
-  plan.chunks_per_wave = nc / waves;
-  plan.n_blocks = blocks_for(rt);
-  plan.lds_bytes = gemv_lds_bytes(xmode, nc, waves, rt, plan.log2_lpr, epi);
-  if (plan.lds_bytes > (size_t)kMaxLds)
+  if (gemv_lds_bytes(xmode, nc, 0) > (size_t)kMaxLds)
     return fail(QINT4_ERR_SHAPE, "%s: k_in %lld needs %zu bytes of LDS (max %d)", fn,
-                (long long)k_in, plan.lds_bytes, kMaxLds);
+                (long long)k_in, gemv_lds_bytes(xmode, nc, 0), kMaxLds);
+  auto tasks_for = [&](int rpt) {
+    int64_t t = 0;
+    for (int i = 0; i < n_outs; ++i) t += (ws[i].n_out + rpt - 1) / rpt;
+    return t;
+  };
+  const GemvPlan plan = plan_gemv(nc, n_cu, xmode, nc, 0, sb_bf16, epi, tasks_for);
+  const int rpt = plan.rt * (64 >> plan.log2_lpr);
+  if (plan.n_tasks > INT32_MAX) return fail(QINT4_ERR_SHAPE, "%s: too many rows", fn);
 
   GemvParams p;
   std::memset(&p, 0, sizeof(p));
   p.n_mats = swiglu ? 2 : n;
-  int64_t b0 = 0;
+  int64_t t0 = 0;
   for (int i = 0; i < n; ++i) {
     p.m[i].codes = ws[i].codes;
     p.m[i].scales = ws[i].scales;
     p.m[i].biases = ws[i].biases;
     p.m[i].y = swiglu ? ys[0] : ys[i];
     p.m[i].n_out = ws[i].n_out;
-    p.m[i].block0 = b0;
-    if (!swiglu) b0 += (ws[i].n_out + rt * rpi - 1) / (rt * rpi);
+    p.task0[i] = (int32_t)t0;
+    if (!swiglu) t0 += (ws[i].n_out + rpt - 1) / rpt;
   }
   p.log2_lpr = plan.log2_lpr;
   p.log2_group = ilog2(ws[0].group_size);
   p.chunks_per_row = nc;
-  p.chunks_per_wave = plan.chunks_per_wave;
+  p.steps_per_task = nc >> plan.log2_lpr;
   p.n_chunks_x = nc;
   p.y_bf16 = y_dtype == QINT4_BF16;
-  p.blocks_per_slot = (int32_t)((ws[0].n_out + rt * rpi - 1) / (rt * rpi));
-  p.n_blocks = plan.n_blocks;
+  p.tasks_per_slot = (int32_t)((ws[0].n_out + rpt - 1) / rpt);
+  p.n_tasks = (int32_t)plan.n_tasks;
   p.x = x;
   p.ids = nullptr;
   p.top_k = 1;
   p.n_experts = 1;
+  p.expert_code_stride = ws[0].n_out * (k_in / 8);  // SwiGLU pair: one "expert" = the matrix
+  p.expert_sb_stride = ws[0].n_out * (k_in / ws[0].group_size);
 
-  hipError_t e = launch_gemv(p, plan, xmode, ws[0].sb_dtype == QINT4_BF16, epi, stream);
+  hipError_t e = launch_gemv(p, plan, xmode, sb_bf16, epi, stream);
   if (e != hipSuccess) return fail(QINT4_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
 }
@@ -421,40 +432,24 @@ qint4_status moe_gather_qgemv_int4(const qint4_matrix *gate, const qint4_matrix 
   // ---- launch A: gate/up of every kept expert, SwiGLU -> h[top_k][inter] (f32) ----
   {
     const int nc = (int)(hidden / 32);
-    int waves = 1, lpr = 1;
-    choose_split(nc, &waves, &lpr);
-    const int rpi = 64 / lpr;
-    int rt = 1;
-    for (int cand : {2, 1}) {
-      const int64_t b = (int64_t)top_k * ((inter + cand * rpi - 1) / (cand * rpi));
-      if (b >= 2 * (int64_t)n_cu || cand == 1) {
-        rt = cand;
-        break;
-      }
-    }
-    GemvPlan plan;
-    plan.waves = waves;
-    plan.rt = rt;
-    plan.log2_lpr = ilog2(lpr);
-    plan.chunks_per_wave = nc / waves;
-    const int64_t bps = (inter + rt * rpi - 1) / (rt * rpi);
-    plan.n_blocks = bps * top_k;
-    plan.lds_bytes = gemv_lds_bytes(xmode_a, nc, waves, rt, plan.log2_lpr, EPI_SWIGLU);
-    if (plan.lds_bytes > (size_t)kMaxLds)
+    if (gemv_lds_bytes(xmode_a, nc, 0) > (size_t)kMaxLds)
       return fail(QINT4_ERR_SHAPE, "%s: hidden %lld needs too much LDS", fn, (long long)hidden);
+    auto tasks_for = [&](int rpt) { return (int64_t)top_k * ((inter + rpt - 1) / rpt); };
+    const GemvPlan plan = plan_gemv(nc, n_cu, xmode_a, nc, 0, sb_bf16, EPI_SWIGLU, tasks_for);
+    const int rpt = plan.rt * (64 >> plan.log2_lpr);
     GemvParams p;
     std::memset(&p, 0, sizeof(p));
     p.n_mats = 2;
-    p.m[0] = {gate->codes, gate->scales, gate->biases, h, inter, 0};
-    p.m[1] = {up->codes, up->scales, up->biases, h, inter, 0};
+    p.m[0] = {gate->codes, gate->scales, gate->biases, h, inter};
+    p.m[1] = {up->codes, up->scales, up->biases, h, inter};
     p.log2_lpr = plan.log2_lpr;
     p.log2_group = ilog2(gate->group_size);
     p.chunks_per_row = nc;
-    p.chunks_per_wave = plan.chunks_per_wave;
+    p.steps_per_task = nc >> plan.log2_lpr;
     p.n_chunks_x = nc;
     p.y_bf16 = 0;
-    p.blocks_per_slot = (int32_t)bps;
-    p.n_blocks = plan.n_blocks;
+    p.tasks_per_slot = (int32_t)((inter + rpt - 1) / rpt);
+    p.n_tasks = (int32_t)plan.n_tasks;
     p.x = x;
     p.ids = ids;
     p.top_k = top_k;
@@ -467,45 +462,35 @@ qint4_status moe_gather_qgemv_int4(const qint4_matrix *gate, const qint4_matrix 
   // ---- launch B: down projection of every slot + weighted combine + residual ----
   {
     const int ncl = (int)(inter / 32);
-    const int lpr = lanes_for(ncl);
-    const int rpi = 64 / lpr;
-    int rt = 1;
-    for (int cand : {2, 1}) {
-      const int64_t b = (hidden + cand * rpi - 1) / (cand * rpi);
-      if (b >= 2 * (int64_t)n_cu || cand == 1) {
-        rt = cand;
-        break;
-      }
-    }
-    GemvPlan plan;
-    plan.waves = 8;
-    plan.rt = rt;
-    plan.log2_lpr = ilog2(lpr);
-    plan.chunks_per_wave = ncl;
-    plan.n_blocks = (hidden + rt * rpi - 1) / (rt * rpi);
-    plan.lds_bytes = gemv_lds_bytes(XM_F32, ncl * top_k, 8, rt, plan.log2_lpr, EPI_MOE_DOWN);
-    if (plan.lds_bytes > (size_t)kMaxLds)
+    const int ncv = ncl * top_k;
+    const int64_t res_rows = residual ? hidden : 0;
+    if (gemv_lds_bytes(XM_F32, ncv, res_rows) > (size_t)kMaxLds)
       return fail(QINT4_ERR_SHAPE, "%s: top_k * inter = %lld needs too much LDS", fn,
                   (long long)(top_k * inter));
+    auto tasks_for = [&](int rpt) { return (hidden + rpt - 1) / rpt; };
+    const GemvPlan plan = plan_gemv(ncv, n_cu, XM_F32, ncv, res_rows, sb_bf16, EPI_MOE_DOWN, tasks_for);
     GemvParams p;
     std::memset(&p, 0, sizeof(p));
     p.n_mats = 1;
-    p.m[0] = {down->codes, down->scales, down->biases, out, hidden, 0};
+    p.m[0] = {down->codes, down->scales, down->biases, out, hidden};
     p.log2_lpr = plan.log2_lpr;
     p.log2_group = ilog2(down->group_size);
     p.chunks_per_row = ncl;
-    p.chunks_per_wave = ncl;
-    p.n_chunks_x = ncl * top_k;
+    p.steps_per_task = ncv >> plan.log2_lpr;
+    p.n_chunks_x = ncv;
     p.y_bf16 = act_dtype == QINT4_BF16;
-    p.n_blocks = plan.n_blocks;
+    p.n_tasks = (int32_t)plan.n_tasks;
     p.x = h;
     p.ids = ids;
     p.wts = wts;
     p.residual = residual;
     p.top_k = top_k;
     p.n_experts = down->n_experts;
+    p.inv_chunks_per_row = 1.0f / (float)ncl;
     p.expert_code_stride = hidden * (inter / 8);
     p.expert_sb_stride = hidden * (inter / down->group_size);
+    p.code_bytes = (int64_t)code_bytes(down);
+    p.sb_bytes = (int64_t)sb_bytes(down);
     hipError_t e = launch_gemv(p, plan, XM_F32, sb_bf16, EPI_MOE_DOWN, stream);
     if (e != hipSuccess) return fail(QINT4_ERR_LAUNCH, "%s: down launch failed: %s", fn, hipGetErrorString(e));
   }

@@ -21,20 +21,24 @@ struct GemvMat {
   const void *biases;
   void *y;                   // output base (EPI_STORE: [n_out]; EPI_SWIGLU: [slots][n_out])
   int64_t n_out;
-  int64_t block0;            // first row block of this matrix (EPI_STORE)
 };
 
+// A "task" is one group of rows (rows_per_task = RT * 64 / lanes_per_row)
+// processed by one wave; a "step" is one 32-code chunk of each of those rows.
 struct GemvParams {
   GemvMat m[kMaxMats];
+  int32_t task0[kMaxMats];   // first task of each matrix (EPI_STORE); static offsets,
+                             // so the kernel loads them once
   int32_t n_mats;
-  int32_t log2_lpr;          // lanes cooperating on one row inside a wave
+  int32_t log2_lpr;          // lanes cooperating on one row (row segment)
   int32_t log2_group;        // log2(group_size)
-  int32_t chunks_per_row;    // k_in / 32 of the matrices' rows
-  int32_t chunks_per_wave;   // chunk range owned by one wave (multiple of lanes per row)
-  int32_t n_chunks_x;        // chunks of the staged activation (k_in/32, or top_k*inter/32)
+  int32_t chunks_per_row;    // k_in / 32 of one stored row
+  int32_t steps_per_task;    // chunk steps per task (virtual row chunks / lanes per row)
+  int32_t n_chunks_x;        // chunks of the staged activation
   int32_t y_bf16;            // output element type
-  int32_t blocks_per_slot;   // EPI_SWIGLU: row blocks per (slot, pair)
-  int64_t n_blocks;          // total row blocks
+  int32_t tasks_per_slot;    // EPI_SWIGLU: tasks per (expert slot)
+  int32_t n_tasks;           // total tasks (< 2^31)
+  int32_t pad1_;
   const void *x;             // activation (bf16 bits or float32)
   // MoE
   const uint32_t *ids;       // device [top_k] or nullptr
@@ -42,16 +46,20 @@ struct GemvParams {
   const void *residual;      // device [n_out] or nullptr (EPI_MOE_DOWN)
   int32_t top_k;
   int32_t n_experts;
+  float inv_chunks_per_row;  // 1.0f / chunks_per_row (EPI_MOE_DOWN slot lookup)
+  int32_t pad_;
   int64_t expert_code_stride;  // u32 words between experts
   int64_t expert_sb_stride;    // elements between experts in scales/biases
+  int64_t code_bytes;          // bytes of codes of one stored matrix / stack (< 2^31)
+  int64_t sb_bytes;            // bytes of scales (= biases) of one matrix / stack
 };
 
 struct GemvPlan {
-  int waves;        // 1, 2, 4 or 8
-  int rt;           // rows per lane: 1, 2 or 4
+  int waves;        // waves per workgroup (1..8)
+  int rt;           // rows per lane per task: 1 or 2
   int log2_lpr;
-  int chunks_per_wave;
-  int64_t n_blocks;
+  int64_t n_tasks;
+  int64_t grid;     // workgroups (persistent)
   size_t lds_bytes;
 };
 
@@ -60,8 +68,12 @@ struct GemvPlan {
 hipError_t launch_gemv(const GemvParams &p, const GemvPlan &plan, int xmode, int sb_bf16,
                        int epi, hipStream_t stream);
 
-// LDS bytes a GEMV launch needs.
-size_t gemv_lds_bytes(int xmode, int n_chunks_x, int waves, int rt, int log2_lpr, int epi);
+// LDS bytes a GEMV launch needs: the staged activation, its chunk sums and
+// (MoE down) the float32 residual row.
+size_t gemv_lds_bytes(int xmode, int n_chunks_x, int64_t residual_rows);
+
+// Resident workgroups per CU of the kernel a plan selects (0 if unknown).
+int gemv_blocks_per_cu(const GemvPlan &plan, int xmode, int sb_bf16, int epi);
 
 struct GemmParams {
   const uint32_t *codes;
