@@ -173,31 +173,78 @@ int lanes_for(int chunks) {
   return l;
 }
 
-// Plan a GEMV-family launch over rows of `ncv` (virtual) chunks.
+constexpr int kMaxWaves = 12;  // waves per workgroup (one persistent workgroup per CU)
+
+// Plan a GEMV-family launch over rows of `cpr` (virtual) chunks.
 // tasks_for(rows_per_task) returns the task count for a task height.
+//
+// Candidates: lanes per row L (the exact divisor of the chunk count, or 32/64
+// with a partial last step), row groups per task RT (1, 2) and waves per CU W
+// (1..8).  Tasks are dealt round-robin to n_cu * W waves, so a CU's critical
+// path is ceil(tasks / (n_cu W)) tasks per wave; the cost of a candidate is
+// that times W waves times the loads of one task.  The cheapest wins (ties:
+// larger RT, then more waves).  A residual row (MoE down) must fit the
+// workgroup's one-pass staging: 4 vectors of 16 bytes per thread.
 template <class TasksFor>
-GemvPlan plan_gemv(int ncv, int n_cu, int xmode, int n_chunks_x, int64_t residual_rows,
-                   int sb_bf16, int epi, TasksFor tasks_for) {
-  GemvPlan plan;
-  const int lpr = lanes_for(ncv);
-  const int rpi = 64 / lpr;
-  plan.log2_lpr = ilog2(lpr);
-  // two rows per lane when that still leaves >= 8 waves of work per CU
-  plan.rt = tasks_for(2 * rpi) >= 8 * (int64_t)n_cu ? 2 : 1;
-  plan.n_tasks = tasks_for(plan.rt * rpi);
-  plan.lds_bytes = gemv_lds_bytes(xmode, n_chunks_x, residual_rows);
-  // about two persistent workgroups per CU, each staging the activation once
-  int k = (int)std::min<size_t>(2, std::max<size_t>(1, (size_t)kMaxLds / plan.lds_bytes));
-  auto shape = [&](int kk) {
-    int64_t w = (plan.n_tasks + (int64_t)n_cu * kk - 1) / ((int64_t)n_cu * kk);
-    plan.waves = (int)std::max<int64_t>(1, std::min<int64_t>(8, w));
-    plan.grid = std::min<int64_t>((plan.n_tasks + plan.waves - 1) / plan.waves, (int64_t)n_cu * kk);
-  };
-  shape(k);
-  const int bpc = gemv_blocks_per_cu(plan, xmode, sb_bf16, epi);
-  if (bpc >= 1 && bpc < k) shape(bpc);
-  if (plan.grid < 1) plan.grid = 1;
-  return plan;
+GemvPlan plan_gemv(int cpr, int n_cu, int xmode, int64_t residual_rows, TasksFor tasks_for) {
+  GemvPlan best{};
+  double best_cost = 1e300;
+  int cand_l[3] = {lanes_for(cpr), 0, 0};
+  int nl = 1;
+  for (int l : {32, 64})
+    if (cpr > l && cpr % l != 0 && l > cand_l[0]) cand_l[nl++] = l;
+  const int xq_octets = (xmode == XM_BF16 ? 2 : 5) * 64;  // octets one wave stages without a stall
+  for (int li = 0; li < nl; ++li) {
+    const int L = cand_l[li];
+    const int spt = (cpr + L - 1) / L;
+    const size_t lds = gemv_lds_bytes(xmode, spt * L, residual_rows);
+    if (lds > (size_t)kMaxLds) continue;
+    for (int rt = 1; rt <= 2; ++rt) {
+      const int64_t n_tasks = tasks_for(rt * (64 / L));
+      for (int w = 1; w <= kMaxWaves; ++w) {
+        if (residual_rows > (int64_t)w * 64 * 4 * 4) continue;
+        const int64_t grid = std::min<int64_t>(n_cu, (n_tasks + w - 1) / w);
+        const int64_t nw = grid * w;
+        const int64_t tpw = (n_tasks + nw - 1) / nw;
+        double cost = (double)tpw * w * spt * rt;
+        if ((int64_t)cpr * 4 > (int64_t)xq_octets * w) cost *= 1.5;  // staging would stall
+        const bool better = cost < best_cost * (1 - 1e-9) ||
+                            (cost <= best_cost * (1 + 1e-9) &&
+                             (rt > best.rt || (rt == best.rt && w > best.waves)));
+        if (better) {
+          best_cost = cost;
+          best.waves = w;
+          best.rt = rt;
+          best.log2_lpr = ilog2(L);
+          best.spt = spt;
+          best.n_tasks = n_tasks;
+          best.grid = grid;
+          best.lds_bytes = lds;
+        }
+      }
+    }
+  }
+  return best;
+}
+
+// Fill the geometry fields of GemvParams from a plan.
+void set_geometry(GemvParams &p, const GemvPlan &plan, int cpr, int ncx, int64_t kwb, int64_t sbrow,
+                  int group_size) {
+  const int L = 1 << plan.log2_lpr;
+  p.log2_lpr = plan.log2_lpr;
+  p.log2_group = ilog2(group_size);
+  p.spt = plan.spt;
+  p.rpt = plan.rt * (64 / L);
+  p.last_lanes = cpr - (plan.spt - 1) * L;
+  p.ncx = ncx;
+  p.ncx_pad = plan.spt * L;
+  p.kwb = (int32_t)kwb;
+  p.sbrow = (int32_t)sbrow;
+  p.n_tasks = (int32_t)plan.n_tasks;
+  p.waves_per_wg = plan.waves;
+  p.n_waves = (int32_t)(plan.grid * plan.waves);
+  p.tasks_q = (int32_t)(plan.n_tasks / p.n_waves);
+  p.tasks_r = (int32_t)(plan.n_tasks % p.n_waves);
 }
 
 }  // namespace
@@ -298,22 +345,23 @@ qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t
   int n_cu = 256;
   st = check_device(&n_cu);
   if (st != QINT4_OK) return prefixed(st, fn);
-  if (gemv_lds_bytes(xmode, nc, 0) > (size_t)kMaxLds)
-    return fail(QINT4_ERR_SHAPE, "%s: k_in %lld needs %zu bytes of LDS (max %d)", fn,
-                (long long)k_in, gemv_lds_bytes(xmode, nc, 0), kMaxLds);
   auto tasks_for = [&](int rpt) {
     int64_t t = 0;
     for (int i = 0; i < n_outs; ++i) t += (ws[i].n_out + rpt - 1) / rpt;
     return t;
   };
-  const GemvPlan plan = plan_gemv(nc, n_cu, xmode, nc, 0, sb_bf16, epi, tasks_for);
-  const int rpt = plan.rt * (64 >> plan.log2_lpr);
+  const GemvPlan plan = plan_gemv(nc, n_cu, xmode, 0, tasks_for);
+  if (plan.waves == 0)
+    return fail(QINT4_ERR_SHAPE, "%s: k_in %lld needs more than %d bytes of LDS", fn,
+                (long long)k_in, kMaxLds);
   if (plan.n_tasks > INT32_MAX) return fail(QINT4_ERR_SHAPE, "%s: too many rows", fn);
+  const int rpt = plan.rt * (64 >> plan.log2_lpr);
 
   GemvParams p;
   std::memset(&p, 0, sizeof(p));
   p.n_mats = swiglu ? 2 : n;
   int64_t t0 = 0;
+  for (int i = 0; i < kMaxMats; ++i) p.task0[i] = INT32_MAX;
   for (int i = 0; i < n; ++i) {
     p.m[i].codes = ws[i].codes;
     p.m[i].scales = ws[i].scales;
@@ -323,20 +371,14 @@ qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t
     p.task0[i] = (int32_t)t0;
     if (!swiglu) t0 += (ws[i].n_out + rpt - 1) / rpt;
   }
-  p.log2_lpr = plan.log2_lpr;
-  p.log2_group = ilog2(ws[0].group_size);
-  p.chunks_per_row = nc;
-  p.steps_per_task = nc >> plan.log2_lpr;
-  p.n_chunks_x = nc;
+  const int64_t sbrow = (k_in / ws[0].group_size) * (int64_t)elem_bytes(ws[0].sb_dtype);
+  set_geometry(p, plan, nc, nc, k_in / 2, sbrow, ws[0].group_size);
   p.y_bf16 = y_dtype == QINT4_BF16;
-  p.tasks_per_slot = (int32_t)((ws[0].n_out + rpt - 1) / rpt);
-  p.n_tasks = (int32_t)plan.n_tasks;
   p.x = x;
   p.ids = nullptr;
   p.top_k = 1;
   p.n_experts = 1;
-  p.expert_code_stride = ws[0].n_out * (k_in / 8);  // SwiGLU pair: one "expert" = the matrix
-  p.expert_sb_stride = ws[0].n_out * (k_in / ws[0].group_size);
+  p.tasks_per_slot = (int32_t)plan.n_tasks;
 
   hipError_t e = launch_gemv(p, plan, xmode, sb_bf16, epi, stream);
   if (e != hipSuccess) return fail(QINT4_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(e));
@@ -432,30 +474,26 @@ qint4_status moe_gather_qgemv_int4(const qint4_matrix *gate, const qint4_matrix 
   // ---- launch A: gate/up of every kept expert, SwiGLU -> h[top_k][inter] (f32) ----
   {
     const int nc = (int)(hidden / 32);
-    if (gemv_lds_bytes(xmode_a, nc, 0) > (size_t)kMaxLds)
-      return fail(QINT4_ERR_SHAPE, "%s: hidden %lld needs too much LDS", fn, (long long)hidden);
     auto tasks_for = [&](int rpt) { return (int64_t)top_k * ((inter + rpt - 1) / rpt); };
-    const GemvPlan plan = plan_gemv(nc, n_cu, xmode_a, nc, 0, sb_bf16, EPI_SWIGLU, tasks_for);
+    const GemvPlan plan = plan_gemv(nc, n_cu, xmode_a, 0, tasks_for);
+    if (plan.waves == 0)
+      return fail(QINT4_ERR_SHAPE, "%s: hidden %lld needs too much LDS", fn, (long long)hidden);
     const int rpt = plan.rt * (64 >> plan.log2_lpr);
     GemvParams p;
     std::memset(&p, 0, sizeof(p));
     p.n_mats = 2;
     p.m[0] = {gate->codes, gate->scales, gate->biases, h, inter};
     p.m[1] = {up->codes, up->scales, up->biases, h, inter};
-    p.log2_lpr = plan.log2_lpr;
-    p.log2_group = ilog2(gate->group_size);
-    p.chunks_per_row = nc;
-    p.steps_per_task = nc >> plan.log2_lpr;
-    p.n_chunks_x = nc;
+    const int64_t sbrow = (hidden / gate->group_size) * (int64_t)elem_bytes(gate->sb_dtype);
+    set_geometry(p, plan, nc, nc, hidden / 2, sbrow, gate->group_size);
     p.y_bf16 = 0;
     p.tasks_per_slot = (int32_t)((inter + rpt - 1) / rpt);
-    p.n_tasks = (int32_t)plan.n_tasks;
     p.x = x;
     p.ids = ids;
     p.top_k = top_k;
     p.n_experts = gate->n_experts;
-    p.expert_code_stride = inter * (hidden / 8);
-    p.expert_sb_stride = inter * (hidden / gate->group_size);
+    p.ecode_bytes = (uint32_t)(inter * (hidden / 2));
+    p.esb_bytes = (uint32_t)(inter * sbrow);
     hipError_t e = launch_gemv(p, plan, xmode_a, sb_bf16, EPI_SWIGLU, stream);
     if (e != hipSuccess) return fail(QINT4_ERR_LAUNCH, "%s: gate/up launch failed: %s", fn, hipGetErrorString(e));
   }
@@ -464,33 +502,30 @@ qint4_status moe_gather_qgemv_int4(const qint4_matrix *gate, const qint4_matrix 
     const int ncl = (int)(inter / 32);
     const int ncv = ncl * top_k;
     const int64_t res_rows = residual ? hidden : 0;
-    if (gemv_lds_bytes(XM_F32, ncv, res_rows) > (size_t)kMaxLds)
+    auto tasks_for = [&](int rpt) { return (hidden + rpt - 1) / rpt; };
+    const GemvPlan plan = plan_gemv(ncv, n_cu, XM_F32, res_rows, tasks_for);
+    if (plan.waves == 0)
       return fail(QINT4_ERR_SHAPE, "%s: top_k * inter = %lld needs too much LDS", fn,
                   (long long)(top_k * inter));
-    auto tasks_for = [&](int rpt) { return (hidden + rpt - 1) / rpt; };
-    const GemvPlan plan = plan_gemv(ncv, n_cu, XM_F32, ncv, res_rows, sb_bf16, EPI_MOE_DOWN, tasks_for);
     GemvParams p;
     std::memset(&p, 0, sizeof(p));
     p.n_mats = 1;
     p.m[0] = {down->codes, down->scales, down->biases, out, hidden};
-    p.log2_lpr = plan.log2_lpr;
-    p.log2_group = ilog2(down->group_size);
-    p.chunks_per_row = ncl;
-    p.steps_per_task = ncv >> plan.log2_lpr;
-    p.n_chunks_x = ncv;
+    const int64_t sbrow = (inter / down->group_size) * (int64_t)elem_bytes(down->sb_dtype);
+    set_geometry(p, plan, ncv, ncv, inter / 2, sbrow, down->group_size);
     p.y_bf16 = act_dtype == QINT4_BF16;
-    p.n_tasks = (int32_t)plan.n_tasks;
     p.x = h;
     p.ids = ids;
     p.wts = wts;
     p.residual = residual;
     p.top_k = top_k;
     p.n_experts = down->n_experts;
-    p.inv_chunks_per_row = 1.0f / (float)ncl;
-    p.expert_code_stride = hidden * (inter / 8);
-    p.expert_sb_stride = hidden * (inter / down->group_size);
-    p.code_bytes = (int64_t)code_bytes(down);
-    p.sb_bytes = (int64_t)sb_bytes(down);
+    p.cpr_e = ncl;
+    p.inv_cpr_e = 1.0f / (float)ncl;
+    p.ecode_bytes = (uint32_t)(hidden * (inter / 2));
+    p.esb_bytes = (uint32_t)(hidden * sbrow);
+    p.code_bytes = (uint32_t)code_bytes(down);
+    p.sb_bytes = (uint32_t)sb_bytes(down);
     hipError_t e = launch_gemv(p, plan, XM_F32, sb_bf16, EPI_MOE_DOWN, stream);
     if (e != hipSuccess) return fail(QINT4_ERR_LAUNCH, "%s: down launch failed: %s", fn, hipGetErrorString(e));
   }

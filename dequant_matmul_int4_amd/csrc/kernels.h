@@ -19,45 +19,58 @@ struct GemvMat {
   const uint32_t *codes;     // expert 0, row 0
   const void *scales;
   const void *biases;
-  void *y;                   // output base (EPI_STORE: [n_out]; EPI_SWIGLU: [slots][n_out])
+  void *y;                   // output base (EPI_SWIGLU: [slots][n_out])
   int64_t n_out;
 };
 
-// A "task" is one group of rows (rows_per_task = RT * 64 / lanes_per_row)
-// processed by one wave; a "step" is one 32-code chunk of each of those rows.
+// Loads in flight per lane (128-bit code loads) in a GEMV wave's register ring.
+constexpr int kSlots = 8;
+
+// Kernel arguments of the GEMV family.  A "task" is rpt rows, all of whose
+// chunks (32 codes = 16 bytes) one wave processes; L lanes cover one row, so a
+// step (one 16-byte load per lane) covers L chunks of 64 / L rows.  Tasks are
+// dealt round-robin: wave w takes tasks w, w + n_waves, ...
 struct GemvParams {
   GemvMat m[kMaxMats];
-  int32_t task0[kMaxMats];   // first task of each matrix (EPI_STORE); static offsets,
-                             // so the kernel loads them once
+  int32_t task0[kMaxMats];   // first task of each matrix (EPI_STORE), INT32_MAX past n_mats
   int32_t n_mats;
-  int32_t log2_lpr;          // lanes cooperating on one row (row segment)
-  int32_t log2_group;        // log2(group_size)
-  int32_t chunks_per_row;    // k_in / 32 of one stored row
-  int32_t steps_per_task;    // chunk steps per task (virtual row chunks / lanes per row)
-  int32_t n_chunks_x;        // chunks of the staged activation
-  int32_t y_bf16;            // output element type
-  int32_t tasks_per_slot;    // EPI_SWIGLU: tasks per (expert slot)
-  int32_t n_tasks;           // total tasks (< 2^31)
-  int32_t pad1_;
-  const void *x;             // activation (bf16 bits or float32)
+  int32_t log2_lpr;          // L = 1 << log2_lpr lanes per row
+  int32_t log2_group;
+  int32_t spt;               // steps per task (the last may be partial)
+  int32_t rpt;               // rows per task
+  int32_t last_lanes;        // lanes of a row holding a chunk in the last step
+  int32_t ncx;               // staged activation chunks
+  int32_t ncx_pad;           // spt * L: staged chunks including zero padding
+  int32_t kwb;               // code bytes of one stored row
+  int32_t sbrow;             // scale (= bias) bytes of one stored row
+  int32_t n_tasks;
+  int32_t tasks_q;           // n_tasks = tasks_q * n_waves + tasks_r
+  int32_t tasks_r;
+  int32_t n_waves;           // waves of the grid
+  int32_t waves_per_wg;
+  int32_t y_bf16;
   // MoE
+  int32_t top_k;
+  int32_t n_experts;
+  int32_t tasks_per_slot;    // EPI_SWIGLU: tasks of one expert slot
+  int32_t pad0_;
+  int32_t cpr_e;             // EPI_MOE_DOWN: chunks of one expert row
+  float inv_cpr_e;
+  uint32_t ecode_bytes;      // code bytes between experts
+  uint32_t esb_bytes;        // scale bytes between experts
+  uint32_t code_bytes;       // EPI_MOE_DOWN: code bytes of the whole stack (< 2^31)
+  uint32_t sb_bytes;         // EPI_MOE_DOWN: scale bytes of the whole stack
+  const void *x;             // activation (bf16 bits or float32), 16-byte aligned
   const uint32_t *ids;       // device [top_k] or nullptr
   const float *wts;          // device [top_k] (EPI_MOE_DOWN)
   const void *residual;      // device [n_out] or nullptr (EPI_MOE_DOWN)
-  int32_t top_k;
-  int32_t n_experts;
-  float inv_chunks_per_row;  // 1.0f / chunks_per_row (EPI_MOE_DOWN slot lookup)
-  int32_t pad_;
-  int64_t expert_code_stride;  // u32 words between experts
-  int64_t expert_sb_stride;    // elements between experts in scales/biases
-  int64_t code_bytes;          // bytes of codes of one stored matrix / stack (< 2^31)
-  int64_t sb_bytes;            // bytes of scales (= biases) of one matrix / stack
 };
 
 struct GemvPlan {
-  int waves;        // waves per workgroup (1..8)
-  int rt;           // rows per lane per task: 1 or 2
+  int waves;        // waves per workgroup
+  int rt;           // row groups per task: 1 or 2
   int log2_lpr;
+  int spt;
   int64_t n_tasks;
   int64_t grid;     // workgroups (persistent)
   size_t lds_bytes;
@@ -68,12 +81,9 @@ struct GemvPlan {
 hipError_t launch_gemv(const GemvParams &p, const GemvPlan &plan, int xmode, int sb_bf16,
                        int epi, hipStream_t stream);
 
-// LDS bytes a GEMV launch needs: the staged activation, its chunk sums and
-// (MoE down) the float32 residual row.
-size_t gemv_lds_bytes(int xmode, int n_chunks_x, int64_t residual_rows);
-
-// Resident workgroups per CU of the kernel a plan selects (0 if unknown).
-int gemv_blocks_per_cu(const GemvPlan &plan, int xmode, int sb_bf16, int epi);
+// LDS bytes a GEMV launch needs: the staged activation (padded to ncx_pad
+// chunks), its chunk sums and (MoE down) the float32 residual row.
+size_t gemv_lds_bytes(int xmode, int ncx_pad, int64_t residual_rows);
 
 struct GemmParams {
   const uint32_t *codes;

@@ -3,8 +3,8 @@
 // One kernel template covers the single GEMV, the multi-projection GEMV that
 // shares one input (q/k/v in one launch), the gate/up pair with a SwiGLU
 // epilogue (dense FFN, and the MoE gate/up phase with device-side expert ids),
-// and the MoE down projection with the weighted 8-way scalar-FMA combine and
-// residual add.
+// and the MoE down projection with the weighted scalar-FMA combine of the kept
+// experts and the residual add.
 //
 // Sources (by page title and passage):
 //   [FFAI #14] thewafflehaus/FFAI pull 14, "feat(everything-bagel): clean
@@ -12,22 +12,31 @@
 //              (weight, scales, biases, in_dim, group_size); batched QKV and
 //              4-way qgemv (one launch, input read once); expert-indexed GEMV
 //              (expert id read on the device); chain8 down+SwiGLU+accumulate
-//              (per-thread accumulator with the slot scalar baked in, reduced
+//              (per-thread accumulator with the slot scalar folded in, reduced
 //              across threads at the end); scalarFMAChain8.
 //   [FFAI #9]  thewafflehaus/FFAI pull 9, "Everything Bagel": fused swiglu.
 //
 // Work decomposition (gfx950 specific, not from the pages):
 //   * A row is split into 32-code chunks (16 bytes of codes = one 128-bit
-//     load, half of a 64-wide group).  LPR lanes of a wave cooperate on one
-//     row (lane j takes chunks j, j+LPR, ...), so consecutive lanes read
-//     consecutive 16 B of a row; a wave task is RT * 64/LPR whole rows.
-//   * Waves are persistent and independent: wave w takes tasks w, w + #waves,
-//     ...  A register ring keeps the next D chunk steps (D * RT loads of
-//     16 B per lane, 8 in total) in flight across task boundaries, and the
-//     first D steps are issued before the activation is staged.
+//     load, inside one group since group_size >= 32).  L lanes of a wave
+//     cooperate on one row (lane j takes chunks j, j + L, ...), so consecutive
+//     lanes read consecutive 16 bytes; a "step" is one such load per lane and
+//     a task is RT * 64/L whole rows.  When L does not divide the chunk count,
+//     the last step of a row is partial.
+//   * Tasks are dealt round-robin over all waves of a persistent grid (wave w
+//     takes tasks w, w + n_waves, ...): at any moment the grid streams one
+//     compact region of each matrix, which the memory system serves better
+//     than many far-apart streams.  The host picks wave counts that divide
+//     the task count where it can, so every wave ends at the same time.
+//   * Each wave keeps kSlots 128-bit code loads (plus their scale and bias
+//     loads) in flight in a register ring that runs across task boundaries;
+//     the first ring fill is issued before the activation is staged.  Few
+//     waves per CU with deep rings: vector registers are plentiful at low
+//     occupancy, and each wave has fewer prologue instructions to amortise.
 //   * The activation is staged once per workgroup in LDS, permuted so that a
 //     lane's 128-bit LDS reads line up with the nibble order of its code
-//     words, together with the sum of every 32-element chunk.
+//     words, together with the sum of every 32-element chunk; it is padded
+//     with zero chunks up to whole steps.
 //   * bf16 activations: a nibble pair (q_i, q_{i+4}) of a word becomes the
 //     bf16 pair (128 + q_i, 128 + q_{i+4}) with one AND-OR (bf16 0x4300 is
 //     128.0 and its mantissa step is 1), and v_dot2_f32_bf16 multiplies it
@@ -41,8 +50,12 @@
 //     reads that expert's codes, and folds the slot weight into its
 //     accumulator (the scalar FMA of that slot), before the lanes are reduced
 //     and the residual added.
-//   * Row sums are reduced across the LPR lanes with DPP (quad_perm,
+//   * Row sums are reduced across the L lanes with DPP (quad_perm,
 //     row_half_mirror, row_mirror) and the gfx950 permlane16/32 swaps.
+//   * Every memory access is a raw buffer load: an offset at or beyond the
+//     resource size returns zero without touching memory, which covers rows
+//     past a matrix's end, the partial last step and skipped experts without
+//     branches.
 
 #include "kernels.h"
 
@@ -53,14 +66,6 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-template <int SBT>
-__device__ __forceinline__ float load_sb(const void *base, int64_t idx) {
-  if constexpr (SBT == 1)
-    return __uint_as_float((uint32_t)(reinterpret_cast<const uint16_t *>(base)[idx]) << 16);
-  else
-    return reinterpret_cast<const float *>(base)[idx];
-}
 
 // Workgroup barrier that orders LDS only.  __syncthreads() also fences
 // global memory, which on gfx9 means draining every outstanding vector memory
@@ -87,6 +92,40 @@ __device__ __forceinline__ void warm_kernargs() {
   // one statement consuming every value: all loads issue, then a single wait
   asm volatile("" ::"s"(v[0]), "s"(v[1]), "s"(v[2]), "s"(v[3]), "s"(v[4]), "s"(v[5]), "s"(v[6]),
                "s"(v[7]));
+}
+
+// Eight 32-bit words from a uniform device address through the scalar cache
+// (lgkmcnt, so the wait does not drain outstanding vector loads).  Word k is
+// read from base[min(k, n - 1)], so nothing past the n-word array is touched.
+__device__ __forceinline__ void scalar_load8(const uint32_t *base, int n, uint32_t (&v)[8]) {
+  const uint32_t *a[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) a[k] = base + (k < n ? k : n - 1);
+  asm volatile(
+      "s_load_dword %0, %8, 0x0\n\t"
+      "s_load_dword %1, %9, 0x0\n\t"
+      "s_load_dword %2, %10, 0x0\n\t"
+      "s_load_dword %3, %11, 0x0\n\t"
+      "s_load_dword %4, %12, 0x0\n\t"
+      "s_load_dword %5, %13, 0x0\n\t"
+      "s_load_dword %6, %14, 0x0\n\t"
+      "s_load_dword %7, %15, 0x0\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      // early-clobber: a result register must not be the address of a later
+      // load in this block (the loads complete asynchronously)
+      : "=&s"(v[0]), "=&s"(v[1]), "=&s"(v[2]), "=&s"(v[3]), "=&s"(v[4]), "=&s"(v[5]),
+        "=&s"(v[6]), "=&s"(v[7])
+      : "s"(a[0]), "s"(a[1]), "s"(a[2]), "s"(a[3]), "s"(a[4]), "s"(a[5]), "s"(a[6]), "s"(a[7])
+      : "memory");
+}
+
+// A VGPR whose lane k (k < 8) holds v[k]; other lanes hold 0.
+__device__ __forceinline__ uint32_t lanes_from_scalars(const uint32_t (&v)[8]) {
+  const int lane = threadIdx.x & 63;
+  uint32_t r = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) r = lane == k ? v[k] : r;
+  return r;
 }
 
 template <int CTRL>
@@ -122,28 +161,32 @@ __device__ __forceinline__ float seg_sum(float v, int l2) {
 }
 
 // sum over one 32-code chunk of (128 + q_k) * x_k, starting from acc.
-// xp: the chunk's 16 bf16 pairs as 4 x uint4 (pair i of word jj is
-// (x[8jj+i], x[8jj+i+4])).
+// xv: the chunk's 16 bf16 pairs as 4 x uint4 (pair i of word jj is
+// (x[8jj+i], x[8jj+i+4])).  One accumulator per word: four independent
+// dependency chains instead of one.
 __device__ __forceinline__ float dot_chunk_bf16(const uint4 q, const uint4 *xv, uint32_t magic,
                                                 float acc) {
   const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  float a[4] = {acc, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     const uint32_t xs[4] = {xv[jj].x, xv[jj].y, xv[jj].z, xv[jj].w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t pq = ((w[jj] >> (4 * i)) & 0x000F000Fu) | magic;
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pq),
-                                            __builtin_bit_cast(bf16x2_t, xs[i]), acc, false);
+      a[jj] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pq),
+                                              __builtin_bit_cast(bf16x2_t, xs[i]), a[jj], false);
     }
   }
-  return acc;
+  return (a[0] + a[1]) + (a[2] + a[3]);
 }
 
 // sum over one 32-code chunk of q_k * x_k in float32.  xv: 8 x float4, word jj
-// uses xv[2jj] = (x0, x2, x4, x6) and xv[2jj+1] = (x1, x3, x5, x7).
+// uses xv[2jj] = (x0, x2, x4, x6) and xv[2jj+1] = (x1, x3, x5, x7).  One
+// accumulator per word (four independent dependency chains).
 __device__ __forceinline__ float dot_chunk_f32(const uint4 q, const float4 *xv, float acc) {
   const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  float c[4] = {acc, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     uint32_t lo = w[jj] & 0x0F0F0F0Fu;
@@ -151,165 +194,22 @@ __device__ __forceinline__ float dot_chunk_f32(const uint4 q, const float4 *xv, 
     // keep the byte split: lets the compiler use v_cvt_f32_ubyte{0..3}
     asm("" : "+v"(lo), "+v"(hi));
     const float4 a = xv[2 * jj], b = xv[2 * jj + 1];
-    acc = fmaf((float)(lo & 0xFFu), a.x, acc);
-    acc = fmaf((float)((lo >> 8) & 0xFFu), a.y, acc);
-    acc = fmaf((float)((lo >> 16) & 0xFFu), a.z, acc);
-    acc = fmaf((float)(lo >> 24), a.w, acc);
-    acc = fmaf((float)(hi & 0xFFu), b.x, acc);
-    acc = fmaf((float)((hi >> 8) & 0xFFu), b.y, acc);
-    acc = fmaf((float)((hi >> 16) & 0xFFu), b.z, acc);
-    acc = fmaf((float)(hi >> 24), b.w, acc);
+    float t = c[jj];
+    t = fmaf((float)(lo & 0xFFu), a.x, t);
+    t = fmaf((float)((lo >> 8) & 0xFFu), a.y, t);
+    t = fmaf((float)((lo >> 16) & 0xFFu), a.z, t);
+    t = fmaf((float)(lo >> 24), a.w, t);
+    t = fmaf((float)(hi & 0xFFu), b.x, t);
+    t = fmaf((float)((hi >> 8) & 0xFFu), b.y, t);
+    t = fmaf((float)((hi >> 16) & 0xFFu), b.z, t);
+    t = fmaf((float)(hi >> 24), b.w, t);
+    c[jj] = t;
   }
-  return acc;
+  return (c[0] + c[1]) + (c[2] + c[3]);
 }
-
-// Stage the activation (n_chunks * 32 elements) into LDS.  Layout is
-// plane-major so that lanes reading consecutive chunks hit consecutive 16 B:
-//   bf16: plane jj (0..3) of chunk c at uint4 index jj * n_chunks + c
-//   f32 : plane pl (0..7) of chunk c at float4 index pl * n_chunks + c
-// xsum[c] = sum of the chunk's 32 elements (float32, fixed order).
-//
-// Thread t handles the 8-element octets t, t + nthreads, ...  Staging is split
-// in two: stage_issue() starts the global loads of the first XQ octets into
-// registers, stage_commit() permutes them into LDS.  Code loads issued in
-// between overlap the activation's round trip: vmcnt drains in issue order,
-// so the commit waits only for the older activation loads.
-constexpr int XQ = 8;
-
-template <int XM>
-struct XRegs {
-  uint4 v[XQ][XM == XM_BF16 ? 1 : 2];
-};
-
-template <int XM>
-__device__ __forceinline__ void stage_load(const void *x, int o, uint4 *v) {
-  if constexpr (XM == XM_BF16) {
-    v[0] = reinterpret_cast<const uint4 *>(x)[o];
-  } else {
-    v[0] = reinterpret_cast<const uint4 *>(x)[2 * o];
-    v[1] = reinterpret_cast<const uint4 *>(x)[2 * o + 1];
-  }
-}
-
-// Writes octet o (already in v) to the LDS planes and its chunk sum.  Must be
-// called by whole quads of lanes (the four octets of a chunk are in one quad).
-template <int XM>
-__device__ __forceinline__ void stage_store(int o, const uint4 *v, int n_chunks,
-                                            unsigned char *xbuf, float *xsum) {
-  const int c = o >> 2, jj = o & 3;
-  float s;
-  if constexpr (XM == XM_BF16) {
-    const uint4 w = v[0];
-    uint4 pr;
-    pr.x = (w.x & 0xFFFFu) | (w.z << 16);
-    pr.y = (w.x >> 16) | (w.z & 0xFFFF0000u);
-    pr.z = (w.y & 0xFFFFu) | (w.w << 16);
-    pr.w = (w.y >> 16) | (w.w & 0xFFFF0000u);
-    reinterpret_cast<uint4 *>(xbuf)[jj * n_chunks + c] = pr;
-    s = ((bf16_lo(w.x) + bf16_hi(w.x)) + (bf16_lo(w.y) + bf16_hi(w.y))) +
-        ((bf16_lo(w.z) + bf16_hi(w.z)) + (bf16_lo(w.w) + bf16_hi(w.w)));
-  } else {
-    const float4 a = __builtin_bit_cast(float4, v[0]);
-    const float4 b = __builtin_bit_cast(float4, v[1]);
-    reinterpret_cast<float4 *>(xbuf)[(2 * jj) * n_chunks + c] = make_float4(a.x, a.z, b.x, b.z);
-    reinterpret_cast<float4 *>(xbuf)[(2 * jj + 1) * n_chunks + c] = make_float4(a.y, a.w, b.y, b.w);
-    s = ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
-  }
-  s += dpp_mov<0xB1>(s);
-  s += dpp_mov<0x4E>(s);
-  if (jj == 0) xsum[c] = s;
-}
-
-template <int XM>
-__device__ __forceinline__ void stage_issue(const void *__restrict__ x, int n_chunks, XRegs<XM> &r) {
-  const int nocts = n_chunks * 4;
-#pragma unroll
-  for (int i = 0; i < XQ; ++i) {
-    // unconditional (clamped) loads: a load inside a branch makes the
-    // compiler copy its result at the join, which waits for it right away
-    const int o = min((int)(threadIdx.x + i * blockDim.x), nocts - 1);
-    stage_load<XM>(x, o, r.v[i]);
-  }
-}
-
-template <int XM>
-__device__ __forceinline__ void stage_commit(const void *__restrict__ x, int n_chunks,
-                                             const XRegs<XM> &r, unsigned char *xbuf, float *xsum) {
-  const int nocts = n_chunks * 4;
-#pragma unroll
-  for (int i = 0; i < XQ; ++i) {
-    const int o = threadIdx.x + i * blockDim.x;
-    if (o < nocts) stage_store<XM>(o, r.v[i], n_chunks, xbuf, xsum);
-  }
-  // octets beyond the first XQ per thread (very long rows): load and store
-  for (int o = threadIdx.x + XQ * blockDim.x; o < nocts; o += blockDim.x) {
-    uint4 v[XM == XM_BF16 ? 1 : 2];
-    stage_load<XM>(x, o, v);
-    stage_store<XM>(o, v, n_chunks, xbuf, xsum);
-  }
-}
-
-// The MoE residual row, staged as float32 in LDS (loads issued with the
-// activation's, before the first code loads; read back at task ends).
-constexpr int RQ = 4;
-
-// nvec: 16-byte vectors readable at res (loads are clamped to it)
-__device__ __forceinline__ void residual_issue(const void *res, int nvec, uint4 (&v)[RQ]) {
-#pragma unroll
-  for (int i = 0; i < RQ; ++i) {
-    const int o = min((int)(threadIdx.x + i * blockDim.x), nvec - 1);
-    v[i] = reinterpret_cast<const uint4 *>(res)[o];
-  }
-}
-
-__device__ __forceinline__ void residual_store(int o, const uint4 w, int bf16, float *dst) {
-  if (bf16) {
-    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      dst[8 * o + 2 * k] = bf16_lo(u[k]);
-      dst[8 * o + 2 * k + 1] = bf16_hi(u[k]);
-    }
-  } else {
-    reinterpret_cast<float4 *>(dst)[o] = __builtin_bit_cast(float4, w);
-  }
-}
-
-__device__ __forceinline__ void residual_commit(const void *res, int n, int bf16, const uint4 (&v)[RQ],
-                                                float *dst) {
-  const int nvec = bf16 ? n / 8 : n / 4;
-#pragma unroll
-  for (int i = 0; i < RQ; ++i) {
-    const int o = threadIdx.x + i * blockDim.x;
-    if (o < nvec) residual_store(o, v[i], bf16, dst);
-  }
-  for (int o = threadIdx.x + RQ * blockDim.x; o < nvec; o += blockDim.x)
-    residual_store(o, reinterpret_cast<const uint4 *>(res)[o], bf16, dst);
-}
-
-__device__ __forceinline__ void store_out(void *y, int64_t i, float v, int bf16) {
-  if (bf16)
-    reinterpret_cast<__bf16 *>(y)[i] = (__bf16)v;
-  else
-    reinterpret_cast<float *>(y)[i] = v;
-}
-
-
-// Registers holding one prefetched step (one 32-code chunk of each of the
-// task's rows, with the matching scale and bias).
-template <int RT, int NS>
-struct StepBuf {
-  uint4 q[NS][RT];
-  uint32_t s[NS][RT];  // raw scale bits (bf16 zero-extended, or float32)
-  uint32_t b[NS][RT];  // raw bias bits; decoded when consumed, so that no
-                       // instruction waits on the load where it is issued
-  float w;  // EPI_MOE_DOWN: weight of the expert slot this lane's chunk belongs to
-};
 
 // Raw buffer resources: a load whose byte offset is >= the resource's
-// num_records returns zero without touching memory.  Steps past a wave's end
-// and rows past a matrix use such an offset, so every load is unconditional
-// (no branch, hence no register copy that would wait on it).
+// num_records returns zero without touching memory.
 constexpr uint32_t kOutOfRange = 0x80000000u;  // resources are < 2 GiB
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
@@ -335,131 +235,295 @@ __device__ __forceinline__ float sb_value(uint32_t bits) {
   return __uint_as_float(SBT == 1 ? (bits << 16) : bits);
 }
 
-// Persistent GEMV kernel.  Wave gw owns the contiguous task range
-// [gw * tpw, (gw + 1) * tpw); a task is rpt = RT * 64/LPR rows, each row
-// covered by LPR lanes.  The loads of the next D steps are always in flight
-// (a register ring of D * RT * NS 128-bit loads per lane), across task
-// boundaries, so a wave streams its rows continuously.  The first D loads are
-// issued before the activation is staged, overlapping that L2 traffic with
-// the first HBM round trip.  Task bookkeeping is incremental 32-bit scalar
-// arithmetic; matrix descriptors and buffer resources are refreshed only when
-// a wave crosses into the next matrix (or expert slot).
+// ---------------------------------------------------------------------------
+// Activation staging
+// ---------------------------------------------------------------------------
+// The activation (ncx chunks of 32 elements) goes to LDS plane-major, so that
+// lanes reading consecutive chunks hit consecutive 16 bytes:
+//   bf16: plane jj (0..3) of chunk c at uint4 index jj * ncx_pad + c
+//   f32 : plane pl (0..7) of chunk c at float4 index pl * ncx_pad + c
+// xsum[c] = sum of the chunk's 32 elements (float32, fixed order).  Chunks
+// ncx .. ncx_pad-1 are zero.
+//
+// Staging runs in rounds of xq<XM>() octets (8 elements) per thread: thread t
+// takes octets base + t, base + t + nthreads, ...  The last round is split in
+// two: stage_issue() starts its loads, stage_commit() permutes them into LDS,
+// and the code loads issued in between overlap the activation's round trip
+// (vmcnt drains in issue order, so the commit waits only for the older
+// activation loads).  Earlier rounds (very long rows only) complete before
+// any code load is issued, so every wait the compiler places after them
+// stays exact.
+template <int XM>
+constexpr int xq() { return XM == XM_BF16 ? 2 : 5; }
+template <int XM>
+constexpr uint32_t octet_bytes() { return XM == XM_BF16 ? 16u : 32u; }
+
+template <int XM>
+struct XRegs {
+  uint4 v[xq<XM>()][XM == XM_BF16 ? 1 : 2];
+};
+
+// Writes octet o (values in v) to the LDS planes and its chunk sum.  Must be
+// called by whole quads of lanes (the four octets of a chunk are in one quad).
+template <int XM>
+__device__ __forceinline__ void stage_store(int o, const uint4 *v, int ncx_pad, unsigned char *xbuf,
+                                            float *xsum) {
+  const int c = o >> 2, jj = o & 3;
+  float s;
+  if constexpr (XM == XM_BF16) {
+    const uint4 w = v[0];
+    uint4 pr;
+    pr.x = (w.x & 0xFFFFu) | (w.z << 16);
+    pr.y = (w.x >> 16) | (w.z & 0xFFFF0000u);
+    pr.z = (w.y & 0xFFFFu) | (w.w << 16);
+    pr.w = (w.y >> 16) | (w.w & 0xFFFF0000u);
+    reinterpret_cast<uint4 *>(xbuf)[jj * ncx_pad + c] = pr;
+    s = ((bf16_lo(w.x) + bf16_hi(w.x)) + (bf16_lo(w.y) + bf16_hi(w.y))) +
+        ((bf16_lo(w.z) + bf16_hi(w.z)) + (bf16_lo(w.w) + bf16_hi(w.w)));
+  } else {
+    const float4 a = __builtin_bit_cast(float4, v[0]);
+    const float4 b = __builtin_bit_cast(float4, v[1]);
+    reinterpret_cast<float4 *>(xbuf)[(2 * jj) * ncx_pad + c] = make_float4(a.x, a.z, b.x, b.z);
+    reinterpret_cast<float4 *>(xbuf)[(2 * jj + 1) * ncx_pad + c] = make_float4(a.y, a.w, b.y, b.w);
+    s = ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
+  }
+  s += dpp_mov<0xB1>(s);
+  s += dpp_mov<0x4E>(s);
+  if (jj == 0) xsum[c] = s;
+}
+
+template <int XM>
+__device__ __forceinline__ void stage_issue(const void *__restrict__ x, int ncx, int base,
+                                            XRegs<XM> &r) {
+  const uint32_t nocts = (uint32_t)ncx * 4;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, nocts * octet_bytes<XM>());
+#pragma unroll
+  for (int i = 0; i < xq<XM>(); ++i) {
+    // unconditional loads (a load inside a branch makes the compiler copy its
+    // result at the join, which waits for it right away); slots past the end
+    // are out of range
+    const uint32_t o = base + threadIdx.x + i * blockDim.x;
+    const uint32_t off = o < nocts ? o * octet_bytes<XM>() : kOutOfRange;
+    r.v[i][0] = buf_load_b128(rx, off);
+    if constexpr (XM == XM_F32) r.v[i][1] = buf_load_b128(rx, off + 16);
+  }
+}
+
+template <int XM>
+__device__ __forceinline__ void stage_commit(int ncx, int ncx_pad, int base, const XRegs<XM> &r,
+                                             unsigned char *xbuf, float *xsum) {
+  const int nocts = ncx * 4;
+#pragma unroll
+  for (int i = 0; i < xq<XM>(); ++i) {
+    const int o = base + threadIdx.x + i * blockDim.x;
+    if (o < nocts) stage_store<XM>(o, r.v[i], ncx_pad, xbuf, xsum);
+  }
+}
+
+// Octets per staging round, the number of rounds, and the first octet of the
+// last round.
+template <int XM>
+__device__ __forceinline__ int stage_last_base(int ncx) {
+  const int per_round = xq<XM>() * blockDim.x;
+  const int rounds = (ncx * 4 + per_round - 1) / per_round;
+  return (rounds - 1) * per_round;
+}
+
+// All staging rounds but the last, each loaded and stored before the next.
+template <int XM>
+__device__ __forceinline__ void stage_early_rounds(const void *__restrict__ x, int ncx, int ncx_pad,
+                                                   unsigned char *xbuf, float *xsum) {
+  const int last = stage_last_base<XM>(ncx);
+  for (int base = 0; base < last; base += xq<XM>() * blockDim.x) {
+    XRegs<XM> r;
+    stage_issue<XM>(x, ncx, base, r);
+    stage_commit<XM>(ncx, ncx_pad, base, r, xbuf, xsum);
+  }
+}
+
+// Zero chunks ncx .. ncx_pad-1 (whole quads: the padding is whole chunks).
+template <int XM>
+__device__ __forceinline__ void stage_padding(int ncx, int ncx_pad, unsigned char *xbuf, float *xsum) {
+  for (int o = ncx * 4 + threadIdx.x; o < ncx_pad * 4; o += blockDim.x) {
+    const uint4 z[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+    stage_store<XM>(o, z, ncx_pad, xbuf, xsum);
+  }
+}
+
+// The MoE residual row, staged as float32 in LDS (loads issued with the
+// activation's, before the first code loads; read back at task ends).  The
+// host guarantees RQ 16-byte vectors per thread cover it.
+constexpr int RQ = 4;
+
+// nvec: 16-byte vectors readable at res (0: no residual; every slot is out
+// of range)
+__device__ __forceinline__ void residual_issue(const void *res, uint32_t nvec, uint4 (&v)[RQ]) {
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(res, nvec * 16);
+#pragma unroll
+  for (int i = 0; i < RQ; ++i) {
+    const uint32_t o = threadIdx.x + i * blockDim.x;
+    v[i] = buf_load_b128(rr, o < nvec ? o * 16 : kOutOfRange);
+  }
+}
+
+__device__ __forceinline__ void residual_store(int o, const uint4 w, int bf16, float *dst) {
+  if (bf16) {
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      dst[8 * o + 2 * k] = bf16_lo(u[k]);
+      dst[8 * o + 2 * k + 1] = bf16_hi(u[k]);
+    }
+  } else {
+    reinterpret_cast<float4 *>(dst)[o] = __builtin_bit_cast(float4, w);
+  }
+}
+
+__device__ __forceinline__ void residual_commit(int n, int bf16, const uint4 (&v)[RQ], float *dst) {
+  const int nvec = bf16 ? n / 8 : n / 4;
+#pragma unroll
+  for (int i = 0; i < RQ; ++i) {
+    const int o = threadIdx.x + i * blockDim.x;
+    if (o < nvec) residual_store(o, v[i], bf16, dst);
+  }
+}
+
+__device__ __forceinline__ void store_out(void *y, int64_t i, float v, int bf16) {
+  if (bf16)
+    reinterpret_cast<__bf16 *>(y)[i] = (__bf16)v;
+  else
+    reinterpret_cast<float *>(y)[i] = v;
+}
+
+// Registers holding one prefetched step (one 32-code chunk of each of the
+// task's row groups, with the matching scale and bias).
+template <int RT, int NS>
+struct StepBuf {
+  uint4 q[NS][RT];
+  uint32_t s[NS][RT];  // raw scale bits (bf16 zero-extended, or float32)
+  uint32_t b[NS][RT];  // raw bias bits; decoded when consumed, so that no
+                       // instruction waits on the load where it is issued
+  float w;  // EPI_MOE_DOWN: weight of the expert slot this lane's chunk belongs to
+};
+
+// ---------------------------------------------------------------------------
+// The kernel
+// ---------------------------------------------------------------------------
+// Wave gw processes tasks gw, gw + n_waves, ... (tasks_q or tasks_q + 1 of
+// them).  A load cursor runs D steps ahead of the consume cursor through the
+// same (task, step) sequence; both are uniform (scalar) state.  Matrix
+// descriptors and buffer resources are refreshed only when the load cursor
+// crosses into another matrix (or expert slot).
 template <int RT, int XM, int SBT, int EPI>
-__global__ void __launch_bounds__(512) qgemv_kernel(const GemvParams p) {
+__global__ void __launch_bounds__(768) qgemv_kernel(const GemvParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   warm_kernargs<sizeof(GemvParams)>();
   constexpr int NS = (EPI == EPI_SWIGLU) ? 2 : 1;  // code streams per row (gate, up)
-  constexpr int D = 8 / (RT * NS);                 // steps in flight
+  constexpr int D = kSlots / (RT * NS);            // steps in flight
   constexpr int XB = (XM == XM_BF16) ? 64 : 128;   // staged bytes per chunk
-  constexpr int SBB = (SBT == 1) ? 2 : 4;          // bytes per scale/bias
+  constexpr uint32_t SBB = (SBT == 1) ? 2 : 4;     // bytes per scale/bias
 
   const int lane = threadIdx.x & 63;
-  const int W = blockDim.x >> 6;
   // wave index made provably uniform: all task bookkeeping stays scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n_waves = gridDim.x * W;
-  const int gw = blockIdx.x * W + wave;
+  const int gw = blockIdx.x * p.waves_per_wg + wave;
+  const int NW = p.n_waves;
   const int l2 = p.log2_lpr;
-  const int j = lane & ((1 << l2) - 1);
+  const int L = 1 << l2;
+  const int j = lane & (L - 1);
   const int sg = lane >> l2;
   const int rpi = 64 >> l2;  // rows per wave instruction
-  const int rpt = RT * rpi;  // rows per task
-  const int spt = p.steps_per_task;
-  const int ncx = p.n_chunks_x;
-  const uint32_t kwb = (uint32_t)p.chunks_per_row * 16;                   // code bytes per row
-  const uint32_t gpr = ((uint32_t)p.chunks_per_row * 32) >> p.log2_group;  // groups per row
-
-  const int tpw = (p.n_tasks + n_waves - 1) / n_waves;
-  const int t_begin = min(gw * tpw, p.n_tasks);
-  const int t_end = min(t_begin + tpw, p.n_tasks);
-  const int S = (t_end - t_begin) * spt;  // steps of this wave
+  const int rpt = p.rpt;     // rows per task (RT * rpi)
+  const int spt = p.spt;
+  const int ncx_pad = p.ncx_pad;
+  const uint32_t kwb = (uint32_t)p.kwb;
+  const uint32_t sbrow = (uint32_t)p.sbrow;
+  const int lg = p.log2_group;
+  const int S = (p.tasks_q + (gw < p.tasks_r ? 1 : 0)) * spt;  // steps of this wave
 
   float *xsum = reinterpret_cast<float *>(smem);
-  unsigned char *xbuf = smem + ((ncx * 4 + 15) & ~15);
-  float *res_lds = reinterpret_cast<float *>(xbuf + (size_t)ncx * XB);  // EPI_MOE_DOWN
+  unsigned char *xbuf = smem + ((ncx_pad * 4 + 15) & ~15);
+  float *res_lds = reinterpret_cast<float *>(xbuf + (size_t)ncx_pad * XB);  // EPI_MOE_DOWN
 
-  // expert ids and slot weights: lane k holds slot k's values
-  uint32_t v_ids = 0;
-  float v_wts = 0.f;
+  // expert ids and slot weights, through the scalar cache: lane k of v_ids /
+  // v_wts holds slot k's values
+  uint32_t v_ids = 0, v_wts = 0;
   if constexpr (EPI != EPI_STORE) {
-    if (p.ids && lane < p.top_k) v_ids = p.ids[lane];
-    if constexpr (EPI == EPI_MOE_DOWN) {
-      if (lane < p.top_k) v_wts = p.wts[lane];
+    if (p.ids) {
+      uint32_t s_ids[8];
+      scalar_load8(p.ids, p.top_k, s_ids);
+      v_ids = lanes_from_scalars(s_ids);
+      if constexpr (EPI == EPI_MOE_DOWN) {
+        uint32_t s_wts[8];
+        scalar_load8(reinterpret_cast<const uint32_t *>(p.wts), p.top_k, s_wts);
+        v_wts = lanes_from_scalars(s_wts);
+      }
     }
   }
   uint32_t magic = 0x43004300u;
   asm volatile("" : "+v"(magic));  // keep in a VGPR so AND-OR stays one VOP3
 
+  // per-lane constant parts of the load offsets
+  const uint32_t lo_c = (uint32_t)sg * kwb + (uint32_t)j * 16;
+  const uint32_t lo_s = (uint32_t)sg * sbrow + (((uint32_t)j * 32) >> lg) * SBB;
+  const uint32_t step_c = (uint32_t)L * 16;
+  const uint32_t step_s = (((uint32_t)L * 32) >> lg) * SBB;
+  const bool lane_in_last = j < p.last_lanes;  // lane holds a chunk in a row's last step
+
   // ---- cursors over (task, step) ----
+  // A cursor walks this wave's tasks t = gw, gw + NW, ...  Moving to the next
+  // task is an add and a compare against the first task of the next matrix
+  // (or expert slot); crossing it, which is rare, re-reads that matrix's
+  // descriptor.
   struct Cur {
-    int task, it;
-    int m, m_end;  // matrix (EPI_STORE) or expert slot (EPI_SWIGLU); first task past it
-    int row0;      // first row of the task inside its matrix
+    int t;       // task
+    int m;       // matrix (EPI_STORE) or expert slot (EPI_SWIGLU)
+    int bound;   // first task past matrix / slot m
+    int row0;    // first row of the task inside its matrix
     int n_rows;
-    bool live;     // EPI_SWIGLU: the slot's expert id is valid
-    const uint32_t *codes[NS];
-    const unsigned char *scl[NS];
-    const unsigned char *bia[NS];
-    void *y;
+    bool live;   // EPI_SWIGLU: the slot's expert id is valid
+    unsigned char *y;  // output of matrix / slot m
   };
-  auto enter = [&](Cur &c, int m) {  // geometry of matrix / slot m
-    c.m = m;
-    c.live = true;
+  const int row_step = NW * rpt;  // rows between a wave's consecutive tasks
+  auto seek = [&](Cur &c) {  // matrix / slot of task c.t, its geometry and row0
+    int m = c.m;
     if constexpr (EPI == EPI_STORE) {
-      c.codes[0] = p.m[m].codes;
-      c.scl[0] = reinterpret_cast<const unsigned char *>(p.m[m].scales);
-      c.bia[0] = reinterpret_cast<const unsigned char *>(p.m[m].biases);
+      while (m + 1 < p.n_mats && c.t >= p.task0[m + 1]) ++m;
+      c.bound = (m + 1 < p.n_mats) ? p.task0[m + 1] : p.n_tasks;
       c.n_rows = (int)p.m[m].n_out;
-      c.y = p.m[m].y;
-      c.m_end = (m + 1 < p.n_mats) ? p.task0[m + 1] : p.n_tasks;
-      c.row0 = (c.task - p.task0[m]) * rpt;
+      c.row0 = (c.t - p.task0[m]) * rpt;
+      c.y = reinterpret_cast<unsigned char *>(p.m[m].y);
     } else if constexpr (EPI == EPI_SWIGLU) {
-      const uint32_t e = (uint32_t)__builtin_amdgcn_readlane((int)v_ids, m);
+      m = min(c.t / p.tasks_per_slot, p.top_k - 1);
+      c.bound = (m + 1 < p.top_k) ? (m + 1) * p.tasks_per_slot : p.n_tasks;
+      const uint32_t e = p.ids ? (uint32_t)__builtin_amdgcn_readlane((int)v_ids, m) : 0u;
       c.live = e < (uint32_t)p.n_experts;
-      const int64_t eo = c.live ? (int64_t)e : 0;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        c.codes[s] = p.m[s].codes + eo * p.expert_code_stride;
-        c.scl[s] = reinterpret_cast<const unsigned char *>(p.m[s].scales) + eo * p.expert_sb_stride * SBB;
-        c.bia[s] = reinterpret_cast<const unsigned char *>(p.m[s].biases) + eo * p.expert_sb_stride * SBB;
-      }
       c.n_rows = (int)p.m[0].n_out;
+      c.row0 = (c.t - m * p.tasks_per_slot) * rpt;
       c.y = reinterpret_cast<unsigned char *>(p.m[0].y) + (int64_t)m * c.n_rows * (p.y_bf16 ? 2 : 4);
-      c.m_end = (m + 1) * p.tasks_per_slot;
-      c.row0 = (c.task - m * p.tasks_per_slot) * rpt;
     } else {
-      c.codes[0] = p.m[0].codes;
-      c.scl[0] = reinterpret_cast<const unsigned char *>(p.m[0].scales);
-      c.bia[0] = reinterpret_cast<const unsigned char *>(p.m[0].biases);
+      c.bound = p.n_tasks;
       c.n_rows = (int)p.m[0].n_out;
-      c.y = p.m[0].y;
-      c.m_end = p.n_tasks;
-      c.row0 = c.task * rpt;
+      c.row0 = c.t * rpt;
+      c.y = reinterpret_cast<unsigned char *>(p.m[0].y);
     }
+    c.m = m;
   };
   auto start = [&](Cur &c) {
-    c.task = t_begin;
-    c.it = 0;
-    int m = 0;
-    if constexpr (EPI == EPI_STORE) {
-      for (int i = 1; i < p.n_mats; ++i)
-        if (t_begin >= p.task0[i]) m = i;
-    } else if constexpr (EPI == EPI_SWIGLU) {
-      m = min(t_begin / p.tasks_per_slot, p.top_k - 1);
-    }
-    enter(c, m);
+    c.t = gw;
+    c.m = 0;
+    c.live = true;
+    seek(c);
   };
-  // next step; returns true when the cursor moved into another matrix / slot
-  auto advance = [&](Cur &c) {
-    if (++c.it < spt) return false;
-    c.it = 0;
-    ++c.task;
-    c.row0 += rpt;
-    if (c.task >= c.m_end && c.task < t_end) {
-      enter(c, c.m + 1);
-      return true;
+  // next task; true when the cursor moved into another matrix / slot
+  auto next_task = [&](Cur &c) {
+    c.t += NW;
+    if (c.t < c.bound) {
+      c.row0 += row_step;
+      return false;
     }
-    return false;
+    if (c.t < p.n_tasks) seek(c);
+    return true;
   };
 
   // ---- load stream ----
@@ -467,59 +531,87 @@ __global__ void __launch_bounds__(512) qgemv_kernel(const GemvParams p) {
   start(lc);
   __amdgpu_buffer_rsrc_t rc[NS], rs[NS], rb[NS];
   auto set_rsrc = [&]() {
+    if constexpr (EPI == EPI_STORE) {
+      const GemvMat &d = p.m[lc.m];
+      rc[0] = make_rsrc(d.codes, (uint32_t)lc.n_rows * kwb);
+      rs[0] = make_rsrc(d.scales, (uint32_t)lc.n_rows * sbrow);
+      rb[0] = make_rsrc(d.biases, (uint32_t)lc.n_rows * sbrow);
+    } else if constexpr (EPI == EPI_SWIGLU) {
+      // a skipped slot (invalid id) reads nothing: zero-size resources
+      const uint32_t e = p.ids ? (uint32_t)__builtin_amdgcn_readlane((int)v_ids, lc.m) : 0u;
+      const uint32_t ee = lc.live ? e : 0u;
+      const uint32_t cb = lc.live ? (uint32_t)lc.n_rows * kwb : 0u;
+      const uint32_t sb = lc.live ? (uint32_t)lc.n_rows * sbrow : 0u;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const uint32_t cb = (EPI == EPI_MOE_DOWN) ? (uint32_t)p.code_bytes : (uint32_t)lc.n_rows * kwb;
-      const uint32_t sbb = (EPI == EPI_MOE_DOWN) ? (uint32_t)p.sb_bytes : (uint32_t)lc.n_rows * gpr * SBB;
-      rc[s] = make_rsrc(lc.codes[s], cb);
-      rs[s] = make_rsrc(lc.scl[s], sbb);
-      rb[s] = make_rsrc(lc.bia[s], sbb);
+      for (int s = 0; s < NS; ++s) {
+        rc[s] = make_rsrc(reinterpret_cast<const unsigned char *>(p.m[s].codes) + (uint64_t)ee * p.ecode_bytes, cb);
+        rs[s] = make_rsrc(reinterpret_cast<const unsigned char *>(p.m[s].scales) + (uint64_t)ee * p.esb_bytes, sb);
+        rb[s] = make_rsrc(reinterpret_cast<const unsigned char *>(p.m[s].biases) + (uint64_t)ee * p.esb_bytes, sb);
+      }
+    } else {
+      rc[0] = make_rsrc(p.m[0].codes, p.code_bytes);
+      rs[0] = make_rsrc(p.m[0].scales, p.sb_bytes);
+      rb[0] = make_rsrc(p.m[0].biases, p.sb_bytes);
     }
   };
   set_rsrc();
+  int lstep = 0;   // steps issued by the load cursor
+  int lit = 0;     // step inside the task
+  uint32_t lstep_c = 0, lstep_s = 0;  // byte offsets of step lit inside a row
   auto load = [&](StepBuf<RT, NS> &bf) {
-    const bool ok = lc.task < t_end;  // past the wave's last step: out of range
-    int c = j + (lc.it << l2);        // chunk of the (virtual) row
-    uint32_t ecode = 0, esb = 0;
+    // past the wave's last step: out of range (the load is still issued, so
+    // the number of loads in flight, and with it every wait, is static)
+    const bool past = lstep++ >= S;
+    uint32_t oc, os;
     if constexpr (EPI == EPI_MOE_DOWN) {
       // virtual row = the kept experts' rows back to back; this lane's slot
-      const int slot = (int)(((float)c + 0.5f) * p.inv_chunks_per_row);
-      c -= slot * p.chunks_per_row;
-      uint32_t e = (uint32_t)__shfl((int)v_ids, slot);
-      float w = __shfl(v_wts, slot);
-      if (e >= (uint32_t)p.n_experts) {  // skipped slot: read expert 0, weight 0
-        e = 0;
-        w = 0.f;
-      }
-      bf.w = w;
-      ecode = e * (uint32_t)(p.expert_code_stride * 4);
-      esb = e * (uint32_t)(p.expert_sb_stride * SBB);
+      const int c = j + lit * L;
+      const int slot = (int)(((float)c + 0.5f) * p.inv_cpr_e);
+      const int cl = c - slot * p.cpr_e;
+      const uint32_t e = (uint32_t)__shfl((int)v_ids, slot);
+      const float w = __uint_as_float((uint32_t)__shfl((int)v_wts, slot));
+      const bool ok = slot < p.top_k && e < (uint32_t)p.n_experts;  // else: skipped, weight 0
+      bf.w = ok ? w : 0.f;
+      const uint32_t rowc = (uint32_t)(lc.row0 + sg) * kwb, rows = (uint32_t)(lc.row0 + sg) * sbrow;
+      oc = ok && !past ? e * p.ecode_bytes + rowc + (uint32_t)cl * 16 : kOutOfRange;
+      os = ok && !past ? e * p.esb_bytes + rows + (((uint32_t)cl * 32) >> lg) * SBB : kOutOfRange;
+    } else {
+      // partial last step: lanes past the row's chunks have nothing to load
+      const bool off = past || (lit == spt - 1 && !lane_in_last);
+      oc = off ? kOutOfRange : lo_c + ((uint32_t)lc.row0 * kwb + lstep_c);
+      os = off ? kOutOfRange : lo_s + ((uint32_t)lc.row0 * sbrow + lstep_s);
     }
-    const uint32_t g = ((uint32_t)c * 32) >> p.log2_group;
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
-      const int row = lc.row0 + r * rpi + sg;
-      const bool okr = ok && row < lc.n_rows;
-      const uint32_t oc = okr ? ecode + (uint32_t)row * kwb + (uint32_t)c * 16 : kOutOfRange;
-      const uint32_t os = okr ? esb + ((uint32_t)row * gpr + g) * SBB : kOutOfRange;
+      // rows past the matrix (or stack) end fall outside the resource: zeros
+      const uint32_t rc_off = (uint32_t)(r * rpi) * kwb;
+      const uint32_t rs_off = (uint32_t)(r * rpi) * sbrow;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        bf.q[s][r] = buf_load_b128(rc[s], oc);
-        bf.s[s][r] = buf_load_sb<SBT>(rs[s], os);
-        bf.b[s][r] = buf_load_sb<SBT>(rb[s], os);
+        bf.q[s][r] = buf_load_b128(rc[s], oc + rc_off);
+        bf.s[s][r] = buf_load_sb<SBT>(rs[s], os + rs_off);
+        bf.b[s][r] = buf_load_sb<SBT>(rb[s], os + rs_off);
       }
     }
-    if (ok && advance(lc)) set_rsrc();
+    // advance the load cursor
+    lstep_c += step_c;
+    lstep_s += step_s;
+    if (++lit == spt) {
+      lit = 0;
+      lstep_c = 0;
+      lstep_s = 0;
+      if (next_task(lc) && lc.t < p.n_tasks) set_rsrc();
+    }
   };
 
+  stage_early_rounds<XM>(p.x, p.ncx, ncx_pad, xbuf, xsum);
+  const int xbase = stage_last_base<XM>(p.ncx);
   XRegs<XM> xr;
-  stage_issue<XM>(p.x, ncx, xr);  // activation loads first (L2), ...
+  stage_issue<XM>(p.x, p.ncx, xbase, xr);  // activation loads first (L2), ...
   uint4 rr[RQ];
   const bool has_res = (EPI == EPI_MOE_DOWN) && p.residual != nullptr;
   if constexpr (EPI == EPI_MOE_DOWN) {
-    // without a residual, harmless clamped loads of the activation's first
-    // 16 bytes keep the issue unconditional
-    const int nvec = has_res ? (int)(p.y_bf16 ? p.m[0].n_out / 8 : p.m[0].n_out / 4) : 1;
+    const uint32_t nvec = has_res ? (uint32_t)(p.y_bf16 ? p.m[0].n_out / 8 : p.m[0].n_out / 4) : 0u;
     residual_issue(has_res ? p.residual : p.x, nvec, rr);
   }
 
@@ -528,8 +620,9 @@ __global__ void __launch_bounds__(512) qgemv_kernel(const GemvParams p) {
 #pragma unroll
   for (int u = 0; u < D; ++u) load(buf[u]);
 
-  stage_commit<XM>(p.x, ncx, xr, xbuf, xsum);
-  if (has_res) residual_commit(p.residual, (int)p.m[0].n_out, p.y_bf16, rr, res_lds);
+  stage_commit<XM>(p.ncx, ncx_pad, xbase, xr, xbuf, xsum);
+  stage_padding<XM>(p.ncx, ncx_pad, xbuf, xsum);
+  if (has_res) residual_commit((int)p.m[0].n_out, p.y_bf16, rr, res_lds);
   lds_barrier();
 
   // ---- consume stream ----
@@ -540,6 +633,7 @@ __global__ void __launch_bounds__(512) qgemv_kernel(const GemvParams p) {
     for (int r = 0; r < RT; ++r) acc[s][r] = 0.f;
   Cur cc;
   start(cc);
+  int cit = 0;  // step inside the task
 
   auto finish = [&]() {
 #pragma unroll
@@ -571,12 +665,12 @@ __global__ void __launch_bounds__(512) qgemv_kernel(const GemvParams p) {
   };
 
   auto consume = [&](const StepBuf<RT, NS> &bf) {
-    const int xc = j + (cc.it << l2);  // staged chunk (virtual row chunk)
+    const int xc = j + cit * L;  // staged chunk (virtual row chunk); < ncx_pad
     const float xs = xsum[xc];
     if constexpr (XM == XM_BF16) {
       uint4 xv[4];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) xv[jj] = reinterpret_cast<const uint4 *>(xbuf)[jj * ncx + xc];
+      for (int jj = 0; jj < 4; ++jj) xv[jj] = reinterpret_cast<const uint4 *>(xbuf)[jj * ncx_pad + xc];
       const float d0 = -128.f * xs;
 #pragma unroll
       for (int s = 0; s < NS; ++s)
@@ -592,7 +686,7 @@ __global__ void __launch_bounds__(512) qgemv_kernel(const GemvParams p) {
     } else {
       float4 xv[8];
 #pragma unroll
-      for (int pl = 0; pl < 8; ++pl) xv[pl] = reinterpret_cast<const float4 *>(xbuf)[pl * ncx + xc];
+      for (int pl = 0; pl < 8; ++pl) xv[pl] = reinterpret_cast<const float4 *>(xbuf)[pl * ncx_pad + xc];
 #pragma unroll
       for (int s = 0; s < NS; ++s)
 #pragma unroll
@@ -605,22 +699,20 @@ __global__ void __launch_bounds__(512) qgemv_kernel(const GemvParams p) {
             acc[s][r] += part;
         }
     }
-    if (cc.it == spt - 1) finish();
-    advance(cc);
+    if (++cit == spt) {
+      finish();
+      cit = 0;
+      next_task(cc);
+    }
   };
 
   for (int s0 = 0; s0 < S; s0 += D) {
 #pragma unroll
     for (int u = 0; u < D; ++u) {
       if (s0 + u < S) consume(buf[u]);
-      load(buf[u]);  // past the wave's last step: out of range, returns zeros
+      load(buf[u]);
     }
   }
-}
-
-template <int RT, int XM, int SBT, int EPI>
-const void *kernel_ptr() {
-  return reinterpret_cast<const void *>(qgemv_kernel<RT, XM, SBT, EPI>);
 }
 
 template <int RT, int XM, int SBT, int EPI>
@@ -643,13 +735,6 @@ hipError_t launch_one(const GemvParams &p, const GemvPlan &plan, hipStream_t str
 // Kernel selection: (rt, xmode, sb_bf16, epi) -> instantiation.  MoE down
 // always stages a float32 activation (the SwiGLU intermediates).
 template <int RT, int EPI>
-const void *select_ptr(int xmode, int sb_bf16) {
-  if (EPI == EPI_MOE_DOWN || xmode == XM_F32)
-    return sb_bf16 ? kernel_ptr<RT, XM_F32, 1, EPI>() : kernel_ptr<RT, XM_F32, 0, EPI>();
-  return sb_bf16 ? kernel_ptr<RT, XM_BF16, 1, EPI>() : kernel_ptr<RT, XM_BF16, 0, EPI>();
-}
-
-template <int RT, int EPI>
 hipError_t launch_sel(const GemvParams &p, const GemvPlan &plan, int xmode, int sb_bf16,
                       hipStream_t s) {
   if (EPI == EPI_MOE_DOWN || xmode == XM_F32)
@@ -659,26 +744,10 @@ hipError_t launch_sel(const GemvParams &p, const GemvPlan &plan, int xmode, int 
 
 }  // namespace
 
-size_t gemv_lds_bytes(int xmode, int n_chunks_x, int64_t residual_rows) {
+size_t gemv_lds_bytes(int xmode, int ncx_pad, int64_t residual_rows) {
   const size_t xb = (xmode == XM_BF16) ? 64 : 128;
-  return (((size_t)n_chunks_x * 4 + 15) & ~(size_t)15) + (size_t)n_chunks_x * xb +
+  return (((size_t)ncx_pad * 4 + 15) & ~(size_t)15) + (size_t)ncx_pad * xb +
          (size_t)residual_rows * 4;
-}
-
-int gemv_blocks_per_cu(const GemvPlan &plan, int xmode, int sb_bf16, int epi) {
-  const void *k = nullptr;
-  switch (epi) {
-    case EPI_STORE: k = plan.rt == 2 ? select_ptr<2, EPI_STORE>(xmode, sb_bf16) : select_ptr<1, EPI_STORE>(xmode, sb_bf16); break;
-    case EPI_SWIGLU: k = plan.rt == 2 ? select_ptr<2, EPI_SWIGLU>(xmode, sb_bf16) : select_ptr<1, EPI_SWIGLU>(xmode, sb_bf16); break;
-    case EPI_MOE_DOWN: k = plan.rt == 2 ? select_ptr<2, EPI_MOE_DOWN>(xmode, sb_bf16) : select_ptr<1, EPI_MOE_DOWN>(xmode, sb_bf16); break;
-    default: return 0;
-  }
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, plan.waves * 64, plan.lds_bytes) != hipSuccess) {
-    (void)hipGetLastError();
-    return 0;
-  }
-  return n;
 }
 
 hipError_t launch_gemv(const GemvParams &p, const GemvPlan &plan, int xmode, int sb_bf16, int epi,
