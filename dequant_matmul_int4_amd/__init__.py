@@ -14,6 +14,7 @@ The names and arguments mirror the C entry points:
 * :func:`moe_gather_qgemv_int4`      -- top-K expert gather + SwiGLU + down +
                                         weighted 8-way combine + residual
 * :func:`qgemm_int4_padT`            -- prefill GEMM with virtual T padding, bf16 MFMA
+* :func:`moe_router_topk`            -- softmax top-K expert routing on the device
 """
 from __future__ import annotations
 
@@ -71,6 +72,7 @@ SIGNATURES = [
                                      ctypes.POINTER(CMatrix), _P, _P, _P, _I32, _P, _P, _I32,
                                      _P, ctypes.c_size_t, _P]),
     ("qgemm_int4_padT", _I32, [ctypes.POINTER(CMatrix), _P, _I64, _I64, _P, _I64, _I32, _P]),
+    ("moe_router_topk", _I32, [_P, _I32, _I64, _I32, _I32, _P, _P, _P]),
     ("qint4_status_string", ctypes.c_char_p, [_I32]),
     ("qint4_last_error", ctypes.c_char_p, []),
     ("qint4_abi_version", _I32, []),
@@ -229,6 +231,27 @@ def qgemm_int4_padT(w: QInt4Matrix, x: torch.Tensor, y: torch.Tensor, stream=Non
                                   y.data_ptr(), y.stride(0), _dt(y), _stream(stream)))
 
 
+def moe_router_topk(logits: torch.Tensor, top_k: int, ids: torch.Tensor, wts: torch.Tensor,
+                    stream=None) -> None:
+    """ids[t], wts[t] = top-K experts of softmax(logits[t]) and their renormalised weights.
+
+    logits: float32/bfloat16 [n_experts] or [n_tokens][n_experts]; ids: int32/uint32 and
+    wts: float32, each [top_k] or [n_tokens][top_k] (all on the device).
+    """
+    if ids.dtype not in (torch.int32, torch.uint32):
+        raise TypeError("ids must be int32/uint32")
+    if wts.dtype != torch.float32:
+        raise TypeError("wts must be float32")
+    n_experts = logits.shape[-1]
+    n_tokens = logits.numel() // max(n_experts, 1)
+    if ids.numel() != n_tokens * top_k or wts.numel() != n_tokens * top_k:
+        raise ValueError("ids and wts must hold n_tokens * top_k elements")
+    _check(load().moe_router_topk(_dev(logits, "logits"), _dt(logits), n_tokens, n_experts,
+                                  int(top_k), _dev(ids, "ids"), _dev(wts, "wts"),
+                                  _stream(stream)))
+
+
 __all__ = ["QInt4Matrix", "Int4Error", "qgemv_int4", "qgemv_int4_multi",
            "moe_gather_qgemv_int4", "moe_gather_qgemv_int4_workspace_bytes", "qgemm_int4_padT",
+           "moe_router_topk",
            "load", "F32", "BF16", "EPI_NONE", "EPI_SWIGLU_PAIR", "LIB_PATH", "SIGNATURES"]

@@ -532,6 +532,36 @@ qint4_status moe_gather_qgemv_int4(const qint4_matrix *gate, const qint4_matrix 
   return ok();
 }
 
+qint4_status moe_router_topk(const void *logits, int32_t logits_dtype, int64_t n_tokens,
+                             int32_t n_experts, int32_t top_k, uint32_t *ids, float *wts,
+                             void *stream) {
+  const char *fn = "moe_router_topk";
+  if (!logits || !ids || !wts) return fail(QINT4_ERR_NULL, "%s: logits/ids/wts is NULL", fn);
+  if (!valid_dtype(logits_dtype))
+    return fail(QINT4_ERR_DTYPE, "%s: logits_dtype %d invalid", fn, logits_dtype);
+  if (top_k < 1 || top_k > QINT4_TOPK_MAX)
+    return fail(QINT4_ERR_SHAPE, "%s: top_k %d not in [1, %d]", fn, top_k, QINT4_TOPK_MAX);
+  if (n_experts < top_k || n_experts > kRouterMaxExperts)
+    return fail(QINT4_ERR_SHAPE, "%s: n_experts %d not in [top_k = %d, %d]", fn, n_experts, top_k,
+                kRouterMaxExperts);
+  if (n_tokens < 1 || n_tokens > ((int64_t)1 << 31))
+    return fail(QINT4_ERR_SHAPE, "%s: n_tokens %lld invalid", fn, (long long)n_tokens);
+  const size_t lb = elem_bytes(logits_dtype);
+  if (!aligned(logits, lb) || !aligned(ids, 4) || !aligned(wts, 4))
+    return fail(QINT4_ERR_ALIGN, "%s: logits/ids/wts not aligned to their element size", fn);
+  Range ins[1], outs[2];
+  ins[0] = range(logits, (size_t)n_tokens * n_experts * lb, "logits");
+  outs[0] = range(ids, (size_t)n_tokens * top_k * 4, "ids");
+  outs[1] = range(wts, (size_t)n_tokens * top_k * 4, "wts");
+  qint4_status st = check_no_overlap(outs, 2, ins, 1);
+  if (st != QINT4_OK) return prefixed(st, fn);
+  if ((st = check_device(nullptr)) != QINT4_OK) return prefixed(st, fn);
+  hipError_t e = launch_router(logits, logits_dtype == QINT4_BF16, n_tokens, n_experts, top_k, ids,
+                               wts, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(QINT4_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
 qint4_status qgemm_int4_padT(const qint4_matrix *w, const void *x, int64_t T, int64_t ldx, void *y,
                              int64_t ldy, int32_t y_dtype, void *stream) {
   const char *fn = "qgemm_int4_padT";

@@ -208,6 +208,35 @@ qint4_status moe_gather_qgemv_int4(const qint4_matrix *gate, const qint4_matrix 
 qint4_status qgemm_int4_padT(const qint4_matrix *w, const void *x, int64_t T, int64_t ldx,
                              void *y, int64_t ldy, int32_t y_dtype, void *stream);
 
+/*
+ * moe_router_topk -- top-K expert routing of n_tokens rows of router logits,
+ * on the device, producing the ids / wts that moe_gather_qgemv_int4 reads.
+ *
+ * [FFAI #14], GPU MoE router commit: a row of logits [n_experts] becomes
+ * [k] u32 expert indices plus [k] weights, a batched form handles one row
+ * per token in one dispatch, and the index buffer is threaded straight into
+ * the expert-indexed GEMV with no host readback.  [FFAI #9], top-K
+ * partial-sort commit: selection order (value desc, index asc).
+ *
+ * Per row: p = softmax(logits); the top_k largest p are kept, equal values
+ * going to the smaller expert index; ids[k] are their expert indices in that
+ * order and wts[k] = p_k / (sum of the kept p), i.e. a softmax over the kept
+ * logits, computed in float32.  NaN logits rank below every number; a row
+ * whose kept logits are all -inf gets weights 1/top_k.
+ *
+ *   logits    device [n_tokens][n_experts], dtype logits_dtype (QINT4_F32 or
+ *             QINT4_BF16), element-aligned
+ *   n_tokens  >= 1
+ *   n_experts top_k..4096
+ *   top_k     1..QINT4_TOPK_MAX
+ *   ids       device uint32 [n_tokens][top_k], fully overwritten
+ *   wts       device float32 [n_tokens][top_k], fully overwritten
+ * One kernel launch on `stream`.
+ */
+qint4_status moe_router_topk(const void *logits, int32_t logits_dtype, int64_t n_tokens,
+                             int32_t n_experts, int32_t top_k, uint32_t *ids, float *wts,
+                             void *stream);
+
 /* Static description of a status code. */
 const char *qint4_status_string(int32_t status);
 

@@ -135,6 +135,25 @@ def test_gemm_validation(lib):
     assert _gemm(lib, _m(), y=A + 0x300000 + 128) == 5
 
 
+def _router(lib, logits=A + 0x300000, dt=0, n_tokens=1, n_experts=128, top_k=8, ids=A + 0x400000,
+            wts=A + 0x410000):
+    return lib.moe_router_topk(logits, dt, n_tokens, n_experts, top_k, ids, wts, None)
+
+
+def test_router_validation(lib):
+    assert _router(lib, logits=0) == 1
+    assert _router(lib, ids=0) == 1
+    assert _router(lib, dt=5) == 3
+    assert _router(lib, top_k=0) == 2
+    assert _router(lib, top_k=9) == 2
+    assert _router(lib, n_experts=4, top_k=8) == 2 and "n_experts" in _err(lib)
+    assert _router(lib, n_experts=4097) == 2
+    assert _router(lib, n_tokens=0) == 2
+    assert _router(lib, logits=A + 0x300002) == 4          # float32 logits misaligned
+    assert _router(lib, ids=A + 0x300000 + 64) == 5        # ids overlap logits
+    assert _router(lib, wts=A + 0x400000 + 8) == 5         # wts overlap ids
+
+
 def test_valid_call_without_device_reports_device_error(lib):
     import torch
 
