@@ -16,7 +16,8 @@ Workloads (default: qkv):
   single   1024x1024 g64 GEMV, fp32 scales/biases, fp32 x and y
   qkv      q/k/v projections of one bf16 4096-vector (4096/1024/1024 rows), one launch
   dense    gate/up 5120->17408 with SwiGLU (fp32 h), then down 17408->5120
-  moe      top-8 of 128 experts, hidden 2048, inter 768, weighted combine + residual
+  moe      top-8 of 128 experts, hidden 2048, inter 768, weighted combine + residual;
+           each step routes its token's logits on the GPU first (--router pre-drawn: skip)
   prefill  K=5120, N=17408 dequant GEMM on bf16 MFMA (--T rows, default 256)
 
 Prints one JSON line.  ``value`` is weight GB/s for the decode workloads and
@@ -52,6 +53,8 @@ def parse():
     ap.add_argument("--T", type=int, default=256, help="prefill rows")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-time budget of the CPU oracle sample (0 disables)")
+    ap.add_argument("--router", choices=("gpu", "pre-drawn"), default="gpu",
+                    help="moe: route each token on the GPU (default) or use pre-drawn ids/weights")
     ap.add_argument("--layers", type=int, default=64,
                     help="dense layers per token assumed for tokens/s-equivalent")
     return ap.parse_args()
@@ -177,11 +180,15 @@ class Dense(Workload):
 
 class MoE(Workload):
     name = "moe_top8_t1"
-    launches_per_step = 2
-    dominant = "qgemv_kernel EPI_SWIGLU (expert gate/up) + EPI_MOE_DOWN"
+    launches_per_step = 3
+    dominant = "router_topk + qgemv_kernel EPI_SWIGLU (expert gate/up) + EPI_MOE_DOWN"
 
-    def __init__(self, q, synth, torch):
+    def __init__(self, q, synth, torch, gpu_router=True):
         self.q = q
+        self.gpu_router = gpu_router
+        if not gpu_router:
+            self.launches_per_step = 2
+            self.dominant = "qgemv_kernel EPI_SWIGLU (expert gate/up) + EPI_MOE_DOWN"
         E, H, I, K = 128, 2048, 768, 8
         stacks = []
         r = 0
@@ -197,10 +204,13 @@ class MoE(Workload):
         gen = torch.Generator(device="cuda")
         gen.manual_seed(3)
         logits = torch.randn(1024, E, device="cuda", generator=gen)
+        self.logits = logits.contiguous()
         p = torch.softmax(logits, dim=-1)
         top = torch.topk(p, K, dim=-1)
         self.ids = top.indices.to(torch.int32).contiguous()
         self.wts = (top.values / top.values.sum(-1, keepdim=True)).float().contiguous()
+        self.ids_buf = torch.empty(K, dtype=torch.int32, device="cuda")
+        self.wts_buf = torch.empty(K, dtype=torch.float32, device="cuda")
         self.x = torch.randn(H, device="cuda").to(torch.bfloat16)
         self.res = torch.randn(H, device="cuda").to(torch.bfloat16)
         self.out = torch.empty(H, device="cuda", dtype=torch.bfloat16)
@@ -210,7 +220,8 @@ class MoE(Workload):
         self.wb = 3 * K * per_expert            # gate + up + down of the 8 kept experts
         self.config = {"workload": self.name, "n_experts": E, "top_k": K, "hidden": H, "inter": I,
                        "group_size": 64, "sb_dtype": "bf16", "x_dtype": "bf16",
-                       "router_draws": 1024, "pool_copies": self.R}
+                       "router_draws": 1024, "router": "gpu" if gpu_router else "pre-drawn",
+                       "pool_copies": self.R}
         self.dtype = "bf16"
 
     def weight_bytes(self):
@@ -222,7 +233,12 @@ class MoE(Workload):
     def step(self, i):
         g, u, d = self.pool[i % self.R]
         j = i % self.ids.shape[0]
-        self.q.moe_gather_qgemv_int4(g, u, d, self.x, self.ids[j], self.wts[j], self.out, self.ws,
+        if self.gpu_router:  # route this token's logits on the device, then gather
+            self.q.moe_router_topk(self.logits[j], 8, self.ids_buf, self.wts_buf)
+            ids, wts = self.ids_buf, self.wts_buf
+        else:
+            ids, wts = self.ids[j], self.wts[j]
+        self.q.moe_gather_qgemv_int4(g, u, d, self.x, ids, wts, self.out, self.ws,
                                      residual=self.res)
 
 
@@ -284,12 +300,14 @@ def cpu_baseline(workload: str, budget_s: float, T: int):
         sample = "full dense layer (seed 2), repeated"
     elif workload == "moe":
         d = synth.moe_layer()
-        ids, wts = oracle.router_topk(d["logits"][0], 8)
         per = d["gate"].weight_bytes // d["gate"].n_experts
         wb = 3 * 8 * per
-        fn = lambda: oracle.moe(d["gate"], d["up"], d["down"], d["x"][0], ids, wts.astype(np.float32),
-                                d["residual"][0], "bf16", threads=threads)
-        sample = "one top-8 token of the 128-expert layer (seed 3), repeated"
+
+        def fn():
+            ids, wts = oracle.router_topk(d["logits"][0], 8)
+            return oracle.moe(d["gate"], d["up"], d["down"], d["x"][0], ids, wts.astype(np.float32),
+                              d["residual"][0], "bf16", threads=threads)
+        sample = "one token of the 128-expert layer (seed 3): router + top-8 experts, repeated"
     else:
         d = synth.prefill_gemm(T=T)
         rows = 64
@@ -348,7 +366,7 @@ def main():
     elif args.workload == "dense":
         wl = Dense(q, synth, torch)
     elif args.workload == "moe":
-        wl = MoE(q, synth, torch)
+        wl = MoE(q, synth, torch, gpu_router=args.router == "gpu")
     else:
         wl = Prefill(q, synth, torch, args.T)
     torch.cuda.synchronize()

@@ -106,7 +106,7 @@ struct GemmParams {
 hipError_t launch_gemm(const GemmParams &p, hipStream_t stream);
 
 // Top-k expert routing of n_rows rows of router logits (float32 or bf16):
-// ids/wts are [n_rows][top_k].  LDS: 4 rows x n_experts floats per workgroup.
+// ids/wts are [n_rows][top_k].
 constexpr int kRouterMaxExperts = 4096;
 hipError_t launch_router(const void *logits, int bf16, int64_t n_rows, int n_experts, int top_k,
                          uint32_t *ids, float *wts, hipStream_t stream);
