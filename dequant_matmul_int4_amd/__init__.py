@@ -11,6 +11,7 @@ The names and arguments mirror the C entry points:
 * :func:`qgemv_int4`                 -- y = W x (T = 1)
 * :func:`qgemv_int4_multi`           -- several projections of one input, one launch;
                                         optional SwiGLU pairing (gate, up -> h)
+* :func:`qgemv_int4_smallm`          -- the same for T = 1..8 activation rows at once
 * :func:`moe_gather_qgemv_int4`      -- top-K expert gather + SwiGLU + down +
                                         weighted 8-way combine + residual
 * :func:`qgemm_int4_padT`            -- prefill GEMM with virtual T padding, bf16 MFMA
@@ -67,6 +68,8 @@ SIGNATURES = [
     ("qgemv_int4", _I32, [ctypes.POINTER(CMatrix), _P, _I32, _P, _I32, _P]),
     ("qgemv_int4_multi", _I32, [_I32, ctypes.POINTER(CMatrix), _P, _I32,
                                 ctypes.POINTER(ctypes.c_void_p), _I32, _I32, _P]),
+    ("qgemv_int4_smallm", _I32, [_I32, ctypes.POINTER(CMatrix), _P, _I32, _I64, _I64,
+                                 ctypes.POINTER(ctypes.c_void_p), _I32, _I32, _P]),
     ("moe_gather_qgemv_int4_workspace_bytes", ctypes.c_size_t, [_I64, _I32]),
     ("moe_gather_qgemv_int4", _I32, [ctypes.POINTER(CMatrix), ctypes.POINTER(CMatrix),
                                      ctypes.POINTER(CMatrix), _P, _P, _P, _I32, _P, _P, _I32,
@@ -183,6 +186,33 @@ def qgemv_int4_multi(ws: Sequence[QInt4Matrix], x: torch.Tensor, ys: Sequence[to
                                    _stream(stream)))
 
 
+SMALLM_MAX = 8
+
+
+def qgemv_int4_smallm(ws: Sequence[QInt4Matrix], x: torch.Tensor, ys: Sequence[torch.Tensor],
+                      epilogue: int = EPI_NONE, stream=None) -> None:
+    """ys[i][t] = W_i x[t] for T = x.shape[0] rows (1..8) in one launch; with
+    EPI_SWIGLU_PAIR, ys[0][t] = silu(W_0 x[t]) * (W_1 x[t]).
+
+    x: [T][ldx] bfloat16 (row stride may exceed k_in; float32 only for T = 1);
+    ys[i]: [T][n_out_i] contiguous, float32 or bfloat16.
+    """
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D [T][ldx] with contiguous rows")
+    if x.device.type != "cuda":
+        raise ValueError("x must be a device tensor")
+    n = len(ws)
+    arr = (CMatrix * max(n, 1))(*[w.c() for w in ws])
+    if len(ys) < 1:
+        raise ValueError("need at least one output")
+    ptrs = (ctypes.c_void_p * max(len(ys), n))(*[_dev(y, "ys[%d]" % i) for i, y in enumerate(ys)])
+    y_dt = _dt(ys[0])
+    if any(_dt(y) != y_dt for y in ys):
+        raise TypeError("all outputs must share one dtype")
+    _check(load().qgemv_int4_smallm(n, arr, x.data_ptr(), _dt(x), x.shape[0], x.stride(0), ptrs,
+                                    y_dt, int(epilogue), _stream(stream)))
+
+
 def moe_gather_qgemv_int4_workspace_bytes(inter: int, top_k: int) -> int:
     return int(load().moe_gather_qgemv_int4_workspace_bytes(int(inter), int(top_k)))
 
@@ -251,7 +281,7 @@ def moe_router_topk(logits: torch.Tensor, top_k: int, ids: torch.Tensor, wts: to
                                   _stream(stream)))
 
 
-__all__ = ["QInt4Matrix", "Int4Error", "qgemv_int4", "qgemv_int4_multi",
+__all__ = ["QInt4Matrix", "Int4Error", "qgemv_int4", "qgemv_int4_multi", "qgemv_int4_smallm",
            "moe_gather_qgemv_int4", "moe_gather_qgemv_int4_workspace_bytes", "qgemm_int4_padT",
            "moe_router_topk",
            "load", "F32", "BF16", "EPI_NONE", "EPI_SWIGLU_PAIR", "LIB_PATH", "SIGNATURES"]

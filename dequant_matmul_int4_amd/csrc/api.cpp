@@ -186,8 +186,10 @@ constexpr int kMaxWaves = 12;  // waves per workgroup (one persistent workgroup 
 // larger RT, then more waves).  A residual row (MoE down) must fit the
 // workgroup's one-pass staging: 4 vectors of 16 bytes per thread.
 template <class TasksFor>
-GemvPlan plan_gemv(int cpr, int n_cu, int xmode, int64_t residual_rows, TasksFor tasks_for) {
+GemvPlan plan_gemv(int cpr, int n_cu, int xmode, int64_t residual_rows, TasksFor tasks_for,
+                   int tt = 1) {
   GemvPlan best{};
+  best.tt = tt;
   double best_cost = 1e300;
   int cand_l[3] = {lanes_for(cpr), 0, 0};
   int nl = 1;
@@ -197,7 +199,7 @@ GemvPlan plan_gemv(int cpr, int n_cu, int xmode, int64_t residual_rows, TasksFor
   for (int li = 0; li < nl; ++li) {
     const int L = cand_l[li];
     const int spt = (cpr + L - 1) / L;
-    const size_t lds = gemv_lds_bytes(xmode, spt * L, residual_rows);
+    const size_t lds = gemv_lds_bytes(xmode, spt * L, residual_rows, tt);
     if (lds > (size_t)kMaxLds) continue;
     for (int rt = 1; rt <= 2; ++rt) {
       const int64_t n_tasks = tasks_for(rt * (64 / L));
@@ -207,7 +209,7 @@ GemvPlan plan_gemv(int cpr, int n_cu, int xmode, int64_t residual_rows, TasksFor
         const int64_t nw = grid * w;
         const int64_t tpw = (n_tasks + nw - 1) / nw;
         double cost = (double)tpw * w * spt * rt;
-        if ((int64_t)cpr * 4 > (int64_t)xq_octets * w) cost *= 1.5;  // staging would stall
+        if ((int64_t)cpr * 4 > (int64_t)xq_octets * w) cost *= 1.5;  // staging needs extra rounds
         const bool better = cost < best_cost * (1 - 1e-9) ||
                             (cost <= best_cost * (1 + 1e-9) &&
                              (rt > best.rt || (rt == best.rt && w > best.waves)));
@@ -274,10 +276,11 @@ int32_t qint4_abi_version(void) { return QINT4_ABI_VERSION; }
 
 namespace {
 
-// Shared body of qgemv_int4 and qgemv_int4_multi.
+// Shared body of qgemv_int4, qgemv_int4_multi and qgemv_int4_smallm: T
+// activation rows x + t * ldx (T = 1: the plain GEMV).
 qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t x_dtype,
-                       void *const *ys, int32_t y_dtype, int32_t epilogue, hipStream_t stream,
-                       const char *fn) {
+                       int64_t T, int64_t ldx, void *const *ys, int32_t y_dtype, int32_t epilogue,
+                       hipStream_t stream, const char *fn) {
   if (n < 1 || n > QINT4_MULTI_MAX)
     return fail(QINT4_ERR_SHAPE, "%s: n = %d not in [1, %d]", fn, n, QINT4_MULTI_MAX);
   if (!ws) return fail(QINT4_ERR_NULL, "%s: matrix array is NULL", fn);
@@ -322,6 +325,13 @@ qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t
   for (int i = 0; i < n_outs; ++i)
     if (!aligned(ys[i], elem_bytes(y_dtype)))
       return fail(QINT4_ERR_ALIGN, "%s: ys[%d] not aligned to its element size", fn, i);
+  if (T < 1 || T > kMaxTokens)
+    return fail(QINT4_ERR_SHAPE, "%s: T = %lld not in [1, %d]", fn, (long long)T, kMaxTokens);
+  if (T > 1 && x_dtype != QINT4_BF16)
+    return fail(QINT4_ERR_DTYPE, "%s: T > 1 needs bfloat16 activations", fn);
+  if (T > 1 && (ldx < ws[0].k_in || ldx % 8 != 0))
+    return fail(QINT4_ERR_SHAPE, "%s: ldx %lld must be >= k_in %lld and a multiple of 8", fn,
+                (long long)ldx, (long long)ws[0].k_in);
 
   // overlap checks
   Range ins[3 * QINT4_MULTI_MAX + 1], outs[QINT4_MULTI_MAX];
@@ -329,11 +339,11 @@ qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t
   static const char *mnames[3] = {"codes", "scales", "biases"};
   for (int i = 0; i < n; ++i) ni += add_matrix_ranges(&ws[i], mnames, ins + ni);
   const int64_t k_in = ws[0].k_in;
-  ins[ni++] = range(x, (size_t)k_in * elem_bytes(x_dtype), "x");
+  ins[ni++] = range(x, (size_t)((T - 1) * ldx + k_in) * elem_bytes(x_dtype), "x");
   static const char *ynames[QINT4_MULTI_MAX] = {"ys[0]", "ys[1]", "ys[2]", "ys[3]",
                                                   "ys[4]", "ys[5]", "ys[6]", "ys[7]"};
   for (int i = 0; i < n_outs; ++i)
-    outs[i] = range(ys[i], (size_t)ws[i].n_out * elem_bytes(y_dtype), ynames[i]);
+    outs[i] = range(ys[i], (size_t)T * ws[i].n_out * elem_bytes(y_dtype), ynames[i]);
   qint4_status st = check_no_overlap(outs, n_outs, ins, ni);
   if (st != QINT4_OK) return prefixed(st, fn);
 
@@ -350,10 +360,11 @@ qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t
     for (int i = 0; i < n_outs; ++i) t += (ws[i].n_out + rpt - 1) / rpt;
     return t;
   };
-  const GemvPlan plan = plan_gemv(nc, n_cu, xmode, 0, tasks_for);
+  const int tt = T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : 8;
+  const GemvPlan plan = plan_gemv(nc, n_cu, xmode, 0, tasks_for, tt);
   if (plan.waves == 0)
-    return fail(QINT4_ERR_SHAPE, "%s: k_in %lld needs more than %d bytes of LDS", fn,
-                (long long)k_in, kMaxLds);
+    return fail(QINT4_ERR_SHAPE, "%s: k_in %lld with T = %lld needs more than %d bytes of LDS", fn,
+                (long long)k_in, (long long)T, kMaxLds);
   if (plan.n_tasks > INT32_MAX) return fail(QINT4_ERR_SHAPE, "%s: too many rows", fn);
   const int rpt = plan.rt * (64 >> plan.log2_lpr);
 
@@ -375,6 +386,8 @@ qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t
   set_geometry(p, plan, nc, nc, k_in / 2, sbrow, ws[0].group_size);
   p.y_bf16 = y_dtype == QINT4_BF16;
   p.x = x;
+  p.n_tok = (int32_t)T;
+  p.ldx = (int32_t)ldx;
   p.ids = nullptr;
   p.top_k = 1;
   p.n_experts = 1;
@@ -394,14 +407,21 @@ qint4_status qgemv_int4(const qint4_matrix *w, const void *x, int32_t x_dtype, v
   if (!w) return fail(QINT4_ERR_NULL, "qgemv_int4: matrix descriptor is NULL");
   void *ys[1] = {y};
   if (!y) return fail(QINT4_ERR_NULL, "qgemv_int4: y is NULL");
-  return run_multi(1, w, x, x_dtype, ys, y_dtype, QINT4_EPI_NONE,
+  return run_multi(1, w, x, x_dtype, 1, w->k_in, ys, y_dtype, QINT4_EPI_NONE,
                    reinterpret_cast<hipStream_t>(stream), "qgemv_int4");
 }
 
 qint4_status qgemv_int4_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t x_dtype,
                               void *const *ys, int32_t y_dtype, int32_t epilogue, void *stream) {
-  return run_multi(n, ws, x, x_dtype, ys, y_dtype, epilogue, reinterpret_cast<hipStream_t>(stream),
-                   "qgemv_int4_multi");
+  return run_multi(n, ws, x, x_dtype, 1, (n >= 1 && ws) ? ws[0].k_in : 0, ys, y_dtype, epilogue,
+                   reinterpret_cast<hipStream_t>(stream), "qgemv_int4_multi");
+}
+
+qint4_status qgemv_int4_smallm(int32_t n, const qint4_matrix *ws, const void *x, int32_t x_dtype,
+                               int64_t T, int64_t ldx, void *const *ys, int32_t y_dtype,
+                               int32_t epilogue, void *stream) {
+  return run_multi(n, ws, x, x_dtype, T, ldx, ys, y_dtype, epilogue,
+                   reinterpret_cast<hipStream_t>(stream), "qgemv_int4_smallm");
 }
 
 size_t moe_gather_qgemv_int4_workspace_bytes(int64_t inter, int32_t top_k) {
@@ -487,6 +507,7 @@ qint4_status moe_gather_qgemv_int4(const qint4_matrix *gate, const qint4_matrix 
     const int64_t sbrow = (hidden / gate->group_size) * (int64_t)elem_bytes(gate->sb_dtype);
     set_geometry(p, plan, nc, nc, hidden / 2, sbrow, gate->group_size);
     p.y_bf16 = 0;
+    p.n_tok = 1;
     p.tasks_per_slot = (int32_t)((inter + rpt - 1) / rpt);
     p.x = x;
     p.ids = ids;
@@ -514,6 +535,7 @@ qint4_status moe_gather_qgemv_int4(const qint4_matrix *gate, const qint4_matrix 
     const int64_t sbrow = (inter / down->group_size) * (int64_t)elem_bytes(down->sb_dtype);
     set_geometry(p, plan, ncv, ncv, inter / 2, sbrow, down->group_size);
     p.y_bf16 = act_dtype == QINT4_BF16;
+    p.n_tok = 1;
     p.x = h;
     p.ids = ids;
     p.wts = wts;

@@ -53,13 +53,15 @@ struct GemvParams {
   int32_t top_k;
   int32_t n_experts;
   int32_t tasks_per_slot;    // EPI_SWIGLU: tasks of one expert slot
-  int32_t pad0_;
+  int32_t n_tok;             // activation rows (tokens) of a small-M call, 1..TT
   int32_t cpr_e;             // EPI_MOE_DOWN: chunks of one expert row
   float inv_cpr_e;
   uint32_t ecode_bytes;      // code bytes between experts
   uint32_t esb_bytes;        // scale bytes between experts
   uint32_t code_bytes;       // EPI_MOE_DOWN: code bytes of the whole stack (< 2^31)
   uint32_t sb_bytes;         // EPI_MOE_DOWN: scale bytes of the whole stack
+  int32_t ldx;               // elements between consecutive activation rows
+  int32_t pad1_;
   const void *x;             // activation (bf16 bits or float32), 16-byte aligned
   const uint32_t *ids;       // device [top_k] or nullptr
   const float *wts;          // device [top_k] (EPI_MOE_DOWN)
@@ -67,6 +69,7 @@ struct GemvParams {
 };
 
 struct GemvPlan {
+  int tt;           // tokens per launch template: 1, 2, 4 or 8
   int waves;        // waves per workgroup
   int rt;           // row groups per task: 1 or 2
   int log2_lpr;
@@ -81,9 +84,12 @@ struct GemvPlan {
 hipError_t launch_gemv(const GemvParams &p, const GemvPlan &plan, int xmode, int sb_bf16,
                        int epi, hipStream_t stream);
 
-// LDS bytes a GEMV launch needs: the staged activation (padded to ncx_pad
-// chunks), its chunk sums and (MoE down) the float32 residual row.
-size_t gemv_lds_bytes(int xmode, int ncx_pad, int64_t residual_rows);
+// LDS bytes a GEMV launch needs: per token, the staged activation (padded to
+// ncx_pad chunks) and its chunk sums; then (MoE down) the float32 residual row.
+size_t gemv_lds_bytes(int xmode, int ncx_pad, int64_t residual_rows, int tt = 1);
+
+// Largest token count of one small-M GEMV launch.
+constexpr int kMaxTokens = 8;
 
 struct GemmParams {
   const uint32_t *codes;

@@ -160,23 +160,29 @@ __device__ __forceinline__ float seg_sum(float v, int l2) {
   return v;
 }
 
-// sum over one 32-code chunk of (128 + q_k) * x_k, starting from acc.
+// The 32 codes of a chunk as 16 bf16 pairs (128 + q_i, 128 + q_{i+4}):
+// pq[4 jj + i] pairs nibbles i and i+4 of word jj.
+__device__ __forceinline__ void decode_chunk_bf16(const uint4 q, uint32_t magic, uint32_t (&pq)[16]) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pq[4 * jj + i] = ((w[jj] >> (4 * i)) & 0x000F000Fu) | magic;
+}
+
+// sum over one decoded chunk of (128 + q_k) * x_k, starting from acc.
 // xv: the chunk's 16 bf16 pairs as 4 x uint4 (pair i of word jj is
 // (x[8jj+i], x[8jj+i+4])).  One accumulator per word: four independent
 // dependency chains instead of one.
-__device__ __forceinline__ float dot_chunk_bf16(const uint4 q, const uint4 *xv, uint32_t magic,
-                                                float acc) {
-  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+__device__ __forceinline__ float dot_pq_bf16(const uint32_t (&pq)[16], const uint4 *xv, float acc) {
   float a[4] = {acc, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     const uint32_t xs[4] = {xv[jj].x, xv[jj].y, xv[jj].z, xv[jj].w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t pq = ((w[jj] >> (4 * i)) & 0x000F000Fu) | magic;
-      a[jj] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pq),
+    for (int i = 0; i < 4; ++i)
+      a[jj] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pq[4 * jj + i]),
                                               __builtin_bit_cast(bf16x2_t, xs[i]), a[jj], false);
-    }
   }
   return (a[0] + a[1]) + (a[2] + a[3]);
 }
@@ -414,7 +420,11 @@ struct StepBuf {
 // same (task, step) sequence; both are uniform (scalar) state.  Matrix
 // descriptors and buffer resources are refreshed only when the load cursor
 // crosses into another matrix (or expert slot).
-template <int RT, int XM, int SBT, int EPI>
+//
+// TT > 1 (small-M products): p.n_tok <= TT activation rows share every code
+// load and its decode; each token has its own staged activation, accumulator
+// and output row.
+template <int RT, int XM, int SBT, int EPI, int TT>
 __global__ void __launch_bounds__(768) qgemv_kernel(const GemvParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   warm_kernargs<sizeof(GemvParams)>();
@@ -441,9 +451,13 @@ __global__ void __launch_bounds__(768) qgemv_kernel(const GemvParams p) {
   const int lg = p.log2_group;
   const int S = (p.tasks_q + (gw < p.tasks_r ? 1 : 0)) * spt;  // steps of this wave
 
+  // LDS: per token, chunk sums then the staged activation; then (MoE down)
+  // the float32 residual row
+  const int xs_bytes = (ncx_pad * 4 + 15) & ~15;
+  const int tok_bytes = xs_bytes + ncx_pad * XB;
   float *xsum = reinterpret_cast<float *>(smem);
-  unsigned char *xbuf = smem + ((ncx_pad * 4 + 15) & ~15);
-  float *res_lds = reinterpret_cast<float *>(xbuf + (size_t)ncx_pad * XB);  // EPI_MOE_DOWN
+  unsigned char *xbuf = smem + xs_bytes;
+  float *res_lds = reinterpret_cast<float *>(smem + (size_t)TT * tok_bytes);  // EPI_MOE_DOWN
 
   // expert ids and slot weights, through the scalar cache: lane k of v_ids /
   // v_wts holds slot k's values
@@ -604,10 +618,19 @@ __global__ void __launch_bounds__(768) qgemv_kernel(const GemvParams p) {
     }
   };
 
-  stage_early_rounds<XM>(p.x, p.ncx, ncx_pad, xbuf, xsum);
+  // token t's activation is x + t * ldx elements; tokens past n_tok stage zeros
+  auto x_tok = [&](int t) {
+    return reinterpret_cast<const unsigned char *>(p.x) + (size_t)t * p.ldx * (XM == XM_BF16 ? 2 : 4);
+  };
+#pragma unroll
+  for (int t = 0; t < TT; ++t)
+    stage_early_rounds<XM>(x_tok(t), t < p.n_tok ? p.ncx : 0, ncx_pad, xbuf + t * tok_bytes,
+                           reinterpret_cast<float *>(reinterpret_cast<unsigned char *>(xsum) + t * tok_bytes));
   const int xbase = stage_last_base<XM>(p.ncx);
-  XRegs<XM> xr;
-  stage_issue<XM>(p.x, p.ncx, xbase, xr);  // activation loads first (L2), ...
+  XRegs<XM> xr[TT];
+#pragma unroll
+  for (int t = 0; t < TT; ++t)  // activation loads first (L2), ...
+    stage_issue<XM>(x_tok(t), t < p.n_tok ? p.ncx : 0, xbase, xr[t]);
   uint4 rr[RQ];
   const bool has_res = (EPI == EPI_MOE_DOWN) && p.residual != nullptr;
   if constexpr (EPI == EPI_MOE_DOWN) {
@@ -620,70 +643,92 @@ __global__ void __launch_bounds__(768) qgemv_kernel(const GemvParams p) {
 #pragma unroll
   for (int u = 0; u < D; ++u) load(buf[u]);
 
-  stage_commit<XM>(p.ncx, ncx_pad, xbase, xr, xbuf, xsum);
-  stage_padding<XM>(p.ncx, ncx_pad, xbuf, xsum);
+#pragma unroll
+  for (int t = 0; t < TT; ++t) {
+    float *xs_t = reinterpret_cast<float *>(reinterpret_cast<unsigned char *>(xsum) + t * tok_bytes);
+    stage_commit<XM>(p.ncx, ncx_pad, xbase, xr[t], xbuf + t * tok_bytes, xs_t);
+    stage_padding<XM>(p.ncx, ncx_pad, xbuf + t * tok_bytes, xs_t);
+  }
   if (has_res) residual_commit((int)p.m[0].n_out, p.y_bf16, rr, res_lds);
   lds_barrier();
 
   // ---- consume stream ----
-  float acc[NS][RT];
+  float acc[TT][NS][RT];
 #pragma unroll
-  for (int s = 0; s < NS; ++s)
+  for (int t = 0; t < TT; ++t)
 #pragma unroll
-    for (int r = 0; r < RT; ++r) acc[s][r] = 0.f;
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int r = 0; r < RT; ++r) acc[t][s][r] = 0.f;
   Cur cc;
   start(cc);
   int cit = 0;  // step inside the task
 
   auto finish = [&]() {
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
+    for (int t = 0; t < TT; ++t) {
+      if (t >= p.n_tok) break;  // uniform
 #pragma unroll
-      for (int r = 0; r < RT; ++r) acc[s][r] = seg_sum(acc[s][r], l2);
-    if (j == 0) {
+      for (int s = 0; s < NS; ++s)
 #pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        const int row = cc.row0 + r * rpi + sg;
-        if (row < cc.n_rows) {
-          if constexpr (EPI == EPI_STORE) {
-            store_out(cc.y, row, acc[0][r], p.y_bf16);
-          } else if constexpr (EPI == EPI_SWIGLU) {
-            const float g = acc[0][r], u = acc[1][r];
-            const float h = cc.live ? (g / (1.f + __expf(-g))) * u : 0.f;
-            store_out(cc.y, row, h, p.y_bf16);
-          } else {
-            const float res = has_res ? res_lds[row] : 0.f;
-            store_out(cc.y, row, res + acc[0][r], p.y_bf16);
+        for (int r = 0; r < RT; ++r) acc[t][s][r] = seg_sum(acc[t][s][r], l2);
+      if (j == 0) {
+        // token t's output row: y + t * n_rows elements
+        void *yt = cc.y + (size_t)t * cc.n_rows * (p.y_bf16 ? 2 : 4);
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+          const int row = cc.row0 + r * rpi + sg;
+          if (row < cc.n_rows) {
+            if constexpr (EPI == EPI_STORE) {
+              store_out(yt, row, acc[t][0][r], p.y_bf16);
+            } else if constexpr (EPI == EPI_SWIGLU) {
+              const float g = acc[t][0][r], u = acc[t][1][r];
+              const float h = cc.live ? (g / (1.f + __expf(-g))) * u : 0.f;
+              store_out(yt, row, h, p.y_bf16);
+            } else {
+              const float res = has_res ? res_lds[row] : 0.f;
+              store_out(yt, row, res + acc[t][0][r], p.y_bf16);
+            }
           }
         }
       }
     }
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
+    for (int t = 0; t < TT; ++t)
 #pragma unroll
-      for (int r = 0; r < RT; ++r) acc[s][r] = 0.f;
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int r = 0; r < RT; ++r) acc[t][s][r] = 0.f;
   };
 
   auto consume = [&](const StepBuf<RT, NS> &bf) {
     const int xc = j + cit * L;  // staged chunk (virtual row chunk); < ncx_pad
-    const float xs = xsum[xc];
     if constexpr (XM == XM_BF16) {
-      uint4 xv[4];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) xv[jj] = reinterpret_cast<const uint4 *>(xbuf)[jj * ncx_pad + xc];
-      const float d0 = -128.f * xs;
 #pragma unroll
       for (int s = 0; s < NS; ++s)
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
-          const float d = dot_chunk_bf16(bf.q[s][r], xv, magic, d0);  // sum q x
-          const float part = fmaf(sb_value<SBT>(bf.s[s][r]), d, sb_value<SBT>(bf.b[s][r]) * xs);
-          if constexpr (EPI == EPI_MOE_DOWN)
-            acc[s][r] = fmaf(bf.w, part, acc[s][r]);
-          else
-            acc[s][r] += part;
+          uint32_t pq[16];
+          decode_chunk_bf16(bf.q[s][r], magic, pq);  // once for every token
+          const float sc = sb_value<SBT>(bf.s[s][r]), bi = sb_value<SBT>(bf.b[s][r]);
+#pragma unroll
+          for (int t = 0; t < TT; ++t) {
+            const unsigned char *xb = xbuf + t * tok_bytes;
+            const float xs = *reinterpret_cast<const float *>(xb - xs_bytes + 4 * xc);
+            uint4 xv[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) xv[jj] = reinterpret_cast<const uint4 *>(xb)[jj * ncx_pad + xc];
+            const float d = dot_pq_bf16(pq, xv, -128.f * xs);  // sum q x
+            const float part = fmaf(sc, d, bi * xs);
+            if constexpr (EPI == EPI_MOE_DOWN)
+              acc[t][s][r] = fmaf(bf.w, part, acc[t][s][r]);
+            else
+              acc[t][s][r] += part;
+          }
         }
     } else {
+      static_assert(XM == XM_BF16 || TT == 1, "float32 activations: one token");
+      const float xs = xsum[xc];
       float4 xv[8];
 #pragma unroll
       for (int pl = 0; pl < 8; ++pl) xv[pl] = reinterpret_cast<const float4 *>(xbuf)[pl * ncx_pad + xc];
@@ -694,9 +739,9 @@ __global__ void __launch_bounds__(768) qgemv_kernel(const GemvParams p) {
           const float d = dot_chunk_f32(bf.q[s][r], xv, 0.f);
           const float part = fmaf(sb_value<SBT>(bf.s[s][r]), d, sb_value<SBT>(bf.b[s][r]) * xs);
           if constexpr (EPI == EPI_MOE_DOWN)
-            acc[s][r] = fmaf(bf.w, part, acc[s][r]);
+            acc[0][s][r] = fmaf(bf.w, part, acc[0][s][r]);
           else
-            acc[s][r] += part;
+            acc[0][s][r] += part;
         }
     }
     if (++cit == spt) {
@@ -715,9 +760,9 @@ __global__ void __launch_bounds__(768) qgemv_kernel(const GemvParams p) {
   }
 }
 
-template <int RT, int XM, int SBT, int EPI>
+template <int RT, int XM, int SBT, int EPI, int TT = 1>
 hipError_t launch_one(const GemvParams &p, const GemvPlan &plan, hipStream_t stream) {
-  auto kern = qgemv_kernel<RT, XM, SBT, EPI>;
+  auto kern = qgemv_kernel<RT, XM, SBT, EPI, TT>;
   // Opt in to more than 64 KB of dynamic LDS once per process and kernel
   // (a benign race: concurrent first calls set the same value).
   static bool big_lds = false;
@@ -744,15 +789,41 @@ hipError_t launch_sel(const GemvParams &p, const GemvPlan &plan, int xmode, int 
 
 }  // namespace
 
-size_t gemv_lds_bytes(int xmode, int ncx_pad, int64_t residual_rows) {
+size_t gemv_lds_bytes(int xmode, int ncx_pad, int64_t residual_rows, int tt) {
   const size_t xb = (xmode == XM_BF16) ? 64 : 128;
-  return (((size_t)ncx_pad * 4 + 15) & ~(size_t)15) + (size_t)ncx_pad * xb +
+  return (size_t)tt * ((((size_t)ncx_pad * 4 + 15) & ~(size_t)15) + (size_t)ncx_pad * xb) +
          (size_t)residual_rows * 4;
+}
+
+// Small-M launches: bf16 activations, store or SwiGLU-pair epilogue.
+template <int TT>
+hipError_t launch_tokens(const GemvParams &p, const GemvPlan &plan, int sb_bf16, int epi,
+                         hipStream_t s) {
+  if (epi == EPI_STORE)
+    return plan.rt == 2 ? (sb_bf16 ? launch_one<2, XM_BF16, 1, EPI_STORE, TT>(p, plan, s)
+                                   : launch_one<2, XM_BF16, 0, EPI_STORE, TT>(p, plan, s))
+                        : (sb_bf16 ? launch_one<1, XM_BF16, 1, EPI_STORE, TT>(p, plan, s)
+                                   : launch_one<1, XM_BF16, 0, EPI_STORE, TT>(p, plan, s));
+  if (epi == EPI_SWIGLU)
+    return plan.rt == 2 ? (sb_bf16 ? launch_one<2, XM_BF16, 1, EPI_SWIGLU, TT>(p, plan, s)
+                                   : launch_one<2, XM_BF16, 0, EPI_SWIGLU, TT>(p, plan, s))
+                        : (sb_bf16 ? launch_one<1, XM_BF16, 1, EPI_SWIGLU, TT>(p, plan, s)
+                                   : launch_one<1, XM_BF16, 0, EPI_SWIGLU, TT>(p, plan, s));
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemv(const GemvParams &p, const GemvPlan &plan, int xmode, int sb_bf16, int epi,
                        hipStream_t stream) {
   if (plan.rt != 1 && plan.rt != 2) return hipErrorInvalidValue;
+  if (plan.tt != 1) {
+    if (xmode != XM_BF16) return hipErrorInvalidValue;
+    switch (plan.tt) {
+      case 2: return launch_tokens<2>(p, plan, sb_bf16, epi, stream);
+      case 4: return launch_tokens<4>(p, plan, sb_bf16, epi, stream);
+      case 8: return launch_tokens<8>(p, plan, sb_bf16, epi, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (epi) {
     case EPI_STORE:
       return plan.rt == 2 ? launch_sel<2, EPI_STORE>(p, plan, xmode, sb_bf16, stream)

@@ -7,6 +7,8 @@
  *   [FFAI #14] thewafflehaus/FFAI pull 14, "feat(everything-bagel): clean
  *              migration of PR #9 + #10 onto updated dev".
  *   [FFAI #9]  thewafflehaus/FFAI pull 9, "Everything Bagel".
+ *   [ds4 #844] antirez/ds4 pull 844, "Ornith 1.5 + Qwen 3.8 27B hybrid runtime
+ *              + DFlash speculative decoding on Metal".
  *
  * ---------------------------------------------------------------------------
  * Weight format (shared by every entry point)
@@ -144,6 +146,27 @@ qint4_status qgemv_int4(const qint4_matrix *w, const void *x, int32_t x_dtype,
 qint4_status qgemv_int4_multi(int32_t n, const qint4_matrix *ws, const void *x,
                               int32_t x_dtype, void *const *ys, int32_t y_dtype,
                               int32_t epilogue, void *stream);
+
+/*
+ * qgemv_int4_smallm -- qgemv_int4_multi for T = 1..QINT4_SMALLM_MAX activation
+ * rows at once (small-M products: a few decode tokens, or the tokens of a
+ * speculative-verify round, against the same weights).
+ *
+ * [ds4 #844], PR body and the commit on small speculative-verify rounds: a
+ * fused gate/up SwiGLU for 1..8 rows, and 2..9-token verify rounds that
+ * cannot fill a 32-row matrix-multiply tile.  Every code load and its nibble decode is shared by the T rows; the
+ * arithmetic per row is exactly that of qgemv_int4_multi.
+ *
+ *   T        1..QINT4_SMALLM_MAX; T > 1 needs x_dtype QINT4_BF16
+ *   x        device [T][ldx], row t at x + t * ldx elements, 16-byte aligned;
+ *            ldx >= k_in, ldx % 8 == 0 when T > 1
+ *   ys       as in qgemv_int4_multi, each output [T][n_out] (row-major)
+ *   other arguments as in qgemv_int4_multi
+ */
+#define QINT4_SMALLM_MAX 8
+qint4_status qgemv_int4_smallm(int32_t n, const qint4_matrix *ws, const void *x,
+                               int32_t x_dtype, int64_t T, int64_t ldx, void *const *ys,
+                               int32_t y_dtype, int32_t epilogue, void *stream);
 
 /*
  * Bytes of device workspace one moe_gather_qgemv_int4 call needs for an

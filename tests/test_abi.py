@@ -135,6 +135,21 @@ def test_gemm_validation(lib):
     assert _gemm(lib, _m(), y=A + 0x300000 + 128) == 5
 
 
+def _smallm(lib, m, T=4, ldx=256, x=A + 0x300000, xdt=1, y=A + 0x400000, ydt=1, epi=0, n=1):
+    ys = (ctypes.c_void_p * 1)(y)
+    return lib.qgemv_int4_smallm(n, ctypes.byref(m), x, xdt, T, ldx, ys, ydt, epi, None)
+
+
+def test_smallm_validation(lib):
+    assert _smallm(lib, _m(), T=0) == 2
+    assert _smallm(lib, _m(), T=9) == 2 and "T = 9" in _err(lib)
+    assert _smallm(lib, _m(), xdt=0) == 3                      # float32 rows need T = 1
+    assert _smallm(lib, _m(), ldx=128) == 2                    # ldx < k_in
+    assert _smallm(lib, _m(), ldx=260) == 2                    # ldx not a multiple of 8
+    assert _smallm(lib, _m(), y=A + 0x300000 + 2 * 512) == 5   # y overlaps row 2 of x
+    assert _smallm(lib, _m(), n=0) == 2
+
+
 def _router(lib, logits=A + 0x300000, dt=0, n_tokens=1, n_experts=128, top_k=8, ids=A + 0x400000,
             wts=A + 0x410000):
     return lib.moe_router_topk(logits, dt, n_tokens, n_experts, top_k, ids, wts, None)

@@ -1,0 +1,106 @@
+"""GPU parity of qgemv_int4_smallm (T = 1..8 activation rows) against the fp64 oracle.
+
+Each token's outputs follow the qgemv_int4 rules (per-element bf16 bound,
+relative L2 for float32); the oracle runs one GEMV per token.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.gpu_common import check, dev_matrix, lib, nan_like, oracle_threads, require_gpu, to_np64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _x(rng, T, k_in, ldx=None):
+    """bf16 bits [T][k_in] and the device tensor [T][ldx] holding them (pad = NaN)."""
+    x = synth.draw_activation(rng, (T, k_in), "bf16")
+    ldx = ldx or k_in
+    dev = torch.full((T, ldx), float("nan"), dtype=torch.bfloat16, device="cuda")
+    dev[:, :k_in] = synth.to_torch(x, "bf16")
+    return x, dev
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("n_out,k_in,g", [(256, 1024, 64), (1000, 2048, 32), (96, 4096, 128),
+                                          (130, 5120, 64)])
+def test_smallm_single_matrix(T, n_out, k_in, g):
+    q = lib()
+    rng = np.random.default_rng(T * 1000 + n_out + k_in)
+    w = synth.draw_matrix(rng, n_out, k_in, g, "bf16")
+    x, xd = _x(rng, T, k_in)
+    y = nan_like((T, n_out), torch.bfloat16)
+    q.qgemv_int4_smallm([dev_matrix(w)], xd, [y])
+    torch.cuda.synchronize()
+    for t in range(T):
+        ref, a = oracle.gemv(w, x[t], "bf16", threads=oracle_threads())
+        check(y[t], ref, a, "smallm T=%d t=%d" % (T, t))
+
+
+@pytest.mark.parametrize("T", [2, 4, 7])
+def test_smallm_qkv_strided_rows_f32_out(T):
+    """Three projections of T shared rows; x rows strided (ldx > k_in); float32 outputs."""
+    q = lib()
+    rng = np.random.default_rng(T)
+    k_in = 2048
+    ws = [synth.draw_matrix(rng, n, k_in, 64, "bf16") for n in (512, 128, 128)]
+    x, xd = _x(rng, T, k_in, ldx=k_in + 64)
+    ys = [nan_like((T, w.n_out), torch.float32) for w in ws]
+    q.qgemv_int4_smallm([dev_matrix(w) for w in ws], xd, ys)
+    torch.cuda.synchronize()
+    for t in range(T):
+        for w, y, (ref, a) in zip(ws, ys, oracle.multi(ws, x[t], "bf16")):
+            check(y[t], ref, a, "smallm qkv t=%d" % t)
+
+
+@pytest.mark.parametrize("T", [1, 3, 8])
+def test_smallm_swiglu_pair(T):
+    """Fused gate/up SwiGLU for T rows; h is float32 [T][inter]."""
+    q = lib()
+    rng = np.random.default_rng(40 + T)
+    hidden, inter = 1024, 768
+    gate = synth.draw_matrix(rng, inter, hidden, 64, "bf16")
+    up = synth.draw_matrix(rng, inter, hidden, 64, "bf16")
+    x, xd = _x(rng, T, hidden)
+    h = nan_like((T, inter), torch.float32)
+    q.qgemv_int4_smallm([dev_matrix(gate), dev_matrix(up)], xd, [h], epilogue=q.EPI_SWIGLU_PAIR)
+    torch.cuda.synchronize()
+    for t in range(T):
+        ref, a = oracle.swiglu_pair(gate, up, x[t], "bf16")
+        got = to_np64(h[t])
+        assert np.all(np.isfinite(got))
+        # float32 SwiGLU of float32 sums: the bound of the T = 1 SwiGLU test
+        assert np.all(np.abs(got - ref) <= 1e-5 * np.abs(ref) + 2.0 ** -16 * a), t
+
+
+def test_smallm_tokens_are_independent_and_exact_repeat():
+    """Row t of a T=8 call equals a T=1 call on row t, bit for bit."""
+    q = lib()
+    rng = np.random.default_rng(77)
+    w = synth.draw_matrix(rng, 384, 3072, 64, "bf16")
+    x, xd = _x(rng, 8, 3072)
+    y8 = nan_like((8, 384), torch.float32)
+    q.qgemv_int4_smallm([dev_matrix(w)], xd, [y8])
+    for t in (0, 5, 7):
+        y1 = nan_like((1, 384), torch.float32)
+        q.qgemv_int4_smallm([dev_matrix(w)], xd[t:t + 1].contiguous(), [y1])
+        torch.cuda.synchronize()
+        assert torch.equal(y1[0], y8[t]), t
+
+
+def test_smallm_rejects_float32_multi_row():
+    q = lib()
+    rng = np.random.default_rng(3)
+    w = synth.draw_matrix(rng, 64, 256, 64, "bf16")
+    x = torch.zeros((2, 256), dtype=torch.float32, device="cuda")
+    y = torch.zeros((2, 64), dtype=torch.float32, device="cuda")
+    with pytest.raises(q.Int4Error) as e:
+        q.qgemv_int4_smallm([dev_matrix(w)], x, [y])
+    assert e.value.status == "ERR_DTYPE"
