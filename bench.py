@@ -49,8 +49,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="qkv",
-                    choices=["single", "qkv", "dense", "moe", "prefill"])
-    ap.add_argument("--T", type=int, default=256, help="prefill rows")
+                    choices=["single", "qkv", "smallm", "dense", "moe", "prefill"])
+    ap.add_argument("--T", type=int, default=None,
+                    help="prefill rows (default 256) or small-M tokens (default 4)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-time budget of the CPU oracle sample (0 disables)")
     ap.add_argument("--router", choices=("gpu", "pre-drawn"), default="gpu",
@@ -138,6 +139,25 @@ class QKV(Workload):
 
     def step(self, i):
         self.q.qgemv_int4_multi(self.pool[i % self.R], self.x, self.ys)
+
+
+class SmallM(QKV):
+    """The q/k/v projection set for T = 1..8 tokens in one launch (small-M products)."""
+
+    def __init__(self, q, synth, torch, T):
+        super().__init__(q, synth, torch)
+        self.T = T
+        self.name = "qkv_smallm_T%d" % T
+        self.dominant = "qgemv_kernel (EPI_STORE, bf16 x, 3 matrices, %d tokens)" % T
+        self.xT = torch.randn(T, 4096, device="cuda").to(torch.bfloat16)
+        self.ysT = [torch.empty(T, n, device="cuda", dtype=torch.bfloat16) for n in (4096, 1024, 1024)]
+        self.config = dict(self.config, workload=self.name, T=T)
+
+    def algo_bytes(self):
+        return self.wb + self.T * (4096 * 2 + 6144 * 2)
+
+    def step(self, i):
+        self.q.qgemv_int4_smallm(self.pool[i % self.R], self.xT, self.ysT)
 
 
 class Dense(Workload):
@@ -293,6 +313,12 @@ def cpu_baseline(workload: str, budget_s: float, T: int):
         wb = sum(w.weight_bytes for w in d["ws"])
         fn = lambda: oracle.multi(d["ws"], d["x"], "bf16", threads=threads)
         sample = "full q/k/v set (seed 1), repeated"
+    elif workload == "smallm":
+        d = synth.qkv_multi()
+        wb = sum(w.weight_bytes for w in d["ws"])
+        xs = [synth.draw_activation(np.random.default_rng(100 + t), (4096,), "bf16") for t in range(T)]
+        fn = lambda: [oracle.multi(d["ws"], x, "bf16", threads=threads) for x in xs]
+        sample = "full q/k/v set (seed 1) for %d tokens, repeated" % T
     elif workload == "dense":
         d = synth.dense_layer()
         wb = sum(d[k].weight_bytes for k in ("gate", "up", "down"))
@@ -343,6 +369,8 @@ def cpu_baseline(workload: str, budget_s: float, T: int):
 
 def main():
     args = parse()
+    if args.T is None:
+        args.T = 4 if args.workload == "smallm" else 256
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -365,6 +393,8 @@ def main():
         wl = QKV(q, synth, torch)
     elif args.workload == "dense":
         wl = Dense(q, synth, torch)
+    elif args.workload == "smallm":
+        wl = SmallM(q, synth, torch, args.T)
     elif args.workload == "moe":
         wl = MoE(q, synth, torch, gpu_router=args.router == "gpu")
     else:
@@ -427,6 +457,8 @@ def main():
         if isinstance(wl, MoE):
             out["tokens_per_s_equiv"] = 1e3 / (ms_step * 40)
             out["tokens_per_s_equiv_layers"] = 40
+        if isinstance(wl, SmallM):
+            out["tokens_per_call"] = wl.T
         # per launch of the step's kernels (one launch for single/qkv; for the
         # two-launch workloads the pair is timed as one unit)
         ach = wl.algo_bytes() / (ms_step * 1e-3) / 1e9
