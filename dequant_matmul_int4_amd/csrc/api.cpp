@@ -201,7 +201,7 @@ GemvPlan plan_gemv(int cpr, int n_cu, int xmode, int64_t residual_rows, TasksFor
     const int spt = (cpr + L - 1) / L;
     const size_t lds = gemv_lds_bytes(xmode, spt * L, residual_rows, tt);
     if (lds > (size_t)kMaxLds) continue;
-    for (int rt = 1; rt <= (tt >= 4 ? 1 : 2); ++rt) {  // 4+ tokens: one row group per lane
+    for (int rt = 1; rt <= 2; ++rt) {
       const int64_t n_tasks = tasks_for(rt * (64 / L));
       for (int w = 1; w <= std::min(kMaxWaves, gemv_max_waves(tt)); ++w) {
         if (residual_rows > (int64_t)w * 64 * 4 * 4) continue;

@@ -91,9 +91,9 @@ size_t gemv_lds_bytes(int xmode, int ncx_pad, int64_t residual_rows, int tt = 1)
 // Largest token count of one small-M GEMV launch.
 constexpr int kMaxTokens = 8;
 
-// Waves per workgroup a GEMV kernel supports: 12, or 8 when 4+ tokens keep
-// more accumulators and staged activations per lane.
-constexpr int gemv_max_waves(int tt) { return tt >= 4 ? 8 : 12; }
+// Waves per workgroup a GEMV kernel supports: 12, or 8 for the 8-token
+// kernels, whose accumulators and decoded weights need up to 256 VGPRs a lane.
+constexpr int gemv_max_waves(int tt) { return tt >= 8 ? 8 : 12; }
 
 struct GemmParams {
   const uint32_t *codes;

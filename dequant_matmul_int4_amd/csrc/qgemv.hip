@@ -425,7 +425,7 @@ struct StepBuf {
 // load and its decode; each token has its own staged activation, accumulator
 // and output row.
 template <int RT, int XM, int SBT, int EPI, int TT>
-__global__ void __launch_bounds__(TT >= 4 ? 512 : 768) qgemv_kernel(const GemvParams p) {
+__global__ void __launch_bounds__(TT >= 8 ? 512 : 768) qgemv_kernel(const GemvParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   warm_kernargs<sizeof(GemvParams)>();
   constexpr int NS = (EPI == EPI_SWIGLU) ? 2 : 1;  // code streams per row (gate, up)
@@ -799,16 +799,6 @@ size_t gemv_lds_bytes(int xmode, int ncx_pad, int64_t residual_rows, int tt) {
 template <int TT>
 hipError_t launch_tokens(const GemvParams &p, const GemvPlan &plan, int sb_bf16, int epi,
                          hipStream_t s) {
-  if constexpr (TT >= 4) {  // the planner gives 4+ tokens one row group per lane
-    if (plan.rt != 1) return hipErrorInvalidValue;
-    if (epi == EPI_STORE)
-      return sb_bf16 ? launch_one<1, XM_BF16, 1, EPI_STORE, TT>(p, plan, s)
-                     : launch_one<1, XM_BF16, 0, EPI_STORE, TT>(p, plan, s);
-    if (epi == EPI_SWIGLU)
-      return sb_bf16 ? launch_one<1, XM_BF16, 1, EPI_SWIGLU, TT>(p, plan, s)
-                     : launch_one<1, XM_BF16, 0, EPI_SWIGLU, TT>(p, plan, s);
-    return hipErrorInvalidValue;
-  }
   if (epi == EPI_STORE)
     return plan.rt == 2 ? (sb_bf16 ? launch_one<2, XM_BF16, 1, EPI_STORE, TT>(p, plan, s)
                                    : launch_one<2, XM_BF16, 0, EPI_STORE, TT>(p, plan, s))
