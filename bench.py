@@ -15,6 +15,8 @@ on the replay stream, bracketed by device synchronisation.
 Workloads (default: qkv):
   single   1024x1024 g64 GEMV, fp32 scales/biases, fp32 x and y
   qkv      q/k/v projections of one bf16 4096-vector (4096/1024/1024 rows), one launch
+  rmsqkv   the same launch with the RMSNorm of the input fused in front
+  smallm   the q/k/v set for --T tokens (1..8, default 4) in one launch
   dense    gate/up 5120->17408 with SwiGLU (fp32 h), then down 17408->5120
   moe      top-8 of 128 experts, hidden 2048, inter 768, weighted combine + residual;
            each step routes its token's logits on the GPU first (--router pre-drawn: skip)
@@ -49,7 +51,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="qkv",
-                    choices=["single", "qkv", "smallm", "dense", "moe", "prefill"])
+                    choices=["single", "qkv", "rmsqkv", "smallm", "dense", "moe", "prefill"])
     ap.add_argument("--T", type=int, default=None,
                     help="prefill rows (default 256) or small-M tokens (default 4)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -158,6 +160,24 @@ class SmallM(QKV):
 
     def step(self, i):
         self.q.qgemv_int4_smallm(self.pool[i % self.R], self.xT, self.ysT)
+
+
+class RmsQKV(QKV):
+    """RMSNorm of the bf16 input fused into the q/k/v projection launch."""
+
+    def __init__(self, q, synth, torch):
+        super().__init__(q, synth, torch)
+        self.name = "rms_qkv_multi_t1"
+        self.dominant = "qgemv_kernel (EPI_STORE, RMSNorm prologue, bf16 x, 3 matrices)"
+        self.gamma = (0.5 + torch.rand(4096, device="cuda")).to(torch.bfloat16)
+        self.eps = 1e-6
+        self.config = dict(self.config, workload=self.name, norm="rmsnorm", eps=self.eps)
+
+    def algo_bytes(self):
+        return super().algo_bytes() + 4096 * 2
+
+    def step(self, i):
+        self.q.rms_norm_qgemv_int4(self.pool[i % self.R], self.x, self.gamma, self.eps, self.ys)
 
 
 class Dense(Workload):
@@ -313,6 +333,12 @@ def cpu_baseline(workload: str, budget_s: float, T: int):
         wb = sum(w.weight_bytes for w in d["ws"])
         fn = lambda: oracle.multi(d["ws"], d["x"], "bf16", threads=threads)
         sample = "full q/k/v set (seed 1), repeated"
+    elif workload == "rmsqkv":
+        d = synth.rms_qkv()
+        wb = sum(w.weight_bytes for w in d["ws"])
+        fn = lambda: oracle.rms_norm_multi(d["ws"], d["x"], "bf16", d["gamma"], d["eps"],
+                                           threads=threads)
+        sample = "full RMSNorm + q/k/v set (seed 5), repeated"
     elif workload == "smallm":
         d = synth.qkv_multi()
         wb = sum(w.weight_bytes for w in d["ws"])
@@ -391,6 +417,8 @@ def main():
         wl = Single(q, synth, torch)
     elif args.workload == "qkv":
         wl = QKV(q, synth, torch)
+    elif args.workload == "rmsqkv":
+        wl = RmsQKV(q, synth, torch)
     elif args.workload == "dense":
         wl = Dense(q, synth, torch)
     elif args.workload == "smallm":

@@ -36,7 +36,8 @@ MULTI_MAX = 8
 TOPK_MAX = 8
 
 STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_DTYPE", 4: "ERR_ALIGN",
-          5: "ERR_ALIAS", 6: "ERR_WORKSPACE", 7: "ERR_DEVICE", 8: "ERR_LAUNCH"}
+          5: "ERR_ALIAS", 6: "ERR_WORKSPACE", 7: "ERR_DEVICE", 8: "ERR_LAUNCH",
+          9: "ERR_VALUE"}
 
 
 class Int4Error(RuntimeError):
@@ -70,6 +71,8 @@ SIGNATURES = [
                                 ctypes.POINTER(ctypes.c_void_p), _I32, _I32, _P]),
     ("qgemv_int4_smallm", _I32, [_I32, ctypes.POINTER(CMatrix), _P, _I32, _I64, _I64,
                                  ctypes.POINTER(ctypes.c_void_p), _I32, _I32, _P]),
+    ("rms_norm_qgemv_int4", _I32, [_I32, ctypes.POINTER(CMatrix), _P, _I32, _P, ctypes.c_float,
+                                   ctypes.POINTER(ctypes.c_void_p), _I32, _I32, _P]),
     ("moe_gather_qgemv_int4_workspace_bytes", ctypes.c_size_t, [_I64, _I32]),
     ("moe_gather_qgemv_int4", _I32, [ctypes.POINTER(CMatrix), ctypes.POINTER(CMatrix),
                                      ctypes.POINTER(CMatrix), _P, _P, _P, _I32, _P, _P, _I32,
@@ -186,6 +189,24 @@ def qgemv_int4_multi(ws: Sequence[QInt4Matrix], x: torch.Tensor, ys: Sequence[to
                                    _stream(stream)))
 
 
+def rms_norm_qgemv_int4(ws: Sequence[QInt4Matrix], x: torch.Tensor, gamma: torch.Tensor, eps: float,
+                        ys: Sequence[torch.Tensor], epilogue: int = EPI_NONE, stream=None) -> None:
+    """ys[i] = W_i (x * gamma / sqrt(mean(x^2) + eps)) in one launch (EPI_SWIGLU_PAIR as in
+    qgemv_int4_multi).  x, gamma: [k_in], one dtype (float32 or bfloat16)."""
+    n = len(ws)
+    arr = (CMatrix * max(n, 1))(*[w.c() for w in ws])
+    if len(ys) < 1:
+        raise ValueError("need at least one output")
+    if gamma.dtype != x.dtype:
+        raise TypeError("gamma must have x's dtype")
+    ptrs = (ctypes.c_void_p * max(len(ys), n))(*[_dev(y, "ys[%d]" % i) for i, y in enumerate(ys)])
+    y_dt = _dt(ys[0])
+    if any(_dt(y) != y_dt for y in ys):
+        raise TypeError("all outputs must share one dtype")
+    _check(load().rms_norm_qgemv_int4(n, arr, _dev(x, "x"), _dt(x), _dev(gamma, "gamma"),
+                                      float(eps), ptrs, y_dt, int(epilogue), _stream(stream)))
+
+
 SMALLM_MAX = 8
 
 
@@ -283,5 +304,5 @@ def moe_router_topk(logits: torch.Tensor, top_k: int, ids: torch.Tensor, wts: to
 
 __all__ = ["QInt4Matrix", "Int4Error", "qgemv_int4", "qgemv_int4_multi", "qgemv_int4_smallm",
            "moe_gather_qgemv_int4", "moe_gather_qgemv_int4_workspace_bytes", "qgemm_int4_padT",
-           "moe_router_topk",
+           "moe_router_topk", "rms_norm_qgemv_int4",
            "load", "F32", "BF16", "EPI_NONE", "EPI_SWIGLU_PAIR", "LIB_PATH", "SIGNATURES"]

@@ -195,7 +195,7 @@ GemvPlan plan_gemv(int cpr, int n_cu, int xmode, int64_t residual_rows, TasksFor
   int nl = 1;
   for (int l : {32, 64})
     if (cpr > l && cpr % l != 0 && l > cand_l[0]) cand_l[nl++] = l;
-  const int xq_octets = (xmode == XM_BF16 ? 2 : 5) * 64;  // octets one wave stages without a stall
+  const int xq_octets = xm_octets(xmode) * 64;  // octets one wave stages without a stall
   for (int li = 0; li < nl; ++li) {
     const int L = cand_l[li];
     const int spt = (cpr + L - 1) / L;
@@ -264,6 +264,7 @@ const char *qint4_status_string(int32_t status) {
     case QINT4_ERR_WORKSPACE: return "workspace missing or too small";
     case QINT4_ERR_DEVICE: return "no gfx950 device";
     case QINT4_ERR_LAUNCH: return "kernel launch failed";
+    case QINT4_ERR_VALUE: return "scalar argument out of range";
     default: return "unknown status";
   }
 }
@@ -278,9 +279,11 @@ namespace {
 
 // Shared body of qgemv_int4, qgemv_int4_multi and qgemv_int4_smallm: T
 // activation rows x + t * ldx (T = 1: the plain GEMV).
+// gamma != NULL: RMSNorm prologue (T must be 1).
 qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t x_dtype,
                        int64_t T, int64_t ldx, void *const *ys, int32_t y_dtype, int32_t epilogue,
-                       hipStream_t stream, const char *fn) {
+                       hipStream_t stream, const char *fn, const void *gamma = nullptr,
+                       float eps = 0.f) {
   if (n < 1 || n > QINT4_MULTI_MAX)
     return fail(QINT4_ERR_SHAPE, "%s: n = %d not in [1, %d]", fn, n, QINT4_MULTI_MAX);
   if (!ws) return fail(QINT4_ERR_NULL, "%s: matrix array is NULL", fn);
@@ -333,13 +336,21 @@ qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t
     return fail(QINT4_ERR_SHAPE, "%s: ldx %lld must be >= k_in %lld and a multiple of 8", fn,
                 (long long)ldx, (long long)ws[0].k_in);
 
+  if (gamma) {
+    if (T != 1) return fail(QINT4_ERR_SHAPE, "%s: the RMSNorm prologue takes one row", fn);
+    if (!aligned(gamma, 16)) return fail(QINT4_ERR_ALIGN, "%s: gamma not 16-byte aligned", fn);
+    if (!(eps > 0.f) || eps > 3.4e38f)
+      return fail(QINT4_ERR_VALUE, "%s: eps %g must be finite and > 0", fn, (double)eps);
+  }
+
   // overlap checks
-  Range ins[3 * QINT4_MULTI_MAX + 1], outs[QINT4_MULTI_MAX];
+  Range ins[3 * QINT4_MULTI_MAX + 2], outs[QINT4_MULTI_MAX];
   int ni = 0;
   static const char *mnames[3] = {"codes", "scales", "biases"};
   for (int i = 0; i < n; ++i) ni += add_matrix_ranges(&ws[i], mnames, ins + ni);
   const int64_t k_in = ws[0].k_in;
   ins[ni++] = range(x, (size_t)((T - 1) * ldx + k_in) * elem_bytes(x_dtype), "x");
+  if (gamma) ins[ni++] = range(gamma, (size_t)k_in * elem_bytes(x_dtype), "gamma");
   static const char *ynames[QINT4_MULTI_MAX] = {"ys[0]", "ys[1]", "ys[2]", "ys[3]",
                                                   "ys[4]", "ys[5]", "ys[6]", "ys[7]"};
   for (int i = 0; i < n_outs; ++i)
@@ -349,7 +360,8 @@ qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t
 
   // plan
   const int nc = (int)(k_in / 32);
-  const int xmode = x_dtype == QINT4_BF16 ? XM_BF16 : XM_F32;
+  const int xmode = gamma ? (x_dtype == QINT4_BF16 ? XM_RMS_BF16 : XM_RMS_F32)
+                          : (x_dtype == QINT4_BF16 ? XM_BF16 : XM_F32);
   const int epi = swiglu ? EPI_SWIGLU : EPI_STORE;
   const int sb_bf16 = ws[0].sb_dtype == QINT4_BF16;
   int n_cu = 256;
@@ -361,7 +373,8 @@ qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t
     return t;
   };
   const int tt = T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : 8;
-  const GemvPlan plan = plan_gemv(nc, n_cu, xmode, 0, tasks_for, tt);
+  // the RMSNorm partial sums take one LDS float per wave
+  const GemvPlan plan = plan_gemv(nc, n_cu, xmode, gamma ? kMaxWaves : 0, tasks_for, tt);
   if (plan.waves == 0)
     return fail(QINT4_ERR_SHAPE, "%s: k_in %lld with T = %lld needs more than %d bytes of LDS", fn,
                 (long long)k_in, (long long)T, kMaxLds);
@@ -386,6 +399,8 @@ qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t
   set_geometry(p, plan, nc, nc, k_in / 2, sbrow, ws[0].group_size);
   p.y_bf16 = y_dtype == QINT4_BF16;
   p.x = x;
+  p.gamma = gamma;
+  p.eps = eps;
   p.n_tok = (int32_t)T;
   p.ldx = (int32_t)ldx;
   p.ids = nullptr;
@@ -415,6 +430,15 @@ qint4_status qgemv_int4_multi(int32_t n, const qint4_matrix *ws, const void *x, 
                               void *const *ys, int32_t y_dtype, int32_t epilogue, void *stream) {
   return run_multi(n, ws, x, x_dtype, 1, (n >= 1 && ws) ? ws[0].k_in : 0, ys, y_dtype, epilogue,
                    reinterpret_cast<hipStream_t>(stream), "qgemv_int4_multi");
+}
+
+qint4_status rms_norm_qgemv_int4(int32_t n, const qint4_matrix *ws, const void *x,
+                                 int32_t x_dtype, const void *gamma, float eps,
+                                 void *const *ys, int32_t y_dtype, int32_t epilogue,
+                                 void *stream) {
+  if (!gamma) return fail(QINT4_ERR_NULL, "rms_norm_qgemv_int4: gamma is NULL");
+  return run_multi(n, ws, x, x_dtype, 1, (n >= 1 && ws) ? ws[0].k_in : 0, ys, y_dtype, epilogue,
+                   reinterpret_cast<hipStream_t>(stream), "rms_norm_qgemv_int4", gamma, eps);
 }
 
 qint4_status qgemv_int4_smallm(int32_t n, const qint4_matrix *ws, const void *x, int32_t x_dtype,

@@ -11,7 +11,15 @@ constexpr int kMaxMats = 8;    // projections per multi call
 constexpr int kMaxTopK = 8;    // experts combined per MoE call
 constexpr int kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
 
-enum XMode { XM_BF16 = 0, XM_F32 = 1 };
+// Activation staging / compute modes of the GEMV family.  XM_RMS_*: the
+// activation is RMS-normalised on the way in -- x and gamma (both bf16, or
+// both float32) are staged as the float32 products x * gamma, the sum of x^2
+// is reduced over the workgroup, and results are scaled by
+// 1 / sqrt(sum(x^2) / k_in + eps) before the epilogue.
+enum XMode { XM_BF16 = 0, XM_F32 = 1, XM_RMS_BF16 = 2, XM_RMS_F32 = 3 };
+constexpr bool xm_rms(int xm) { return xm == XM_RMS_BF16 || xm == XM_RMS_F32; }
+// Octets (8 activation elements) one thread stages per round.
+constexpr int xm_octets(int xm) { return xm == XM_BF16 ? 2 : xm == XM_F32 ? 5 : xm == XM_RMS_BF16 ? 4 : 3; }
 enum Epi { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_MOE_DOWN = 2 };
 
 // One matrix (or expert stack) as the GEMV kernels see it.
@@ -61,11 +69,12 @@ struct GemvParams {
   uint32_t code_bytes;       // EPI_MOE_DOWN: code bytes of the whole stack (< 2^31)
   uint32_t sb_bytes;         // EPI_MOE_DOWN: scale bytes of the whole stack
   int32_t ldx;               // elements between consecutive activation rows
-  int32_t pad1_;
+  float eps;                 // XM_RMS_*: RMSNorm epsilon
   const void *x;             // activation (bf16 bits or float32), 16-byte aligned
   const uint32_t *ids;       // device [top_k] or nullptr
   const float *wts;          // device [top_k] (EPI_MOE_DOWN)
   const void *residual;      // device [n_out] or nullptr (EPI_MOE_DOWN)
+  const void *gamma;         // XM_RMS_*: RMSNorm weight [k_in], the activation's dtype
 };
 
 struct GemvPlan {
@@ -79,13 +88,16 @@ struct GemvPlan {
   size_t lds_bytes;
 };
 
-// Launch one GEMV-family kernel.  `xmode`: XM_BF16 or XM_F32 staging;
+static_assert(sizeof(GemvParams) <= 512, "GEMV kernel arguments exceed 8 cache lines");
+
+// Launch one GEMV-family kernel.  `xmode`: an XMode;
 // `sb_bf16`: scales/biases element type; `epi`: Epi.
 hipError_t launch_gemv(const GemvParams &p, const GemvPlan &plan, int xmode, int sb_bf16,
                        int epi, hipStream_t stream);
 
 // LDS bytes a GEMV launch needs: per token, the staged activation (padded to
-// ncx_pad chunks) and its chunk sums; then (MoE down) the float32 residual row.
+// ncx_pad chunks) and its chunk sums; then (MoE down) the float32 residual row
+// or (XM_RMS_*) one float per wave.
 size_t gemv_lds_bytes(int xmode, int ncx_pad, int64_t residual_rows, int tt = 1);
 
 // Largest token count of one small-M GEMV launch.

@@ -15,6 +15,11 @@
 //              (per-thread accumulator with the slot scalar folded in, reduced
 //              across threads at the end); scalarFMAChain8.
 //   [FFAI #9]  thewafflehaus/FFAI pull 9, "Everything Bagel": fused swiglu.
+//   [FFAI #14] also: the RMSNorm-fused qgemv wrappers (the normalised
+//              activation goes straight into the dequant GEMV, one launch).
+//   [ds4 #844] antirez/ds4 pull 844, "Ornith 1.5 + Qwen 3.8 27B hybrid
+//              runtime + DFlash speculative decoding on Metal", commit making
+//              both norm kernels use 1 / sqrt(mean + eps) rather than rsqrt.
 //
 // Work decomposition (gfx950 specific, not from the pages):
 //   * A row is split into 32-code chunks (16 bytes of codes = one 128-bit
@@ -50,6 +55,11 @@
 //     reads that expert's codes, and folds the slot weight into its
 //     accumulator (the scalar FMA of that slot), before the lanes are reduced
 //     and the residual added.
+//   * RMSNorm prologue (XM_RMS_*): the staged activation is x * gamma in
+//     float32 and every workgroup reduces sum(x^2) over the whole row while
+//     staging it; since the norm is one scalar per row,
+//       W (x * gamma / rms) = (W (x * gamma)) / rms,
+//     the row sums are scaled by 1 / sqrt(sum(x^2) / k_in + eps) at the end.
 //   * Row sums are reduced across the L lanes with DPP (quad_perm,
 //     row_half_mirror, row_mirror) and the gfx950 permlane16/32 swaps.
 //   * Every memory access is a raw buffer load: an offset at or beyond the
@@ -260,20 +270,25 @@ __device__ __forceinline__ float sb_value(uint32_t bits) {
 // any code load is issued, so every wait the compiler places after them
 // stays exact.
 template <int XM>
-constexpr int xq() { return XM == XM_BF16 ? 2 : 5; }
+constexpr int xq() { return xm_octets(XM); }
+// Bytes of one octet of the input activation (and of gamma).
 template <int XM>
-constexpr uint32_t octet_bytes() { return XM == XM_BF16 ? 16u : 32u; }
+constexpr uint32_t octet_bytes() { return (XM == XM_BF16 || XM == XM_RMS_BF16) ? 16u : 32u; }
+// 16-byte vectors loaded per octet: the activation's, then (XM_RMS_*) gamma's.
+template <int XM>
+constexpr int octet_vecs() { return XM == XM_BF16 ? 1 : XM == XM_F32 || XM == XM_RMS_BF16 ? 2 : 4; }
 
 template <int XM>
 struct XRegs {
-  uint4 v[xq<XM>()][XM == XM_BF16 ? 1 : 2];
+  uint4 v[xq<XM>()][octet_vecs<XM>()];
 };
 
-// Writes octet o (values in v) to the LDS planes and its chunk sum.  Must be
-// called by whole quads of lanes (the four octets of a chunk are in one quad).
+// Writes octet o (values in v) to the LDS planes and its chunk sum; XM_RMS_*
+// add the octet's sum of x^2 to ssq.  Must be called by whole quads of lanes
+// (the four octets of a chunk are in one quad).
 template <int XM>
 __device__ __forceinline__ void stage_store(int o, const uint4 *v, int ncx_pad, unsigned char *xbuf,
-                                            float *xsum) {
+                                            float *xsum, float &ssq) {
   const int c = o >> 2, jj = o & 3;
   float s;
   if constexpr (XM == XM_BF16) {
@@ -287,22 +302,54 @@ __device__ __forceinline__ void stage_store(int o, const uint4 *v, int ncx_pad, 
     s = ((bf16_lo(w.x) + bf16_hi(w.x)) + (bf16_lo(w.y) + bf16_hi(w.y))) +
         ((bf16_lo(w.z) + bf16_hi(w.z)) + (bf16_lo(w.w) + bf16_hi(w.w)));
   } else {
-    const float4 a = __builtin_bit_cast(float4, v[0]);
-    const float4 b = __builtin_bit_cast(float4, v[1]);
-    reinterpret_cast<float4 *>(xbuf)[(2 * jj) * ncx_pad + c] = make_float4(a.x, a.z, b.x, b.z);
-    reinterpret_cast<float4 *>(xbuf)[(2 * jj + 1) * ncx_pad + c] = make_float4(a.y, a.w, b.y, b.w);
-    s = ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
+    float e[8];  // the octet's staged values, element order
+    if constexpr (XM == XM_F32) {
+      const float4 a = __builtin_bit_cast(float4, v[0]);
+      const float4 b = __builtin_bit_cast(float4, v[1]);
+      e[0] = a.x; e[1] = a.y; e[2] = a.z; e[3] = a.w;
+      e[4] = b.x; e[5] = b.y; e[6] = b.z; e[7] = b.w;
+    } else {
+      float xe[8], ge[8];
+      if constexpr (XM == XM_RMS_F32) {
+        const float4 xa = __builtin_bit_cast(float4, v[0]), xb = __builtin_bit_cast(float4, v[1]);
+        const float4 ga = __builtin_bit_cast(float4, v[2]), gb = __builtin_bit_cast(float4, v[3]);
+        xe[0] = xa.x; xe[1] = xa.y; xe[2] = xa.z; xe[3] = xa.w;
+        xe[4] = xb.x; xe[5] = xb.y; xe[6] = xb.z; xe[7] = xb.w;
+        ge[0] = ga.x; ge[1] = ga.y; ge[2] = ga.z; ge[3] = ga.w;
+        ge[4] = gb.x; ge[5] = gb.y; ge[6] = gb.z; ge[7] = gb.w;
+      } else {  // XM_RMS_BF16: bf16 products and squares are exact in float32
+        const uint32_t xw[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
+        const uint32_t gw[4] = {v[1].x, v[1].y, v[1].z, v[1].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          xe[2 * i] = bf16_lo(xw[i]);
+          xe[2 * i + 1] = bf16_hi(xw[i]);
+          ge[2 * i] = bf16_lo(gw[i]);
+          ge[2 * i + 1] = bf16_hi(gw[i]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        ssq = fmaf(xe[i], xe[i], ssq);
+        e[i] = xe[i] * ge[i];
+      }
+    }
+    reinterpret_cast<float4 *>(xbuf)[(2 * jj) * ncx_pad + c] = make_float4(e[0], e[2], e[4], e[6]);
+    reinterpret_cast<float4 *>(xbuf)[(2 * jj + 1) * ncx_pad + c] = make_float4(e[1], e[3], e[5], e[7]);
+    s = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
   }
   s += dpp_mov<0xB1>(s);
   s += dpp_mov<0x4E>(s);
   if (jj == 0) xsum[c] = s;
 }
 
+// gamma: XM_RMS_* only (the RMSNorm weight, same layout as x).
 template <int XM>
-__device__ __forceinline__ void stage_issue(const void *__restrict__ x, int ncx, int base,
-                                            XRegs<XM> &r) {
+__device__ __forceinline__ void stage_issue(const void *__restrict__ x, const void *__restrict__ gamma,
+                                            int ncx, int base, XRegs<XM> &r) {
   const uint32_t nocts = (uint32_t)ncx * 4;
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, nocts * octet_bytes<XM>());
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(xm_rms(XM) ? gamma : x, nocts * octet_bytes<XM>());
 #pragma unroll
   for (int i = 0; i < xq<XM>(); ++i) {
     // unconditional loads (a load inside a branch makes the compiler copy its
@@ -310,19 +357,24 @@ __device__ __forceinline__ void stage_issue(const void *__restrict__ x, int ncx,
     // are out of range
     const uint32_t o = base + threadIdx.x + i * blockDim.x;
     const uint32_t off = o < nocts ? o * octet_bytes<XM>() : kOutOfRange;
-    r.v[i][0] = buf_load_b128(rx, off);
-    if constexpr (XM == XM_F32) r.v[i][1] = buf_load_b128(rx, off + 16);
+    constexpr int XV = xm_rms(XM) ? octet_vecs<XM>() / 2 : octet_vecs<XM>();  // vectors of x
+#pragma unroll
+    for (int k = 0; k < XV; ++k) r.v[i][k] = buf_load_b128(rx, off + 16 * k);
+    if constexpr (xm_rms(XM)) {
+#pragma unroll
+      for (int k = 0; k < XV; ++k) r.v[i][XV + k] = buf_load_b128(rg, off + 16 * k);
+    }
   }
 }
 
 template <int XM>
 __device__ __forceinline__ void stage_commit(int ncx, int ncx_pad, int base, const XRegs<XM> &r,
-                                             unsigned char *xbuf, float *xsum) {
+                                             unsigned char *xbuf, float *xsum, float &ssq) {
   const int nocts = ncx * 4;
 #pragma unroll
   for (int i = 0; i < xq<XM>(); ++i) {
     const int o = base + threadIdx.x + i * blockDim.x;
-    if (o < nocts) stage_store<XM>(o, r.v[i], ncx_pad, xbuf, xsum);
+    if (o < nocts) stage_store<XM>(o, r.v[i], ncx_pad, xbuf, xsum, ssq);
   }
 }
 
@@ -337,22 +389,26 @@ __device__ __forceinline__ int stage_last_base(int ncx) {
 
 // All staging rounds but the last, each loaded and stored before the next.
 template <int XM>
-__device__ __forceinline__ void stage_early_rounds(const void *__restrict__ x, int ncx, int ncx_pad,
-                                                   unsigned char *xbuf, float *xsum) {
+__device__ __forceinline__ void stage_early_rounds(const void *__restrict__ x, const void *__restrict__ gamma,
+                                                   int ncx, int ncx_pad, unsigned char *xbuf,
+                                                   float *xsum, float &ssq) {
   const int last = stage_last_base<XM>(ncx);
   for (int base = 0; base < last; base += xq<XM>() * blockDim.x) {
     XRegs<XM> r;
-    stage_issue<XM>(x, ncx, base, r);
-    stage_commit<XM>(ncx, ncx_pad, base, r, xbuf, xsum);
+    stage_issue<XM>(x, gamma, ncx, base, r);
+    stage_commit<XM>(ncx, ncx_pad, base, r, xbuf, xsum, ssq);
   }
 }
 
 // Zero chunks ncx .. ncx_pad-1 (whole quads: the padding is whole chunks).
 template <int XM>
-__device__ __forceinline__ void stage_padding(int ncx, int ncx_pad, unsigned char *xbuf, float *xsum) {
+__device__ __forceinline__ void stage_padding(int ncx, int ncx_pad, unsigned char *xbuf, float *xsum,
+                                              float &ssq) {
   for (int o = ncx * 4 + threadIdx.x; o < ncx_pad * 4; o += blockDim.x) {
-    const uint4 z[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
-    stage_store<XM>(o, z, ncx_pad, xbuf, xsum);
+    uint4 z[octet_vecs<XM>()];
+#pragma unroll
+    for (int k = 0; k < octet_vecs<XM>(); ++k) z[k] = make_uint4(0, 0, 0, 0);
+    stage_store<XM>(o, z, ncx_pad, xbuf, xsum, ssq);
   }
 }
 
@@ -431,6 +487,7 @@ __global__ void __launch_bounds__(TT >= 8 ? 512 : 768) qgemv_kernel(const GemvPa
   constexpr int NS = (EPI == EPI_SWIGLU) ? 2 : 1;  // code streams per row (gate, up)
   constexpr int D = kSlots / (RT * NS);            // steps in flight
   constexpr int XB = (XM == XM_BF16) ? 64 : 128;   // staged bytes per chunk
+  static_assert(!xm_rms(XM) || (TT == 1 && EPI != EPI_MOE_DOWN), "RMSNorm prologue: one token");
   constexpr uint32_t SBB = (SBT == 1) ? 2 : 4;     // bytes per scale/bias
 
   const int lane = threadIdx.x & 63;
@@ -452,7 +509,7 @@ __global__ void __launch_bounds__(TT >= 8 ? 512 : 768) qgemv_kernel(const GemvPa
   const int S = (p.tasks_q + (gw < p.tasks_r ? 1 : 0)) * spt;  // steps of this wave
 
   // LDS: per token, chunk sums then the staged activation; then (MoE down)
-  // the float32 residual row
+  // the float32 residual row, or (XM_RMS_*) one partial sum of x^2 per wave
   const int xs_bytes = (ncx_pad * 4 + 15) & ~15;
   const int tok_bytes = xs_bytes + ncx_pad * XB;
   float *xsum = reinterpret_cast<float *>(smem);
@@ -622,15 +679,17 @@ __global__ void __launch_bounds__(TT >= 8 ? 512 : 768) qgemv_kernel(const GemvPa
   auto x_tok = [&](int t) {
     return reinterpret_cast<const unsigned char *>(p.x) + (size_t)t * p.ldx * (XM == XM_BF16 ? 2 : 4);
   };
+  float ssq = 0.f;  // XM_RMS_*: this thread's share of sum(x^2)
 #pragma unroll
   for (int t = 0; t < TT; ++t)
-    stage_early_rounds<XM>(x_tok(t), t < p.n_tok ? p.ncx : 0, ncx_pad, xbuf + t * tok_bytes,
-                           reinterpret_cast<float *>(reinterpret_cast<unsigned char *>(xsum) + t * tok_bytes));
+    stage_early_rounds<XM>(x_tok(t), p.gamma, t < p.n_tok ? p.ncx : 0, ncx_pad, xbuf + t * tok_bytes,
+                           reinterpret_cast<float *>(reinterpret_cast<unsigned char *>(xsum) + t * tok_bytes),
+                           ssq);
   const int xbase = stage_last_base<XM>(p.ncx);
   XRegs<XM> xr[TT];
 #pragma unroll
   for (int t = 0; t < TT; ++t)  // activation loads first (L2), ...
-    stage_issue<XM>(x_tok(t), t < p.n_tok ? p.ncx : 0, xbase, xr[t]);
+    stage_issue<XM>(x_tok(t), p.gamma, t < p.n_tok ? p.ncx : 0, xbase, xr[t]);
   uint4 rr[RQ];
   const bool has_res = (EPI == EPI_MOE_DOWN) && p.residual != nullptr;
   if constexpr (EPI == EPI_MOE_DOWN) {
@@ -646,11 +705,23 @@ __global__ void __launch_bounds__(TT >= 8 ? 512 : 768) qgemv_kernel(const GemvPa
 #pragma unroll
   for (int t = 0; t < TT; ++t) {
     float *xs_t = reinterpret_cast<float *>(reinterpret_cast<unsigned char *>(xsum) + t * tok_bytes);
-    stage_commit<XM>(p.ncx, ncx_pad, xbase, xr[t], xbuf + t * tok_bytes, xs_t);
-    stage_padding<XM>(p.ncx, ncx_pad, xbuf + t * tok_bytes, xs_t);
+    stage_commit<XM>(p.ncx, ncx_pad, xbase, xr[t], xbuf + t * tok_bytes, xs_t, ssq);
+    stage_padding<XM>(p.ncx, ncx_pad, xbuf + t * tok_bytes, xs_t, ssq);
   }
   if (has_res) residual_commit((int)p.m[0].n_out, p.y_bf16, rr, res_lds);
+  if constexpr (xm_rms(XM)) {
+    const float wave_ssq = seg_sum(ssq, 6);
+    if (lane == 0) res_lds[wave] = wave_ssq;
+  }
   lds_barrier();
+
+  // RMSNorm: every wave sums the per-wave partials in the same order
+  float inv_rms = 1.f;
+  if constexpr (xm_rms(XM)) {
+    float tot = 0.f;
+    for (int wv = 0; wv < p.waves_per_wg; ++wv) tot += res_lds[wv];
+    inv_rms = 1.f / sqrtf(tot / (float)(p.ncx * 32) + p.eps);
+  }
 
   // ---- consume stream ----
   float acc[TT][NS][RT];
@@ -671,7 +742,10 @@ __global__ void __launch_bounds__(TT >= 8 ? 512 : 768) qgemv_kernel(const GemvPa
 #pragma unroll
       for (int s = 0; s < NS; ++s)
 #pragma unroll
-        for (int r = 0; r < RT; ++r) acc[t][s][r] = seg_sum(acc[t][s][r], l2);
+        for (int r = 0; r < RT; ++r) {
+          acc[t][s][r] = seg_sum(acc[t][s][r], l2);
+          if constexpr (xm_rms(XM)) acc[t][s][r] *= inv_rms;
+        }
       if (j == 0) {
         // token t's output row: y + t * n_rows elements
         void *yt = cc.y + (size_t)t * cc.n_rows * (p.y_bf16 ? 2 : 4);
@@ -782,6 +856,16 @@ hipError_t launch_one(const GemvParams &p, const GemvPlan &plan, hipStream_t str
 template <int RT, int EPI>
 hipError_t launch_sel(const GemvParams &p, const GemvPlan &plan, int xmode, int sb_bf16,
                       hipStream_t s) {
+  if constexpr (EPI != EPI_MOE_DOWN) {
+    if (xmode == XM_RMS_BF16)
+      return sb_bf16 ? launch_one<RT, XM_RMS_BF16, 1, EPI>(p, plan, s)
+                     : launch_one<RT, XM_RMS_BF16, 0, EPI>(p, plan, s);
+    if (xmode == XM_RMS_F32)
+      return sb_bf16 ? launch_one<RT, XM_RMS_F32, 1, EPI>(p, plan, s)
+                     : launch_one<RT, XM_RMS_F32, 0, EPI>(p, plan, s);
+  } else if (xm_rms(xmode)) {
+    return hipErrorInvalidValue;
+  }
   if (EPI == EPI_MOE_DOWN || xmode == XM_F32)
     return sb_bf16 ? launch_one<RT, XM_F32, 1, EPI>(p, plan, s) : launch_one<RT, XM_F32, 0, EPI>(p, plan, s);
   return sb_bf16 ? launch_one<RT, XM_BF16, 1, EPI>(p, plan, s) : launch_one<RT, XM_BF16, 0, EPI>(p, plan, s);

@@ -88,7 +88,8 @@ typedef enum qint4_status {
   QINT4_ERR_ALIAS = 5,      /* an output overlaps an input                     */
   QINT4_ERR_WORKSPACE = 6,  /* workspace NULL or smaller than required         */
   QINT4_ERR_DEVICE = 7,     /* no current gfx950 device                        */
-  QINT4_ERR_LAUNCH = 8      /* the HIP runtime rejected a kernel launch        */
+  QINT4_ERR_LAUNCH = 8,     /* the HIP runtime rejected a kernel launch        */
+  QINT4_ERR_VALUE = 9       /* a scalar argument is outside its valid range    */
 } qint4_status;
 
 /* One packed matrix, or a stack of n_experts matrices of the same shape. */
@@ -167,6 +168,35 @@ qint4_status qgemv_int4_multi(int32_t n, const qint4_matrix *ws, const void *x,
 qint4_status qgemv_int4_smallm(int32_t n, const qint4_matrix *ws, const void *x,
                                int32_t x_dtype, int64_t T, int64_t ldx, void *const *ys,
                                int32_t y_dtype, int32_t epilogue, void *stream);
+
+/*
+ * rms_norm_qgemv_int4 -- qgemv_int4_multi of the RMS-normalised input, in
+ * the same single launch:
+ *
+ *   ys[i] = W_i xn,   xn[k] = x[k] * gamma[k] / sqrt(mean_k(x[k]^2) + eps)
+ *
+ * (SWIGLU_PAIR: ys[0] = silu(W_0 xn) * (W_1 xn)).
+ *
+ * [FFAI #14], commit wrapping the RMSNorm-fused qgemv: the normalised
+ * activation is fed straight into the int4 dequant GEMV instead of a norm
+ * launch followed by a GEMV launch, saving the round trip of the normalised
+ * vector through memory (used for the final norm + LM head, and for any
+ * pre-norm -> int4 projection).  [ds4 #844], commit unifying the norm
+ * kernels: the normaliser is 1 / sqrt(mean + eps).
+ *
+ * The normalised vector is never rounded: the kernel stages x * gamma in
+ * float32 (exact for bf16 inputs), reduces sum(x^2) in float32, and scales
+ * the float32 row sums by 1 / sqrt(sum / k_in + eps) -- the same value, since
+ * the norm is one scalar per input row.
+ *
+ *   gamma   device [k_in], dtype x_dtype, 16-byte aligned (the norm weight)
+ *   eps     finite, > 0 (QINT4_ERR_VALUE otherwise)
+ *   other arguments as in qgemv_int4_multi (one activation row)
+ */
+qint4_status rms_norm_qgemv_int4(int32_t n, const qint4_matrix *ws, const void *x,
+                                 int32_t x_dtype, const void *gamma, float eps,
+                                 void *const *ys, int32_t y_dtype, int32_t epilogue,
+                                 void *stream);
 
 /*
  * Bytes of device workspace one moe_gather_qgemv_int4 call needs for an

@@ -175,6 +175,43 @@ def multi(ws: Sequence, x: np.ndarray, x_dtype: str, threads: int = 1):
 
 
 # --------------------------------------------------------------------------
+# RMSNorm prologue
+# --------------------------------------------------------------------------
+
+def rms_norm(x: np.ndarray, x_dtype: str, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """xn[k] = x[k] * gamma[k] / sqrt(mean_j x[j]^2 + eps) in float64.
+
+    [FFAI #14], commit wrapping the RMSNorm-fused qgemv: the normalised
+    activation feeds the int4 dequant GEMV directly.  [ds4 #844], commit
+    unifying the norm kernels: the normaliser is 1 / sqrt(mean + eps).  gamma
+    is stored in x's dtype; eps is used as given (callers pass the float32
+    value the library receives).
+    """
+    x64 = widen(x, x_dtype)
+    g64 = widen(gamma, x_dtype)
+    if x64.shape != g64.shape or x64.ndim != 1:
+        raise ValueError("x and gamma must be equal-length vectors")
+    ms = np.mean(x64 * x64)
+    return x64 * g64 / np.sqrt(ms + float(eps))
+
+
+def rms_norm_multi(ws: Sequence, x: np.ndarray, x_dtype: str, gamma: np.ndarray, eps: float,
+                   threads: int = 1):
+    """Projections of one RMS-normalised input; a list of (y, a) as in multi()."""
+    xn = rms_norm(x, x_dtype, gamma, eps)
+    return [gemv_f64(w, xn, threads=threads) for w in ws]
+
+
+def rms_norm_swiglu_pair(gate, up, x: np.ndarray, x_dtype: str, gamma: np.ndarray, eps: float,
+                         threads: int = 1):
+    """silu(gate xn) * (up xn) of the RMS-normalised input; (h, a_h) as in swiglu_pair()."""
+    xn = rms_norm(x, x_dtype, gamma, eps)
+    g, ag = gemv_f64(gate, xn, threads=threads)
+    u, au = gemv_f64(up, xn, threads=threads)
+    return swiglu(g, u), 1.1 * np.abs(u) * ag + np.abs(silu(g)) * au
+
+
+# --------------------------------------------------------------------------
 # SwiGLU, dense FFN, router, MoE
 # --------------------------------------------------------------------------
 

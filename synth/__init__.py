@@ -118,6 +118,12 @@ def draw_activation(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
     return a if dtype == F32 else f32_to_bf16_bits(a)
 
 
+def draw_norm_weight(rng: np.random.Generator, n: int, dtype: str) -> np.ndarray:
+    """RMSNorm weight [n]: uniform in [0.5, 1.5], stored in dtype (bf16 as bits)."""
+    g = rng.uniform(0.5, 1.5, size=n).astype(np.float32)
+    return g if dtype == F32 else f32_to_bf16_bits(g)
+
+
 # --------------------------------------------------------------------------
 # Workload recipes.  Default sizes are the decode/prefill shapes measured;
 # tests pass smaller sizes to the same recipes.
@@ -139,6 +145,18 @@ def qkv_multi(seed: int = 1, hidden: int = 4096, outs=(4096, 1024, 1024), group_
     ws = [draw_matrix(rng, n, hidden, group_size, BF16, keep_raw=keep_raw) for n in outs]
     x = draw_activation(rng, (hidden,), BF16)
     return {"ws": ws, "x": x, "x_dtype": BF16}
+
+
+def rms_qkv(seed: int = 5, hidden: int = 4096, outs=(4096, 1024, 1024), group_size: int = 64,
+            eps: float = 1e-6) -> dict:
+    """The q/k/v projection set behind an RMSNorm of its bf16 input: the qkv_multi
+    recipe, then the norm weight (bf16, uniform in [0.5, 1.5]); eps is the
+    float32 value passed to the library."""
+    rng = np.random.default_rng(seed)
+    ws = [draw_matrix(rng, n, hidden, group_size, BF16) for n in outs]
+    x = draw_activation(rng, (hidden,), BF16)
+    gamma = draw_norm_weight(rng, hidden, BF16)
+    return {"ws": ws, "x": x, "gamma": gamma, "eps": float(np.float32(eps)), "x_dtype": BF16}
 
 
 def dense_layer(seed: int = 2, hidden: int = 5120, inter: int = 17408, group_size: int = 64,

@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(9):
+    for code in range(10):
         assert lib.qint4_status_string(code)
     assert lib.qint4_status_string(99) == b"unknown status"
 
@@ -148,6 +148,26 @@ def test_smallm_validation(lib):
     assert _smallm(lib, _m(), ldx=260) == 2                    # ldx not a multiple of 8
     assert _smallm(lib, _m(), y=A + 0x300000 + 2 * 512) == 5   # y overlaps row 2 of x
     assert _smallm(lib, _m(), n=0) == 2
+
+
+def _rms(lib, m, n=1, x=A + 0x300000, gamma=A + 0x310000, eps=1e-6, y=A + 0x400000, xdt=1,
+         ydt=1, epi=0):
+    arr = (q.CMatrix * 2)(m, m)
+    ys = (ctypes.c_void_p * 2)(y, y + 0x10000)
+    return lib.rms_norm_qgemv_int4(n, arr, x, xdt, gamma, eps, ys, ydt, epi, None)
+
+
+def test_rms_norm_validation(lib):
+    assert _rms(lib, _m(), gamma=0) == 1 and "gamma" in _err(lib)
+    assert _rms(lib, _m(), gamma=A + 0x310008) == 4              # gamma misaligned
+    assert _rms(lib, _m(), eps=0.0) == 9 and "eps" in _err(lib)
+    assert _rms(lib, _m(), eps=-1e-6) == 9
+    assert _rms(lib, _m(), eps=float("nan")) == 9
+    assert _rms(lib, _m(), eps=float("inf")) == 9
+    assert _rms(lib, _m(), y=A + 0x310000 + 64) == 5             # y overlaps gamma
+    assert _rms(lib, _m(), n=0) == 2
+    assert _rms(lib, _m(), xdt=7) == 3
+    assert _rms(lib, _m(), n=1, epi=1) == 2                      # SwiGLU needs two matrices
 
 
 def _router(lib, logits=A + 0x300000, dt=0, n_tokens=1, n_experts=128, top_k=8, ids=A + 0x400000,

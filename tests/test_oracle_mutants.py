@@ -133,7 +133,31 @@ def _combine_unweighted(residual64, scalars, values):
     return out
 
 
+def _rms_sum_not_mean(x, x_dtype, gamma, eps):
+    x64, g64 = oracle.widen(x, x_dtype), oracle.widen(gamma, x_dtype)
+    return x64 * g64 / np.sqrt(np.sum(x64 * x64) + eps)
+
+
+def _rms_eps_outside_sqrt(x, x_dtype, gamma, eps):
+    x64, g64 = oracle.widen(x, x_dtype), oracle.widen(gamma, x_dtype)
+    return x64 * g64 / (np.sqrt(np.mean(x64 * x64)) + eps)
+
+
+def _rms_no_gamma(x, x_dtype, gamma, eps):
+    x64 = oracle.widen(x, x_dtype)
+    return x64 / np.sqrt(np.mean(x64 * x64) + eps)
+
+
+def _rms_no_sqrt(x, x_dtype, gamma, eps):
+    x64, g64 = oracle.widen(x, x_dtype), oracle.widen(gamma, x_dtype)
+    return x64 * g64 / (np.mean(x64 * x64) + eps)
+
+
 PY_MUTANTS = [
+    ("rms_sum_not_mean", "rms_norm", _rms_sum_not_mean),
+    ("rms_eps_outside_sqrt", "rms_norm", _rms_eps_outside_sqrt),
+    ("rms_no_gamma", "rms_norm", _rms_no_gamma),
+    ("rms_no_sqrt", "rms_norm", _rms_no_sqrt),
     ("router_tiebreak_index_desc", "router_topk", _router_desc_index_tiebreak),
     ("router_not_renormalised", "router_topk", _router_no_renorm),
     ("silu_is_sigmoid", "silu", _silu_sigmoid_only),
@@ -142,6 +166,10 @@ PY_MUTANTS = [
 ]
 
 PY_PINS = [
+    (pins.test_rms_norm_bruteforce_exact_rational, {}),
+    (pins.test_rms_norm_unit_rms_and_scale_invariance, {}),
+    (pins.test_rms_norm_one_hot_selects_scaled_column, {}),
+    (pins.test_rms_norm_eps_inside_square_root, {}),
     (pins.test_router_worked_example_from_pages, {}),
     (pins.test_router_tie_break_index_ascending, {}),
     (pins.test_silu_against_scipy_expit, {}),

@@ -483,3 +483,80 @@ def test_gemm_bruteforce_small_exact():
             exact = sum(Fraction(float(Wr[o, k])) * Fraction(float(Xv[t, k])) for k in range(64))
             bound = 64 * 2.0 ** -53 * float(A[t, o])
             assert abs(Fraction(float(Y[t, o])) - exact) <= Fraction(bound)
+
+
+# --------------------------------------------------------------------------
+# RMSNorm prologue
+# --------------------------------------------------------------------------
+
+def test_rms_norm_bruteforce_exact_rational():
+    """x in {+3, -3}, eps = 7: mean(x^2) + eps = 16 is a perfect square, so
+    xn = x * gamma / 4 exactly and the normalised GEMV has an exact rational
+    value (hex-digit unpack, Fractions).  A sum in place of the mean, eps
+    outside the square root or a dropped gamma changes the result."""
+    for seed in range(20):
+        rng = np.random.default_rng(5000 + seed)
+        k_in = 64 if seed % 2 else 128
+        w = _rand_mat(rng, 8, k_in, 32 if seed % 3 == 0 else 64, synth.BF16)
+        x = (3.0 * rng.choice([-1.0, 1.0], size=k_in)).astype(np.float32)
+        gamma = rng.uniform(0.5, 1.5, size=k_in).astype(np.float32)
+        xn = oracle.rms_norm(x, synth.F32, gamma, 7.0)
+        expect = [Fraction(float(a)) * Fraction(float(g)) / 4 for a, g in zip(x, gamma)]
+        assert [Fraction(float(v)) for v in xn] == expect
+        (y, a), = oracle.rms_norm_multi([w], x, synth.F32, gamma, 7.0)
+        s = oracle.widen(w.scales, w.sb_dtype)
+        b = oracle.widen(w.biases, w.sb_dtype)
+        ys, mags = _exact_gemv(w.codes, s, b, w.group_size, [float(e) for e in expect])
+        for o in range(w.n_out):
+            bound = k_in * 2.0 ** -53 * float(mags[o])
+            assert abs(Fraction(float(y[o])) - ys[o]) <= Fraction(bound), o
+
+
+def test_rms_norm_unit_rms_and_scale_invariance():
+    """gamma = 1, eps = 0: the output has mean square 1, and scaling x by a
+    power of two leaves it unchanged (bit for bit)."""
+    rng = np.random.default_rng(31)
+    x = synth.draw_activation(rng, (4096,), synth.BF16)
+    ones = synth.f32_to_bf16_bits(np.ones(4096, np.float32))
+    xn = oracle.rms_norm(x, synth.BF16, ones, 0.0)
+    assert abs(np.mean(xn * xn) - 1.0) < 1e-14
+    x4 = synth.f32_to_bf16_bits(4.0 * synth.bf16_bits_to_f32(x))
+    assert np.array_equal(oracle.rms_norm(x4, synth.BF16, ones, 0.0), xn)
+
+
+def test_rms_norm_one_hot_selects_scaled_column():
+    """x = a e_k, eps = 0: xn = sqrt(K) sign(a) gamma_k e_k, so W xn is column k
+    of the dequantised matrix times sqrt(K) sign(a) gamma_k."""
+    rng = np.random.default_rng(32)
+    K = 256
+    w = _rand_mat(rng, 16, K, 64, synth.BF16)
+    gamma = rng.uniform(0.5, 2.0, size=K).astype(np.float32)
+    W = oracle.dequant(w)
+    for k, a in ((0, 1.5), (77, -0.25), (255, 3.0)):
+        x = np.zeros(K, np.float32)
+        x[k] = a
+        (y, _), = oracle.rms_norm_multi([w], x, synth.F32, gamma, 0.0)
+        np.testing.assert_allclose(y, 16.0 * np.sign(a) * float(gamma[k]) * W[:, k], rtol=1e-14)
+
+
+def test_rms_norm_eps_inside_square_root():
+    """When eps dominates mean(x^2) the normaliser tends to 1 / sqrt(eps)."""
+    rng = np.random.default_rng(33)
+    x = (1e-9 * rng.standard_normal(512)).astype(np.float32)
+    gamma = rng.uniform(0.5, 1.5, size=512).astype(np.float32)
+    xn = oracle.rms_norm(x, synth.F32, gamma, 4.0)
+    np.testing.assert_allclose(xn, x.astype(np.float64) * gamma / 2.0, rtol=1e-12)
+
+
+def test_rms_norm_swiglu_pair_composes():
+    """The SwiGLU variant equals silu(gate xn) * (up xn) built from the pinned parts."""
+    rng = np.random.default_rng(34)
+    gate = _rand_mat(rng, 32, 128, 64, synth.BF16)
+    up = _rand_mat(rng, 32, 128, 64, synth.BF16)
+    x = synth.draw_activation(rng, (128,), synth.BF16)
+    gamma = synth.draw_activation(rng, (128,), synth.BF16)
+    h, _ = oracle.rms_norm_swiglu_pair(gate, up, x, synth.BF16, gamma, 1e-6)
+    xn = oracle.rms_norm(x, synth.BF16, gamma, 1e-6)
+    g = oracle.dequant(gate) @ xn
+    u = oracle.dequant(up) @ xn
+    np.testing.assert_allclose(h, g / (1.0 + np.exp(-g)) * u, rtol=1e-12, atol=1e-300)
