@@ -21,6 +21,7 @@ Workloads (default: qkv):
   moe      top-8 of 128 experts, hidden 2048, inter 768, weighted combine + residual;
            each step routes its token's logits on the GPU first (--router pre-drawn: skip)
   prefill  K=5120, N=17408 dequant GEMM on bf16 MFMA (--T rows, default 256)
+  quant    the offline quantiser: 17408x5120 float32 -> g64 codes, bf16 scales/biases
 
 Prints one JSON line.  ``value`` is weight GB/s for the decode workloads and
 TFLOP/s for prefill.  ``roofline`` describes the dominant kernel, ``cpu_baseline``
@@ -51,7 +52,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="qkv",
-                    choices=["single", "qkv", "rmsqkv", "smallm", "dense", "moe", "prefill"])
+                    choices=["single", "qkv", "rmsqkv", "smallm", "dense", "moe", "prefill", "quant"])
     ap.add_argument("--T", type=int, default=None,
                     help="prefill rows (default 256) or small-M tokens (default 4)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -178,6 +179,42 @@ class RmsQKV(QKV):
 
     def step(self, i):
         self.q.rms_norm_qgemv_int4(self.pool[i % self.R], self.x, self.gamma, self.eps, self.ys)
+
+
+class Quant(Workload):
+    """The offline quantiser on the dense layer's gate matrix: 17408 x 5120 float32 weights
+    -> g64 codes with bf16 scales/biases (bytes moved: weights read + packed matrix written)."""
+    name = "quantize_17408x5120_f32_g64"
+    dominant = "quantize_kernel (min/max group affine)"
+
+    def __init__(self, q, synth, torch):
+        self.q = q
+        N, K = 17408, 5120
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(11)
+        one = N * K * 4
+        self.R = max(1, math.ceil(POOL_BYTES / one))
+        self.pool = [0.02 * torch.randn(N, K, device="cuda", generator=gen) for _ in range(self.R)]
+        self.out = q.quantize_int4(self.pool[0], 64, torch.bfloat16)
+        self.wb = one
+        self.out_bytes = self.out.weight_bytes
+        self.config = {"workload": self.name, "n_out": N, "k_in": K, "group_size": 64,
+                       "w_dtype": "f32", "sb_dtype": "bf16", "pool_copies": self.R}
+        self.dtype = "f32"
+        self.torch = torch
+
+    def weight_bytes(self):
+        return self.wb
+
+    def algo_bytes(self):
+        return self.wb + self.out_bytes
+
+    def step(self, i):
+        o = self.out
+        self.q._check(self.q.load().quantize_int4(
+            self.pool[i % self.R].data_ptr(), self.q.F32, 17408, 5120, 64, self.q.BF16,
+            o.codes.data_ptr(), o.scales.data_ptr(), o.biases.data_ptr(),
+            self.torch.cuda.current_stream().cuda_stream))
 
 
 class Dense(Workload):
@@ -360,6 +397,14 @@ def cpu_baseline(workload: str, budget_s: float, T: int):
             return oracle.moe(d["gate"], d["up"], d["down"], d["x"][0], ids, wts.astype(np.float32),
                               d["residual"][0], "bf16", threads=threads)
         sample = "one token of the 128-expert layer (seed 3): router + top-8 experts, repeated"
+    elif workload == "quant":
+        rng = np.random.default_rng(11)
+        rows = 512
+        W = synth.draw_float_weights(rng, (rows, 5120), "f32")
+        wb = W.nbytes
+        fn = lambda: oracle.quantize(W, "f32", 64, "bf16")
+        sample = "%d x 5120 rows of float32 weights per call (numpy float32, one thread)" % rows
+        threads = 1
     else:
         d = synth.prefill_gemm(T=T)
         rows = 64
@@ -419,6 +464,8 @@ def main():
         wl = QKV(q, synth, torch)
     elif args.workload == "rmsqkv":
         wl = RmsQKV(q, synth, torch)
+    elif args.workload == "quant":
+        wl = Quant(q, synth, torch)
     elif args.workload == "dense":
         wl = Dense(q, synth, torch)
     elif args.workload == "smallm":

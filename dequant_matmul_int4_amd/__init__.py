@@ -20,6 +20,7 @@ The names and arguments mirror the C entry points:
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from typing import Optional, Sequence
 
@@ -79,6 +80,7 @@ SIGNATURES = [
                                      _P, ctypes.c_size_t, _P]),
     ("qgemm_int4_padT", _I32, [ctypes.POINTER(CMatrix), _P, _I64, _I64, _P, _I64, _I32, _P]),
     ("moe_router_topk", _I32, [_P, _I32, _I64, _I32, _I32, _P, _P, _P]),
+    ("quantize_int4", _I32, [_P, _I32, _I64, _I64, _I32, _I32, _P, _P, _P, _P]),
     ("qint4_status_string", ctypes.c_char_p, [_I32]),
     ("qint4_last_error", ctypes.c_char_p, []),
     ("qint4_abi_version", _I32, []),
@@ -207,6 +209,26 @@ def rms_norm_qgemv_int4(ws: Sequence[QInt4Matrix], x: torch.Tensor, gamma: torch
                                       float(eps), ptrs, y_dt, int(epilogue), _stream(stream)))
 
 
+def quantize_int4(w: torch.Tensor, group_size: int = 64, sb_dtype: torch.dtype = torch.bfloat16,
+                  stream=None) -> QInt4Matrix:
+    """Quantise float weights [n_out][k_in] (or an expert stack [E][n_out][k_in]) on the device
+    into a new QInt4Matrix (codes from the stored scale/bias; see quantize_int4 in qint4.h)."""
+    if w.dim() not in (2, 3):
+        raise ValueError("w must be [n_out, k_in] or [E, n_out, k_in]")
+    k_in = w.shape[-1]
+    if k_in % group_size:
+        raise ValueError("k_in must be a multiple of group_size")
+    lead = tuple(w.shape[:-1])
+    codes = torch.empty(lead + (k_in // 8,), dtype=torch.int32, device=w.device)
+    scales = torch.empty(lead + (k_in // group_size,), dtype=sb_dtype, device=w.device)
+    biases = torch.empty_like(scales)
+    n_rows = math.prod(lead)
+    _check(load().quantize_int4(_dev(w, "w"), _dt(w), n_rows, k_in, int(group_size), _dt(scales),
+                                codes.data_ptr(), scales.data_ptr(), biases.data_ptr(),
+                                _stream(stream)))
+    return QInt4Matrix(codes, scales, biases, group_size)
+
+
 SMALLM_MAX = 8
 
 
@@ -304,5 +326,5 @@ def moe_router_topk(logits: torch.Tensor, top_k: int, ids: torch.Tensor, wts: to
 
 __all__ = ["QInt4Matrix", "Int4Error", "qgemv_int4", "qgemv_int4_multi", "qgemv_int4_smallm",
            "moe_gather_qgemv_int4", "moe_gather_qgemv_int4_workspace_bytes", "qgemm_int4_padT",
-           "moe_router_topk", "rms_norm_qgemv_int4",
+           "moe_router_topk", "rms_norm_qgemv_int4", "quantize_int4",
            "load", "F32", "BF16", "EPI_NONE", "EPI_SWIGLU_PAIR", "LIB_PATH", "SIGNATURES"]

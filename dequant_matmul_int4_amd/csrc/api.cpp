@@ -608,6 +608,52 @@ qint4_status moe_router_topk(const void *logits, int32_t logits_dtype, int64_t n
   return ok();
 }
 
+qint4_status quantize_int4(const void *w, int32_t w_dtype, int64_t n_rows, int64_t k_in,
+                           int32_t group_size, int32_t sb_dtype, uint32_t *codes, void *scales,
+                           void *biases, void *stream) {
+  const char *fn = "quantize_int4";
+  if (!w || !codes || !scales || !biases)
+    return fail(QINT4_ERR_NULL, "%s: w/codes/scales/biases is NULL", fn);
+  if (!valid_dtype(w_dtype)) return fail(QINT4_ERR_DTYPE, "%s: w_dtype %d invalid", fn, w_dtype);
+  if (!valid_dtype(sb_dtype)) return fail(QINT4_ERR_DTYPE, "%s: sb_dtype %d invalid", fn, sb_dtype);
+  if (group_size != 32 && group_size != 64 && group_size != 128)
+    return fail(QINT4_ERR_SHAPE, "%s: group_size %d not in {32, 64, 128}", fn, group_size);
+  if (k_in < group_size || k_in > kMaxK || k_in % group_size != 0)
+    return fail(QINT4_ERR_SHAPE, "%s: k_in %lld must be a multiple of group_size %d in [%d, 2^20]",
+                fn, (long long)k_in, group_size, group_size);
+  if (n_rows < 1 || n_rows > ((int64_t)1 << 34) / k_in)
+    return fail(QINT4_ERR_SHAPE, "%s: n_rows %lld out of range", fn, (long long)n_rows);
+  const size_t wb = elem_bytes(w_dtype), sbb = elem_bytes(sb_dtype);
+  if (!aligned(w, 16) || !aligned(codes, 16))
+    return fail(QINT4_ERR_ALIGN, "%s: w and codes must be 16-byte aligned", fn);
+  if (!aligned(scales, sbb) || !aligned(biases, sbb))
+    return fail(QINT4_ERR_ALIGN, "%s: scales/biases not aligned to %zu bytes", fn, sbb);
+  const size_t n_groups = (size_t)n_rows * (size_t)(k_in / group_size);
+  Range ins[1], outs[3];
+  ins[0] = range(w, (size_t)n_rows * k_in * wb, "w");
+  outs[0] = range(codes, (size_t)n_rows * k_in / 2, "codes");
+  outs[1] = range(scales, n_groups * sbb, "scales");
+  outs[2] = range(biases, n_groups * sbb, "biases");
+  qint4_status st = check_no_overlap(outs, 3, ins, 1);
+  if (st != QINT4_OK) return prefixed(st, fn);
+  if ((st = check_device(nullptr)) != QINT4_OK) return prefixed(st, fn);
+  // launches of whole rows spanning < 2 GiB of weights each
+  const int64_t row_bytes = k_in * (int64_t)wb;
+  const int64_t rows_per = std::max<int64_t>(1, (((int64_t)1 << 31) - 1) / row_bytes);
+  const int64_t gpr = k_in / group_size;
+  for (int64_t r0 = 0; r0 < n_rows; r0 += rows_per) {
+    const int64_t nr = std::min(rows_per, n_rows - r0);
+    hipError_t e = launch_quantize(
+        reinterpret_cast<const unsigned char *>(w) + r0 * row_bytes, w_dtype == QINT4_BF16,
+        nr * k_in / 8, group_size, sb_dtype == QINT4_BF16, codes + r0 * (k_in / 8),
+        reinterpret_cast<unsigned char *>(scales) + r0 * gpr * (int64_t)sbb,
+        reinterpret_cast<unsigned char *>(biases) + r0 * gpr * (int64_t)sbb,
+        reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(QINT4_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  }
+  return ok();
+}
+
 qint4_status qgemm_int4_padT(const qint4_matrix *w, const void *x, int64_t T, int64_t ldx, void *y,
                              int64_t ldy, int32_t y_dtype, void *stream) {
   const char *fn = "qgemm_int4_padT";

@@ -130,6 +130,12 @@ hipError_t launch_gemm(const GemmParams &p, hipStream_t stream);
 // Top-k expert routing of n_rows rows of router logits (float32 or bf16):
 // ids/wts are [n_rows][top_k].
 constexpr int kRouterMaxExperts = 4096;
+
+// Quantise n_words * 8 row-major weights (bf16 or float32; n_words * 8 * the
+// weight size < 2 GiB) into codes / scales / biases with group_size in
+// {32, 64, 128}; group g covers words g * group_size / 8 ...
+hipError_t launch_quantize(const void *w, int w_bf16, int64_t n_words, int group_size, int sb_bf16,
+                           uint32_t *codes, void *scales, void *biases, hipStream_t stream);
 hipError_t launch_router(const void *logits, int bf16, int64_t n_rows, int n_experts, int top_k,
                          uint32_t *ids, float *wts, hipStream_t stream);
 

@@ -290,6 +290,33 @@ qint4_status moe_router_topk(const void *logits, int32_t logits_dtype, int64_t n
                              int32_t n_experts, int32_t top_k, uint32_t *ids, float *wts,
                              void *stream);
 
+/*
+ * quantize_int4 -- the offline int4 group-affine quantiser: float weights
+ * [n_rows][k_in] -> codes, scales and biases in the format above.
+ *
+ * [ds4 #844], PR body (verification list): the 4-bit group-64 affine type
+ * derives its codes from the serialised bf16 scale/bias.  The pages give no
+ * other rule; this is the plain min/max affine quantiser.  Per group:
+ *
+ *   s = (max w - min w) / 15,  b = min w           (float32)
+ *   s', b' = the stored values (sb_dtype bf16: rounded to nearest even)
+ *   q = clamp(rint((w - b') / s'), 0, 15)          (float32, ties to even;
+ *                                                   q = 0 where s' == 0)
+ *
+ *   w         device [n_rows][k_in], dtype w_dtype (QINT4_F32 or QINT4_BF16),
+ *             16-byte aligned; values must be finite and their per-group
+ *             range finite in float32 (otherwise the codes are unspecified)
+ *   n_rows    rows (n_experts * n_out for an expert stack; the layouts match)
+ *   k_in      multiple of group_size, group_size in {32, 64, 128}
+ *   codes     device uint32 [n_rows][k_in/8], 16-byte aligned, overwritten
+ *   scales,   device [n_rows][k_in/group_size], dtype sb_dtype, overwritten
+ *   biases
+ * One kernel launch per 2 GiB of weights, on `stream`.
+ */
+qint4_status quantize_int4(const void *w, int32_t w_dtype, int64_t n_rows, int64_t k_in,
+                           int32_t group_size, int32_t sb_dtype, uint32_t *codes, void *scales,
+                           void *biases, void *stream);
+
 /* Static description of a status code. */
 const char *qint4_status_string(int32_t status);
 

@@ -341,6 +341,53 @@ def moe(gate, up, down, x: np.ndarray, ids: Sequence[int], wts: Sequence[float],
 
 
 # --------------------------------------------------------------------------
+# quantiser
+# --------------------------------------------------------------------------
+
+def _bf16_bits_of(v32: np.ndarray) -> np.ndarray:
+    """Bit patterns of float32 values that are already bfloat16 values (upper halves)."""
+    return (np.ascontiguousarray(v32, dtype=np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def quantize(w: np.ndarray, w_dtype: str, group_size: int, sb_dtype: str):
+    """Min/max group-affine int4 quantiser.  Returns (codes uint32 [..., k_in/8],
+    scales, biases [..., k_in/group_size] stored in sb_dtype, bf16 as bits).
+
+    [ds4 #844], PR body (verification list): the codes come from the stored
+    (bf16-rounded) scale and bias.  Per group: s = (max - min) / 15, b = min,
+    s' and b' their stored values, q = clamp(rint((w - b') / s'), 0, 15)
+    (0 where s' == 0).  The integer decision is taken in float32, the
+    precision the device kernel computes it in: numpy float32 subtraction and
+    division are IEEE operations rounded to nearest, and rint rounds ties to
+    even.
+    """
+    w32 = widen(w, w_dtype).astype(np.float32)  # exact: the stored values
+    k_in = w32.shape[-1]
+    if k_in % group_size:
+        raise ValueError("k_in must be a multiple of group_size")
+    G = w32.reshape(w32.shape[:-1] + (k_in // group_size, group_size))
+    lo = G.min(axis=-1)
+    hi = G.max(axis=-1)
+    s = (hi - lo) / np.float32(15.0)
+    b = lo
+    if sb_dtype == BF16:
+        s = round_bf16(s.astype(np.float64)).astype(np.float32)
+        b = round_bf16(b.astype(np.float64)).astype(np.float32)
+    sn, bn = s[..., None], b[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = np.rint((G - bn) / np.where(sn > 0, sn, np.float32(1.0)))
+    q = np.where(sn > 0, np.clip(t, 0, 15), 0).astype(np.uint32).reshape(w32.shape)
+    # pack: code k of a row at bits 4 * (k % 8) of word k // 8
+    qw = q.reshape(q.shape[:-1] + (k_in // 8, 8))
+    codes = np.zeros(qw.shape[:-1], dtype=np.uint32)
+    for k in range(8):
+        codes |= qw[..., k] << np.uint32(4 * k)
+    if sb_dtype == BF16:
+        return codes, _bf16_bits_of(s), _bf16_bits_of(b)
+    return codes, s.astype(np.float32), b.astype(np.float32)
+
+
+# --------------------------------------------------------------------------
 # prefill GEMM
 # --------------------------------------------------------------------------
 

@@ -118,6 +118,12 @@ def draw_activation(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
     return a if dtype == F32 else f32_to_bf16_bits(a)
 
 
+def draw_float_weights(rng: np.random.Generator, shape, dtype: str, std: float = 0.02) -> np.ndarray:
+    """Unquantised weights N(0, std^2) (the quantiser's input), float32 or bf16 bits."""
+    a = (std * rng.standard_normal(size=shape)).astype(np.float32)
+    return a if dtype == F32 else f32_to_bf16_bits(a)
+
+
 def draw_norm_weight(rng: np.random.Generator, n: int, dtype: str) -> np.ndarray:
     """RMSNorm weight [n]: uniform in [0.5, 1.5], stored in dtype (bf16 as bits)."""
     g = rng.uniform(0.5, 1.5, size=n).astype(np.float32)

@@ -196,3 +196,22 @@ def test_valid_call_without_device_reports_device_error(lib):
         pytest.skip("a GPU is present; fake pointers must never reach a launch")
     assert _gemv(lib, _m()) == 7
     assert "device" in _err(lib)
+
+
+def _quant(lib, w=A, wdt=0, n_rows=64, k_in=256, g=64, sbdt=1, codes=A + 0x100000,
+           scales=A + 0x200000, biases=A + 0x210000):
+    return lib.quantize_int4(w, wdt, n_rows, k_in, g, sbdt, codes, scales, biases, None)
+
+
+def test_quantize_validation(lib):
+    assert _quant(lib, w=0) == 1
+    assert _quant(lib, biases=0) == 1
+    assert _quant(lib, wdt=3) == 3
+    assert _quant(lib, sbdt=2) == 3
+    assert _quant(lib, g=48) == 2
+    assert _quant(lib, k_in=96) == 2 and "k_in" in _err(lib)
+    assert _quant(lib, n_rows=0) == 2
+    assert _quant(lib, w=A + 8) == 4
+    assert _quant(lib, scales=A + 0x200001) == 4
+    assert _quant(lib, codes=A + 0x100) == 5                    # codes overlap w
+    assert _quant(lib, biases=A + 0x200000 + 64) == 5           # biases overlap scales

@@ -153,7 +153,36 @@ def _rms_no_sqrt(x, x_dtype, gamma, eps):
     return x64 * g64 / (np.mean(x64 * x64) + eps)
 
 
+def _quant_variant(denom=15.0, use_raw=False, rounder=np.rint):
+    real = oracle.quantize
+
+    def fn(w, w_dtype, group_size, sb_dtype):
+        w32 = oracle.widen(w, w_dtype).astype(np.float32)
+        G = w32.reshape(w32.shape[:-1] + (w32.shape[-1] // group_size, group_size))
+        lo, hi = G.min(-1), G.max(-1)
+        s = (hi - lo) / np.float32(denom)
+        codes, s_st, b_st = real(w, w_dtype, group_size, sb_dtype)
+        sd = oracle.widen(s_st, sb_dtype).astype(np.float32) if not use_raw else s
+        bd = oracle.widen(b_st, sb_dtype).astype(np.float32) if not use_raw else lo
+        if denom != 15.0:
+            sd = s if sb_dtype == "f32" else oracle.round_bf16(s.astype(np.float64)).astype(np.float32)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            t = rounder((G - bd[..., None]) / np.where(sd > 0, sd, 1)[..., None])
+        q = np.where(sd[..., None] > 0, np.clip(t, 0, 15), 0).astype(np.uint32).reshape(w32.shape)
+        qw = q.reshape(q.shape[:-1] + (q.shape[-1] // 8, 8))
+        c = np.zeros(qw.shape[:-1], np.uint32)
+        for k in range(8):
+            c |= qw[..., k] << np.uint32(4 * k)
+        if denom != 15.0:
+            s_st = sd if sb_dtype == "f32" else (sd.view(np.uint32) >> 16).astype(np.uint16)
+        return c, s_st, b_st
+    return fn
+
+
 PY_MUTANTS = [
+    ("quant_codes_from_raw_scale", "quantize", _quant_variant(use_raw=True)),
+    ("quant_denominator_16", "quantize", _quant_variant(denom=16.0)),
+    ("quant_floor_not_round", "quantize", _quant_variant(rounder=np.floor)),
     ("rms_sum_not_mean", "rms_norm", _rms_sum_not_mean),
     ("rms_eps_outside_sqrt", "rms_norm", _rms_eps_outside_sqrt),
     ("rms_no_gamma", "rms_norm", _rms_no_gamma),
@@ -166,6 +195,9 @@ PY_MUTANTS = [
 ]
 
 PY_PINS = [
+    (pins.test_quantize_recovers_exact_grid, {"group": 64, "sbt": "bf16"}),
+    (pins.test_quantize_picks_nearest_stored_grid_point, {"sbt": "bf16"}),
+    (pins.test_quantize_scale_spans_the_group_range, {}),
     (pins.test_rms_norm_bruteforce_exact_rational, {}),
     (pins.test_rms_norm_unit_rms_and_scale_invariance, {}),
     (pins.test_rms_norm_one_hot_selects_scaled_column, {}),

@@ -560,3 +560,96 @@ def test_rms_norm_swiglu_pair_composes():
     g = oracle.dequant(gate) @ xn
     u = oracle.dequant(up) @ xn
     np.testing.assert_allclose(h, g / (1.0 + np.exp(-g)) * u, rtol=1e-12, atol=1e-300)
+
+
+# --------------------------------------------------------------------------
+# quantiser
+# --------------------------------------------------------------------------
+
+def _qmat(codes, s, b, n_out, k_in, group, sbt):
+    return synth.QMatrix(codes=codes, scales=s, biases=b, sb_dtype=sbt, group_size=group,
+                         n_out=n_out, k_in=k_in)
+
+
+@pytest.mark.parametrize("group", [32, 64, 128])
+@pytest.mark.parametrize("sbt", [synth.F32, synth.BF16])
+def test_quantize_recovers_exact_grid(group, sbt):
+    """Weights on a grid s q + b where every group holds codes 0 and 15 and
+    s = 2^-e, b = m * s are exactly representable: the quantiser returns the
+    same codes, scales and biases."""
+    rng = np.random.default_rng(group)
+    n_out, k_in = 12, 4 * group
+    raw = rng.integers(0, 16, size=(n_out, k_in), dtype=np.uint8)
+    raw[:, ::group] = 0
+    raw[:, 1::group] = 15
+    e = rng.integers(4, 9, size=(n_out, k_in // group))
+    s = np.ldexp(1.0, -e).astype(np.float32)
+    b = (rng.integers(-12, -4, size=s.shape) * s).astype(np.float32)
+    sb = (lambda a: synth.f32_to_bf16_bits(a)) if sbt == synth.BF16 else (lambda a: a)
+    w = _qmat(synth.pack_codes(raw), sb(s), sb(b), n_out, k_in, group, sbt)
+    W = oracle.dequant(w).astype(np.float32)
+    assert np.array_equal(W.astype(np.float64), oracle.dequant(w))  # exact in float32
+    codes, s2, b2 = oracle.quantize(W, synth.F32, group, sbt)
+    assert np.array_equal(codes, w.codes)
+    assert np.array_equal(s2, w.scales) and np.array_equal(b2, w.biases)
+
+
+@pytest.mark.parametrize("sbt", [synth.F32, synth.BF16])
+def test_quantize_picks_nearest_stored_grid_point(sbt):
+    """Every code is the one whose s' q + b' (stored s', b') is nearest to w --
+    checked by brute force over the 16 codes in float64 (a float32 rounding
+    of (w - b') / s' may only matter within 1e-5 s' of a midpoint)."""
+    rng = np.random.default_rng(7 if sbt == synth.F32 else 8)
+    W = rng.standard_normal((40, 256)).astype(np.float32)
+    codes, s, b = oracle.quantize(W, synth.F32, 64, sbt)
+    w = _qmat(codes, s, b, 40, 256, 64, sbt)
+    q = oracle.unpack(codes, 256).astype(np.float64)
+    s64 = np.repeat(oracle.widen(s, sbt), 64, axis=1)
+    b64 = np.repeat(oracle.widen(b, sbt), 64, axis=1)
+    cand = s64[..., None] * np.arange(16.0) + b64[..., None]
+    err_all = np.abs(cand - W[..., None].astype(np.float64))
+    chosen = np.take_along_axis(err_all, q.astype(np.int64)[..., None], axis=-1)[..., 0]
+    assert np.all(chosen <= err_all.min(axis=-1) + 1e-5 * s64)
+    assert np.array_equal(oracle.dequant(w), s64 * q + b64)
+
+
+def test_quantize_scale_spans_the_group_range():
+    """float32 storage: b is the group minimum and b + 15 s its maximum (to rounding),
+    so the extreme weights get codes 0 and 15."""
+    rng = np.random.default_rng(9)
+    W = (rng.standard_normal((16, 512)) * 0.05).astype(np.float32)
+    codes, s, b = oracle.quantize(W, synth.F32, 64, synth.F32)
+    G = W.reshape(16, 8, 64)
+    assert np.array_equal(b, G.min(axis=-1))
+    np.testing.assert_allclose(b.astype(np.float64) + 15.0 * s, G.max(axis=-1), rtol=1e-6)
+    q = oracle.unpack(codes, 512).reshape(16, 8, 64)
+    assert np.all(q[np.arange(16)[:, None], np.arange(8)[None, :], G.argmin(-1)] == 0)
+    assert np.all(q[np.arange(16)[:, None], np.arange(8)[None, :], G.argmax(-1)] == 15)
+
+
+def test_quantize_constant_group_and_bf16_input():
+    """A constant group gives s = 0, b = the constant and codes 0; bf16 input widens exactly."""
+    W = np.full((2, 128), 0.375, np.float32)
+    W[1, 64:] = np.linspace(-1, 1, 64, dtype=np.float32)
+    for wt in (synth.F32, synth.BF16):
+        Win = W if wt == synth.F32 else synth.f32_to_bf16_bits(W)
+        codes, s, b = oracle.quantize(Win, wt, 64, synth.F32)
+        assert s[0, 0] == 0 and s[0, 1] == 0 and s[1, 0] == 0 and b[0, 0] == np.float32(0.375)
+        assert np.all(oracle.unpack(codes, 128)[0] == 0)
+        assert s[1, 1] > 0
+
+
+def test_quantize_codes_follow_rounded_not_raw_scale():
+    """bf16 storage: codes are taken against the rounded s', b'.  Codes computed
+    against the raw float32 s, b differ for some weights (the page's fixtures
+    tell the two rules apart in the same way), and those are never nearer to w
+    on the stored grid."""
+    rng = np.random.default_rng(10)
+    W = rng.standard_normal((64, 512)).astype(np.float32)
+    codes, s, b = oracle.quantize(W, synth.F32, 64, synth.BF16)
+    _, s32, b32 = oracle.quantize(W, synth.F32, 64, synth.F32)
+    G = W.reshape(64, 8, 64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q_raw = np.clip(np.rint((G - b32[..., None]) / s32[..., None]), 0, 15).reshape(64, 512)
+    q = oracle.unpack(codes, 512)
+    assert np.count_nonzero(q != q_raw) > 0
