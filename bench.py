@@ -21,6 +21,7 @@ Workloads (default: qkv):
   moe      top-8 of 128 experts, hidden 2048, inter 768, weighted combine + residual;
            each step routes its token's logits on the GPU first (--router pre-drawn: skip)
   prefill  K=5120, N=17408 dequant GEMM on bf16 MFMA (--T rows, default 256)
+  moeprefill  --T tokens through the 128-expert top-8 layer at once (router + sorted GEMMs)
   quant    the offline quantiser: 17408x5120 float32 -> g64 codes, bf16 scales/biases
 
 Prints one JSON line.  ``value`` is weight GB/s for the decode workloads and
@@ -52,7 +53,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="qkv",
-                    choices=["single", "qkv", "rmsqkv", "smallm", "dense", "moe", "prefill", "quant"])
+                    choices=["single", "qkv", "rmsqkv", "smallm", "dense", "moe", "moeprefill", "prefill",
+                             "quant"])
     ap.add_argument("--T", type=int, default=None,
                     help="prefill rows (default 256) or small-M tokens (default 4)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -319,6 +321,59 @@ class MoE(Workload):
                                      residual=self.res)
 
 
+class MoEPrefill(Workload):
+    """T tokens through the 128-expert top-8 layer at once: device router over the T rows,
+    then the expert-sorted gather GEMMs (sort, gate/up + SwiGLU, down, combine)."""
+    launches_per_step = 5
+    dominant = "moe_gemm_kernel (gate/up SwiGLU, down) on bf16 MFMA"
+
+    def __init__(self, q, synth, torch, T):
+        self.q, self.T = q, T
+        E, H, I, K = 128, 2048, 768, 8
+        self.name = "moe_prefill_top8_T%d" % T
+        stacks = []
+        r = 0
+        while True:
+            stacks.append((_mat(q, synth, I, H, "bf16", 7 * r, n_experts=E),
+                           _mat(q, synth, I, H, "bf16", 7 * r + 1, n_experts=E),
+                           _mat(q, synth, H, I, "bf16", 7 * r + 2, n_experts=E)))
+            r += 1
+            if r * sum(m.weight_bytes for m in stacks[0]) >= POOL_BYTES:
+                break
+        self.pool, self.R = stacks, len(stacks)
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(6)
+        self.logits = torch.randn(T, E, device="cuda", generator=gen)
+        self.x = torch.randn(T, H, device="cuda", generator=gen).to(torch.bfloat16)
+        self.res = torch.randn(T, H, device="cuda", generator=gen).to(torch.bfloat16)
+        self.out = torch.empty(T, H, device="cuda", dtype=torch.bfloat16)
+        self.ids = torch.empty(T, K, dtype=torch.int32, device="cuda")
+        self.wts = torch.empty(T, K, dtype=torch.float32, device="cuda")
+        self.ws = torch.empty(q.moe_prefill_qgemm_int4_workspace_bytes(T, K, E, H, I),
+                              dtype=torch.uint8, device="cuda")
+        q.moe_router_topk(self.logits, K, self.ids, self.wts)
+        touched = int(torch.unique(self.ids).numel())
+        per_expert = 3 * (I * H // 2 + 2 * 2 * I * H // 64)
+        self.wb = touched * per_expert              # weights of the experts the step touches
+        self.flops = 6.0 * T * K * I * H
+        self.config = {"workload": self.name, "T": T, "n_experts": E, "top_k": K, "hidden": H,
+                       "inter": I, "group_size": 64, "sb_dtype": "bf16", "x_dtype": "bf16",
+                       "experts_touched": touched, "router": "gpu", "pool_copies": self.R}
+        self.dtype = "bf16"
+
+    def weight_bytes(self):
+        return self.wb
+
+    def algo_bytes(self):
+        return self.wb + self.T * 2048 * 2 * 3 + self.T * 128 * 4
+
+    def step(self, i):
+        g, u, d = self.pool[i % self.R]
+        self.q.moe_router_topk(self.logits, 8, self.ids, self.wts)
+        self.q.moe_prefill_qgemm_int4(g, u, d, self.x, self.ids, self.wts, self.out, self.ws,
+                                      residual=self.res)
+
+
 class Prefill(Workload):
     dominant = "qgemm_kernel (bf16 MFMA)"
 
@@ -397,6 +452,26 @@ def cpu_baseline(workload: str, budget_s: float, T: int):
             return oracle.moe(d["gate"], d["up"], d["down"], d["x"][0], ids, wts.astype(np.float32),
                               d["residual"][0], "bf16", threads=threads)
         sample = "one token of the 128-expert layer (seed 3): router + top-8 experts, repeated"
+    elif workload == "moeprefill":
+        d = synth.moe_prefill_layer(T=max(T, 2))
+        ntok = 2
+        pairs = [oracle.router_topk(d["logits"][t].astype(np.float64), 8) for t in range(ntok)]
+        ids = np.array([p_[0] for p_ in pairs])
+        wts = np.array([p_[1] for p_ in pairs], dtype=np.float32)
+        fn = lambda: oracle.moe_prefill(d["gate"], d["up"], d["down"], d["x"][:ntok], ids, wts,
+                                        d["residual"][:ntok], threads=threads)
+        flops_per_call = 6.0 * ntok * 8 * 768 * 2048
+        sample = "%d tokens of the 128-expert layer (seed 6) per call: router + 8 experts each" % ntok
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            fn()
+            n += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        el = time.perf_counter() - t0
+        return {"value": flops_per_call * n / el / 1e12, "unit": "TFLOP/s", "cores": threads,
+                "kind": "oracle", "sample": sample + "; %d calls in %.1f s" % (n, el)}
     elif workload == "quant":
         rng = np.random.default_rng(11)
         rows = 512
@@ -466,6 +541,8 @@ def main():
         wl = RmsQKV(q, synth, torch)
     elif args.workload == "quant":
         wl = Quant(q, synth, torch)
+    elif args.workload == "moeprefill":
+        wl = MoEPrefill(q, synth, torch, args.T)
     elif args.workload == "dense":
         wl = Dense(q, synth, torch)
     elif args.workload == "smallm":
@@ -515,7 +592,25 @@ def main():
            "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic (seeded, device-generated pool)",
            "config": wl.config}
-    if isinstance(wl, Prefill):
+    if isinstance(wl, MoEPrefill):
+        tflops = wl.flops / (ms_step * 1e-3) / 1e12
+        gbs = wl.algo_bytes() / (ms_step * 1e-3) / 1e9
+        out.update({"value": tflops, "unit": "TFLOP/s", "tokens_per_s": wl.T * 1e3 / ms_step,
+                    "weight_GBps": wl.weight_bytes() / (ms_step * 1e-3) / 1e9})
+        # the bound is whichever ideal time is longer: the touched weights at HBM peak or
+        # the products at dense bf16 MFMA peak
+        t_hbm = wl.algo_bytes() / (HBM_PEAK_GBS * 1e9)
+        t_mfma = wl.flops / (BF16_MFMA_PEAK_TFLOPS * 1e12)
+        if t_mfma >= t_hbm:
+            out["roofline"] = {"bound": "mfma", "achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS,
+                               "unit": "TFLOP/s", "frac": tflops / BF16_MFMA_PEAK_TFLOPS,
+                               "traffic": None, "kernel": wl.dominant,
+                               "launches_per_step": wl.launches_per_step}
+        else:
+            out["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": wl.dominant,
+                               "launches_per_step": wl.launches_per_step}
+    elif isinstance(wl, Prefill):
         tflops = wl.flops / (ms_step * 1e-3) / 1e12
         out.update({"value": tflops, "unit": "TFLOP/s",
                     "weight_GBps": wl.weight_bytes() / (ms_step * 1e-3) / 1e9,

@@ -80,6 +80,10 @@ SIGNATURES = [
                                      _P, ctypes.c_size_t, _P]),
     ("qgemm_int4_padT", _I32, [ctypes.POINTER(CMatrix), _P, _I64, _I64, _P, _I64, _I32, _P]),
     ("moe_router_topk", _I32, [_P, _I32, _I64, _I32, _I32, _P, _P, _P]),
+    ("moe_prefill_qgemm_int4_workspace_bytes", ctypes.c_size_t, [_I64, _I32, _I32, _I64, _I64]),
+    ("moe_prefill_qgemm_int4", _I32, [ctypes.POINTER(CMatrix), ctypes.POINTER(CMatrix),
+                                      ctypes.POINTER(CMatrix), _P, _I64, _I64, _P, _P, _I32, _P, _P,
+                                      _I32, _P, ctypes.c_size_t, _P]),
     ("quantize_int4", _I32, [_P, _I32, _I64, _I64, _I32, _I32, _P, _P, _P, _P]),
     ("qint4_status_string", ctypes.c_char_p, [_I32]),
     ("qint4_last_error", ctypes.c_char_p, []),
@@ -229,6 +233,36 @@ def quantize_int4(w: torch.Tensor, group_size: int = 64, sb_dtype: torch.dtype =
     return QInt4Matrix(codes, scales, biases, group_size)
 
 
+def moe_prefill_qgemm_int4_workspace_bytes(T: int, top_k: int, n_experts: int, hidden: int,
+                                           inter: int) -> int:
+    return int(load().moe_prefill_qgemm_int4_workspace_bytes(int(T), int(top_k), int(n_experts),
+                                                              int(hidden), int(inter)))
+
+
+def moe_prefill_qgemm_int4(gate: QInt4Matrix, up: QInt4Matrix, down: QInt4Matrix, x: torch.Tensor,
+                           ids: torch.Tensor, wts: torch.Tensor, out: torch.Tensor,
+                           workspace: torch.Tensor, residual: Optional[torch.Tensor] = None,
+                           stream=None) -> None:
+    """out[t] = residual[t] + sum_k wts[t,k] * down[ids[t,k]] (silu(gate[.] x[t]) * up[.] x[t])
+    for all T rows of x ([T][ldx] bf16) at once; ids int32/uint32 [T][top_k], wts float32 [T][top_k],
+    out (and residual) [T][hidden] float32/bfloat16, workspace of
+    moe_prefill_qgemm_int4_workspace_bytes(...) bytes."""
+    if x.dim() != 2 or x.stride(1) != 1 or x.device.type != "cuda":
+        raise ValueError("x must be a 2-D device tensor [T][ldx] with contiguous rows")
+    if ids.dtype not in (torch.int32, torch.uint32) or ids.dim() != 2 or ids.shape[0] != x.shape[0]:
+        raise ValueError("ids must be int32/uint32 [T][top_k]")
+    if wts.dtype != torch.float32 or wts.shape != ids.shape:
+        raise ValueError("wts must be float32 of ids' shape")
+    if residual is not None and residual.dtype != out.dtype:
+        raise TypeError("residual must have out's dtype")
+    g, u, d = gate.c(), up.c(), down.c()
+    _check(load().moe_prefill_qgemm_int4(
+        ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), x.data_ptr(), x.shape[0], x.stride(0),
+        _dev(ids, "ids"), _dev(wts, "wts"), ids.shape[1],
+        None if residual is None else _dev(residual, "residual"), _dev(out, "out"), _dt(out),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
 SMALLM_MAX = 8
 
 
@@ -327,4 +361,5 @@ def moe_router_topk(logits: torch.Tensor, top_k: int, ids: torch.Tensor, wts: to
 __all__ = ["QInt4Matrix", "Int4Error", "qgemv_int4", "qgemv_int4_multi", "qgemv_int4_smallm",
            "moe_gather_qgemv_int4", "moe_gather_qgemv_int4_workspace_bytes", "qgemm_int4_padT",
            "moe_router_topk", "rms_norm_qgemv_int4", "quantize_int4",
+           "moe_prefill_qgemm_int4", "moe_prefill_qgemm_int4_workspace_bytes",
            "load", "F32", "BF16", "EPI_NONE", "EPI_SWIGLU_PAIR", "LIB_PATH", "SIGNATURES"]

@@ -608,6 +608,165 @@ qint4_status moe_router_topk(const void *logits, int32_t logits_dtype, int64_t n
   return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+// Workspace layout of moe_prefill_qgemm_int4 (every region 256-byte aligned).
+struct PrefillWs {
+  size_t perm, pos, tiles, h_hi, h_lo, d, total;
+  int64_t max_tiles;
+};
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+bool prefill_ws(int64_t T, int32_t top_k, int32_t n_experts, int64_t hidden, int64_t inter,
+                PrefillWs *w) {
+  if (T < 1 || top_k < 1 || top_k > QINT4_TOPK_MAX || n_experts < 1 ||
+      n_experts > kMaxExpertsPrefill || hidden < 1 || hidden > kMaxK || inter < 1 || inter > kMaxK)
+    return false;
+  const int64_t P = T * top_k;
+  if (P > ((int64_t)1 << 24)) return false;
+  // row tiles of at most 32 rows bound every tile size: ceil(P / 32) + one
+  // partial tile per expert that has rows
+  w->max_tiles = (P + 31) / 32 + std::min<int64_t>(n_experts, P);
+  size_t o = 0;
+  w->perm = o;  o = align256(o + (size_t)P * 4);
+  w->pos = o;   o = align256(o + (size_t)P * 4);
+  w->tiles = o; o = align256(o + (size_t)(1 + 3 * w->max_tiles) * 4);
+  w->h_hi = o;  o = align256(o + (size_t)P * inter * 2);
+  w->h_lo = o;  o = align256(o + (size_t)P * inter * 2);
+  w->d = o;     o = align256(o + (size_t)P * hidden * 4);
+  w->total = o;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_prefill_qgemm_int4_workspace_bytes(int64_t T, int32_t top_k, int32_t n_experts,
+                                              int64_t hidden, int64_t inter) {
+  PrefillWs w;
+  return prefill_ws(T, top_k, n_experts, hidden, inter, &w) ? w.total : 0;
+}
+
+qint4_status moe_prefill_qgemm_int4(const qint4_matrix *gate, const qint4_matrix *up,
+                                    const qint4_matrix *down, const void *x, int64_t T, int64_t ldx,
+                                    const uint32_t *ids, const float *wts, int32_t top_k,
+                                    const void *residual, void *out, int32_t out_dtype,
+                                    void *workspace, size_t workspace_bytes, void *stream_) {
+  const char *fn = "moe_prefill_qgemm_int4";
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  qint4_status st;
+  if ((st = check_matrix(gate, "gate", true)) != QINT4_OK) return st;
+  if ((st = check_matrix(up, "up", true)) != QINT4_OK) return st;
+  if ((st = check_matrix(down, "down", true)) != QINT4_OK) return st;
+  if (!x || !ids || !wts || !out) return fail(QINT4_ERR_NULL, "%s: x/ids/wts/out is NULL", fn);
+  if (!valid_dtype(out_dtype)) return fail(QINT4_ERR_DTYPE, "%s: out_dtype %d invalid", fn, out_dtype);
+  if (top_k < 1 || top_k > QINT4_TOPK_MAX)
+    return fail(QINT4_ERR_SHAPE, "%s: top_k %d not in [1, %d]", fn, top_k, QINT4_TOPK_MAX);
+  if (gate->n_experts != up->n_experts || gate->n_experts != down->n_experts)
+    return fail(QINT4_ERR_SHAPE, "%s: n_experts differ (gate %d, up %d, down %d)", fn,
+                gate->n_experts, up->n_experts, down->n_experts);
+  if (gate->n_experts > kMaxExpertsPrefill)
+    return fail(QINT4_ERR_SHAPE, "%s: n_experts %d > %d", fn, gate->n_experts, kMaxExpertsPrefill);
+  if (gate->group_size != up->group_size || gate->group_size != down->group_size ||
+      gate->sb_dtype != up->sb_dtype || gate->sb_dtype != down->sb_dtype)
+    return fail(QINT4_ERR_SHAPE, "%s: gate/up/down must share group_size and sb_dtype", fn);
+  const int64_t hidden = gate->k_in, inter = gate->n_out;
+  if (up->k_in != hidden || up->n_out != inter)
+    return fail(QINT4_ERR_SHAPE, "%s: up is %lldx%lld, gate is %lldx%lld", fn, (long long)up->n_out,
+                (long long)up->k_in, (long long)inter, (long long)hidden);
+  if (down->k_in != inter || down->n_out != hidden)
+    return fail(QINT4_ERR_SHAPE, "%s: down is %lldx%lld, expected %lldx%lld", fn,
+                (long long)down->n_out, (long long)down->k_in, (long long)hidden, (long long)inter);
+  PrefillWs lay;
+  if (T < 1 || !prefill_ws(T, top_k, gate->n_experts, hidden, inter, &lay))
+    return fail(QINT4_ERR_SHAPE, "%s: T = %lld with top_k %d out of range (T * top_k <= 2^24)", fn,
+                (long long)T, top_k);
+  if (ldx < hidden || ldx % 8 != 0)
+    return fail(QINT4_ERR_SHAPE, "%s: ldx %lld must be >= hidden %lld and a multiple of 8", fn,
+                (long long)ldx, (long long)hidden);
+  if (!aligned(x, 16) || !aligned(out, 16) || (residual && !aligned(residual, 16)))
+    return fail(QINT4_ERR_ALIGN, "%s: x/out/residual not 16-byte aligned", fn);
+  if (!aligned(ids, 4) || !aligned(wts, 4)) return fail(QINT4_ERR_ALIGN, "%s: ids/wts misaligned", fn);
+  if (!workspace || workspace_bytes < lay.total)
+    return fail(QINT4_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn,
+                workspace ? workspace_bytes : (size_t)0, lay.total);
+  if (!aligned(workspace, 256)) return fail(QINT4_ERR_ALIGN, "%s: workspace not 256-byte aligned", fn);
+
+  const size_t ob = elem_bytes(out_dtype);
+  const int64_t P = T * top_k;
+  Range ins[14], outs[2];
+  int ni = 0;
+  static const char *gn[3] = {"gate.codes", "gate.scales", "gate.biases"};
+  static const char *un[3] = {"up.codes", "up.scales", "up.biases"};
+  static const char *dn[3] = {"down.codes", "down.scales", "down.biases"};
+  ni += add_matrix_ranges(gate, gn, ins + ni);
+  ni += add_matrix_ranges(up, un, ins + ni);
+  ni += add_matrix_ranges(down, dn, ins + ni);
+  ins[ni++] = range(x, (size_t)((T - 1) * ldx + hidden) * 2, "x");
+  ins[ni++] = range(ids, (size_t)P * 4, "ids");
+  ins[ni++] = range(wts, (size_t)P * 4, "wts");
+  if (residual) ins[ni++] = range(residual, (size_t)T * hidden * ob, "residual");
+  outs[0] = range(out, (size_t)T * hidden * ob, "out");
+  outs[1] = range(workspace, lay.total, "workspace");
+  if ((st = check_no_overlap(outs, 2, ins, ni)) != QINT4_OK) return prefixed(st, fn);
+  if ((st = check_device(nullptr)) != QINT4_OK) return prefixed(st, fn);
+
+  unsigned char *ws = reinterpret_cast<unsigned char *>(workspace);
+  uint32_t *perm = reinterpret_cast<uint32_t *>(ws + lay.perm);
+  uint32_t *pos = reinterpret_cast<uint32_t *>(ws + lay.pos);
+  uint32_t *tiles = reinterpret_cast<uint32_t *>(ws + lay.tiles);
+  // row tile height from the mean rows per touched expert (uniform routing)
+  const int64_t touched = std::min<int64_t>(gate->n_experts, P);
+  const int64_t mean_rows = (P + touched - 1) / touched;
+  const int bm = mean_rows <= 32 ? 32 : mean_rows <= 96 ? 64 : 128;
+  const int64_t max_mtiles = (P + bm - 1) / bm + touched;
+  if (max_mtiles * ((std::max(hidden, inter) + 31) / 32) >= INT32_MAX)
+    return fail(QINT4_ERR_SHAPE, "%s: T * top_k too large for one launch at this width", fn);
+
+  hipError_t e = launch_moe_sort(ids, P, gate->n_experts, bm, perm, pos, tiles, (int)lay.max_tiles,
+                                 stream);
+  MoeGemmParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.perm = perm;
+  p.tiles = tiles;
+  p.top_k = top_k;
+  p.max_mtiles = (int32_t)max_mtiles;
+  p.sb_bf16 = gate->sb_dtype == QINT4_BF16;
+  p.log2_group = ilog2(gate->group_size);
+  if (e == hipSuccess) {  // gate/up + SwiGLU -> h (hi, lo)
+    p.codes0 = gate->codes; p.scales0 = gate->scales; p.biases0 = gate->biases;
+    p.codes1 = up->codes;   p.scales1 = up->scales;   p.biases1 = up->biases;
+    p.a0 = x;
+    p.lda = ldx;
+    p.y0 = ws + lay.h_hi;
+    p.y1 = ws + lay.h_lo;
+    p.n_out = (int32_t)inter;
+    p.k_in = (int32_t)hidden;
+    e = launch_moe_gemm(p, 0, bm, stream);
+  }
+  if (e == hipSuccess) {  // down -> d
+    p.codes0 = down->codes; p.scales0 = down->scales; p.biases0 = down->biases;
+    p.codes1 = nullptr;     p.scales1 = nullptr;      p.biases1 = nullptr;
+    p.a0 = ws + lay.h_hi;
+    p.a1 = ws + lay.h_lo;
+    p.lda = inter;
+    p.y0 = ws + lay.d;
+    p.y1 = nullptr;
+    p.n_out = (int32_t)hidden;
+    p.k_in = (int32_t)inter;
+    e = launch_moe_gemm(p, 1, bm, stream);
+  }
+  if (e == hipSuccess)
+    e = launch_moe_combine(reinterpret_cast<const float *>(ws + lay.d), pos, wts, top_k, residual, out,
+                           out_dtype == QINT4_BF16, T, (int)hidden, stream);
+  if (e != hipSuccess) return fail(QINT4_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
 qint4_status quantize_int4(const void *w, int32_t w_dtype, int64_t n_rows, int64_t k_in,
                            int32_t group_size, int32_t sb_dtype, uint32_t *codes, void *scales,
                            void *biases, void *stream) {

@@ -131,6 +131,29 @@ hipError_t launch_gemm(const GemmParams &p, hipStream_t stream);
 // ids/wts are [n_rows][top_k].
 constexpr int kRouterMaxExperts = 4096;
 
+// MoE prefill (expert-sorted gather GEMMs).
+constexpr int kMaxExpertsPrefill = 4096;
+
+struct MoeGemmParams {
+  const uint32_t *codes0, *codes1;  // gate and up stacks, or the down stack (codes0)
+  const void *scales0, *scales1;
+  const void *biases0, *biases1;
+  const void *a0, *a1;    // gate/up: x bf16 [T][lda]; down: h hi / lo planes, bf16 [P][lda]
+  void *y0, *y1;          // gate/up: h hi / lo planes, bf16 [P][n_out]; down: d, float32 [P][n_out]
+  const uint32_t *perm;   // sorted slot -> pair index t * top_k + k
+  const uint32_t *tiles;  // [0] = row tiles, then (expert, first slot, rows) per tile
+  int64_t lda;
+  int32_t n_out, k_in, log2_group, sb_bf16, top_k, max_mtiles;
+};
+
+hipError_t launch_moe_sort(const uint32_t *ids, int64_t n_pairs, int n_experts, int bm, uint32_t *perm,
+                           uint32_t *pos, uint32_t *tiles, int max_tiles, hipStream_t stream);
+// down = 0: gate/up + SwiGLU; down = 1: down projection.  bm: 32, 64 or 128.
+hipError_t launch_moe_gemm(const MoeGemmParams &p, int down, int bm, hipStream_t stream);
+hipError_t launch_moe_combine(const float *d, const uint32_t *pos, const float *wts, int top_k,
+                              const void *residual, void *out, int out_bf16, int64_t T, int hidden,
+                              hipStream_t stream);
+
 // Quantise n_words * 8 row-major weights (bf16 or float32; n_words * 8 * the
 // weight size < 2 GiB) into codes / scales / biases with group_size in
 // {32, 64, 128}; group g covers words g * group_size / 8 ...

@@ -1,0 +1,461 @@
+// moe_prefill.hip -- top-K mixture of experts for T tokens at once (prefill),
+// as expert-sorted gather GEMMs on gfx950 bf16 MFMA.
+//
+// Sources (by page title and passage):
+//   [FFAI #9]  thewafflehaus/FFAI pull 9, "Everything Bagel": the batched
+//              MoE path fans the T * topK (token, slot) rows into one GEMM per
+//              gate / up / down, sorted by expert id so that a row tile shares
+//              one expert's weights; CSR expert offsets are built from the
+//              sorted top-K ids; a scatter-sum unpermutes the results; the
+//              m1 gather GEMM wiring.
+//   [FFAI #14] thewafflehaus/FFAI pull 14, "feat(everything-bagel): clean
+//              migration of PR #9 + #10 onto updated dev": the chain8
+//              combine out = residual + sum_k w_k d_k, the fused SwiGLU.
+//
+// Stages (four launches on one stream, no host round trip):
+//   1. moe_sort_kernel (one workgroup): counting sort of the P = T * top_k
+//      pairs p = t * top_k + k by expert id.  Writes perm[slot] = p,
+//      pos[p] = slot (or 0xFFFFFFFF for an id >= n_experts, which contributes
+//      nothing), and a table of row tiles: tile i covers sorted slots
+//      row0 .. row0 + rows - 1 of one expert (rows <= BM).  The order of the
+//      pairs inside one expert's segment does not affect any result: every
+//      GEMM row is computed independently of the other rows of its tile.
+//   2. moe_gemm_kernel<GATEUP>: for each tile, the gathered activation rows
+//      x[p / top_k] times the tile expert's gate and up matrices (weights
+//      dequantised in float32, rounded to bf16 in LDS, as in the dense
+//      prefill GEMM), float32 accumulators, then h = silu(g) * u.  h is kept
+//      to float32 accuracy as two bf16 planes, hi = bf16(h), lo = bf16(h - hi)
+//      (hi + lo carries 16 significant bits), in sorted order.
+//   3. moe_gemm_kernel<DOWN>: h rows times the down matrix, as
+//      hi * W + lo * W (two MFMAs per fragment), float32 result d in sorted
+//      order.
+//   4. moe_combine_kernel: out[t] = residual[t] + sum_k wts[t][k] d[pos[t][k]].
+
+#include "kernels.h"
+
+namespace qint4 {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int BK = 64;
+constexpr int LDK = BK + 8;  // padded LDS row (bf16 elements)
+constexpr uint32_t kNoSlot = 0xFFFFFFFFu;
+
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// ---------------------------------------------------------------------------
+// 1. sort
+// ---------------------------------------------------------------------------
+
+constexpr int kSortThreads = 1024;
+
+// Exclusive scan of v[0..n) in LDS (n <= 4 * kSortThreads) by the whole
+// workgroup; v[n] receives the total.  Each thread scans 4 consecutive
+// entries, waves scan their threads' sums with shuffles, one wave scans the
+// wave totals.
+__device__ void block_exclusive_scan(uint32_t *v, int n, uint32_t *wave_tot) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t loc[4], s = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int j = 4 * tid + i;
+    loc[i] = j < n ? v[j] : 0u;
+    s += loc[i];
+  }
+  uint32_t inc = s;  // inclusive scan over the wave
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t o = __shfl_up(inc, d);
+    if (lane >= d) inc += o;
+  }
+  if (lane == 63) wave_tot[wave] = inc;
+  lds_barrier();
+  if (wave == 0) {
+    constexpr int NW = kSortThreads / 64;
+    uint32_t t = lane < NW ? wave_tot[lane] : 0u, ti = t;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t o = __shfl_up(ti, d);
+      if (lane >= d) ti += o;
+    }
+    if (lane < NW) wave_tot[lane] = ti - t;   // exclusive wave offsets
+    if (lane == NW - 1) wave_tot[NW] = ti;     // total
+  }
+  lds_barrier();
+  uint32_t run = wave_tot[wave] + inc - s;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int j = 4 * tid + i;
+    if (j < n) v[j] = run;
+    run += loc[i];
+  }
+  if (tid == 0) v[n] = wave_tot[kSortThreads / 64];
+  lds_barrier();
+}
+
+__global__ void __launch_bounds__(kSortThreads)
+    moe_sort_kernel(const uint32_t *__restrict__ ids, int64_t n_pairs, int n_experts, int bm,
+                    uint32_t *__restrict__ perm, uint32_t *__restrict__ pos,
+                    uint32_t *__restrict__ tiles, int max_tiles) {
+  // tiles: [0] tile count, then per tile (expert, row0, rows) at 1 + 3i
+  __shared__ uint32_t cnt[kMaxExpertsPrefill + 1];
+  __shared__ uint32_t tcnt[kMaxExpertsPrefill + 1];
+  __shared__ uint32_t wave_tot[kSortThreads / 64 + 1];
+  const int tid = threadIdx.x;
+  for (int e = tid; e <= n_experts; e += kSortThreads) cnt[e] = 0u;
+  lds_barrier();
+  for (int64_t p = tid; p < n_pairs; p += kSortThreads) {
+    const uint32_t e = ids[p];
+    if (e < (uint32_t)n_experts) atomicAdd(&cnt[e], 1u);
+  }
+  lds_barrier();
+  for (int e = tid; e < n_experts; e += kSortThreads) tcnt[e] = (cnt[e] + bm - 1) / bm;
+  lds_barrier();
+  block_exclusive_scan(cnt, n_experts, wave_tot);   // cnt[e] = first slot of expert e
+  block_exclusive_scan(tcnt, n_experts, wave_tot);  // tcnt[e] = first tile of expert e
+  const uint32_t n_tiles = tcnt[n_experts];
+  if (tid == 0) tiles[0] = n_tiles <= (uint32_t)max_tiles ? n_tiles : 0u;  // never exceeded
+  for (int e = tid; e < n_experts; e += kSortThreads) {
+    const uint32_t r0 = cnt[e], n = cnt[e + 1] - r0, t0 = tcnt[e];
+    for (uint32_t j = 0; j * bm < n; ++j) {
+      const uint32_t i = t0 + j;
+      if (i < (uint32_t)max_tiles) {
+        tiles[1 + 3 * i] = (uint32_t)e;
+        tiles[2 + 3 * i] = r0 + j * bm;
+        tiles[3 + 3 * i] = min((uint32_t)bm, n - j * bm);
+      }
+    }
+  }
+  lds_barrier();
+  // scatter: cnt[e] is now the next free slot of expert e
+  for (int64_t p = tid; p < n_pairs; p += kSortThreads) {
+    const uint32_t e = ids[p];
+    uint32_t slot = kNoSlot;
+    if (e < (uint32_t)n_experts) {
+      slot = atomicAdd(&cnt[e], 1u);
+      perm[slot] = (uint32_t)p;
+    }
+    pos[p] = slot;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2./3. grouped gather GEMM
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2_t v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// 8 codes of one word -> 8 bf16 weights (k order) as a uint4: float32
+// s * q + b rounded to nearest even.
+__device__ __forceinline__ uint4 dequant_word(uint32_t w, float s, float b) {
+  uint32_t lo = w & 0x0F0F0F0Fu;         // codes 0, 2, 4, 6 in bytes 0..3
+  uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // codes 1, 3, 5, 7
+  asm("" : "+v"(lo), "+v"(hi));
+  uint4 r;
+  r.x = pack_bf16x2(fmaf(s, (float)(lo & 0xFFu), b), fmaf(s, (float)(hi & 0xFFu), b));
+  r.y = pack_bf16x2(fmaf(s, (float)((lo >> 8) & 0xFFu), b), fmaf(s, (float)((hi >> 8) & 0xFFu), b));
+  r.z = pack_bf16x2(fmaf(s, (float)((lo >> 16) & 0xFFu), b), fmaf(s, (float)((hi >> 16) & 0xFFu), b));
+  r.w = pack_bf16x2(fmaf(s, (float)(lo >> 24), b), fmaf(s, (float)(hi >> 24), b));
+  return r;
+}
+
+enum { MG_GATEUP = 0, MG_DOWN = 1 };
+
+template <int MODE, int BM, int BN, int WM, int WN>
+__global__ void __launch_bounds__(WM * WN * 64) moe_gemm_kernel(const MoeGemmParams p) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int NB = MODE == MG_GATEUP ? 2 : 1;  // weight matrices (gate, up) or (down)
+  constexpr int NA = MODE == MG_GATEUP ? 1 : 2;  // activation planes (x) or (h hi, h lo)
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 32, FN = TN / 32;
+  constexpr int WCH = (2 * BN * NB + NT - 1) / NT;  // 16-byte code loads per thread per step
+  constexpr int XCH = (8 * BM * NA + NT - 1) / NT;  // 16-byte activation loads per thread per step
+  static_assert(FM >= 1 && FN >= 1, "tile");
+
+  __shared__ __attribute__((aligned(16))) uint16_t sa[NA][BM * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t sw[NB][BN * LDK];
+
+  const int mt = blockIdx.x % p.max_mtiles;
+  const int nt = blockIdx.x / p.max_mtiles;
+  if (mt >= (int)p.tiles[0]) return;  // whole workgroup: past the last row tile
+  const uint32_t e = p.tiles[1 + 3 * mt];
+  const int64_t row0 = p.tiles[2 + 3 * mt];
+  const int rows = (int)p.tiles[3 + 3 * mt];
+  const int n0 = nt * BN;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int cpr = p.k_in / 32;
+  const int64_t gpr = (int64_t)p.k_in >> p.log2_group;
+  const int nsteps = (p.k_in + BK - 1) / BK;
+  const int64_t ecodes = (int64_t)e * p.n_out * (p.k_in / 8);  // words before expert e
+  const int64_t esb = (int64_t)e * p.n_out * gpr;              // groups before expert e
+
+  // per-thread load assignments
+  int w_mat[WCH], w_row[WCH], w_half[WCH];
+  bool w_act[WCH];
+#pragma unroll
+  for (int i = 0; i < WCH; ++i) {
+    const int t = tid + i * NT;
+    w_act[i] = t < 2 * BN * NB;
+    w_mat[i] = w_act[i] ? t / (2 * BN) : 0;
+    w_row[i] = (t % (2 * BN)) >> 1;
+    w_half[i] = t & 1;
+  }
+  const unsigned char *x_src[XCH];  // row base of each activation load (nullptr: zero row)
+  int x_pl[XCH], x_row[XCH], x_seg[XCH];
+  bool x_act[XCH];
+#pragma unroll
+  for (int i = 0; i < XCH; ++i) {
+    const int t = tid + i * NT;
+    x_act[i] = t < 8 * BM * NA;
+    x_pl[i] = x_act[i] ? t / (8 * BM) : 0;
+    x_row[i] = (t % (8 * BM)) >> 3;
+    x_seg[i] = t & 7;
+    x_src[i] = nullptr;
+    if (x_act[i] && x_row[i] < rows) {
+      const int64_t slot = row0 + x_row[i];
+      if constexpr (MODE == MG_GATEUP) {
+        const int64_t tok = p.perm[slot] / (uint32_t)p.top_k;
+        x_src[i] = reinterpret_cast<const unsigned char *>(p.a0) + tok * p.lda * 2;
+      } else {
+        x_src[i] = reinterpret_cast<const unsigned char *>(x_pl[i] ? p.a1 : p.a0) + slot * p.lda * 2;
+      }
+    }
+  }
+
+  uint4 wq[WCH];
+  float ws_[WCH], wb_[WCH];
+  uint4 xq[XCH];
+
+  auto load_step = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < WCH; ++i) {
+      const int o = n0 + w_row[i];
+      const int kc = kt * 2 + w_half[i];
+      if (w_act[i] && o < p.n_out && kc < cpr) {
+        const uint32_t *codes = w_mat[i] ? p.codes1 : p.codes0;
+        const void *sc = w_mat[i] ? p.scales1 : p.scales0;
+        const void *bi = w_mat[i] ? p.biases1 : p.biases0;
+        wq[i] = reinterpret_cast<const uint4 *>(codes + ecodes + (int64_t)o * (p.k_in / 8))[kc];
+        const int64_t gi = esb + (int64_t)o * gpr + (((int64_t)kc * 32) >> p.log2_group);
+        if (p.sb_bf16) {
+          ws_[i] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(sc)[gi] << 16);
+          wb_[i] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(bi)[gi] << 16);
+        } else {
+          ws_[i] = reinterpret_cast<const float *>(sc)[gi];
+          wb_[i] = reinterpret_cast<const float *>(bi)[gi];
+        }
+      } else {
+        wq[i] = make_uint4(0, 0, 0, 0);
+        ws_[i] = 0.f;
+        wb_[i] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+      const int k = kt * BK + x_seg[i] * 8;
+      if (x_src[i] && k < p.k_in)
+        xq[i] = *reinterpret_cast<const uint4 *>(x_src[i] + (int64_t)k * 2);
+      else
+        xq[i] = make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  auto store_step = [&]() {
+#pragma unroll
+    for (int i = 0; i < WCH; ++i) {
+      if (!w_act[i]) continue;
+      uint16_t *dst = sw[w_mat[i]] + w_row[i] * LDK + w_half[i] * 32;
+      const uint32_t w4[4] = {wq[i].x, wq[i].y, wq[i].z, wq[i].w};
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        *reinterpret_cast<uint4 *>(dst + jj * 8) = dequant_word(w4[jj], ws_[i], wb_[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < XCH; ++i)
+      if (x_act[i]) *reinterpret_cast<uint4 *>(sa[x_pl[i]] + x_row[i] * LDK + x_seg[i] * 8) = xq[i];
+  };
+
+  f32x16_t acc[NB][FM][FN];
+#pragma unroll
+  for (int m = 0; m < NB; ++m)
+#pragma unroll
+    for (int a = 0; a < FM; ++a)
+#pragma unroll
+      for (int b = 0; b < FN; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[m][a][b][v] = 0.f;
+
+  load_step(0);
+  for (int kt = 0; kt < nsteps; ++kt) {
+    store_step();
+    lds_barrier();
+    if (kt + 1 < nsteps) load_step(kt + 1);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int koff = kk * 16 + (lane >> 5) * 8;
+      bf16x8_t af[NA][FM], bfr[NB][FN];
+#pragma unroll
+      for (int pl = 0; pl < NA; ++pl)
+#pragma unroll
+        for (int a = 0; a < FM; ++a)
+          af[pl][a] = *reinterpret_cast<const bf16x8_t *>(sa[pl] + (wm * TM + a * 32 + (lane & 31)) * LDK + koff);
+#pragma unroll
+      for (int m = 0; m < NB; ++m)
+#pragma unroll
+        for (int b = 0; b < FN; ++b)
+          bfr[m][b] = *reinterpret_cast<const bf16x8_t *>(sw[m] + (wn * TN + b * 32 + (lane & 31)) * LDK + koff);
+#pragma unroll
+      for (int m = 0; m < NB; ++m)
+#pragma unroll
+        for (int a = 0; a < FM; ++a)
+#pragma unroll
+          for (int b = 0; b < FN; ++b)
+#pragma unroll
+            for (int pl = 0; pl < NA; ++pl)
+              acc[m][a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[pl][a], bfr[m][b], acc[m][a][b], 0, 0, 0);
+    }
+    lds_barrier();
+  }
+
+  // epilogue: accumulator element v of lane l is row 8*(v/4) + 4*(l/32) + v%4,
+  // column l%32 of the 32x32 sub-tile
+#pragma unroll
+  for (int a = 0; a < FM; ++a)
+#pragma unroll
+    for (int b = 0; b < FN; ++b) {
+      const int col = n0 + wn * TN + b * 32 + (lane & 31);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = wm * TM + a * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (r < rows && col < p.n_out) {
+          const int64_t i = (row0 + r) * p.n_out + col;
+          if constexpr (MODE == MG_GATEUP) {
+            const float g = acc[0][a][b][v], u = acc[1][a][b][v];
+            const float h = (g / (1.f + __expf(-g))) * u;
+            const __bf16 hi = (__bf16)h;
+            reinterpret_cast<__bf16 *>(p.y0)[i] = hi;
+            reinterpret_cast<__bf16 *>(p.y1)[i] = (__bf16)(h - (float)hi);
+          } else {
+            reinterpret_cast<float *>(p.y0)[i] = acc[0][a][b][v];
+          }
+        }
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 4. unpermute + combine
+// ---------------------------------------------------------------------------
+
+// One thread per (token, 8 consecutive outputs).
+__global__ void __launch_bounds__(256)
+    moe_combine_kernel(const float *__restrict__ d, const uint32_t *__restrict__ pos,
+                       const float *__restrict__ wts, int top_k, const void *__restrict__ residual,
+                       void *__restrict__ out, int out_bf16, int64_t T, int hidden) {
+  const int n8 = hidden / 8;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= T * n8) return;
+  const int64_t t = i / n8;
+  const int c = (int)(i % n8) * 8;
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  for (int k = 0; k < top_k; ++k) {
+    const uint32_t s = pos[t * top_k + k];
+    if (s == kNoSlot) continue;
+    const float w = wts[t * top_k + k];
+    const float4 *src = reinterpret_cast<const float4 *>(d + (int64_t)s * hidden + c);
+    const float4 a = src[0], b = src[1];
+    acc[0] = fmaf(w, a.x, acc[0]);
+    acc[1] = fmaf(w, a.y, acc[1]);
+    acc[2] = fmaf(w, a.z, acc[2]);
+    acc[3] = fmaf(w, a.w, acc[3]);
+    acc[4] = fmaf(w, b.x, acc[4]);
+    acc[5] = fmaf(w, b.y, acc[5]);
+    acc[6] = fmaf(w, b.z, acc[6]);
+    acc[7] = fmaf(w, b.w, acc[7]);
+  }
+  const int64_t o = t * hidden + c;
+  if (out_bf16) {
+    if (residual) {
+      const uint4 r = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(residual) + o);
+      const uint32_t rr[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[2 * j] += __uint_as_float(rr[j] << 16);
+        acc[2 * j + 1] += __uint_as_float(rr[j] & 0xFFFF0000u);
+      }
+    }
+    uint4 v;
+    v.x = pack_bf16x2(acc[0], acc[1]);
+    v.y = pack_bf16x2(acc[2], acc[3]);
+    v.z = pack_bf16x2(acc[4], acc[5]);
+    v.w = pack_bf16x2(acc[6], acc[7]);
+    *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(out) + o) = v;
+  } else {
+    if (residual) {
+      const float4 *r = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(residual) + o);
+      const float4 a = r[0], b = r[1];
+      acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+      acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+    }
+    float4 *dst = reinterpret_cast<float4 *>(reinterpret_cast<float *>(out) + o);
+    dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  }
+}
+
+template <int MODE, int BM, int BN, int WM, int WN>
+hipError_t launch_mg(MoeGemmParams p, hipStream_t stream) {
+  const int64_t grid = (int64_t)p.max_mtiles * ((p.n_out + BN - 1) / BN);
+  hipLaunchKernelGGL((moe_gemm_kernel<MODE, BM, BN, WM, WN>), dim3((unsigned)grid),
+                     dim3(WM * WN * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_mode(const MoeGemmParams &p, int bm, hipStream_t stream) {
+  if (bm == 32) return launch_mg<MODE, 32, 128, 1, 4>(p, stream);
+  if (bm == 64) return launch_mg<MODE, 64, 64, 2, 2>(p, stream);
+  if (bm == 128) return launch_mg<MODE, 128, 64, 2, 2>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_moe_sort(const uint32_t *ids, int64_t n_pairs, int n_experts, int bm, uint32_t *perm,
+                           uint32_t *pos, uint32_t *tiles, int max_tiles, hipStream_t stream) {
+  hipLaunchKernelGGL(moe_sort_kernel, dim3(1), dim3(kSortThreads), 0, stream, ids, n_pairs, n_experts,
+                     bm, perm, pos, tiles, max_tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_gemm(const MoeGemmParams &p, int down, int bm, hipStream_t stream) {
+  return down ? launch_mode<MG_DOWN>(p, bm, stream) : launch_mode<MG_GATEUP>(p, bm, stream);
+}
+
+hipError_t launch_moe_combine(const float *d, const uint32_t *pos, const float *wts, int top_k,
+                              const void *residual, void *out, int out_bf16, int64_t T, int hidden,
+                              hipStream_t stream) {
+  const int64_t n = T * (hidden / 8);
+  const int64_t grid = (n + 255) / 256;
+  hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)grid), dim3(256), 0, stream, d, pos, wts,
+                     top_k, residual, out, out_bf16, T, hidden);
+  return hipGetLastError();
+}
+
+}  // namespace qint4

@@ -241,6 +241,52 @@ qint4_status moe_gather_qgemv_int4(const qint4_matrix *gate, const qint4_matrix 
                                    void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Bytes of device workspace one moe_prefill_qgemm_int4 call needs (0 for
+ * invalid sizes: T * top_k must be in [1, 2^24], n_experts <= 4096).
+ */
+size_t moe_prefill_qgemm_int4_workspace_bytes(int64_t T, int32_t top_k, int32_t n_experts,
+                                              int64_t hidden, int64_t inter);
+
+/*
+ * moe_prefill_qgemm_int4 -- T tokens through a top-K mixture of experts at
+ * once (prefill), on bf16 matrix cores:
+ *
+ *   out[t] = residual[t] + sum_{k < top_k} wts[t][k] * W'_down[e] h_tk,
+ *   h_tk   = silu(W'_gate[e] x[t]) * (W'_up[e] x[t]),   e = ids[t][k]
+ *
+ * where W' are the weights dequantised in float32 and rounded to bfloat16
+ * (nearest even), as in qgemm_int4_padT; accumulation is float32 and h is
+ * carried between the two products to float32 accuracy (two bf16 planes).
+ *
+ * [FFAI #9], batched MoE commits: the T * top_k (token, slot) rows are fanned
+ * into one GEMM per gate / up / down, sorted by expert id so that a row tile
+ * shares one expert's weights, with CSR expert offsets built from the sorted
+ * ids, and a scatter-sum unpermutes the rows afterwards.  [FFAI #14]: the
+ * chain8 weighted combine and the residual add.  Here the sort runs on the
+ * device, so ids produced by moe_router_topk are used without a host read.
+ *
+ *   gate, up  stacks [E][inter][hidden]; down [E][hidden][inter]; shared E
+ *             (<= 4096), group_size and sb_dtype
+ *   x         device bf16 [T][ldx], 16-byte aligned; ldx >= hidden, ldx % 8 == 0
+ *   T         tokens, 1 <= T * top_k <= 2^24
+ *   ids       device uint32 [T][top_k]; an id >= E contributes nothing
+ *   wts       device float32 [T][top_k]
+ *   top_k     1..QINT4_TOPK_MAX
+ *   residual  device [T][hidden] of out_dtype, 16-byte aligned, or NULL
+ *   out       device [T][hidden], dtype out_dtype (QINT4_F32 or QINT4_BF16),
+ *             16-byte aligned; fully overwritten
+ *   workspace device scratch, 256-byte aligned, at least
+ *             moe_prefill_qgemm_int4_workspace_bytes(T, top_k, E, hidden,
+ *             inter) bytes; contents on entry ignored, on return unspecified
+ * Four kernel launches on `stream` (sort, gate/up, down, combine).
+ */
+qint4_status moe_prefill_qgemm_int4(const qint4_matrix *gate, const qint4_matrix *up,
+                                    const qint4_matrix *down, const void *x, int64_t T, int64_t ldx,
+                                    const uint32_t *ids, const float *wts, int32_t top_k,
+                                    const void *residual, void *out, int32_t out_dtype,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * qgemm_int4_padT -- prefill: Y[t][o] = sum_k bf16(w[o][k]) * X[t][k], t < T.
  *
  * [FFAI #9], dequantGemmDynamicM commit: T is padded up to a multiple of 32

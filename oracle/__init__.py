@@ -399,6 +399,25 @@ def round_bf16(v: np.ndarray) -> np.ndarray:
     return out
 
 
+def gemm_f64(w, X64: np.ndarray, round_w: bool = True, expert: Optional[int] = None,
+             threads: int = 1) -> Tuple[np.ndarray, np.ndarray]:
+    """Y[t][o] = sum_k w'[o][k] X64[t][k] and A = sum_k |w' X| for float64 rows X64
+    (w' = bf16(w) when round_w); one matrix or expert ``expert`` of a stack."""
+    c, s, b = _slab(w, expert)
+    c = np.ascontiguousarray(c, dtype=np.uint32)
+    sd = np.ascontiguousarray(widen(s, w.sb_dtype))
+    bd = np.ascontiguousarray(widen(b, w.sb_dtype))
+    X64 = np.ascontiguousarray(X64, dtype=np.float64)
+    if X64.ndim != 2 or X64.shape[1] != w.k_in:
+        raise ValueError("X must be [T][k_in]")
+    T = X64.shape[0]
+    Y = np.empty((T, w.n_out), dtype=np.float64)
+    A = np.empty((T, w.n_out), dtype=np.float64)
+    _load().orc_gemm(_p(c), _p(sd), _p(bd), w.n_out, w.k_in, w.group_size, _p(X64), T,
+                     int(bool(round_w)), _p(Y), _p(A), int(threads))
+    return Y, A
+
+
 def gemm(w, X: np.ndarray, x_dtype: str = BF16, round_w: bool = True,
          threads: int = 1) -> Tuple[np.ndarray, np.ndarray]:
     """Full Y[t][o] = sum_k w'[o][k] X[t][k] for all T rows (small sizes).
@@ -407,16 +426,58 @@ def gemm(w, X: np.ndarray, x_dtype: str = BF16, round_w: bool = True,
     away ([FFAI #9], dequantGemmDynamicM T-padding driver), so the result for
     the T real rows is this plain product; w' = bf16(w) when round_w.
     """
-    c = np.ascontiguousarray(w.codes, dtype=np.uint32)
-    sd = np.ascontiguousarray(widen(w.scales, w.sb_dtype))
-    bd = np.ascontiguousarray(widen(w.biases, w.sb_dtype))
-    X64 = np.ascontiguousarray(widen(X, x_dtype))
+    return gemm_f64(w, widen(X, x_dtype), round_w=round_w, threads=threads)
+
+
+def moe_prefill(gate, up, down, X: np.ndarray, ids: np.ndarray, wts: np.ndarray,
+                residual: Optional[np.ndarray], res_dtype: str = BF16,
+                tokens: Optional[Sequence[int]] = None, threads: int = 1):
+    """T tokens through the top-K MoE in the prefill form.
+
+    [FFAI #9], batched MoE commits: the T * topK (token, slot) rows are fanned
+    into one GEMM per gate / up / down, sorted by expert id, then unpermuted by
+    a scatter-sum.  Sorting and tiling change no row's value, so each token's
+    output is the decode step of moe() computed with the prefill GEMM's weights
+    w' = bf16(w) (the dequantised weight rounded to bfloat16, as in gemm()):
+      h_k = silu(W'_gate[e] x) * (W'_up[e] x),  out = residual + sum_k w_k W'_down[e] h_k,
+    e = ids[t][k]; ids outside [0, n_experts) contribute nothing.  X is bf16
+    [T][hidden]; residual (or None) is [T][hidden] in res_dtype.
+
+    Returns (out [n][hidden], a_out [n][hidden]) for the rows ``tokens``
+    (default: all), a_out bounding the float32 accumulation noise as in moe().
+    """
+    X64 = widen(X, BF16)
     T = X64.shape[0]
-    Y = np.empty((T, w.n_out), dtype=np.float64)
-    A = np.empty((T, w.n_out), dtype=np.float64)
-    _load().orc_gemm(_p(c), _p(sd), _p(bd), w.n_out, w.k_in, w.group_size, _p(X64), T,
-                     int(bool(round_w)), _p(Y), _p(A), int(threads))
-    return Y, A
+    tokens = range(T) if tokens is None else tokens
+    outs, mags = [], []
+    for t in tokens:
+        x64 = X64[t][None, :]
+        res64 = None if residual is None else widen(residual[t], res_dtype)
+        ds, scal, ms = [], [], []
+        for e, a_k in zip(ids[t], wts[t]):
+            e = int(e)
+            if e < 0 or e >= gate.n_experts:
+                continue
+            g, ag = gemm_f64(gate, x64, expert=e, threads=threads)
+            u, au = gemm_f64(up, x64, expert=e, threads=threads)
+            g, ag, u, au = g[0], ag[0], u[0], au[0]
+            h = swiglu(g, u)
+            a_h = 1.1 * np.abs(u) * ag + np.abs(silu(g)) * au
+            d, ad = gemm_f64(down, h[None, :], expert=e, threads=threads)
+            # the chained term: what h's error carries through |W'_down|
+            ad = ad[0] + (1.0 + 2.0 ** -8) * gemv_absw(down, a_h, expert=e, threads=threads)
+            ds.append(d[0])
+            scal.append(float(a_k))
+            ms.append(abs(float(a_k)) * ad)
+        if ds:
+            out = combine(res64, scal, ds)
+            a = np.sum(ms, axis=0) + (0.0 if res64 is None else np.abs(res64))
+        else:
+            out = np.zeros(down.n_out) if res64 is None else res64.copy()
+            a = np.zeros(down.n_out) if res64 is None else np.abs(res64)
+        outs.append(out)
+        mags.append(a)
+    return np.array(outs), np.array(mags)
 
 
 def gemm_entries(w, X: np.ndarray, t_idx: np.ndarray, o_idx: np.ndarray,

@@ -193,6 +193,14 @@ def moe_layer(seed: int = 3, n_experts: int = 128, hidden: int = 2048, inter: in
             "logits": logits, "x_dtype": BF16}
 
 
+def moe_prefill_layer(seed: int = 6, T: int = 256, n_experts: int = 128, hidden: int = 2048,
+                      inter: int = 768, group_size: int = 64) -> dict:
+    """Top-K MoE prefill: the moe_layer recipe with T rows of x, residual and
+    N(0,1) router logits (the decode workload's per-token draws, T at once)."""
+    return moe_layer(seed=seed, n_experts=n_experts, hidden=hidden, inter=inter,
+                     group_size=group_size, n_tokens=T)
+
+
 PREFILL_T = (32, 256, 1000, 1024, 4096)
 
 

@@ -215,3 +215,28 @@ def test_quantize_validation(lib):
     assert _quant(lib, scales=A + 0x200001) == 4
     assert _quant(lib, codes=A + 0x100) == 5                    # codes overlap w
     assert _quant(lib, biases=A + 0x200000 + 64) == 5           # biases overlap scales
+
+
+def _moep(lib, T=4, top_k=2, E=4, hidden=256, inter=128, x=A + 0x300000, ldx=256, ids=A + 0x310000,
+          wts=A + 0x320000, res=0, out=A + 0x400000, odt=1, ws=A + 0x1000000, ws_bytes=1 << 30):
+    g = _m(n_out=inter, k_in=hidden, e=E)
+    u = q.CMatrix(A + 0x500000, A + 0x600000, A + 0x700000, inter, hidden, 64, E, 1, 0)
+    d = q.CMatrix(A + 0x800000, A + 0x900000, A + 0xA00000, hidden, inter, 64, E, 1, 0)
+    return lib.moe_prefill_qgemm_int4(ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), x, T, ldx,
+                                      ids, wts, top_k, res, out, odt, ws, ws_bytes, None)
+
+
+def test_moe_prefill_validation(lib):
+    assert lib.moe_prefill_qgemm_int4_workspace_bytes(0, 8, 128, 2048, 768) == 0
+    assert lib.moe_prefill_qgemm_int4_workspace_bytes(1 << 22, 8, 128, 2048, 768) == 0
+    assert lib.moe_prefill_qgemm_int4_workspace_bytes(4, 8, 5000, 2048, 768) == 0
+    assert lib.moe_prefill_qgemm_int4_workspace_bytes(256, 8, 128, 2048, 768) > 256 * 8 * (2048 + 768) * 4
+    assert _moep(lib, x=0) == 1
+    assert _moep(lib, top_k=9) == 2
+    assert _moep(lib, T=0) == 2
+    assert _moep(lib, ldx=200) == 2
+    assert _moep(lib, odt=4) == 3
+    assert _moep(lib, x=A + 0x300008) == 4
+    assert _moep(lib, ws=A + 0x1000010) == 4
+    assert _moep(lib, ws_bytes=1024) == 6
+    assert _moep(lib, out=A + 0x300000 + 64) == 5                # out overlaps x

@@ -653,3 +653,68 @@ def test_quantize_codes_follow_rounded_not_raw_scale():
         q_raw = np.clip(np.rint((G - b32[..., None]) / s32[..., None]), 0, 15).reshape(64, 512)
     q = oracle.unpack(codes, 512)
     assert np.count_nonzero(q != q_raw) > 0
+
+
+# --------------------------------------------------------------------------
+# MoE prefill
+# --------------------------------------------------------------------------
+
+def _exact_bf16_moe(seed, E=5, hidden=128, inter=64):
+    """A MoE layer whose dequantised weights are bf16 values already (power-of-two
+    scales, biases multiples of the scale), so rounding to bf16 is the identity."""
+    rng = np.random.default_rng(seed)
+
+    def stack(n_out, k_in):
+        raw = rng.integers(0, 16, size=(E, n_out, k_in), dtype=np.uint8)
+        s = np.ldexp(1.0, -rng.integers(5, 9, size=(E, n_out, k_in // 64))).astype(np.float32)
+        b = (rng.integers(-10, -5, size=s.shape) * s).astype(np.float32)
+        return synth.QMatrix(codes=synth.pack_codes(raw), scales=synth.f32_to_bf16_bits(s),
+                             biases=synth.f32_to_bf16_bits(b), sb_dtype=synth.BF16, group_size=64,
+                             n_out=n_out, k_in=k_in, n_experts=E)
+    return stack(inter, hidden), stack(inter, hidden), stack(hidden, inter), rng
+
+
+def test_moe_prefill_equals_decode_moe_when_weights_are_bf16():
+    """With bf16-exact weights the prefill form is the pinned decode moe() token by token."""
+    gate, up, down, rng = _exact_bf16_moe(1)
+    T, K = 6, 3
+    X = synth.draw_activation(rng, (T, 128), synth.BF16)
+    ids = rng.integers(0, 5, size=(T, K))
+    ids[2, 1] = 9  # out of range: contributes nothing
+    wts = rng.uniform(0.1, 1.0, size=(T, K)).astype(np.float32)
+    res = synth.draw_activation(rng, (T, 128), synth.BF16)
+    out, a = oracle.moe_prefill(gate, up, down, X, ids, wts, res)
+    for t in range(T):
+        ref, a_ref = oracle.moe(gate, up, down, X[t], ids[t], wts[t], res[t], synth.BF16)
+        np.testing.assert_allclose(out[t], ref, rtol=1e-12, atol=1e-12 * float(np.max(a_ref)))
+
+
+def test_moe_prefill_rounds_weights_to_bf16():
+    """Generic weights: each expert's contribution is the prefill GEMM (pinned gemm())
+    of its rounded weights; one kept slot with weight 1 and no residual isolates it."""
+    d = synth.moe_layer(seed=4, n_experts=4, hidden=128, inter=64, n_tokens=2)
+    gate, up, down = d["gate"], d["up"], d["down"]
+    X = np.stack([d["x"][0], d["x"][1]])
+    ids = np.array([[2], [0]])
+    wts = np.ones((2, 1), np.float32)
+    out, _ = oracle.moe_prefill(gate, up, down, X, ids, wts, None)
+    for t in range(2):
+        e = int(ids[t][0])
+        xt = oracle.widen(X[t], synth.BF16)
+        W = lambda m: oracle.round_bf16(oracle.dequant(m, expert=e))
+        g, u = W(gate) @ xt, W(up) @ xt
+        h = g / (1.0 + np.exp(-g)) * u
+        np.testing.assert_allclose(out[t], W(down) @ h, rtol=1e-10, atol=1e-12)
+
+
+def test_moe_prefill_tokens_are_independent():
+    """Permuting the tokens permutes the outputs (no cross-token term)."""
+    gate, up, down, rng = _exact_bf16_moe(2)
+    T, K = 5, 2
+    X = synth.draw_activation(rng, (T, 128), synth.BF16)
+    ids = rng.integers(0, 5, size=(T, K))
+    wts = rng.uniform(0.1, 1.0, size=(T, K)).astype(np.float32)
+    out, _ = oracle.moe_prefill(gate, up, down, X, ids, wts, None)
+    perm = np.array([3, 0, 4, 1, 2])
+    out_p, _ = oracle.moe_prefill(gate, up, down, X[perm], ids[perm], wts[perm], None)
+    np.testing.assert_array_equal(out_p, out[perm])
