@@ -855,7 +855,17 @@ qint4_status qgemm_int4_padT(const qint4_matrix *w, const void *x, int64_t T, in
   p.log2_group = ilog2(w->group_size);
   p.y_bf16 = y_dtype == QINT4_BF16;
   p.sb_bf16 = w->sb_dtype == QINT4_BF16;
-  hipError_t e = launch_gemm(p, reinterpret_cast<hipStream_t>(stream));
+  // T <= 64: weights straight from HBM into MFMA registers (qgemm_stream.hip),
+  // activation tiles in LDS; longer T: LDS-tiled weights (qgemm.hip), which
+  // amortise the dequantisation over more rows.  The stream kernel addresses
+  // X through 32-bit byte offsets.  (Measured on MI355X at N = 17408,
+  // K = 5120: T = 16 / 32 / 64 in 41 / 45 / 63 us against 80 / 82 / 93 us.)
+  const bool x_fits = (T - 1) * ldx + w->k_in < ((int64_t)1 << 30);
+  hipError_t e;
+  if (x_fits && T <= 64)
+    e = launch_gemm_stream(p, 0, reinterpret_cast<hipStream_t>(stream));
+  else
+    e = launch_gemm(p, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(QINT4_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
 }

@@ -126,6 +126,9 @@ struct GemmParams {
 };
 
 hipError_t launch_gemm(const GemmParams &p, hipStream_t stream);
+// Register-resident-weight GEMM (qgemm_stream.hip); cfg selects the token
+// block / row tiles per wave / waves / prefetch depth.
+hipError_t launch_gemm_stream(const GemmParams &p, int cfg, hipStream_t stream);
 
 // Top-k expert routing of n_rows rows of router logits (float32 or bf16):
 // ids/wts are [n_rows][top_k].
