@@ -22,6 +22,7 @@ Workloads (default: qkv):
            each step routes its token's logits on the GPU first (--router pre-drawn: skip)
   prefill  K=5120, N=17408 dequant GEMM on bf16 MFMA (--T rows, default 256)
   moeprefill  --T tokens through the 128-expert top-8 layer at once (router + sorted GEMMs)
+  copy     calibration: a 256 MiB device copy (reference for the HBM byte counters)
   quant    the offline quantiser: 17408x5120 float32 -> g64 codes, bf16 scales/biases
 
 Prints one JSON line.  ``value`` is weight GB/s for the decode workloads and
@@ -44,6 +45,47 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 POOL_BYTES = 1 << 30
+
+# HBM traffic per step from rocprofv3 counters (one pass with FETCH_SIZE, one
+# with WRITE_SIZE, KiB per dispatch, summed over the step's library kernels).
+# Scale factors from the copy workload (256 MiB read + 256 MiB written per
+# dispatch): FETCH_SIZE read 131,087 KiB -> x2.000; WRITE_SIZE 262,144 KiB -> x1.000.
+# Valid only for the kernel sources they were taken with (SOURCE_HASH); any
+# change to a kernel source makes the figure null until it is measured again.
+TRAFFIC_FETCH_SCALE = 262144.0 / 131087.3
+TRAFFIC_WRITE_SCALE = 1.0
+TRAFFIC_SOURCE_HASH = "3813cec2a2176e8c"
+TRAFFIC_KIB = {  # workload: (FETCH_SIZE KiB, WRITE_SIZE KiB) per step, unscaled
+    "qkv_multi_t1": (7061.1, 16.0),
+    "dense_ffn_t1": (49295.3 + 25354.8, 110.6 + 16.0),
+    "moe_top8_t1": (8.8 + 7020.8 + 3825.2, 0.1 + 24.0 + 8.0),
+    "prefill_gemm_T32": (25878.3, 1088.0),
+    "prefill_gemm_T4096": (478425.1, 161234.2),
+    "moe_prefill_top8_T256": (131.8 + 8.0 + 763218.2 + 94260.9 + 8757.5, 16.0 + 17.5 + 6144.0 + 16384.0 + 1024.0),
+    "quantize_17408x5120_f32_g64": (174106.5, 48960.0),
+}
+
+
+def kernel_source_hash() -> str:
+    import glob
+    import hashlib
+    csrc = os.path.join(ROOT, "dequant_matmul_int4_amd", "csrc")
+    files = sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h")) +
+                   glob.glob(os.path.join(csrc, "*.cpp")))
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_bytes(workload_name: str):
+    """Measured HBM bytes per step, or None (not measured, or kernels changed since)."""
+    t = TRAFFIC_KIB.get(workload_name)
+    if t is None or kernel_source_hash() != TRAFFIC_SOURCE_HASH:
+        return None
+    return (t[0] * TRAFFIC_FETCH_SCALE + t[1] * TRAFFIC_WRITE_SCALE) * 1024.0
 METRIC = "weight GB/s and % of HBM peak for T=1 int4 GEMV; tokens/s-equivalent"
 
 
@@ -54,13 +96,16 @@ def parse():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="qkv",
                     choices=["single", "qkv", "rmsqkv", "smallm", "dense", "moe", "moeprefill", "prefill",
-                             "quant"])
+                             "quant", "copy"])
     ap.add_argument("--T", type=int, default=None,
                     help="prefill rows (default 256) or small-M tokens (default 4)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-time budget of the CPU oracle sample (0 disables)")
     ap.add_argument("--router", choices=("gpu", "pre-drawn"), default="gpu",
                     help="moe: route each token on the GPU (default) or use pre-drawn ids/weights")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch the steps one by one instead of replaying a HIP graph "
+                         "(for counter collection; the timing then includes launch gaps)")
     ap.add_argument("--layers", type=int, default=64,
                     help="dense layers per token assumed for tokens/s-equivalent")
     return ap.parse_args()
@@ -217,6 +262,31 @@ class Quant(Workload):
             self.pool[i % self.R].data_ptr(), self.q.F32, 17408, 5120, 64, self.q.BF16,
             o.codes.data_ptr(), o.scales.data_ptr(), o.biases.data_ptr(),
             self.torch.cuda.current_stream().cuda_stream))
+
+
+class Copy(Workload):
+    """Calibration only: torch's device-to-device copy of a known number of bytes
+    (256 MiB read + 256 MiB written per step), the reference for the HBM byte
+    counters the roofline's traffic figures are scaled by."""
+    name = "copy_256MiB"
+    dominant = "torch elementwise copy"
+
+    def __init__(self, q, synth, torch):
+        self.nbytes = 256 << 20
+        self.src = [torch.empty(self.nbytes // 4, device="cuda").uniform_() for _ in range(4)]
+        self.dst = torch.empty_like(self.src[0])
+        self.R = 4
+        self.config = {"workload": self.name, "bytes_read": self.nbytes, "bytes_written": self.nbytes}
+        self.dtype = "f32"
+
+    def weight_bytes(self):
+        return self.nbytes
+
+    def algo_bytes(self):
+        return 2 * self.nbytes
+
+    def step(self, i):
+        self.dst.copy_(self.src[i % self.R])
 
 
 class Dense(Workload):
@@ -541,6 +611,8 @@ def main():
         wl = RmsQKV(q, synth, torch)
     elif args.workload == "quant":
         wl = Quant(q, synth, torch)
+    elif args.workload == "copy":
+        wl = Copy(q, synth, torch)
     elif args.workload == "moeprefill":
         wl = MoEPrefill(q, synth, torch, args.T)
     elif args.workload == "dense":
@@ -562,28 +634,40 @@ def main():
         wl.step(0)
     stream.synchronize()
 
-    g_warm = torch.cuda.CUDAGraph()
-    g_main = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_warm, stream=stream):
-        for i in range(W):
-            wl.step(i)
-    with torch.cuda.graph(g_main, stream=stream):
-        for i in range(K):
-            wl.step(W + i)
-    torch.cuda.synchronize()
-
-    with torch.cuda.stream(stream):
-        g_warm.replay()
-    torch.cuda.synchronize()
-
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        ev0.record(stream)
-        g_main.replay()
-        ev1.record(stream)
-    torch.cuda.synchronize()
+    if args.no_graph:
+        with torch.cuda.stream(stream):
+            for i in range(W):
+                wl.step(i)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            ev0.record(stream)
+            for i in range(K):
+                wl.step(W + i)
+            ev1.record(stream)
+        torch.cuda.synchronize()
+    else:
+        g_warm = torch.cuda.CUDAGraph()
+        g_main = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_warm, stream=stream):
+            for i in range(W):
+                wl.step(i)
+        with torch.cuda.graph(g_main, stream=stream):
+            for i in range(K):
+                wl.step(W + i)
+        torch.cuda.synchronize()
+
+        with torch.cuda.stream(stream):
+            g_warm.replay()
+        torch.cuda.synchronize()
+
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            ev0.record(stream)
+            g_main.replay()
+            ev1.record(stream)
+        torch.cuda.synchronize()
     ms_total = ev0.elapsed_time(ev1)
     ms_step = ms_total / K
     print("# timed %d steps in %.3f ms" % (K, ms_total), file=sys.stderr, flush=True)
@@ -604,11 +688,11 @@ def main():
         if t_mfma >= t_hbm:
             out["roofline"] = {"bound": "mfma", "achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS,
                                "unit": "TFLOP/s", "frac": tflops / BF16_MFMA_PEAK_TFLOPS,
-                               "traffic": None, "kernel": wl.dominant,
+                               "traffic": traffic_bytes(wl.name), "kernel": wl.dominant,
                                "launches_per_step": wl.launches_per_step}
         else:
             out["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                               "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": wl.dominant,
+                               "frac": gbs / HBM_PEAK_GBS, "traffic": traffic_bytes(wl.name), "kernel": wl.dominant,
                                "launches_per_step": wl.launches_per_step}
     elif isinstance(wl, Prefill):
         tflops = wl.flops / (ms_step * 1e-3) / 1e12
@@ -616,7 +700,7 @@ def main():
                     "weight_GBps": wl.weight_bytes() / (ms_step * 1e-3) / 1e9,
                     "mfma_util": tflops / BF16_MFMA_PEAK_TFLOPS})
         out["roofline"] = {"bound": "mfma", "achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS,
-                           "unit": "TFLOP/s", "frac": tflops / BF16_MFMA_PEAK_TFLOPS, "traffic": None}
+                           "unit": "TFLOP/s", "frac": tflops / BF16_MFMA_PEAK_TFLOPS, "traffic": traffic_bytes(wl.name)}
     else:
         gbs = wl.weight_bytes() / (ms_step * 1e-3) / 1e9
         out.update({"value": gbs, "unit": "GB/s", "pct_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS,
@@ -633,9 +717,9 @@ def main():
         # two-launch workloads the pair is timed as one unit)
         ach = wl.algo_bytes() / (ms_step * 1e-3) / 1e9
         out["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": ach / HBM_PEAK_GBS, "traffic": None, "kernel": wl.dominant,
+                           "frac": ach / HBM_PEAK_GBS, "traffic": traffic_bytes(wl.name), "kernel": wl.dominant,
                            "launches_per_step": wl.launches_per_step}
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and args.workload != "copy":
         out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds, args.T)
     print(json.dumps(out), flush=True)
 
