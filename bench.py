@@ -19,7 +19,8 @@ Workloads (default: qkv):
   smallm   the q/k/v set for --T tokens (1..8, default 4) in one launch
   dense    gate/up 5120->17408 with SwiGLU (fp32 h), then down 17408->5120
   moe      top-8 of 128 experts, hidden 2048, inter 768, weighted combine + residual;
-           each step routes its token's logits on the GPU first (--router pre-drawn: skip)
+           each step routes its token's logits inside the gate/up launch (--router gpu: with the
+           separate router kernel; --router pre-drawn: host-drawn ids)
   prefill  K=5120, N=17408 dequant GEMM on bf16 MFMA (--T rows, default 256)
   moeprefill  --T tokens through the 128-expert top-8 layer at once (router + sorted GEMMs)
   copy     calibration: a 256 MiB device copy (reference for the HBM byte counters)
@@ -101,8 +102,9 @@ def parse():
                     help="prefill rows (default 256) or small-M tokens (default 4)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-time budget of the CPU oracle sample (0 disables)")
-    ap.add_argument("--router", choices=("gpu", "pre-drawn"), default="gpu",
-                    help="moe: route each token on the GPU (default) or use pre-drawn ids/weights")
+    ap.add_argument("--router", choices=("fused", "gpu", "pre-drawn"), default="fused",
+                    help="moe: route each token inside the gate/up launch (default), with the "
+                         "separate router kernel, or use pre-drawn ids/weights")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch the steps one by one instead of replaying a HIP graph "
                          "(for counter collection; the timing then includes launch gaps)")
@@ -332,12 +334,13 @@ class MoE(Workload):
     launches_per_step = 3
     dominant = "router_topk + qgemv_kernel EPI_SWIGLU (expert gate/up) + EPI_MOE_DOWN"
 
-    def __init__(self, q, synth, torch, gpu_router=True):
+    def __init__(self, q, synth, torch, router="fused"):
         self.q = q
-        self.gpu_router = gpu_router
-        if not gpu_router:
+        self.router = router
+        if router != "gpu":
             self.launches_per_step = 2
-            self.dominant = "qgemv_kernel EPI_SWIGLU (expert gate/up) + EPI_MOE_DOWN"
+            self.dominant = "qgemv_kernel EPI_SWIGLU (expert gate/up%s) + EPI_MOE_DOWN" % (
+                ", routing its token" if router == "fused" else "")
         E, H, I, K = 128, 2048, 768, 8
         stacks = []
         r = 0
@@ -369,7 +372,7 @@ class MoE(Workload):
         self.wb = 3 * K * per_expert            # gate + up + down of the 8 kept experts
         self.config = {"workload": self.name, "n_experts": E, "top_k": K, "hidden": H, "inter": I,
                        "group_size": 64, "sb_dtype": "bf16", "x_dtype": "bf16",
-                       "router_draws": 1024, "router": "gpu" if gpu_router else "pre-drawn",
+                       "router_draws": 1024, "router": router,
                        "pool_copies": self.R}
         self.dtype = "bf16"
 
@@ -382,7 +385,11 @@ class MoE(Workload):
     def step(self, i):
         g, u, d = self.pool[i % self.R]
         j = i % self.ids.shape[0]
-        if self.gpu_router:  # route this token's logits on the device, then gather
+        if self.router == "fused":  # routed inside the gate/up launch
+            self.q.moe_route_gather_qgemv_int4(g, u, d, self.x, self.logits[j], 8, self.ids_buf,
+                                               self.wts_buf, self.out, self.ws, residual=self.res)
+            return
+        if self.router == "gpu":  # route this token's logits on the device, then gather
             self.q.moe_router_topk(self.logits[j], 8, self.ids_buf, self.wts_buf)
             ids, wts = self.ids_buf, self.wts_buf
         else:
@@ -620,7 +627,7 @@ def main():
     elif args.workload == "smallm":
         wl = SmallM(q, synth, torch, args.T)
     elif args.workload == "moe":
-        wl = MoE(q, synth, torch, gpu_router=args.router == "gpu")
+        wl = MoE(q, synth, torch, router=args.router)
     else:
         wl = Prefill(q, synth, torch, args.T)
     torch.cuda.synchronize()

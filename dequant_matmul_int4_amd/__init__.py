@@ -78,6 +78,9 @@ SIGNATURES = [
     ("moe_gather_qgemv_int4", _I32, [ctypes.POINTER(CMatrix), ctypes.POINTER(CMatrix),
                                      ctypes.POINTER(CMatrix), _P, _P, _P, _I32, _P, _P, _I32,
                                      _P, ctypes.c_size_t, _P]),
+    ("moe_route_gather_qgemv_int4", _I32, [ctypes.POINTER(CMatrix), ctypes.POINTER(CMatrix),
+                                           ctypes.POINTER(CMatrix), _P, _P, _I32, _I32, _P, _P, _I32,
+                                           _P, _P, _P, ctypes.c_size_t, _P]),
     ("qgemm_int4_padT", _I32, [ctypes.POINTER(CMatrix), _P, _I64, _I64, _P, _I64, _I32, _P]),
     ("moe_router_topk", _I32, [_P, _I32, _I64, _I32, _I32, _P, _P, _P]),
     ("moe_prefill_qgemm_int4_workspace_bytes", ctypes.c_size_t, [_I64, _I32, _I32, _I64, _I64]),
@@ -263,6 +266,26 @@ def moe_prefill_qgemm_int4(gate: QInt4Matrix, up: QInt4Matrix, down: QInt4Matrix
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
+def moe_route_gather_qgemv_int4(gate: QInt4Matrix, up: QInt4Matrix, down: QInt4Matrix,
+                                x: torch.Tensor, logits: torch.Tensor, top_k: int,
+                                ids: torch.Tensor, wts: torch.Tensor, out: torch.Tensor,
+                                workspace: torch.Tensor, residual: Optional[torch.Tensor] = None,
+                                stream=None) -> None:
+    """moe_router_topk + moe_gather_qgemv_int4 for one token, routed inside the gate/up launch.
+    logits: [n_experts] float32/bfloat16 (n_experts <= 256); ids (int32/uint32) and wts
+    (float32) [top_k] are outputs."""
+    if ids.dtype not in (torch.int32, torch.uint32) or wts.dtype != torch.float32:
+        raise TypeError("ids must be int32/uint32 and wts float32")
+    if residual is not None and residual.dtype != x.dtype:
+        raise TypeError("residual must have x's dtype")
+    g, u, d = gate.c(), up.c(), down.c()
+    _check(load().moe_route_gather_qgemv_int4(
+        ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), _dev(x, "x"), _dev(logits, "logits"),
+        _dt(logits), int(top_k), None if residual is None else _dev(residual, "residual"),
+        _dev(out, "out"), _dt(x), _dev(ids, "ids"), _dev(wts, "wts"), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
 SMALLM_MAX = 8
 
 
@@ -362,4 +385,5 @@ __all__ = ["QInt4Matrix", "Int4Error", "qgemv_int4", "qgemv_int4_multi", "qgemv_
            "moe_gather_qgemv_int4", "moe_gather_qgemv_int4_workspace_bytes", "qgemm_int4_padT",
            "moe_router_topk", "rms_norm_qgemv_int4", "quantize_int4",
            "moe_prefill_qgemm_int4", "moe_prefill_qgemm_int4_workspace_bytes",
+           "moe_route_gather_qgemv_int4",
            "load", "F32", "BF16", "EPI_NONE", "EPI_SWIGLU_PAIR", "LIB_PATH", "SIGNATURES"]

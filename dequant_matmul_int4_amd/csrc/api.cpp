@@ -399,7 +399,7 @@ qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t
   set_geometry(p, plan, nc, nc, k_in / 2, sbrow, ws[0].group_size);
   p.y_bf16 = y_dtype == QINT4_BF16;
   p.x = x;
-  p.gamma = gamma;
+  p.aux = gamma;
   p.eps = eps;
   p.n_tok = (int32_t)T;
   p.ldx = (int32_t)ldx;
@@ -453,13 +453,18 @@ size_t moe_gather_qgemv_int4_workspace_bytes(int64_t inter, int32_t top_k) {
   return (size_t)top_k * (size_t)inter * sizeof(float);
 }
 
-qint4_status moe_gather_qgemv_int4(const qint4_matrix *gate, const qint4_matrix *up,
-                                   const qint4_matrix *down, const void *x, const uint32_t *ids,
-                                   const float *wts, int32_t top_k, const void *residual, void *out,
-                                   int32_t act_dtype, void *workspace, size_t workspace_bytes,
-                                   void *stream_) {
-  const char *fn = "moe_gather_qgemv_int4";
-  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+}  // extern "C"
+
+namespace {
+
+// Shared body of moe_gather_qgemv_int4 and moe_route_gather_qgemv_int4
+// (logits != NULL: the gate/up launch ranks the logits itself and writes ids
+// and wts, which the down launch then reads).
+qint4_status run_moe(const qint4_matrix *gate, const qint4_matrix *up, const qint4_matrix *down,
+                     const void *x, const uint32_t *ids, const float *wts, int32_t top_k,
+                     const void *residual, void *out, int32_t act_dtype, void *workspace,
+                     size_t workspace_bytes, hipStream_t stream, const char *fn,
+                     const void *logits, int32_t logits_dtype) {
   qint4_status st;
   if ((st = check_matrix(gate, "gate", true)) != QINT4_OK) return st;
   if ((st = check_matrix(up, "up", true)) != QINT4_OK) return st;
@@ -486,14 +491,25 @@ qint4_status moe_gather_qgemv_int4(const qint4_matrix *gate, const qint4_matrix 
   const size_t ab = elem_bytes(act_dtype);
   if (!aligned(out, ab) || (residual && !aligned(residual, ab)))
     return fail(QINT4_ERR_ALIGN, "%s: out/residual not aligned to element size", fn);
+  if (logits) {
+    if (!valid_dtype(logits_dtype))
+      return fail(QINT4_ERR_DTYPE, "%s: logits_dtype %d invalid", fn, logits_dtype);
+    if (gate->n_experts > kRouteMaxExperts || gate->n_experts < top_k)
+      return fail(QINT4_ERR_SHAPE,
+                  "%s: routing in the gate/up launch needs top_k <= n_experts <= %d (got %d); "
+                  "use moe_router_topk + moe_gather_qgemv_int4",
+                  fn, kRouteMaxExperts, gate->n_experts);
+    if (!aligned(logits, elem_bytes(logits_dtype)))
+      return fail(QINT4_ERR_ALIGN, "%s: logits not aligned to its element size", fn);
+  }
   const size_t need = moe_gather_qgemv_int4_workspace_bytes(inter, top_k);
   if (!workspace || workspace_bytes < need)
     return fail(QINT4_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn,
                 workspace ? workspace_bytes : (size_t)0, need);
   if (!aligned(workspace, 16)) return fail(QINT4_ERR_ALIGN, "%s: workspace not 16-byte aligned", fn);
 
-  Range ins[13], outs[2];
-  int ni = 0;
+  Range ins[14], outs[4];
+  int ni = 0, no = 0;
   static const char *gn[3] = {"gate.codes", "gate.scales", "gate.biases"};
   static const char *un[3] = {"up.codes", "up.scales", "up.biases"};
   static const char *dn[3] = {"down.codes", "down.scales", "down.biases"};
@@ -501,12 +517,18 @@ qint4_status moe_gather_qgemv_int4(const qint4_matrix *gate, const qint4_matrix 
   ni += add_matrix_ranges(up, un, ins + ni);
   ni += add_matrix_ranges(down, dn, ins + ni);
   ins[ni++] = range(x, (size_t)hidden * ab, "x");
-  ins[ni++] = range(ids, (size_t)top_k * 4, "ids");
-  ins[ni++] = range(wts, (size_t)top_k * 4, "wts");
+  if (logits) {  // ids and wts are outputs
+    ins[ni++] = range(logits, (size_t)gate->n_experts * elem_bytes(logits_dtype), "logits");
+    outs[no++] = range(ids, (size_t)top_k * 4, "ids");
+    outs[no++] = range(wts, (size_t)top_k * 4, "wts");
+  } else {
+    ins[ni++] = range(ids, (size_t)top_k * 4, "ids");
+    ins[ni++] = range(wts, (size_t)top_k * 4, "wts");
+  }
   if (residual) ins[ni++] = range(residual, (size_t)hidden * ab, "residual");
-  outs[0] = range(out, (size_t)hidden * ab, "out");
-  outs[1] = range(workspace, need, "workspace");
-  if ((st = check_no_overlap(outs, 2, ins, ni)) != QINT4_OK) return prefixed(st, fn);
+  outs[no++] = range(out, (size_t)hidden * ab, "out");
+  outs[no++] = range(workspace, need, "workspace");
+  if ((st = check_no_overlap(outs, no, ins, ni)) != QINT4_OK) return prefixed(st, fn);
 
   int n_cu = 256;
   if ((st = check_device(&n_cu)) != QINT4_OK) return prefixed(st, fn);
@@ -534,7 +556,10 @@ qint4_status moe_gather_qgemv_int4(const qint4_matrix *gate, const qint4_matrix 
     p.n_tok = 1;
     p.tasks_per_slot = (int32_t)((inter + rpt - 1) / rpt);
     p.x = x;
-    p.ids = ids;
+    p.ids = const_cast<uint32_t *>(ids);  // written only when routing
+    p.wts = const_cast<float *>(wts);
+    p.aux = logits;
+    p.route = logits ? (logits_dtype == QINT4_BF16 ? 2 : 1) : 0;
     p.top_k = top_k;
     p.n_experts = gate->n_experts;
     p.ecode_bytes = (uint32_t)(inter * (hidden / 2));
@@ -561,9 +586,9 @@ qint4_status moe_gather_qgemv_int4(const qint4_matrix *gate, const qint4_matrix 
     p.y_bf16 = act_dtype == QINT4_BF16;
     p.n_tok = 1;
     p.x = h;
-    p.ids = ids;
-    p.wts = wts;
-    p.residual = residual;
+    p.ids = const_cast<uint32_t *>(ids);  // read only
+    p.wts = const_cast<float *>(wts);
+    p.aux = residual;
     p.top_k = top_k;
     p.n_experts = down->n_experts;
     p.cpr_e = ncl;
@@ -576,6 +601,32 @@ qint4_status moe_gather_qgemv_int4(const qint4_matrix *gate, const qint4_matrix 
     if (e != hipSuccess) return fail(QINT4_ERR_LAUNCH, "%s: down launch failed: %s", fn, hipGetErrorString(e));
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+qint4_status moe_gather_qgemv_int4(const qint4_matrix *gate, const qint4_matrix *up,
+                                   const qint4_matrix *down, const void *x, const uint32_t *ids,
+                                   const float *wts, int32_t top_k, const void *residual, void *out,
+                                   int32_t act_dtype, void *workspace, size_t workspace_bytes,
+                                   void *stream) {
+  return run_moe(gate, up, down, x, ids, wts, top_k, residual, out, act_dtype, workspace,
+                 workspace_bytes, reinterpret_cast<hipStream_t>(stream), "moe_gather_qgemv_int4",
+                 nullptr, 0);
+}
+
+qint4_status moe_route_gather_qgemv_int4(const qint4_matrix *gate, const qint4_matrix *up,
+                                         const qint4_matrix *down, const void *x,
+                                         const void *logits, int32_t logits_dtype, int32_t top_k,
+                                         const void *residual, void *out, int32_t act_dtype,
+                                         uint32_t *ids, float *wts, void *workspace,
+                                         size_t workspace_bytes, void *stream) {
+  if (!logits) return fail(QINT4_ERR_NULL, "moe_route_gather_qgemv_int4: logits is NULL");
+  return run_moe(gate, up, down, x, ids, wts, top_k, residual, out, act_dtype, workspace,
+                 workspace_bytes, reinterpret_cast<hipStream_t>(stream),
+                 "moe_route_gather_qgemv_int4", logits, logits_dtype);
 }
 
 qint4_status moe_router_topk(const void *logits, int32_t logits_dtype, int64_t n_tokens,

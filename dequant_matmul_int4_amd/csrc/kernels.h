@@ -71,11 +71,18 @@ struct GemvParams {
   int32_t ldx;               // elements between consecutive activation rows
   float eps;                 // XM_RMS_*: RMSNorm epsilon
   const void *x;             // activation (bf16 bits or float32), 16-byte aligned
-  const uint32_t *ids;       // device [top_k] or nullptr
-  const float *wts;          // device [top_k] (EPI_MOE_DOWN)
-  const void *residual;      // device [n_out] or nullptr (EPI_MOE_DOWN)
-  const void *gamma;         // XM_RMS_*: RMSNorm weight [k_in], the activation's dtype
+  uint32_t *ids;             // device [top_k] or nullptr: read, or (route != 0) written by
+                             // the first wave of the grid
+  float *wts;                // device [top_k]: read (EPI_MOE_DOWN), or written when routing
+  const void *aux;           // EPI_MOE_DOWN: residual [n_out] or nullptr; XM_RMS_*: RMSNorm
+                             // weight [k_in] (the activation's dtype); routing: logits [n_experts]
+  int32_t route;             // EPI_SWIGLU: 0 = ids given; 1 / 2 = every wave ranks the float32 /
+                             // bf16 logits itself (n_experts <= kRouteMaxExperts)
+  int32_t pad_;
 };
+
+// Experts one wave ranks in registers when the gate/up launch routes its token.
+constexpr int kRouteMaxExperts = 256;
 
 struct GemvPlan {
   int tt;           // tokens per launch template: 1, 2, 4 or 8

@@ -68,6 +68,7 @@
 //     branches.
 
 #include "kernels.h"
+#include "topk_wave.h"
 
 namespace qint4 {
 namespace {
@@ -519,7 +520,26 @@ __global__ void __launch_bounds__(TT >= 8 ? 512 : 768) qgemv_kernel(const GemvPa
   // expert ids and slot weights, through the scalar cache: lane k of v_ids /
   // v_wts holds slot k's values
   uint32_t v_ids = 0, v_wts = 0;
-  if constexpr (EPI != EPI_STORE) {
+  // Routing (EPI_SWIGLU, p.route != 0): this token's router logits are loaded
+  // here (lane l: experts l, l + 64, ...; indices past n_experts clamped, so
+  // every load is unconditional) and ranked after the activation loads are
+  // issued, so the two round trips overlap.
+  constexpr int RK = kRouteMaxExperts / 64;
+  float key[RK];
+  if constexpr (EPI == EPI_SWIGLU) {
+    if (p.route) {
+#pragma unroll
+      for (int s = 0; s < RK; ++s) {
+        const int i = min(lane + 64 * s, p.n_experts - 1);
+        key[s] = p.route == 2 ? bf16_lo(reinterpret_cast<const uint16_t *>(p.aux)[i])
+                              : reinterpret_cast<const float *>(p.aux)[i];
+      }
+    } else if (p.ids) {
+      uint32_t s_ids[8];
+      scalar_load8(p.ids, p.top_k, s_ids);
+      v_ids = lanes_from_scalars(s_ids);
+    }
+  } else if constexpr (EPI == EPI_MOE_DOWN) {
     if (p.ids) {
       uint32_t s_ids[8];
       scalar_load8(p.ids, p.top_k, s_ids);
@@ -598,8 +618,7 @@ __global__ void __launch_bounds__(TT >= 8 ? 512 : 768) qgemv_kernel(const GemvPa
   };
 
   // ---- load stream ----
-  Cur lc;
-  start(lc);
+  Cur lc;  // started once the expert ids are known
   __amdgpu_buffer_rsrc_t rc[NS], rs[NS], rb[NS];
   auto set_rsrc = [&]() {
     if constexpr (EPI == EPI_STORE) {
@@ -625,7 +644,6 @@ __global__ void __launch_bounds__(TT >= 8 ? 512 : 768) qgemv_kernel(const GemvPa
       rb[0] = make_rsrc(p.m[0].biases, p.sb_bytes);
     }
   };
-  set_rsrc();
   int lstep = 0;   // steps issued by the load cursor
   int lit = 0;     // step inside the task
   uint32_t lstep_c = 0, lstep_s = 0;  // byte offsets of step lit inside a row
@@ -682,20 +700,47 @@ __global__ void __launch_bounds__(TT >= 8 ? 512 : 768) qgemv_kernel(const GemvPa
   float ssq = 0.f;  // XM_RMS_*: this thread's share of sum(x^2)
 #pragma unroll
   for (int t = 0; t < TT; ++t)
-    stage_early_rounds<XM>(x_tok(t), p.gamma, t < p.n_tok ? p.ncx : 0, ncx_pad, xbuf + t * tok_bytes,
+    stage_early_rounds<XM>(x_tok(t), p.aux, t < p.n_tok ? p.ncx : 0, ncx_pad, xbuf + t * tok_bytes,
                            reinterpret_cast<float *>(reinterpret_cast<unsigned char *>(xsum) + t * tok_bytes),
                            ssq);
   const int xbase = stage_last_base<XM>(p.ncx);
   XRegs<XM> xr[TT];
 #pragma unroll
   for (int t = 0; t < TT; ++t)  // activation loads first (L2), ...
-    stage_issue<XM>(x_tok(t), p.gamma, t < p.n_tok ? p.ncx : 0, xbase, xr[t]);
+    stage_issue<XM>(x_tok(t), p.aux, t < p.n_tok ? p.ncx : 0, xbase, xr[t]);
   uint4 rr[RQ];
-  const bool has_res = (EPI == EPI_MOE_DOWN) && p.residual != nullptr;
+  const bool has_res = (EPI == EPI_MOE_DOWN) && p.aux != nullptr;
   if constexpr (EPI == EPI_MOE_DOWN) {
     const uint32_t nvec = has_res ? (uint32_t)(p.y_bf16 ? p.m[0].n_out / 8 : p.m[0].n_out / 4) : 0u;
-    residual_issue(has_res ? p.residual : p.x, nvec, rr);
+    residual_issue(has_res ? p.aux : p.x, nvec, rr);
   }
+
+  if constexpr (EPI == EPI_SWIGLU) {
+    if (p.route) {
+      // rank the logits (every wave the same way); lane k < top_k takes slot
+      // k.  The first wave of the grid writes the ids and weights out for the
+      // down launch and the caller.
+      int sel_i[8];
+      float sel_v[8];
+      if (p.n_experts <= 128) {
+        const float k2[2] = {key[0], key[1]};
+        topk::select<2>(k2, p.n_experts, p.top_k, sel_i, sel_v);
+      } else {
+        topk::select<RK>(key, p.n_experts, p.top_k, sel_i, sel_v);
+      }
+      int id = 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (lane == k) id = sel_i[k];
+      v_ids = (uint32_t)id;
+      if (blockIdx.x == 0 && wave == 0 && lane < p.top_k) {
+        p.ids[lane] = (uint32_t)id;
+        p.wts[lane] = topk::slot_weight(sel_v, p.top_k, lane);
+      }
+    }
+  }
+  start(lc);
+  set_rsrc();
 
   // ... then the first D steps of codes (HBM).
   StepBuf<RT, NS> buf[D];

@@ -241,6 +241,32 @@ qint4_status moe_gather_qgemv_int4(const qint4_matrix *gate, const qint4_matrix 
                                    void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * moe_route_gather_qgemv_int4 -- moe_router_topk followed by
+ * moe_gather_qgemv_int4 for one token, with the routing done inside the
+ * gate/up launch: every wave of that launch ranks the token's logits itself
+ * (exactly as moe_router_topk does), so the router's separate launch and its
+ * dependency gap disappear.  ids and wts are written by the gate/up launch
+ * and read by the down launch; on return (after the stream work) they hold
+ * the same values moe_router_topk would have written, and out equals the
+ * two-call result bit for bit.
+ *
+ * [FFAI #14], GPU MoE router commit (router output threaded straight into the
+ * expert-indexed GEMV); the other passages as for moe_gather_qgemv_int4.
+ *
+ *   logits        device [n_experts], dtype logits_dtype (QINT4_F32 or
+ *                 QINT4_BF16), element-aligned; n_experts = the stacks'
+ *                 n_experts, top_k <= n_experts <= 256
+ *   ids, wts      device uint32 [top_k] / float32 [top_k], OUTPUTS, written
+ *   other arguments as in moe_gather_qgemv_int4
+ */
+qint4_status moe_route_gather_qgemv_int4(const qint4_matrix *gate, const qint4_matrix *up,
+                                         const qint4_matrix *down, const void *x,
+                                         const void *logits, int32_t logits_dtype, int32_t top_k,
+                                         const void *residual, void *out, int32_t act_dtype,
+                                         uint32_t *ids, float *wts, void *workspace,
+                                         size_t workspace_bytes, void *stream);
+
+/*
  * Bytes of device workspace one moe_prefill_qgemm_int4 call needs (0 for
  * invalid sizes: T * top_k must be in [1, 2^24], n_experts <= 4096).
  */

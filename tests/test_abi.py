@@ -240,3 +240,22 @@ def test_moe_prefill_validation(lib):
     assert _moep(lib, ws=A + 0x1000010) == 4
     assert _moep(lib, ws_bytes=1024) == 6
     assert _moep(lib, out=A + 0x300000 + 64) == 5                # out overlaps x
+
+
+def test_route_gather_validation(lib):
+    g = _m(n_out=128, k_in=256, e=8)
+    u = q.CMatrix(A + 0x500000, A + 0x600000, A + 0x700000, 128, 256, 64, 8, 1, 0)
+    d = q.CMatrix(A + 0x800000, A + 0x900000, A + 0xA00000, 256, 128, 64, 8, 1, 0)
+
+    def call(logits=A + 0x300400, ldt=0, top_k=4, ids=A + 0x310000, wts=A + 0x320000, e=8):
+        g.n_experts = u.n_experts = d.n_experts = e
+        return lib.moe_route_gather_qgemv_int4(ctypes.byref(g), ctypes.byref(u), ctypes.byref(d),
+                                               A + 0x300000, logits, ldt, top_k, None, A + 0x400000,
+                                               1, ids, wts, A + 0x1000000, 1 << 20, None)
+    assert call(logits=0) == 1 and "logits" in _err(lib)
+    assert call(ldt=5) == 3
+    assert call(e=300) == 2 and "256" in _err(lib)
+    assert call(top_k=9) == 2
+    assert call(logits=A + 0x300402) == 4                   # float32 logits misaligned
+    assert call(ids=A + 0x300400 + 8) == 5                  # ids (an output) overlaps logits
+    assert call(ids=A + 0x400000) == 5                      # ids overlaps out

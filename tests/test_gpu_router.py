@@ -115,3 +115,72 @@ def test_router_feeds_moe_without_host_round_trip():
     ref, a_ref = oracle.moe(d["gate"], d["up"], d["down"], d["x"][0], ref_ids,
                             wts.cpu().numpy(), d["residual"][0], "bf16")
     check(out, ref, a_ref, "router + moe")
+
+
+def _moe_inputs(E, top_k, seed, logit_dtype="f32"):
+    d = synth.moe_layer(seed=seed, n_experts=E, hidden=256, inter=128)
+    logits = d["logits"][0]
+    if logit_dtype == "bf16":
+        logits = synth.f32_to_bf16_bits(logits)
+    return d, logits
+
+
+@pytest.mark.parametrize("E,top_k", [(8, 1), (8, 8), (64, 4), (128, 8), (256, 8), (200, 3)])
+@pytest.mark.parametrize("logit_dtype", ["f32", "bf16"])
+def test_fused_route_gather_equals_router_then_gather(E, top_k, logit_dtype):
+    """moe_route_gather_qgemv_int4 == moe_router_topk + moe_gather_qgemv_int4, bit for bit
+    (ids, weights and the output), and the oracle agrees."""
+    q = lib()
+    d, logits = _moe_inputs(E, top_k, seed=E * 10 + top_k, logit_dtype=logit_dtype)
+    gate, up, down = (dev_matrix(d[k]) for k in ("gate", "up", "down"))
+    lg = synth.to_torch(logits, logit_dtype)
+    x = synth.to_torch(d["x"][0], "bf16")
+    res = synth.to_torch(d["residual"][0], "bf16")
+    ws = torch.empty(q.moe_gather_qgemv_int4_workspace_bytes(128, top_k), dtype=torch.uint8, device="cuda")
+    ids1 = torch.full((top_k,), -1, dtype=torch.int32, device="cuda")
+    wts1 = torch.full((top_k,), float("nan"), dtype=torch.float32, device="cuda")
+    out1 = nan_like(256, torch.bfloat16)
+    q.moe_router_topk(lg, top_k, ids1, wts1)
+    q.moe_gather_qgemv_int4(gate, up, down, x, ids1, wts1, out1, ws, residual=res)
+    ids2 = torch.full((top_k,), -1, dtype=torch.int32, device="cuda")
+    wts2 = torch.full((top_k,), float("nan"), dtype=torch.float32, device="cuda")
+    out2 = nan_like(256, torch.bfloat16)
+    q.moe_route_gather_qgemv_int4(gate, up, down, x, lg, top_k, ids2, wts2, out2, ws, residual=res)
+    torch.cuda.synchronize()
+    assert torch.equal(ids1, ids2)
+    assert torch.equal(wts1.view(torch.int32), wts2.view(torch.int32))
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    l64 = (synth.bf16_bits_to_f32(logits) if logit_dtype == "bf16" else logits).astype(np.float64)
+    ref_ids, _ = oracle.router_topk(l64, top_k)
+    assert ids2.cpu().numpy().tolist() == ref_ids.tolist()
+    ref, a = oracle.moe(d["gate"], d["up"], d["down"], d["x"][0], ref_ids, wts2.cpu().numpy(),
+                        d["residual"][0], "bf16")
+    check(out2, ref, a, "fused route+gather")
+
+
+def test_fused_route_gather_nan_and_all_neg_inf():
+    """NaN logits rank last; an all -inf row keeps experts 0..k-1 with weights 1/k."""
+    q = lib()
+    for case in ("nan", "neginf"):
+        d, logits = _moe_inputs(64, 4, seed=3)
+        logits = logits.copy()
+        if case == "nan":
+            logits[::2] = np.nan
+        else:
+            logits[:] = -np.inf
+        gate, up, down = (dev_matrix(d[k]) for k in ("gate", "up", "down"))
+        lg = synth.to_torch(logits, "f32")
+        x = synth.to_torch(d["x"][0], "bf16")
+        ws = torch.empty(q.moe_gather_qgemv_int4_workspace_bytes(128, 4), dtype=torch.uint8, device="cuda")
+        ids = torch.empty(4, dtype=torch.int32, device="cuda")
+        wts = torch.empty(4, dtype=torch.float32, device="cuda")
+        out = nan_like(256, torch.bfloat16)
+        q.moe_route_gather_qgemv_int4(gate, up, down, x, lg, 4, ids, wts, out, ws)
+        ids_r = torch.empty(4, dtype=torch.int32, device="cuda")
+        wts_r = torch.empty(4, dtype=torch.float32, device="cuda")
+        q.moe_router_topk(lg, 4, ids_r, wts_r)
+        torch.cuda.synchronize()
+        assert torch.equal(ids, ids_r) and torch.equal(wts, wts_r), case
+        if case == "neginf":
+            assert ids.cpu().tolist() == [0, 1, 2, 3] and np.allclose(wts.cpu().numpy(), 0.25)
+        assert torch.isfinite(out.float()).all()
