@@ -739,6 +739,10 @@ qint4_status moe_prefill_qgemm_int4(const qint4_matrix *gate, const qint4_matrix
   if (ldx < hidden || ldx % 8 != 0)
     return fail(QINT4_ERR_SHAPE, "%s: ldx %lld must be >= hidden %lld and a multiple of 8", fn,
                 (long long)ldx, (long long)hidden);
+  // the GEMMs address x and the h planes through 32-bit byte offsets
+  if (T * ldx * 2 >= ((int64_t)1 << 31) || T * top_k * inter * 2 >= ((int64_t)1 << 31))
+    return fail(QINT4_ERR_SHAPE, "%s: T = %lld rows too many for this width (x or h over 2 GiB)",
+                fn, (long long)T);
   if (!aligned(x, 16) || !aligned(out, 16) || (residual && !aligned(residual, 16)))
     return fail(QINT4_ERR_ALIGN, "%s: x/out/residual not 16-byte aligned", fn);
   if (!aligned(ids, 4) || !aligned(wts, 4)) return fail(QINT4_ERR_ALIGN, "%s: ids/wts misaligned", fn);

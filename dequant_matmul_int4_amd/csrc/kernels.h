@@ -154,6 +154,8 @@ struct MoeGemmParams {
   const uint32_t *tiles;  // [0] = row tiles, then (expert, first slot, rows) per tile
   int64_t lda;
   int32_t n_out, k_in, log2_group, sb_bf16, top_k, max_mtiles;
+  int32_t sb_lds;         // 1: each workgroup stages its rows' scales / biases in LDS once
+  int32_t pad_;
 };
 
 hipError_t launch_moe_sort(const uint32_t *ids, int64_t n_pairs, int n_experts, int bm, uint32_t *perm,

@@ -173,7 +173,19 @@ __device__ __forceinline__ uint4 dequant_word(uint32_t w, float s, float b) {
 
 enum { MG_GATEUP = 0, MG_DOWN = 1 };
 
-template <int MODE, int BM, int BN, int WM, int WN>
+constexpr uint32_t kMgOOR = 0x80000000u;  // an offset past every resource: reads zero
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mg_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 mg_ld128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  const v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
+}
+
+template <int MODE, int BM, int BN, int WM, int WN, int PF>
 __global__ void __launch_bounds__(WM * WN * 64) moe_gemm_kernel(const MoeGemmParams p) {
   constexpr int NT = WM * WN * 64;
   constexpr int NB = MODE == MG_GATEUP ? 2 : 1;  // weight matrices (gate, up) or (down)
@@ -186,6 +198,9 @@ __global__ void __launch_bounds__(WM * WN * 64) moe_gemm_kernel(const MoeGemmPar
 
   __shared__ __attribute__((aligned(16))) uint16_t sa[NA][BM * LDK];
   __shared__ __attribute__((aligned(16))) uint16_t sw[NB][BN * LDK];
+  // p.sb_lds: the scales then biases of this workgroup's BN rows of each
+  // matrix for the whole K range (dynamic LDS, 2 * NB * BN * sbrow bytes)
+  extern __shared__ __attribute__((aligned(16))) unsigned char sbtab[];
 
   const int mt = blockIdx.x % p.max_mtiles;
   const int nt = blockIdx.x / p.max_mtiles;
@@ -198,10 +213,55 @@ __global__ void __launch_bounds__(WM * WN * 64) moe_gemm_kernel(const MoeGemmPar
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int cpr = p.k_in / 32;
-  const int64_t gpr = (int64_t)p.k_in >> p.log2_group;
-  const int nsteps = (p.k_in + BK - 1) / BK;
-  const int64_t ecodes = (int64_t)e * p.n_out * (p.k_in / 8);  // words before expert e
-  const int64_t esb = (int64_t)e * p.n_out * gpr;              // groups before expert e
+  const uint32_t gpr = (uint32_t)p.k_in >> p.log2_group;
+  const uint32_t sbb = p.sb_bf16 ? 2 : 4;
+  const uint32_t kwb = (uint32_t)p.k_in / 2;   // code bytes per row
+  const uint32_t sbrow = gpr * sbb;            // scale (= bias) bytes per row
+  // K steps rounded up to whole prefetch rounds; steps past the end load
+  // out-of-range zeros and add nothing
+  const int nsteps = ((p.k_in + BK - 1) / BK + PF - 1) / PF * PF;
+
+  // Raw buffer resources over this tile expert's slab of each weight matrix
+  // (and the activation): an offset at or past the end reads zero without
+  // touching memory, so every load below is unconditional.
+  __amdgpu_buffer_rsrc_t rcw[NB], rsw[NB], rbw[NB];
+#pragma unroll
+  for (int m = 0; m < NB; ++m) {
+    const unsigned char *c = reinterpret_cast<const unsigned char *>(m ? p.codes1 : p.codes0);
+    const unsigned char *sc = reinterpret_cast<const unsigned char *>(m ? p.scales1 : p.scales0);
+    const unsigned char *bi = reinterpret_cast<const unsigned char *>(m ? p.biases1 : p.biases0);
+    rcw[m] = mg_rsrc(c + (uint64_t)e * p.n_out * kwb, (uint32_t)p.n_out * kwb);
+    rsw[m] = mg_rsrc(sc + (uint64_t)e * p.n_out * sbrow, (uint32_t)p.n_out * sbrow);
+    rbw[m] = mg_rsrc(bi + (uint64_t)e * p.n_out * sbrow, (uint32_t)p.n_out * sbrow);
+  }
+
+  // Scale / bias table: one coalesced pass over the contiguous BN * sbrow
+  // bytes of each array (16-, 4- or 2-byte units, whichever the alignment
+  // allows), instead of two scattered 2-byte loads per chunk and step.
+  if (p.sb_lds) {
+    const uint32_t bytes = (uint32_t)BN * sbrow;
+#pragma unroll
+    for (int a = 0; a < 2 * NB; ++a) {
+      const __amdgpu_buffer_rsrc_t r = (a & 1) ? rbw[a >> 1] : rsw[a >> 1];
+      const unsigned char *src = reinterpret_cast<const unsigned char *>((a & 1) ? ((a >> 1) ? p.biases1 : p.biases0)
+                                                                                : ((a >> 1) ? p.scales1 : p.scales0)) +
+                                 ((uint64_t)e * p.n_out + n0) * sbrow;
+      const uint32_t base = (uint32_t)n0 * sbrow;   // offset of row n0 in the expert's slab
+      unsigned char *dst = sbtab + (uint32_t)a * bytes;
+      const uintptr_t al = reinterpret_cast<uintptr_t>(src) | bytes;
+      if ((al & 15) == 0) {
+        for (uint32_t j = tid * 16; j < bytes; j += NT * 16)
+          *reinterpret_cast<uint4 *>(dst + j) = mg_ld128(r, base + j);
+      } else if ((al & 3) == 0) {
+        for (uint32_t j = tid * 4; j < bytes; j += NT * 4)
+          *reinterpret_cast<uint32_t *>(dst + j) = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, base + j, 0, 0);
+      } else {
+        for (uint32_t j = tid * 2; j < bytes; j += NT * 2)
+          *reinterpret_cast<uint16_t *>(dst + j) = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, base + j, 0, 0);
+      }
+    }
+    lds_barrier();
+  }
 
   // per-thread load assignments
   int w_mat[WCH], w_row[WCH], w_half[WCH];
@@ -210,83 +270,98 @@ __global__ void __launch_bounds__(WM * WN * 64) moe_gemm_kernel(const MoeGemmPar
   for (int i = 0; i < WCH; ++i) {
     const int t = tid + i * NT;
     w_act[i] = t < 2 * BN * NB;
-    w_mat[i] = w_act[i] ? t / (2 * BN) : 0;
+    // one matrix per wave (64 divides 2 * BN): the buffer resource stays scalar
+    static_assert((2 * BN) % 64 == 0 && (8 * BM) % 64 == 0, "per-wave matrix / plane");
+    w_mat[i] = __builtin_amdgcn_readfirstlane(w_act[i] ? t / (2 * BN) : 0);
     w_row[i] = (t % (2 * BN)) >> 1;
     w_half[i] = t & 1;
   }
-  const unsigned char *x_src[XCH];  // row base of each activation load (nullptr: zero row)
+  // activation loads: row base offset in bytes, or kMgOOR for a row past the tile
+  uint32_t x_off[XCH];
   int x_pl[XCH], x_row[XCH], x_seg[XCH];
   bool x_act[XCH];
 #pragma unroll
   for (int i = 0; i < XCH; ++i) {
     const int t = tid + i * NT;
     x_act[i] = t < 8 * BM * NA;
-    x_pl[i] = x_act[i] ? t / (8 * BM) : 0;
+    x_pl[i] = __builtin_amdgcn_readfirstlane(x_act[i] ? t / (8 * BM) : 0);
     x_row[i] = (t % (8 * BM)) >> 3;
     x_seg[i] = t & 7;
-    x_src[i] = nullptr;
+    x_off[i] = kMgOOR;
     if (x_act[i] && x_row[i] < rows) {
       const int64_t slot = row0 + x_row[i];
-      if constexpr (MODE == MG_GATEUP) {
-        const int64_t tok = p.perm[slot] / (uint32_t)p.top_k;
-        x_src[i] = reinterpret_cast<const unsigned char *>(p.a0) + tok * p.lda * 2;
-      } else {
-        x_src[i] = reinterpret_cast<const unsigned char *>(x_pl[i] ? p.a1 : p.a0) + slot * p.lda * 2;
-      }
+      if constexpr (MODE == MG_GATEUP)
+        x_off[i] = (uint32_t)((int64_t)(p.perm[slot] / (uint32_t)p.top_k) * p.lda * 2);
+      else
+        x_off[i] = (uint32_t)(slot * p.lda * 2);
     }
   }
+  const __amdgpu_buffer_rsrc_t rxa[2] = {mg_rsrc(p.a0, 0x7FFFFFF0u), mg_rsrc(NA > 1 ? p.a1 : p.a0, 0x7FFFFFF0u)};
 
-  uint4 wq[WCH];
-  float ws_[WCH], wb_[WCH];
-  uint4 xq[XCH];
-
-  auto load_step = [&](int kt) {
+  // register ring of PF prefetched steps
+  struct Step {
+    uint4 wq[WCH];
+    uint32_t ws[WCH], wb[WCH];
+    uint4 xq[XCH];
+  };
+  auto load_step = [&](int kt, Step &st) {
 #pragma unroll
     for (int i = 0; i < WCH; ++i) {
       const int o = n0 + w_row[i];
       const int kc = kt * 2 + w_half[i];
-      if (w_act[i] && o < p.n_out && kc < cpr) {
-        const uint32_t *codes = w_mat[i] ? p.codes1 : p.codes0;
-        const void *sc = w_mat[i] ? p.scales1 : p.scales0;
-        const void *bi = w_mat[i] ? p.biases1 : p.biases0;
-        wq[i] = reinterpret_cast<const uint4 *>(codes + ecodes + (int64_t)o * (p.k_in / 8))[kc];
-        const int64_t gi = esb + (int64_t)o * gpr + (((int64_t)kc * 32) >> p.log2_group);
-        if (p.sb_bf16) {
-          ws_[i] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(sc)[gi] << 16);
-          wb_[i] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(bi)[gi] << 16);
-        } else {
-          ws_[i] = reinterpret_cast<const float *>(sc)[gi];
-          wb_[i] = reinterpret_cast<const float *>(bi)[gi];
-        }
+      const bool ok = w_act[i] && kc < cpr;  // rows past n_out fall outside the resource
+      const uint32_t oc = ok ? (uint32_t)o * kwb + (uint32_t)kc * 16 : kMgOOR;
+      const uint32_t os = ok ? (uint32_t)o * sbrow + (((uint32_t)kc * 32) >> p.log2_group) * sbb : kMgOOR;
+      const int m = w_mat[i];
+      st.wq[i] = mg_ld128(m ? rcw[NB - 1] : rcw[0], oc);
+      if (p.sb_lds) {  // read from the LDS table when the step is stored
+        st.ws[i] = 0;
+        st.wb[i] = 0;
+      } else if (p.sb_bf16) {
+        st.ws[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(m ? rsw[NB - 1] : rsw[0], os, 0, 0) << 16;
+        st.wb[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(m ? rbw[NB - 1] : rbw[0], os, 0, 0) << 16;
       } else {
-        wq[i] = make_uint4(0, 0, 0, 0);
-        ws_[i] = 0.f;
-        wb_[i] = 0.f;
+        st.ws[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(m ? rsw[NB - 1] : rsw[0], os, 0, 0);
+        st.wb[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(m ? rbw[NB - 1] : rbw[0], os, 0, 0);
       }
     }
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
       const int k = kt * BK + x_seg[i] * 8;
-      if (x_src[i] && k < p.k_in)
-        xq[i] = *reinterpret_cast<const uint4 *>(x_src[i] + (int64_t)k * 2);
-      else
-        xq[i] = make_uint4(0, 0, 0, 0);
+      const uint32_t off = (x_off[i] != kMgOOR && k < p.k_in) ? x_off[i] + (uint32_t)k * 2 : kMgOOR;
+      st.xq[i] = mg_ld128(x_pl[i] ? rxa[1] : rxa[0], off);
     }
   };
 
-  auto store_step = [&]() {
+  auto store_step = [&](int kt, const Step &st) {
 #pragma unroll
     for (int i = 0; i < WCH; ++i) {
       if (!w_act[i]) continue;
       uint16_t *dst = sw[w_mat[i]] + w_row[i] * LDK + w_half[i] * 32;
-      const uint32_t w4[4] = {wq[i].x, wq[i].y, wq[i].z, wq[i].w};
+      const uint32_t w4[4] = {st.wq[i].x, st.wq[i].y, st.wq[i].z, st.wq[i].w};
+      float sc = __uint_as_float(st.ws[i]), bi = __uint_as_float(st.wb[i]);
+      if (p.sb_lds) {
+        const int kc = kt * 2 + w_half[i];
+        const uint32_t bytes = (uint32_t)BN * sbrow;
+        // chunks past k_in read group 0 (finite) and meet zero codes
+        const uint32_t o = (uint32_t)w_row[i] * sbrow +
+                           (kc < cpr ? (((uint32_t)kc * 32) >> p.log2_group) * sbb : 0u);
+        const unsigned char *ts = sbtab + (uint32_t)(2 * w_mat[i]) * bytes + o;
+        if (p.sb_bf16) {
+          sc = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t *>(ts) << 16);
+          bi = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t *>(ts + bytes) << 16);
+        } else {
+          sc = *reinterpret_cast<const float *>(ts);
+          bi = *reinterpret_cast<const float *>(ts + bytes);
+        }
+      }
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
-        *reinterpret_cast<uint4 *>(dst + jj * 8) = dequant_word(w4[jj], ws_[i], wb_[i]);
+        *reinterpret_cast<uint4 *>(dst + jj * 8) = dequant_word(w4[jj], sc, bi);
     }
 #pragma unroll
     for (int i = 0; i < XCH; ++i)
-      if (x_act[i]) *reinterpret_cast<uint4 *>(sa[x_pl[i]] + x_row[i] * LDK + x_seg[i] * 8) = xq[i];
+      if (x_act[i]) *reinterpret_cast<uint4 *>(sa[x_pl[i]] + x_row[i] * LDK + x_seg[i] * 8) = st.xq[i];
   };
 
   f32x16_t acc[NB][FM][FN];
@@ -299,11 +374,15 @@ __global__ void __launch_bounds__(WM * WN * 64) moe_gemm_kernel(const MoeGemmPar
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[m][a][b][v] = 0.f;
 
-  load_step(0);
-  for (int kt = 0; kt < nsteps; ++kt) {
-    store_step();
+  Step ring[PF];
+#pragma unroll
+  for (int u = 0; u < PF; ++u) load_step(u, ring[u]);
+  for (int k0 = 0; k0 < nsteps; k0 += PF) {
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+    store_step(k0 + u, ring[u]);
     lds_barrier();
-    if (kt + 1 < nsteps) load_step(kt + 1);
+    load_step(k0 + u + PF, ring[u]);  // refill the slot just stored
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       const int koff = kk * 16 + (lane >> 5) * 8;
@@ -329,6 +408,7 @@ __global__ void __launch_bounds__(WM * WN * 64) moe_gemm_kernel(const MoeGemmPar
               acc[m][a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[pl][a], bfr[m][b], acc[m][a][b], 0, 0, 0);
     }
     lds_barrier();
+    }
   }
 
   // epilogue: accumulator element v of lane l is row 8*(v/4) + 4*(l/32) + v%4,
@@ -419,11 +499,28 @@ __global__ void __launch_bounds__(256)
   }
 }
 
-template <int MODE, int BM, int BN, int WM, int WN>
+template <int MODE, int BM, int BN, int WM, int WN, int PF = 3>
 hipError_t launch_mg(MoeGemmParams p, hipStream_t stream) {
+  constexpr int NB = MODE == MG_GATEUP ? 2 : 1, NA = MODE == MG_GATEUP ? 1 : 2;
+  constexpr size_t kStatic = (size_t)(NA * BM + NB * BN) * LDK * 2;
   const int64_t grid = (int64_t)p.max_mtiles * ((p.n_out + BN - 1) / BN);
-  hipLaunchKernelGGL((moe_gemm_kernel<MODE, BM, BN, WM, WN>), dim3((unsigned)grid),
-                     dim3(WM * WN * 64), 0, stream, p);
+  // the scale / bias table in LDS when it fits next to the tiles
+  const size_t sbrow = (size_t)(p.k_in >> p.log2_group) * (p.sb_bf16 ? 2 : 4);
+  const size_t tab = 2 * (size_t)NB * BN * sbrow;
+  p.sb_lds = tab <= 96 * 1024 && kStatic + tab <= (size_t)kMaxLds;
+  const size_t dyn = p.sb_lds ? tab : 0;
+  auto kern = moe_gemm_kernel<MODE, BM, BN, WM, WN, PF>;
+  // Opt in to the LDS left next to the static tiles once per process and
+  // kernel (a benign race: concurrent first calls set the same value).
+  static bool opted = false;
+  if (dyn > 0 && !opted) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)(kMaxLds - kStatic));
+    if (e != hipSuccess) return e;
+    opted = true;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(WM * WN * 64), dyn, stream, p);
   return hipGetLastError();
 }
 
