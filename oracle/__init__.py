@@ -402,7 +402,8 @@ def round_bf16(v: np.ndarray) -> np.ndarray:
 def gemm_f64(w, X64: np.ndarray, round_w: bool = True, expert: Optional[int] = None,
              threads: int = 1) -> Tuple[np.ndarray, np.ndarray]:
     """Y[t][o] = sum_k w'[o][k] X64[t][k] and A = sum_k |w' X| for float64 rows X64
-    (w' = bf16(w) when round_w); one matrix or expert ``expert`` of a stack."""
+    (w' = bf16(f32(w)) when round_w: the weight dequantised in float32, then rounded to
+    bfloat16); one matrix or expert ``expert`` of a stack."""
     c, s, b = _slab(w, expert)
     c = np.ascontiguousarray(c, dtype=np.uint32)
     sd = np.ascontiguousarray(widen(s, w.sb_dtype))
@@ -424,7 +425,8 @@ def gemm(w, X: np.ndarray, x_dtype: str = BF16, round_w: bool = True,
 
     Padding T up to a multiple of 32 appends zero rows whose outputs are sliced
     away ([FFAI #9], dequantGemmDynamicM T-padding driver), so the result for
-    the T real rows is this plain product; w' = bf16(w) when round_w.
+    the T real rows is this plain product; w' = bf16(f32(w)) when round_w (float32
+    dequantisation, then bfloat16).
     """
     return gemm_f64(w, widen(X, x_dtype), round_w=round_w, threads=threads)
 
@@ -438,7 +440,7 @@ def moe_prefill(gate, up, down, X: np.ndarray, ids: np.ndarray, wts: np.ndarray,
     into one GEMM per gate / up / down, sorted by expert id, then unpermuted by
     a scatter-sum.  Sorting and tiling change no row's value, so each token's
     output is the decode step of moe() computed with the prefill GEMM's weights
-    w' = bf16(w) (the dequantised weight rounded to bfloat16, as in gemm()):
+    w' = bf16(f32(w)) (the float32-dequantised weight rounded to bfloat16, as in gemm()):
       h_k = silu(W'_gate[e] x) * (W'_up[e] x),  out = residual + sum_k w_k W'_down[e] h_k,
     e = ids[t][k]; ids outside [0, n_experts) contribute nothing.  X is bf16
     [T][hidden]; residual (or None) is [T][hidden] in res_dtype.

@@ -137,6 +137,20 @@ double orc_round_bf16(double v)
     return ldexp(r, e - 8);
 }
 
+/*
+ * The prefill weight w' as the dequant GEMMs use it: s * q + b computed in
+ * float32 (one rounding, as a float32 fused multiply-add gives) and then
+ * rounded to bfloat16.  The pages fix no precision for the dequantisation;
+ * float32 is the kernels' own, so the bf16 value of a weight -- a rounding
+ * decision -- is taken in the same precision on both sides.  w is the exact
+ * s * q + b (in double it is exact: s, b float32 or bf16, q < 16).  With bf16
+ * scales and biases of similar magnitude the float32 step is exact.
+ */
+static double prefill_weight(double w)
+{
+    return orc_round_bf16((double)(float)w);
+}
+
 /* Elementwise round-to-bfloat16 of an array (in place allowed). */
 void orc_round_bf16_array(const double *v, int64_t n, double *out)
 {
@@ -145,7 +159,7 @@ void orc_round_bf16_array(const double *v, int64_t n, double *out)
 
 /*
  * Sampled prefill GEMM entries: for each pair i, y[i] = Y[t_idx[i]][o_idx[i]]
- *   = sum_k w'[o][k] * X[t][k], with w' = round_bf16(w) when round_w != 0,
+ *   = sum_k w'[o][k] * X[t][k], with w' = prefill_weight(w) when round_w != 0,
  * else the exact w.  X is T x ldx (row-major, doubles).
  */
 void orc_gemm_entries(const uint32_t *codes, const double *scales, const double *biases,
@@ -162,7 +176,7 @@ void orc_gemm_entries(const uint32_t *codes, const double *scales, const double 
         double acc = 0.0, mag = 0.0;
         for (int64_t k = 0; k < k_in; ++k) {
             double w = weight_at(codes, scales, biases, o, k, k_in, group);
-            if (round_w) w = orc_round_bf16(w);
+            if (round_w) w = prefill_weight(w);
             double term = w * X[t * ldx + k];
             acc += term;
             mag += fabs(term);
@@ -188,7 +202,7 @@ void orc_gemm(const uint32_t *codes, const double *scales, const double *biases,
             double acc = 0.0, mag = 0.0;
             for (int64_t k = 0; k < k_in; ++k) {
                 double w = weight_at(codes, scales, biases, o, k, k_in, group);
-                if (round_w) w = orc_round_bf16(w);
+                if (round_w) w = prefill_weight(w);
                 double term = w * X[t * k_in + k];
                 acc += term;
                 mag += fabs(term);

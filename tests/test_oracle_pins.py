@@ -440,12 +440,35 @@ def test_gemm_rows_match_gemv_with_rounded_weights():
     for t in range(5):
         y, _ = oracle.gemv(w, X[t], synth.BF16)
         assert np.array_equal(Y[t], y)
-    # the bf16-weight variant multiplies round_bf16(W) with X (numpy matmul)
+    # the bf16-weight variant multiplies round_bf16(float32(W)) with X (numpy matmul)
     Yr, _ = oracle.gemm(w, X, synth.BF16, round_w=True)
-    Wr = oracle.round_bf16(oracle.dequant(w))
+    Wr = oracle.round_bf16(oracle.dequant(w).astype(np.float32).astype(np.float64))
     assert np.allclose(Yr, oracle.widen(X, synth.BF16) @ Wr.T, rtol=1e-12, atol=1e-12)
     # and the rounding is real: a sizeable share of weights is not bf16-exact
     assert np.mean(Wr != oracle.dequant(w)) > 0.2
+
+
+def test_gemm_weight_dequantised_in_float32_then_rounded_to_bf16():
+    """The prefill weight is bf16(float32(s q + b)), not bf16 of the exact value.
+
+    s = 1/2 + 2^-24 and b = 1/2 + 2^-8 (both float32), q = 1: the exact weight is
+    1 + 2^-8 + 2^-24.  In float32 (ulp 2^-23 at 1) that is a tie, which goes to the
+    even neighbour 1 + 2^-8; that is again a bf16 tie (ulp 2^-7), which goes to the
+    even neighbour 1.0.  Rounded once from the exact value it would be 1 + 2^-7.
+    A one-hot X row reads the weight out.  With bf16 scales the float32 step is
+    exact and the two readings agree (second row: s = 3/8, b = -1, q = 5 -> 7/8)."""
+    raw = np.zeros((2, 64), np.uint8)
+    raw[0, 0] = 1
+    raw[1, 0] = 5
+    w = _mat(raw, np.array([[0.5 + 2.0 ** -24], [0.375]], np.float32),
+             np.array([[0.5 + 2.0 ** -8], [-1.0]], np.float32), 64)
+    X = np.zeros((1, 64), np.uint16)
+    X[0, 0] = 0x3F80                                                 # bf16 1.0
+    Y, _ = oracle.gemm(w, X, synth.BF16, round_w=True)
+    assert Y[0, 0] == 1.0
+    assert Y[0, 1] == 0.875
+    Yx, _ = oracle.gemm(w, X, synth.BF16, round_w=False)
+    assert Yx[0, 0] == 1 + 2.0 ** -8 + 2.0 ** -24                     # exact weight
 
 
 def test_gemm_entries_match_full():
