@@ -15,6 +15,7 @@ The names and arguments mirror the C entry points:
 * :func:`moe_gather_qgemv_int4`      -- top-K expert gather + SwiGLU + down +
                                         weighted 8-way combine + residual
 * :func:`qgemm_int4_padT`            -- prefill GEMM with virtual T padding, bf16 MFMA
+* :func:`qgemm_int4_padT_ws`         -- the same with a workspace (K split for T <= 64)
 * :func:`moe_router_topk`            -- softmax top-K expert routing on the device
 """
 from __future__ import annotations
@@ -82,6 +83,9 @@ SIGNATURES = [
                                            ctypes.POINTER(CMatrix), _P, _P, _I32, _I32, _P, _P, _I32,
                                            _P, _P, _P, ctypes.c_size_t, _P]),
     ("qgemm_int4_padT", _I32, [ctypes.POINTER(CMatrix), _P, _I64, _I64, _P, _I64, _I32, _P]),
+    ("qgemm_int4_padT_ws", _I32, [ctypes.POINTER(CMatrix), _P, _I64, _I64, _P, _I64, _I32, _P,
+                                  ctypes.c_size_t, _P]),
+    ("qgemm_int4_padT_workspace_bytes", ctypes.c_size_t, [_I64, _I64, _I64]),
     ("moe_router_topk", _I32, [_P, _I32, _I64, _I32, _I32, _P, _P, _P]),
     ("moe_prefill_qgemm_int4_workspace_bytes", ctypes.c_size_t, [_I64, _I32, _I32, _I64, _I64]),
     ("moe_prefill_qgemm_int4", _I32, [ctypes.POINTER(CMatrix), ctypes.POINTER(CMatrix),
@@ -345,9 +349,7 @@ def moe_gather_qgemv_int4(gate: QInt4Matrix, up: QInt4Matrix, down: QInt4Matrix,
         _stream(stream)))
 
 
-def qgemm_int4_padT(w: QInt4Matrix, x: torch.Tensor, y: torch.Tensor, stream=None) -> None:
-    """Y[t] = bf16(W) X[t] for t < T.  x: bfloat16 [T][ldx] (row stride may exceed k_in);
-    y: [T][ldy] float32/bfloat16."""
+def _gemm_args(x: torch.Tensor, y: torch.Tensor) -> None:
     if x.dtype != torch.bfloat16:
         raise TypeError("x must be bfloat16")
     if x.dim() != 2 or y.dim() != 2 or x.shape[0] != y.shape[0]:
@@ -356,9 +358,33 @@ def qgemm_int4_padT(w: QInt4Matrix, x: torch.Tensor, y: torch.Tensor, stream=Non
         raise ValueError("rows of x and y must be contiguous")
     if x.device.type != "cuda" or y.device.type != "cuda":
         raise ValueError("x and y must be device tensors")
+
+
+def qgemm_int4_padT(w: QInt4Matrix, x: torch.Tensor, y: torch.Tensor, stream=None) -> None:
+    """Y[t] = bf16(W) X[t] for t < T.  x: bfloat16 [T][ldx] (row stride may exceed k_in);
+    y: [T][ldy] float32/bfloat16."""
+    _gemm_args(x, y)
     cm = w.c()
     _check(load().qgemm_int4_padT(ctypes.byref(cm), x.data_ptr(), x.shape[0], x.stride(0),
                                   y.data_ptr(), y.stride(0), _dt(y), _stream(stream)))
+
+
+def qgemm_int4_padT_workspace_bytes(T: int, n_out: int, k_in: int) -> int:
+    """Workspace bytes for the full K split of qgemm_int4_padT_ws on the current device."""
+    return int(load().qgemm_int4_padT_workspace_bytes(int(T), int(n_out), int(k_in)))
+
+
+def qgemm_int4_padT_ws(w: QInt4Matrix, x: torch.Tensor, y: torch.Tensor,
+                       workspace: Optional[torch.Tensor], stream=None) -> None:
+    """qgemm_int4_padT with a scratch workspace (device tensor, 256-byte aligned, or None):
+    for T <= 64 the K range is split over workgroups into float32 partials."""
+    _gemm_args(x, y)
+    cm = w.c()
+    ws_p = _dev(workspace, "workspace") if workspace is not None else None
+    ws_n = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().qgemm_int4_padT_ws(ctypes.byref(cm), x.data_ptr(), x.shape[0], x.stride(0),
+                                     y.data_ptr(), y.stride(0), _dt(y), ws_p, ws_n,
+                                     _stream(stream)))
 
 
 def moe_router_topk(logits: torch.Tensor, top_k: int, ids: torch.Tensor, wts: torch.Tensor,
@@ -383,6 +409,7 @@ def moe_router_topk(logits: torch.Tensor, top_k: int, ids: torch.Tensor, wts: to
 
 __all__ = ["QInt4Matrix", "Int4Error", "qgemv_int4", "qgemv_int4_multi", "qgemv_int4_smallm",
            "moe_gather_qgemv_int4", "moe_gather_qgemv_int4_workspace_bytes", "qgemm_int4_padT",
+           "qgemm_int4_padT_ws", "qgemm_int4_padT_workspace_bytes",
            "moe_router_topk", "rms_norm_qgemv_int4", "quantize_int4",
            "moe_prefill_qgemm_int4", "moe_prefill_qgemm_int4_workspace_bytes",
            "moe_route_gather_qgemv_int4",

@@ -868,9 +868,10 @@ qint4_status quantize_int4(const void *w, int32_t w_dtype, int64_t n_rows, int64
   return ok();
 }
 
-qint4_status qgemm_int4_padT(const qint4_matrix *w, const void *x, int64_t T, int64_t ldx, void *y,
-                             int64_t ldy, int32_t y_dtype, void *stream) {
-  const char *fn = "qgemm_int4_padT";
+// Shared by qgemm_int4_padT (no workspace) and qgemm_int4_padT_ws.
+static qint4_status run_gemm(const char *fn, const qint4_matrix *w, const void *x, int64_t T,
+                             int64_t ldx, void *y, int64_t ldy, int32_t y_dtype, void *ws,
+                             size_t ws_bytes, void *stream) {
   qint4_status st;
   if ((st = check_matrix(w, "w", false)) != QINT4_OK) return st;
   if (!x || !y) return fail(QINT4_ERR_NULL, "%s: x or y is NULL", fn);
@@ -887,13 +888,38 @@ qint4_status qgemm_int4_padT(const qint4_matrix *w, const void *x, int64_t T, in
   if (!aligned(y, elem_bytes(y_dtype))) return fail(QINT4_ERR_ALIGN, "%s: y misaligned", fn);
   if (w->n_out > INT32_MAX || w->k_in > INT32_MAX) return fail(QINT4_ERR_SHAPE, "%s: too large", fn);
 
-  Range ins[4], outs[1];
+  if (!ws) ws_bytes = 0;
+  if (ws && !aligned(ws, 256)) return fail(QINT4_ERR_ALIGN, "%s: workspace not 256-byte aligned", fn);
+
+  Range ins[4], outs[2];
   static const char *mn[3] = {"codes", "scales", "biases"};
   int ni = add_matrix_ranges(w, mn, ins);
   ins[ni++] = range(x, (size_t)((T - 1) * ldx + w->k_in) * 2, "x");
-  outs[0] = range(y, (size_t)((T - 1) * ldy + w->n_out) * elem_bytes(y_dtype), "y");
-  if ((st = check_no_overlap(outs, 1, ins, ni)) != QINT4_OK) return prefixed(st, fn);
-  if ((st = check_device(nullptr)) != QINT4_OK) return prefixed(st, fn);
+  int no = 0;
+  outs[no++] = range(y, (size_t)((T - 1) * ldy + w->n_out) * elem_bytes(y_dtype), "y");
+  if ((st = check_no_overlap(outs, no, ins, ni)) != QINT4_OK) return prefixed(st, fn);
+  int n_cu = 256;
+  if ((st = check_device(&n_cu)) != QINT4_OK) return prefixed(st, fn);
+
+  // T <= 64: weights straight from HBM into MFMA registers, split over K when
+  // the workspace allows (qgemm_stream.hip); longer T: LDS-tiled weights
+  // (qgemm.hip), which amortise the dequantisation over more rows.  The
+  // stream kernel addresses X through 32-bit byte offsets.
+  const bool stream_path = T <= kStreamMaxT && (T - 1) * ldx + w->k_in < ((int64_t)1 << 30);
+  StreamPlan plan{};
+  size_t ws_used = 0;
+  if (stream_path) {
+    const bool sb16 = w->sb_dtype == QINT4_BF16;
+    const bool sb_dwords = !sb16 || ((w->k_in / w->group_size) % 2 == 0 && aligned(w->scales, 4) &&
+                                     aligned(w->biases, 4));
+    plan = plan_gemm_stream(T, w->n_out, w->k_in, ilog2(w->group_size), sb16, sb_dwords, n_cu,
+                            (int64_t)std::min<size_t>(ws_bytes, (size_t)INT64_MAX));
+    ws_used = gemm_stream_ws_bytes(plan, T, w->n_out);
+  }
+  if (ws_used) {
+    outs[no++] = range(ws, ws_used, "workspace");
+    if ((st = check_no_overlap(outs, no, ins, ni)) != QINT4_OK) return prefixed(st, fn);
+  }
 
   GemmParams p;
   std::memset(&p, 0, sizeof(p));
@@ -910,19 +936,36 @@ qint4_status qgemm_int4_padT(const qint4_matrix *w, const void *x, int64_t T, in
   p.log2_group = ilog2(w->group_size);
   p.y_bf16 = y_dtype == QINT4_BF16;
   p.sb_bf16 = w->sb_dtype == QINT4_BF16;
-  // T <= 64: weights straight from HBM into MFMA registers (qgemm_stream.hip),
-  // activation tiles in LDS; longer T: LDS-tiled weights (qgemm.hip), which
-  // amortise the dequantisation over more rows.  The stream kernel addresses
-  // X through 32-bit byte offsets.  (Measured on MI355X at N = 17408,
-  // K = 5120: T = 16 / 32 / 64 in 41 / 45 / 63 us against 80 / 82 / 93 us.)
-  const bool x_fits = (T - 1) * ldx + w->k_in < ((int64_t)1 << 30);
+  p.part = reinterpret_cast<float *>(ws);
+  p.ksplit = 1;
   hipError_t e;
-  if (x_fits && T <= 64)
-    e = launch_gemm_stream(p, 0, reinterpret_cast<hipStream_t>(stream));
+  if (stream_path)
+    e = launch_gemm_stream(p, plan, reinterpret_cast<hipStream_t>(stream));
   else
     e = launch_gemm(p, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(QINT4_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
+}
+
+qint4_status qgemm_int4_padT(const qint4_matrix *w, const void *x, int64_t T, int64_t ldx, void *y,
+                             int64_t ldy, int32_t y_dtype, void *stream) {
+  return run_gemm("qgemm_int4_padT", w, x, T, ldx, y, ldy, y_dtype, nullptr, 0, stream);
+}
+
+size_t qgemm_int4_padT_workspace_bytes(int64_t T, int64_t n_out, int64_t k_in) {
+  if (T < 1 || T > kStreamMaxT || n_out < 1 || n_out > INT32_MAX || k_in < 32 || k_in > kMaxK)
+    return 0;
+  int n_cu = 256;
+  if (check_device(&n_cu) != QINT4_OK) return 0;
+  // the split plan depends on the shape and the device only
+  return gemm_stream_ws_bytes(plan_gemm_stream(T, n_out, k_in, 6, 1, true, n_cu, -1), T, n_out);
+}
+
+qint4_status qgemm_int4_padT_ws(const qint4_matrix *w, const void *x, int64_t T, int64_t ldx,
+                                void *y, int64_t ldy, int32_t y_dtype, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+  return run_gemm("qgemm_int4_padT_ws", w, x, T, ldx, y, ldy, y_dtype, workspace, workspace_bytes,
+                  stream);
 }
 
 }  // extern "C"

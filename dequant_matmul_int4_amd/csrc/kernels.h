@@ -130,12 +130,35 @@ struct GemmParams {
   int32_t sb_bf16;
   int32_t m_tiles;
   int32_t n_tiles;
+  // split-K (stream kernel): ksplit workgroups share a row block and a token
+  // block, each summing split_steps 128-k steps into part[slice][T][n_out]
+  // (float32); a reduce kernel adds the slices into y.  ksplit == 1 writes y.
+  float *part;
+  int32_t ksplit;
+  int32_t split_steps;
+  int32_t sb_tab_dw;         // dwords of one wave's scale (or bias) table in LDS, 0: none
+  int32_t pad_;
 };
 
 hipError_t launch_gemm(const GemmParams &p, hipStream_t stream);
-// Register-resident-weight GEMM (qgemm_stream.hip); cfg selects the token
-// block / row tiles per wave / waves / prefetch depth.
-hipError_t launch_gemm_stream(const GemmParams &p, int cfg, hipStream_t stream);
+
+// Register-resident-weight GEMM for T <= 64 (qgemm_stream.hip).
+struct StreamPlan {
+  int mt;           // 16-token blocks per workgroup (1, 2 or 4)
+  int depth;        // weight steps in flight per wave
+  int ksplit;       // K slices (1: no workspace needed)
+  int split_steps;  // 128-k steps per slice
+  int sb_lds;       // scales / biases staged in LDS once per wave
+};
+constexpr int kStreamMaxT = 64;
+// Plan for a T x n_out x k_in product on a device with n_cu compute units;
+// ksplit is limited to what ws_bytes holds (ws_bytes < 0: no limit).
+// sb_dwords: every row of the scale and bias arrays starts dword-aligned
+// (required for the LDS scale tables).
+StreamPlan plan_gemm_stream(int64_t T, int64_t n_out, int64_t k_in, int log2_group, int sb_bf16,
+                            bool sb_dwords, int n_cu, int64_t ws_bytes);
+size_t gemm_stream_ws_bytes(const StreamPlan &plan, int64_t T, int64_t n_out);
+hipError_t launch_gemm_stream(const GemmParams &p, const StreamPlan &plan, hipStream_t stream);
 
 // Top-k expert routing of n_rows rows of router logits (float32 or bf16):
 // ids/wts are [n_rows][top_k].

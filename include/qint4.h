@@ -334,6 +334,38 @@ qint4_status qgemm_int4_padT(const qint4_matrix *w, const void *x, int64_t T, in
                              void *y, int64_t ldy, int32_t y_dtype, void *stream);
 
 /*
+ * qgemm_int4_padT_ws -- qgemm_int4_padT with a scratch workspace, the same
+ * product and arguments, the same bf16 weight rounding; only the summation
+ * order over k differs.
+ *
+ * For T <= 64 the product is a weight stream with too few 16-row tiles to
+ * occupy the GPU (a 17408-row matrix has 1088); with a workspace the K range
+ * is cut into slices summed by different workgroups into float32 partial
+ * planes, which a second kernel adds into y.  Same citations as
+ * qgemm_int4_padT (the T-padding driver; the outDim guard).
+ *
+ *   workspace        device scratch, 256-byte aligned, or NULL; contents on
+ *                    entry ignored, on return unspecified; must not overlap
+ *                    w, x or y.  Calls that share a workspace must be
+ *                    ordered (one stream), as for any output buffer.
+ *   workspace_bytes  its size.  The call uses at most this much and never
+ *                    fails for want of space: a smaller (or NULL) workspace
+ *                    means fewer slices (none: the plain kernel).
+ * One or two kernel launches on `stream`.
+ */
+qint4_status qgemm_int4_padT_ws(const qint4_matrix *w, const void *x, int64_t T, int64_t ldx,
+                                void *y, int64_t ldy, int32_t y_dtype, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
+/*
+ * Workspace bytes with which qgemm_int4_padT_ws runs its full K split for a
+ * T x n_out x k_in product on the current device; 0 when it uses none (T > 64
+ * or a shape that does not split).  Depends on the current device's compute
+ * unit count; 0 when no usable device is current.
+ */
+size_t qgemm_int4_padT_workspace_bytes(int64_t T, int64_t n_out, int64_t k_in);
+
+/*
  * moe_router_topk -- top-K expert routing of n_tokens rows of router logits,
  * on the device, producing the ids / wts that moe_gather_qgemv_int4 reads.
  *

@@ -133,6 +133,16 @@ def test_gemm_validation(lib):
     assert _gemm(lib, _m(), ldy=32) == 2
     assert _gemm(lib, _m(), x=A + 0x300008) == 4
     assert _gemm(lib, _m(), y=A + 0x300000 + 128) == 5
+    ws = lambda **k: lib.qgemm_int4_padT_ws(ctypes.byref(_m()), A + 0x300000, 32, 256,  # noqa: E731
+                                            A + 0x400000, 64, 1, k.get("ws", A + 0x800000),
+                                            k.get("n", 1 << 20), None)
+    assert ws(ws=A + 0x800040) == 4                          # workspace not 256-byte aligned
+    # sizes are device-dependent: without a device the query reports no split
+    import torch
+    if not torch.cuda.is_available():
+        assert lib.qgemm_int4_padT_workspace_bytes(32, 17408, 5120) == 0
+    assert lib.qgemm_int4_padT_workspace_bytes(65, 17408, 5120) == 0   # T > 64: no split
+    assert lib.qgemm_int4_padT_workspace_bytes(0, 17408, 5120) == 0
 
 
 def _smallm(lib, m, T=4, ldx=256, x=A + 0x300000, xdt=1, y=A + 0x400000, ydt=1, epi=0, n=1):
