@@ -906,6 +906,9 @@ static qint4_status run_gemm(const char *fn, const qint4_matrix *w, const void *
   // (qgemm.hip), which amortise the dequantisation over more rows.  The
   // stream kernel addresses X through 32-bit byte offsets.
   const bool stream_path = T <= kStreamMaxT && (T - 1) * ldx + w->k_in < ((int64_t)1 << 30);
+  // the tiled kernel addresses a 128-row block of X through 32-bit offsets
+  if (!stream_path && 128 * ldx * 2 >= ((int64_t)1 << 31))
+    return fail(QINT4_ERR_SHAPE, "%s: ldx %lld too large for T > %d", fn, (long long)ldx, kStreamMaxT);
   StreamPlan plan{};
   size_t ws_used = 0;
   if (stream_path) {

@@ -1,4 +1,5 @@
-// qgemm.hip -- prefill int4 dequant GEMM on gfx950 bf16 MFMA.
+// qgemm.hip -- prefill int4 dequant GEMM on gfx950 bf16 MFMA, LDS-tiled
+// (the T > 64 path; qgemm_stream.hip serves T <= 64).
 //
 //   Y[t][o] = sum_k bf16(s[o][k/g] * q[o][k] + b[o][k/g]) * X[t][k],  t < T
 //
@@ -10,13 +11,22 @@
 //
 // Tiling (gfx950): a workgroup owns a BM x BN tile of Y and walks K in steps
 // of 64 (one 64-group, or two 32-groups).  Per step every thread loads 32
-// codes of one W row (a 128-bit load) with that group's scale and bias,
-// dequantises them in float32, rounds to bf16 (v_cvt_pk_bf16_f32,
+// codes of one W row (a 128-bit load), dequantises them in float32 with that
+// group's scale and bias, rounds to bf16 (v_cvt_pk_bf16_f32,
 // round-to-nearest-even) and writes them to LDS; the X tile is copied to LDS
 // as bf16.  Waves then run v_mfma_f32_32x32x16_bf16 on 32x32 sub-tiles with
-// float32 accumulators.  The next step's global loads are issued before the
-// MFMAs of the current step so that HBM latency overlaps the math; the
-// barriers order LDS only, so they do not wait for those loads.
+// float32 accumulators.
+//   * The global loads of PF steps are kept in flight in a register ring, so
+//     HBM latency is covered by PF steps of MFMA work rather than one; the
+//     barriers order LDS only and never wait for those loads.
+//   * Every load is a raw buffer load: rows past T or n_out and chunks past
+//     k_in read as zero without touching memory, so no load sits behind a
+//     branch (a branch around a load in the ring would make the compiler wait
+//     for every load in flight).
+//   * The scales and biases of the workgroup's BN rows for the whole K range
+//     are copied into LDS once, with coalesced loads, when they fit next to
+//     the tiles: per-step 2-byte loads from BN scattered rows otherwise cost
+//     more memory-pipeline work than the code loads.
 
 #include "kernels.h"
 
@@ -29,13 +39,24 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int BK = 64;
 constexpr int LDK = BK + 8;  // padded LDS row (bf16 elements): spreads rows over banks
+constexpr uint32_t kOOR = 0x80000000u;
 
 // Workgroup barrier that orders LDS only: __syncthreads() would also wait for
-// every outstanding global load, including the next step's prefetch.
+// every outstanding global load, including the prefetched steps.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  const v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -58,7 +79,8 @@ __device__ __forceinline__ uint4 dequant_word(uint32_t w, float s, float b) {
   return r;
 }
 
-template <int BM, int BN, int WM, int WN>
+// SBL: the scales and biases of the BN rows are staged in dynamic LDS.
+template <int BM, int BN, int WM, int WN, int PF, bool SBL>
 __global__ void __launch_bounds__(WM * WN * 64) qgemm_kernel(const GemmParams p) {
   constexpr int NT = WM * WN * 64;
   constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
@@ -69,6 +91,9 @@ __global__ void __launch_bounds__(WM * WN * 64) qgemm_kernel(const GemmParams p)
 
   __shared__ __attribute__((aligned(16))) uint16_t sx[BM * LDK];
   __shared__ __attribute__((aligned(16))) uint16_t sw[BN * LDK];
+  // the scales then the biases of this workgroup's BN rows for the whole K
+  // range (dynamic LDS, 2 * BN * sbrow bytes) when SBL
+  extern __shared__ __attribute__((aligned(16))) unsigned char sbtab[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -80,12 +105,48 @@ __global__ void __launch_bounds__(WM * WN * 64) qgemm_kernel(const GemmParams p)
   const int n0 = nt * BN;
 
   const int cpr = p.k_in / 32;                   // 32-code chunks per W row
-  const int64_t gpr = (int64_t)p.k_in >> p.log2_group;
-  const int nsteps = (p.k_in + BK - 1) / BK;
-  const int sbb = p.sb_bf16 ? 2 : 4;
+  const uint32_t gpr = (uint32_t)p.k_in >> p.log2_group;
+  const uint32_t sbb = p.sb_bf16 ? 2 : 4;
+  const uint32_t kwb = (uint32_t)p.k_in / 2;     // code bytes per row
+  const uint32_t sbrow = gpr * sbb;              // scale (= bias) bytes per row
+  // K steps rounded up to whole prefetch rounds; steps past the end load
+  // out-of-range zeros and add nothing
+  const int nsteps = ((p.k_in + BK - 1) / BK + PF - 1) / PF * PF;
 
-  // per-thread load assignments
-  // (threads past the tile's chunk count idle: w_act / x_act false)
+  const __amdgpu_buffer_rsrc_t rc = rsrc(p.codes, (uint32_t)p.n_out * kwb);
+  const __amdgpu_buffer_rsrc_t rs = rsrc(p.scales, (uint32_t)p.n_out * sbrow);
+  const __amdgpu_buffer_rsrc_t rb = rsrc(p.biases, (uint32_t)p.n_out * sbrow);
+  // X from this tile's first row on: rows past T lie outside the resource
+  const int64_t rows_here = p.T - m0 < BM ? p.T - m0 : BM;
+  const __amdgpu_buffer_rsrc_t rx =
+      rsrc(p.x + m0 * p.ldx, (uint32_t)(((rows_here - 1) * p.ldx + p.k_in) * 2));
+
+  if constexpr (SBL) {
+    // one coalesced pass over the contiguous BN * sbrow bytes of each array
+    // (16-, 4- or 2-byte units, whichever the alignment allows); rows past
+    // n_out read as zero
+    const uint32_t bytes = (uint32_t)BN * sbrow;
+    const uint32_t base = (uint32_t)n0 * sbrow;
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const __amdgpu_buffer_rsrc_t r = a ? rb : rs;
+      const uintptr_t al = reinterpret_cast<uintptr_t>(a ? p.biases : p.scales) | base | bytes;
+      unsigned char *dst = sbtab + (uint32_t)a * bytes;
+      if ((al & 15) == 0) {
+        for (uint32_t j = tid * 16; j < bytes; j += NT * 16)
+          *reinterpret_cast<uint4 *>(dst + j) = ld128(r, base + j);
+      } else if ((al & 3) == 0) {
+        for (uint32_t j = tid * 4; j < bytes; j += NT * 4)
+          *reinterpret_cast<uint32_t *>(dst + j) = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, base + j, 0, 0);
+      } else {
+        for (uint32_t j = tid * 2; j < bytes; j += NT * 2)
+          *reinterpret_cast<uint16_t *>(dst + j) = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, base + j, 0, 0);
+      }
+    }
+    lds_barrier();
+  }
+
+  // per-thread load assignments (threads past the tile's chunk count idle)
   int w_row[WCH], w_half[WCH];
   bool w_act[WCH];
 #pragma unroll
@@ -105,56 +166,69 @@ __global__ void __launch_bounds__(WM * WN * 64) qgemm_kernel(const GemmParams p)
     x_seg[i] = t & 7;
   }
 
-  uint4 wq[WCH];
-  float ws_[WCH], wb_[WCH];
-  uint4 xq[XCH];
-
-  auto load_step = [&](int kt) {
+  struct Step {
+    uint4 wq[WCH];
+    uint32_t ws[WCH], wb[WCH];
+    uint4 xq[XCH];
+  };
+  auto load_step = [&](int kt, Step &st) {
 #pragma unroll
     for (int i = 0; i < WCH; ++i) {
-      const int o = n0 + w_row[i];
       const int kc = kt * 2 + w_half[i];
-      const bool ok = w_act[i] && (o < p.n_out) && (kc < cpr);
-      if (ok) {
-        wq[i] = reinterpret_cast<const uint4 *>(p.codes)[(int64_t)o * (cpr) + kc];
-        const int64_t gi = (int64_t)o * gpr + (((int64_t)kc * 32) >> p.log2_group);
-        if (sbb == 2) {
-          ws_[i] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(p.scales)[gi] << 16);
-          wb_[i] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(p.biases)[gi] << 16);
-        } else {
-          ws_[i] = reinterpret_cast<const float *>(p.scales)[gi];
-          wb_[i] = reinterpret_cast<const float *>(p.biases)[gi];
-        }
+      const bool ok = w_act[i] && kc < cpr;  // rows past n_out fall outside the resource
+      const uint32_t o = (uint32_t)(n0 + w_row[i]);
+      st.wq[i] = ld128(rc, ok ? o * kwb + (uint32_t)kc * 16 : kOOR);
+      if constexpr (SBL) {  // read from the LDS table when the step is stored
+        st.ws[i] = 0;
+        st.wb[i] = 0;
       } else {
-        wq[i] = make_uint4(0, 0, 0, 0);
-        ws_[i] = 0.f;
-        wb_[i] = 0.f;
+        const uint32_t os = ok ? o * sbrow + (((uint32_t)kc * 32) >> p.log2_group) * sbb : kOOR;
+        if (p.sb_bf16) {
+          st.ws[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, os, 0, 0) << 16;
+          st.wb[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, os, 0, 0) << 16;
+        } else {
+          st.ws[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, os, 0, 0);
+          st.wb[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rb, os, 0, 0);
+        }
       }
     }
 #pragma unroll
     for (int i = 0; i < XCH; ++i) {
-      const int64_t t = m0 + x_row[i];
       const int k = kt * BK + x_seg[i] * 8;
-      if (x_act[i] && t < p.T && k < p.k_in)
-        xq[i] = *reinterpret_cast<const uint4 *>(p.x + t * p.ldx + k);
-      else
-        xq[i] = make_uint4(0, 0, 0, 0);
+      const bool ok = x_act[i] && x_row[i] < rows_here && k < p.k_in;
+      st.xq[i] = ld128(rx, ok ? (uint32_t)((x_row[i] * p.ldx + k) * 2) : kOOR);
     }
   };
 
-  auto store_step = [&]() {
+  auto store_step = [&](int kt, const Step &st) {
 #pragma unroll
     for (int i = 0; i < WCH; ++i) {
       if (!w_act[i]) continue;
       uint16_t *dst = sw + w_row[i] * LDK + w_half[i] * 32;
-      const uint32_t w4[4] = {wq[i].x, wq[i].y, wq[i].z, wq[i].w};
+      const uint32_t w4[4] = {st.wq[i].x, st.wq[i].y, st.wq[i].z, st.wq[i].w};
+      float sc = __uint_as_float(st.ws[i]), bi = __uint_as_float(st.wb[i]);
+      if constexpr (SBL) {
+        const int kc = kt * 2 + w_half[i];
+        const uint32_t bytes = (uint32_t)BN * sbrow;
+        // chunks past k_in read group 0 (finite) and meet zero codes
+        const uint32_t o = (uint32_t)w_row[i] * sbrow +
+                           (kc < cpr ? (((uint32_t)kc * 32) >> p.log2_group) * sbb : 0u);
+        const unsigned char *ts = sbtab + o;
+        if (p.sb_bf16) {
+          sc = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t *>(ts) << 16);
+          bi = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t *>(ts + bytes) << 16);
+        } else {
+          sc = *reinterpret_cast<const float *>(ts);
+          bi = *reinterpret_cast<const float *>(ts + bytes);
+        }
+      }
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
-        *reinterpret_cast<uint4 *>(dst + jj * 8) = dequant_word(w4[jj], ws_[i], wb_[i]);
+        *reinterpret_cast<uint4 *>(dst + jj * 8) = dequant_word(w4[jj], sc, bi);
     }
 #pragma unroll
     for (int i = 0; i < XCH; ++i)
-      if (x_act[i]) *reinterpret_cast<uint4 *>(sx + x_row[i] * LDK + x_seg[i] * 8) = xq[i];
+      if (x_act[i]) *reinterpret_cast<uint4 *>(sx + x_row[i] * LDK + x_seg[i] * 8) = st.xq[i];
   };
 
   f32x16_t acc[FM][FN];
@@ -165,28 +239,33 @@ __global__ void __launch_bounds__(WM * WN * 64) qgemm_kernel(const GemmParams p)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
 
-  load_step(0);
-  for (int kt = 0; kt < nsteps; ++kt) {
-    store_step();
-    lds_barrier();
-    if (kt + 1 < nsteps) load_step(kt + 1);
+  Step ring[PF];
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int koff = kk * 16 + (lane >> 5) * 8;
-      bf16x8_t af[FM], bfr[FN];
+  for (int u = 0; u < PF; ++u) load_step(u, ring[u]);
+  for (int k0 = 0; k0 < nsteps; k0 += PF) {
 #pragma unroll
-      for (int a = 0; a < FM; ++a)
-        af[a] = *reinterpret_cast<const bf16x8_t *>(sx + (wm * TM + a * 32 + (lane & 31)) * LDK + koff);
+    for (int u = 0; u < PF; ++u) {
+      store_step(k0 + u, ring[u]);
+      lds_barrier();
+      load_step(k0 + u + PF, ring[u]);  // refill the slot just stored
 #pragma unroll
-      for (int b = 0; b < FN; ++b)
-        bfr[b] = *reinterpret_cast<const bf16x8_t *>(sw + (wn * TN + b * 32 + (lane & 31)) * LDK + koff);
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        const int koff = kk * 16 + (lane >> 5) * 8;
+        bf16x8_t af[FM], bfr[FN];
 #pragma unroll
-      for (int a = 0; a < FM; ++a)
+        for (int a = 0; a < FM; ++a)
+          af[a] = *reinterpret_cast<const bf16x8_t *>(sx + (wm * TM + a * 32 + (lane & 31)) * LDK + koff);
 #pragma unroll
         for (int b = 0; b < FN; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
+          bfr[b] = *reinterpret_cast<const bf16x8_t *>(sw + (wn * TN + b * 32 + (lane & 31)) * LDK + koff);
+#pragma unroll
+        for (int a = 0; a < FM; ++a)
+#pragma unroll
+          for (int b = 0; b < FN; ++b)
+            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
+      }
+      lds_barrier();
     }
-    lds_barrier();
   }
 
   // epilogue: accumulator element v of lane l is row 8*(v/4) + 4*(l/32) + v%4,
@@ -209,13 +288,32 @@ __global__ void __launch_bounds__(WM * WN * 64) qgemm_kernel(const GemmParams p)
     }
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int PF = 3>
 hipError_t launch_tile(GemmParams p, hipStream_t stream) {
+  constexpr size_t kStatic = (size_t)(BM + BN) * LDK * 2;
   p.m_tiles = (int)((p.T + BM - 1) / BM);
   p.n_tiles = (p.n_out + BN - 1) / BN;
   const int64_t grid = (int64_t)p.m_tiles * p.n_tiles;
-  hipLaunchKernelGGL((qgemm_kernel<BM, BN, WM, WN>), dim3((unsigned)grid), dim3(WM * WN * 64), 0,
-                     stream, p);
+  // the scale / bias table in LDS when it fits next to the tiles
+  const size_t sbrow = (size_t)(p.k_in >> p.log2_group) * (p.sb_bf16 ? 2 : 4);
+  const size_t tab = 2 * (size_t)BN * sbrow;
+  if (!(tab <= 96 * 1024 && kStatic + tab <= (size_t)kMaxLds)) {
+    hipLaunchKernelGGL((qgemm_kernel<BM, BN, WM, WN, PF, false>), dim3((unsigned)grid),
+                       dim3(WM * WN * 64), 0, stream, p);
+    return hipGetLastError();
+  }
+  auto kern = qgemm_kernel<BM, BN, WM, WN, PF, true>;
+  // Opt in to the LDS left next to the static tiles once per process and
+  // kernel (a benign race: concurrent first calls set the same value).
+  static bool opted = false;
+  if (!opted) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)(kMaxLds - kStatic));
+    if (e != hipSuccess) return e;
+    opted = true;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(WM * WN * 64), tab, stream, p);
   return hipGetLastError();
 }
 
