@@ -344,36 +344,51 @@ __global__ void __launch_bounds__((kW + 1) * 64) qgemm_stream_kernel(const GemmP
     }
 }
 
-// Y[t][o] = sum over slices of part[slice][t][o]; one thread per 4 outputs.
+// Y[t][o] = sum over slices of part[slice][t][o]; one thread per 8 outputs.
+// The planes are read eight at a time with every load issued before the
+// first add, so a thread waits for memory once per eight planes.
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float *__restrict__ part, int ksplit,
                                                             int64_t T, int n_out, void *y, int64_t ldy,
                                                             int y_bf16) {
-  const int64_t n4 = (int64_t)n_out / 4;
+  const int64_t n8 = (int64_t)n_out / 8;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= T * n4) return;
-  const int64_t t = i / n4;
-  const int o = (int)(i - t * n4) * 4;
+  if (i >= T * n8) return;
+  const int64_t t = i / n8;
+  const int o = (int)(i - t * n8) * 8;
   const int64_t plane = T * (int64_t)n_out;
-  float4 s = *reinterpret_cast<const float4 *>(part + t * n_out + o);
-  for (int k = 1; k < ksplit; ++k) {
-    const float4 v = *reinterpret_cast<const float4 *>(part + k * plane + t * n_out + o);
-    s.x += v.x;
-    s.y += v.y;
-    s.z += v.z;
-    s.w += v.w;
+  const float *src = part + t * n_out + o;
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  for (int k0 = 0; k0 < ksplit; k0 += 8) {
+    float4 v[8][2];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float4 *q = reinterpret_cast<const float4 *>(src + (int64_t)min(k0 + k, ksplit - 1) * plane);
+      v[k][0] = q[0];
+      v[k][1] = q[1];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (k0 + k >= ksplit) break;
+      acc[0] += v[k][0].x;
+      acc[1] += v[k][0].y;
+      acc[2] += v[k][0].z;
+      acc[3] += v[k][0].w;
+      acc[4] += v[k][1].x;
+      acc[5] += v[k][1].y;
+      acc[6] += v[k][1].z;
+      acc[7] += v[k][1].w;
+    }
   }
   if (y_bf16) {
     __bf16 *d = reinterpret_cast<__bf16 *>(y) + t * ldy + o;
-    d[0] = (__bf16)s.x;
-    d[1] = (__bf16)s.y;
-    d[2] = (__bf16)s.z;
-    d[3] = (__bf16)s.w;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) d[j] = (__bf16)acc[j];
   } else {
     float *d = reinterpret_cast<float *>(y) + t * ldy + o;
-    d[0] = s.x;
-    d[1] = s.y;
-    d[2] = s.z;
-    d[3] = s.w;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) d[j] = acc[j];
   }
 }
 
@@ -491,7 +506,7 @@ hipError_t launch_gemm_stream(const GemmParams &p_in, const StreamPlan &plan, hi
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess || p.ksplit == 1) return e;
-  const int64_t n = p.T * (p.n_out / 4);
+  const int64_t n = p.T * (p.n_out / 8);
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
                      (const float *)p.part, p.ksplit, p.T, p.n_out, p.y, p.ldy, p.y_bf16);
   return hipGetLastError();
