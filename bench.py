@@ -55,14 +55,17 @@ POOL_BYTES = 1 << 30
 # change to a kernel source makes the figure null until it is measured again.
 TRAFFIC_FETCH_SCALE = 262144.0 / 131087.3
 TRAFFIC_WRITE_SCALE = 1.0
-TRAFFIC_SOURCE_HASH = "3813cec2a2176e8c"
+TRAFFIC_SOURCE_HASH = "7f812ca13e3b2399"
 TRAFFIC_KIB = {  # workload: (FETCH_SIZE KiB, WRITE_SIZE KiB) per step, unscaled
-    "qkv_multi_t1": (7061.1, 16.0),
-    "dense_ffn_t1": (49295.3 + 25354.8, 110.6 + 16.0),
-    "moe_top8_t1": (8.8 + 7020.8 + 3825.2, 0.1 + 24.0 + 8.0),
-    "prefill_gemm_T32": (25878.3, 1088.0),
-    "prefill_gemm_T4096": (478425.1, 161234.2),
-    "moe_prefill_top8_T256": (131.8 + 8.0 + 763218.2 + 94260.9 + 8757.5, 16.0 + 17.5 + 6144.0 + 16384.0 + 1024.0),
+    "qkv_multi_t1": (7053.6, 16.0),
+    "rms_qkv_multi_t1": (7113.2, 16.0),
+    "dense_ffn_t1": (49304.3 + 25368.5, 110.9 + 16.0),
+    "moe_top8_t1": (7091.4 + 3815.9, 24.1 + 8.0),
+    "prefill_gemm_T32": (32793.7 + 3290.1, 6528.0 + 1088.0),
+    "prefill_gemm_T256": (54175.5, 8704.0),
+    "prefill_gemm_T1024": (219102.4, 34816.0),
+    "prefill_gemm_T4096": (512286.4, 139710.7),
+    "moe_prefill_top8_T256": (118.8 + 8.0 + 116798.6 + 62247.1 + 8757.5, 16.0 + 17.5 + 6144.0 + 16384.0 + 1024.0),
     "quantize_17408x5120_f32_g64": (174106.5, 48960.0),
 }
 
@@ -337,6 +340,8 @@ class MoE(Workload):
     def __init__(self, q, synth, torch, router="fused"):
         self.q = q
         self.router = router
+        if router != "fused":
+            self.name = "moe_top8_t1_%s_router" % router.replace("-", "")
         if router != "gpu":
             self.launches_per_step = 2
             self.dominant = "qgemv_kernel EPI_SWIGLU (expert gate/up%s) + EPI_MOE_DOWN" % (
