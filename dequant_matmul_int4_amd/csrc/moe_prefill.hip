@@ -524,17 +524,19 @@ hipError_t launch_mg(MoeGemmParams p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Tiles by row-tile height (measured on MI355X, 128 experts, hidden 2048,
-// inter 768): the down product (N = hidden) runs best on 128-wide column
-// tiles with a 2-step ring; the gate/up pair (two weight tiles per step) on
-// 64-wide ones.
+// Tiles and ring depths by row-tile height (measured on MI355X, 128
+// experts, hidden 2048, inter 768): the down product (N = hidden) runs best
+// on 128-wide column tiles with a 2-step ring; the gate/up pair (two weight
+// tiles per step) on 64-wide ones, except 32-row tiles, which stream
+// 128-wide tiles 4 steps ahead.
 template <int MODE>
 hipError_t launch_mode(const MoeGemmParams &p, int bm, hipStream_t stream) {
-  if (bm == 32) return launch_mg<MODE, 32, 128, 1, 4>(p, stream);
   if constexpr (MODE == MG_DOWN) {
+    if (bm == 32) return launch_mg<MODE, 32, 128, 1, 4, 2>(p, stream);
     if (bm == 64) return launch_mg<MODE, 64, 128, 2, 2, 2>(p, stream);
     if (bm == 128) return launch_mg<MODE, 128, 128, 2, 4, 2>(p, stream);
   } else {
+    if (bm == 32) return launch_mg<MODE, 32, 128, 1, 4, 4>(p, stream);
     if (bm == 64) return launch_mg<MODE, 64, 64, 2, 2>(p, stream);
     if (bm == 128) return launch_mg<MODE, 128, 64, 2, 2>(p, stream);
   }

@@ -18,7 +18,8 @@
 // float32 accumulators.
 //   * The global loads of PF steps are kept in flight in a register ring, so
 //     HBM latency is covered by PF steps of MFMA work rather than one; the
-//     barriers order LDS only and never wait for those loads.
+//     barriers order LDS only and never wait for those loads.  PF = 2 (3
+//     and 4 measured 1-6% slower at N = 17408, K = 5120).
 //   * Every load is a raw buffer load: rows past T or n_out and chunks past
 //     k_in read as zero without touching memory, so no load sits behind a
 //     branch (a branch around a load in the ring would make the compiler wait
@@ -288,7 +289,7 @@ __global__ void __launch_bounds__(WM * WN * 64) qgemm_kernel(const GemmParams p)
     }
 }
 
-template <int BM, int BN, int WM, int WN, int PF = 3>
+template <int BM, int BN, int WM, int WN, int PF = 2>
 hipError_t launch_tile(GemmParams p, hipStream_t stream) {
   constexpr size_t kStatic = (size_t)(BM + BN) * LDK * 2;
   p.m_tiles = (int)((p.T + BM - 1) / BM);
