@@ -12,7 +12,7 @@ a packed weight has ``in_dim = shape[1] * 8``, i.e. 8 codes per u32 along
 * ``codes``  -- uint32 ``[E][n_out][k_in/8]`` (E omitted for a plain matrix).
   Code ``k`` of a row sits in word ``k // 8`` at bits ``4*(k % 8)`` ..
   ``4*(k % 8)+3`` (low nibble first).  The pages never print the nibble order;
-  this is the reading taken, written down in the design doc.
+  this is the plainest reading (the first code in the least significant bits).
 * ``scales``/``biases`` -- ``[E][n_out][k_in/group_size]``, either float32 or
   bfloat16.  bfloat16 arrays are held as their raw uint16 bit patterns because
   numpy has no bfloat16 type.
