@@ -5,11 +5,28 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace qint4 {
 
 constexpr int kMaxMats = 8;    // projections per multi call
 constexpr int kMaxTopK = 8;    // experts combined per MoE call
 constexpr int kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
+
+// Lets kernel `kern` use `bytes` of dynamic LDS (more than the default 64 KB)
+// on the current device, once per device: bit d of `done` records device d
+// (devices past 63 set the attribute on every call).  Concurrent first calls
+// both set the same value.
+inline hipError_t lds_opt_in(const void *kern, int bytes, std::atomic<uint64_t> &done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 
 // Activation staging / compute modes of the GEMV family.  XM_RMS_*: the
 // activation is RMS-normalised on the way in -- x and gamma (both bf16, or

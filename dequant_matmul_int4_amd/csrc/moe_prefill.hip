@@ -510,15 +510,11 @@ hipError_t launch_mg(MoeGemmParams p, hipStream_t stream) {
   p.sb_lds = tab <= 96 * 1024 && kStatic + tab <= (size_t)kMaxLds;
   const size_t dyn = p.sb_lds ? tab : 0;
   auto kern = moe_gemm_kernel<MODE, BM, BN, WM, WN, PF>;
-  // Opt in to the LDS left next to the static tiles once per process and
-  // kernel (a benign race: concurrent first calls set the same value).
-  static bool opted = false;
-  if (dyn > 0 && !opted) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)(kMaxLds - kStatic));
+  // opt in to the LDS left next to the static tiles (once per device)
+  static std::atomic<uint64_t> opted{0};
+  if (dyn > 0) {
+    hipError_t e = lds_opt_in(reinterpret_cast<const void *>(kern), (int)(kMaxLds - kStatic), opted);
     if (e != hipSuccess) return e;
-    opted = true;
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(WM * WN * 64), dyn, stream, p);
   return hipGetLastError();

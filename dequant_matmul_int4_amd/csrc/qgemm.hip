@@ -304,16 +304,10 @@ hipError_t launch_tile(GemmParams p, hipStream_t stream) {
     return hipGetLastError();
   }
   auto kern = qgemm_kernel<BM, BN, WM, WN, PF, true>;
-  // Opt in to the LDS left next to the static tiles once per process and
-  // kernel (a benign race: concurrent first calls set the same value).
-  static bool opted = false;
-  if (!opted) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)(kMaxLds - kStatic));
-    if (e != hipSuccess) return e;
-    opted = true;
-  }
+  // opt in to the LDS left next to the static tiles (once per device)
+  static std::atomic<uint64_t> opted{0};
+  hipError_t e = lds_opt_in(reinterpret_cast<const void *>(kern), (int)(kMaxLds - kStatic), opted);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(WM * WN * 64), tab, stream, p);
   return hipGetLastError();
 }

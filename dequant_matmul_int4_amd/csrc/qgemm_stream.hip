@@ -397,14 +397,11 @@ constexpr int nbuf_for(int mt) { return mt == 4 ? 2 : 3; }
 template <int MT, int D, int SBT, bool SBL>
 hipError_t launch_cfg(const GemmParams &p, size_t lds, size_t grid, hipStream_t stream) {
   auto kern = qgemm_stream_kernel<MT, D, nbuf_for(MT), SBT, SBL>;
-  // Opt in to the LDS limit once per process and kernel (a benign race:
-  // concurrent first calls set the same value).
-  static bool opted = false;
-  if (lds > 64 * 1024 && !opted) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+  // opt in to the LDS limit (once per device)
+  static std::atomic<uint64_t> opted{0};
+  if (lds > 64 * 1024) {
+    hipError_t e = lds_opt_in(reinterpret_cast<const void *>(kern), kMaxLds, opted);
     if (e != hipSuccess) return e;
-    opted = true;
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3((kW + 1) * 64), lds, stream, p);
   return hipGetLastError();

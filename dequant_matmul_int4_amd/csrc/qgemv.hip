@@ -882,14 +882,11 @@ __global__ void __launch_bounds__(TT >= 8 ? 512 : 768) qgemv_kernel(const GemvPa
 template <int RT, int XM, int SBT, int EPI, int TT = 1>
 hipError_t launch_one(const GemvParams &p, const GemvPlan &plan, hipStream_t stream) {
   auto kern = qgemv_kernel<RT, XM, SBT, EPI, TT>;
-  // Opt in to more than 64 KB of dynamic LDS once per process and kernel
-  // (a benign race: concurrent first calls set the same value).
-  static bool big_lds = false;
-  if (plan.lds_bytes > 64 * 1024 && !big_lds) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+  // opt in to more than 64 KB of dynamic LDS (once per device)
+  static std::atomic<uint64_t> big_lds{0};
+  if (plan.lds_bytes > 64 * 1024) {
+    hipError_t e = lds_opt_in(reinterpret_cast<const void *>(kern), kMaxLds, big_lds);
     if (e != hipSuccess) return e;
-    big_lds = true;
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)plan.grid), dim3(plan.waves * 64), plan.lds_bytes,
                      stream, p);
