@@ -55,18 +55,18 @@ POOL_BYTES = 1 << 30
 # change to a kernel source makes the figure null until it is measured again.
 TRAFFIC_FETCH_SCALE = 262144.0 / 131087.3
 TRAFFIC_WRITE_SCALE = 1.0
-TRAFFIC_SOURCE_HASH = "7f812ca13e3b2399"
+TRAFFIC_SOURCE_HASH = "6e917157b79a2238"
 TRAFFIC_KIB = {  # workload: (FETCH_SIZE KiB, WRITE_SIZE KiB) per step, unscaled
     "qkv_multi_t1": (7053.6, 16.0),
     "rms_qkv_multi_t1": (7113.2, 16.0),
-    "dense_ffn_t1": (49304.3 + 25368.5, 110.9 + 16.0),
-    "moe_top8_t1": (7091.4 + 3815.9, 24.1 + 8.0),
-    "prefill_gemm_T32": (32793.7 + 3290.1, 6528.0 + 1088.0),
-    "prefill_gemm_T256": (54175.5, 8704.0),
-    "prefill_gemm_T1024": (219102.4, 34816.0),
-    "prefill_gemm_T4096": (512286.4, 139710.7),
-    "moe_prefill_top8_T256": (118.8 + 8.0 + 116798.6 + 62247.1 + 8757.5, 16.0 + 17.5 + 6144.0 + 16384.0 + 1024.0),
-    "quantize_17408x5120_f32_g64": (174106.5, 48960.0),
+    "dense_ffn_t1": (49304.6 + 25368.1, 110.6 + 16.0),
+    "moe_top8_t1": (7091.4 + 3816.1, 24.1 + 8.0),
+    "prefill_gemm_T32": (32795.7 + 3290.1, 6528.0 + 1088.0),
+    "prefill_gemm_T256": (54164.7, 8704.0),
+    "prefill_gemm_T1024": (219160.8, 34816.0),
+    "prefill_gemm_T4096": (511630.9, 139687.9),
+    "moe_prefill_top8_T256": (118.8 + 8.0 + 116767.5 + 62466.5 + 8757.5, 16.0 + 17.5 + 6144.0 + 16384.0 + 1024.0),
+    "quantize_17408x5120_f32_g64": (174107.3, 48960.0),
 }
 
 
