@@ -95,7 +95,8 @@ struct GemvParams {
                              // weight [k_in] (the activation's dtype); routing: logits [n_experts]
   int32_t route;             // EPI_SWIGLU: 0 = ids given; 1 / 2 = every wave ranks the float32 /
                              // bf16 logits itself (n_experts <= kRouteMaxExperts)
-  int32_t pad_;
+  int32_t stage_last;        // first octet of the activation's last staging round (set by
+                             // launch_gemv)
 };
 
 // Experts one wave ranks in registers when the gate/up launch routes its token.

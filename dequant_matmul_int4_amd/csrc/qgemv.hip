@@ -67,6 +67,8 @@
 //     past a matrix's end, the partial last step and skipped experts without
 //     branches.
 
+#include <algorithm>
+
 #include "kernels.h"
 #include "topk_wave.h"
 
@@ -263,7 +265,9 @@ __device__ __forceinline__ float sb_value(uint32_t bits) {
 // ncx .. ncx_pad-1 are zero.
 //
 // Staging runs in rounds of xq<XM>() octets (8 elements) per thread: thread t
-// takes octets base + t, base + t + nthreads, ...  The last round is split in
+// of the nthr threads takes octets base + t, base + t + nthr, ...  (nthr comes
+// from the kernel arguments rather than the dispatch packet, whose line the
+// argument prefetch does not cover.)  The last round is split in
 // two: stage_issue() starts its loads, stage_commit() permutes them into LDS,
 // and the code loads issued in between overlap the activation's round trip
 // (vmcnt drains in issue order, so the commit waits only for the older
@@ -347,7 +351,7 @@ __device__ __forceinline__ void stage_store(int o, const uint4 *v, int ncx_pad, 
 // gamma: XM_RMS_* only (the RMSNorm weight, same layout as x).
 template <int XM>
 __device__ __forceinline__ void stage_issue(const void *__restrict__ x, const void *__restrict__ gamma,
-                                            int ncx, int base, XRegs<XM> &r) {
+                                            int ncx, int base, int nthr, XRegs<XM> &r) {
   const uint32_t nocts = (uint32_t)ncx * 4;
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, nocts * octet_bytes<XM>());
   const __amdgpu_buffer_rsrc_t rg = make_rsrc(xm_rms(XM) ? gamma : x, nocts * octet_bytes<XM>());
@@ -356,7 +360,7 @@ __device__ __forceinline__ void stage_issue(const void *__restrict__ x, const vo
     // unconditional loads (a load inside a branch makes the compiler copy its
     // result at the join, which waits for it right away); slots past the end
     // are out of range
-    const uint32_t o = base + threadIdx.x + i * blockDim.x;
+    const uint32_t o = base + threadIdx.x + i * nthr;
     const uint32_t off = o < nocts ? o * octet_bytes<XM>() : kOutOfRange;
     constexpr int XV = xm_rms(XM) ? octet_vecs<XM>() / 2 : octet_vecs<XM>();  // vectors of x
 #pragma unroll
@@ -369,43 +373,34 @@ __device__ __forceinline__ void stage_issue(const void *__restrict__ x, const vo
 }
 
 template <int XM>
-__device__ __forceinline__ void stage_commit(int ncx, int ncx_pad, int base, const XRegs<XM> &r,
+__device__ __forceinline__ void stage_commit(int ncx, int ncx_pad, int base, int nthr, const XRegs<XM> &r,
                                              unsigned char *xbuf, float *xsum, float &ssq) {
   const int nocts = ncx * 4;
 #pragma unroll
   for (int i = 0; i < xq<XM>(); ++i) {
-    const int o = base + threadIdx.x + i * blockDim.x;
+    const int o = base + threadIdx.x + i * nthr;
     if (o < nocts) stage_store<XM>(o, r.v[i], ncx_pad, xbuf, xsum, ssq);
   }
 }
 
-// Octets per staging round, the number of rounds, and the first octet of the
-// last round.
-template <int XM>
-__device__ __forceinline__ int stage_last_base(int ncx) {
-  const int per_round = xq<XM>() * blockDim.x;
-  const int rounds = (ncx * 4 + per_round - 1) / per_round;
-  return (rounds - 1) * per_round;
-}
-
-// All staging rounds but the last, each loaded and stored before the next.
+// All staging rounds but the last (the one starting at octet `last`), each
+// loaded and stored before the next.
 template <int XM>
 __device__ __forceinline__ void stage_early_rounds(const void *__restrict__ x, const void *__restrict__ gamma,
-                                                   int ncx, int ncx_pad, unsigned char *xbuf,
-                                                   float *xsum, float &ssq) {
-  const int last = stage_last_base<XM>(ncx);
-  for (int base = 0; base < last; base += xq<XM>() * blockDim.x) {
+                                                   int ncx, int ncx_pad, int last, int nthr,
+                                                   unsigned char *xbuf, float *xsum, float &ssq) {
+  for (int base = 0; base < last; base += xq<XM>() * nthr) {
     XRegs<XM> r;
-    stage_issue<XM>(x, gamma, ncx, base, r);
-    stage_commit<XM>(ncx, ncx_pad, base, r, xbuf, xsum, ssq);
+    stage_issue<XM>(x, gamma, ncx, base, nthr, r);
+    stage_commit<XM>(ncx, ncx_pad, base, nthr, r, xbuf, xsum, ssq);
   }
 }
 
 // Zero chunks ncx .. ncx_pad-1 (whole quads: the padding is whole chunks).
 template <int XM>
-__device__ __forceinline__ void stage_padding(int ncx, int ncx_pad, unsigned char *xbuf, float *xsum,
-                                              float &ssq) {
-  for (int o = ncx * 4 + threadIdx.x; o < ncx_pad * 4; o += blockDim.x) {
+__device__ __forceinline__ void stage_padding(int ncx, int ncx_pad, int nthr, unsigned char *xbuf,
+                                              float *xsum, float &ssq) {
+  for (int o = ncx * 4 + threadIdx.x; o < ncx_pad * 4; o += nthr) {
     uint4 z[octet_vecs<XM>()];
 #pragma unroll
     for (int k = 0; k < octet_vecs<XM>(); ++k) z[k] = make_uint4(0, 0, 0, 0);
@@ -420,11 +415,11 @@ constexpr int RQ = 4;
 
 // nvec: 16-byte vectors readable at res (0: no residual; every slot is out
 // of range)
-__device__ __forceinline__ void residual_issue(const void *res, uint32_t nvec, uint4 (&v)[RQ]) {
+__device__ __forceinline__ void residual_issue(const void *res, uint32_t nvec, int nthr, uint4 (&v)[RQ]) {
   const __amdgpu_buffer_rsrc_t rr = make_rsrc(res, nvec * 16);
 #pragma unroll
   for (int i = 0; i < RQ; ++i) {
-    const uint32_t o = threadIdx.x + i * blockDim.x;
+    const uint32_t o = threadIdx.x + i * nthr;
     v[i] = buf_load_b128(rr, o < nvec ? o * 16 : kOutOfRange);
   }
 }
@@ -442,11 +437,11 @@ __device__ __forceinline__ void residual_store(int o, const uint4 w, int bf16, f
   }
 }
 
-__device__ __forceinline__ void residual_commit(int n, int bf16, const uint4 (&v)[RQ], float *dst) {
+__device__ __forceinline__ void residual_commit(int n, int bf16, int nthr, const uint4 (&v)[RQ], float *dst) {
   const int nvec = bf16 ? n / 8 : n / 4;
 #pragma unroll
   for (int i = 0; i < RQ; ++i) {
-    const int o = threadIdx.x + i * blockDim.x;
+    const int o = threadIdx.x + i * nthr;
     if (o < nvec) residual_store(o, v[i], bf16, dst);
   }
 }
@@ -481,12 +476,18 @@ struct StepBuf {
 // TT > 1 (small-M products): p.n_tok <= TT activation rows share every code
 // load and its decode; each token has its own staged activation, accumulator
 // and output row.
-template <int RT, int XM, int SBT, int EPI, int TT>
+//
+// P > 0 (one pass): no wave has more than P steps.  The ring is P steps deep
+// and is filled once; nothing is loaded after the prologue, so no load is
+// issued for a step past the wave's end except when the wave has fewer than
+// P steps.
+template <int RT, int XM, int SBT, int EPI, int TT, int P>
 __global__ void __launch_bounds__(TT >= 8 ? 512 : 768) qgemv_kernel(const GemvParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   warm_kernargs<sizeof(GemvParams)>();
   constexpr int NS = (EPI == EPI_SWIGLU) ? 2 : 1;  // code streams per row (gate, up)
-  constexpr int D = kSlots / (RT * NS);            // steps in flight
+  constexpr int D = P > 0 ? P : kSlots / (RT * NS);  // steps in flight
+  static_assert(D * RT * NS <= kSlots, "ring deeper than the register budget");
   constexpr int XB = (XM == XM_BF16) ? 64 : 128;   // staged bytes per chunk
   static_assert(!xm_rms(XM) || (TT == 1 && EPI != EPI_MOE_DOWN), "RMSNorm prologue: one token");
   constexpr uint32_t SBB = (SBT == 1) ? 2 : 4;     // bytes per scale/bias
@@ -495,6 +496,7 @@ __global__ void __launch_bounds__(TT >= 8 ? 512 : 768) qgemv_kernel(const GemvPa
   // wave index made provably uniform: all task bookkeeping stays scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int gw = blockIdx.x * p.waves_per_wg + wave;
+  const int nthr = p.waves_per_wg * 64;  // threads of the workgroup
   const int NW = p.n_waves;
   const int l2 = p.log2_lpr;
   const int L = 1 << l2;
@@ -579,10 +581,22 @@ __global__ void __launch_bounds__(TT >= 8 ? 512 : 768) qgemv_kernel(const GemvPa
   auto seek = [&](Cur &c) {  // matrix / slot of task c.t, its geometry and row0
     int m = c.m;
     if constexpr (EPI == EPI_STORE) {
-      while (m + 1 < p.n_mats && c.t >= p.task0[m + 1]) ++m;
-      c.bound = (m + 1 < p.n_mats) ? p.task0[m + 1] : p.n_tasks;
+      // task0 is ascending with INT32_MAX past n_mats: the matrix is the count
+      // of later starts at or below t, its start the largest of them and the
+      // bound the smallest start above t (all read at once, no dependent loads)
+      m = 0;
+      int first = 0, bound = p.n_tasks;
+#pragma unroll
+      for (int i = 1; i < kMaxMats; ++i) {
+        const int t0 = p.task0[i];
+        const bool in = c.t >= t0;
+        m += in ? 1 : 0;
+        first = in ? t0 : first;
+        bound = (!in && t0 < bound) ? t0 : bound;
+      }
+      c.bound = bound;
       c.n_rows = (int)p.m[m].n_out;
-      c.row0 = (c.t - p.task0[m]) * rpt;
+      c.row0 = (c.t - first) * rpt;
       c.y = reinterpret_cast<unsigned char *>(p.m[m].y);
     } else if constexpr (EPI == EPI_SWIGLU) {
       m = min(c.t / p.tasks_per_slot, p.top_k - 1);
@@ -647,7 +661,8 @@ __global__ void __launch_bounds__(TT >= 8 ? 512 : 768) qgemv_kernel(const GemvPa
   int lstep = 0;   // steps issued by the load cursor
   int lit = 0;     // step inside the task
   uint32_t lstep_c = 0, lstep_s = 0;  // byte offsets of step lit inside a row
-  auto load = [&](StepBuf<RT, NS> &bf) {
+  // advance = false: the last load of a one-pass ring (the cursor is not needed again)
+  auto load = [&](StepBuf<RT, NS> &bf, bool advance) {
     // past the wave's last step: out of range (the load is still issued, so
     // the number of loads in flight, and with it every wait, is static)
     const bool past = lstep++ >= S;
@@ -683,6 +698,7 @@ __global__ void __launch_bounds__(TT >= 8 ? 512 : 768) qgemv_kernel(const GemvPa
       }
     }
     // advance the load cursor
+    if (!advance) return;
     lstep_c += step_c;
     lstep_s += step_s;
     if (++lit == spt) {
@@ -698,21 +714,22 @@ __global__ void __launch_bounds__(TT >= 8 ? 512 : 768) qgemv_kernel(const GemvPa
     return reinterpret_cast<const unsigned char *>(p.x) + (size_t)t * p.ldx * (XM == XM_BF16 ? 2 : 4);
   };
   float ssq = 0.f;  // XM_RMS_*: this thread's share of sum(x^2)
+  const int xbase = p.stage_last;
 #pragma unroll
   for (int t = 0; t < TT; ++t)
-    stage_early_rounds<XM>(x_tok(t), p.aux, t < p.n_tok ? p.ncx : 0, ncx_pad, xbuf + t * tok_bytes,
+    stage_early_rounds<XM>(x_tok(t), p.aux, t < p.n_tok ? p.ncx : 0, ncx_pad, t < p.n_tok ? xbase : 0,
+                           nthr, xbuf + t * tok_bytes,
                            reinterpret_cast<float *>(reinterpret_cast<unsigned char *>(xsum) + t * tok_bytes),
                            ssq);
-  const int xbase = stage_last_base<XM>(p.ncx);
   XRegs<XM> xr[TT];
 #pragma unroll
   for (int t = 0; t < TT; ++t)  // activation loads first (L2), ...
-    stage_issue<XM>(x_tok(t), p.aux, t < p.n_tok ? p.ncx : 0, xbase, xr[t]);
+    stage_issue<XM>(x_tok(t), p.aux, t < p.n_tok ? p.ncx : 0, xbase, nthr, xr[t]);
   uint4 rr[RQ];
   const bool has_res = (EPI == EPI_MOE_DOWN) && p.aux != nullptr;
   if constexpr (EPI == EPI_MOE_DOWN) {
     const uint32_t nvec = has_res ? (uint32_t)(p.y_bf16 ? p.m[0].n_out / 8 : p.m[0].n_out / 4) : 0u;
-    residual_issue(has_res ? p.aux : p.x, nvec, rr);
+    residual_issue(has_res ? p.aux : p.x, nvec, nthr, rr);
   }
 
   if constexpr (EPI == EPI_SWIGLU) {
@@ -745,15 +762,15 @@ __global__ void __launch_bounds__(TT >= 8 ? 512 : 768) qgemv_kernel(const GemvPa
   // ... then the first D steps of codes (HBM).
   StepBuf<RT, NS> buf[D];
 #pragma unroll
-  for (int u = 0; u < D; ++u) load(buf[u]);
+  for (int u = 0; u < D; ++u) load(buf[u], P == 0 || u + 1 < D);
 
 #pragma unroll
   for (int t = 0; t < TT; ++t) {
     float *xs_t = reinterpret_cast<float *>(reinterpret_cast<unsigned char *>(xsum) + t * tok_bytes);
-    stage_commit<XM>(p.ncx, ncx_pad, xbase, xr[t], xbuf + t * tok_bytes, xs_t, ssq);
-    stage_padding<XM>(p.ncx, ncx_pad, xbuf + t * tok_bytes, xs_t, ssq);
+    stage_commit<XM>(p.ncx, ncx_pad, xbase, nthr, xr[t], xbuf + t * tok_bytes, xs_t, ssq);
+    stage_padding<XM>(p.ncx, ncx_pad, nthr, xbuf + t * tok_bytes, xs_t, ssq);
   }
-  if (has_res) residual_commit((int)p.m[0].n_out, p.y_bf16, rr, res_lds);
+  if (has_res) residual_commit((int)p.m[0].n_out, p.y_bf16, nthr, rr, res_lds);
   if constexpr (xm_rms(XM)) {
     const float wave_ssq = seg_sum(ssq, 6);
     if (lane == 0) res_lds[wave] = wave_ssq;
@@ -870,18 +887,36 @@ __global__ void __launch_bounds__(TT >= 8 ? 512 : 768) qgemv_kernel(const GemvPa
     }
   };
 
-  for (int s0 = 0; s0 < S; s0 += D) {
+  if constexpr (P > 0) {
 #pragma unroll
-    for (int u = 0; u < D; ++u) {
-      if (s0 + u < S) consume(buf[u]);
-      load(buf[u]);
+    for (int u = 0; u < D; ++u)
+      if (u < S) consume(buf[u]);
+  } else {
+    for (int s0 = 0; s0 < S; s0 += D) {
+#pragma unroll
+      for (int u = 0; u < D; ++u) {
+        if (s0 + u < S) consume(buf[u]);
+        load(buf[u], true);
+      }
     }
   }
 }
 
+// Steps of the busiest wave of a launch.
+int64_t max_wave_steps(const GemvParams &p, const GemvPlan &plan) {
+  return (((int64_t)plan.n_tasks + p.n_waves - 1) / p.n_waves) * plan.spt;
+}
+
 template <int RT, int XM, int SBT, int EPI, int TT = 1>
 hipError_t launch_one(const GemvParams &p, const GemvPlan &plan, hipStream_t stream) {
-  auto kern = qgemv_kernel<RT, XM, SBT, EPI, TT>;
+  auto kern = qgemv_kernel<RT, XM, SBT, EPI, TT, 0>;
+  // one-pass kernels for the stored-output GEMVs whose waves have one or two
+  // steps (T = 1 and the narrow small-M launches)
+  if constexpr (EPI == EPI_STORE && TT <= 4) {
+    const int64_t smax = max_wave_steps(p, plan);
+    if (smax == 1) kern = qgemv_kernel<RT, XM, SBT, EPI, TT, 1>;
+    if (smax == 2) kern = qgemv_kernel<RT, XM, SBT, EPI, TT, 2>;
+  }
   // opt in to more than 64 KB of dynamic LDS (once per device)
   static std::atomic<uint64_t> big_lds{0};
   if (plan.lds_bytes > 64 * 1024) {
@@ -938,9 +973,14 @@ hipError_t launch_tokens(const GemvParams &p, const GemvPlan &plan, int sb_bf16,
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemv(const GemvParams &p, const GemvPlan &plan, int xmode, int sb_bf16, int epi,
+hipError_t launch_gemv(const GemvParams &p_in, const GemvPlan &plan, int xmode, int sb_bf16, int epi,
                        hipStream_t stream) {
   if (plan.rt != 1 && plan.rt != 2) return hipErrorInvalidValue;
+  // activation staging rounds of xm_octets(xmode) octets per thread
+  GemvParams p = p_in;
+  const int64_t per_round = (int64_t)xm_octets(xmode) * plan.waves * 64;
+  const int64_t rounds = ((int64_t)p.ncx * 4 + per_round - 1) / per_round;
+  p.stage_last = (int32_t)(std::max<int64_t>(rounds, 1) - 1) * (int32_t)per_round;
   if (plan.tt != 1) {
     if (xmode != XM_BF16) return hipErrorInvalidValue;
     switch (plan.tt) {
