@@ -910,12 +910,21 @@ int64_t max_wave_steps(const GemvParams &p, const GemvPlan &plan) {
 template <int RT, int XM, int SBT, int EPI, int TT = 1>
 hipError_t launch_one(const GemvParams &p, const GemvPlan &plan, hipStream_t stream) {
   auto kern = qgemv_kernel<RT, XM, SBT, EPI, TT, 0>;
-  // one-pass kernels for the stored-output GEMVs whose waves have one or two
-  // steps (T = 1 and the narrow small-M launches)
-  if constexpr (EPI == EPI_STORE && TT <= 4) {
+  // One-pass kernels when no wave has more than 4 steps, for the launches
+  // where that happens: the stored-output GEMVs (T = 1 and the narrow small-M
+  // launches), the expert gate/up pair and the MoE down projection.
+  constexpr int NS = (EPI == EPI_SWIGLU) ? 2 : 1;
+  constexpr bool one_pass = (EPI == EPI_STORE && TT <= 4) ||
+                            (TT == 1 && EPI == EPI_SWIGLU && !xm_rms(XM)) || EPI == EPI_MOE_DOWN;
+  if constexpr (one_pass) {
     const int64_t smax = max_wave_steps(p, plan);
-    if (smax == 1) kern = qgemv_kernel<RT, XM, SBT, EPI, TT, 1>;
-    if (smax == 2) kern = qgemv_kernel<RT, XM, SBT, EPI, TT, 2>;
+    if (smax == 1) {
+      kern = qgemv_kernel<RT, XM, SBT, EPI, TT, 1>;
+    } else if (smax == 2) {
+      if constexpr (2 * RT * NS <= kSlots) kern = qgemv_kernel<RT, XM, SBT, EPI, TT, 2>;
+    } else if (smax <= 4) {
+      if constexpr (4 * RT * NS <= kSlots) kern = qgemv_kernel<RT, XM, SBT, EPI, TT, 4>;
+    }
   }
   // opt in to more than 64 KB of dynamic LDS (once per device)
   static std::atomic<uint64_t> big_lds{0};
