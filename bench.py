@@ -53,20 +53,20 @@ POOL_BYTES = 1 << 30
 # dispatch): FETCH_SIZE read 131,087 KiB -> x2.000; WRITE_SIZE 262,144 KiB -> x1.000.
 # Valid only for the kernel sources they were taken with (SOURCE_HASH); any
 # change to a kernel source makes the figure null until it is measured again.
-TRAFFIC_FETCH_SCALE = 262144.0 / 131087.3
+TRAFFIC_FETCH_SCALE = 262144.0 / 131087.2
 TRAFFIC_WRITE_SCALE = 1.0
-TRAFFIC_SOURCE_HASH = "6e917157b79a2238"
+TRAFFIC_SOURCE_HASH = "e2068b2e426c84ca"
 TRAFFIC_KIB = {  # workload: (FETCH_SIZE KiB, WRITE_SIZE KiB) per step, unscaled
-    "qkv_multi_t1": (7053.6, 16.0),
-    "rms_qkv_multi_t1": (7113.2, 16.0),
-    "dense_ffn_t1": (49304.6 + 25368.1, 110.6 + 16.0),
-    "moe_top8_t1": (7091.4 + 3816.1, 24.1 + 8.0),
-    "prefill_gemm_T32": (32795.7 + 3290.1, 6528.0 + 1088.0),
-    "prefill_gemm_T256": (54164.7, 8704.0),
-    "prefill_gemm_T1024": (219160.8, 34816.0),
-    "prefill_gemm_T4096": (511630.9, 139687.9),
-    "moe_prefill_top8_T256": (118.8 + 8.0 + 116767.5 + 62466.5 + 8757.5, 16.0 + 17.5 + 6144.0 + 16384.0 + 1024.0),
-    "quantize_17408x5120_f32_g64": (174107.3, 48960.0),
+    "qkv_multi_t1": (7002.1, 16.0),
+    "rms_qkv_multi_t1": (7055.6, 16.0),
+    "dense_ffn_t1": (49301.9 + 25354.7, 109.1 + 16.0),
+    "moe_top8_t1": (7052.0 + 3796.0, 24.1 + 8.0),
+    "prefill_gemm_T32": (32797.4 + 3290.1, 6528.0 + 1088.0),
+    "prefill_gemm_T256": (54165.7, 8704.0),
+    "prefill_gemm_T1024": (219141.7, 34816.0),
+    "prefill_gemm_T4096": (512609.8, 139755.2),
+    "moe_prefill_top8_T256": (118.8 + 8.0 + 119164.4 + 62457.3 + 8757.6, 16.0 + 17.5 + 6144.0 + 16384.0 + 1024.0),
+    "quantize_17408x5120_f32_g64": (174106.1, 48960.0),
 }
 
 
