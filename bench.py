@@ -55,7 +55,7 @@ POOL_BYTES = 1 << 30
 # change to a kernel source makes the figure null until it is measured again.
 TRAFFIC_FETCH_SCALE = 262144.0 / 131087.2
 TRAFFIC_WRITE_SCALE = 1.0
-TRAFFIC_SOURCE_HASH = "e2068b2e426c84ca"
+TRAFFIC_SOURCE_HASH = "b00dad12809727de"
 TRAFFIC_KIB = {  # workload: (FETCH_SIZE KiB, WRITE_SIZE KiB) per step, unscaled
     "qkv_multi_t1": (7002.1, 16.0),
     "rms_qkv_multi_t1": (7055.6, 16.0),
@@ -71,16 +71,20 @@ TRAFFIC_KIB = {  # workload: (FETCH_SIZE KiB, WRITE_SIZE KiB) per step, unscaled
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources' code: line comments and whitespace do not count, so an edit
+    that only touches comments keeps the measured traffic figures valid."""
     import glob
     import hashlib
+    import re
     csrc = os.path.join(ROOT, "dequant_matmul_int4_amd", "csrc")
     files = sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h")) +
                    glob.glob(os.path.join(csrc, "*.cpp")))
     h = hashlib.sha256()
     for f in files:
         h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            code = re.sub(r"//[^\n]*", "", fh.read())
+        h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 

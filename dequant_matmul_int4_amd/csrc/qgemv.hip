@@ -38,6 +38,10 @@
 //     the first ring fill is issued before the activation is staged.  Few
 //     waves per CU with deep rings: vector registers are plentiful at low
 //     occupancy, and each wave has fewer prologue instructions to amortise.
+//     When no wave of a launch has more than P = 1, 2 or 4 steps, a one-pass
+//     instantiation sizes the ring to P and fills it once: the streaming ring
+//     would also issue its refills, all out of range at that point, and those
+//     instructions compete with the real loads for the memory pipeline.
 //   * The activation is staged once per workgroup in LDS, permuted so that a
 //     lane's 128-bit LDS reads line up with the nibble order of its code
 //     words, together with the sum of every 32-element chunk; it is padded
