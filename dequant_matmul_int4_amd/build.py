@@ -21,7 +21,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqint4.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["api.cpp", "qgemv.hip", "qgemm.hip", "router.hip", "quant.hip", "moe_prefill.hip", "qgemm_stream.hip"]
+SOURCES = ["api.cpp", "qgemv.hip", "qgemv_mfma.hip", "qgemm.hip", "router.hip", "quant.hip", "moe_prefill.hip",
+           "qgemm_stream.hip"]
 ARCH = "gfx950"
 
 

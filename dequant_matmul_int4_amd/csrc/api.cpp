@@ -280,10 +280,12 @@ namespace {
 // Shared body of qgemv_int4, qgemv_int4_multi and qgemv_int4_smallm: T
 // activation rows x + t * ldx (T = 1: the plain GEMV).
 // gamma != NULL: RMSNorm prologue (T must be 1).
+// batched: a qgemv_int4_smallm call, whose rows must not depend on T (the
+// stored-output bf16 form then runs on MFMA for every T, T = 1 included).
 qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t x_dtype,
                        int64_t T, int64_t ldx, void *const *ys, int32_t y_dtype, int32_t epilogue,
                        hipStream_t stream, const char *fn, const void *gamma = nullptr,
-                       float eps = 0.f) {
+                       float eps = 0.f, bool batched = false) {
   if (n < 1 || n > QINT4_MULTI_MAX)
     return fail(QINT4_ERR_SHAPE, "%s: n = %d not in [1, %d]", fn, n, QINT4_MULTI_MAX);
   if (!ws) return fail(QINT4_ERR_NULL, "%s: matrix array is NULL", fn);
@@ -373,6 +375,45 @@ qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t
     return t;
   };
   const int tt = T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : 8;
+  const int64_t sbrow_b = (k_in / ws[0].group_size) * (int64_t)elem_bytes(ws[0].sb_dtype);
+
+  // small-M calls with bf16 activations into stored outputs: MFMA tiles of 16
+  // rows when the shape allows, for every T alike (so a T-row call equals T
+  // one-row calls)
+  if (batched && !swiglu && !gamma && x_dtype == QINT4_BF16 &&
+      gemv_mfma_supported(k_in, ws[0].group_size)) {
+    if (((T - 1) * ldx + k_in) * 2 >= ((int64_t)1 << 31))
+      return fail(QINT4_ERR_SHAPE, "%s: activation rows span 2 GiB or more", fn);
+    GemvParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.n_mats = n;
+    int64_t tiles = 0;
+    for (int i = 0; i < kMaxMats; ++i) p.task0[i] = INT32_MAX;
+    for (int i = 0; i < n; ++i) {
+      p.m[i].codes = ws[i].codes;
+      p.m[i].scales = ws[i].scales;
+      p.m[i].biases = ws[i].biases;
+      p.m[i].y = ys[i];
+      p.m[i].n_out = ws[i].n_out;
+      p.task0[i] = (int32_t)tiles;
+      tiles += (ws[i].n_out + 15) / 16;
+    }
+    if (tiles > INT32_MAX) return fail(QINT4_ERR_SHAPE, "%s: too many rows", fn);
+    p.n_tasks = (int32_t)tiles;
+    p.kwb = (int32_t)(k_in / 2);
+    p.sbrow = (int32_t)sbrow_b;
+    p.log2_group = ilog2(ws[0].group_size);
+    p.ncx = (int32_t)(k_in / 32);
+    p.waves_per_wg = (int32_t)(k_in / 512);
+    p.n_tok = (int32_t)T;
+    p.ldx = (int32_t)ldx;
+    p.x = x;
+    p.y_bf16 = y_dtype == QINT4_BF16;
+    hipError_t e = launch_gemv_mfma(p, tt, ws[0].group_size, sb_bf16, tiles, stream);
+    if (e != hipSuccess) return fail(QINT4_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
+  }
+
   // the RMSNorm partial sums take one LDS float per wave
   const GemvPlan plan = plan_gemv(nc, n_cu, xmode, gamma ? kMaxWaves : 0, tasks_for, tt);
   if (plan.waves == 0)
@@ -445,7 +486,8 @@ qint4_status qgemv_int4_smallm(int32_t n, const qint4_matrix *ws, const void *x,
                                int64_t T, int64_t ldx, void *const *ys, int32_t y_dtype,
                                int32_t epilogue, void *stream) {
   return run_multi(n, ws, x, x_dtype, T, ldx, ys, y_dtype, epilogue,
-                   reinterpret_cast<hipStream_t>(stream), "qgemv_int4_smallm");
+                   reinterpret_cast<hipStream_t>(stream), "qgemv_int4_smallm", nullptr, 0.f,
+                   true);
 }
 
 size_t moe_gather_qgemv_int4_workspace_bytes(int64_t inter, int32_t top_k) {

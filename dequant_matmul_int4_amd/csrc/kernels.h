@@ -120,6 +120,15 @@ static_assert(sizeof(GemvParams) <= 512, "GEMV kernel arguments exceed 8 cache l
 hipError_t launch_gemv(const GemvParams &p, const GemvPlan &plan, int xmode, int sb_bf16,
                        int epi, hipStream_t stream);
 
+// The stored-output GEMV family with bf16 activations on MFMA (qgemv_mfma.hip):
+// tiles of 16 rows (task0[i] = first tile of matrix i), waves_per_wg = k_in /
+// 512 K slices per tile, n_tok rows of x with stride ldx, ncx = k_in / 32.
+// Supported shapes take this path for every token count.
+bool gemv_mfma_supported(int64_t k_in, int group_size);
+size_t gemv_mfma_lds_bytes(int tt, int group_size, int64_t k_in);
+hipError_t launch_gemv_mfma(const GemvParams &p, int tt, int group_size, int sb_bf16, int64_t n_tiles,
+                            hipStream_t stream);
+
 // LDS bytes a GEMV launch needs: per token, the staged activation (padded to
 // ncx_pad chunks) and its chunk sums; then (MoE down) the float32 residual row
 // or (XM_RMS_*) one float per wave.

@@ -1,0 +1,346 @@
+// qgemv_mfma.hip -- the stored-output int4 GEMV family with bf16 activations,
+// for 1..8 activation rows, on gfx950 MFMA (v_mfma_f32_16x16x32_bf16).
+//
+// Sources (by page title and passage):
+//   [FFAI #14] thewafflehaus/FFAI pull 14, "feat(everything-bagel): clean
+//              migration of PR #9 + #10 onto updated dev": int4 GEMV wrappers
+//              (weight, scales, biases, in_dim, group_size); batched QKV
+//              (several projections of one input in one launch).
+//   [ds4 #844] antirez/ds4 pull 844, "Ornith 1.5 + Qwen 3.8 27B hybrid
+//              runtime + DFlash speculative decoding on Metal": small row
+//              counts (speculative-verify rounds below the MMA tile) and the
+//              contract that a batched call reproduces sequential calls
+//              bit for bit.
+//
+// The product per row and group is the factorised affine form used by the
+// GEMV kernels:
+//     sum_k (s q_k + b) x_k = s * (sum_k (128 + q_k) x_k - 128 sum x) + b sum x,
+// with (128 + q) formed exactly as bf16 (bits 0x4300 | q).  Here the inner
+// sums come from MFMA instead of v_dot2: the codes are the B operand (16 rows
+// of a tile as its N columns), the staged activation rows the A operand (its
+// M rows; rows past T repeat the last token and are never stored).  Every
+// output element is one column of the product, so a token's result does not
+// depend on how many tokens share the launch: a T-row call equals T one-row
+// calls bit for bit.
+//
+// Work decomposition (gfx950 specific, not from the pages):
+//   * A workgroup owns a tile of 16 rows of one matrix; its KS waves split
+//     k_in into slices of 512 (16 chunks of 32 codes, 4 steps of 128).
+//   * Lane (r, kb) = (lane % 16, lane / 16) loads, per step, the 16-byte
+//     chunk 4*step + kb of row r: a load instruction covers 16 rows x 64
+//     contiguous bytes.  An MFMA takes 8 codes (one word) per lane, and its
+//     32-deep K must stay inside one group; a 4 x 4 exchange of words between
+//     the lanes 16 apart (two permlane32 and two permlane16 swaps) leaves lane
+//     (r, kb) with word kb of each of the step's 4 chunks, so MFMA i covers
+//     exactly chunk 4*step + i.
+//   * Each wave stages its own activation slice (all T rows) in its own LDS
+//     region, permuted to the nibble-pair order of the decoded words, with the
+//     per-group sums of every row, and the (scale, bias) pairs of its 16 rows
+//     and groups: no workgroup barrier until the final reduction.
+//   * After each group's chunks, lane (r, kb) applies row r's scale and bias
+//     to its 4 accumulators (tokens 4*kb .. 4*kb + 3).  At the end the waves
+//     write their accumulators to LDS and the workgroup sums the K slices in
+//     wave order and stores the T x 16 outputs.
+
+#include "kernels.h"
+
+namespace qint4 {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kChunksPerWave = 16;  // 512 k per wave
+constexpr int kTileRows = 16;
+constexpr uint32_t kOutOfRange = 0x80000000u;  // resources are < 2 GiB
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load_b128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  const v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
+}
+
+template <int SBT>
+__device__ __forceinline__ uint32_t buf_load_sb(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (SBT == 1)
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+  else
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+template <int SBT>
+__device__ __forceinline__ float sb_value(uint32_t bits) {
+  return __uint_as_float(SBT == 1 ? (bits << 16) : bits);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Touch every 64-byte line of the kernel arguments with back-to-back scalar
+// loads and one wait, rather than several dependent rounds of misses.
+__device__ __forceinline__ void warm_kernargs() {
+  typedef const uint32_t __attribute__((address_space(4))) *kptr;
+  const kptr ka = (kptr)__builtin_amdgcn_kernarg_segment_ptr();
+  uint32_t v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (i * 64 < (int)sizeof(GemvParams)) ? ka[i * 16] : 0u;
+  asm volatile("" ::"s"(v[0]), "s"(v[1]), "s"(v[2]), "s"(v[3]), "s"(v[4]), "s"(v[5]), "s"(v[6]),
+               "s"(v[7]));
+}
+
+// Workgroup barrier ordering LDS only (no drain of outstanding vector loads).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned segments of 2^L2 lanes (L2 = 2, 3 or 4); all lanes active.
+template <int L2>
+__device__ __forceinline__ float seg_sum(float v) {
+  v += dpp_mov<0xB1>(v);                    // lane ^ 1
+  v += dpp_mov<0x4E>(v);                    // lane ^ 2
+  if constexpr (L2 >= 3) v += dpp_mov<0x141>(v);  // other quad of 8
+  if constexpr (L2 >= 4) v += dpp_mov<0x140>(v);  // other half of 16
+  return v;
+}
+
+__device__ __forceinline__ void store_out(void *y, int64_t i, float v, int bf16) {
+  if (bf16)
+    reinterpret_cast<__bf16 *>(y)[i] = (__bf16)v;
+  else
+    reinterpret_cast<float *>(y)[i] = v;
+}
+
+// LDS bytes of one wave's region: TT staged rows of 16 chunks (plus 16 bytes
+// of padding per row against bank conflicts), the per-group sums of 16 token
+// slots, and the (scale, bias) pairs of 16 rows.  At least 1 KB: the region
+// also takes the wave's accumulators for the final reduction.
+constexpr int wave_region_bytes(int tt, int cpg) {
+  const int ng = kChunksPerWave / cpg;
+  const int b = tt * (kChunksPerWave * 64 + 16) + ng * 16 * 4 + ng * 16 * 8;
+  return b > 1024 ? b : 1024;
+}
+
+template <int SBT, int CPG, int TT>
+__global__ void __launch_bounds__(1024) qgemv_mfma_kernel(const GemvParams p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  warm_kernargs();
+  constexpr int NG = kChunksPerWave / CPG;  // groups per wave
+  constexpr int TS = kChunksPerWave * 64 + 16;
+  constexpr int WR = wave_region_bytes(TT, CPG);
+  constexpr uint32_t SBB = (SBT == 1) ? 2 : 4;
+  constexpr int TE = (NG * 16 + 63) / 64;  // (scale, bias) entries per lane
+
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int T = p.n_tok;
+
+  // the tile's matrix: count of later matrix starts at or below the tile
+  const int tile = blockIdx.x;
+  int m = 0, first = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxMats; ++i) {
+    const int t0 = p.task0[i];
+    const bool in = tile >= t0;
+    m += in ? 1 : 0;
+    first = in ? t0 : first;
+  }
+  const GemvMat &mat = p.m[m];
+  const int n_rows = (int)mat.n_out;
+  const int row0 = (tile - first) * kTileRows;
+  const uint32_t kwb = (uint32_t)p.kwb, sbrow = (uint32_t)p.sbrow;
+  const int r = lane & 15, kb = lane >> 4;
+  const int c0 = wv * kChunksPerWave;  // first chunk of this wave's slice
+  const int g0 = c0 / CPG;
+
+  unsigned char *reg = smem + wv * WR;
+  unsigned char *xst = reg;                                                // [TT][16 chunks][4 words] x 16 B
+  float *xsum = reinterpret_cast<float *>(reg + TT * TS);                  // [NG][16 tokens]
+  float2 *tbl = reinterpret_cast<float2 *>(reg + TT * TS + NG * 16 * 4);   // [NG][16 rows]
+
+  // ---- loads: activation rows first (L2), then scales/biases, then codes ----
+  // lane covers elements 8 lane .. 8 lane + 7 of the slice of each token
+  const __amdgpu_buffer_rsrc_t rx =
+      make_rsrc(p.x, (uint32_t)(((int64_t)(T - 1) * p.ldx + (int64_t)p.ncx * 32) * 2));
+  uint4 xv[TT];
+#pragma unroll
+  for (int t = 0; t < TT; ++t) {
+    const uint32_t off =
+        t < T ? (uint32_t)(((int64_t)t * p.ldx + (int64_t)c0 * 32 + lane * 8) * 2) : kOutOfRange;
+    xv[t] = buf_load_b128(rx, off);
+  }
+  // keep the issue order (activation, scales/biases, codes): the staging then
+  // waits only for the activation loads
+  __builtin_amdgcn_sched_barrier(0);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(mat.scales, (uint32_t)n_rows * sbrow);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(mat.biases, (uint32_t)n_rows * sbrow);
+  uint32_t sr[TE], br[TE];
+#pragma unroll
+  for (int j = 0; j < TE; ++j) {
+    const int e = lane + 64 * j;  // entry (group e / 16, row e % 16)
+    const uint32_t off = e < NG * 16
+                             ? (uint32_t)(row0 + (e & 15)) * sbrow + (uint32_t)(g0 + (e >> 4)) * SBB
+                             : kOutOfRange;
+    sr[j] = buf_load_sb<SBT>(rs, off);
+    br[j] = buf_load_sb<SBT>(rb, off);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(mat.codes, (uint32_t)n_rows * kwb);
+  uint4 cw[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    cw[s] = buf_load_b128(rc, (uint32_t)(row0 + r) * kwb + (uint32_t)(c0 + 4 * s + kb) * 16);
+
+  // ---- stage the activation slice and its per-group sums ----
+#pragma unroll
+  for (int t = 0; t < TT; ++t) {
+    if (t >= T) break;  // uniform
+    const uint4 w = xv[t];
+    uint4 pr;  // pairs (x_i, x_{i+4}): the order of the decoded nibble pairs
+    pr.x = (w.x & 0xFFFFu) | (w.z << 16);
+    pr.y = (w.x >> 16) | (w.z & 0xFFFF0000u);
+    pr.z = (w.y & 0xFFFFu) | (w.w << 16);
+    pr.w = (w.y >> 16) | (w.w & 0xFFFF0000u);
+    *reinterpret_cast<uint4 *>(xst + t * TS + lane * 16) = pr;
+    float s8 = ((bf16_lo(w.x) + bf16_hi(w.x)) + (bf16_lo(w.y) + bf16_hi(w.y))) +
+               ((bf16_lo(w.z) + bf16_hi(w.z)) + (bf16_lo(w.w) + bf16_hi(w.w)));
+    constexpr int L2 = CPG == 1 ? 2 : CPG == 2 ? 3 : 4;  // lanes of one group: 4 * CPG
+    s8 = seg_sum<L2>(s8);
+    if ((lane & (4 * CPG - 1)) == 0) xsum[(lane / (4 * CPG)) * 16 + t] = s8;
+  }
+#pragma unroll
+  for (int j = 0; j < TE; ++j) {
+    const int e = lane + 64 * j;
+    if (e < NG * 16) tbl[e] = make_float2(sb_value<SBT>(sr[j]), sb_value<SBT>(br[j]));
+  }
+
+  // ---- products ----
+  uint32_t magic = 0x43004300u;
+  asm volatile("" : "+v"(magic));  // keep in a VGPR so AND-OR stays one VOP3
+  const int nn = min(lane & 15, T - 1);  // token of this lane's A row
+  const unsigned char *xa = xst + nn * TS + kb * 16;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    uint32_t w0 = cw[s].x, w1 = cw[s].y, w2 = cw[s].z, w3 = cw[s].w;
+    // lane (r, kb) holds chunk 4s + kb; exchange so that it holds word kb of
+    // chunks 4s .. 4s + 3 (a 4 x 4 transpose over the lanes 16 apart)
+    {
+      auto a = __builtin_amdgcn_permlane32_swap(w0, w2, false, false);
+      w0 = a[0];
+      w2 = a[1];
+      auto b = __builtin_amdgcn_permlane32_swap(w1, w3, false, false);
+      w1 = b[0];
+      w3 = b[1];
+      auto e = __builtin_amdgcn_permlane16_swap(w0, w1, false, false);
+      w0 = e[0];
+      w1 = e[1];
+      auto f = __builtin_amdgcn_permlane16_swap(w2, w3, false, false);
+      w2 = f[0];
+      w3 = f[1];
+    }
+    const uint32_t wd[4] = {w0, w1, w2, w3};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ch = 4 * s + i;  // chunk of the slice
+      uint32_t pq[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) pq[k] = ((wd[i] >> (4 * k)) & 0x000F000Fu) | magic;
+      const uint4 xq = *reinterpret_cast<const uint4 *>(xa + ch * 64);
+      const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, make_uint4(pq[0], pq[1], pq[2], pq[3]));
+      const bf16x8_t ax = __builtin_bit_cast(bf16x8_t, xq);
+      const f32x4_t cin = (ch % CPG == 0) ? f32x4_t{0.f, 0.f, 0.f, 0.f} : c;
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, bw, cin, 0, 0, 0);
+      if ((ch + 1) % CPG == 0) {
+        const int g = ch / CPG;
+        const float2 sbv = tbl[g * 16 + r];
+        const f32x4_t xs = *reinterpret_cast<const f32x4_t *>(xsum + g * 16 + 4 * kb);
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) {
+          const float d = c[mm] - 128.f * xs[mm];
+          acc[mm] += fmaf(sbv.x, d, sbv.y * xs[mm]);
+        }
+      }
+    }
+  }
+
+  // ---- sum the K slices (wave order) and store ----
+  *reinterpret_cast<f32x4_t *>(reg + lane * 16) = acc;  // this wave is done with its region
+  lds_barrier();
+  const int KS = p.waves_per_wg;
+  for (int o = threadIdx.x; o < kTileRows * T; o += KS * 64) {
+    const int rr = o & 15, n = o >> 4;
+    const int src = (rr + 16 * (n >> 2)) * 16 + (n & 3) * 4;  // lane and accumulator of (n, rr)
+    float v = 0.f;
+    for (int w = 0; w < KS; ++w) v += *reinterpret_cast<const float *>(smem + w * WR + src);
+    const int row = row0 + rr;
+    if (row < n_rows) store_out(mat.y, (int64_t)n * n_rows + row, v, p.y_bf16);
+  }
+}
+
+template <int SBT, int CPG, int TT>
+hipError_t launch_mfma(const GemvParams &p, int64_t grid, int ks, hipStream_t stream) {
+  auto kern = qgemv_mfma_kernel<SBT, CPG, TT>;
+  const size_t lds = (size_t)ks * wave_region_bytes(TT, CPG);
+  static std::atomic<uint64_t> big_lds{0};
+  if (lds > 64 * 1024) {
+    hipError_t e = lds_opt_in(reinterpret_cast<const void *>(kern), kMaxLds, big_lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(ks * 64), lds, stream, p);
+  return hipGetLastError();
+}
+
+template <int SBT, int CPG>
+hipError_t launch_tt(const GemvParams &p, int tt, int64_t grid, int ks, hipStream_t s) {
+  switch (tt) {
+    case 1: return launch_mfma<SBT, CPG, 1>(p, grid, ks, s);
+    case 2: return launch_mfma<SBT, CPG, 2>(p, grid, ks, s);
+    case 4: return launch_mfma<SBT, CPG, 4>(p, grid, ks, s);
+    case 8: return launch_mfma<SBT, CPG, 8>(p, grid, ks, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+size_t gemv_mfma_lds_bytes(int tt, int group_size, int64_t k_in) {
+  const int cpg = group_size / 32;
+  return (size_t)(k_in / (32 * kChunksPerWave)) * (size_t)wave_region_bytes(tt, cpg);
+}
+
+bool gemv_mfma_supported(int64_t k_in, int group_size) {
+  if (group_size != 32 && group_size != 64 && group_size != 128) return false;
+  if (k_in % (32 * kChunksPerWave) != 0) return false;
+  const int64_t ks = k_in / (32 * kChunksPerWave);
+  if (ks < 1 || ks > 16) return false;
+  // every token count takes this path or none does (rows of a T-row call equal
+  // one-row calls bit for bit), so the largest staging must fit
+  return gemv_mfma_lds_bytes(kMaxTokens, group_size, k_in) <= (size_t)kMaxLds;
+}
+
+hipError_t launch_gemv_mfma(const GemvParams &p, int tt, int group_size, int sb_bf16, int64_t n_tiles,
+                            hipStream_t stream) {
+  const int ks = p.waves_per_wg;
+  if (ks < 1 || ks > 16 || n_tiles < 1) return hipErrorInvalidValue;
+  switch (group_size) {
+    case 32: return sb_bf16 ? launch_tt<1, 1>(p, tt, n_tiles, ks, stream) : launch_tt<0, 1>(p, tt, n_tiles, ks, stream);
+    case 64: return sb_bf16 ? launch_tt<1, 2>(p, tt, n_tiles, ks, stream) : launch_tt<0, 2>(p, tt, n_tiles, ks, stream);
+    case 128: return sb_bf16 ? launch_tt<1, 4>(p, tt, n_tiles, ks, stream) : launch_tt<0, 4>(p, tt, n_tiles, ks, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace qint4

@@ -155,8 +155,16 @@ qint4_status qgemv_int4_multi(int32_t n, const qint4_matrix *ws, const void *x,
  *
  * [ds4 #844], PR body and the commit on small speculative-verify rounds: a
  * fused gate/up SwiGLU for 1..8 rows, and 2..9-token verify rounds that
- * cannot fill a 32-row matrix-multiply tile.  Every code load and its nibble decode is shared by the T rows; the
- * arithmetic per row is exactly that of qgemv_int4_multi.
+ * cannot fill a 32-row matrix-multiply tile; and its batched-vs-sequential
+ * contract: row t of a T-row call equals a T = 1 call of this function on
+ * row t, bit for bit.  Every code load and its nibble decode is shared by the
+ * T rows.  The per-group form is that of qgemv_int4_multi,
+ *   s * (sum (128 + q) x - 128 sum x) + b sum x,
+ * but with bf16 activations, stored outputs (QINT4_EPI_NONE), group_size 32,
+ * 64 or 128 and k_in a multiple of 512 up to 8192, the inner sums come from
+ * MFMA for every T: those results agree with qgemv_int4_multi's to the
+ * rounding of float32 sums, not bit for bit.  Other calls run the
+ * qgemv_int4_multi arithmetic per row.
  *
  *   T        1..QINT4_SMALLM_MAX; T > 1 needs x_dtype QINT4_BF16
  *   x        device [T][ldx], row t at x + t * ldx elements, 16-byte aligned;

@@ -22,6 +22,7 @@ def test_case_tables_reach_every_ring_form():
     assert {c[3] for c in GEMV_CASES} == {0, 1, 2, 4}
     assert {c[4] for c in GEMV_CASES if c[3] == 4} == {3, 4}
     assert {c[3] for c in SMALLM_CASES} == {0, 1, 2, 4}
+    assert all(c[2] % 512 for c in SMALLM_CASES)  # off the small-M MFMA route
     assert {c[2] for c in SWIGLU_CASES} == {0, 1, 2, 4}
     assert {c[4] for c in MOE_CASES} == {0, 1, 2} and {c[5] for c in MOE_CASES} == {0, 1, 2, 4}
 

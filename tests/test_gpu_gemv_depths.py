@@ -50,12 +50,13 @@ def test_gemv_ring_forms(n_out, k_in, x_dt, depth, steps):
     check(y, y_ref, a_ref, "gemv %dx%d %s depth %d" % (n_out, k_in, x_dt, depth))
 
 
-# (T, n_out, k_in, ring depth, steps)
+# (T, n_out, k_in, ring depth, steps); k_in not a multiple of 512, so that the
+# small-M call runs the GEMV rings rather than the MFMA form
 SMALLM_CASES = [
-    (2, 8, 1024, 1, 1),
-    (2, 9000, 2048, 2, 2),
-    (4, 20000, 2048, 4, 4),
-    (4, 16000, 2048, 0, 7),
+    (2, 64, 256, 1, 1),
+    (2, 8, 2304, 2, 2),
+    (4, 2000, 2304, 4, 3),
+    (4, 5000, 2304, 0, 9),
 ]
 
 

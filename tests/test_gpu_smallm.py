@@ -104,3 +104,46 @@ def test_smallm_rejects_float32_multi_row():
     with pytest.raises(q.Int4Error) as e:
         q.qgemv_int4_smallm([dev_matrix(w)], x, [y])
     assert e.value.status == "ERR_DTYPE"
+
+
+# The MFMA form of small-M calls (bf16 activations, stored outputs, group 32/64/128,
+# k_in a multiple of 512 up to 8192): one wave per 512-k slice of a 16-row tile.
+@pytest.mark.parametrize("n_out,k_in,g,sb", [(40, 512, 64, "bf16"), (37, 8192, 64, "bf16"),
+                                             (300, 1536, 32, "f32"), (129, 2560, 128, "f32"),
+                                             (16, 4096, 128, "bf16")])
+@pytest.mark.parametrize("T", [1, 3, 8])
+def test_smallm_mfma_form_shapes(T, n_out, k_in, g, sb):
+    """One wave per tile (k_in 512: 128 outputs over 64 threads), sixteen (8192), float32
+    scales, ragged 16-row tiles, padded activation rows (ldx > k_in)."""
+    q = lib()
+    rng = np.random.default_rng(T * 7 + n_out + k_in)
+    w = synth.draw_matrix(rng, n_out, k_in, g, sb)
+    x, xd = _x(rng, T, k_in, ldx=k_in + 24)
+    y = torch.full((T, n_out), float("nan"), dtype=torch.bfloat16, device="cuda")
+    q.qgemv_int4_smallm([dev_matrix(w)], xd, [y])
+    torch.cuda.synchronize()
+    for t in range(T):
+        ref, a = oracle.gemv(w, x[t], "bf16", threads=oracle_threads())
+        check(y[t], ref, a, "smallm mfma T=%d t=%d %dx%d g%d %s" % (T, t, n_out, k_in, g, sb))
+
+
+def test_smallm_mfma_rows_independent_of_T_and_close_to_the_gemv():
+    """Rows of a T = 5 call equal T = 1 calls bit for bit; a T = 1 small-M call (MFMA sums)
+    agrees with qgemv_int4 (v_dot2 sums) within float32 rounding of the sums."""
+    q = lib()
+    rng = np.random.default_rng(91)
+    w = synth.draw_matrix(rng, 200, 2048, 64, "bf16")
+    x, xd = _x(rng, 5, 2048)
+    y5 = nan_like((5, 200), torch.float32)
+    q.qgemv_int4_smallm([dev_matrix(w)], xd, [y5])
+    for t in range(5):
+        y1 = nan_like((1, 200), torch.float32)
+        q.qgemv_int4_smallm([dev_matrix(w)], xd[t:t + 1].contiguous(), [y1])
+        yg = nan_like(200, torch.float32)
+        q.qgemv_int4(dev_matrix(w), xd[t].contiguous(), yg)
+        torch.cuda.synchronize()
+        assert torch.equal(y1[0], y5[t]), t
+        ref, a = oracle.gemv(w, x[t], "bf16")
+        check(y5[t], ref, a, "smallm mfma t=%d" % t)
+        diff = (y1[0].double() - yg.double()).abs().cpu().numpy()
+        assert np.all(diff <= 2.0 ** -16 * a), t
