@@ -404,7 +404,7 @@ qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t
     p.sbrow = (int32_t)sbrow_b;
     p.log2_group = ilog2(ws[0].group_size);
     p.ncx = (int32_t)(k_in / 32);
-    p.waves_per_wg = (int32_t)(k_in / 512);
+    p.waves_per_wg = gemv_mfma_waves(k_in);
     p.n_tok = (int32_t)T;
     p.ldx = (int32_t)ldx;
     p.x = x;

@@ -125,6 +125,7 @@ hipError_t launch_gemv(const GemvParams &p, const GemvPlan &plan, int xmode, int
 // 512 K slices per tile, n_tok rows of x with stride ldx, ncx = k_in / 32.
 // Supported shapes take this path for every token count.
 bool gemv_mfma_supported(int64_t k_in, int group_size);
+int gemv_mfma_waves(int64_t k_in);  // K slices (waves) per tile
 size_t gemv_mfma_lds_bytes(int tt, int group_size, int64_t k_in);
 hipError_t launch_gemv_mfma(const GemvParams &p, int tt, int group_size, int sb_bf16, int64_t n_tiles,
                             hipStream_t stream);

@@ -25,7 +25,7 @@
 //
 // Work decomposition (gfx950 specific, not from the pages):
 //   * A workgroup owns a tile of 16 rows of one matrix; its KS waves split
-//     k_in into slices of 512 (16 chunks of 32 codes, 4 steps of 128).
+//     k_in into slices of kChunksPerWave chunks of 32 codes (steps of 128).
 //   * Lane (r, kb) = (lane % 16, lane / 16) loads, per step, the 16-byte
 //     chunk 4*step + kb of row r: a load instruction covers 16 rows x 64
 //     contiguous bytes.  An MFMA takes 8 codes (one word) per lane, and its
@@ -50,7 +50,12 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kChunksPerWave = 16;  // 512 k per wave
+#ifndef QINT4_MFMA_CHUNKS_PER_WAVE
+#define QINT4_MFMA_CHUNKS_PER_WAVE 16
+#endif
+constexpr int kChunksPerWave = QINT4_MFMA_CHUNKS_PER_WAVE;  // 32-code chunks per wave
+constexpr int kSteps = kChunksPerWave / 4;                   // 128-k steps per wave
+static_assert(kChunksPerWave % 4 == 0 && kChunksPerWave >= 4, "whole 128-k steps");
 constexpr int kTileRows = 16;
 constexpr uint32_t kOutOfRange = 0x80000000u;  // resources are < 2 GiB
 
@@ -170,15 +175,19 @@ __global__ void __launch_bounds__(1024) qgemv_mfma_kernel(const GemvParams p) {
   float2 *tbl = reinterpret_cast<float2 *>(reg + TT * TS + NG * 16 * 4);   // [NG][16 rows]
 
   // ---- loads: activation rows first (L2), then scales/biases, then codes ----
-  // lane covers elements 8 lane .. 8 lane + 7 of the slice of each token
+  // the slice of a token is U 16-byte units (8 elements each); unit
+  // u = lane + 64 i of the wave's TT * U is element 8 (u % U) of token u / U
+  constexpr int U = kChunksPerWave * 4;
+  constexpr int XR = (TT * U + 63) / 64;  // staging rounds
   const __amdgpu_buffer_rsrc_t rx =
       make_rsrc(p.x, (uint32_t)(((int64_t)(T - 1) * p.ldx + (int64_t)p.ncx * 32) * 2));
-  uint4 xv[TT];
+  uint4 xv[XR];
 #pragma unroll
-  for (int t = 0; t < TT; ++t) {
+  for (int i = 0; i < XR; ++i) {
+    const int u = lane + 64 * i, t = u / U, lu = u % U;
     const uint32_t off =
-        t < T ? (uint32_t)(((int64_t)t * p.ldx + (int64_t)c0 * 32 + lane * 8) * 2) : kOutOfRange;
-    xv[t] = buf_load_b128(rx, off);
+        t < T ? (uint32_t)(((int64_t)t * p.ldx + (int64_t)c0 * 32 + lu * 8) * 2) : kOutOfRange;
+    xv[i] = buf_load_b128(rx, off);
   }
   // keep the issue order (activation, scales/biases, codes): the staging then
   // waits only for the activation loads
@@ -197,27 +206,29 @@ __global__ void __launch_bounds__(1024) qgemv_mfma_kernel(const GemvParams p) {
   }
   __builtin_amdgcn_sched_barrier(0);
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(mat.codes, (uint32_t)n_rows * kwb);
-  uint4 cw[4];
+  uint4 cw[kSteps];
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
+  for (int s = 0; s < kSteps; ++s)
     cw[s] = buf_load_b128(rc, (uint32_t)(row0 + r) * kwb + (uint32_t)(c0 + 4 * s + kb) * 16);
 
   // ---- stage the activation slice and its per-group sums ----
+  // (all lanes take part in every round: the group sums reduce over 4 * CPG
+  // neighbouring lanes, which never straddle two tokens since U % 16 == 0)
 #pragma unroll
-  for (int t = 0; t < TT; ++t) {
-    if (t >= T) break;  // uniform
-    const uint4 w = xv[t];
+  for (int i = 0; i < XR; ++i) {
+    const int u = lane + 64 * i, t = u / U, lu = u % U;
+    const uint4 w = xv[i];
     uint4 pr;  // pairs (x_i, x_{i+4}): the order of the decoded nibble pairs
     pr.x = (w.x & 0xFFFFu) | (w.z << 16);
     pr.y = (w.x >> 16) | (w.z & 0xFFFF0000u);
     pr.z = (w.y & 0xFFFFu) | (w.w << 16);
     pr.w = (w.y >> 16) | (w.w & 0xFFFF0000u);
-    *reinterpret_cast<uint4 *>(xst + t * TS + lane * 16) = pr;
+    if (t < T) *reinterpret_cast<uint4 *>(xst + t * TS + lu * 16) = pr;
     float s8 = ((bf16_lo(w.x) + bf16_hi(w.x)) + (bf16_lo(w.y) + bf16_hi(w.y))) +
                ((bf16_lo(w.z) + bf16_hi(w.z)) + (bf16_lo(w.w) + bf16_hi(w.w)));
     constexpr int L2 = CPG == 1 ? 2 : CPG == 2 ? 3 : 4;  // lanes of one group: 4 * CPG
     s8 = seg_sum<L2>(s8);
-    if ((lane & (4 * CPG - 1)) == 0) xsum[(lane / (4 * CPG)) * 16 + t] = s8;
+    if (t < T && (lu & (4 * CPG - 1)) == 0) xsum[(lu / (4 * CPG)) * 16 + t] = s8;
   }
 #pragma unroll
   for (int j = 0; j < TE; ++j) {
@@ -233,7 +244,7 @@ __global__ void __launch_bounds__(1024) qgemv_mfma_kernel(const GemvParams p) {
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   f32x4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
+  for (int s = 0; s < kSteps; ++s) {
     uint32_t w0 = cw[s].x, w1 = cw[s].y, w2 = cw[s].z, w3 = cw[s].w;
     // lane (r, kb) holds chunk 4s + kb; exchange so that it holds word kb of
     // chunks 4s .. 4s + 3 (a 4 x 4 transpose over the lanes 16 apart)
@@ -320,6 +331,8 @@ size_t gemv_mfma_lds_bytes(int tt, int group_size, int64_t k_in) {
   const int cpg = group_size / 32;
   return (size_t)(k_in / (32 * kChunksPerWave)) * (size_t)wave_region_bytes(tt, cpg);
 }
+
+int gemv_mfma_waves(int64_t k_in) { return (int)(k_in / (32 * kChunksPerWave)); }
 
 bool gemv_mfma_supported(int64_t k_in, int group_size) {
   if (group_size != 32 && group_size != 64 && group_size != 128) return false;
