@@ -55,18 +55,18 @@ POOL_BYTES = 1 << 30
 # change to a kernel source makes the figure null until it is measured again.
 TRAFFIC_FETCH_SCALE = 262144.0 / 131087.2
 TRAFFIC_WRITE_SCALE = 1.0
-TRAFFIC_SOURCE_HASH = "b00dad12809727de"
+TRAFFIC_SOURCE_HASH = "6640dc37d5a22f7a"
 TRAFFIC_KIB = {  # workload: (FETCH_SIZE KiB, WRITE_SIZE KiB) per step, unscaled
     "qkv_multi_t1": (7002.1, 16.0),
-    "rms_qkv_multi_t1": (7055.6, 16.0),
-    "dense_ffn_t1": (49301.9 + 25354.7, 109.1 + 16.0),
-    "moe_top8_t1": (7052.0 + 3796.0, 24.1 + 8.0),
-    "prefill_gemm_T32": (32797.4 + 3290.1, 6528.0 + 1088.0),
-    "prefill_gemm_T256": (54165.7, 8704.0),
-    "prefill_gemm_T1024": (219141.7, 34816.0),
-    "prefill_gemm_T4096": (512609.8, 139755.2),
-    "moe_prefill_top8_T256": (118.8 + 8.0 + 119164.4 + 62457.3 + 8757.6, 16.0 + 17.5 + 6144.0 + 16384.0 + 1024.0),
-    "quantize_17408x5120_f32_g64": (174106.1, 48960.0),
+    "rms_qkv_multi_t1": (7055.7, 16.0),
+    "dense_ffn_t1": (74656.1, 126.5),
+    "moe_top8_t1": (10847.9, 32.1),
+    "prefill_gemm_T32": (36088.3, 7616.0),
+    "prefill_gemm_T256": (54165.0, 8704.0),
+    "prefill_gemm_T1024": (219200.8, 34816.0),
+    "prefill_gemm_T4096": (512313.7, 139688.2),
+    "moe_prefill_top8_T256": (188126.9, 23585.5),
+    "quantize_17408x5120_f32_g64": (174106.7, 48960.0),
 }
 
 
@@ -207,7 +207,7 @@ class SmallM(QKV):
         super().__init__(q, synth, torch)
         self.T = T
         self.name = "qkv_smallm_T%d" % T
-        self.dominant = "qgemv_kernel (EPI_STORE, bf16 x, 3 matrices, %d tokens)" % T
+        self.dominant = "qgemv_mfma_kernel (bf16 x, 3 matrices, %d tokens)" % T
         self.xT = torch.randn(T, 4096, device="cuda").to(torch.bfloat16)
         self.ysT = [torch.empty(T, n, device="cuda", dtype=torch.bfloat16) for n in (4096, 1024, 1024)]
         self.config = dict(self.config, workload=self.name, T=T)
