@@ -377,11 +377,11 @@ qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t
   const int tt = T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : 8;
   const int64_t sbrow_b = (k_in / ws[0].group_size) * (int64_t)elem_bytes(ws[0].sb_dtype);
 
-  // small-M calls with bf16 activations into stored outputs: MFMA tiles of 16
-  // rows when the shape allows, for every T alike (so a T-row call equals T
-  // one-row calls)
-  if (batched && !swiglu && !gamma && x_dtype == QINT4_BF16 &&
-      gemv_mfma_supported(k_in, ws[0].group_size)) {
+  // small-M calls with bf16 activations (stored outputs or the gate/up pair):
+  // MFMA tiles of 16 rows when the shape allows, for every T alike (so a T-row
+  // call equals T one-row calls)
+  if (batched && !gamma && x_dtype == QINT4_BF16 &&
+      gemv_mfma_supported(k_in, ws[0].group_size, swiglu ? 2 : 1)) {
     if (((T - 1) * ldx + k_in) * 2 >= ((int64_t)1 << 31))
       return fail(QINT4_ERR_SHAPE, "%s: activation rows span 2 GiB or more", fn);
     GemvParams p;
@@ -393,8 +393,9 @@ qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t
       p.m[i].codes = ws[i].codes;
       p.m[i].scales = ws[i].scales;
       p.m[i].biases = ws[i].biases;
-      p.m[i].y = ys[i];
+      p.m[i].y = swiglu ? ys[0] : ys[i];
       p.m[i].n_out = ws[i].n_out;
+      if (swiglu && i > 0) continue;  // the pair shares the gate's tiles
       p.task0[i] = (int32_t)tiles;
       tiles += (ws[i].n_out + 15) / 16;
     }
@@ -409,7 +410,7 @@ qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t
     p.ldx = (int32_t)ldx;
     p.x = x;
     p.y_bf16 = y_dtype == QINT4_BF16;
-    hipError_t e = launch_gemv_mfma(p, tt, ws[0].group_size, sb_bf16, tiles, stream);
+    hipError_t e = launch_gemv_mfma(p, tt, ws[0].group_size, sb_bf16, swiglu ? 1 : 0, tiles, stream);
     if (e != hipSuccess) return fail(QINT4_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return ok();
   }

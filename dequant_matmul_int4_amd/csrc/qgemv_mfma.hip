@@ -127,23 +127,27 @@ __device__ __forceinline__ void store_out(void *y, int64_t i, float v, int bf16)
     reinterpret_cast<float *>(y)[i] = v;
 }
 
-// LDS bytes of one wave's region: TT staged rows of 16 chunks (plus 16 bytes
+// LDS bytes of one wave's region: TT staged rows of the slice (plus 16 bytes
 // of padding per row against bank conflicts), the per-group sums of 16 token
-// slots, and the (scale, bias) pairs of 16 rows.  At least 1 KB: the region
-// also takes the wave's accumulators for the final reduction.
-constexpr int wave_region_bytes(int tt, int cpg) {
+// slots, and the (scale, bias) pairs of 16 rows for each of the NS code
+// streams.  At least NS KB: the region also takes the wave's accumulators for
+// the final reduction.
+constexpr int wave_region_bytes(int tt, int cpg, int ns) {
   const int ng = kChunksPerWave / cpg;
-  const int b = tt * (kChunksPerWave * 64 + 16) + ng * 16 * 4 + ng * 16 * 8;
-  return b > 1024 ? b : 1024;
+  const int b = tt * (kChunksPerWave * 64 + 16) + ng * 16 * 4 + ns * ng * 16 * 8;
+  return b > ns * 1024 ? b : ns * 1024;
 }
 
-template <int SBT, int CPG, int TT>
+// NS = 1: stored outputs of up to kMaxMats matrices (tile t of matrix i from
+// task0[i]).  NS = 2: the gate/up pair (m[0], m[1]) with the SwiGLU epilogue
+// h = silu(gate) * up written to m[0].y.
+template <int SBT, int CPG, int TT, int NS>
 __global__ void __launch_bounds__(1024) qgemv_mfma_kernel(const GemvParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   warm_kernargs();
   constexpr int NG = kChunksPerWave / CPG;  // groups per wave
   constexpr int TS = kChunksPerWave * 64 + 16;
-  constexpr int WR = wave_region_bytes(TT, CPG);
+  constexpr int WR = wave_region_bytes(TT, CPG, NS);
   constexpr uint32_t SBB = (SBT == 1) ? 2 : 4;
   constexpr int TE = (NG * 16 + 63) / 64;  // (scale, bias) entries per lane
 
@@ -154,15 +158,17 @@ __global__ void __launch_bounds__(1024) qgemv_mfma_kernel(const GemvParams p) {
   // the tile's matrix: count of later matrix starts at or below the tile
   const int tile = blockIdx.x;
   int m = 0, first = 0;
+  if constexpr (NS == 1) {
 #pragma unroll
-  for (int i = 1; i < kMaxMats; ++i) {
-    const int t0 = p.task0[i];
-    const bool in = tile >= t0;
-    m += in ? 1 : 0;
-    first = in ? t0 : first;
+    for (int i = 1; i < kMaxMats; ++i) {
+      const int t0 = p.task0[i];
+      const bool in = tile >= t0;
+      m += in ? 1 : 0;
+      first = in ? t0 : first;
+    }
   }
-  const GemvMat &mat = p.m[m];
-  const int n_rows = (int)mat.n_out;
+  const int n_rows = (int)p.m[m].n_out;
+  void *const y = p.m[m].y;
   const int row0 = (tile - first) * kTileRows;
   const uint32_t kwb = (uint32_t)p.kwb, sbrow = (uint32_t)p.sbrow;
   const int r = lane & 15, kb = lane >> 4;
@@ -170,9 +176,9 @@ __global__ void __launch_bounds__(1024) qgemv_mfma_kernel(const GemvParams p) {
   const int g0 = c0 / CPG;
 
   unsigned char *reg = smem + wv * WR;
-  unsigned char *xst = reg;                                                // [TT][16 chunks][4 words] x 16 B
+  unsigned char *xst = reg;                                                // [TT][chunks][4 words] x 16 B
   float *xsum = reinterpret_cast<float *>(reg + TT * TS);                  // [NG][16 tokens]
-  float2 *tbl = reinterpret_cast<float2 *>(reg + TT * TS + NG * 16 * 4);   // [NG][16 rows]
+  float2 *tbl = reinterpret_cast<float2 *>(reg + TT * TS + NG * 16 * 4);   // [NS][NG][16 rows]
 
   // ---- loads: activation rows first (L2), then scales/biases, then codes ----
   // the slice of a token is U 16-byte units (8 elements each); unit
@@ -192,24 +198,31 @@ __global__ void __launch_bounds__(1024) qgemv_mfma_kernel(const GemvParams p) {
   // keep the issue order (activation, scales/biases, codes): the staging then
   // waits only for the activation loads
   __builtin_amdgcn_sched_barrier(0);
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(mat.scales, (uint32_t)n_rows * sbrow);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(mat.biases, (uint32_t)n_rows * sbrow);
-  uint32_t sr[TE], br[TE];
+  uint32_t sr[NS][TE], br[NS][TE];
 #pragma unroll
-  for (int j = 0; j < TE; ++j) {
-    const int e = lane + 64 * j;  // entry (group e / 16, row e % 16)
-    const uint32_t off = e < NG * 16
-                             ? (uint32_t)(row0 + (e & 15)) * sbrow + (uint32_t)(g0 + (e >> 4)) * SBB
-                             : kOutOfRange;
-    sr[j] = buf_load_sb<SBT>(rs, off);
-    br[j] = buf_load_sb<SBT>(rb, off);
+  for (int st = 0; st < NS; ++st) {
+    const GemvMat &mat = p.m[m + st];
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(mat.scales, (uint32_t)n_rows * sbrow);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(mat.biases, (uint32_t)n_rows * sbrow);
+#pragma unroll
+    for (int j = 0; j < TE; ++j) {
+      const int e = lane + 64 * j;  // entry (group e / 16, row e % 16)
+      const uint32_t off = e < NG * 16
+                               ? (uint32_t)(row0 + (e & 15)) * sbrow + (uint32_t)(g0 + (e >> 4)) * SBB
+                               : kOutOfRange;
+      sr[st][j] = buf_load_sb<SBT>(rs, off);
+      br[st][j] = buf_load_sb<SBT>(rb, off);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
-  const __amdgpu_buffer_rsrc_t rc = make_rsrc(mat.codes, (uint32_t)n_rows * kwb);
-  uint4 cw[kSteps];
+  uint4 cw[NS][kSteps];
 #pragma unroll
-  for (int s = 0; s < kSteps; ++s)
-    cw[s] = buf_load_b128(rc, (uint32_t)(row0 + r) * kwb + (uint32_t)(c0 + 4 * s + kb) * 16);
+  for (int st = 0; st < NS; ++st) {
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.m[m + st].codes, (uint32_t)n_rows * kwb);
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s)
+      cw[st][s] = buf_load_b128(rc, (uint32_t)(row0 + r) * kwb + (uint32_t)(c0 + 4 * s + kb) * 16);
+  }
 
   // ---- stage the activation slice and its per-group sums ----
   // (all lanes take part in every round: the group sums reduce over 4 * CPG
@@ -231,24 +244,32 @@ __global__ void __launch_bounds__(1024) qgemv_mfma_kernel(const GemvParams p) {
     if (t < T && (lu & (4 * CPG - 1)) == 0) xsum[(lu / (4 * CPG)) * 16 + t] = s8;
   }
 #pragma unroll
-  for (int j = 0; j < TE; ++j) {
-    const int e = lane + 64 * j;
-    if (e < NG * 16) tbl[e] = make_float2(sb_value<SBT>(sr[j]), sb_value<SBT>(br[j]));
-  }
+  for (int st = 0; st < NS; ++st)
+#pragma unroll
+    for (int j = 0; j < TE; ++j) {
+      const int e = lane + 64 * j;
+      if (e < NG * 16) tbl[st * NG * 16 + e] = make_float2(sb_value<SBT>(sr[st][j]), sb_value<SBT>(br[st][j]));
+    }
 
   // ---- products ----
   uint32_t magic = 0x43004300u;
   asm volatile("" : "+v"(magic));  // keep in a VGPR so AND-OR stays one VOP3
   const int nn = min(lane & 15, T - 1);  // token of this lane's A row
   const unsigned char *xa = xst + nn * TS + kb * 16;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t acc[NS], c[NS];
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    acc[st] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    c[st] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
 #pragma unroll
   for (int s = 0; s < kSteps; ++s) {
-    uint32_t w0 = cw[s].x, w1 = cw[s].y, w2 = cw[s].z, w3 = cw[s].w;
-    // lane (r, kb) holds chunk 4s + kb; exchange so that it holds word kb of
-    // chunks 4s .. 4s + 3 (a 4 x 4 transpose over the lanes 16 apart)
-    {
+    uint32_t wd[NS][4];
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      uint32_t w0 = cw[st][s].x, w1 = cw[st][s].y, w2 = cw[st][s].z, w3 = cw[st][s].w;
+      // lane (r, kb) holds chunk 4s + kb; exchange so that it holds word kb of
+      // chunks 4s .. 4s + 3 (a 4 x 4 transpose over the lanes 16 apart)
       auto a = __builtin_amdgcn_permlane32_swap(w0, w2, false, false);
       w0 = a[0];
       w2 = a[1];
@@ -261,50 +282,67 @@ __global__ void __launch_bounds__(1024) qgemv_mfma_kernel(const GemvParams p) {
       auto f = __builtin_amdgcn_permlane16_swap(w2, w3, false, false);
       w2 = f[0];
       w3 = f[1];
+      wd[st][0] = w0;
+      wd[st][1] = w1;
+      wd[st][2] = w2;
+      wd[st][3] = w3;
     }
-    const uint32_t wd[4] = {w0, w1, w2, w3};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ch = 4 * s + i;  // chunk of the slice
-      uint32_t pq[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) pq[k] = ((wd[i] >> (4 * k)) & 0x000F000Fu) | magic;
       const uint4 xq = *reinterpret_cast<const uint4 *>(xa + ch * 64);
-      const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, make_uint4(pq[0], pq[1], pq[2], pq[3]));
       const bf16x8_t ax = __builtin_bit_cast(bf16x8_t, xq);
-      const f32x4_t cin = (ch % CPG == 0) ? f32x4_t{0.f, 0.f, 0.f, 0.f} : c;
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, bw, cin, 0, 0, 0);
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        uint32_t pq[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) pq[k] = ((wd[st][i] >> (4 * k)) & 0x000F000Fu) | magic;
+        const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, make_uint4(pq[0], pq[1], pq[2], pq[3]));
+        const f32x4_t cin = (ch % CPG == 0) ? f32x4_t{0.f, 0.f, 0.f, 0.f} : c[st];
+        c[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, bw, cin, 0, 0, 0);
+      }
       if ((ch + 1) % CPG == 0) {
         const int g = ch / CPG;
-        const float2 sbv = tbl[g * 16 + r];
         const f32x4_t xs = *reinterpret_cast<const f32x4_t *>(xsum + g * 16 + 4 * kb);
 #pragma unroll
-        for (int mm = 0; mm < 4; ++mm) {
-          const float d = c[mm] - 128.f * xs[mm];
-          acc[mm] += fmaf(sbv.x, d, sbv.y * xs[mm]);
+        for (int st = 0; st < NS; ++st) {
+          const float2 sbv = tbl[(st * NG + g) * 16 + r];
+#pragma unroll
+          for (int mm = 0; mm < 4; ++mm) {
+            const float d = c[st][mm] - 128.f * xs[mm];
+            acc[st][mm] += fmaf(sbv.x, d, sbv.y * xs[mm]);
+          }
         }
       }
     }
   }
 
   // ---- sum the K slices (wave order) and store ----
-  *reinterpret_cast<f32x4_t *>(reg + lane * 16) = acc;  // this wave is done with its region
+#pragma unroll
+  for (int st = 0; st < NS; ++st)  // this wave is done with its region
+    *reinterpret_cast<f32x4_t *>(reg + st * 1024 + lane * 16) = acc[st];
   lds_barrier();
   const int KS = p.waves_per_wg;
   for (int o = threadIdx.x; o < kTileRows * T; o += KS * 64) {
     const int rr = o & 15, n = o >> 4;
     const int src = (rr + 16 * (n >> 2)) * 16 + (n & 3) * 4;  // lane and accumulator of (n, rr)
-    float v = 0.f;
-    for (int w = 0; w < KS; ++w) v += *reinterpret_cast<const float *>(smem + w * WR + src);
+    float v[NS];
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      v[st] = 0.f;
+      for (int w = 0; w < KS; ++w) v[st] += *reinterpret_cast<const float *>(smem + w * WR + st * 1024 + src);
+    }
+    float out = v[0];
+    if constexpr (NS == 2) out = (v[0] / (1.f + __expf(-v[0]))) * v[1];
     const int row = row0 + rr;
-    if (row < n_rows) store_out(mat.y, (int64_t)n * n_rows + row, v, p.y_bf16);
+    if (row < n_rows) store_out(y, (int64_t)n * n_rows + row, out, p.y_bf16);
   }
 }
 
-template <int SBT, int CPG, int TT>
+template <int SBT, int CPG, int TT, int NS>
 hipError_t launch_mfma(const GemvParams &p, int64_t grid, int ks, hipStream_t stream) {
-  auto kern = qgemv_mfma_kernel<SBT, CPG, TT>;
-  const size_t lds = (size_t)ks * wave_region_bytes(TT, CPG);
+  auto kern = qgemv_mfma_kernel<SBT, CPG, TT, NS>;
+  const size_t lds = (size_t)ks * wave_region_bytes(TT, CPG, NS);
   static std::atomic<uint64_t> big_lds{0};
   if (lds > 64 * 1024) {
     hipError_t e = lds_opt_in(reinterpret_cast<const void *>(kern), kMaxLds, big_lds);
@@ -314,46 +352,53 @@ hipError_t launch_mfma(const GemvParams &p, int64_t grid, int ks, hipStream_t st
   return hipGetLastError();
 }
 
-template <int SBT, int CPG>
+template <int SBT, int CPG, int NS>
 hipError_t launch_tt(const GemvParams &p, int tt, int64_t grid, int ks, hipStream_t s) {
   switch (tt) {
-    case 1: return launch_mfma<SBT, CPG, 1>(p, grid, ks, s);
-    case 2: return launch_mfma<SBT, CPG, 2>(p, grid, ks, s);
-    case 4: return launch_mfma<SBT, CPG, 4>(p, grid, ks, s);
-    case 8: return launch_mfma<SBT, CPG, 8>(p, grid, ks, s);
+    case 1: return launch_mfma<SBT, CPG, 1, NS>(p, grid, ks, s);
+    case 2: return launch_mfma<SBT, CPG, 2, NS>(p, grid, ks, s);
+    case 4: return launch_mfma<SBT, CPG, 4, NS>(p, grid, ks, s);
+    case 8: return launch_mfma<SBT, CPG, 8, NS>(p, grid, ks, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int NS>
+hipError_t launch_group(const GemvParams &p, int tt, int group_size, int sb_bf16, int64_t grid, int ks,
+                        hipStream_t s) {
+  switch (group_size) {
+    case 32: return sb_bf16 ? launch_tt<1, 1, NS>(p, tt, grid, ks, s) : launch_tt<0, 1, NS>(p, tt, grid, ks, s);
+    case 64: return sb_bf16 ? launch_tt<1, 2, NS>(p, tt, grid, ks, s) : launch_tt<0, 2, NS>(p, tt, grid, ks, s);
+    case 128: return sb_bf16 ? launch_tt<1, 4, NS>(p, tt, grid, ks, s) : launch_tt<0, 4, NS>(p, tt, grid, ks, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-size_t gemv_mfma_lds_bytes(int tt, int group_size, int64_t k_in) {
+size_t gemv_mfma_lds_bytes(int tt, int group_size, int64_t k_in, int streams) {
   const int cpg = group_size / 32;
-  return (size_t)(k_in / (32 * kChunksPerWave)) * (size_t)wave_region_bytes(tt, cpg);
+  return (size_t)(k_in / (32 * kChunksPerWave)) * (size_t)wave_region_bytes(tt, cpg, streams);
 }
 
 int gemv_mfma_waves(int64_t k_in) { return (int)(k_in / (32 * kChunksPerWave)); }
 
-bool gemv_mfma_supported(int64_t k_in, int group_size) {
+bool gemv_mfma_supported(int64_t k_in, int group_size, int streams) {
   if (group_size != 32 && group_size != 64 && group_size != 128) return false;
   if (k_in % (32 * kChunksPerWave) != 0) return false;
   const int64_t ks = k_in / (32 * kChunksPerWave);
   if (ks < 1 || ks > 16) return false;
   // every token count takes this path or none does (rows of a T-row call equal
   // one-row calls bit for bit), so the largest staging must fit
-  return gemv_mfma_lds_bytes(kMaxTokens, group_size, k_in) <= (size_t)kMaxLds;
+  return gemv_mfma_lds_bytes(kMaxTokens, group_size, k_in, streams) <= (size_t)kMaxLds;
 }
 
-hipError_t launch_gemv_mfma(const GemvParams &p, int tt, int group_size, int sb_bf16, int64_t n_tiles,
-                            hipStream_t stream) {
+hipError_t launch_gemv_mfma(const GemvParams &p, int tt, int group_size, int sb_bf16, int swiglu,
+                            int64_t n_tiles, hipStream_t stream) {
   const int ks = p.waves_per_wg;
   if (ks < 1 || ks > 16 || n_tiles < 1) return hipErrorInvalidValue;
-  switch (group_size) {
-    case 32: return sb_bf16 ? launch_tt<1, 1>(p, tt, n_tiles, ks, stream) : launch_tt<0, 1>(p, tt, n_tiles, ks, stream);
-    case 64: return sb_bf16 ? launch_tt<1, 2>(p, tt, n_tiles, ks, stream) : launch_tt<0, 2>(p, tt, n_tiles, ks, stream);
-    case 128: return sb_bf16 ? launch_tt<1, 4>(p, tt, n_tiles, ks, stream) : launch_tt<0, 4>(p, tt, n_tiles, ks, stream);
-    default: return hipErrorInvalidValue;
-  }
+  return swiglu ? launch_group<2>(p, tt, group_size, sb_bf16, n_tiles, ks, stream)
+                : launch_group<1>(p, tt, group_size, sb_bf16, n_tiles, ks, stream);
 }
 
 }  // namespace qint4

@@ -160,9 +160,9 @@ qint4_status qgemv_int4_multi(int32_t n, const qint4_matrix *ws, const void *x,
  * row t, bit for bit.  Every code load and its nibble decode is shared by the
  * T rows.  The per-group form is that of qgemv_int4_multi,
  *   s * (sum (128 + q) x - 128 sum x) + b sum x,
- * but with bf16 activations, stored outputs (QINT4_EPI_NONE), group_size 32,
- * 64 or 128 and k_in a multiple of 512 up to 8192, the inner sums come from
- * MFMA for every T: those results agree with qgemv_int4_multi's to the
+ * but with bf16 activations, group_size 32, 64 or 128 and k_in a multiple of
+ * 512 up to 8192 (stored outputs or the gate/up pair), the inner sums come
+ * from MFMA for every T: those results agree with qgemv_int4_multi's to the
  * rounding of float32 sums, not bit for bit.  Other calls run the
  * qgemv_int4_multi arithmetic per row.
  *

@@ -147,3 +147,45 @@ def test_smallm_mfma_rows_independent_of_T_and_close_to_the_gemv():
         check(y5[t], ref, a, "smallm mfma t=%d" % t)
         diff = (y1[0].double() - yg.double()).abs().cpu().numpy()
         assert np.all(diff <= 2.0 ** -16 * a), t
+
+
+@pytest.mark.parametrize("inter,hidden,g,sb,h_dt", [(1000, 2560, 32, "f32", "bf16"),
+                                                    (37, 8192, 128, "bf16", "f32"),
+                                                    (48, 512, 64, "bf16", "bf16")])
+@pytest.mark.parametrize("T", [1, 5, 8])
+def test_smallm_swiglu_pair_mfma_form(T, inter, hidden, g, sb, h_dt):
+    """The gate/up pair on the MFMA form: two code streams per 16-row tile, SwiGLU after
+    the sum of the K slices; group 32 with float32 scales, 16 waves per tile, one wave."""
+    q = lib()
+    rng = np.random.default_rng(T + inter + hidden)
+    gate = synth.draw_matrix(rng, inter, hidden, g, sb)
+    up = synth.draw_matrix(rng, inter, hidden, g, sb)
+    x, xd = _x(rng, T, hidden)
+    h = torch.full((T, inter), float("nan"), dtype=torch.bfloat16 if h_dt == "bf16" else torch.float32,
+                   device="cuda")
+    q.qgemv_int4_smallm([dev_matrix(gate), dev_matrix(up)], xd, [h], epilogue=q.EPI_SWIGLU_PAIR)
+    torch.cuda.synchronize()
+    for t in range(T):
+        ref, a = oracle.swiglu_pair(gate, up, x[t], "bf16")
+        got = to_np64(h[t])
+        assert np.all(np.isfinite(got))
+        if h_dt == "bf16":
+            check(h[t], ref, a, "swiglu mfma T=%d t=%d" % (T, t))
+        else:
+            assert np.all(np.abs(got - ref) <= 1e-5 * np.abs(ref) + 2.0 ** -16 * a), t
+
+
+def test_smallm_swiglu_pair_rows_independent_of_T():
+    q = lib()
+    rng = np.random.default_rng(12)
+    gate = synth.draw_matrix(rng, 320, 3072, 64, "bf16")
+    up = synth.draw_matrix(rng, 320, 3072, 64, "bf16")
+    x, xd = _x(rng, 6, 3072)
+    h6 = nan_like((6, 320), torch.float32)
+    q.qgemv_int4_smallm([dev_matrix(gate), dev_matrix(up)], xd, [h6], epilogue=q.EPI_SWIGLU_PAIR)
+    for t in (0, 3, 5):
+        h1 = nan_like((1, 320), torch.float32)
+        q.qgemv_int4_smallm([dev_matrix(gate), dev_matrix(up)], xd[t:t + 1].contiguous(), [h1],
+                            epilogue=q.EPI_SWIGLU_PAIR)
+        torch.cuda.synchronize()
+        assert torch.equal(h1[0], h6[t]), t
