@@ -55,18 +55,18 @@ POOL_BYTES = 1 << 30
 # change to a kernel source makes the figure null until it is measured again.
 TRAFFIC_FETCH_SCALE = 262144.0 / 131087.2
 TRAFFIC_WRITE_SCALE = 1.0
-TRAFFIC_SOURCE_HASH = "6640dc37d5a22f7a"
+TRAFFIC_SOURCE_HASH = "898ba556cf8c17dd"
 TRAFFIC_KIB = {  # workload: (FETCH_SIZE KiB, WRITE_SIZE KiB) per step, unscaled
     "qkv_multi_t1": (7002.1, 16.0),
-    "rms_qkv_multi_t1": (7055.7, 16.0),
-    "dense_ffn_t1": (74656.1, 126.5),
-    "moe_top8_t1": (10847.9, 32.1),
-    "prefill_gemm_T32": (36088.3, 7616.0),
-    "prefill_gemm_T256": (54165.0, 8704.0),
-    "prefill_gemm_T1024": (219200.8, 34816.0),
-    "prefill_gemm_T4096": (512313.7, 139688.2),
-    "moe_prefill_top8_T256": (188126.9, 23585.5),
-    "quantize_17408x5120_f32_g64": (174106.7, 48960.0),
+    "rms_qkv_multi_t1": (7055.6, 16.0),
+    "dense_ffn_t1": (74653.5, 125.5),
+    "moe_top8_t1": (10847.8, 32.1),
+    "prefill_gemm_T32": (36086.2, 7616.0),
+    "prefill_gemm_T256": (54164.9, 8704.0),
+    "prefill_gemm_T1024": (219143.3, 34816.0),
+    "prefill_gemm_T4096": (511968.4, 139705.1),
+    "moe_prefill_top8_T256": (188082.1, 23585.5),
+    "quantize_17408x5120_f32_g64": (174106.6, 48960.0),
 }
 
 
