@@ -110,7 +110,8 @@ def test_smallm_rejects_float32_multi_row():
 # k_in a multiple of 512 up to 8192): one wave per 512-k slice of a 16-row tile.
 @pytest.mark.parametrize("n_out,k_in,g,sb", [(40, 512, 64, "bf16"), (37, 8192, 64, "bf16"),
                                              (300, 1536, 32, "f32"), (129, 2560, 128, "f32"),
-                                             (16, 4096, 128, "bf16")])
+                                             (16, 4096, 128, "bf16"), (1, 512, 128, "bf16"),
+                                             (17, 1024, 32, "f32")])
 @pytest.mark.parametrize("T", [1, 3, 8])
 def test_smallm_mfma_form_shapes(T, n_out, k_in, g, sb):
     """One wave per tile (k_in 512: 128 outputs over 64 threads), sixteen (8192), float32
