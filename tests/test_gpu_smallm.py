@@ -190,3 +190,41 @@ def test_smallm_swiglu_pair_rows_independent_of_T():
                             epilogue=q.EPI_SWIGLU_PAIR)
         torch.cuda.synchronize()
         assert torch.equal(h1[0], h6[t]), t
+
+
+def _rows(w, idx):
+    """The rows idx of a plain matrix, as a matrix of its own (for sampled oracle rows)."""
+    import dataclasses
+    return dataclasses.replace(w, codes=np.ascontiguousarray(w.codes[idx]),
+                               scales=np.ascontiguousarray(w.scales[idx]),
+                               biases=np.ascontiguousarray(w.biases[idx]), n_out=len(idx),
+                               raw_codes=None)
+
+
+def test_smallm_workload_sizes_mfma_form():
+    """The benchmark shapes on the MFMA form: q/k/v (4096 -> 4096/1024/1024) at T = 8, every
+    output against the oracle; the 5120 -> 17408 gate/up pair at T = 8 on 512 sampled rows."""
+    q = lib()
+    d = synth.qkv_multi()
+    rng = np.random.default_rng(808)
+    x, xd = _x(rng, 8, 4096)
+    ys = [torch.full((8, w.n_out), float("nan"), dtype=torch.bfloat16, device="cuda") for w in d["ws"]]
+    q.qgemv_int4_smallm([dev_matrix(w) for w in d["ws"]], xd, ys)
+    torch.cuda.synchronize()
+    for t in range(8):
+        for i, (w, y, (ref, a)) in enumerate(zip(d["ws"], ys, oracle.multi(d["ws"], x[t], "bf16",
+                                                                             threads=oracle_threads()))):
+            check(y[t], ref, a, "qkv T=8 t=%d m=%d" % (t, i))
+
+    dl = synth.dense_layer()
+    x, xd = _x(rng, 8, 5120)
+    h = nan_like((8, 17408), torch.float32)
+    q.qgemv_int4_smallm([dev_matrix(dl["gate"]), dev_matrix(dl["up"])], xd, [h],
+                        epilogue=q.EPI_SWIGLU_PAIR)
+    torch.cuda.synchronize()
+    idx = np.sort(rng.choice(17408, size=512, replace=False))
+    gs, us = _rows(dl["gate"], idx), _rows(dl["up"], idx)
+    hs = to_np64(h)[:, idx]
+    for t in range(8):
+        ref, a = oracle.swiglu_pair(gs, us, x[t], "bf16")
+        assert np.all(np.abs(hs[t] - ref) <= 1e-5 * np.abs(ref) + 2.0 ** -16 * a), t
