@@ -182,8 +182,10 @@ constexpr int kMaxWaves = 12;  // waves per workgroup (one persistent workgroup 
 // with a partial last step), row groups per task RT (1, 2) and waves per CU W
 // (1..8).  Tasks are dealt round-robin to n_cu * W waves, so a CU's critical
 // path is ceil(tasks / (n_cu W)) tasks per wave; the cost of a candidate is
-// that times W waves times the loads of one task.  The cheapest wins (ties:
-// larger RT, then more waves).  A residual row (MoE down) must fit the
+// that times W waves times the loads of one task.  Activations staged as
+// float32 (128 LDS bytes per chunk, read once per step for the RT row groups
+// of a task) add one load's worth per step: taller tasks share those reads.
+// The cheapest wins (ties: larger RT, then more waves).  A residual row (MoE down) must fit the
 // workgroup's one-pass staging: 4 vectors of 16 bytes per thread.
 template <class TasksFor>
 GemvPlan plan_gemv(int cpr, int n_cu, int xmode, int64_t residual_rows, TasksFor tasks_for,
@@ -196,6 +198,7 @@ GemvPlan plan_gemv(int cpr, int n_cu, int xmode, int64_t residual_rows, TasksFor
   for (int l : {32, 64})
     if (cpr > l && cpr % l != 0 && l > cand_l[0]) cand_l[nl++] = l;
   const int xq_octets = xm_octets(xmode) * 64;  // octets one wave stages without a stall
+  const double x_reads = xmode == XM_BF16 ? 0.0 : 1.0;  // LDS activation reads per step
   for (int li = 0; li < nl; ++li) {
     const int L = cand_l[li];
     const int spt = (cpr + L - 1) / L;
@@ -208,7 +211,7 @@ GemvPlan plan_gemv(int cpr, int n_cu, int xmode, int64_t residual_rows, TasksFor
         const int64_t grid = std::min<int64_t>(n_cu, (n_tasks + w - 1) / w);
         const int64_t nw = grid * w;
         const int64_t tpw = (n_tasks + nw - 1) / nw;
-        double cost = (double)tpw * w * spt * rt;
+        double cost = (double)tpw * w * spt * (rt + x_reads);
         if ((int64_t)cpr * 4 > (int64_t)xq_octets * w) cost *= 1.5;  // staging needs extra rounds
         const bool better = cost < best_cost * (1 - 1e-9) ||
                             (cost <= best_cost * (1 + 1e-9) &&

@@ -44,7 +44,7 @@ def plan(cpr: int, xm: str, tasks_for, residual_rows: int = 0, tt: int = 1):
                     continue
                 grid = min(N_CU, -(-n_tasks // w))
                 tpw = -(-n_tasks // (grid * w))
-                cost = tpw * w * spt * rt
+                cost = tpw * w * spt * (rt + (0.0 if xm == "bf16" else 1.0))
                 if cpr * 4 > XM_OCTETS[xm] * 64 * w:
                     cost *= 1.5
                 better = cost < best_cost * (1 - 1e-9) or (
