@@ -1,5 +1,6 @@
-// qgemv_mfma.hip -- the stored-output int4 GEMV family with bf16 activations,
-// for 1..8 activation rows, on gfx950 MFMA (v_mfma_f32_16x16x32_bf16).
+// qgemv_mfma.hip -- small-M int4 products with bf16 activations, 1..8
+// activation rows (stored outputs of up to 8 matrices, or the gate/up pair
+// with the SwiGLU epilogue), on gfx950 MFMA (v_mfma_f32_16x16x32_bf16).
 //
 // Sources (by page title and passage):
 //   [FFAI #14] thewafflehaus/FFAI pull 14, "feat(everything-bagel): clean
