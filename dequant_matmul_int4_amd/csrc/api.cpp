@@ -587,7 +587,8 @@ qint4_status run_moe(const qint4_matrix *gate, const qint4_matrix *up, const qin
   {
     const int nc = (int)(hidden / 32);
     auto tasks_for = [&](int rpt) { return (int64_t)top_k * ((inter + rpt - 1) / rpt); };
-    const GemvPlan plan = plan_gemv(nc, n_cu, xmode_a, 0, tasks_for);
+    // routing in this launch: 16 floats of LDS hand the ranked ids to every wave
+    const GemvPlan plan = plan_gemv(nc, n_cu, xmode_a, logits ? 16 : 0, tasks_for);
     if (plan.waves == 0)
       return fail(QINT4_ERR_SHAPE, "%s: hidden %lld needs too much LDS", fn, (long long)hidden);
     const int rpt = plan.rt * (64 >> plan.log2_lpr);

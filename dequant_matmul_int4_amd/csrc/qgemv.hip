@@ -738,26 +738,33 @@ __global__ void __launch_bounds__(TT >= 8 ? 512 : 768) qgemv_kernel(const GemvPa
 
   if constexpr (EPI == EPI_SWIGLU) {
     if (p.route) {
-      // rank the logits (every wave the same way); lane k < top_k takes slot
-      // k.  The first wave of the grid writes the ids and weights out for the
-      // down launch and the caller.
-      int sel_i[8];
-      float sel_v[8];
-      if (p.n_experts <= 128) {
-        const float k2[2] = {key[0], key[1]};
-        topk::select<2>(k2, p.n_experts, p.top_k, sel_i, sel_v);
-      } else {
-        topk::select<RK>(key, p.n_experts, p.top_k, sel_i, sel_v);
-      }
-      int id = 0;
+      // the first wave of each workgroup ranks the logits (every workgroup
+      // the same way) and hands the ids to the others through LDS, so the
+      // ranking does not take every wave's SIMD time while the code loads
+      // wait for it; lane k < top_k takes slot k.  The first wave of the grid
+      // also writes the ids and weights out for the down launch and the caller.
+      uint32_t *rid = reinterpret_cast<uint32_t *>(res_lds);  // 8 ids (64 B reserved by the host)
+      if (wave == 0) {
+        int sel_i[8];
+        float sel_v[8];
+        if (p.n_experts <= 128) {
+          const float k2[2] = {key[0], key[1]};
+          topk::select<2>(k2, p.n_experts, p.top_k, sel_i, sel_v);
+        } else {
+          topk::select<RK>(key, p.n_experts, p.top_k, sel_i, sel_v);
+        }
+        int id = 0;
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        if (lane == k) id = sel_i[k];
-      v_ids = (uint32_t)id;
-      if (blockIdx.x == 0 && wave == 0 && lane < p.top_k) {
-        p.ids[lane] = (uint32_t)id;
-        p.wts[lane] = topk::slot_weight(sel_v, p.top_k, lane);
+        for (int k = 0; k < 8; ++k)
+          if (lane == k) id = sel_i[k];
+        if (lane < 8) rid[lane] = (uint32_t)id;
+        if (blockIdx.x == 0 && lane < p.top_k) {
+          p.ids[lane] = (uint32_t)id;
+          p.wts[lane] = topk::slot_weight(sel_v, p.top_k, lane);
+        }
       }
+      lds_barrier();
+      v_ids = lane < 8 ? rid[lane] : 0u;
     }
   }
   start(lc);
