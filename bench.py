@@ -53,20 +53,20 @@ POOL_BYTES = 1 << 30
 # dispatch): FETCH_SIZE read 131,087 KiB -> x2.000; WRITE_SIZE 262,144 KiB -> x1.000.
 # Valid only for the kernel sources they were taken with (SOURCE_HASH); any
 # change to a kernel source makes the figure null until it is measured again.
-TRAFFIC_FETCH_SCALE = 262144.0 / 131086.9
+TRAFFIC_FETCH_SCALE = 262144.0 / 131087.2
 TRAFFIC_WRITE_SCALE = 1.0
-TRAFFIC_SOURCE_HASH = "1c1faad6357b438f"
+TRAFFIC_SOURCE_HASH = "453a4df9fa0418eb"
 TRAFFIC_KIB = {  # workload: (FETCH_SIZE KiB, WRITE_SIZE KiB) per step, unscaled
-    "qkv_multi_t1": (7002.1, 16.0),
-    "rms_qkv_multi_t1": (7055.6, 16.0),
-    "dense_ffn_t1": (74557.0, 124.8),
-    "moe_top8_t1": (10847.8, 32.1),
-    "prefill_gemm_T32": (36085.0, 7616.0),
-    "prefill_gemm_T256": (54165.3, 8704.0),
-    "prefill_gemm_T1024": (219124.5, 34816.0),
-    "prefill_gemm_T4096": (512641.3, 139854.3),
-    "moe_prefill_top8_T256": (189428.8, 23585.6),
-    "quantize_17408x5120_f32_g64": (174106.6, 48960.0),
+    "qkv_multi_t1": (7004.1, 16.0),
+    "rms_qkv_multi_t1": (7056.7, 16.0),
+    "dense_ffn_t1": (74536.3, 127.4),
+    "moe_top8_t1": (10844.3, 32.1),
+    "prefill_gemm_T32": (36086.0, 7616.0),
+    "prefill_gemm_T256": (54164.6, 8704.0),
+    "prefill_gemm_T1024": (219157.1, 34816.0),
+    "prefill_gemm_T4096": (512334.2, 139694.0),
+    "moe_prefill_top8_T256": (188023.1, 23585.5),
+    "quantize_17408x5120_f32_g64": (174106.0, 48960.0),
 }
 
 
