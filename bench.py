@@ -7,12 +7,22 @@ One "step" is one pass of the workload's hot path over one token (T=1 decode
 workloads) or one T-row block (prefill).  Inputs live in HBM before timing
 starts.  Each step uses the next copy of a rotating pool of distinct weight
 sets whose total exceeds 1 GiB, so every step streams its weights from HBM
-rather than from the 256 MB last-level cache.  The steps are captured once in
-a HIP graph and replayed: at a few microseconds per kernel, host-side launch
-cost would otherwise decide the rate.  Timing is HIP events around the replay
-on the replay stream, bracketed by device synchronisation.
+rather than from the 256 MB last-level cache.  The W warm-up steps and the K
+timed steps are captured as two HIP graphs (at a few microseconds per kernel,
+host-side launch cost would otherwise decide the rate).  One repetition is:
+device synchronisation, the warm-up graph, an event, the K-step graph, an
+event, device synchronisation -- so the timed region holds exactly the K steps
+and the warm-up keeps the GPU busy while the timed graph is submitted.  The
+line reports the median over 5 repetitions.
 
-Workloads (default: qkv):
+Each kernel launch of a step is also timed on its own (K launches of it in a
+graph, same repetitions): ``roofline`` is the dominant kernel's algorithmic
+bytes (or flops) per launch over its median launch duration.  Next to it, the
+same run measures a stream-read ceiling (a plain read kernel over an equal
+number of bytes, from a 1 GiB rotating pool) and, for the prefill GEMM,
+torch's bf16 matmul of the same shape.
+
+Workloads (default: dense):
   single   1024x1024 g64 GEMV, fp32 scales/biases, fp32 x and y
   qkv      q/k/v projections of one bf16 4096-vector (4096/1024/1024 rows), one launch
   rmsqkv   the same launch with the RMSNorm of the input fused in front
@@ -27,8 +37,8 @@ Workloads (default: qkv):
   quant    the offline quantiser: 17408x5120 float32 -> g64 codes, bf16 scales/biases
 
 Prints one JSON line.  ``value`` is weight GB/s for the decode workloads and
-TFLOP/s for prefill.  ``roofline`` describes the dominant kernel, ``cpu_baseline``
-the fp64 CPU oracle timed on a bounded sample of the same workload.
+TFLOP/s for prefill.  ``cpu_baseline`` is the fp64 CPU oracle timed on a
+bounded sample of the same workload, on one core and on all cores.
 """
 from __future__ import annotations
 
@@ -51,38 +61,26 @@ POOL_BYTES = 1 << 30
 # with WRITE_SIZE, KiB per dispatch, summed over the step's library kernels).
 # Scale factors from the copy workload (256 MiB read + 256 MiB written per
 # dispatch): FETCH_SIZE read 131,087 KiB -> x2.000; WRITE_SIZE 262,144 KiB -> x1.000.
-# Valid only for the kernel sources they were taken with (SOURCE_HASH); any
-# change to a kernel source makes the figure null until it is measured again.
+# Each figure is valid only for the sources it was taken with: `hash` covers the
+# listed kernel sources (comments and whitespace excluded), and any change to
+# them makes the figure null until it is measured again.
 TRAFFIC_FETCH_SCALE = 262144.0 / 131087.2
 TRAFFIC_WRITE_SCALE = 1.0
-TRAFFIC_SOURCE_HASH = "453a4df9fa0418eb"
-TRAFFIC_KIB = {  # workload: (FETCH_SIZE KiB, WRITE_SIZE KiB) per step, unscaled
-    "qkv_multi_t1": (7004.1, 16.0),
-    "rms_qkv_multi_t1": (7056.7, 16.0),
-    "dense_ffn_t1": (74536.3, 127.4),
-    "moe_top8_t1": (10844.3, 32.1),
-    "prefill_gemm_T32": (36086.0, 7616.0),
-    "prefill_gemm_T256": (54164.6, 8704.0),
-    "prefill_gemm_T1024": (219157.1, 34816.0),
-    "prefill_gemm_T4096": (512334.2, 139694.0),
-    "moe_prefill_top8_T256": (188023.1, 23585.5),
-    "quantize_17408x5120_f32_g64": (174106.0, 48960.0),
+GEMV_SRC = ("kernels.h", "api.cpp", "qgemv.hip", "topk_wave.h")
+TRAFFIC = {  # workload: (sources, source hash, FETCH_SIZE KiB, WRITE_SIZE KiB) per step, unscaled
 }
 
 
-def kernel_source_hash() -> str:
-    """Hash of the kernel sources' code: line comments and whitespace do not count, so an edit
-    that only touches comments keeps the measured traffic figures valid."""
-    import glob
+def kernel_source_hash(files) -> str:
+    """Hash of the listed kernel sources' code: line comments and whitespace do not count,
+    so an edit that only touches comments keeps the measured traffic figures valid."""
     import hashlib
     import re
     csrc = os.path.join(ROOT, "dequant_matmul_int4_amd", "csrc")
-    files = sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h")) +
-                   glob.glob(os.path.join(csrc, "*.cpp")))
     h = hashlib.sha256()
-    for f in files:
-        h.update(os.path.basename(f).encode())
-        with open(f, encoding="utf-8") as fh:
+    for name in sorted(files):
+        h.update(name.encode())
+        with open(os.path.join(csrc, name), encoding="utf-8") as fh:
             code = re.sub(r"//[^\n]*", "", fh.read())
         h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
@@ -90,24 +88,26 @@ def kernel_source_hash() -> str:
 
 def traffic_bytes(workload_name: str):
     """Measured HBM bytes per step, or None (not measured, or kernels changed since)."""
-    t = TRAFFIC_KIB.get(workload_name)
-    if t is None or kernel_source_hash() != TRAFFIC_SOURCE_HASH:
+    t = TRAFFIC.get(workload_name)
+    if t is None or kernel_source_hash(t[0]) != t[1]:
         return None
-    return (t[0] * TRAFFIC_FETCH_SCALE + t[1] * TRAFFIC_WRITE_SCALE) * 1024.0
+    return (t[2] * TRAFFIC_FETCH_SCALE + t[3] * TRAFFIC_WRITE_SCALE) * 1024.0
+
+
 METRIC = "weight GB/s and % of HBM peak for T=1 int4 GEMV; tokens/s-equivalent"
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default="qkv",
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="dense",
                     choices=["single", "qkv", "rmsqkv", "smallm", "dense", "moe", "moeprefill", "prefill",
                              "quant", "copy"])
     ap.add_argument("--T", type=int, default=None,
                     help="prefill rows (default 256) or small-M tokens (default 4)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+    ap.add_argument("--cpu-seconds", type=float, default=16.0,
                     help="wall-time budget of the CPU oracle sample (0 disables)")
     ap.add_argument("--router", choices=("fused", "gpu", "pre-drawn"), default="fused",
                     help="moe: route each token inside the gate/up launch (default), with the "
@@ -115,6 +115,8 @@ def parse():
     ap.add_argument("--no-graph", action="store_true",
                     help="launch the steps one by one instead of replaying a HIP graph "
                          "(for counter collection; the timing then includes launch gaps)")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the stream-read (and bf16 GEMM) ceilings measured next to the workload")
     ap.add_argument("--layers", type=int, default=64,
                     help="dense layers per token assumed for tokens/s-equivalent")
     return ap.parse_args()
@@ -132,6 +134,13 @@ class Workload:
     def weight_bytes(self) -> int: ...
     def algo_bytes(self) -> int: ...  # bytes the step's kernels must move (weights + activations)
     def step(self, i: int) -> None: ...
+
+    def parts(self):
+        """The step's library calls, each timed on its own: (kernel label, fn(i), algorithmic
+        bytes per call, algorithmic flops per call, kernel launches per call).  The first
+        is the dominant one, the kernel ``roofline`` describes."""
+        return [(self.dominant, self.step, self.algo_bytes(), float(getattr(self, "flops", 0.0)),
+                 self.launches_per_step)]
 
 
 def _mat(q, synth, n_out, k_in, sb, seed, n_experts=1, g=64):
@@ -330,10 +339,23 @@ class Dense(Workload):
     def algo_bytes(self):
         return self.wb + 5120 * 2 + 17408 * 4 * 2 + 5120 * 2
 
-    def step(self, i):
-        g, u, d = self.pool[i % self.R]
+    def gate_up(self, i):
+        g, u, _ = self.pool[i % self.R]
         self.q.qgemv_int4_multi([g, u], self.x, [self.h], epilogue=self.q.EPI_SWIGLU_PAIR)
-        self.q.qgemv_int4(d, self.h, self.y)
+
+    def down(self, i):
+        self.q.qgemv_int4(self.pool[i % self.R][2], self.h, self.y)
+
+    def step(self, i):
+        self.gate_up(i)
+        self.down(i)
+
+    def parts(self):
+        g, u, d = self.pool[0]
+        return [("qgemv_kernel EPI_SWIGLU (gate/up pair, bf16 x, fp32 h)", self.gate_up,
+                 g.weight_bytes + u.weight_bytes + 5120 * 2 + 17408 * 4, 0.0, 1),
+                ("qgemv_kernel EPI_STORE (down, fp32 h, bf16 y)", self.down,
+                 d.weight_bytes + 17408 * 4 + 5120 * 2, 0.0, 1)]
 
 
 class MoE(Workload):
@@ -501,97 +523,90 @@ class Prefill(Workload):
 # CPU baseline: the fp64 oracle on a bounded sample of the same workload
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(workload: str, budget_s: float, T: int):
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_sample(workload: str, T: int, threads: int):
+    """(fn, amount per call, unit, description, fixed thread count or None) for the oracle on
+    a bounded sample of the workload: amount is weight bytes (GB/s) or flops (TFLOP/s)."""
     import numpy as np
 
     import oracle
     import synth
 
-    threads = max(1, min(oracle.max_threads(), os.cpu_count() or 1))
     if workload == "single":
         d = synth.single_gemv()
-        wb = d["w"].weight_bytes
-        fn = lambda: oracle.gemv(d["w"], d["x"], "f32", threads=threads)
-        sample = "full 1024x1024 GEMV (seed 0), repeated"
-    elif workload == "qkv":
-        d = synth.qkv_multi()
-        wb = sum(w.weight_bytes for w in d["ws"])
-        fn = lambda: oracle.multi(d["ws"], d["x"], "bf16", threads=threads)
-        sample = "full q/k/v set (seed 1), repeated"
-    elif workload == "rmsqkv":
-        d = synth.rms_qkv()
-        wb = sum(w.weight_bytes for w in d["ws"])
-        fn = lambda: oracle.rms_norm_multi(d["ws"], d["x"], "bf16", d["gamma"], d["eps"],
-                                           threads=threads)
-        sample = "full RMSNorm + q/k/v set (seed 5), repeated"
-    elif workload == "smallm":
-        d = synth.qkv_multi()
-        wb = sum(w.weight_bytes for w in d["ws"])
-        xs = [synth.draw_activation(np.random.default_rng(100 + t), (4096,), "bf16") for t in range(T)]
-        fn = lambda: [oracle.multi(d["ws"], x, "bf16", threads=threads) for x in xs]
-        sample = "full q/k/v set (seed 1) for %d tokens, repeated" % T
-    elif workload == "dense":
+        return (lambda: oracle.gemv(d["w"], d["x"], "f32", threads=threads), d["w"].weight_bytes,
+                "GB/s", "full 1024x1024 GEMV (seed 0), repeated", None)
+    if workload in ("qkv", "rmsqkv", "smallm"):
+        if workload == "rmsqkv":
+            d = synth.rms_qkv()
+            fn = lambda: oracle.rms_norm_multi(d["ws"], d["x"], "bf16", d["gamma"], d["eps"],
+                                               threads=threads)
+            desc = "full RMSNorm + q/k/v set (seed 5), repeated"
+        elif workload == "qkv":
+            d = synth.qkv_multi()
+            fn = lambda: oracle.multi(d["ws"], d["x"], "bf16", threads=threads)
+            desc = "full q/k/v set (seed 1), repeated"
+        else:
+            d = synth.qkv_multi()
+            xs = [synth.draw_activation(np.random.default_rng(100 + t), (4096,), "bf16")
+                  for t in range(T)]
+            fn = lambda: [oracle.multi(d["ws"], x, "bf16", threads=threads) for x in xs]
+            desc = "full q/k/v set (seed 1) for %d tokens, repeated" % T
+        return fn, sum(w.weight_bytes for w in d["ws"]), "GB/s", desc, None
+    if workload == "dense":
         d = synth.dense_layer()
-        wb = sum(d[k].weight_bytes for k in ("gate", "up", "down"))
-        fn = lambda: oracle.dense_ffn(d["gate"], d["up"], d["down"], d["x"], "bf16", threads=threads)
-        sample = "full dense layer (seed 2), repeated"
-    elif workload == "moe":
+        return (lambda: oracle.dense_ffn(d["gate"], d["up"], d["down"], d["x"], "bf16", threads=threads),
+                sum(d[k].weight_bytes for k in ("gate", "up", "down")), "GB/s",
+                "full dense layer (seed 2): gate/up + SwiGLU + down, repeated", None)
+    if workload == "moe":
         d = synth.moe_layer()
         per = d["gate"].weight_bytes // d["gate"].n_experts
-        wb = 3 * 8 * per
 
         def fn():
             ids, wts = oracle.router_topk(d["logits"][0], 8)
             return oracle.moe(d["gate"], d["up"], d["down"], d["x"][0], ids, wts.astype(np.float32),
                               d["residual"][0], "bf16", threads=threads)
-        sample = "one token of the 128-expert layer (seed 3): router + top-8 experts, repeated"
-    elif workload == "moeprefill":
+        return fn, 3 * 8 * per, "GB/s", ("one token of the 128-expert layer (seed 3): router + top-8 "
+                                         "experts, repeated"), None
+    if workload == "moeprefill":
         d = synth.moe_prefill_layer(T=max(T, 2))
         ntok = 2
         pairs = [oracle.router_topk(d["logits"][t].astype(np.float64), 8) for t in range(ntok)]
         ids = np.array([p_[0] for p_ in pairs])
         wts = np.array([p_[1] for p_ in pairs], dtype=np.float32)
-        fn = lambda: oracle.moe_prefill(d["gate"], d["up"], d["down"], d["x"][:ntok], ids, wts,
-                                        d["residual"][:ntok], threads=threads)
-        flops_per_call = 6.0 * ntok * 8 * 768 * 2048
-        sample = "%d tokens of the 128-expert layer (seed 6) per call: router + 8 experts each" % ntok
-        t0 = time.perf_counter()
-        n = 0
-        while True:
-            fn()
-            n += 1
-            if time.perf_counter() - t0 >= budget_s:
-                break
-        el = time.perf_counter() - t0
-        return {"value": flops_per_call * n / el / 1e12, "unit": "TFLOP/s", "cores": threads,
-                "kind": "oracle", "sample": sample + "; %d calls in %.1f s" % (n, el)}
-    elif workload == "quant":
+        return (lambda: oracle.moe_prefill(d["gate"], d["up"], d["down"], d["x"][:ntok], ids, wts,
+                                           d["residual"][:ntok], threads=threads),
+                6.0 * ntok * 8 * 768 * 2048, "TFLOP/s",
+                "%d tokens of the 128-expert layer (seed 6) per call: router + 8 experts each" % ntok,
+                None)
+    if workload == "quant":
         rng = np.random.default_rng(11)
         rows = 512
         W = synth.draw_float_weights(rng, (rows, 5120), "f32")
-        wb = W.nbytes
-        fn = lambda: oracle.quantize(W, "f32", 64, "bf16")
-        sample = "%d x 5120 rows of float32 weights per call (numpy float32, one thread)" % rows
-        threads = 1
-    else:
-        d = synth.prefill_gemm(T=T)
-        rows = 64
-        rng = np.random.default_rng(0)
-        t_idx = np.repeat(np.arange(min(T, 4)), rows // min(T, 4))
-        o_idx = rng.integers(0, d["w"].n_out, t_idx.size)
-        fn = lambda: oracle.gemm_entries(d["w"], d["X"], t_idx, o_idx, "bf16", threads=threads)
-        flops_per_call = 2.0 * t_idx.size * 5120
-        sample = "%d sampled output entries of the T=%d GEMM per call" % (t_idx.size, T)
-        t0 = time.perf_counter()
-        n = 0
-        while True:
-            fn()
-            n += 1
-            if time.perf_counter() - t0 >= budget_s:
-                break
-        el = time.perf_counter() - t0
-        return {"value": flops_per_call * n / el / 1e12, "unit": "TFLOP/s", "cores": threads,
-                "kind": "oracle", "sample": sample + "; %d calls in %.1f s" % (n, el)}
+        return (lambda: oracle.quantize(W, "f32", 64, "bf16"), W.nbytes, "GB/s",
+                "%d x 5120 rows of float32 weights per call (numpy float32, one thread)" % rows, 1)
+    d = synth.prefill_gemm(T=T)
+    rows = 64
+    rng = np.random.default_rng(0)
+    t_idx = np.repeat(np.arange(min(T, 4)), rows // min(T, 4))
+    o_idx = rng.integers(0, d["w"].n_out, t_idx.size)
+    return (lambda: oracle.gemm_entries(d["w"], d["X"], t_idx, o_idx, "bf16", threads=threads),
+            2.0 * t_idx.size * 5120, "TFLOP/s",
+            "%d sampled output entries of the T=%d GEMM per call" % (t_idx.size, T), None)
+
+
+def _rate(fn, amount, unit, budget_s):
+    fn()  # first call outside the clock (library load, caches)
     t0 = time.perf_counter()
     n = 0
     while True:
@@ -600,11 +615,132 @@ def cpu_baseline(workload: str, budget_s: float, T: int):
         if time.perf_counter() - t0 >= budget_s:
             break
     el = time.perf_counter() - t0
-    return {"value": wb * n / el / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": sample + "; %d calls in %.1f s" % (n, el)}
+    scale = 1e12 if unit == "TFLOP/s" else 1e9
+    return amount * n / el / scale, n, el
+
+
+def cpu_baseline(workload: str, budget_s: float, T: int):
+    """The fp64 oracle as it stands on the host: all cores (the reported value), then one
+    core, each for about budget_s / 2 seconds."""
+    import oracle
+
+    all_threads = max(1, min(oracle.max_threads(), os.cpu_count() or 1))
+    fn, amount, unit, desc, fixed = _oracle_sample(workload, T, all_threads)
+    threads = fixed or all_threads
+    v, n, el = _rate(fn, amount, unit, budget_s / 2)
+    out = {"value": v, "unit": unit, "cores": threads, "kind": "oracle",
+           "sample": desc + "; %d calls in %.1f s on %d thread(s)" % (n, el, threads),
+           "cpu_model": _cpu_model(), "host_cores": os.cpu_count()}
+    if threads > 1:
+        fn1, amount1, _, _, _ = _oracle_sample(workload, T, 1)
+        v1, n1, el1 = _rate(fn1, amount1, unit, budget_s / 2)
+        out["value_1core"] = v1
+        out["sample_1core"] = "%d calls in %.1f s on 1 thread" % (n1, el1)
+    else:
+        out["value_1core"] = v
+    return out
 
 
 # ---------------------------------------------------------------------------
+
+REPS = 5
+
+
+class Timer:
+    """Median-of-REPS graph timing of a per-step callable on one stream (see the module
+    docstring for the shape of one repetition)."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+
+    def ms_per_step(self, fn, K, W, first=0, no_graph=False):
+        torch, stream = self.torch, self.stream
+        times = []
+        if no_graph:  # launches one by one (for counter collection)
+            for _ in range(REPS):
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                with torch.cuda.stream(stream):
+                    for i in range(W):
+                        fn(first + i)
+                    e0.record(stream)
+                    for i in range(K):
+                        fn(first + W + i)
+                    e1.record(stream)
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1) / K)
+        else:
+            g_warm, g_main = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_warm, stream=stream):
+                for i in range(W):
+                    fn(first + i)
+            with torch.cuda.graph(g_main, stream=stream):
+                for i in range(K):
+                    fn(first + W + i)
+            torch.cuda.synchronize()
+            for _ in range(REPS):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                with torch.cuda.stream(stream):
+                    if W:
+                        g_warm.replay()
+                    e0.record(stream)
+                    g_main.replay()
+                    e1.record(stream)
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1) / K)
+            del g_warm, g_main
+        s = sorted(times)
+        return s[len(s) // 2], times
+
+
+def stream_ceiling(torch, timer, nbytes, K, W):
+    """Median time of a plain 128-bit read of nbytes (next buffer of a >= 1 GiB pool per
+    launch), best over a few grid sizes; None when the calibration library is missing."""
+    import ctypes
+    path = os.path.join(ROOT, "dequant_matmul_int4_amd", "libqint4_calib.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.qint4_calib_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                            ctypes.c_int, ctypes.c_void_p]
+    nb = (nbytes + 15) // 16 * 16
+    R = max(2, math.ceil(POOL_BYTES / nb))
+    pool = [torch.empty(nb, dtype=torch.uint8, device="cuda").random_(0, 256) for _ in range(R)]
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    best = None
+    for grid in (1024, 2048, 4096, 8192):
+        def fn(i, grid=grid):
+            rc = lib.qint4_calib_stream_read(pool[i % R].data_ptr(), nb, sink.data_ptr(), grid,
+                                             torch.cuda.current_stream().cuda_stream)
+            if rc != 0:
+                raise RuntimeError("stream read launch failed: %d" % rc)
+        ms, _ = timer.ms_per_step(fn, K, W)
+        if best is None or ms < best[0]:
+            best = (ms, grid)
+    del pool
+    ms, grid = best
+    return {"bytes": nb, "us": ms * 1e3, "GBps": nb / (ms * 1e-3) / 1e9,
+            "frac_of_peak": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "grid": grid,
+            "kernel": "stream_read_kernel (libqint4_calib.so, 128-bit loads)"}
+
+
+def gemm_ceiling(torch, timer, T, K_, W_steps):
+    """torch's bf16 matmul (hipBLASLt) of the same shape, T x 5120 @ 5120 x 17408, over 6
+    rotating weight copies: the measured dense bf16 GEMM rate on this GPU."""
+    a = torch.randn(T, 5120, device="cuda").to(torch.bfloat16)
+    ws = [torch.randn(17408, 5120, device="cuda").to(torch.bfloat16) for _ in range(6)]
+    y = torch.empty(T, 17408, device="cuda", dtype=torch.bfloat16)
+
+    def fn(i):
+        torch.matmul(a, ws[i % 6].t(), out=y)
+    ms, _ = timer.ms_per_step(fn, K_, W_steps)
+    del ws
+    return {"us": ms * 1e3, "TFLOPs": 2.0 * T * 5120 * 17408 / (ms * 1e-3) / 1e12,
+            "kernel": "torch.matmul bf16 (hipBLASLt)"}
+
 
 def main():
     args = parse()
@@ -652,86 +788,44 @@ def main():
 
     K, W = args.steps, args.warmup
     stream = torch.cuda.Stream()
+    timer = Timer(torch, stream)
     # eager warm-up call (caches device properties, sets kernel attributes)
     with torch.cuda.stream(stream):
         wl.step(0)
     stream.synchronize()
 
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    if args.no_graph:
-        with torch.cuda.stream(stream):
-            for i in range(W):
-                wl.step(i)
-        torch.cuda.synchronize()
-        with torch.cuda.stream(stream):
-            ev0.record(stream)
-            for i in range(K):
-                wl.step(W + i)
-            ev1.record(stream)
-        torch.cuda.synchronize()
-    else:
-        g_warm = torch.cuda.CUDAGraph()
-        g_main = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_warm, stream=stream):
-            for i in range(W):
-                wl.step(i)
-        with torch.cuda.graph(g_main, stream=stream):
-            for i in range(K):
-                wl.step(W + i)
-        torch.cuda.synchronize()
-
-        with torch.cuda.stream(stream):
-            g_warm.replay()
-        torch.cuda.synchronize()
-
-        torch.cuda.synchronize()
-        with torch.cuda.stream(stream):
-            ev0.record(stream)
-            g_main.replay()
-            ev1.record(stream)
-        torch.cuda.synchronize()
-    ms_total = ev0.elapsed_time(ev1)
-    ms_step = ms_total / K
-    print("# timed %d steps in %.3f ms" % (K, ms_total), file=sys.stderr, flush=True)
+    ms_step, reps = timer.ms_per_step(wl.step, K, W, no_graph=args.no_graph)
+    print("# %d steps x %d repetitions: %s ms/step" % (K, REPS, ", ".join("%.5f" % t for t in reps)),
+          file=sys.stderr, flush=True)
 
     out = {"metric": METRIC, "n_gpus": 1, "steps": K, "warmup": W,
            "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic (seeded, device-generated pool)",
-           "config": wl.config}
-    if isinstance(wl, MoEPrefill):
-        tflops = wl.flops / (ms_step * 1e-3) / 1e12
-        gbs = wl.algo_bytes() / (ms_step * 1e-3) / 1e9
-        out.update({"value": tflops, "unit": "TFLOP/s", "tokens_per_s": wl.T * 1e3 / ms_step,
-                    "weight_GBps": wl.weight_bytes() / (ms_step * 1e-3) / 1e9})
-        # the bound is whichever ideal time is longer: the touched weights at HBM peak or
-        # the products at dense bf16 MFMA peak
-        t_hbm = wl.algo_bytes() / (HBM_PEAK_GBS * 1e9)
-        t_mfma = wl.flops / (BF16_MFMA_PEAK_TFLOPS * 1e12)
-        if t_mfma >= t_hbm:
-            out["roofline"] = {"bound": "mfma", "achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS,
-                               "unit": "TFLOP/s", "frac": tflops / BF16_MFMA_PEAK_TFLOPS,
-                               "traffic": traffic_bytes(wl.name), "kernel": wl.dominant,
-                               "launches_per_step": wl.launches_per_step}
+           "config": wl.config, "repetitions": REPS, "ms_per_step_reps": reps}
+
+    # each library call of the step on its own: K calls in a graph, same repetitions
+    parts = []
+    for label, fn, nbytes, flops, launches in wl.parts():
+        if len(wl.parts()) == 1:
+            ms = ms_step
         else:
-            out["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                               "frac": gbs / HBM_PEAK_GBS, "traffic": traffic_bytes(wl.name), "kernel": wl.dominant,
-                               "launches_per_step": wl.launches_per_step}
-    elif isinstance(wl, Prefill):
+            ms, _ = timer.ms_per_step(fn, K, W, no_graph=args.no_graph)
+        parts.append({"kernel": label, "us": ms * 1e3, "bytes": nbytes, "flops": flops,
+                      "GBps": nbytes / (ms * 1e-3) / 1e9,
+                      "TFLOPs": flops / (ms * 1e-3) / 1e12 if flops else None,
+                      "launches": launches})
+    if len(parts) > 1:
+        out["kernels"] = parts
+    dom = parts[0]
+
+    gemm_like = isinstance(wl, (Prefill, MoEPrefill))
+    if gemm_like:
         tflops = wl.flops / (ms_step * 1e-3) / 1e12
-        gbs = wl.algo_bytes() / (ms_step * 1e-3) / 1e9
         out.update({"value": tflops, "unit": "TFLOP/s",
                     "weight_GBps": wl.weight_bytes() / (ms_step * 1e-3) / 1e9,
                     "mfma_util": tflops / BF16_MFMA_PEAK_TFLOPS})
-        # bound: the longer of the ideal times (bytes at HBM peak, products at MFMA peak)
-        if wl.flops / (BF16_MFMA_PEAK_TFLOPS * 1e12) >= wl.algo_bytes() / (HBM_PEAK_GBS * 1e9):
-            out["roofline"] = {"bound": "mfma", "achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS,
-                               "unit": "TFLOP/s", "frac": tflops / BF16_MFMA_PEAK_TFLOPS}
-        else:
-            out["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                               "frac": gbs / HBM_PEAK_GBS}
-        out["roofline"].update({"traffic": traffic_bytes(wl.name), "kernel": wl.dominant,
-                                "launches_per_step": wl.launches_per_step})
+        if isinstance(wl, MoEPrefill):
+            out["tokens_per_s"] = wl.T * 1e3 / ms_step
     else:
         gbs = wl.weight_bytes() / (ms_step * 1e-3) / 1e9
         out.update({"value": gbs, "unit": "GB/s", "pct_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS,
@@ -739,17 +833,48 @@ def main():
         if isinstance(wl, Dense):
             out["tokens_per_s_equiv"] = 1e3 / (ms_step * args.layers)
             out["tokens_per_s_equiv_layers"] = args.layers
+            out["tokens_per_s_equiv_note"] = "assumed layer count (the sources give none for this shape)"
         if isinstance(wl, MoE):
             out["tokens_per_s_equiv"] = 1e3 / (ms_step * 40)
             out["tokens_per_s_equiv_layers"] = 40
         if isinstance(wl, SmallM):
             out["tokens_per_call"] = wl.T
-        # per launch of the step's kernels (one launch for single/qkv; for the
-        # two-launch workloads the pair is timed as one unit)
-        ach = wl.algo_bytes() / (ms_step * 1e-3) / 1e9
+
+    # roofline of the dominant kernel: the longer of its ideal times decides the bound
+    t_hbm = dom["bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = dom["flops"] / (BF16_MFMA_PEAK_TFLOPS * 1e12)
+    ms_dom = dom["us"] * 1e-3
+    if t_mfma > t_hbm:
+        ach = dom["flops"] / (ms_dom * 1e-3) / 1e12
+        out["roofline"] = {"bound": "mfma", "achieved": ach, "peak": BF16_MFMA_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": ach / BF16_MFMA_PEAK_TFLOPS}
+    else:
+        ach = dom["bytes"] / (ms_dom * 1e-3) / 1e9
         out["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": ach / HBM_PEAK_GBS, "traffic": traffic_bytes(wl.name), "kernel": wl.dominant,
-                           "launches_per_step": wl.launches_per_step}
+                           "frac": ach / HBM_PEAK_GBS}
+    out["roofline"].update({"traffic": traffic_bytes(wl.name), "kernel": dom["kernel"],
+                            "kernel_us": dom["us"], "launches_per_call": dom["launches"],
+                            "algorithmic_bytes": dom["bytes"],
+                            "algorithmic_flops": dom["flops"] or None})
+
+    # measured ceilings of the same size, same run
+    if not args.no_ceiling and args.workload != "copy":
+        ceil = stream_ceiling(torch, timer, wl.weight_bytes(), K, W)
+        if ceil is not None:
+            out["stream_ceiling"] = ceil
+            if not gemm_like:
+                out["pct_stream_ceiling"] = 100.0 * out["value"] / ceil["GBps"]
+            if out["roofline"]["bound"] == "hbm" and dom["bytes"] != wl.weight_bytes():
+                cd = stream_ceiling(torch, timer, dom["bytes"], K, W)
+                if cd is not None:
+                    out["roofline"]["stream_ceiling_GBps"] = cd["GBps"]
+            elif out["roofline"]["bound"] == "hbm":
+                out["roofline"]["stream_ceiling_GBps"] = ceil["GBps"]
+        if isinstance(wl, Prefill):
+            gc = gemm_ceiling(torch, timer, wl.T, min(K, 50), min(W, 5))
+            out["gemm_ceiling"] = gc
+            out["pct_gemm_ceiling"] = 100.0 * out["value"] / gc["TFLOPs"]
+
     if args.cpu_seconds > 0 and args.workload != "copy":
         out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_seconds, args.T)
     print(json.dumps(out), flush=True)

@@ -19,6 +19,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqint4.so")
+# measurement aid (the stream-read ceiling bench.py reports), not part of the library
+CALIB_LIB = os.path.join(PKG, "libqint4_calib.so")
+CALIB_SOURCES = ["calib_read.hip"]
 BUILD_DIR = os.path.join(PKG, "_build")
 
 SOURCES = ["api.cpp", "qgemv.hip", "qgemv_mfma.hip", "qgemm.hip", "router.hip", "quant.hip", "moe_prefill.hip",
@@ -52,19 +55,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 and link libqint4.so; returns its path."""
-    workers = min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
-    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source for gfx950 and link libqint4.so (and the benchmark's
+    calibration library libqint4_calib.so); returns the path of libqint4.so."""
+    srcs = SOURCES + CALIB_SOURCES
+    workers = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in CALIB_SOURCES], CALIB_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", CALIB_LIB)
     return LIB
 
 

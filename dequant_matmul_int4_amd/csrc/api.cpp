@@ -340,6 +340,11 @@ qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t
   if (T > 1 && (ldx < ws[0].k_in || ldx % 8 != 0))
     return fail(QINT4_ERR_SHAPE, "%s: ldx %lld must be >= k_in %lld and a multiple of 8", fn,
                 (long long)ldx, (long long)ws[0].k_in);
+  // every kernel of this family addresses the activation rows through 32-bit
+  // element strides and byte offsets
+  if (((T - 1) * ldx + ws[0].k_in) * (int64_t)elem_bytes(x_dtype) >= ((int64_t)1 << 31))
+    return fail(QINT4_ERR_SHAPE, "%s: activation rows span 2 GiB or more (ldx %lld)", fn,
+                (long long)ldx);
 
   if (gamma) {
     if (T != 1) return fail(QINT4_ERR_SHAPE, "%s: the RMSNorm prologue takes one row", fn);
@@ -385,8 +390,6 @@ qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t
   // call equals T one-row calls)
   if (batched && !gamma && x_dtype == QINT4_BF16 &&
       gemv_mfma_supported(k_in, ws[0].group_size, swiglu ? 2 : 1)) {
-    if (((T - 1) * ldx + k_in) * 2 >= ((int64_t)1 << 31))
-      return fail(QINT4_ERR_SHAPE, "%s: activation rows span 2 GiB or more", fn);
     GemvParams p;
     std::memset(&p, 0, sizeof(p));
     p.n_mats = n;

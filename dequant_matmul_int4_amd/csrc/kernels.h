@@ -6,6 +6,8 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
+#include <unordered_map>
 
 namespace qint4 {
 
@@ -13,18 +15,28 @@ constexpr int kMaxMats = 8;    // projections per multi call
 constexpr int kMaxTopK = 8;    // experts combined per MoE call
 constexpr int kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
 
-// Lets kernel `kern` use `bytes` of dynamic LDS (more than the default 64 KB)
-// on the current device, once per device: bit d of `done` records device d
-// (devices past 63 set the attribute on every call).  Concurrent first calls
-// both set the same value.
-inline hipError_t lds_opt_in(const void *kern, int bytes, std::atomic<uint64_t> &done) {
+// Lets kernel `kern` use up to `bytes` of dynamic LDS (more than the default
+// 64 KB) on the current device.  The attribute is set once per (kernel,
+// device) pair: a registry keyed by the kernel's address records the devices
+// done (bit d = device d; devices past 63 set the attribute on every call).
+// Concurrent first calls both set the same value.
+inline hipError_t lds_opt_in(const void *kern, int bytes) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
-  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  static std::mutex mu;
+  static std::unordered_map<const void *, uint64_t> done;
+  if (bit) {
+    std::lock_guard<std::mutex> g(mu);
+    auto it = done.find(kern);
+    if (it != done.end() && (it->second & bit)) return hipSuccess;
+  }
   e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+  if (e == hipSuccess && bit) {
+    std::lock_guard<std::mutex> g(mu);
+    done[kern] |= bit;
+  }
   return e;
 }
 

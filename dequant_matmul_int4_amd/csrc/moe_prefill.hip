@@ -511,9 +511,8 @@ hipError_t launch_mg(MoeGemmParams p, hipStream_t stream) {
   const size_t dyn = p.sb_lds ? tab : 0;
   auto kern = moe_gemm_kernel<MODE, BM, BN, WM, WN, PF>;
   // opt in to the LDS left next to the static tiles (once per device)
-  static std::atomic<uint64_t> opted{0};
   if (dyn > 0) {
-    hipError_t e = lds_opt_in(reinterpret_cast<const void *>(kern), (int)(kMaxLds - kStatic), opted);
+    hipError_t e = lds_opt_in(reinterpret_cast<const void *>(kern), (int)(kMaxLds - kStatic));
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(WM * WN * 64), dyn, stream, p);

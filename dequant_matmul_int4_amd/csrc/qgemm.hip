@@ -305,8 +305,7 @@ hipError_t launch_tile(GemmParams p, hipStream_t stream) {
   }
   auto kern = qgemm_kernel<BM, BN, WM, WN, PF, true>;
   // opt in to the LDS left next to the static tiles (once per device)
-  static std::atomic<uint64_t> opted{0};
-  hipError_t e = lds_opt_in(reinterpret_cast<const void *>(kern), (int)(kMaxLds - kStatic), opted);
+  hipError_t e = lds_opt_in(reinterpret_cast<const void *>(kern), (int)(kMaxLds - kStatic));
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(WM * WN * 64), tab, stream, p);
   return hipGetLastError();

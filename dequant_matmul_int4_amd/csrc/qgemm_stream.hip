@@ -398,9 +398,8 @@ template <int MT, int D, int SBT, bool SBL>
 hipError_t launch_cfg(const GemmParams &p, size_t lds, size_t grid, hipStream_t stream) {
   auto kern = qgemm_stream_kernel<MT, D, nbuf_for(MT), SBT, SBL>;
   // opt in to the LDS limit (once per device)
-  static std::atomic<uint64_t> opted{0};
   if (lds > 64 * 1024) {
-    hipError_t e = lds_opt_in(reinterpret_cast<const void *>(kern), kMaxLds, opted);
+    hipError_t e = lds_opt_in(reinterpret_cast<const void *>(kern), kMaxLds);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3((kW + 1) * 64), lds, stream, p);

@@ -938,9 +938,8 @@ hipError_t launch_one(const GemvParams &p, const GemvPlan &plan, hipStream_t str
     }
   }
   // opt in to more than 64 KB of dynamic LDS (once per device)
-  static std::atomic<uint64_t> big_lds{0};
   if (plan.lds_bytes > 64 * 1024) {
-    hipError_t e = lds_opt_in(reinterpret_cast<const void *>(kern), kMaxLds, big_lds);
+    hipError_t e = lds_opt_in(reinterpret_cast<const void *>(kern), kMaxLds);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)plan.grid), dim3(plan.waves * 64), plan.lds_bytes,

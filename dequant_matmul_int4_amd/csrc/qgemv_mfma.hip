@@ -51,10 +51,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-#ifndef QINT4_MFMA_CHUNKS_PER_WAVE
-#define QINT4_MFMA_CHUNKS_PER_WAVE 16
-#endif
-constexpr int kChunksPerWave = QINT4_MFMA_CHUNKS_PER_WAVE;  // 32-code chunks per wave
+constexpr int kChunksPerWave = 16;  // 32-code chunks per wave (8 and 32 measured no faster)
 constexpr int kSteps = kChunksPerWave / 4;                   // 128-k steps per wave
 static_assert(kChunksPerWave % 4 == 0 && kChunksPerWave >= 4, "whole 128-k steps");
 constexpr int kTileRows = 16;
@@ -344,9 +341,8 @@ template <int SBT, int CPG, int TT, int NS>
 hipError_t launch_mfma(const GemvParams &p, int64_t grid, int ks, hipStream_t stream) {
   auto kern = qgemv_mfma_kernel<SBT, CPG, TT, NS>;
   const size_t lds = (size_t)ks * wave_region_bytes(TT, CPG, NS);
-  static std::atomic<uint64_t> big_lds{0};
   if (lds > 64 * 1024) {
-    hipError_t e = lds_opt_in(reinterpret_cast<const void *>(kern), kMaxLds, big_lds);
+    hipError_t e = lds_opt_in(reinterpret_cast<const void *>(kern), kMaxLds);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(ks * 64), lds, stream, p);

@@ -74,6 +74,7 @@ def _load():
                                          ctypes.c_int, P, P, ctypes.c_int]
         lib.orc_gemm.argtypes = [P, P, P, I64, I64, I64, P, I64, ctypes.c_int, P, P,
                                  ctypes.c_int]
+        lib.orc_gemm.restype = ctypes.c_int
         lib.orc_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -402,8 +403,8 @@ def round_bf16(v: np.ndarray) -> np.ndarray:
 def gemm_f64(w, X64: np.ndarray, round_w: bool = True, expert: Optional[int] = None,
              threads: int = 1) -> Tuple[np.ndarray, np.ndarray]:
     """Y[t][o] = sum_k w'[o][k] X64[t][k] and A = sum_k |w' X| for float64 rows X64
-    (w' = bf16(f32(w)) when round_w: the weight dequantised in float32, then rounded to
-    bfloat16); one matrix or expert ``expert`` of a stack."""
+    (w' = the exact weight s q + b rounded once to the nearest bfloat16, ties to even,
+    when round_w); one matrix or expert ``expert`` of a stack."""
     c, s, b = _slab(w, expert)
     c = np.ascontiguousarray(c, dtype=np.uint32)
     sd = np.ascontiguousarray(widen(s, w.sb_dtype))
@@ -414,8 +415,10 @@ def gemm_f64(w, X64: np.ndarray, round_w: bool = True, expert: Optional[int] = N
     T = X64.shape[0]
     Y = np.empty((T, w.n_out), dtype=np.float64)
     A = np.empty((T, w.n_out), dtype=np.float64)
-    _load().orc_gemm(_p(c), _p(sd), _p(bd), w.n_out, w.k_in, w.group_size, _p(X64), T,
-                     int(bool(round_w)), _p(Y), _p(A), int(threads))
+    rc = _load().orc_gemm(_p(c), _p(sd), _p(bd), w.n_out, w.k_in, w.group_size, _p(X64), T,
+                          int(bool(round_w)), _p(Y), _p(A), int(threads))
+    if rc != 0:
+        raise MemoryError("orc_gemm: row buffer allocation failed")
     return Y, A
 
 
@@ -425,8 +428,10 @@ def gemm(w, X: np.ndarray, x_dtype: str = BF16, round_w: bool = True,
 
     Padding T up to a multiple of 32 appends zero rows whose outputs are sliced
     away ([FFAI #9], dequantGemmDynamicM T-padding driver), so the result for
-    the T real rows is this plain product; w' = bf16(f32(w)) when round_w (float32
-    dequantisation, then bfloat16).
+    the T real rows is this plain product.  When round_w, w' is the weight
+    dequantised to bfloat16 before the product ([FFAI #9], the padded dequant GEMM
+    multiplies bf16 weight tiles): the exact s q + b rounded once to the nearest
+    bfloat16, ties to even.
     """
     return gemm_f64(w, widen(X, x_dtype), round_w=round_w, threads=threads)
 
@@ -437,46 +442,56 @@ def moe_prefill(gate, up, down, X: np.ndarray, ids: np.ndarray, wts: np.ndarray,
     """T tokens through the top-K MoE in the prefill form.
 
     [FFAI #9], batched MoE commits: the T * topK (token, slot) rows are fanned
-    into one GEMM per gate / up / down, sorted by expert id, then unpermuted by
-    a scatter-sum.  Sorting and tiling change no row's value, so each token's
-    output is the decode step of moe() computed with the prefill GEMM's weights
-    w' = bf16(f32(w)) (the float32-dequantised weight rounded to bfloat16, as in gemm()):
+    into one GEMM per gate / up / down, grouped by expert id, then unpermuted by
+    a scatter-sum.  Here the rows of each expert go through that expert's
+    prefill GEMMs (gemm(), weights w' = RNE_bf16(s q + b)) in one call each;
+    grouping changes no row's value, so each token's output is the decode step
+    of moe() with the prefill weights:
       h_k = silu(W'_gate[e] x) * (W'_up[e] x),  out = residual + sum_k w_k W'_down[e] h_k,
     e = ids[t][k]; ids outside [0, n_experts) contribute nothing.  X is bf16
     [T][hidden]; residual (or None) is [T][hidden] in res_dtype.
 
     Returns (out [n][hidden], a_out [n][hidden]) for the rows ``tokens``
-    (default: all), a_out bounding the float32 accumulation noise as in moe().
+    (default: all), a_out bounding the float32 accumulation noise as in moe():
+    the down product's own sum |w' h| plus sum |w'| a_h, what the error bound a_h
+    of the float32 intermediate h carries through it.
     """
     X64 = widen(X, BF16)
     T = X64.shape[0]
-    tokens = range(T) if tokens is None else tokens
+    tokens = list(range(T)) if tokens is None else [int(t) for t in tokens]
+    ids = np.asarray(ids)
+    n, top_k, hidden = len(tokens), ids.shape[1], down.n_out
+    D = np.zeros((n, top_k, hidden))
+    AD = np.zeros((n, top_k, hidden))
+    valid = np.zeros((n, top_k), bool)
+    tok_idx = np.repeat(np.arange(n), top_k)          # (token position, slot) rows
+    slot_idx = np.tile(np.arange(top_k), n)
+    expert = ids[np.asarray(tokens, dtype=np.int64)].reshape(-1).astype(np.int64)
+    for e in np.unique(expert):
+        if e < 0 or e >= gate.n_experts:
+            continue
+        sel = np.nonzero(expert == e)[0]
+        Xe = X64[np.asarray(tokens)[tok_idx[sel]]]
+        g, ag = gemm_f64(gate, Xe, expert=int(e), threads=threads)
+        u, au = gemm_f64(up, Xe, expert=int(e), threads=threads)
+        h = swiglu(g, u)
+        a_h = 1.1 * np.abs(u) * ag + np.abs(silu(g)) * au
+        d, ad = gemm_f64(down, h, expert=int(e), threads=threads)
+        _, carried = gemm_f64(down, a_h, expert=int(e), threads=threads)  # sum |w'| a_h
+        D[tok_idx[sel], slot_idx[sel]] = d
+        AD[tok_idx[sel], slot_idx[sel]] = ad + carried
+        valid[tok_idx[sel], slot_idx[sel]] = True
     outs, mags = [], []
-    for t in tokens:
-        x64 = X64[t][None, :]
+    for i, t in enumerate(tokens):
         res64 = None if residual is None else widen(residual[t], res_dtype)
-        ds, scal, ms = [], [], []
-        for e, a_k in zip(ids[t], wts[t]):
-            e = int(e)
-            if e < 0 or e >= gate.n_experts:
-                continue
-            g, ag = gemm_f64(gate, x64, expert=e, threads=threads)
-            u, au = gemm_f64(up, x64, expert=e, threads=threads)
-            g, ag, u, au = g[0], ag[0], u[0], au[0]
-            h = swiglu(g, u)
-            a_h = 1.1 * np.abs(u) * ag + np.abs(silu(g)) * au
-            d, ad = gemm_f64(down, h[None, :], expert=e, threads=threads)
-            # the chained term: what h's error carries through |W'_down|
-            ad = ad[0] + (1.0 + 2.0 ** -8) * gemv_absw(down, a_h, expert=e, threads=threads)
-            ds.append(d[0])
-            scal.append(float(a_k))
-            ms.append(abs(float(a_k)) * ad)
-        if ds:
-            out = combine(res64, scal, ds)
-            a = np.sum(ms, axis=0) + (0.0 if res64 is None else np.abs(res64))
+        ks = [k for k in range(top_k) if valid[i, k]]
+        if ks:
+            out = combine(res64, [float(wts[t][k]) for k in ks], [D[i, k] for k in ks])
+            a = sum(abs(float(wts[t][k])) * AD[i, k] for k in ks)
+            a = a + (0.0 if res64 is None else np.abs(res64))
         else:
-            out = np.zeros(down.n_out) if res64 is None else res64.copy()
-            a = np.zeros(down.n_out) if res64 is None else np.abs(res64)
+            out = np.zeros(hidden) if res64 is None else res64.copy()
+            a = np.zeros(hidden) if res64 is None else np.abs(res64)
         outs.append(out)
         mags.append(a)
     return np.array(outs), np.array(mags)

@@ -32,6 +32,7 @@
  * only changes which thread computes a row, never the arithmetic of a row.
  */
 #include <math.h>
+#include <stdlib.h>
 #include <stdint.h>
 #include <stddef.h>
 
@@ -138,17 +139,16 @@ double orc_round_bf16(double v)
 }
 
 /*
- * The prefill weight w' as the dequant GEMMs use it: s * q + b computed in
- * float32 (one rounding, as a float32 fused multiply-add gives) and then
- * rounded to bfloat16.  The pages fix no precision for the dequantisation;
- * float32 is the kernels' own, so the bf16 value of a weight -- a rounding
- * decision -- is taken in the same precision on both sides.  w is the exact
- * s * q + b (in double it is exact: s, b float32 or bf16, q < 16).  With bf16
- * scales and biases of similar magnitude the float32 step is exact.
+ * The prefill weight w' as the dequant GEMMs define it: the weight
+ * dequantised and rounded to bfloat16 before the product (thewafflehaus/FFAI
+ * pull 9, "Everything Bagel", the T-padded dequant GEMM: weights dequantised
+ * to bf16, then multiplied on the matrix units).  w is the exact s * q + b
+ * (exact in double: s, b float32 or bf16, q < 16), rounded once to the
+ * nearest bfloat16, ties to even.
  */
 static double prefill_weight(double w)
 {
-    return orc_round_bf16((double)(float)w);
+    return orc_round_bf16(w);
 }
 
 /* Elementwise round-to-bfloat16 of an array (in place allowed). */
@@ -188,30 +188,49 @@ void orc_gemm_entries(const uint32_t *codes, const double *scales, const double 
     (void)n_out;
 }
 
-/* Full prefill GEMM over all T x n_out entries (small sizes only). */
-void orc_gemm(const uint32_t *codes, const double *scales, const double *biases,
-              int64_t n_out, int64_t k_in, int64_t group, const double *X, int64_t T,
-              int round_w, double *Y, double *A, int threads)
+/*
+ * Full prefill GEMM over all T x n_out entries.  Each row of w' is
+ * dequantised once into a buffer and then multiplied with every X row; every
+ * entry is still the plain index-order sum over k.  Returns -1 if the row
+ * buffer cannot be allocated, 0 otherwise.
+ */
+int orc_gemm(const uint32_t *codes, const double *scales, const double *biases,
+             int64_t n_out, int64_t k_in, int64_t group, const double *X, int64_t T,
+             int round_w, double *Y, double *A, int threads)
 {
+    int failed = 0;
 #ifdef _OPENMP
     if (threads < 1) threads = 1;
-#pragma omp parallel for num_threads(threads) schedule(static)
+#pragma omp parallel num_threads(threads) reduction(|:failed)
 #endif
-    for (int64_t o = 0; o < n_out; ++o) {
-        for (int64_t t = 0; t < T; ++t) {
-            double acc = 0.0, mag = 0.0;
+    {
+        double *wrow = (double *)malloc((size_t)k_in * sizeof(double));
+        if (!wrow) failed = 1;
+#ifdef _OPENMP
+#pragma omp for schedule(static)
+#endif
+        for (int64_t o = 0; o < n_out; ++o) {
+            if (!wrow) continue;
             for (int64_t k = 0; k < k_in; ++k) {
                 double w = weight_at(codes, scales, biases, o, k, k_in, group);
-                if (round_w) w = prefill_weight(w);
-                double term = w * X[t * k_in + k];
-                acc += term;
-                mag += fabs(term);
+                wrow[k] = round_w ? prefill_weight(w) : w;
             }
-            Y[t * n_out + o] = acc;
-            if (A) A[t * n_out + o] = mag;
+            for (int64_t t = 0; t < T; ++t) {
+                const double *x = X + t * k_in;
+                double acc = 0.0, mag = 0.0;
+                for (int64_t k = 0; k < k_in; ++k) {
+                    double term = wrow[k] * x[k];
+                    acc += term;
+                    mag += fabs(term);
+                }
+                Y[t * n_out + o] = acc;
+                if (A) A[t * n_out + o] = mag;
+            }
         }
+        free(wrow);
     }
     (void)threads;
+    return failed ? -1 : 0;
 }
 
 int orc_max_threads(void)

@@ -22,6 +22,7 @@ A = 0x7F0000000000  # fake, 256-byte aligned device-looking addresses
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"^\s*#.*$", "", text, flags=re.M)  # preprocessor lines (macros)
     return sorted(set(re.findall(r"\b([A-Za-z_0-9]+)\s*\(", text)) - {"if", "sizeof"})
 
 
@@ -158,6 +159,10 @@ def test_smallm_validation(lib):
     assert _smallm(lib, _m(), ldx=260) == 2                    # ldx not a multiple of 8
     assert _smallm(lib, _m(), y=A + 0x300000 + 2 * 512) == 5   # y overlaps row 2 of x
     assert _smallm(lib, _m(), n=0) == 2
+    # rows more than 2 GiB apart: rejected before any path is chosen (k_in 17408 takes the
+    # GEMV form, 4096 the MFMA form)
+    for k in (17408, 4096):
+        assert _smallm(lib, _m(k_in=k), T=2, ldx=1 << 30) == 2 and "2 GiB" in _err(lib)
 
 
 def _rms(lib, m, n=1, x=A + 0x300000, gamma=A + 0x310000, eps=1e-6, y=A + 0x400000, xdt=1,

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import synth
-from tests.gpu_common import check_bf16, dev_matrix, lib, require_gpu, to_np64
+from tests.gpu_common import check_bf16, check_f32, dev_matrix, lib, require_gpu, to_np64
 
 pytestmark = pytest.mark.gpu
 
@@ -66,8 +66,9 @@ def test_gemv_constant_codes(code, x_dt, sbd):
     lib().qgemv_int4(dev_matrix(w), synth.to_torch(x, x_dt), y)
     torch.cuda.synchronize()
     ref, A = _closed(w, _x64(x, x_dt)[None, :], code)
-    # float32 accumulation bound (the closed form is exact in float64)
-    assert np.all(np.abs(to_np64(y) - ref[0]) <= 2.0 ** -16 * A[0] + 1e-30)
+    # relative L2 and the per-element float32 accumulation bound (the closed form is
+    # exact in float64)
+    check_f32(to_np64(y), ref[0], "constant codes %d %s/%s" % (code, x_dt, sbd), a_ref=A[0])
 
 
 @pytest.mark.parametrize("code", [0, 15])
@@ -89,15 +90,17 @@ def test_gemm_constant_codes(code, T, ws):
     else:
         q.qgemm_int4_padT(dev_matrix(w), synth.to_torch(X, "bf16"), y)
     torch.cuda.synchronize()
-    # the bf16 weight of each group, float32 FMA then round to nearest even
-    s32 = _sb64(w, "scales").astype(np.float32)
-    b32 = _sb64(w, "biases").astype(np.float32)
-    wf = (np.float32(code) * s32 + b32).astype(np.float32)    # exact for bf16 s, b, small code
+    # the bf16 weight of each group: the exact code * s + b rounded once to nearest
+    # even; for bf16 s, b and a small code the product is exact in float32, so
+    # torch's float32 -> bf16 cast rounds the exact value
+    w_exact = code * _sb64(w, "scales") + _sb64(w, "biases")
+    wf = w_exact.astype(np.float32)
+    assert np.array_equal(wf.astype(np.float64), w_exact)
     wb = torch.tensor(wf).to(torch.bfloat16).float().numpy().astype(np.float64)
     Xg = _x64(X, "bf16").reshape(T, -1, 64).sum(axis=2)
     ref = Xg @ wb.T
     A = np.abs(Xg) @ np.abs(wb).T
-    assert np.all(np.abs(to_np64(y) - ref) <= 2.0 ** -16 * A + 1e-30)
+    check_f32(to_np64(y), ref, "gemm constant codes %d T=%d" % (code, T), a_ref=A)
 
 
 def test_moe_scalar_fma_chain_is_linear_in_slot_weights():

@@ -5,7 +5,7 @@ import torch
 
 import oracle
 import synth
-from tests.gpu_common import (check, dev_matrix, lib, nan_like, oracle_threads, require_gpu,
+from tests.gpu_common import (check, check_f32, dev_matrix, lib, nan_like, oracle_threads, require_gpu,
                               to_np64)
 
 pytestmark = pytest.mark.gpu
@@ -139,7 +139,7 @@ def test_swiglu_pair_small(h_dt):
     if h_dt == "f32":
         # h is a float32 SwiGLU of float32 sums: bound by the propagated accumulation noise
         got = to_np64(h)
-        assert np.all(np.abs(got - h_ref) <= 1e-5 * np.abs(h_ref) + 2.0 ** -16 * a_h)
+        check_f32(got, h_ref, "swiglu pair h", a_ref=a_h)
     else:
         check(h, h_ref, a_h, "swiglu bf16")
 
@@ -158,6 +158,6 @@ def test_dense_layer_workload():
     y_ref, a_y, h_ref, a_h = oracle.dense_ffn(d["gate"], d["up"], d["down"], d["x"], "bf16",
                                               threads=oracle_threads())
     got_h = to_np64(h)
-    assert np.all(np.abs(got_h - h_ref) <= 1e-5 * np.abs(h_ref) + 2.0 ** -16 * a_h)
+    check_f32(got_h, h_ref, "dense h (fp32 SwiGLU)", a_ref=a_h)
     rel = check(y, y_ref, a_y, "dense down")
     print("dense layer max rel %.3e" % rel)

@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import synth
-from tests.gpu_common import check, dev_matrix, lib, nan_like, oracle_threads, require_gpu, to_np64
+from tests.gpu_common import check, check_f32, dev_matrix, lib, nan_like, oracle_threads, require_gpu, to_np64
 
 pytestmark = pytest.mark.gpu
 
@@ -81,7 +81,7 @@ def test_rms_swiglu_pair():
     got = to_np64(h)
     assert np.all(np.isfinite(got))
     # float32 SwiGLU of float32 sums: the bound of the plain SwiGLU test
-    assert np.all(np.abs(got - ref) <= 1e-5 * np.abs(ref) + 2.0 ** -16 * a)
+    check_f32(got, ref, "rms swiglu h", a_ref=a)
 
 
 def test_rms_one_hot_column():

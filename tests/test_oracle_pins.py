@@ -181,8 +181,8 @@ def _check_against_exact(w, x, x_dtype):
 
 
 def test_bruteforce_8x64_random():
-    """Exact rational brute force on 8x64, one group of 64: 200 seeded cases."""
-    for seed in range(200):
+    """Exact rational brute force on 8x64, one group of 64: 1000 seeded cases."""
+    for seed in range(1000):
         rng = np.random.default_rng(10_000 + seed)
         sbt = synth.F32 if seed % 2 == 0 else synth.BF16
         w = _rand_mat(rng, 8, 64, 64, sbt)
@@ -440,35 +440,39 @@ def test_gemm_rows_match_gemv_with_rounded_weights():
     for t in range(5):
         y, _ = oracle.gemv(w, X[t], synth.BF16)
         assert np.array_equal(Y[t], y)
-    # the bf16-weight variant multiplies round_bf16(float32(W)) with X (numpy matmul)
+    # the bf16-weight variant multiplies round_bf16(W) with X (numpy matmul)
     Yr, _ = oracle.gemm(w, X, synth.BF16, round_w=True)
-    Wr = oracle.round_bf16(oracle.dequant(w).astype(np.float32).astype(np.float64))
+    Wr = oracle.round_bf16(oracle.dequant(w))
     assert np.allclose(Yr, oracle.widen(X, synth.BF16) @ Wr.T, rtol=1e-12, atol=1e-12)
     # and the rounding is real: a sizeable share of weights is not bf16-exact
     assert np.mean(Wr != oracle.dequant(w)) > 0.2
 
 
-def test_gemm_weight_dequantised_in_float32_then_rounded_to_bf16():
-    """The prefill weight is bf16(float32(s q + b)), not bf16 of the exact value.
+def test_gemm_weight_is_rounded_once_to_bf16():
+    """The prefill weight is the exact s q + b rounded once to the nearest bfloat16.
 
-    s = 1/2 + 2^-24 and b = 1/2 + 2^-8 (both float32), q = 1: the exact weight is
-    1 + 2^-8 + 2^-24.  In float32 (ulp 2^-23 at 1) that is a tie, which goes to the
-    even neighbour 1 + 2^-8; that is again a bf16 tie (ulp 2^-7), which goes to the
-    even neighbour 1.0.  Rounded once from the exact value it would be 1 + 2^-7.
-    A one-hot X row reads the weight out.  With bf16 scales the float32 step is
-    exact and the two readings agree (second row: s = 3/8, b = -1, q = 5 -> 7/8)."""
-    raw = np.zeros((2, 64), np.uint8)
+    Hand-derived cases, read out through one-hot X rows (bf16 ulp at 1 is 2^-7, so the
+    bf16 neighbours of values just above 1 are 1 and 1 + 2^-7, with midpoint 1 + 2^-8):
+      row 0: s = 1/2 + 2^-24, b = 1/2 + 2^-8, q = 1 -> exact 1 + 2^-8 + 2^-24, just above
+             the midpoint -> 1 + 2^-7.  (Rounding to float32 first would land on the
+             midpoint 1 + 2^-8 and then tie to even at 1.0: a double rounding.)
+      row 1: s = 1/2, b = 1/2 + 2^-8, q = 1 -> exactly the midpoint -> ties to even 1.0.
+      row 2: s = 3/8, b = -1, q = 5 -> 7/8, bf16-exact."""
+    raw = np.zeros((3, 64), np.uint8)
     raw[0, 0] = 1
-    raw[1, 0] = 5
-    w = _mat(raw, np.array([[0.5 + 2.0 ** -24], [0.375]], np.float32),
-             np.array([[0.5 + 2.0 ** -8], [-1.0]], np.float32), 64)
+    raw[1, 0] = 1
+    raw[2, 0] = 5
+    w = _mat(raw, np.array([[0.5 + 2.0 ** -24], [0.5], [0.375]], np.float32),
+             np.array([[0.5 + 2.0 ** -8], [0.5 + 2.0 ** -8], [-1.0]], np.float32), 64)
     X = np.zeros((1, 64), np.uint16)
     X[0, 0] = 0x3F80                                                 # bf16 1.0
     Y, _ = oracle.gemm(w, X, synth.BF16, round_w=True)
-    assert Y[0, 0] == 1.0
-    assert Y[0, 1] == 0.875
+    assert Y[0, 0] == 1.0 + 2.0 ** -7
+    assert Y[0, 1] == 1.0
+    assert Y[0, 2] == 0.875
     Yx, _ = oracle.gemm(w, X, synth.BF16, round_w=False)
     assert Yx[0, 0] == 1 + 2.0 ** -8 + 2.0 ** -24                     # exact weight
+    assert Yx[0, 1] == 1 + 2.0 ** -8
 
 
 def test_gemm_entries_match_full():
