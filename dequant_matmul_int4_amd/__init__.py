@@ -79,6 +79,9 @@ SIGNATURES = [
     ("moe_gather_qgemv_int4", _I32, [ctypes.POINTER(CMatrix), ctypes.POINTER(CMatrix),
                                      ctypes.POINTER(CMatrix), _P, _P, _P, _I32, _P, _P, _I32,
                                      _P, ctypes.c_size_t, _P]),
+    ("moe_gather_qgemv_int4_noalloc", _I32, [ctypes.POINTER(CMatrix), ctypes.POINTER(CMatrix),
+                                             ctypes.POINTER(CMatrix), _P, _P, _P, _I32, _P, _P,
+                                             _I32, _P]),
     ("moe_route_gather_qgemv_int4", _I32, [ctypes.POINTER(CMatrix), ctypes.POINTER(CMatrix),
                                            ctypes.POINTER(CMatrix), _P, _P, _I32, _I32, _P, _P, _I32,
                                            _P, _P, _P, ctypes.c_size_t, _P]),
@@ -349,6 +352,33 @@ def moe_gather_qgemv_int4(gate: QInt4Matrix, up: QInt4Matrix, down: QInt4Matrix,
         _stream(stream)))
 
 
+def moe_gather_qgemv_int4_noalloc(gate: QInt4Matrix, up: QInt4Matrix, down: QInt4Matrix,
+                                  x: torch.Tensor, ids: torch.Tensor, wts: torch.Tensor,
+                                  out: torch.Tensor, residual: Optional[torch.Tensor] = None,
+                                  stream=None) -> None:
+    """moe_gather_qgemv_int4 with the library's static per-device scratch instead of a
+    workspace (for callers that cannot allocate); top_k * inter * 4 bytes must fit in
+    NOALLOC_SCRATCH_BYTES.  Calls that overlap on one GPU race on that scratch."""
+    if ids.dtype not in (torch.int32, torch.uint32):
+        raise TypeError("ids must be int32/uint32")
+    if wts.dtype != torch.float32:
+        raise TypeError("wts must be float32")
+    if ids.numel() != wts.numel():
+        raise ValueError("ids and wts must have the same length")
+    g, u, d = gate.c(), up.c(), down.c()
+    res_p = _dev(residual, "residual") if residual is not None else None
+    if residual is not None and residual.dtype != out.dtype:
+        raise TypeError("residual and out must share a dtype")
+    if x.dtype != out.dtype:
+        raise TypeError("x and out must share a dtype")
+    _check(load().moe_gather_qgemv_int4_noalloc(
+        ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), _dev(x, "x"), _dev(ids, "ids"),
+        _dev(wts, "wts"), ids.numel(), res_p, _dev(out, "out"), _dt(out), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 1 << 20  # QINT4_NOALLOC_SCRATCH_BYTES of include/qint4.h
+
+
 def _gemm_args(x: torch.Tensor, y: torch.Tensor) -> None:
     if x.dtype != torch.bfloat16:
         raise TypeError("x must be bfloat16")
@@ -412,5 +442,5 @@ __all__ = ["QInt4Matrix", "Int4Error", "qgemv_int4", "qgemv_int4_multi", "qgemv_
            "qgemm_int4_padT_ws", "qgemm_int4_padT_workspace_bytes",
            "moe_router_topk", "rms_norm_qgemv_int4", "quantize_int4",
            "moe_prefill_qgemm_int4", "moe_prefill_qgemm_int4_workspace_bytes",
-           "moe_route_gather_qgemv_int4",
+           "moe_route_gather_qgemv_int4", "moe_gather_qgemv_int4_noalloc", "NOALLOC_SCRATCH_BYTES",
            "load", "F32", "BF16", "EPI_NONE", "EPI_SWIGLU_PAIR", "LIB_PATH", "SIGNATURES"]

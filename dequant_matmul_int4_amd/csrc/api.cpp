@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstring>
 #include <algorithm>
+#include <mutex>
 
 #include "kernels.h"
 #include "qint4.h"
@@ -665,6 +666,66 @@ qint4_status moe_gather_qgemv_int4(const qint4_matrix *gate, const qint4_matrix 
   return run_moe(gate, up, down, x, ids, wts, top_k, residual, out, act_dtype, workspace,
                  workspace_bytes, reinterpret_cast<hipStream_t>(stream), "moe_gather_qgemv_int4",
                  nullptr, 0);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The scratch of moe_gather_qgemv_int4_noalloc: one copy on every GPU the
+// library runs on.  Host code never uses this name as an address (on the host
+// it is only a stand-in for the symbol); it looks up each device's copy with
+// hipGetSymbolAddress and passes that pointer on.
+__device__ __align__(256) unsigned char scratch[QINT4_NOALLOC_SCRATCH_BYTES];
+
+// Device address of the current device's scratch, looked up once per device
+// (the current device is the one the lookup resolves for).
+qint4_status scratch_address(void **out, const char *fn) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return fail(QINT4_ERR_DEVICE, "%s: no current HIP device", fn);
+  }
+  if (dev >= 64) return fail(QINT4_ERR_DEVICE, "%s: device ordinal %d not supported", fn, dev);
+  static std::mutex mu;
+  static void *addr[64] = {};
+  std::lock_guard<std::mutex> g(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return fail(QINT4_ERR_DEVICE, "%s: hipGetSymbolAddress of the scratch array failed: %s", fn,
+                  hipGetErrorString(e));
+    }
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return QINT4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+qint4_status moe_gather_qgemv_int4_noalloc(const qint4_matrix *gate, const qint4_matrix *up,
+                                           const qint4_matrix *down, const void *x,
+                                           const uint32_t *ids, const float *wts, int32_t top_k,
+                                           const void *residual, void *out, int32_t act_dtype,
+                                           void *stream) {
+  const char *fn = "moe_gather_qgemv_int4_noalloc";
+  if (!gate) return fail(QINT4_ERR_NULL, "%s: gate is NULL", fn);
+  const size_t need = moe_gather_qgemv_int4_workspace_bytes(gate->n_out, top_k);
+  if (need > QINT4_NOALLOC_SCRATCH_BYTES)
+    return fail(QINT4_ERR_WORKSPACE,
+                "%s: top_k %d x inter %lld needs %zu bytes of scratch, more than the %u the "
+                "library holds per device (use moe_gather_qgemv_int4 with a workspace)",
+                fn, top_k, (long long)gate->n_out, need, (unsigned)QINT4_NOALLOC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  qint4_status st = scratch_address(&ws, fn);
+  if (st != QINT4_OK) return st;
+  return run_moe(gate, up, down, x, ids, wts, top_k, residual, out, act_dtype, ws,
+                 QINT4_NOALLOC_SCRATCH_BYTES, reinterpret_cast<hipStream_t>(stream), fn, nullptr, 0);
 }
 
 qint4_status moe_route_gather_qgemv_int4(const qint4_matrix *gate, const qint4_matrix *up,

@@ -249,6 +249,31 @@ qint4_status moe_gather_qgemv_int4(const qint4_matrix *gate, const qint4_matrix 
                                    void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * moe_gather_qgemv_int4_noalloc -- moe_gather_qgemv_int4 without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.
+ *
+ * Same arguments (less the workspace), result and launches as
+ * moe_gather_qgemv_int4.  The float32 SwiGLU intermediates go to a static
+ * device array inside the library, QINT4_NOALLOC_SCRATCH_BYTES on each GPU it
+ * runs on (held until the process ends); its address is looked up once per
+ * device, on the first call there.  The call allocates nothing.
+ *
+ *   top_k * inter * 4 <= QINT4_NOALLOC_SCRATCH_BYTES, else QINT4_ERR_WORKSPACE
+ *   (nothing is launched).
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents; a call reads only what it wrote earlier in the same call.  Calls
+ * that overlap on one GPU (unordered streams) race on the array: order them,
+ * or give each its own workspace through moe_gather_qgemv_int4.
+ */
+#define QINT4_NOALLOC_SCRATCH_BYTES (1u << 20)
+qint4_status moe_gather_qgemv_int4_noalloc(const qint4_matrix *gate, const qint4_matrix *up,
+                                           const qint4_matrix *down, const void *x,
+                                           const uint32_t *ids, const float *wts, int32_t top_k,
+                                           const void *residual, void *out, int32_t act_dtype,
+                                           void *stream);
+
+/*
  * moe_route_gather_qgemv_int4 -- moe_router_topk followed by
  * moe_gather_qgemv_int4 for one token, with the routing done inside the
  * gate/up launch: every wave of that launch ranks the token's logits itself
