@@ -25,6 +25,7 @@ torch's bf16 matmul of the same shape.
 Workloads (default: dense):
   single   1024x1024 g64 GEMV, fp32 scales/biases, fp32 x and y
   qkv      q/k/v projections of one bf16 4096-vector (4096/1024/1024 rows), one launch
+  qkvprefill  the q/k/v projections of --T rows in one multi-matrix GEMM launch
   rmsqkv   the same launch with the RMSNorm of the input fused in front
   smallm   the q/k/v set for --T tokens (1..8, default 4) in one launch
   dense    gate/up 5120->17408 with SwiGLU (fp32 h), then down 17408->5120
@@ -104,7 +105,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="dense",
                     choices=["single", "qkv", "rmsqkv", "smallm", "dense", "moe", "moeprefill", "prefill",
-                             "quant", "copy"])
+                             "qkvprefill", "quant", "copy"])
     ap.add_argument("--T", type=int, default=None,
                     help="prefill rows (default 256) or small-M tokens (default 4)")
     ap.add_argument("--cpu-seconds", type=float, default=16.0,
@@ -519,6 +520,35 @@ class Prefill(Workload):
         self.q.qgemm_int4_padT_ws(self.pool[i % self.R], self.x, self.y, self.ws)
 
 
+class QKVPrefill(QKV):
+    """q/k/v prefill: T rows of a 4096-wide bf16 block through the 4096 -> 4096/1024/1024
+    projections in one qgemm_int4_padT_multi launch (timed beside three qgemm_int4_padT calls)."""
+
+    def __init__(self, q, synth, torch, T):
+        super().__init__(q, synth, torch)
+        self.T = T
+        self.name = "qkv_prefill_T%d" % T
+        self.dominant = "qgemm_int4_padT_multi (q/k/v, one launch, bf16 MFMA)"
+        self.xT = torch.randn(T, 4096, device="cuda").to(torch.bfloat16)
+        self.ysT = [torch.empty(T, n, device="cuda", dtype=torch.bfloat16) for n in (4096, 1024, 1024)]
+        self.flops = 2.0 * T * 4096 * 6144
+        self.config = dict(self.config, workload=self.name, T=T)
+
+    def algo_bytes(self):
+        return self.wb + self.T * (4096 * 2 + 6144 * 2)
+
+    def step(self, i):
+        self.q.qgemm_int4_padT_multi(self.pool[i % self.R], self.xT, self.ysT)
+
+    def separate(self, i):
+        for w, y in zip(self.pool[i % self.R], self.ysT):
+            self.q.qgemm_int4_padT(w, self.xT, y)
+
+    def parts(self):
+        return [(self.dominant, self.step, self.algo_bytes(), self.flops, 1),
+                ("three qgemm_int4_padT calls (q, k, v)", self.separate, self.algo_bytes(), self.flops, 3)]
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline: the fp64 oracle on a bounded sample of the same workload
 # ---------------------------------------------------------------------------
@@ -595,6 +625,15 @@ def _oracle_sample(workload: str, T: int, threads: int):
         W = synth.draw_float_weights(rng, (rows, 5120), "f32")
         return (lambda: oracle.quantize(W, "f32", 64, "bf16"), W.nbytes, "GB/s",
                 "%d x 5120 rows of float32 weights per call (numpy float32, one thread)" % rows, 1)
+    if workload == "qkvprefill":
+        d = synth.qkv_multi()
+        X = synth.draw_activation(np.random.default_rng(600 + T), (T, 4096), "bf16")
+        rng = np.random.default_rng(0)
+        t_idx = np.repeat(np.arange(min(T, 4)), 64 // min(T, 4))
+        picks = [(w, rng.integers(0, w.n_out, t_idx.size)) for w in d["ws"]]
+        return (lambda: [oracle.gemm_entries(w, X, t_idx, o, "bf16", threads=threads) for w, o in picks],
+                3 * 2.0 * t_idx.size * 4096, "TFLOP/s",
+                "%d sampled output entries of each of q, k, v (T=%d) per call" % (t_idx.size, T), None)
     d = synth.prefill_gemm(T=T)
     rows = 64
     rng = np.random.default_rng(0)
@@ -778,6 +817,8 @@ def main():
         wl = Dense(q, synth, torch)
     elif args.workload == "smallm":
         wl = SmallM(q, synth, torch, args.T)
+    elif args.workload == "qkvprefill":
+        wl = QKVPrefill(q, synth, torch, args.T)
     elif args.workload == "moe":
         wl = MoE(q, synth, torch, router=args.router)
     else:
@@ -818,7 +859,7 @@ def main():
         out["kernels"] = parts
     dom = parts[0]
 
-    gemm_like = isinstance(wl, (Prefill, MoEPrefill))
+    gemm_like = isinstance(wl, (Prefill, MoEPrefill, QKVPrefill))
     if gemm_like:
         tflops = wl.flops / (ms_step * 1e-3) / 1e12
         out.update({"value": tflops, "unit": "TFLOP/s",

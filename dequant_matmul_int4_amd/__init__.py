@@ -89,6 +89,9 @@ SIGNATURES = [
     ("qgemm_int4_padT_ws", _I32, [ctypes.POINTER(CMatrix), _P, _I64, _I64, _P, _I64, _I32, _P,
                                   ctypes.c_size_t, _P]),
     ("qgemm_int4_padT_workspace_bytes", ctypes.c_size_t, [_I64, _I64, _I64]),
+    ("qgemm_int4_padT_multi", _I32, [_I32, ctypes.POINTER(CMatrix), _P, _I64, _I64,
+                                     ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_int64),
+                                     _I32, _P]),
     ("moe_router_topk", _I32, [_P, _I32, _I64, _I32, _I32, _P, _P, _P]),
     ("moe_prefill_qgemm_int4_workspace_bytes", ctypes.c_size_t, [_I64, _I32, _I32, _I64, _I64]),
     ("moe_prefill_qgemm_int4", _I32, [ctypes.POINTER(CMatrix), ctypes.POINTER(CMatrix),
@@ -399,6 +402,23 @@ def qgemm_int4_padT(w: QInt4Matrix, x: torch.Tensor, y: torch.Tensor, stream=Non
                                   y.data_ptr(), y.stride(0), _dt(y), _stream(stream)))
 
 
+def qgemm_int4_padT_multi(ws: Sequence[QInt4Matrix], x: torch.Tensor, ys: Sequence[torch.Tensor],
+                          stream=None) -> None:
+    """Y_i[t] = bf16(W_i) X[t] for t < T and every matrix i, in one launch.  x: bfloat16
+    [T][ldx]; ys[i]: [T][ldy_i] float32/bfloat16, all of one dtype."""
+    if len(ws) != len(ys) or not ws:
+        raise ValueError("one output per matrix")
+    for y in ys:
+        _gemm_args(x, y)
+    if len({y.dtype for y in ys}) != 1:
+        raise TypeError("all outputs must share a dtype")
+    arr = (CMatrix * len(ws))(*[w.c() for w in ws])
+    yp = (ctypes.c_void_p * len(ys))(*[y.data_ptr() for y in ys])
+    ld = (ctypes.c_int64 * len(ys))(*[y.stride(0) for y in ys])
+    _check(load().qgemm_int4_padT_multi(len(ws), arr, x.data_ptr(), x.shape[0], x.stride(0), yp,
+                                        ld, _dt(ys[0]), _stream(stream)))
+
+
 def qgemm_int4_padT_workspace_bytes(T: int, n_out: int, k_in: int) -> int:
     """Workspace bytes for the full K split of qgemm_int4_padT_ws on the current device."""
     return int(load().qgemm_int4_padT_workspace_bytes(int(T), int(n_out), int(k_in)))
@@ -439,7 +459,7 @@ def moe_router_topk(logits: torch.Tensor, top_k: int, ids: torch.Tensor, wts: to
 
 __all__ = ["QInt4Matrix", "Int4Error", "qgemv_int4", "qgemv_int4_multi", "qgemv_int4_smallm",
            "moe_gather_qgemv_int4", "moe_gather_qgemv_int4_workspace_bytes", "qgemm_int4_padT",
-           "qgemm_int4_padT_ws", "qgemm_int4_padT_workspace_bytes",
+           "qgemm_int4_padT_ws", "qgemm_int4_padT_workspace_bytes", "qgemm_int4_padT_multi",
            "moe_router_topk", "rms_norm_qgemv_int4", "quantize_int4",
            "moe_prefill_qgemm_int4", "moe_prefill_qgemm_int4_workspace_bytes",
            "moe_route_gather_qgemv_int4", "moe_gather_qgemv_int4_noalloc", "NOALLOC_SCRATCH_BYTES",

@@ -1017,8 +1017,8 @@ static qint4_status run_gemm(const char *fn, const qint4_matrix *w, const void *
   // (qgemm.hip), which amortise the dequantisation over more rows.  The
   // stream kernel addresses X through 32-bit byte offsets.
   const bool stream_path = T <= kStreamMaxT && (T - 1) * ldx + w->k_in < ((int64_t)1 << 30);
-  // the tiled kernel addresses a 128-row block of X through 32-bit offsets
-  if (!stream_path && 128 * ldx * 2 >= ((int64_t)1 << 31))
+  // the tiled kernel addresses one tile's rows of X through 32-bit offsets
+  if (!stream_path && (int64_t)kGemmTileRows * ldx * 2 >= ((int64_t)1 << 31))
     return fail(QINT4_ERR_SHAPE, "%s: ldx %lld too large for T > %d", fn, (long long)ldx, kStreamMaxT);
   StreamPlan plan{};
   size_t ws_used = 0;
@@ -1053,10 +1053,22 @@ static qint4_status run_gemm(const char *fn, const qint4_matrix *w, const void *
   p.part = reinterpret_cast<float *>(ws);
   p.ksplit = 1;
   hipError_t e;
-  if (stream_path)
+  if (stream_path) {
     e = launch_gemm_stream(p, plan, reinterpret_cast<hipStream_t>(stream));
-  else
-    e = launch_gemm(p, reinterpret_cast<hipStream_t>(stream));
+  } else {
+    GemmMultiParams mp;
+    std::memset(&mp, 0, sizeof(mp));
+    mp.m[0] = {w->codes, w->scales, w->biases, y, ldy, (int32_t)w->n_out, 0};
+    mp.n_mats = 1;
+    mp.x = reinterpret_cast<const uint16_t *>(x);
+    mp.T = T;
+    mp.ldx = ldx;
+    mp.k_in = (int32_t)w->k_in;
+    mp.log2_group = ilog2(w->group_size);
+    mp.y_bf16 = y_dtype == QINT4_BF16;
+    mp.sb_bf16 = w->sb_dtype == QINT4_BF16;
+    e = launch_gemm(mp, reinterpret_cast<hipStream_t>(stream));
+  }
   if (e != hipSuccess) return fail(QINT4_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
 }
@@ -1080,6 +1092,88 @@ qint4_status qgemm_int4_padT_ws(const qint4_matrix *w, const void *x, int64_t T,
                                 size_t workspace_bytes, void *stream) {
   return run_gemm("qgemm_int4_padT_ws", w, x, T, ldx, y, ldy, y_dtype, workspace, workspace_bytes,
                   stream);
+}
+
+
+qint4_status qgemm_int4_padT_multi(int32_t n, const qint4_matrix *ws, const void *x, int64_t T,
+                                   int64_t ldx, void *const *ys, const int64_t *ldys,
+                                   int32_t y_dtype, void *stream) {
+  const char *fn = "qgemm_int4_padT_multi";
+  if (n < 1 || n > QINT4_MULTI_MAX)
+    return fail(QINT4_ERR_SHAPE, "%s: n = %d not in [1, %d]", fn, n, QINT4_MULTI_MAX);
+  if (!ws) return fail(QINT4_ERR_NULL, "%s: matrix array is NULL", fn);
+  if (!ys) return fail(QINT4_ERR_NULL, "%s: output array is NULL", fn);
+  if (!x) return fail(QINT4_ERR_NULL, "%s: x is NULL", fn);
+  if (!valid_dtype(y_dtype)) return fail(QINT4_ERR_DTYPE, "%s: y_dtype %d invalid", fn, y_dtype);
+  char name[32];
+  qint4_status st;
+  for (int i = 0; i < n; ++i) {
+    snprintf(name, sizeof(name), "ws[%d]", i);
+    if ((st = check_matrix(&ws[i], name, false)) != QINT4_OK) return st;
+    if (!ys[i]) return fail(QINT4_ERR_NULL, "%s: ys[%d] is NULL", fn, i);
+    if (ws[i].n_out % 32 != 0)
+      return fail(QINT4_ERR_SHAPE, "%s: ws[%d].n_out (%lld) must be a multiple of 32 (GEMM tile)", fn,
+                  i, (long long)ws[i].n_out);
+    if (ws[i].n_out > INT32_MAX / 2) return fail(QINT4_ERR_SHAPE, "%s: ws[%d] too large", fn, i);
+    const int64_t ldy = ldys ? ldys[i] : ws[i].n_out;
+    if (ldy < ws[i].n_out)
+      return fail(QINT4_ERR_SHAPE, "%s: ldys[%d] %lld < n_out %lld", fn, i, (long long)ldy,
+                  (long long)ws[i].n_out);
+    if (!aligned(ys[i], elem_bytes(y_dtype)))
+      return fail(QINT4_ERR_ALIGN, "%s: ys[%d] misaligned", fn, i);
+  }
+  for (int i = 1; i < n; ++i) {
+    if (ws[i].k_in != ws[0].k_in)
+      return fail(QINT4_ERR_SHAPE,
+                  "%s: packed width mismatch: ws[%d].k_in = %lld (%lld words) but ws[0].k_in = %lld "
+                  "(%lld words)",
+                  fn, i, (long long)ws[i].k_in, (long long)ws[i].k_in / 8, (long long)ws[0].k_in,
+                  (long long)ws[0].k_in / 8);
+    if (ws[i].group_size != ws[0].group_size)
+      return fail(QINT4_ERR_SHAPE, "%s: ws[%d].group_size %d != ws[0].group_size %d", fn, i,
+                  ws[i].group_size, ws[0].group_size);
+    if (ws[i].sb_dtype != ws[0].sb_dtype)
+      return fail(QINT4_ERR_DTYPE, "%s: ws[%d].sb_dtype differs from ws[0]", fn, i);
+  }
+  const int64_t k_in = ws[0].k_in;
+  if (T < 1 || T > ((int64_t)1 << 31)) return fail(QINT4_ERR_SHAPE, "%s: T = %lld invalid", fn, (long long)T);
+  if (ldx < k_in || ldx % 8 != 0)
+    return fail(QINT4_ERR_SHAPE, "%s: ldx %lld must be >= k_in %lld and a multiple of 8", fn,
+                (long long)ldx, (long long)k_in);
+  if (!aligned(x, 16)) return fail(QINT4_ERR_ALIGN, "%s: x not 16-byte aligned", fn);
+  if ((int64_t)kGemmTileRows * ldx * 2 >= ((int64_t)1 << 31))
+    return fail(QINT4_ERR_SHAPE, "%s: ldx %lld too large", fn, (long long)ldx);
+
+  Range ins[3 * QINT4_MULTI_MAX + 1], outs[QINT4_MULTI_MAX];
+  int ni = 0;
+  static const char *mnames[3] = {"codes", "scales", "biases"};
+  for (int i = 0; i < n; ++i) ni += add_matrix_ranges(&ws[i], mnames, ins + ni);
+  ins[ni++] = range(x, (size_t)((T - 1) * ldx + k_in) * 2, "x");
+  static const char *ynames[QINT4_MULTI_MAX] = {"ys[0]", "ys[1]", "ys[2]", "ys[3]",
+                                                  "ys[4]", "ys[5]", "ys[6]", "ys[7]"};
+  for (int i = 0; i < n; ++i) {
+    const int64_t ldy = ldys ? ldys[i] : ws[i].n_out;
+    outs[i] = range(ys[i], (size_t)((T - 1) * ldy + ws[i].n_out) * elem_bytes(y_dtype), ynames[i]);
+  }
+  if ((st = check_no_overlap(outs, n, ins, ni)) != QINT4_OK) return prefixed(st, fn);
+  if ((st = check_device(nullptr)) != QINT4_OK) return prefixed(st, fn);
+
+  GemmMultiParams mp;
+  std::memset(&mp, 0, sizeof(mp));
+  for (int i = 0; i < n; ++i)
+    mp.m[i] = {ws[i].codes, ws[i].scales, ws[i].biases, ys[i], ldys ? ldys[i] : ws[i].n_out,
+               (int32_t)ws[i].n_out, 0};
+  mp.n_mats = n;
+  mp.x = reinterpret_cast<const uint16_t *>(x);
+  mp.T = T;
+  mp.ldx = ldx;
+  mp.k_in = (int32_t)k_in;
+  mp.log2_group = ilog2(ws[0].group_size);
+  mp.y_bf16 = y_dtype == QINT4_BF16;
+  mp.sb_bf16 = ws[0].sb_dtype == QINT4_BF16;
+  hipError_t e = launch_gemm(mp, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(QINT4_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
 }
 
 }  // extern "C"

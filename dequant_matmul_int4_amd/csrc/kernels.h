@@ -182,7 +182,42 @@ struct GemmParams {
   int32_t pad_;
 };
 
-hipError_t launch_gemm(const GemmParams &p, hipStream_t stream);
+// LDS-tiled prefill GEMM (qgemm.hip) over the matrix table of GemmMultiParams.
+struct GemmMultiParams;
+hipError_t launch_gemm(const GemmMultiParams &p, hipStream_t stream);
+
+// Prefill GEMM over the output tiles of up to kMaxMats matrices that share X
+// (k_in, group size and scale dtype); n_out % 32 == 0 each.  tile0 / m_tiles /
+// n_tiles / tiles / per_xcd are filled in by the launcher.
+struct GemmMat {
+  const uint32_t *codes;
+  const void *scales;
+  const void *biases;
+  void *y;                   // [T][ldy]
+  int64_t ldy;
+  int32_t n_out;
+  int32_t tile0;             // first weight tile of this matrix
+};
+struct GemmMultiParams {
+  GemmMat m[kMaxMats];
+  const uint16_t *x;         // bf16 [T][ldx]
+  int64_t T;
+  int64_t ldx;
+  int32_t k_in;
+  int32_t log2_group;
+  int32_t y_bf16;
+  int32_t sb_bf16;
+  int32_t n_mats;
+  int32_t m_tiles;
+  int32_t n_tiles;           // weight tiles of all matrices
+  int32_t tiles;
+  int32_t per_xcd;           // tiles each of the eight XCDs takes
+  int32_t pad_;
+};
+static_assert(sizeof(GemmMultiParams) <= 512, "GEMM kernel arguments exceed 8 cache lines");
+// Token rows of one tile of the LDS-tiled GEMM (at most); the host keeps that
+// many rows of X addressable through 32-bit offsets.
+constexpr int kGemmTileRows = 128;
 
 // Register-resident-weight GEMM for T <= 64 (qgemm_stream.hip).
 struct StreamPlan {

@@ -1,21 +1,30 @@
 // qgemm.hip -- prefill int4 dequant GEMM on gfx950 bf16 MFMA, LDS-tiled
-// (the T > 64 path; qgemm_stream.hip serves T <= 64).
+// (the T > 64 path of qgemm_int4_padT, and every qgemm_int4_padT_multi call;
+// qgemm_stream.hip serves qgemm_int4_padT at T <= 64).
 //
-//   Y[t][o] = sum_k bf16(s[o][k/g] * q[o][k] + b[o][k/g]) * X[t][k],  t < T
+//   Y_i[t][o] = sum_k bf16(s_i[o][k/g] * q_i[o][k] + b_i[o][k/g]) * X[t][k],  t < T
 //
-// Source: thewafflehaus/FFAI pull 9, "Everything Bagel", commit adding the
+// Sources: thewafflehaus/FFAI pull 9, "Everything Bagel", commit adding the
 // dequantGemmDynamicM T-padding driver (T rounded up to a multiple of 32 with
 // zero rows, first T rows kept), and pull 14, commit adding the outDim % 32
-// guard for that GEMM.  Here the padding is virtual: X rows >= T load as zero
-// and Y rows >= T are never stored, so neither buffer is copied or padded.
+// guard for that GEMM and the batched QKV / batched-4 projections sharing one
+// input in one launch (M > 1: separate outputs).  Here the padding is
+// virtual: X rows >= T load as zero and Y rows >= T are never stored, so
+// neither buffer is copied or padded.
 //
-// Tiling (gfx950): a workgroup owns a BM x BN tile of Y and walks K in steps
+// Tiling (gfx950): a workgroup owns a BM x BN tile of one matrix's output (the
+// weight tiles of all matrices of a call form one grid) and walks K in steps
 // of 64 (one 64-group, or two 32-groups).  Per step every thread loads 32
 // codes of one W row (a 128-bit load), dequantises them in float32 with that
 // group's scale and bias, rounds to bf16 (v_cvt_pk_bf16_f32,
 // round-to-nearest-even) and writes them to LDS; the X tile is copied to LDS
 // as bf16.  Waves then run v_mfma_f32_32x32x16_bf16 on 32x32 sub-tiles with
 // float32 accumulators.
+//   * Tile order: workgroups are dealt to the eight XCDs round-robin, and each
+//     XCD takes a contiguous range of a grouped order (4 token tiles per
+//     weight tile, then the next weight tile), so the tiles resident on an
+//     XCD share their weight and activation blocks in its L2 (T = 1024:
+//     302 -> 267 us, T = 4096: 982 -> 893 us at N = 17408, K = 5120).
 //   * The global loads of PF steps are kept in flight in a register ring, so
 //     HBM latency is covered by PF steps of MFMA work rather than one; the
 //     barriers order LDS only and never wait for those loads.  PF = 2 (3
@@ -82,7 +91,7 @@ __device__ __forceinline__ uint4 dequant_word(uint32_t w, float s, float b) {
 
 // SBL: the scales and biases of the BN rows are staged in dynamic LDS.
 template <int BM, int BN, int WM, int WN, int PF, bool SBL>
-__global__ void __launch_bounds__(WM * WN * 64) qgemm_kernel(const GemmParams p) {
+__global__ void __launch_bounds__(WM * WN * 64) qgemm_kernel(const GemmMultiParams p) {
   constexpr int NT = WM * WN * 64;
   constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
   constexpr int FM = TM / 32, FN = TN / 32;  // 32x32 MFMA tiles per wave
@@ -99,11 +108,25 @@ __global__ void __launch_bounds__(WM * WN * 64) qgemm_kernel(const GemmParams p)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
 
-  // tile order: m fastest, so workgroups launched together share W columns
-  const int mt = blockIdx.x % p.m_tiles;
-  const int nt = blockIdx.x / p.m_tiles;
+  // Tile order: workgroups are dealt to the eight XCDs round-robin (workgroup
+  // b runs on XCD b % 8); each XCD takes a contiguous range of a grouped order
+  // (GROUP_M token tiles per weight tile, then the next weight tile), so the
+  // tiles resident on one XCD share weight and activation blocks in its L2.
+  constexpr int GROUP_M = 4;
+  const int bid = blockIdx.x;
+  const int sq = (bid & 7) * p.per_xcd + (bid >> 3);
+  if (sq >= p.tiles) return;
+  const int grp = sq / (GROUP_M * p.n_tiles);
+  const int rr = sq - grp * GROUP_M * p.n_tiles;
+  const int gsz = min(GROUP_M, p.m_tiles - grp * GROUP_M);
+  const int nt_all = rr / gsz;
+  const int mt = grp * GROUP_M + (rr - nt_all * gsz);
+  int mi = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxMats; ++i) mi += nt_all >= p.m[i].tile0 ? 1 : 0;
+  const GemmMat &M = p.m[mi];
   const int64_t m0 = (int64_t)mt * BM;
-  const int n0 = nt * BN;
+  const int n0 = (nt_all - M.tile0) * BN;
 
   const int cpr = p.k_in / 32;                   // 32-code chunks per W row
   const uint32_t gpr = (uint32_t)p.k_in >> p.log2_group;
@@ -114,9 +137,9 @@ __global__ void __launch_bounds__(WM * WN * 64) qgemm_kernel(const GemmParams p)
   // out-of-range zeros and add nothing
   const int nsteps = ((p.k_in + BK - 1) / BK + PF - 1) / PF * PF;
 
-  const __amdgpu_buffer_rsrc_t rc = rsrc(p.codes, (uint32_t)p.n_out * kwb);
-  const __amdgpu_buffer_rsrc_t rs = rsrc(p.scales, (uint32_t)p.n_out * sbrow);
-  const __amdgpu_buffer_rsrc_t rb = rsrc(p.biases, (uint32_t)p.n_out * sbrow);
+  const __amdgpu_buffer_rsrc_t rc = rsrc(M.codes, (uint32_t)M.n_out * kwb);
+  const __amdgpu_buffer_rsrc_t rs = rsrc(M.scales, (uint32_t)M.n_out * sbrow);
+  const __amdgpu_buffer_rsrc_t rb = rsrc(M.biases, (uint32_t)M.n_out * sbrow);
   // X from this tile's first row on: rows past T lie outside the resource
   const int64_t rows_here = p.T - m0 < BM ? p.T - m0 : BM;
   const __amdgpu_buffer_rsrc_t rx =
@@ -131,7 +154,7 @@ __global__ void __launch_bounds__(WM * WN * 64) qgemm_kernel(const GemmParams p)
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
       const __amdgpu_buffer_rsrc_t r = a ? rb : rs;
-      const uintptr_t al = reinterpret_cast<uintptr_t>(a ? p.biases : p.scales) | base | bytes;
+      const uintptr_t al = reinterpret_cast<uintptr_t>(a ? M.biases : M.scales) | base | bytes;
       unsigned char *dst = sbtab + (uint32_t)a * bytes;
       if ((al & 15) == 0) {
         for (uint32_t j = tid * 16; j < bytes; j += NT * 16)
@@ -279,35 +302,48 @@ __global__ void __launch_bounds__(WM * WN * 64) qgemm_kernel(const GemmParams p)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int64_t row = m0 + wm * TM + a * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (row < p.T && col < p.n_out) {
+        if (row < p.T && col < M.n_out) {
           if (p.y_bf16)
-            reinterpret_cast<__bf16 *>(p.y)[row * p.ldy + col] = (__bf16)acc[a][b][v];
+            reinterpret_cast<__bf16 *>(M.y)[row * M.ldy + col] = (__bf16)acc[a][b][v];
           else
-            reinterpret_cast<float *>(p.y)[row * p.ldy + col] = acc[a][b][v];
+            reinterpret_cast<float *>(M.y)[row * M.ldy + col] = acc[a][b][v];
         }
       }
     }
 }
 
 template <int BM, int BN, int WM, int WN, int PF = 2>
-hipError_t launch_tile(GemmParams p, hipStream_t stream) {
+hipError_t launch_tile(GemmMultiParams p, hipStream_t stream) {
   constexpr size_t kStatic = (size_t)(BM + BN) * LDK * 2;
   p.m_tiles = (int)((p.T + BM - 1) / BM);
-  p.n_tiles = (p.n_out + BN - 1) / BN;
-  const int64_t grid = (int64_t)p.m_tiles * p.n_tiles;
+  int t = 0;
+  for (int i = 0; i < kMaxMats; ++i) {
+    if (i < p.n_mats) {
+      p.m[i].tile0 = t;
+      t += (p.m[i].n_out + BN - 1) / BN;
+    } else {
+      p.m[i].tile0 = INT32_MAX;
+    }
+  }
+  p.n_tiles = t;
+  const int64_t tiles = (int64_t)p.m_tiles * p.n_tiles;
+  if (tiles > INT32_MAX / 2) return hipErrorInvalidValue;
+  p.tiles = (int32_t)tiles;
+  p.per_xcd = (int32_t)((tiles + 7) / 8);
+  const unsigned grid = (unsigned)(8 * p.per_xcd);
   // the scale / bias table in LDS when it fits next to the tiles
   const size_t sbrow = (size_t)(p.k_in >> p.log2_group) * (p.sb_bf16 ? 2 : 4);
   const size_t tab = 2 * (size_t)BN * sbrow;
   if (!(tab <= 96 * 1024 && kStatic + tab <= (size_t)kMaxLds)) {
-    hipLaunchKernelGGL((qgemm_kernel<BM, BN, WM, WN, PF, false>), dim3((unsigned)grid),
-                       dim3(WM * WN * 64), 0, stream, p);
+    hipLaunchKernelGGL((qgemm_kernel<BM, BN, WM, WN, PF, false>), dim3(grid), dim3(WM * WN * 64), 0,
+                       stream, p);
     return hipGetLastError();
   }
   auto kern = qgemm_kernel<BM, BN, WM, WN, PF, true>;
   // opt in to the LDS left next to the static tiles (once per device)
   hipError_t e = lds_opt_in(reinterpret_cast<const void *>(kern), (int)(kMaxLds - kStatic));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(WM * WN * 64), tab, stream, p);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(WM * WN * 64), tab, stream, p);
   return hipGetLastError();
 }
 
@@ -315,7 +351,8 @@ hipError_t launch_tile(GemmParams p, hipStream_t stream) {
 
 // Tile by T (measured on MI355X at N = 17408, K = 5120): narrow tiles keep
 // more workgroups per CU for short T; 8-wave 128x128 tiles up to T = 2048.
-hipError_t launch_gemm(const GemmParams &p, hipStream_t stream) {
+hipError_t launch_gemm(const GemmMultiParams &p, hipStream_t stream) {
+  if (p.n_mats < 1 || p.n_mats > kMaxMats) return hipErrorInvalidValue;
   if (p.T <= 32) return launch_tile<32, 64, 1, 2>(p, stream);
   if (p.T <= 64) return launch_tile<64, 64, 2, 2>(p, stream);
   if (p.T <= 256) return launch_tile<128, 64, 2, 2>(p, stream);

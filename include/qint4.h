@@ -391,6 +391,36 @@ qint4_status qgemm_int4_padT_ws(const qint4_matrix *w, const void *x, int64_t T,
                                 size_t workspace_bytes, void *stream);
 
 /*
+ * qgemm_int4_padT_multi -- the prefill GEMM of n matrices that share one
+ * activation block, in ONE launch:
+ *
+ *   Y_i[t][o] = sum_k bf16(w_i[o][k]) * X[t][k],   t < T,  i < n
+ *
+ * [FFAI #14], batched QKV and batched-4 qgemv commits: the q/k/v (or four)
+ * projections of one input run as one kernel whose M > 1 path writes three
+ * (four) separate outputs; [FFAI #9], dequantGemmDynamicM commit: T padded
+ * to a multiple of 32 with zero rows, the first T rows kept (virtual here, as
+ * in qgemm_int4_padT).  The weights are dequantised and rounded to bf16 as in
+ * qgemm_int4_padT and multiplied on bf16 MFMA with float32 accumulation; each
+ * output tile belongs to one matrix, and the tiles of all matrices are one
+ * grid, so the launch reads X once per token tile and weight tile pair.
+ *
+ *   n       1..QINT4_MULTI_MAX matrices; equal k_in, group_size and sb_dtype;
+ *           n_experts == 1; n_out % 32 == 0 each
+ *   ws      host array [n] of matrix descriptors
+ *   x       device bf16 [T][ldx], 16-byte aligned; ldx >= k_in, ldx % 8 == 0
+ *   T       rows of x and of every output, T >= 1
+ *   ys      host array [n] of device outputs, ys[i] is [T][ldys[i]] of y_dtype
+ *           (QINT4_F32 or QINT4_BF16); rows < T fully overwritten, columns
+ *           >= n_out and rows >= T never written
+ *   ldys    host array [n] of row strides (>= n_out), or NULL for n_out each
+ * One kernel launch on `stream`; no workspace.
+ */
+qint4_status qgemm_int4_padT_multi(int32_t n, const qint4_matrix *ws, const void *x, int64_t T,
+                                   int64_t ldx, void *const *ys, const int64_t *ldys,
+                                   int32_t y_dtype, void *stream);
+
+/*
  * Workspace bytes with which qgemm_int4_padT_ws runs its full K split for a
  * T x n_out x k_in product on the current device; 0 when it uses none (T > 64
  * or a shape that does not split).  Depends on the current device's compute

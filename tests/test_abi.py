@@ -274,3 +274,25 @@ def test_route_gather_validation(lib):
     assert call(logits=A + 0x300402) == 4                   # float32 logits misaligned
     assert call(ids=A + 0x300400 + 8) == 5                  # ids (an output) overlaps logits
     assert call(ids=A + 0x400000) == 5                      # ids overlaps out
+
+
+def _gemm_multi(lib, ms, x=A + 0x300000, T=100, ldx=None, ys=None, ldys=None, ydt=1):
+    arr = (q.CMatrix * len(ms))(*ms)
+    ys = ys or [A + 0x1000000 + 0x100000 * i for i in range(len(ms))]
+    yp = (ctypes.c_void_p * len(ys))(*ys)
+    ld = (ctypes.c_int64 * len(ms))(*(ldys or [m.n_out for m in ms]))
+    return lib.qgemm_int4_padT_multi(len(ms), arr, x, T, ldx or ms[0].k_in, yp, ld, ydt, None)
+
+
+def test_gemm_multi_validation(lib):
+    m = [_m(), _m(n_out=32), _m(n_out=96)]
+    assert lib.qgemm_int4_padT_multi(0, None, A, 4, 256, None, None, 1, None) == 2
+    assert _gemm_multi(lib, [_m(n_out=48)]) == 2 and "multiple of 32" in _err(lib)
+    assert _gemm_multi(lib, [_m(), _m(k_in=512)]) == 2 and "packed width" in _err(lib)
+    assert _gemm_multi(lib, [_m(), _m(g=32)]) == 2
+    assert _gemm_multi(lib, m, T=0) == 2
+    assert _gemm_multi(lib, m, ldx=260) == 2
+    assert _gemm_multi(lib, m, ldys=[64, 16, 96]) == 2                     # ldy < n_out
+    assert _gemm_multi(lib, m, ys=[A + 0x300000, A + 0x2000000, A + 0x2100000]) == 5  # y over x
+    assert _gemm_multi(lib, m, ys=[A + 0x2000000, A + 0x2000000 + 64, A + 0x2100000]) == 5
+    assert _gemm_multi(lib, m, ydt=4) == 3
