@@ -301,7 +301,7 @@ SMALLM_MAX = 8
 
 def qgemv_int4_smallm(ws: Sequence[QInt4Matrix], x: torch.Tensor, ys: Sequence[torch.Tensor],
                       epilogue: int = EPI_NONE, stream=None) -> None:
-    """ys[i][t] = W_i x[t] for T = x.shape[0] rows (1..8) in one launch; with
+    """ys[i][t] = W_i x[t] for T = x.shape[0] rows (1..16) sharing the weight stream; with
     EPI_SWIGLU_PAIR, ys[0][t] = silu(W_0 x[t]) * (W_1 x[t]).
 
     x: [T][ldx] bfloat16 (row stride may exceed k_in; float32 only for T = 1);

@@ -334,8 +334,8 @@ qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t
   for (int i = 0; i < n_outs; ++i)
     if (!aligned(ys[i], elem_bytes(y_dtype)))
       return fail(QINT4_ERR_ALIGN, "%s: ys[%d] not aligned to its element size", fn, i);
-  if (T < 1 || T > kMaxTokens)
-    return fail(QINT4_ERR_SHAPE, "%s: T = %lld not in [1, %d]", fn, (long long)T, kMaxTokens);
+  if (T < 1 || T > QINT4_SMALLM_MAX)
+    return fail(QINT4_ERR_SHAPE, "%s: T = %lld not in [1, %d]", fn, (long long)T, QINT4_SMALLM_MAX);
   if (T > 1 && x_dtype != QINT4_BF16)
     return fail(QINT4_ERR_DTYPE, "%s: T > 1 needs bfloat16 activations", fn);
   if (T > 1 && (ldx < ws[0].k_in || ldx % 8 != 0))
@@ -383,7 +383,9 @@ qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t
     for (int i = 0; i < n_outs; ++i) t += (ws[i].n_out + rpt - 1) / rpt;
     return t;
   };
-  const int tt = T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : 8;
+  // token-count template of a launch of nt rows
+  auto tt_for = [](int64_t nt) { return nt <= 1 ? 1 : nt <= 2 ? 2 : nt <= 4 ? 4 : nt <= 8 ? 8 : 16; };
+  const size_t yb = elem_bytes(y_dtype);
   const int64_t sbrow_b = (k_in / ws[0].group_size) * (int64_t)elem_bytes(ws[0].sb_dtype);
 
   // small-M calls with bf16 activations (stored outputs or the gate/up pair):
@@ -413,17 +415,38 @@ qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t
     p.log2_group = ilog2(ws[0].group_size);
     p.ncx = (int32_t)(k_in / 32);
     p.waves_per_wg = gemv_mfma_waves(k_in);
-    p.n_tok = (int32_t)T;
     p.ldx = (int32_t)ldx;
-    p.x = x;
     p.y_bf16 = y_dtype == QINT4_BF16;
-    hipError_t e = launch_gemv_mfma(p, tt, ws[0].group_size, sb_bf16, swiglu ? 1 : 0, tiles, stream);
-    if (e != hipSuccess) return fail(QINT4_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    // all T rows in one launch (16 tokens fill the MFMA's rows) when their
+    // staged activations fit in LDS, else blocks of 8 rows; a row's result is
+    // the same either way
+    const int blk = (T > kMaxTokens && gemv_mfma_lds_bytes(QINT4_SMALLM_MAX, ws[0].group_size, k_in,
+                                                           swiglu ? 2 : 1) > (size_t)kMaxLds)
+                        ? kMaxTokens
+                        : QINT4_SMALLM_MAX;
+    for (int64_t t0 = 0; t0 < T; t0 += blk) {
+      const int64_t nt = std::min<int64_t>(blk, T - t0);
+      p.n_tok = (int32_t)nt;
+      p.x = reinterpret_cast<const unsigned char *>(x) + (size_t)t0 * ldx * 2;
+      for (int i = 0; i < n; ++i)
+        p.m[i].y = reinterpret_cast<unsigned char *>(swiglu ? ys[0] : ys[i]) +
+                   (size_t)t0 * (swiglu ? ws[0].n_out : ws[i].n_out) * yb;
+      hipError_t e = launch_gemv_mfma(p, tt_for(nt), ws[0].group_size, sb_bf16, swiglu ? 1 : 0, tiles,
+                                      stream);
+      if (e != hipSuccess) return fail(QINT4_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    }
     return ok();
   }
 
-  // the RMSNorm partial sums take one LDS float per wave
-  const GemvPlan plan = plan_gemv(nc, n_cu, xmode, gamma ? kMaxWaves : 0, tasks_for, tt);
+  // the RMSNorm partial sums take one LDS float per wave; blocks of at most
+  // kMaxTokens rows per launch, fewer where that many staged rows do not fit
+  // in LDS (each row's result is the same whatever the block)
+  int tt = tt_for(std::min<int64_t>(T, kMaxTokens));
+  GemvPlan plan = plan_gemv(nc, n_cu, xmode, gamma ? kMaxWaves : 0, tasks_for, tt);
+  while (plan.waves == 0 && tt > 1) {
+    tt /= 2;
+    plan = plan_gemv(nc, n_cu, xmode, gamma ? kMaxWaves : 0, tasks_for, tt);
+  }
   if (plan.waves == 0)
     return fail(QINT4_ERR_SHAPE, "%s: k_in %lld with T = %lld needs more than %d bytes of LDS", fn,
                 (long long)k_in, (long long)T, kMaxLds);
@@ -447,18 +470,24 @@ qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t
   const int64_t sbrow = (k_in / ws[0].group_size) * (int64_t)elem_bytes(ws[0].sb_dtype);
   set_geometry(p, plan, nc, nc, k_in / 2, sbrow, ws[0].group_size);
   p.y_bf16 = y_dtype == QINT4_BF16;
-  p.x = x;
   p.aux = gamma;
   p.eps = eps;
-  p.n_tok = (int32_t)T;
   p.ldx = (int32_t)ldx;
   p.ids = nullptr;
   p.top_k = 1;
   p.n_experts = 1;
   p.tasks_per_slot = (int32_t)plan.n_tasks;
 
-  hipError_t e = launch_gemv(p, plan, xmode, sb_bf16, epi, stream);
-  if (e != hipSuccess) return fail(QINT4_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  for (int64_t t0 = 0; t0 < T; t0 += tt) {
+    const int64_t nt = std::min<int64_t>(tt, T - t0);
+    p.n_tok = (int32_t)nt;
+    p.x = reinterpret_cast<const unsigned char *>(x) + (size_t)t0 * ldx * elem_bytes(x_dtype);
+    for (int i = 0; i < n; ++i)
+      p.m[i].y = reinterpret_cast<unsigned char *>(swiglu ? ys[0] : ys[i]) +
+                 (size_t)t0 * (swiglu ? ws[0].n_out : ws[i].n_out) * yb;
+    hipError_t e = launch_gemv(p, plan, xmode, sb_bf16, epi, stream);
+    if (e != hipSuccess) return fail(QINT4_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  }
   return ok();
 }
 

@@ -356,6 +356,7 @@ hipError_t launch_tt(const GemvParams &p, int tt, int64_t grid, int ks, hipStrea
     case 2: return launch_mfma<SBT, CPG, 2, NS>(p, grid, ks, s);
     case 4: return launch_mfma<SBT, CPG, 4, NS>(p, grid, ks, s);
     case 8: return launch_mfma<SBT, CPG, 8, NS>(p, grid, ks, s);
+    case 16: return launch_mfma<SBT, CPG, 16, NS>(p, grid, ks, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -166,13 +166,16 @@ qint4_status qgemv_int4_multi(int32_t n, const qint4_matrix *ws, const void *x,
  * rounding of float32 sums, not bit for bit.  Other calls run the
  * qgemv_int4_multi arithmetic per row.
  *
- *   T        1..QINT4_SMALLM_MAX; T > 1 needs x_dtype QINT4_BF16
+ *   T        1..QINT4_SMALLM_MAX (16); T > 1 needs x_dtype QINT4_BF16.  Up
+ *            to 16 rows share one weight stream on the MFMA form (8 where the
+ *            16 staged rows would not fit in LDS: k_in above 4096 or so, two
+ *            launches), 8 per launch on the other form
  *   x        device [T][ldx], row t at x + t * ldx elements, 16-byte aligned;
  *            ldx >= k_in, ldx % 8 == 0 when T > 1
  *   ys       as in qgemv_int4_multi, each output [T][n_out] (row-major)
  *   other arguments as in qgemv_int4_multi
  */
-#define QINT4_SMALLM_MAX 8
+#define QINT4_SMALLM_MAX 16
 qint4_status qgemv_int4_smallm(int32_t n, const qint4_matrix *ws, const void *x,
                                int32_t x_dtype, int64_t T, int64_t ldx, void *const *ys,
                                int32_t y_dtype, int32_t epilogue, void *stream);

@@ -153,7 +153,7 @@ def _smallm(lib, m, T=4, ldx=256, x=A + 0x300000, xdt=1, y=A + 0x400000, ydt=1, 
 
 def test_smallm_validation(lib):
     assert _smallm(lib, _m(), T=0) == 2
-    assert _smallm(lib, _m(), T=9) == 2 and "T = 9" in _err(lib)
+    assert _smallm(lib, _m(), T=17) == 2 and "T = 17" in _err(lib)
     assert _smallm(lib, _m(), xdt=0) == 3                      # float32 rows need T = 1
     assert _smallm(lib, _m(), ldx=128) == 2                    # ldx < k_in
     assert _smallm(lib, _m(), ldx=260) == 2                    # ldx not a multiple of 8

@@ -1,4 +1,4 @@
-"""GPU parity of qgemv_int4_smallm (T = 1..8 activation rows) against the fp64 oracle.
+"""GPU parity of qgemv_int4_smallm (T = 1..16 activation rows) against the fp64 oracle.
 
 Each token's outputs follow the qgemv_int4 rules (per-element bf16 bound,
 relative L2 for float32); the oracle runs one GEMV per token.
@@ -28,9 +28,9 @@ def _x(rng, T, k_in, ldx=None):
     return x, dev
 
 
-@pytest.mark.parametrize("T", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 8, 9, 13, 16])
 @pytest.mark.parametrize("n_out,k_in,g", [(256, 1024, 64), (1000, 2048, 32), (96, 4096, 128),
-                                          (130, 5120, 64)])
+                                          (130, 5120, 64), (64, 640, 64)])
 def test_smallm_single_matrix(T, n_out, k_in, g):
     q = lib()
     rng = np.random.default_rng(T * 1000 + n_out + k_in)
@@ -44,7 +44,7 @@ def test_smallm_single_matrix(T, n_out, k_in, g):
         check(y[t], ref, a, "smallm T=%d t=%d" % (T, t))
 
 
-@pytest.mark.parametrize("T", [2, 4, 7])
+@pytest.mark.parametrize("T", [2, 4, 7, 11, 16])
 def test_smallm_qkv_strided_rows_f32_out(T):
     """Three projections of T shared rows; x rows strided (ldx > k_in); float32 outputs."""
     q = lib()
@@ -217,3 +217,42 @@ def test_smallm_workload_sizes_mfma_form():
     for t in range(8):
         ref, a = oracle.swiglu_pair(dl["gate"], dl["up"], x[t], "bf16", threads=oracle_threads())
         check_f32(hs[t], ref, "smallm dense gate/up T=8 t=%d" % t, a_ref=a)
+
+
+@pytest.mark.parametrize("k_in", [2048, 6144, 17408])
+def test_smallm_sixteen_rows_equal_single_rows(k_in):
+    """Row t of a T = 16 call equals a T = 1 call on row t bit for bit: all 16 rows in one
+    MFMA launch (k_in 2048), two 8-row MFMA launches (6144: 16 staged rows exceed LDS), and
+    the GEMV form (17408, not a multiple of 512 ... 8192)."""
+    q = lib()
+    rng = np.random.default_rng(k_in)
+    w = synth.draw_matrix(rng, 96, k_in, 64, "bf16")
+    x, xd = _x(rng, 16, k_in)
+    y16 = nan_like((16, 96), torch.float32)
+    q.qgemv_int4_smallm([dev_matrix(w)], xd, [y16])
+    for t in (0, 7, 8, 15):
+        y1 = nan_like((1, 96), torch.float32)
+        q.qgemv_int4_smallm([dev_matrix(w)], xd[t:t + 1].contiguous(), [y1])
+        torch.cuda.synchronize()
+        assert torch.equal(y1[0], y16[t]), t
+    for t in range(16):
+        ref, a = oracle.gemv(w, x[t], "bf16")
+        check(y16[t], ref, a, "smallm T=16 k=%d t=%d" % (k_in, t))
+
+
+@pytest.mark.parametrize("T", [9, 16])
+def test_smallm_swiglu_pair_verify_rounds(T):
+    """The gate/up pair for 9- and 16-token verify rounds (hidden 2048: one launch; 5120:
+    blocks of 8 rows)."""
+    q = lib()
+    for hidden in (2048, 5120):
+        rng = np.random.default_rng(T * 31 + hidden)
+        gate = synth.draw_matrix(rng, 384, hidden, 64, "bf16")
+        up = synth.draw_matrix(rng, 384, hidden, 64, "bf16")
+        x, xd = _x(rng, T, hidden)
+        h = nan_like((T, 384), torch.float32)
+        q.qgemv_int4_smallm([dev_matrix(gate), dev_matrix(up)], xd, [h], epilogue=q.EPI_SWIGLU_PAIR)
+        torch.cuda.synchronize()
+        for t in range(T):
+            ref, a = oracle.swiglu_pair(gate, up, x[t], "bf16")
+            check_f32(to_np64(h[t]), ref, "swiglu T=%d hidden %d t=%d" % (T, hidden, t), a_ref=a)
