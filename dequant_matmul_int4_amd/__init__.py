@@ -61,6 +61,27 @@ class CMatrix(ctypes.Structure):
                 ("reserved", ctypes.c_int32)]
 
 
+class CGemvForm(ctypes.Structure):
+    """qint4_gemv_form of include/qint4.h."""
+    _fields_ = [("kernel", ctypes.c_int32), ("tokens", ctypes.c_int32),
+                ("launches", ctypes.c_int64), ("grid", ctypes.c_int64), ("tasks", ctypes.c_int64),
+                ("waves", ctypes.c_int32), ("lanes", ctypes.c_int32),
+                ("rows_per_task", ctypes.c_int32), ("steps_per_task", ctypes.c_int32),
+                ("busiest_wave_steps", ctypes.c_int64), ("ring_depth", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+    def as_dict(self) -> dict:
+        d = {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+        d["kernel"] = "mfma" if self.kernel == FORM_MFMA else "ring"
+        return d
+
+
+FORM_RING = 0
+FORM_MFMA = 1
+CALL_QGEMV = 0
+CALL_RMS_NORM = 1
+CALL_SMALLM = 2
+
 _lib = None
 
 # (name, restype, argtypes) of every symbol include/qint4.h declares
@@ -98,6 +119,10 @@ SIGNATURES = [
                                       ctypes.POINTER(CMatrix), _P, _I64, _I64, _P, _P, _I32, _P, _P,
                                       _I32, _P, ctypes.c_size_t, _P]),
     ("quantize_int4", _I32, [_P, _I32, _I64, _I64, _I32, _I32, _P, _P, _P, _P]),
+    ("qint4_plan_qgemv", _I32, [_I32, _I32, ctypes.POINTER(ctypes.c_int64), _I64, _I32, _I32, _I64,
+                                _I32, _I32, ctypes.POINTER(CGemvForm)]),
+    ("qint4_plan_moe_gather", _I32, [_I64, _I64, _I32, _I32, _I32, _I32, _I32, _I32,
+                                     ctypes.POINTER(CGemvForm)]),
     ("qint4_status_string", ctypes.c_char_p, [_I32]),
     ("qint4_last_error", ctypes.c_char_p, []),
     ("qint4_abi_version", _I32, []),
@@ -296,7 +321,7 @@ def moe_route_gather_qgemv_int4(gate: QInt4Matrix, up: QInt4Matrix, down: QInt4M
         workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
-SMALLM_MAX = 8
+SMALLM_MAX = 16  # QINT4_SMALLM_MAX of include/qint4.h
 
 
 def qgemv_int4_smallm(ws: Sequence[QInt4Matrix], x: torch.Tensor, ys: Sequence[torch.Tensor],
@@ -464,3 +489,31 @@ __all__ = ["QInt4Matrix", "Int4Error", "qgemv_int4", "qgemv_int4_multi", "qgemv_
            "moe_prefill_qgemm_int4", "moe_prefill_qgemm_int4_workspace_bytes",
            "moe_route_gather_qgemv_int4", "moe_gather_qgemv_int4_noalloc", "NOALLOC_SCRATCH_BYTES",
            "load", "F32", "BF16", "EPI_NONE", "EPI_SWIGLU_PAIR", "LIB_PATH", "SIGNATURES"]
+
+
+_DTYPE_CODES = {"f32": 0, "bf16": 1, torch.float32: 0, torch.bfloat16: 1}
+
+
+def plan_qgemv(n_outs: Sequence[int], k_in: int, group_size: int = 64, x_dtype="bf16", T: int = 1,
+               epilogue: int = EPI_NONE, call: int = CALL_QGEMV, n_cu: int = 0) -> dict:
+    """The launch form of a qgemv_int4 / _multi (call CALL_QGEMV), rms_norm_qgemv_int4
+    (CALL_RMS_NORM) or qgemv_int4_smallm (CALL_SMALLM) call with these shapes, planned by
+    the library's own planner (host only; n_cu = 0 plans for the current device)."""
+    n = len(n_outs)
+    arr = (ctypes.c_int64 * max(n, 1))(*[int(v) for v in n_outs])
+    form = CGemvForm()
+    _check(load().qint4_plan_qgemv(int(call), n, arr, int(k_in), int(group_size),
+                                   _DTYPE_CODES[x_dtype], int(T), int(epilogue), int(n_cu),
+                                   ctypes.byref(form)))
+    return form.as_dict()
+
+
+def plan_moe_gather(hidden: int, inter: int, top_k: int, group_size: int = 64, act_dtype="bf16",
+                    routed: bool = False, residual: bool = True, n_cu: int = 0):
+    """(gate/up form, down form) of a moe_gather_qgemv_int4 (routed: moe_route_gather_qgemv_int4)
+    call with these shapes, planned by the library's own planner (host only)."""
+    forms = (CGemvForm * 2)()
+    _check(load().qint4_plan_moe_gather(int(hidden), int(inter), int(top_k), int(group_size),
+                                        _DTYPE_CODES[act_dtype], int(bool(routed)),
+                                        int(bool(residual)), int(n_cu), forms))
+    return forms[0].as_dict(), forms[1].as_dict()

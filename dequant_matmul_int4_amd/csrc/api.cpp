@@ -253,6 +253,106 @@ void set_geometry(GemvParams &p, const GemvPlan &plan, int cpr, int ncx, int64_t
   p.tasks_r = (int32_t)(plan.n_tasks % p.n_waves);
 }
 
+// Token-count template of a launch of nt activation rows.
+int tt_for(int64_t nt) { return nt <= 1 ? 1 : nt <= 2 ? 2 : nt <= 4 ? 4 : nt <= 8 ? 8 : 16; }
+
+int multi_xmode(int32_t x_dtype, bool rms) {
+  return rms ? (x_dtype == QINT4_BF16 ? XM_RMS_BF16 : XM_RMS_F32)
+             : (x_dtype == QINT4_BF16 ? XM_BF16 : XM_F32);
+}
+
+// What a qgemv_int4 / _multi / rms_norm_qgemv_int4 / _smallm call launches,
+// from its shapes alone: the calls follow it and the plan query reports it.
+struct MultiPlan {
+  bool mfma = false;  // small-M MFMA tiles of 16 rows
+  int blk = 0;        // activation rows per launch
+  int64_t tiles = 0;  // MFMA: tiles per launch
+  GemvPlan plan{};    // otherwise: the persistent GEMV plan
+};
+
+// n_outs matrices of n_out[i] rows (the gate/up pair: the gate alone) over
+// k_in columns; T activation rows of x_dtype; rms: the RMSNorm prologue;
+// batched: a qgemv_int4_smallm call.
+qint4_status plan_multi(int n_outs, const int64_t *n_out, int64_t k_in, int group_size,
+                        int32_t x_dtype, int64_t T, bool swiglu, bool rms, bool batched, int n_cu,
+                        MultiPlan *mp) {
+  *mp = MultiPlan{};
+  const int streams = swiglu ? 2 : 1;
+  if (batched && !rms && x_dtype == QINT4_BF16 && gemv_mfma_supported(k_in, group_size, streams)) {
+    int64_t tiles = 0;
+    for (int i = 0; i < n_outs; ++i) tiles += (n_out[i] + 15) / 16;
+    if (tiles > INT32_MAX) return fail(QINT4_ERR_SHAPE, "too many rows");
+    mp->mfma = true;
+    mp->tiles = tiles;
+    // all T rows in one launch (16 tokens fill the MFMA's rows) when their
+    // staged activations fit in LDS, else blocks of 8 rows; a row's result is
+    // the same either way
+    mp->blk = (T > kMaxTokens &&
+               gemv_mfma_lds_bytes(QINT4_SMALLM_MAX, group_size, k_in, streams) > (size_t)kMaxLds)
+                  ? kMaxTokens
+                  : QINT4_SMALLM_MAX;
+    return QINT4_OK;
+  }
+  const int nc = (int)(k_in / 32);
+  const int xmode = multi_xmode(x_dtype, rms);
+  auto tasks_for = [&](int rpt) {
+    int64_t t = 0;
+    for (int i = 0; i < n_outs; ++i) t += (n_out[i] + rpt - 1) / rpt;
+    return t;
+  };
+  // the RMSNorm partial sums take one LDS float per wave; blocks of at most
+  // kMaxTokens rows per launch, fewer where that many staged rows do not fit
+  // in LDS (each row's result is the same whatever the block)
+  int tt = tt_for(std::min<int64_t>(T, kMaxTokens));
+  GemvPlan plan = plan_gemv(nc, n_cu, xmode, rms ? kMaxWaves : 0, tasks_for, tt);
+  while (plan.waves == 0 && tt > 1) {
+    tt /= 2;
+    plan = plan_gemv(nc, n_cu, xmode, rms ? kMaxWaves : 0, tasks_for, tt);
+  }
+  if (plan.waves == 0)
+    return fail(QINT4_ERR_SHAPE, "k_in %lld with T = %lld needs more than %d bytes of LDS",
+                (long long)k_in, (long long)T, kMaxLds);
+  if (plan.n_tasks > INT32_MAX) return fail(QINT4_ERR_SHAPE, "too many rows");
+  mp->plan = plan;
+  mp->blk = tt;
+  return QINT4_OK;
+}
+
+// The two launches of an expert-gather decode call: gate/up of every kept
+// expert (routed: ranking the logits itself) and the down projection with the
+// weighted combine (residual: adding a residual row).
+qint4_status plan_moe(int64_t hidden, int64_t inter, int32_t top_k, int32_t act_dtype, bool routed,
+                      bool residual, int n_cu, GemvPlan *gate_up, GemvPlan *down) {
+  const int xmode_a = act_dtype == QINT4_BF16 ? XM_BF16 : XM_F32;
+  auto gu_tasks = [&](int rpt) { return (int64_t)top_k * ((inter + rpt - 1) / rpt); };
+  // routing in the gate/up launch: 16 floats of LDS hand the ranked ids to every wave
+  *gate_up = plan_gemv((int)(hidden / 32), n_cu, xmode_a, routed ? 16 : 0, gu_tasks);
+  if (gate_up->waves == 0) return fail(QINT4_ERR_SHAPE, "hidden %lld needs too much LDS", (long long)hidden);
+  auto down_tasks = [&](int rpt) { return (hidden + rpt - 1) / rpt; };
+  *down = plan_gemv((int)(inter / 32) * top_k, n_cu, XM_F32, residual ? hidden : 0, down_tasks);
+  if (down->waves == 0)
+    return fail(QINT4_ERR_SHAPE, "top_k * inter = %lld needs too much LDS", (long long)(top_k * inter));
+  if (gate_up->n_tasks > INT32_MAX || down->n_tasks > INT32_MAX)
+    return fail(QINT4_ERR_SHAPE, "too many rows");
+  return QINT4_OK;
+}
+
+// The form a planned persistent GEMV launch takes.
+void ring_form(const GemvPlan &plan, int xmode, int epi, int64_t launches, qint4_gemv_form *f) {
+  std::memset(f, 0, sizeof(*f));
+  f->kernel = QINT4_FORM_RING;
+  f->tokens = plan.tt;
+  f->launches = launches;
+  f->waves = plan.waves;
+  f->grid = plan.grid;
+  f->tasks = plan.n_tasks;
+  f->lanes = 1 << plan.log2_lpr;
+  f->rows_per_task = plan.rt * (64 >> plan.log2_lpr);
+  f->steps_per_task = plan.spt;
+  f->busiest_wave_steps = gemv_busiest_steps(plan);
+  f->ring_depth = gemv_ring_depth(plan, xmode, epi);
+}
+
 }  // namespace
 
 extern "C" {
@@ -371,28 +471,25 @@ qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t
 
   // plan
   const int nc = (int)(k_in / 32);
-  const int xmode = gamma ? (x_dtype == QINT4_BF16 ? XM_RMS_BF16 : XM_RMS_F32)
-                          : (x_dtype == QINT4_BF16 ? XM_BF16 : XM_F32);
+  const int xmode = multi_xmode(x_dtype, gamma != nullptr);
   const int epi = swiglu ? EPI_SWIGLU : EPI_STORE;
   const int sb_bf16 = ws[0].sb_dtype == QINT4_BF16;
   int n_cu = 256;
   st = check_device(&n_cu);
   if (st != QINT4_OK) return prefixed(st, fn);
-  auto tasks_for = [&](int rpt) {
-    int64_t t = 0;
-    for (int i = 0; i < n_outs; ++i) t += (ws[i].n_out + rpt - 1) / rpt;
-    return t;
-  };
-  // token-count template of a launch of nt rows
-  auto tt_for = [](int64_t nt) { return nt <= 1 ? 1 : nt <= 2 ? 2 : nt <= 4 ? 4 : nt <= 8 ? 8 : 16; };
+  int64_t n_out[QINT4_MULTI_MAX];
+  for (int i = 0; i < n_outs; ++i) n_out[i] = ws[i].n_out;
+  MultiPlan mp;
+  st = plan_multi(n_outs, n_out, k_in, ws[0].group_size, x_dtype, T, swiglu, gamma != nullptr,
+                  batched, n_cu, &mp);
+  if (st != QINT4_OK) return prefixed(st, fn);
   const size_t yb = elem_bytes(y_dtype);
   const int64_t sbrow_b = (k_in / ws[0].group_size) * (int64_t)elem_bytes(ws[0].sb_dtype);
 
   // small-M calls with bf16 activations (stored outputs or the gate/up pair):
   // MFMA tiles of 16 rows when the shape allows, for every T alike (so a T-row
   // call equals T one-row calls)
-  if (batched && !gamma && x_dtype == QINT4_BF16 &&
-      gemv_mfma_supported(k_in, ws[0].group_size, swiglu ? 2 : 1)) {
+  if (mp.mfma) {
     GemvParams p;
     std::memset(&p, 0, sizeof(p));
     p.n_mats = n;
@@ -408,7 +505,6 @@ qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t
       p.task0[i] = (int32_t)tiles;
       tiles += (ws[i].n_out + 15) / 16;
     }
-    if (tiles > INT32_MAX) return fail(QINT4_ERR_SHAPE, "%s: too many rows", fn);
     p.n_tasks = (int32_t)tiles;
     p.kwb = (int32_t)(k_in / 2);
     p.sbrow = (int32_t)sbrow_b;
@@ -417,15 +513,8 @@ qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t
     p.waves_per_wg = gemv_mfma_waves(k_in);
     p.ldx = (int32_t)ldx;
     p.y_bf16 = y_dtype == QINT4_BF16;
-    // all T rows in one launch (16 tokens fill the MFMA's rows) when their
-    // staged activations fit in LDS, else blocks of 8 rows; a row's result is
-    // the same either way
-    const int blk = (T > kMaxTokens && gemv_mfma_lds_bytes(QINT4_SMALLM_MAX, ws[0].group_size, k_in,
-                                                           swiglu ? 2 : 1) > (size_t)kMaxLds)
-                        ? kMaxTokens
-                        : QINT4_SMALLM_MAX;
-    for (int64_t t0 = 0; t0 < T; t0 += blk) {
-      const int64_t nt = std::min<int64_t>(blk, T - t0);
+    for (int64_t t0 = 0; t0 < T; t0 += mp.blk) {
+      const int64_t nt = std::min<int64_t>(mp.blk, T - t0);
       p.n_tok = (int32_t)nt;
       p.x = reinterpret_cast<const unsigned char *>(x) + (size_t)t0 * ldx * 2;
       for (int i = 0; i < n; ++i)
@@ -438,19 +527,8 @@ qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t
     return ok();
   }
 
-  // the RMSNorm partial sums take one LDS float per wave; blocks of at most
-  // kMaxTokens rows per launch, fewer where that many staged rows do not fit
-  // in LDS (each row's result is the same whatever the block)
-  int tt = tt_for(std::min<int64_t>(T, kMaxTokens));
-  GemvPlan plan = plan_gemv(nc, n_cu, xmode, gamma ? kMaxWaves : 0, tasks_for, tt);
-  while (plan.waves == 0 && tt > 1) {
-    tt /= 2;
-    plan = plan_gemv(nc, n_cu, xmode, gamma ? kMaxWaves : 0, tasks_for, tt);
-  }
-  if (plan.waves == 0)
-    return fail(QINT4_ERR_SHAPE, "%s: k_in %lld with T = %lld needs more than %d bytes of LDS", fn,
-                (long long)k_in, (long long)T, kMaxLds);
-  if (plan.n_tasks > INT32_MAX) return fail(QINT4_ERR_SHAPE, "%s: too many rows", fn);
+  const GemvPlan &plan = mp.plan;
+  const int tt = mp.blk;
   const int rpt = plan.rt * (64 >> plan.log2_lpr);
 
   GemvParams p;
@@ -615,15 +693,15 @@ qint4_status run_moe(const qint4_matrix *gate, const qint4_matrix *up, const qin
   const int sb_bf16 = gate->sb_dtype == QINT4_BF16;
   const int xmode_a = act_dtype == QINT4_BF16 ? XM_BF16 : XM_F32;
   float *h = reinterpret_cast<float *>(workspace);
+  GemvPlan plan_a, plan_b;
+  st = plan_moe(hidden, inter, top_k, act_dtype, logits != nullptr, residual != nullptr, n_cu, &plan_a,
+                &plan_b);
+  if (st != QINT4_OK) return prefixed(st, fn);
 
   // ---- launch A: gate/up of every kept expert, SwiGLU -> h[top_k][inter] (f32) ----
   {
     const int nc = (int)(hidden / 32);
-    auto tasks_for = [&](int rpt) { return (int64_t)top_k * ((inter + rpt - 1) / rpt); };
-    // routing in this launch: 16 floats of LDS hand the ranked ids to every wave
-    const GemvPlan plan = plan_gemv(nc, n_cu, xmode_a, logits ? 16 : 0, tasks_for);
-    if (plan.waves == 0)
-      return fail(QINT4_ERR_SHAPE, "%s: hidden %lld needs too much LDS", fn, (long long)hidden);
+    const GemvPlan &plan = plan_a;
     const int rpt = plan.rt * (64 >> plan.log2_lpr);
     GemvParams p;
     std::memset(&p, 0, sizeof(p));
@@ -651,12 +729,7 @@ qint4_status run_moe(const qint4_matrix *gate, const qint4_matrix *up, const qin
   {
     const int ncl = (int)(inter / 32);
     const int ncv = ncl * top_k;
-    const int64_t res_rows = residual ? hidden : 0;
-    auto tasks_for = [&](int rpt) { return (hidden + rpt - 1) / rpt; };
-    const GemvPlan plan = plan_gemv(ncv, n_cu, XM_F32, res_rows, tasks_for);
-    if (plan.waves == 0)
-      return fail(QINT4_ERR_SHAPE, "%s: top_k * inter = %lld needs too much LDS", fn,
-                  (long long)(top_k * inter));
+    const GemvPlan &plan = plan_b;
     GemvParams p;
     std::memset(&p, 0, sizeof(p));
     p.n_mats = 1;
@@ -1202,6 +1275,107 @@ qint4_status qgemm_int4_padT_multi(int32_t n, const qint4_matrix *ws, const void
   mp.sb_bf16 = ws[0].sb_dtype == QINT4_BF16;
   hipError_t e = launch_gemm(mp, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(QINT4_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Launch plans (host only)
+// ---------------------------------------------------------------------------
+
+namespace {
+
+qint4_status check_plan_shape(int64_t n_out, int64_t k_in, int32_t group_size, const char *name) {
+  if (group_size != 32 && group_size != 64 && group_size != 128)
+    return fail(QINT4_ERR_SHAPE, "%s: group_size %d not in {32, 64, 128}", name, group_size);
+  if (n_out < 1 || n_out > kMaxRows)
+    return fail(QINT4_ERR_SHAPE, "%s: n_out %lld out of range [1, 2^30]", name, (long long)n_out);
+  if (k_in < group_size || k_in > kMaxK || k_in % group_size != 0)
+    return fail(QINT4_ERR_SHAPE, "%s: k_in %lld must be a multiple of group_size %d in [%d, 2^20]",
+                name, (long long)k_in, group_size, group_size);
+  if ((size_t)n_out * (size_t)(k_in / 2) >= kMaxMatrixBytes)
+    return fail(QINT4_ERR_SHAPE, "%s: code bytes exceed the 2 GiB limit", name);
+  return QINT4_OK;
+}
+
+// CU count to plan for: n_cu itself, or (0) the current device's.
+qint4_status plan_cus(int32_t n_cu, int *out) {
+  if (n_cu < 0) return fail(QINT4_ERR_VALUE, "n_cu %d < 0", n_cu);
+  if (n_cu > 0) {
+    *out = n_cu;
+    return QINT4_OK;
+  }
+  return check_device(out);
+}
+
+}  // namespace
+
+extern "C" {
+
+qint4_status qint4_plan_qgemv(int32_t call, int32_t n, const int64_t *n_outs, int64_t k_in,
+                              int32_t group_size, int32_t x_dtype, int64_t T, int32_t epilogue,
+                              int32_t n_cu, qint4_gemv_form *form) {
+  const char *fn = "qint4_plan_qgemv";
+  if (!form || !n_outs) return fail(QINT4_ERR_NULL, "%s: form or n_outs is NULL", fn);
+  if (call != QINT4_CALL_QGEMV && call != QINT4_CALL_RMS_NORM && call != QINT4_CALL_SMALLM)
+    return fail(QINT4_ERR_VALUE, "%s: call %d invalid", fn, call);
+  if (n < 1 || n > QINT4_MULTI_MAX)
+    return fail(QINT4_ERR_SHAPE, "%s: n = %d not in [1, %d]", fn, n, QINT4_MULTI_MAX);
+  if (!valid_dtype(x_dtype)) return fail(QINT4_ERR_DTYPE, "%s: x_dtype %d invalid", fn, x_dtype);
+  if (epilogue != QINT4_EPI_NONE && epilogue != QINT4_EPI_SWIGLU_PAIR)
+    return fail(QINT4_ERR_SHAPE, "%s: epilogue %d invalid", fn, epilogue);
+  const bool swiglu = epilogue == QINT4_EPI_SWIGLU_PAIR;
+  if (swiglu && (n != 2 || n_outs[0] != n_outs[1]))
+    return fail(QINT4_ERR_SHAPE, "%s: SWIGLU_PAIR needs two matrices of equal n_out", fn);
+  qint4_status st;
+  for (int i = 0; i < n; ++i)
+    if ((st = check_plan_shape(n_outs[i], k_in, group_size, fn)) != QINT4_OK) return st;
+  const int64_t t_max = call == QINT4_CALL_SMALLM ? QINT4_SMALLM_MAX : 1;
+  if (T < 1 || T > t_max)
+    return fail(QINT4_ERR_SHAPE, "%s: T = %lld not in [1, %lld]", fn, (long long)T, (long long)t_max);
+  if (T > 1 && x_dtype != QINT4_BF16)
+    return fail(QINT4_ERR_DTYPE, "%s: T > 1 needs bfloat16 activations", fn);
+  int cus = 0;
+  if ((st = plan_cus(n_cu, &cus)) != QINT4_OK) return prefixed(st, fn);
+  const bool rms = call == QINT4_CALL_RMS_NORM;
+  MultiPlan mp;
+  st = plan_multi(swiglu ? 1 : n, n_outs, k_in, group_size, x_dtype, T, swiglu, rms,
+                  call == QINT4_CALL_SMALLM, cus, &mp);
+  if (st != QINT4_OK) return prefixed(st, fn);
+  const int64_t launches = (T + mp.blk - 1) / mp.blk;
+  if (mp.mfma) {
+    std::memset(form, 0, sizeof(*form));
+    form->kernel = QINT4_FORM_MFMA;
+    form->tokens = tt_for(std::min<int64_t>(T, mp.blk));
+    form->launches = launches;
+    form->grid = mp.tiles;
+    form->tasks = mp.tiles;
+    form->waves = gemv_mfma_waves(k_in);
+  } else {
+    ring_form(mp.plan, multi_xmode(x_dtype, rms), swiglu ? EPI_SWIGLU : EPI_STORE, launches, form);
+  }
+  return ok();
+}
+
+qint4_status qint4_plan_moe_gather(int64_t hidden, int64_t inter, int32_t top_k,
+                                   int32_t group_size, int32_t act_dtype, int32_t routed,
+                                   int32_t residual, int32_t n_cu, qint4_gemv_form *forms) {
+  const char *fn = "qint4_plan_moe_gather";
+  if (!forms) return fail(QINT4_ERR_NULL, "%s: forms is NULL", fn);
+  if (!valid_dtype(act_dtype)) return fail(QINT4_ERR_DTYPE, "%s: act_dtype %d invalid", fn, act_dtype);
+  if (top_k < 1 || top_k > QINT4_TOPK_MAX)
+    return fail(QINT4_ERR_SHAPE, "%s: top_k %d not in [1, %d]", fn, top_k, QINT4_TOPK_MAX);
+  qint4_status st;
+  if ((st = check_plan_shape(inter, hidden, group_size, fn)) != QINT4_OK) return st;
+  if ((st = check_plan_shape(hidden, inter, group_size, fn)) != QINT4_OK) return st;
+  int cus = 0;
+  if ((st = plan_cus(n_cu, &cus)) != QINT4_OK) return prefixed(st, fn);
+  GemvPlan a, b;
+  st = plan_moe(hidden, inter, top_k, act_dtype, routed != 0, residual != 0, cus, &a, &b);
+  if (st != QINT4_OK) return prefixed(st, fn);
+  ring_form(a, act_dtype == QINT4_BF16 ? XM_BF16 : XM_F32, EPI_SWIGLU, 1, &forms[0]);
+  ring_form(b, XM_F32, EPI_MOE_DOWN, 1, &forms[1]);
   return ok();
 }
 

@@ -127,6 +127,34 @@ struct GemvPlan {
 
 static_assert(sizeof(GemvParams) <= 512, "GEMV kernel arguments exceed 8 cache lines");
 
+// Launches with one-pass kernels (a ring of depth 1, 2 or 4 filled once, for
+// launches where no wave has more steps than that): the stored-output GEMVs
+// of up to 4 tokens, the one-token gate/up pair without the RMSNorm prologue
+// and the MoE down projection.  Every other launch streams its ring.
+constexpr bool gemv_has_one_pass(int epi, int tt, int xmode) {
+  return (epi == EPI_STORE && tt <= 4) || (tt == 1 && epi == EPI_SWIGLU && !xm_rms(xmode)) ||
+         epi == EPI_MOE_DOWN;
+}
+
+// Steps of the busiest wave of a planned launch (tasks are dealt round-robin).
+inline int64_t gemv_busiest_steps(const GemvPlan &plan) {
+  const int64_t nw = plan.grid * plan.waves;
+  return nw > 0 ? (plan.n_tasks + nw - 1) / nw * plan.spt : 0;
+}
+
+// Ring depth a planned launch runs with: 1, 2 or 4 (one pass) or 0 (the
+// streaming ring).  A one-pass ring holds depth * rt * streams loads per lane,
+// within kSlots.
+inline int gemv_ring_depth(const GemvPlan &plan, int xmode, int epi) {
+  if (!gemv_has_one_pass(epi, plan.tt, xmode)) return 0;
+  const int loads = plan.rt * (epi == EPI_SWIGLU ? 2 : 1);
+  const int64_t s = gemv_busiest_steps(plan);
+  if (s == 1) return 1;
+  if (s == 2 && 2 * loads <= kSlots) return 2;
+  if (s >= 3 && s <= 4 && 4 * loads <= kSlots) return 4;
+  return 0;
+}
+
 // Launch one GEMV-family kernel.  `xmode`: an XMode;
 // `sb_bf16`: scales/biases element type; `epi`: Epi.
 hipError_t launch_gemv(const GemvParams &p, const GemvPlan &plan, int xmode, int sb_bf16,

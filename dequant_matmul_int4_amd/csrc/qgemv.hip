@@ -913,28 +913,24 @@ __global__ void __launch_bounds__(TT >= 8 ? 512 : 768) qgemv_kernel(const GemvPa
   }
 }
 
-// Steps of the busiest wave of a launch.
-int64_t max_wave_steps(const GemvParams &p, const GemvPlan &plan) {
-  return (((int64_t)plan.n_tasks + p.n_waves - 1) / p.n_waves) * plan.spt;
-}
-
 template <int RT, int XM, int SBT, int EPI, int TT = 1>
 hipError_t launch_one(const GemvParams &p, const GemvPlan &plan, hipStream_t stream) {
   auto kern = qgemv_kernel<RT, XM, SBT, EPI, TT, 0>;
-  // One-pass kernels when no wave has more than 4 steps, for the launches
-  // where that happens: the stored-output GEMVs (T = 1 and the narrow small-M
-  // launches), the expert gate/up pair and the MoE down projection.
+  // the ring form the plan calls for (gemv_ring_depth is also what the
+  // library's plan query reports)
   constexpr int NS = (EPI == EPI_SWIGLU) ? 2 : 1;
-  constexpr bool one_pass = (EPI == EPI_STORE && TT <= 4) ||
-                            (TT == 1 && EPI == EPI_SWIGLU && !xm_rms(XM)) || EPI == EPI_MOE_DOWN;
-  if constexpr (one_pass) {
-    const int64_t smax = max_wave_steps(p, plan);
-    if (smax == 1) {
-      kern = qgemv_kernel<RT, XM, SBT, EPI, TT, 1>;
-    } else if (smax == 2) {
-      if constexpr (2 * RT * NS <= kSlots) kern = qgemv_kernel<RT, XM, SBT, EPI, TT, 2>;
-    } else if (smax <= 4) {
-      if constexpr (4 * RT * NS <= kSlots) kern = qgemv_kernel<RT, XM, SBT, EPI, TT, 4>;
+  if (plan.rt != RT || plan.tt != TT || plan.grid * plan.waves != p.n_waves)
+    return hipErrorInvalidValue;
+  if constexpr (gemv_has_one_pass(EPI, TT, XM)) {
+    switch (gemv_ring_depth(plan, XM, EPI)) {
+      case 1: kern = qgemv_kernel<RT, XM, SBT, EPI, TT, 1>; break;
+      case 2:
+        if constexpr (2 * RT * NS <= kSlots) kern = qgemv_kernel<RT, XM, SBT, EPI, TT, 2>;
+        break;
+      case 4:
+        if constexpr (4 * RT * NS <= kSlots) kern = qgemv_kernel<RT, XM, SBT, EPI, TT, 4>;
+        break;
+      default: break;
     }
   }
   // opt in to more than 64 KB of dynamic LDS (once per device)

@@ -487,6 +487,67 @@ qint4_status quantize_int4(const void *w, int32_t w_dtype, int64_t n_rows, int64
                            int32_t group_size, int32_t sb_dtype, uint32_t *codes, void *scales,
                            void *biases, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * Launch plans (host only)
+ * ---------------------------------------------------------------------------
+ * qint4_plan_qgemv, qint4_plan_moe_gather -- the launches a GEMV-family call
+ * with these shapes makes, planned by the same code the call runs, without
+ * touching device memory or launching anything.  For tests and tuning: a
+ * planner change that moves a shape to another kernel form shows here.
+ *
+ * The persistent GEMV kernels (QINT4_FORM_RING) deal tasks of rows_per_task
+ * rows round-robin to grid * waves waves; `lanes` lanes cover one row, and a
+ * step is one 16-byte code load per lane.  Each wave keeps a ring of loads in
+ * flight: ring_depth 0 is the streaming ring, refilled while it is consumed;
+ * 1, 2 or 4 is a ring filled once, taken when no wave has more steps than
+ * that.  The small-M MFMA kernels (QINT4_FORM_MFMA) run one 16-row tile per
+ * workgroup, its K range split over `waves` waves.  ([FFAI #9], the note on
+ * T=1 decode negative results, structural conclusion: decode is bound by the
+ * bandwidth of the expert weight gather; the plan keeps enough loads in
+ * flight on every CU.)
+ *
+ *   call       QINT4_CALL_QGEMV (qgemv_int4, qgemv_int4_multi),
+ *              QINT4_CALL_RMS_NORM (rms_norm_qgemv_int4) or
+ *              QINT4_CALL_SMALLM (qgemv_int4_smallm)
+ *   n, n_outs  the call's matrix count and the n_out of each (host array)
+ *   k_in, group_size, x_dtype, T, epilogue   as the call takes them
+ *              (T = 1 except for QINT4_CALL_SMALLM)
+ *   hidden, inter, top_k, group_size, act_dtype   as moe_gather_qgemv_int4
+ *              takes them; routed != 0: moe_route_gather_qgemv_int4 (the
+ *              gate/up launch ranks the logits); residual != 0: a residual row
+ *   n_cu       compute units to plan for; 0 = the current device's (which must
+ *              then be a gfx950 GPU)
+ *   form       host: the one form every launch of the call takes
+ *   forms      host [2]: the gate/up launch, then the down launch
+ * Returns QINT4_ERR_SHAPE / _DTYPE / _VALUE / _NULL for arguments the call
+ * itself would reject on these grounds.
+ */
+enum { QINT4_FORM_RING = 0, QINT4_FORM_MFMA = 1 };
+enum { QINT4_CALL_QGEMV = 0, QINT4_CALL_RMS_NORM = 1, QINT4_CALL_SMALLM = 2 };
+
+typedef struct qint4_gemv_form {
+  int32_t kernel;              /* QINT4_FORM_RING or QINT4_FORM_MFMA                 */
+  int32_t tokens;              /* token template: most activation rows per launch    */
+  int64_t launches;            /* launches the call makes                            */
+  int64_t grid;                /* workgroups per launch                              */
+  int64_t tasks;               /* ring: tasks; MFMA: 16-row tiles                    */
+  int32_t waves;               /* waves per workgroup                                */
+  int32_t lanes;               /* ring: lanes per row                                */
+  int32_t rows_per_task;       /* ring                                               */
+  int32_t steps_per_task;      /* ring                                               */
+  int64_t busiest_wave_steps;  /* ring: steps of the wave with the most tasks        */
+  int32_t ring_depth;          /* ring: 0 streaming; 1, 2 or 4 one pass              */
+  int32_t reserved;
+} qint4_gemv_form;
+
+qint4_status qint4_plan_qgemv(int32_t call, int32_t n, const int64_t *n_outs, int64_t k_in,
+                              int32_t group_size, int32_t x_dtype, int64_t T, int32_t epilogue,
+                              int32_t n_cu, qint4_gemv_form *form);
+
+qint4_status qint4_plan_moe_gather(int64_t hidden, int64_t inter, int32_t top_k,
+                                   int32_t group_size, int32_t act_dtype, int32_t routed,
+                                   int32_t residual, int32_t n_cu, qint4_gemv_form *forms);
+
 /* Static description of a status code. */
 const char *qint4_status_string(int32_t status);
 

@@ -1,33 +1,110 @@
-"""The ring-form case tables of test_gpu_gemv_depths agree with the planner mirror (CPU)."""
-from tests import gemv_plan
+"""The ring-form case tables of test_gpu_gemv_depths, checked on the CPU against the library's
+own planner (the host-only plan query of libqint4.so, planning for 256 CUs): a planner change
+that moves a case off the form it was chosen for fails here, without a GPU."""
+import ctypes
+
+import pytest
+
+import dequant_matmul_int4_amd as q
 from tests.test_gpu_gemv_depths import GEMV_CASES, MOE_CASES, SMALLM_CASES, SWIGLU_CASES
+
+N_CU = 256  # MI355X
+
+
+def _ring(form):
+    assert form["kernel"] == "ring"
+    return form["ring_depth"], form["busiest_wave_steps"]
 
 
 def test_case_tables_reach_every_ring_form():
     for n_out, k_in, x_dt, depth, steps in GEMV_CASES:
-        p = gemv_plan.plan(k_in // 32, x_dt, lambda rpt: -(-n_out // rpt))
-        assert (gemv_plan.ring_depth(p), gemv_plan.max_wave_steps(p)) == (depth, steps)
+        assert _ring(q.plan_qgemv([n_out], k_in, x_dtype=x_dt, n_cu=N_CU)) == (depth, steps)
     for T, n_out, k_in, depth, steps in SMALLM_CASES:
-        p = gemv_plan.plan(k_in // 32, "bf16", lambda rpt: -(-n_out // rpt), tt=T)
-        assert (gemv_plan.ring_depth(p), gemv_plan.max_wave_steps(p)) == (depth, steps)
+        f = q.plan_qgemv([n_out], k_in, T=T, call=q.CALL_SMALLM, n_cu=N_CU)
+        assert _ring(f) == (depth, steps) and f["tokens"] == T
     for n_out, k_in, depth, steps in SWIGLU_CASES:
-        p = gemv_plan.plan(k_in // 32, "bf16", lambda rpt: -(-n_out // rpt))
-        assert (gemv_plan.ring_depth(p, streams=2), gemv_plan.max_wave_steps(p)) == (depth, steps)
+        f = q.plan_qgemv([n_out, n_out], k_in, epilogue=q.EPI_SWIGLU_PAIR, n_cu=N_CU)
+        assert _ring(f) == (depth, steps)
     for hidden, inter, top_k, residual, d_gu, d_down in MOE_CASES:
-        pg = gemv_plan.plan(hidden // 32, "bf16", lambda rpt: top_k * -(-inter // rpt))
-        pd = gemv_plan.plan(top_k * inter // 32, "f32", lambda rpt: -(-hidden // rpt),
-                            residual_rows=hidden if residual else 0)
-        assert (gemv_plan.ring_depth(pg, streams=2), gemv_plan.ring_depth(pd)) == (d_gu, d_down)
+        gu, down = q.plan_moe_gather(hidden, inter, top_k, group_size=64 if inter % 64 == 0 else 32,
+                                     residual=residual, n_cu=N_CU)
+        assert (gu["ring_depth"], down["ring_depth"]) == (d_gu, d_down)
     # every form is reached: one pass 1, 2, 4 (also with a short wave) and streaming
     assert {c[3] for c in GEMV_CASES} == {0, 1, 2, 4}
     assert {c[4] for c in GEMV_CASES if c[3] == 4} == {3, 4}
     assert {c[3] for c in SMALLM_CASES} == {0, 1, 2, 4}
-    assert all(c[2] % 512 for c in SMALLM_CASES)  # off the small-M MFMA route
     assert {c[2] for c in SWIGLU_CASES} == {0, 1, 2, 4}
     assert {c[4] for c in MOE_CASES} == {0, 1, 2} and {c[5] for c in MOE_CASES} == {0, 1, 2, 4}
 
 
-def test_mirror_plans_the_qkv_projection_as_one_task_per_wave():
-    """q/k/v of a 4096 activation (6144 rows): 12 waves per CU, 2 rows per task, 2 steps."""
-    p = gemv_plan.plan(128, "bf16", lambda rpt: sum(-(-n // rpt) for n in (4096, 1024, 1024)))
-    assert p[:4] == (12, 2, 64, 2) and gemv_plan.ring_depth(p) == 2
+def test_qkv_projection_is_one_task_pair_per_wave():
+    """q/k/v of a 4096 activation (6144 rows): 12 waves per CU, 64 lanes a row, 2 rows per task,
+    one task per wave, so a one-pass ring of depth 2."""
+    f = q.plan_qgemv([4096, 1024, 1024], 4096, n_cu=N_CU)
+    assert (f["waves"], f["lanes"], f["rows_per_task"], f["steps_per_task"]) == (12, 64, 2, 2)
+    assert f["grid"] == N_CU and f["ring_depth"] == 2 and f["launches"] == 1
+
+
+@pytest.mark.parametrize("n_outs,k_in,x_dt,epi,call,T", [
+    ([17408, 17408], 5120, "bf16", q.EPI_SWIGLU_PAIR, q.CALL_QGEMV, 1),
+    ([5120], 17408, "f32", q.EPI_NONE, q.CALL_QGEMV, 1),
+    ([4096, 1024, 1024], 4096, "bf16", q.EPI_NONE, q.CALL_RMS_NORM, 1),
+    ([4096, 1024, 1024], 4096, "f32", q.EPI_NONE, q.CALL_RMS_NORM, 1),
+    ([5000], 2304, "bf16", q.EPI_NONE, q.CALL_SMALLM, 13),
+    ([3, 9, 100, 31, 2, 7, 1, 64], 192, "bf16", q.EPI_NONE, q.CALL_QGEMV, 1),
+])
+def test_ring_plans_cover_every_row_and_chunk(n_outs, k_in, x_dt, epi, call, T):
+    """Whatever the planner picks: tasks cover every row, lanes x steps cover every 32-code
+    chunk of a row, the grid fits the CUs, the waves fit a workgroup, and token blocks cover T."""
+    f = q.plan_qgemv(n_outs, k_in, x_dtype=x_dt, T=T, epilogue=epi, call=call, n_cu=N_CU)
+    assert f["kernel"] == "ring"
+    rows = n_outs[:1] if epi == q.EPI_SWIGLU_PAIR else n_outs
+    assert f["tasks"] == sum(-(-n // f["rows_per_task"]) for n in rows)
+    assert f["rows_per_task"] * f["lanes"] in (64, 128)
+    assert f["lanes"] * f["steps_per_task"] >= k_in // 32 > f["lanes"] * (f["steps_per_task"] - 1)
+    assert 1 <= f["grid"] <= N_CU and 1 <= f["waves"] <= 12
+    assert f["busiest_wave_steps"] == -(-f["tasks"] // (f["grid"] * f["waves"])) * f["steps_per_task"]
+    assert f["launches"] * f["tokens"] >= T > (f["launches"] - 1) * f["tokens"]
+    assert f["ring_depth"] in (0, 1, 2, 4)
+    if f["ring_depth"]:
+        assert f["busiest_wave_steps"] <= f["ring_depth"]
+
+
+def test_smallm_mfma_form():
+    """k_in a multiple of 512 (at most 16 K slices of 512) with bf16 activations: the small-M
+    call takes 16-row MFMA tiles, all 16 tokens in one launch where their staged rows fit in LDS,
+    else blocks of 8.  Wider rows (the 17408-column down projection) take the GEMV rings in
+    token blocks whose staged rows fit."""
+    f = q.plan_qgemv([4096, 1024, 1024], 4096, T=16, call=q.CALL_SMALLM, n_cu=N_CU)
+    assert (f["kernel"], f["tokens"], f["launches"], f["tasks"]) == ("mfma", 16, 1, 6144 // 16)
+    f = q.plan_qgemv([17408], 5120, T=16, call=q.CALL_SMALLM, n_cu=N_CU)
+    assert (f["kernel"], f["tokens"], f["launches"], f["waves"]) == ("mfma", 8, 2, 10)
+    f = q.plan_qgemv([17408], 5120, T=1, call=q.CALL_SMALLM, n_cu=N_CU)
+    assert (f["kernel"], f["tokens"], f["launches"]) == ("mfma", 1, 1)
+    f = q.plan_qgemv([5120], 17408, T=16, call=q.CALL_SMALLM, n_cu=N_CU)
+    assert (f["kernel"], f["tokens"], f["launches"]) == ("ring", 4, 4)
+
+
+def test_plan_query_rejects_what_the_calls_reject():
+    lib = q.load()
+    form = q.CGemvForm()
+    n1 = (ctypes.c_int64 * 2)(64, 64)
+    bad = [
+        (q.CALL_QGEMV, 1, n1, 100, 64, 1, 1, 0, 256),     # k_in not a multiple of group_size
+        (q.CALL_QGEMV, 1, n1, 128, 48, 1, 1, 0, 256),     # group_size
+        (q.CALL_QGEMV, 0, n1, 128, 64, 1, 1, 0, 256),     # n
+        (q.CALL_QGEMV, 1, n1, 128, 64, 1, 2, 0, 256),     # T > 1 outside small-M
+        (q.CALL_SMALLM, 1, n1, 128, 64, 1, 17, 0, 256),   # T beyond the small-M limit
+        (q.CALL_SMALLM, 1, n1, 128, 64, 0, 2, 0, 256),    # T > 1 with float32 activations
+        (q.CALL_QGEMV, 1, n1, 128, 64, 1, 1, 1, 256),     # SWIGLU_PAIR with one matrix
+        (q.CALL_QGEMV, 1, n1, 128, 64, 2, 1, 0, 256),     # dtype
+        (7, 1, n1, 128, 64, 1, 1, 0, 256),                # call
+        (q.CALL_QGEMV, 1, n1, 128, 64, 1, 1, 0, -1),      # n_cu
+    ]
+    for args in bad:
+        assert lib.qint4_plan_qgemv(*args, ctypes.byref(form)) != 0, args
+    assert lib.qint4_plan_qgemv(q.CALL_QGEMV, 1, n1, 128, 64, 1, 1, 0, 256, None) == 1
+    forms = (q.CGemvForm * 2)()
+    assert lib.qint4_plan_moe_gather(2048, 768, 9, 64, 1, 0, 1, 256, forms) != 0    # top_k
+    assert lib.qint4_plan_moe_gather(2048, 100, 8, 64, 1, 0, 1, 256, forms) != 0    # inter
+    assert lib.qint4_plan_moe_gather(2048, 768, 8, 64, 1, 0, 1, 256, forms) == 0

@@ -1,15 +1,14 @@
 """GPU parity of every GEMV ring form: one pass with depth 1, 2 and 4 (including a wave that
 has fewer steps than its ring) and the streaming ring, for each launch that has them.
 
-Shapes are picked with the planner mirror in tests/gemv_plan.py; each case asserts the depth
-it was chosen for, so a planner change that moves a shape off its form is seen here."""
+Each case asserts, through the library's host-only plan query for the device it runs on, the
+form it was chosen for (tests/test_gemv_plan.py checks the same tables on the CPU for 256 CUs)."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import synth
-from tests import gemv_plan
 from tests.gpu_common import check, dev_matrix, lib, nan_like, oracle_threads, require_gpu
 
 pytestmark = pytest.mark.gpu
@@ -37,9 +36,9 @@ GEMV_CASES = [
 
 @pytest.mark.parametrize("n_out,k_in,x_dt,depth,steps", GEMV_CASES)
 def test_gemv_ring_forms(n_out, k_in, x_dt, depth, steps):
-    p = gemv_plan.plan(k_in // 32, x_dt, lambda rpt: -(-n_out // rpt))
-    assert (gemv_plan.ring_depth(p), gemv_plan.max_wave_steps(p)) == (depth, steps)
     q = lib()
+    f = q.plan_qgemv([n_out], k_in, x_dtype=x_dt)
+    assert (f["kernel"], f["ring_depth"], f["busiest_wave_steps"]) == ("ring", depth, steps)
     rng = np.random.default_rng(n_out + 7 * k_in)
     w = synth.draw_matrix(rng, n_out, k_in, 64, "bf16")
     x = synth.draw_activation(rng, (k_in,), x_dt)
@@ -62,9 +61,9 @@ SMALLM_CASES = [
 
 @pytest.mark.parametrize("T,n_out,k_in,depth,steps", SMALLM_CASES)
 def test_smallm_ring_forms(T, n_out, k_in, depth, steps):
-    p = gemv_plan.plan(k_in // 32, "bf16", lambda rpt: -(-n_out // rpt), tt=T)
-    assert (gemv_plan.ring_depth(p), gemv_plan.max_wave_steps(p)) == (depth, steps)
     q = lib()
+    f = q.plan_qgemv([n_out], k_in, T=T, call=q.CALL_SMALLM)
+    assert (f["kernel"], f["ring_depth"], f["busiest_wave_steps"]) == ("ring", depth, steps)
     rng = np.random.default_rng(T * 1000 + n_out)
     w = synth.draw_matrix(rng, n_out, k_in, 64, "bf16")
     x = synth.draw_activation(rng, (T, k_in), "bf16")
@@ -87,9 +86,9 @@ SWIGLU_CASES = [
 
 @pytest.mark.parametrize("n_out,k_in,depth,steps", SWIGLU_CASES)
 def test_swiglu_ring_forms(n_out, k_in, depth, steps):
-    p = gemv_plan.plan(k_in // 32, "bf16", lambda rpt: -(-n_out // rpt))
-    assert (gemv_plan.ring_depth(p, streams=2), gemv_plan.max_wave_steps(p)) == (depth, steps)
     q = lib()
+    f = q.plan_qgemv([n_out, n_out], k_in, epilogue=q.EPI_SWIGLU_PAIR)
+    assert (f["kernel"], f["ring_depth"], f["busiest_wave_steps"]) == ("ring", depth, steps)
     rng = np.random.default_rng(n_out * 3 + k_in)
     gate = synth.draw_matrix(rng, n_out, k_in, 64, "bf16")
     up = synth.draw_matrix(rng, n_out, k_in, 64, "bf16")
@@ -115,11 +114,10 @@ MOE_CASES = [
 
 @pytest.mark.parametrize("hidden,inter,top_k,residual,d_gu,d_down", MOE_CASES)
 def test_moe_ring_forms(hidden, inter, top_k, residual, d_gu, d_down):
-    pg = gemv_plan.plan(hidden // 32, "bf16", lambda rpt: top_k * -(-inter // rpt))
-    pd = gemv_plan.plan(top_k * inter // 32, "f32", lambda rpt: -(-hidden // rpt),
-                        residual_rows=hidden if residual else 0)
-    assert (gemv_plan.ring_depth(pg, streams=2), gemv_plan.ring_depth(pd)) == (d_gu, d_down)
     q = lib()
+    gu, dn = q.plan_moe_gather(hidden, inter, top_k, group_size=64 if inter % 64 == 0 else 32,
+                               residual=residual)
+    assert (gu["ring_depth"], dn["ring_depth"]) == (d_gu, d_down)
     d = synth.moe_layer(seed=hidden + inter + top_k, n_experts=16, hidden=hidden, inter=inter,
                         group_size=64 if inter % 64 == 0 else 32)
     ids, wts = oracle.router_topk(d["logits"][0], top_k)
