@@ -27,7 +27,7 @@ Workloads (default: dense):
   qkv      q/k/v projections of one bf16 4096-vector (4096/1024/1024 rows), one launch
   qkvprefill  the q/k/v projections of --T rows in one multi-matrix GEMM launch
   rmsqkv   the same launch with the RMSNorm of the input fused in front
-  smallm   the q/k/v set for --T tokens (1..8, default 4) in one launch
+  smallm   the q/k/v set for --T tokens (1..16, default 4) in one call
   dense    gate/up 5120->17408 with SwiGLU (fp32 h), then down 17408->5120
   moe      top-8 of 128 experts, hidden 2048, inter 768, weighted combine + residual;
            each step routes its token's logits inside the gate/up launch (--router gpu: with the
@@ -775,6 +775,11 @@ def gemm_ceiling(torch, timer, T, K_, W_steps):
 
     def fn(i):
         torch.matmul(a, ws[i % 6].t(), out=y)
+    # one eager call first: hipBLASLt sets itself up on its first product, which
+    # is not allowed inside a graph capture
+    with torch.cuda.stream(timer.stream):
+        fn(0)
+    torch.cuda.synchronize()
     ms, _ = timer.ms_per_step(fn, K_, W_steps)
     del ws
     return {"us": ms * 1e3, "TFLOPs": 2.0 * T * 5120 * 17408 / (ms * 1e-3) / 1e12,
