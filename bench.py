@@ -58,17 +58,38 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 POOL_BYTES = 1 << 30
 
-# HBM traffic per step from rocprofv3 counters (one pass with FETCH_SIZE, one
-# with WRITE_SIZE, KiB per dispatch, summed over the step's library kernels).
-# Scale factors from the copy workload (256 MiB read + 256 MiB written per
-# dispatch): FETCH_SIZE read 131,087 KiB -> x2.000; WRITE_SIZE 262,144 KiB -> x1.000.
-# Each figure is valid only for the sources it was taken with: `hash` covers the
-# listed kernel sources (comments and whitespace excluded), and any change to
-# them makes the figure null until it is measured again.
-TRAFFIC_FETCH_SCALE = 262144.0 / 131087.2
+# HBM traffic from rocprofv3 counters (one pass with FETCH_SIZE, one with
+# WRITE_SIZE, KiB per dispatch, calls launched one by one with --no-graph) for
+# the unit the roofline describes: the dominant kernel where a step has several
+# timed parts (dense: the gate/up launch), else the step's library kernels
+# summed.  Scale factors from the copy workload (256 MiB read + 256 MiB written
+# per dispatch): FETCH_SIZE read 131,084 KiB -> x2.000; WRITE_SIZE 262,144 KiB
+# -> x1.000.  Each figure is valid only for the sources it was taken with: the
+# hash covers the listed kernel sources (comments and whitespace excluded), and
+# any change to them makes the figure null until it is measured again.
+TRAFFIC_FETCH_SCALE = 262144.0 / 131084.1
 TRAFFIC_WRITE_SCALE = 1.0
 GEMV_SRC = ("kernels.h", "api.cpp", "qgemv.hip", "topk_wave.h")
-TRAFFIC = {  # workload: (sources, source hash, FETCH_SIZE KiB, WRITE_SIZE KiB) per step, unscaled
+SMALLM_SRC = ("kernels.h", "api.cpp", "qgemv_mfma.hip")
+STREAM_SRC = ("kernels.h", "api.cpp", "qgemm_stream.hip")
+GEMM_SRC = ("kernels.h", "api.cpp", "qgemm.hip")
+MOEP_SRC = ("kernels.h", "api.cpp", "moe_prefill.hip", "router.hip", "topk_wave.h")
+QUANT_SRC = ("kernels.h", "api.cpp", "quant.hip")
+TRAFFIC = {  # workload: (sources, source hash, FETCH_SIZE KiB, WRITE_SIZE KiB), unscaled
+    "dense_ffn_t1": (GEMV_SRC, "5a99be7ac70382f9", 49304.9, 112.6),
+    "moe_top8_t1": (GEMV_SRC, "5a99be7ac70382f9", 10843.3, 32.1),
+    "qkv_multi_t1": (GEMV_SRC, "5a99be7ac70382f9", 7003.6, 16.0),
+    "rms_qkv_multi_t1": (GEMV_SRC, "5a99be7ac70382f9", 7056.1, 16.0),
+    "qkv_smallm_T4": (SMALLM_SRC, "a99060455c95cd70", 7087.2, 48.0),
+    "qkv_smallm_T16": (SMALLM_SRC, "a99060455c95cd70", 7499.1, 192.0),
+    "prefill_gemm_T32": (STREAM_SRC, "d14b9cce6839ce0f", 36096.5, 7616.0),
+    "prefill_gemm_T256": (GEMM_SRC, "c9b865bd804e8ed7", 34845.6, 8704.0),
+    "prefill_gemm_T1024": (GEMM_SRC, "c9b865bd804e8ed7", 138838.3, 34816.0),
+    "prefill_gemm_T4096": (GEMM_SRC, "c9b865bd804e8ed7", 514743.3, 139858.2),
+    "qkv_prefill_T256": (GEMM_SRC, "c9b865bd804e8ed7", 12470.0, 1849.3),
+    "qkv_prefill_T4096": (GEMM_SRC, "c9b865bd804e8ed7", 73278.5, 29651.0),
+    "moe_prefill_top8_T256": (MOEP_SRC, "cfc7140df3e3865a", 188062.5, 23585.5),
+    "quantize_17408x5120_f32_g64": (QUANT_SRC, "c37b41eaf454e8b1", 174101.4, 48960.0),
 }
 
 

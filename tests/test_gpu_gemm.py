@@ -104,3 +104,24 @@ def test_prefill_workload_full(T):
     y = _gemm(d["w"], d["X"], torch.bfloat16)
     rel = check_gemm(y, Y_ref, A_ref, "prefill T=%d" % T)
     print("prefill T=%d max rel %.3e" % (T, rel))
+
+
+@pytest.mark.parametrize("T,n_out,k_in,g,sbd,y_dt", [
+    (2049, 32, 64, 64, "bf16", torch.bfloat16),
+    (2100, 544, 96, 32, "f32", torch.float32),
+    (2200, 1056, 320, 64, "bf16", torch.float32),
+    (4100, 96, 1024, 128, "bf16", torch.bfloat16),
+    (2049, 512, 640, 64, "f32", torch.bfloat16),
+])
+def test_gemm_long_prompt_full(T, n_out, k_in, g, sbd, y_dt):
+    """Long prompts (the 128 x 512-tile form): ragged T, n_out not a multiple of the tile,
+    k_in not a multiple of 64, both scale dtypes and output dtypes; every output."""
+    rng = np.random.default_rng(T + 3 * n_out + k_in)
+    w = synth.draw_matrix(rng, n_out, k_in, g, sbd)
+    X = synth.draw_activation(rng, (T, k_in), "bf16")
+    y = _gemm(w, X, y_dt)
+    Y_ref, A_ref = oracle.gemm(w, X, "bf16", round_w=True, threads=oracle_threads())
+    slack, n_sites = gemm_rounding_slack(w, X)
+    if sbd == "bf16":
+        assert n_sites == 0
+    check_gemm(y, Y_ref, A_ref, "gemm long %d/%d/%d %s" % (T, n_out, k_in, sbd), slack=slack)

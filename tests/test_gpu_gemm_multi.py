@@ -32,7 +32,7 @@ def _run(ws, X, y_dt=torch.bfloat16, ldys=None, fill=float("nan")):
     return bufs
 
 
-@pytest.mark.parametrize("T", [1, 17, 64, 65, 100, 257, 300])
+@pytest.mark.parametrize("T", [1, 17, 64, 65, 100, 257, 300, 2049])
 @pytest.mark.parametrize("g,sbd,y_dt", [(64, "bf16", torch.bfloat16), (32, "f32", torch.float32),
                                         (128, "bf16", torch.float32)])
 def test_multi_small_ragged(T, g, sbd, y_dt):
@@ -50,11 +50,12 @@ def test_multi_small_ragged(T, g, sbd, y_dt):
         check_gemm(y, Y, A, "multi T=%d m=%d" % (T, i), slack=slack)
 
 
-def test_multi_canaries_strides_and_eight_matrices():
+@pytest.mark.parametrize("T", [130, 2050])
+def test_multi_canaries_strides_and_eight_matrices(T):
     """Eight matrices with row strides above n_out: columns past n_out keep their canary."""
-    rng = np.random.default_rng(501)
-    k_in, T = 256, 130
-    outs = [32, 64, 256, 32, 96, 512, 32, 160]
+    rng = np.random.default_rng(501 + T)
+    k_in = 256
+    outs = [32, 64, 256, 32, 96, 544, 32, 160]
     ws = [synth.draw_matrix(rng, n, k_in, 64, "bf16") for n in outs]
     X = synth.draw_activation(rng, (T, k_in), "bf16")
     ldys = [n + 24 for n in outs]
@@ -65,16 +66,17 @@ def test_multi_canaries_strides_and_eight_matrices():
         assert torch.all(y[:, w.n_out:] == 5.0)
 
 
-def test_multi_equals_single_calls_bit_for_bit():
+@pytest.mark.parametrize("T", [200, 2100])
+def test_multi_equals_single_calls_bit_for_bit(T):
     """For T > 64 each output equals qgemm_int4_padT of its matrix alone (same tiles)."""
     q = lib()
     rng = np.random.default_rng(502)
     ws = [synth.draw_matrix(rng, n, 1024, 64, "bf16") for n in (256, 128, 128)]
-    X = synth.draw_activation(rng, (200, 1024), "bf16")
+    X = synth.draw_activation(rng, (T, 1024), "bf16")
     ys = _run(ws, X, torch.float32)
     xs = synth.to_torch(X, "bf16")
     for w, y in zip(ws, ys):
-        y1 = torch.full((200, w.n_out), float("nan"), dtype=torch.float32, device="cuda")
+        y1 = torch.full((T, w.n_out), float("nan"), dtype=torch.float32, device="cuda")
         q.qgemm_int4_padT(dev_matrix(w), xs, y1)
         torch.cuda.synchronize()
         assert torch.equal(y, y1)
