@@ -419,7 +419,7 @@ class MoE(Workload):
         self.x = torch.randn(H, device="cuda").to(torch.bfloat16)
         self.res = torch.randn(H, device="cuda").to(torch.bfloat16)
         self.out = torch.empty(H, device="cuda", dtype=torch.bfloat16)
-        self.ws = torch.empty(q.moe_gather_qgemv_int4_workspace_bytes(I, K), dtype=torch.uint8,
+        self.ws = torch.empty(q.moe_gather_qgemv_int4_workspace_bytes(stacks[0][2], K), dtype=torch.uint8,
                               device="cuda")
         per_expert = (I * H // 2 + 2 * 2 * I * H // 64)
         self.wb = 3 * K * per_expert            # gate + up + down of the 8 kept experts

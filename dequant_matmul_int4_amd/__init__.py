@@ -96,7 +96,7 @@ SIGNATURES = [
                                  ctypes.POINTER(ctypes.c_void_p), _I32, _I32, _P]),
     ("rms_norm_qgemv_int4", _I32, [_I32, ctypes.POINTER(CMatrix), _P, _I32, _P, ctypes.c_float,
                                    ctypes.POINTER(ctypes.c_void_p), _I32, _I32, _P]),
-    ("moe_gather_qgemv_int4_workspace_bytes", ctypes.c_size_t, [_I64, _I32]),
+    ("moe_gather_qgemv_int4_workspace_bytes", ctypes.c_size_t, [ctypes.POINTER(CMatrix), _I32]),
     ("moe_gather_qgemv_int4", _I32, [ctypes.POINTER(CMatrix), ctypes.POINTER(CMatrix),
                                      ctypes.POINTER(CMatrix), _P, _P, _P, _I32, _P, _P, _I32,
                                      _P, ctypes.c_size_t, _P]),
@@ -348,8 +348,10 @@ def qgemv_int4_smallm(ws: Sequence[QInt4Matrix], x: torch.Tensor, ys: Sequence[t
                                     y_dt, int(epilogue), _stream(stream)))
 
 
-def moe_gather_qgemv_int4_workspace_bytes(inter: int, top_k: int) -> int:
-    return int(load().moe_gather_qgemv_int4_workspace_bytes(int(inter), int(top_k)))
+def moe_gather_qgemv_int4_workspace_bytes(down: QInt4Matrix, top_k: int) -> int:
+    """Workspace bytes of a moe_gather_qgemv_int4 call with this down stack and top_k."""
+    m = down.c()
+    return int(load().moe_gather_qgemv_int4_workspace_bytes(ctypes.byref(m), int(top_k)))
 
 
 def moe_gather_qgemv_int4(gate: QInt4Matrix, up: QInt4Matrix, down: QInt4Matrix,
@@ -359,7 +361,7 @@ def moe_gather_qgemv_int4(gate: QInt4Matrix, up: QInt4Matrix, down: QInt4Matrix,
     """out = residual + sum_k wts[k] * down[ids[k]] (silu(gate[ids[k]] x) * up[ids[k]] x).
 
     ids: int32/uint32 [top_k] on the device; wts: float32 [top_k]; workspace: any
-    device tensor of at least moe_gather_qgemv_int4_workspace_bytes(inter, top_k) bytes.
+    device tensor of at least moe_gather_qgemv_int4_workspace_bytes(down, top_k) bytes.
     """
     if ids.dtype not in (torch.int32, torch.uint32):
         raise TypeError("ids must be int32/uint32")

@@ -96,6 +96,13 @@ qint4_status check_matrix_size(const qint4_matrix *w, const char *name) {
 constexpr int64_t kMaxK = 1 << 20;
 constexpr int64_t kMaxRows = (int64_t)1 << 30;
 
+// Workspace of an expert-gather decode call: the float32 SwiGLU
+// intermediates, inter of them per kept expert (0 for sizes it rejects).
+size_t moe_ws_bytes(int64_t inter, int32_t top_k) {
+  if (inter < 1 || inter > kMaxK || top_k < 1 || top_k > QINT4_TOPK_MAX) return 0;
+  return (size_t)top_k * (size_t)inter * sizeof(float);
+}
+
 qint4_status check_matrix(const qint4_matrix *w, const char *name, bool experts_ok) {
   if (!w) return fail(QINT4_ERR_NULL, "%s: matrix descriptor is NULL", name);
   if (!w->codes || !w->scales || !w->biases)
@@ -605,9 +612,8 @@ qint4_status qgemv_int4_smallm(int32_t n, const qint4_matrix *ws, const void *x,
                    true);
 }
 
-size_t moe_gather_qgemv_int4_workspace_bytes(int64_t inter, int32_t top_k) {
-  if (inter < 1 || inter > kMaxK || top_k < 1 || top_k > QINT4_TOPK_MAX) return 0;
-  return (size_t)top_k * (size_t)inter * sizeof(float);
+size_t moe_gather_qgemv_int4_workspace_bytes(const qint4_matrix *down, int32_t top_k) {
+  return down ? moe_ws_bytes(down->k_in, top_k) : 0;
 }
 
 }  // extern "C"
@@ -659,7 +665,7 @@ qint4_status run_moe(const qint4_matrix *gate, const qint4_matrix *up, const qin
     if (!aligned(logits, elem_bytes(logits_dtype)))
       return fail(QINT4_ERR_ALIGN, "%s: logits not aligned to its element size", fn);
   }
-  const size_t need = moe_gather_qgemv_int4_workspace_bytes(inter, top_k);
+  const size_t need = moe_ws_bytes(inter, top_k);
   if (!workspace || workspace_bytes < need)
     return fail(QINT4_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn,
                 workspace ? workspace_bytes : (size_t)0, need);
@@ -817,7 +823,7 @@ qint4_status moe_gather_qgemv_int4_noalloc(const qint4_matrix *gate, const qint4
                                            void *stream) {
   const char *fn = "moe_gather_qgemv_int4_noalloc";
   if (!gate) return fail(QINT4_ERR_NULL, "%s: gate is NULL", fn);
-  const size_t need = moe_gather_qgemv_int4_workspace_bytes(gate->n_out, top_k);
+  const size_t need = moe_ws_bytes(gate->n_out, top_k);
   if (need > QINT4_NOALLOC_SCRATCH_BYTES)
     return fail(QINT4_ERR_WORKSPACE,
                 "%s: top_k %d x inter %lld needs %zu bytes of scratch, more than the %u the "

@@ -210,11 +210,13 @@ qint4_status rms_norm_qgemv_int4(int32_t n, const qint4_matrix *ws, const void *
                                  void *stream);
 
 /*
- * Bytes of device workspace one moe_gather_qgemv_int4 call needs for an
- * expert intermediate width `inter` and `top_k` kept experts (the float32
- * SwiGLU intermediates, one row per kept expert).  0 for invalid sizes.
+ * Bytes of device workspace one moe_gather_qgemv_int4 call needs with the
+ * down-projection stack `down` (host descriptor; only its k_in, the expert
+ * intermediate width inter, is read) and `top_k` kept experts: the float32
+ * SwiGLU intermediates, one row of inter per kept expert.  0 when down is NULL
+ * or its k_in or top_k is outside the range the call accepts.
  */
-size_t moe_gather_qgemv_int4_workspace_bytes(int64_t inter, int32_t top_k);
+size_t moe_gather_qgemv_int4_workspace_bytes(const qint4_matrix *down, int32_t top_k);
 
 /*
  * moe_gather_qgemv_int4 -- one token through a top-K mixture of experts.
@@ -240,7 +242,7 @@ size_t moe_gather_qgemv_int4_workspace_bytes(int64_t inter, int32_t top_k);
  *   out       device [hidden], dtype act_dtype; every element overwritten
  *   act_dtype QINT4_F32 or QINT4_BF16
  *   workspace device scratch of at least
- *             moe_gather_qgemv_int4_workspace_bytes(inter, top_k) bytes,
+ *             moe_gather_qgemv_int4_workspace_bytes(down, top_k) bytes,
  *             16-byte aligned; contents on entry are ignored, contents on
  *             return are unspecified.  One workspace per concurrent call.
  * Two kernel launches on `stream` (gate/up + SwiGLU, then down + combine).

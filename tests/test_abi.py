@@ -103,15 +103,17 @@ def _moe(lib, top_k=8, ws_bytes=None, ws=A + 0x900000, e=(16, 16, 16), out=A + 0
     gate = _m(A, A + 0x10000, A + 0x20000, inter, hidden, 64, e[0], 1)
     up = _m(A + 0x100000, A + 0x110000, A + 0x120000, inter, hidden, 64, e[1], 1)
     down = _m(A + 0x200000, A + 0x210000, A + 0x220000, hidden, inter, 64, e[2], 1)
-    need = lib.moe_gather_qgemv_int4_workspace_bytes(inter, max(1, min(top_k, 8)))
+    need = lib.moe_gather_qgemv_int4_workspace_bytes(ctypes.byref(down), max(1, min(top_k, 8)))
     return lib.moe_gather_qgemv_int4(ctypes.byref(gate), ctypes.byref(up), ctypes.byref(down),
                                      A + 0x300000, A + 0x310000, A + 0x320000, top_k, residual, out,
                                      1, ws, need if ws_bytes is None else ws_bytes, None)
 
 
 def test_moe_validation(lib):
-    assert lib.moe_gather_qgemv_int4_workspace_bytes(768, 8) == 8 * 768 * 4
-    assert lib.moe_gather_qgemv_int4_workspace_bytes(768, 9) == 0
+    down = _m(A, A + 0x10000, A + 0x20000, 2048, 768, 64, 128, 1)
+    assert lib.moe_gather_qgemv_int4_workspace_bytes(ctypes.byref(down), 8) == 8 * 768 * 4
+    assert lib.moe_gather_qgemv_int4_workspace_bytes(ctypes.byref(down), 9) == 0
+    assert lib.moe_gather_qgemv_int4_workspace_bytes(None, 8) == 0
     assert _moe(lib, top_k=0) == 2
     assert _moe(lib, top_k=9) == 2
     assert _moe(lib, e=(16, 16, 8)) == 2

@@ -114,7 +114,7 @@ def test_moe_scalar_fma_chain_is_linear_in_slot_weights():
 
     def run(ids, wts):
         out = torch.full((512,), float("nan"), dtype=torch.bfloat16, device="cuda")
-        ws = torch.empty(q.moe_gather_qgemv_int4_workspace_bytes(256, len(ids)), dtype=torch.uint8,
+        ws = torch.empty(q.moe_gather_qgemv_int4_workspace_bytes(d, len(ids)), dtype=torch.uint8,
                          device="cuda")
         q.moe_gather_qgemv_int4(g, u, d, x, torch.tensor(ids, dtype=torch.int32, device="cuda"),
                                 wts, out, ws)

@@ -127,7 +127,7 @@ def test_moe_ring_forms(hidden, inter, top_k, residual, d_gu, d_down):
     x = synth.to_torch(d["x"][0], "bf16")
     ids_t = torch.tensor(np.asarray(ids, dtype=np.int64).astype(np.int32), device="cuda")
     wts_t = torch.tensor(wts32, device="cuda")
-    ws = torch.empty(q.moe_gather_qgemv_int4_workspace_bytes(inter, top_k), dtype=torch.uint8,
+    ws = torch.empty(q.moe_gather_qgemv_int4_workspace_bytes(down, top_k), dtype=torch.uint8,
                      device="cuda")
     out = nan_like(hidden, torch.bfloat16)
     q.moe_gather_qgemv_int4(gate, up, down, x, ids_t, wts_t, out, ws,

@@ -24,7 +24,7 @@ def _run(d, ids, wts, residual, act="bf16", tok=0):
     ids_t = torch.tensor(np.asarray(ids, dtype=np.int64).astype(np.uint32).view(np.int32),
                          device="cuda")
     wts_t = torch.tensor(np.asarray(wts, dtype=np.float32), device="cuda")
-    ws = torch.empty(q.moe_gather_qgemv_int4_workspace_bytes(inter, len(ids)), dtype=torch.uint8,
+    ws = torch.empty(q.moe_gather_qgemv_int4_workspace_bytes(down, len(ids)), dtype=torch.uint8,
                      device="cuda")
     out = nan_like(hidden, torch.bfloat16 if act == "bf16" else torch.float32)
     q.moe_gather_qgemv_int4(gate, up, down, x, ids_t, wts_t, out, ws, residual=res)

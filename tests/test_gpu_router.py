@@ -102,7 +102,7 @@ def test_router_feeds_moe_without_host_round_trip():
     logits = torch.tensor(d["logits"][0][None, :].astype(np.float32), device="cuda")
     ids = torch.empty(8, dtype=torch.int32, device="cuda")
     wts = torch.empty(8, dtype=torch.float32, device="cuda")
-    ws = torch.empty(q.moe_gather_qgemv_int4_workspace_bytes(inter, 8), dtype=torch.uint8,
+    ws = torch.empty(q.moe_gather_qgemv_int4_workspace_bytes(down, 8), dtype=torch.uint8,
                      device="cuda")
     out = nan_like(hidden, torch.bfloat16)
     x = synth.to_torch(d["x"][0], "bf16")
@@ -136,7 +136,7 @@ def test_fused_route_gather_equals_router_then_gather(E, top_k, logit_dtype):
     lg = synth.to_torch(logits, logit_dtype)
     x = synth.to_torch(d["x"][0], "bf16")
     res = synth.to_torch(d["residual"][0], "bf16")
-    ws = torch.empty(q.moe_gather_qgemv_int4_workspace_bytes(128, top_k), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(q.moe_gather_qgemv_int4_workspace_bytes(down, top_k), dtype=torch.uint8, device="cuda")
     ids1 = torch.full((top_k,), -1, dtype=torch.int32, device="cuda")
     wts1 = torch.full((top_k,), float("nan"), dtype=torch.float32, device="cuda")
     out1 = nan_like(256, torch.bfloat16)
@@ -171,7 +171,7 @@ def test_fused_route_gather_nan_and_all_neg_inf():
         gate, up, down = (dev_matrix(d[k]) for k in ("gate", "up", "down"))
         lg = synth.to_torch(logits, "f32")
         x = synth.to_torch(d["x"][0], "bf16")
-        ws = torch.empty(q.moe_gather_qgemv_int4_workspace_bytes(128, 4), dtype=torch.uint8, device="cuda")
+        ws = torch.empty(q.moe_gather_qgemv_int4_workspace_bytes(down, 4), dtype=torch.uint8, device="cuda")
         ids = torch.empty(4, dtype=torch.int32, device="cuda")
         wts = torch.empty(4, dtype=torch.float32, device="cuda")
         out = nan_like(256, torch.bfloat16)

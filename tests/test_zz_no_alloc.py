@@ -31,8 +31,7 @@ def _both(q, mats, m, ids, wts, hidden, residual=True):
     wts_d = torch.tensor(wts, dtype=torch.float32, device="cuda")
     out_ws = torch.full((hidden,), float("nan"), dtype=torch.bfloat16, device="cuda")
     out_na = torch.full((hidden,), float("nan"), dtype=torch.bfloat16, device="cuda")
-    inter = m["gate"].n_out
-    ws = torch.empty(q.moe_gather_qgemv_int4_workspace_bytes(inter, len(ids)), dtype=torch.uint8,
+    ws = torch.empty(q.moe_gather_qgemv_int4_workspace_bytes(mats[2], len(ids)), dtype=torch.uint8,
                      device="cuda")
     q.moe_gather_qgemv_int4(*mats, x, ids_d, wts_d, out_ws, ws, residual=res)
     q.moe_gather_qgemv_int4_noalloc(*mats, x, ids_d, wts_d, out_na, residual=res)
