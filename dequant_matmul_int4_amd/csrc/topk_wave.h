@@ -13,82 +13,69 @@ namespace qint4 {
 namespace topk {
 constexpr float kNegInf = -__builtin_inff();
 
-static __device__ __forceinline__ bool better(float a, int ia, float b, int ib) {
-  return a > b || (a == b && ia < ib);
-}
-
 template <int CTRL>
-static __device__ __forceinline__ int dpp(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+static __device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
-// Keep the better of (v, i) and a partner's (pv, pi).
-static __device__ __forceinline__ void take(float &v, int &i, float pv, int pi) {
-  if (better(pv, pi, v, i)) {
-    v = pv;
-    i = pi;
-  }
-}
-
-// Wave-wide best (value desc, index asc); every lane gets the winner.  DPP
-// within rows of 16 lanes, then the gfx950 permlane16/32 swaps across rows.
-static __device__ __forceinline__ void wave_best(float &v, int &i) {
-#define QINT4_DPP_STEP(CTRL) \
-  take(v, i, __int_as_float(dpp<CTRL>(__float_as_int(v))), dpp<CTRL>(i))
-  QINT4_DPP_STEP(0xB1);   // quad_perm [1,0,3,2]
-  QINT4_DPP_STEP(0x4E);   // quad_perm [2,3,0,1]
-  QINT4_DPP_STEP(0x141);  // row_half_mirror
-  QINT4_DPP_STEP(0x140);  // row_mirror
-#undef QINT4_DPP_STEP
+// Wave-wide maximum, in every lane: DPP within rows of 16 lanes, then the
+// gfx950 permlane16/32 swaps across rows.
+static __device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp_f<0x140>(v));  // row_mirror
   {
-    auto pv = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    auto pi = __builtin_amdgcn_permlane16_swap((unsigned)i, (unsigned)i, false, false);
-    take(v, i, __uint_as_float(pv[0]), (int)pi[0]);
-    take(v, i, __uint_as_float(pv[1]), (int)pi[1]);
+    auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
   }
   {
-    auto pv = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    auto pi = __builtin_amdgcn_permlane32_swap((unsigned)i, (unsigned)i, false, false);
-    take(v, i, __uint_as_float(pv[0]), (int)pi[0]);
-    take(v, i, __uint_as_float(pv[1]), (int)pi[1]);
+    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
   }
+  return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(v)));
 }
-
 
 // One row of n_experts logits ranked by one wave: NPL keys per lane (lane l
 // holds experts l, l + 64, ...; NaN ranks as -inf, experts >= n_experts are
-// excluded), top_k rounds of the wave-wide best (value desc, index asc).
+// excluded).  Each of the top_k rounds takes the wave-wide maximum m of the
+// keys still in play, then the lowest expert index holding m: a ballot of
+// the keys equal to m, slot by slot (slot s holds indices 64 s .. 64 s + 63,
+// so the first non-empty ballot's lowest lane is the lowest index).  That is
+// the order (value desc, index asc).
 // Returns in every lane: sel_i[k] / sel_v[k] for k < top_k (uniform values).
 template <int NPL>
 static __device__ __forceinline__ void select(const float (&key_in)[NPL], int n_experts, int top_k,
                                               int (&sel_i)[8], float (&sel_v)[8]) {
   const int lane = threadIdx.x & 63;
   float key[NPL];
-  uint64_t taken = 0;
+  bool live[NPL];
 #pragma unroll
   for (int s = 0; s < NPL; ++s) {
     const float x = key_in[s];
     key[s] = (x != x) ? kNegInf : x;
-    if (lane + 64 * s >= n_experts) taken |= (uint64_t)1 << s;
+    live[s] = lane + 64 * s < n_experts;
   }
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     sel_i[k] = 0;
     sel_v[k] = kNegInf;
     if (k < top_k) {
-      // this lane's best element not chosen in an earlier round
-      float bv = kNegInf;
-      int bi = 0x7fffffff;
+      float bv = kNegInf;  // this lane's largest key still in play
+#pragma unroll
+      for (int s = 0; s < NPL; ++s) bv = live[s] ? fmaxf(bv, key[s]) : bv;
+      const float m = wave_max(bv);
+      int win = 0x7fffffff;  // no key left in play (the hosts reject top_k > n_experts)
+#pragma unroll
+      for (int s = NPL - 1; s >= 0; --s) {
+        const uint64_t b = __builtin_amdgcn_ballot_w64(live[s] && key[s] == m);
+        if (b) win = 64 * s + (int)__builtin_ctzll(b);
+      }
+      sel_i[k] = win;
+      sel_v[k] = m;
 #pragma unroll
       for (int s = 0; s < NPL; ++s)
-        if (!((taken >> s) & 1) && better(key[s], lane + 64 * s, bv, bi)) {
-          bv = key[s];
-          bi = lane + 64 * s;
-        }
-      wave_best(bv, bi);
-      sel_i[k] = __builtin_amdgcn_readfirstlane(bi);
-      sel_v[k] = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(bv)));
-      if (lane == (sel_i[k] & 63)) taken |= (uint64_t)1 << (sel_i[k] >> 6);
+        if (win == lane + 64 * s) live[s] = false;
     }
   }
 }
