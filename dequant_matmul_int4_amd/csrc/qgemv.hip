@@ -136,6 +136,41 @@ __device__ __forceinline__ void scalar_load8(const uint32_t *base, int n, uint32
       : "memory");
 }
 
+// Two such 8-word reads, va from a and vb from b, with one wait: word k of
+// each is read at element min(k, n - 1) (byte offsets in SGPRs).
+__device__ __forceinline__ void scalar_load8x2(const uint32_t *a, const uint32_t *b, int n, uint32_t (&va)[8],
+                                               uint32_t (&vb)[8]) {
+  uint32_t o[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) o[k] = 4u * (uint32_t)(k < n ? k : n - 1);
+  asm volatile(
+      "s_load_dword %0, %16, %18\n\t"
+      "s_load_dword %1, %16, %19\n\t"
+      "s_load_dword %2, %16, %20\n\t"
+      "s_load_dword %3, %16, %21\n\t"
+      "s_load_dword %4, %16, %22\n\t"
+      "s_load_dword %5, %16, %23\n\t"
+      "s_load_dword %6, %16, %24\n\t"
+      "s_load_dword %7, %16, %25\n\t"
+      "s_load_dword %8, %17, %18\n\t"
+      "s_load_dword %9, %17, %19\n\t"
+      "s_load_dword %10, %17, %20\n\t"
+      "s_load_dword %11, %17, %21\n\t"
+      "s_load_dword %12, %17, %22\n\t"
+      "s_load_dword %13, %17, %23\n\t"
+      "s_load_dword %14, %17, %24\n\t"
+      "s_load_dword %15, %17, %25\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      // early-clobber: no result register may alias an address or offset
+      // still to be used by a later load of the block
+      : "=&s"(va[0]), "=&s"(va[1]), "=&s"(va[2]), "=&s"(va[3]), "=&s"(va[4]), "=&s"(va[5]),
+        "=&s"(va[6]), "=&s"(va[7]), "=&s"(vb[0]), "=&s"(vb[1]), "=&s"(vb[2]), "=&s"(vb[3]),
+        "=&s"(vb[4]), "=&s"(vb[5]), "=&s"(vb[6]), "=&s"(vb[7])
+      : "s"(a), "s"(b), "s"(o[0]), "s"(o[1]), "s"(o[2]), "s"(o[3]), "s"(o[4]), "s"(o[5]), "s"(o[6]),
+        "s"(o[7])
+      : "memory");
+}
+
 // A VGPR whose lane k (k < 8) holds v[k]; other lanes hold 0.
 __device__ __forceinline__ uint32_t lanes_from_scalars(const uint32_t (&v)[8]) {
   const int lane = threadIdx.x & 63;
@@ -525,6 +560,7 @@ __global__ void __launch_bounds__(TT >= 8 ? 512 : 768) qgemv_kernel(const GemvPa
 
   // expert ids and slot weights, through the scalar cache: lane k of v_ids /
   // v_wts holds slot k's values
+  // (given ids are read once the activation loads are in flight, below)
   uint32_t v_ids = 0, v_wts = 0;
   // Routing (EPI_SWIGLU, p.route != 0): this token's router logits are loaded
   // here (lane l: experts l, l + 64, ...; indices past n_experts clamped, so
@@ -539,21 +575,6 @@ __global__ void __launch_bounds__(TT >= 8 ? 512 : 768) qgemv_kernel(const GemvPa
         const int i = min(lane + 64 * s, p.n_experts - 1);
         key[s] = p.route == 2 ? bf16_lo(reinterpret_cast<const uint16_t *>(p.aux)[i])
                               : reinterpret_cast<const float *>(p.aux)[i];
-      }
-    } else if (p.ids) {
-      uint32_t s_ids[8];
-      scalar_load8(p.ids, p.top_k, s_ids);
-      v_ids = lanes_from_scalars(s_ids);
-    }
-  } else if constexpr (EPI == EPI_MOE_DOWN) {
-    if (p.ids) {
-      uint32_t s_ids[8];
-      scalar_load8(p.ids, p.top_k, s_ids);
-      v_ids = lanes_from_scalars(s_ids);
-      if constexpr (EPI == EPI_MOE_DOWN) {
-        uint32_t s_wts[8];
-        scalar_load8(reinterpret_cast<const uint32_t *>(p.wts), p.top_k, s_wts);
-        v_wts = lanes_from_scalars(s_wts);
       }
     }
   }
@@ -765,6 +786,23 @@ __global__ void __launch_bounds__(TT >= 8 ? 512 : 768) qgemv_kernel(const GemvPa
       }
       lds_barrier();
       v_ids = lane < 8 ? rid[lane] : 0u;
+    }
+  }
+  // Given expert ids (and, for the down projection, the slot weights), read
+  // through the scalar cache while the activation loads are in flight; the
+  // wait for them does not drain those vector loads.
+  if constexpr (EPI == EPI_SWIGLU) {
+    if (!p.route && p.ids) {
+      uint32_t s_ids[8];
+      scalar_load8(p.ids, p.top_k, s_ids);
+      v_ids = lanes_from_scalars(s_ids);
+    }
+  } else if constexpr (EPI == EPI_MOE_DOWN) {
+    if (p.ids) {
+      uint32_t s_ids[8], s_wts[8];
+      scalar_load8x2(p.ids, reinterpret_cast<const uint32_t *>(p.wts), p.top_k, s_ids, s_wts);
+      v_ids = lanes_from_scalars(s_ids);
+      v_wts = lanes_from_scalars(s_wts);
     }
   }
   start(lc);
