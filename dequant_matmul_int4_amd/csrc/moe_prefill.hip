@@ -55,6 +55,7 @@ __device__ __forceinline__ void lds_barrier() {
 // ---------------------------------------------------------------------------
 
 constexpr int kSortThreads = 1024;
+constexpr int kSortBatch = 16;  // ids in flight per thread
 
 // Exclusive scan of v[0..n) in LDS (n <= 4 * kSortThreads) by the whole
 // workgroup; v[n] receives the total.  Each thread scans 4 consecutive
@@ -111,9 +112,18 @@ __global__ void __launch_bounds__(kSortThreads)
   const int tid = threadIdx.x;
   for (int e = tid; e <= n_experts; e += kSortThreads) cnt[e] = 0u;
   lds_barrier();
-  for (int64_t p = tid; p < n_pairs; p += kSortThreads) {
-    const uint32_t e = ids[p];
-    if (e < (uint32_t)n_experts) atomicAdd(&cnt[e], 1u);
+  // ids are read kSortBatch per thread at a time, all loads issued before
+  // any is used: one memory round trip per batch rather than per id
+  for (int64_t b = 0; b < n_pairs; b += (int64_t)kSortThreads * kSortBatch) {
+    uint32_t e[kSortBatch];
+#pragma unroll
+    for (int u = 0; u < kSortBatch; ++u) {
+      const int64_t p = b + tid + (int64_t)u * kSortThreads;
+      e[u] = p < n_pairs ? ids[p] : 0xFFFFFFFFu;
+    }
+#pragma unroll
+    for (int u = 0; u < kSortBatch; ++u)
+      if (e[u] < (uint32_t)n_experts) atomicAdd(&cnt[e[u]], 1u);
   }
   lds_barrier();
   for (int e = tid; e < n_experts; e += kSortThreads) tcnt[e] = (cnt[e] + bm - 1) / bm;
@@ -135,14 +145,25 @@ __global__ void __launch_bounds__(kSortThreads)
   }
   lds_barrier();
   // scatter: cnt[e] is now the next free slot of expert e
-  for (int64_t p = tid; p < n_pairs; p += kSortThreads) {
-    const uint32_t e = ids[p];
-    uint32_t slot = kNoSlot;
-    if (e < (uint32_t)n_experts) {
-      slot = atomicAdd(&cnt[e], 1u);
-      perm[slot] = (uint32_t)p;
+  for (int64_t b = 0; b < n_pairs; b += (int64_t)kSortThreads * kSortBatch) {
+    uint32_t e[kSortBatch];
+#pragma unroll
+    for (int u = 0; u < kSortBatch; ++u) {
+      const int64_t p = b + tid + (int64_t)u * kSortThreads;
+      e[u] = p < n_pairs ? ids[p] : 0xFFFFFFFFu;
     }
-    pos[p] = slot;
+#pragma unroll
+    for (int u = 0; u < kSortBatch; ++u) {
+      const int64_t p = b + tid + (int64_t)u * kSortThreads;
+      if (p < n_pairs) {
+        uint32_t slot = kNoSlot;
+        if (e[u] < (uint32_t)n_experts) {
+          slot = atomicAdd(&cnt[e[u]], 1u);
+          perm[slot] = (uint32_t)p;
+        }
+        pos[p] = slot;
+      }
+    }
   }
 }
 
@@ -454,20 +475,34 @@ __global__ void __launch_bounds__(256)
   float acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.f;
-  for (int k = 0; k < top_k; ++k) {
-    const uint32_t s = pos[t * top_k + k];
-    if (s == kNoSlot) continue;
-    const float w = wts[t * top_k + k];
-    const float4 *src = reinterpret_cast<const float4 *>(d + (int64_t)s * hidden + c);
-    const float4 a = src[0], b = src[1];
-    acc[0] = fmaf(w, a.x, acc[0]);
-    acc[1] = fmaf(w, a.y, acc[1]);
-    acc[2] = fmaf(w, a.z, acc[2]);
-    acc[3] = fmaf(w, a.w, acc[3]);
-    acc[4] = fmaf(w, b.x, acc[4]);
-    acc[5] = fmaf(w, b.y, acc[5]);
-    acc[6] = fmaf(w, b.z, acc[6]);
-    acc[7] = fmaf(w, b.w, acc[7]);
+  // every slot's loads are issued before the first is used (a skipped slot
+  // reads row 0 and adds nothing); the slots are still added in order k
+  uint32_t sl[kMaxTopK];
+  float w[kMaxTopK];
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) {
+    sl[k] = k < top_k ? pos[t * top_k + k] : kNoSlot;
+    w[k] = k < top_k ? wts[t * top_k + k] : 0.f;
+  }
+  float4 a[kMaxTopK], b[kMaxTopK];
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) {
+    const float4 *src =
+        reinterpret_cast<const float4 *>(d + (int64_t)(sl[k] == kNoSlot ? 0u : sl[k]) * hidden + c);
+    a[k] = src[0];
+    b[k] = src[1];
+  }
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) {
+    if (sl[k] == kNoSlot) continue;
+    acc[0] = fmaf(w[k], a[k].x, acc[0]);
+    acc[1] = fmaf(w[k], a[k].y, acc[1]);
+    acc[2] = fmaf(w[k], a[k].z, acc[2]);
+    acc[3] = fmaf(w[k], a[k].w, acc[3]);
+    acc[4] = fmaf(w[k], b[k].x, acc[4]);
+    acc[5] = fmaf(w[k], b[k].y, acc[5]);
+    acc[6] = fmaf(w[k], b[k].z, acc[6]);
+    acc[7] = fmaf(w[k], b[k].w, acc[7]);
   }
   const int64_t o = t * hidden + c;
   if (out_bf16) {
