@@ -274,6 +274,7 @@ struct MultiPlan {
   bool mfma = false;  // small-M MFMA tiles of 16 rows
   int blk = 0;        // activation rows per launch
   int64_t tiles = 0;  // MFMA: tiles per launch
+  int64_t grid = 0;   // MFMA: workgroups per launch (each takes tiles i, i + grid, ...)
   GemvPlan plan{};    // otherwise: the persistent GEMV plan
 };
 
@@ -298,6 +299,17 @@ qint4_status plan_multi(int n_outs, const int64_t *n_out, int64_t k_in, int grou
                gemv_mfma_lds_bytes(QINT4_SMALLM_MAX, group_size, k_in, streams) > (size_t)kMaxLds)
                   ? kMaxTokens
                   : QINT4_SMALLM_MAX;
+    // From 8 tokens on, staging the activation slices costs about as much as a
+    // tile: as many workgroups as the CUs hold at once (LDS, and 16 waves per
+    // CU at the kernel's 128 registers), each staging once for all of its
+    // tiles (17408 x 5120 gate/up pair at T = 8: 42 -> 38 us; q/k/v at
+    // T = 16: 13.2 -> 10.1 us).  Up to 4 tokens a workgroup per tile is
+    // faster (the pair at T = 1..4: 30-32 us against 38 us).
+    const int tt = tt_for(std::min<int64_t>(T, mp->blk));
+    const size_t lds = gemv_mfma_lds_bytes(tt, group_size, k_in, streams);
+    const int ks = gemv_mfma_waves(k_in);
+    const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>((int64_t)(kMaxLds / lds), 16 / ks));
+    mp->grid = std::min<int64_t>(tiles, per_cu * n_cu);  // launches of 8 or more tokens
     return QINT4_OK;
   }
   const int nc = (int)(k_in / 32);
@@ -527,8 +539,9 @@ qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t
       for (int i = 0; i < n; ++i)
         p.m[i].y = reinterpret_cast<unsigned char *>(swiglu ? ys[0] : ys[i]) +
                    (size_t)t0 * (swiglu ? ws[0].n_out : ws[i].n_out) * yb;
-      hipError_t e = launch_gemv_mfma(p, tt_for(nt), ws[0].group_size, sb_bf16, swiglu ? 1 : 0, tiles,
-                                      stream);
+      const int tt = tt_for(nt);
+      hipError_t e = launch_gemv_mfma(p, tt, ws[0].group_size, sb_bf16, swiglu ? 1 : 0,
+                                      tt <= 4 ? tiles : mp.grid, stream);
       if (e != hipSuccess) return fail(QINT4_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(e));
     }
     return ok();
@@ -1355,7 +1368,7 @@ qint4_status qint4_plan_qgemv(int32_t call, int32_t n, const int64_t *n_outs, in
     form->kernel = QINT4_FORM_MFMA;
     form->tokens = tt_for(std::min<int64_t>(T, mp.blk));
     form->launches = launches;
-    form->grid = mp.tiles;
+    form->grid = form->tokens <= 4 ? mp.tiles : mp.grid;  // the first launch
     form->tasks = mp.tiles;
     form->waves = gemv_mfma_waves(k_in);
   } else {

@@ -160,17 +160,17 @@ inline int gemv_ring_depth(const GemvPlan &plan, int xmode, int epi) {
 hipError_t launch_gemv(const GemvParams &p, const GemvPlan &plan, int xmode, int sb_bf16,
                        int epi, hipStream_t stream);
 
-// Small-M GEMVs with bf16 activations on MFMA (qgemv_mfma.hip): tiles of 16
-// rows (stored outputs: task0[i] = first tile of matrix i; swiglu: the gate/up
-// pair m[0], m[1] with h in m[0].y), gemv_mfma_waves(k_in) K slices per tile,
-// n_tok rows of x with stride ldx, ncx = k_in / 32.  streams: 1 (stored
-// outputs) or 2 (gate/up pair).  Supported shapes take this path for every
-// token count.
+// Small-M GEMVs with bf16 activations on MFMA (qgemv_mfma.hip): n_tasks tiles
+// of 16 rows (stored outputs: task0[i] = first tile of matrix i; swiglu: the
+// gate/up pair m[0], m[1] with h in m[0].y), gemv_mfma_waves(k_in) K slices per
+// tile, n_tok rows of x with stride ldx, ncx = k_in / 32.  streams: 1 (stored
+// outputs) or 2 (gate/up pair).  `grid` workgroups (1..n_tasks) take tiles
+// i, i + grid, ...  Supported shapes take this path for every token count.
 bool gemv_mfma_supported(int64_t k_in, int group_size, int streams);
 int gemv_mfma_waves(int64_t k_in);  // K slices (waves) per tile
 size_t gemv_mfma_lds_bytes(int tt, int group_size, int64_t k_in, int streams);
 hipError_t launch_gemv_mfma(const GemvParams &p, int tt, int group_size, int sb_bf16, int swiglu,
-                            int64_t n_tiles, hipStream_t stream);
+                            int64_t grid, hipStream_t stream);
 
 // LDS bytes a GEMV launch needs: per token, the staged activation (padded to
 // ncx_pad chunks) and its chunk sums; then (MoE down) the float32 residual row

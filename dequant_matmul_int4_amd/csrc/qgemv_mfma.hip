@@ -1,4 +1,4 @@
-// qgemv_mfma.hip -- small-M int4 products with bf16 activations, 1..8
+// qgemv_mfma.hip -- small-M int4 products with bf16 activations, 1..16
 // activation rows (stored outputs of up to 8 matrices, or the gate/up pair
 // with the SwiGLU epilogue), on gfx950 MFMA (v_mfma_f32_16x16x32_bf16).
 //
@@ -25,8 +25,12 @@
 // calls bit for bit.
 //
 // Work decomposition (gfx950 specific, not from the pages):
-//   * A workgroup owns a tile of 16 rows of one matrix; its KS waves split
-//     k_in into slices of kChunksPerWave chunks of 32 codes (steps of 128).
+//   * A workgroup takes tiles of 16 rows of one matrix (tiles blockIdx.x,
+//     blockIdx.x + gridDim.x, ...: one each when every tile has its own
+//     workgroup, more when the staged rows limit the chip to one workgroup
+//     per CU); its KS waves split k_in into slices of kChunksPerWave chunks
+//     of 32 codes (steps of 128).  The activation slices are staged once per
+//     workgroup and serve all of its tiles.
 //   * Lane (r, kb) = (lane % 16, lane / 16) loads, per step, the 16-byte
 //     chunk 4*step + kb of row r: a load instruction covers 16 rows x 64
 //     contiguous bytes.  An MFMA takes 8 codes (one word) per lane, and its
@@ -128,12 +132,12 @@ __device__ __forceinline__ void store_out(void *y, int64_t i, float v, int bf16)
 // LDS bytes of one wave's region: TT staged rows of the slice (plus 16 bytes
 // of padding per row against bank conflicts), the per-group sums of 16 token
 // slots, and the (scale, bias) pairs of 16 rows for each of the NS code
-// streams.  At least NS KB: the region also takes the wave's accumulators for
-// the final reduction.
+// streams -- at least NS KB, since that last part also takes the wave's
+// accumulators for each tile's final reduction.
 constexpr int wave_region_bytes(int tt, int cpg, int ns) {
   const int ng = kChunksPerWave / cpg;
-  const int b = tt * (kChunksPerWave * 64 + 16) + ng * 16 * 4 + ns * ng * 16 * 8;
-  return b > ns * 1024 ? b : ns * 1024;
+  const int tb = ns * ng * 16 * 8;
+  return tt * (kChunksPerWave * 64 + 16) + ng * 16 * 4 + (tb > ns * 1024 ? tb : ns * 1024);
 }
 
 // NS = 1: stored outputs of up to kMaxMats matrices (tile t of matrix i from
@@ -148,26 +152,14 @@ __global__ void __launch_bounds__(1024) qgemv_mfma_kernel(const GemvParams p) {
   constexpr int WR = wave_region_bytes(TT, CPG, NS);
   constexpr uint32_t SBB = (SBT == 1) ? 2 : 4;
   constexpr int TE = (NG * 16 + 63) / 64;  // (scale, bias) entries per lane
+  // several tiles per workgroup from 8 tokens on; up to 4 tokens every tile
+  // has its own workgroup (the host launches one per tile), and the kernel
+  // keeps the registers of a single pass
+  constexpr bool kPersist = TT >= 8;
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int T = p.n_tok;
-
-  // the tile's matrix: count of later matrix starts at or below the tile
-  const int tile = blockIdx.x;
-  int m = 0, first = 0;
-  if constexpr (NS == 1) {
-#pragma unroll
-    for (int i = 1; i < kMaxMats; ++i) {
-      const int t0 = p.task0[i];
-      const bool in = tile >= t0;
-      m += in ? 1 : 0;
-      first = in ? t0 : first;
-    }
-  }
-  const int n_rows = (int)p.m[m].n_out;
-  void *const y = p.m[m].y;
-  const int row0 = (tile - first) * kTileRows;
   const uint32_t kwb = (uint32_t)p.kwb, sbrow = (uint32_t)p.sbrow;
   const int r = lane & 15, kb = lane >> 4;
   const int c0 = wv * kChunksPerWave;  // first chunk of this wave's slice
@@ -176,9 +168,57 @@ __global__ void __launch_bounds__(1024) qgemv_mfma_kernel(const GemvParams p) {
   unsigned char *reg = smem + wv * WR;
   unsigned char *xst = reg;                                                // [TT][chunks][4 words] x 16 B
   float *xsum = reinterpret_cast<float *>(reg + TT * TS);                  // [NG][16 tokens]
-  float2 *tbl = reinterpret_cast<float2 *>(reg + TT * TS + NG * 16 * 4);   // [NS][NG][16 rows]
+  constexpr int TBL = TT * TS + NG * 16 * 4;  // (scale, bias) table, then each tile's accumulators
+  float2 *tbl = reinterpret_cast<float2 *>(reg + TBL);                     // [NS][NG][16 rows]
 
-  // ---- loads: activation rows first (L2), then scales/biases, then codes ----
+  // Matrix, first row and row count of a tile (the count of later matrix
+  // starts at or below the tile picks the matrix).
+  struct TileAt {
+    int m, row0, n_rows;
+  };
+  auto tile_at = [&](int tile) {
+    int m = 0, first = 0;
+    if constexpr (NS == 1) {
+#pragma unroll
+      for (int i = 1; i < kMaxMats; ++i) {
+        const int t0 = p.task0[i];
+        const bool in = tile >= t0;
+        m += in ? 1 : 0;
+        first = in ? t0 : first;
+      }
+    }
+    return TileAt{m, (tile - first) * kTileRows, (int)p.m[m].n_out};
+  };
+  // scales/biases, then codes, of a tile (into the registers below)
+  uint32_t sr[NS][TE], br[NS][TE];
+  uint4 cw[NS][kSteps];
+  auto load_tile = [&](const TileAt &ti) {
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      const GemvMat &mat = p.m[ti.m + st];
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(mat.scales, (uint32_t)ti.n_rows * sbrow);
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(mat.biases, (uint32_t)ti.n_rows * sbrow);
+#pragma unroll
+      for (int j = 0; j < TE; ++j) {
+        const int e = lane + 64 * j;  // entry (group e / 16, row e % 16)
+        const uint32_t off = e < NG * 16
+                                 ? (uint32_t)(ti.row0 + (e & 15)) * sbrow + (uint32_t)(g0 + (e >> 4)) * SBB
+                                 : kOutOfRange;
+        sr[st][j] = buf_load_sb<SBT>(rs, off);
+        br[st][j] = buf_load_sb<SBT>(rb, off);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.m[ti.m + st].codes, (uint32_t)ti.n_rows * kwb);
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s)
+        cw[st][s] = buf_load_b128(rc, (uint32_t)(ti.row0 + r) * kwb + (uint32_t)(c0 + 4 * s + kb) * 16);
+    }
+  };
+
+  // ---- loads: activation rows first (L2), then the first tile's ----
   // the slice of a token is U 16-byte units (8 elements each); unit
   // u = lane + 64 i of the wave's TT * U is element 8 (u % U) of token u / U
   constexpr int U = kChunksPerWave * 4;
@@ -196,33 +236,11 @@ __global__ void __launch_bounds__(1024) qgemv_mfma_kernel(const GemvParams p) {
   // keep the issue order (activation, scales/biases, codes): the staging then
   // waits only for the activation loads
   __builtin_amdgcn_sched_barrier(0);
-  uint32_t sr[NS][TE], br[NS][TE];
-#pragma unroll
-  for (int st = 0; st < NS; ++st) {
-    const GemvMat &mat = p.m[m + st];
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(mat.scales, (uint32_t)n_rows * sbrow);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(mat.biases, (uint32_t)n_rows * sbrow);
-#pragma unroll
-    for (int j = 0; j < TE; ++j) {
-      const int e = lane + 64 * j;  // entry (group e / 16, row e % 16)
-      const uint32_t off = e < NG * 16
-                               ? (uint32_t)(row0 + (e & 15)) * sbrow + (uint32_t)(g0 + (e >> 4)) * SBB
-                               : kOutOfRange;
-      sr[st][j] = buf_load_sb<SBT>(rs, off);
-      br[st][j] = buf_load_sb<SBT>(rb, off);
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  uint4 cw[NS][kSteps];
-#pragma unroll
-  for (int st = 0; st < NS; ++st) {
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.m[m + st].codes, (uint32_t)n_rows * kwb);
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s)
-      cw[st][s] = buf_load_b128(rc, (uint32_t)(row0 + r) * kwb + (uint32_t)(c0 + 4 * s + kb) * 16);
-  }
+  int tile = blockIdx.x;  // tiles blockIdx.x, blockIdx.x + gridDim.x, ... (uniform)
+  TileAt cur = tile_at(tile);
+  load_tile(cur);
 
-  // ---- stage the activation slice and its per-group sums ----
+  // ---- stage the activation slice and its per-group sums (once) ----
   // (all lanes take part in every round: the group sums reduce over 4 * CPG
   // neighbouring lanes, which never straddle two tokens since U % 16 == 0)
 #pragma unroll
@@ -241,102 +259,121 @@ __global__ void __launch_bounds__(1024) qgemv_mfma_kernel(const GemvParams p) {
     s8 = seg_sum<L2>(s8);
     if (t < T && (lu & (4 * CPG - 1)) == 0) xsum[(lu / (4 * CPG)) * 16 + t] = s8;
   }
-#pragma unroll
-  for (int st = 0; st < NS; ++st)
-#pragma unroll
-    for (int j = 0; j < TE; ++j) {
-      const int e = lane + 64 * j;
-      if (e < NG * 16) tbl[st * NG * 16 + e] = make_float2(sb_value<SBT>(sr[st][j]), sb_value<SBT>(br[st][j]));
-    }
 
-  // ---- products ----
   uint32_t magic = 0x43004300u;
   asm volatile("" : "+v"(magic));  // keep in a VGPR so AND-OR stays one VOP3
   const int nn = min(lane & 15, T - 1);  // token of this lane's A row
   const unsigned char *xa = xst + nn * TS + kb * 16;
-  f32x4_t acc[NS], c[NS];
+  const int KS = p.waves_per_wg;
+
+  while (true) {
 #pragma unroll
-  for (int st = 0; st < NS; ++st) {
-    acc[st] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    c[st] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
+    for (int st = 0; st < NS; ++st)
 #pragma unroll
-  for (int s = 0; s < kSteps; ++s) {
-    uint32_t wd[NS][4];
+      for (int j = 0; j < TE; ++j) {
+        const int e = lane + 64 * j;
+        if (e < NG * 16) tbl[st * NG * 16 + e] = make_float2(sb_value<SBT>(sr[st][j]), sb_value<SBT>(br[st][j]));
+      }
+
+    // ---- products ----
+    f32x4_t acc[NS], c[NS];
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
-      uint32_t w0 = cw[st][s].x, w1 = cw[st][s].y, w2 = cw[st][s].z, w3 = cw[st][s].w;
-      // lane (r, kb) holds chunk 4s + kb; exchange so that it holds word kb of
-      // chunks 4s .. 4s + 3 (a 4 x 4 transpose over the lanes 16 apart)
-      auto a = __builtin_amdgcn_permlane32_swap(w0, w2, false, false);
-      w0 = a[0];
-      w2 = a[1];
-      auto b = __builtin_amdgcn_permlane32_swap(w1, w3, false, false);
-      w1 = b[0];
-      w3 = b[1];
-      auto e = __builtin_amdgcn_permlane16_swap(w0, w1, false, false);
-      w0 = e[0];
-      w1 = e[1];
-      auto f = __builtin_amdgcn_permlane16_swap(w2, w3, false, false);
-      w2 = f[0];
-      w3 = f[1];
-      wd[st][0] = w0;
-      wd[st][1] = w1;
-      wd[st][2] = w2;
-      wd[st][3] = w3;
+      acc[st] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      c[st] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ch = 4 * s + i;  // chunk of the slice
-      const uint4 xq = *reinterpret_cast<const uint4 *>(xa + ch * 64);
-      const bf16x8_t ax = __builtin_bit_cast(bf16x8_t, xq);
+    for (int s = 0; s < kSteps; ++s) {
+      uint32_t wd[NS][4];
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        uint32_t pq[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) pq[k] = ((wd[st][i] >> (4 * k)) & 0x000F000Fu) | magic;
-        const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, make_uint4(pq[0], pq[1], pq[2], pq[3]));
-        const f32x4_t cin = (ch % CPG == 0) ? f32x4_t{0.f, 0.f, 0.f, 0.f} : c[st];
-        c[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, bw, cin, 0, 0, 0);
+        uint32_t w0 = cw[st][s].x, w1 = cw[st][s].y, w2 = cw[st][s].z, w3 = cw[st][s].w;
+        // lane (r, kb) holds chunk 4s + kb; exchange so that it holds word kb of
+        // chunks 4s .. 4s + 3 (a 4 x 4 transpose over the lanes 16 apart)
+        auto a = __builtin_amdgcn_permlane32_swap(w0, w2, false, false);
+        w0 = a[0];
+        w2 = a[1];
+        auto b = __builtin_amdgcn_permlane32_swap(w1, w3, false, false);
+        w1 = b[0];
+        w3 = b[1];
+        auto e = __builtin_amdgcn_permlane16_swap(w0, w1, false, false);
+        w0 = e[0];
+        w1 = e[1];
+        auto f = __builtin_amdgcn_permlane16_swap(w2, w3, false, false);
+        w2 = f[0];
+        w3 = f[1];
+        wd[st][0] = w0;
+        wd[st][1] = w1;
+        wd[st][2] = w2;
+        wd[st][3] = w3;
       }
-      if ((ch + 1) % CPG == 0) {
-        const int g = ch / CPG;
-        const f32x4_t xs = *reinterpret_cast<const f32x4_t *>(xsum + g * 16 + 4 * kb);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ch = 4 * s + i;  // chunk of the slice
+        const uint4 xq = *reinterpret_cast<const uint4 *>(xa + ch * 64);
+        const bf16x8_t ax = __builtin_bit_cast(bf16x8_t, xq);
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
-          const float2 sbv = tbl[(st * NG + g) * 16 + r];
+          uint32_t pq[4];
 #pragma unroll
-          for (int mm = 0; mm < 4; ++mm) {
-            const float d = c[st][mm] - 128.f * xs[mm];
-            acc[st][mm] += fmaf(sbv.x, d, sbv.y * xs[mm]);
+          for (int k = 0; k < 4; ++k) pq[k] = ((wd[st][i] >> (4 * k)) & 0x000F000Fu) | magic;
+          const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, make_uint4(pq[0], pq[1], pq[2], pq[3]));
+          const f32x4_t cin = (ch % CPG == 0) ? f32x4_t{0.f, 0.f, 0.f, 0.f} : c[st];
+          c[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, bw, cin, 0, 0, 0);
+        }
+        if ((ch + 1) % CPG == 0) {
+          const int g = ch / CPG;
+          const f32x4_t xs = *reinterpret_cast<const f32x4_t *>(xsum + g * 16 + 4 * kb);
+#pragma unroll
+          for (int st = 0; st < NS; ++st) {
+            const float2 sbv = tbl[(st * NG + g) * 16 + r];
+#pragma unroll
+            for (int mm = 0; mm < 4; ++mm) {
+              const float d = c[st][mm] - 128.f * xs[mm];
+              acc[st][mm] += fmaf(sbv.x, d, sbv.y * xs[mm]);
+            }
           }
         }
       }
     }
-  }
 
-  // ---- sum the K slices (wave order) and store ----
+    // ---- sum the K slices (wave order) and store ----
+    auto reduce_store = [&](const TileAt &done) {
 #pragma unroll
-  for (int st = 0; st < NS; ++st)  // this wave is done with its region
-    *reinterpret_cast<f32x4_t *>(reg + st * 1024 + lane * 16) = acc[st];
-  lds_barrier();
-  const int KS = p.waves_per_wg;
-  for (int o = threadIdx.x; o < kTileRows * T; o += KS * 64) {
-    const int rr = o & 15, n = o >> 4;
-    const int src = (rr + 16 * (n >> 2)) * 16 + (n & 3) * 4;  // lane and accumulator of (n, rr)
-    float v[NS];
+      for (int st = 0; st < NS; ++st)  // over this wave's table, which the products no longer read
+        *reinterpret_cast<f32x4_t *>(reg + TBL + st * 1024 + lane * 16) = acc[st];
+      lds_barrier();
+      void *const y = p.m[done.m].y;
+      for (int o = threadIdx.x; o < kTileRows * T; o += KS * 64) {
+        const int rr = o & 15, n = o >> 4;
+        const int src = (rr + 16 * (n >> 2)) * 16 + (n & 3) * 4;  // lane and accumulator of (n, rr)
+        float v[NS];
 #pragma unroll
-    for (int st = 0; st < NS; ++st) {
-      v[st] = 0.f;
-      for (int w = 0; w < KS; ++w) v[st] += *reinterpret_cast<const float *>(smem + w * WR + st * 1024 + src);
+        for (int st = 0; st < NS; ++st) {
+          v[st] = 0.f;
+          for (int w = 0; w < KS; ++w)
+            v[st] += *reinterpret_cast<const float *>(smem + w * WR + TBL + st * 1024 + src);
+        }
+        float out = v[0];
+        if constexpr (NS == 2) out = (v[0] / (1.f + __expf(-v[0]))) * v[1];
+        const int row = done.row0 + rr;
+        if (row < done.n_rows) store_out(y, (int64_t)n * done.n_rows + row, out, p.y_bf16);
+      }
+    };
+    const int next = tile + (int)gridDim.x;
+    if (!kPersist || next >= p.n_tasks) {  // uniform: the workgroup's last tile
+      reduce_store(cur);
+      break;
     }
-    float out = v[0];
-    if constexpr (NS == 2) out = (v[0] / (1.f + __expf(-v[0]))) * v[1];
-    const int row = row0 + rr;
-    if (row < n_rows) store_out(y, (int64_t)n * n_rows + row, out, p.y_bf16);
+    // the next tile's loads overlap this tile's reduction
+    const TileAt done = cur;
+    cur = tile_at(next);
+    load_tile(cur);
+    reduce_store(done);
+    lds_barrier();  // every wave has read the accumulators before the next tables land
+    tile = next;
   }
 }
-
 template <int SBT, int CPG, int TT, int NS>
 hipError_t launch_mfma(const GemvParams &p, int64_t grid, int ks, hipStream_t stream) {
   auto kern = qgemv_mfma_kernel<SBT, CPG, TT, NS>;
@@ -392,11 +429,12 @@ bool gemv_mfma_supported(int64_t k_in, int group_size, int streams) {
 }
 
 hipError_t launch_gemv_mfma(const GemvParams &p, int tt, int group_size, int sb_bf16, int swiglu,
-                            int64_t n_tiles, hipStream_t stream) {
+                            int64_t grid, hipStream_t stream) {
   const int ks = p.waves_per_wg;
-  if (ks < 1 || ks > 16 || n_tiles < 1) return hipErrorInvalidValue;
-  return swiglu ? launch_group<2>(p, tt, group_size, sb_bf16, n_tiles, ks, stream)
-                : launch_group<1>(p, tt, group_size, sb_bf16, n_tiles, ks, stream);
+  if (ks < 1 || ks > 16 || grid < 1 || grid > p.n_tasks || (tt <= 4 && grid != p.n_tasks))
+    return hipErrorInvalidValue;
+  return swiglu ? launch_group<2>(p, tt, group_size, sb_bf16, grid, ks, stream)
+                : launch_group<1>(p, tt, group_size, sb_bf16, grid, ks, stream);
 }
 
 }  // namespace qint4

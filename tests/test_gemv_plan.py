@@ -77,6 +77,7 @@ def test_smallm_mfma_form():
     token blocks whose staged rows fit."""
     f = q.plan_qgemv([4096, 1024, 1024], 4096, T=16, call=q.CALL_SMALLM, n_cu=N_CU)
     assert (f["kernel"], f["tokens"], f["launches"], f["tasks"]) == ("mfma", 16, 1, 6144 // 16)
+    assert f["grid"] == N_CU  # one 145 KB workgroup per CU, each staging its rows once for its tiles
     f = q.plan_qgemv([17408], 5120, T=16, call=q.CALL_SMALLM, n_cu=N_CU)
     assert (f["kernel"], f["tokens"], f["launches"], f["waves"]) == ("mfma", 8, 2, 10)
     f = q.plan_qgemv([17408], 5120, T=1, call=q.CALL_SMALLM, n_cu=N_CU)

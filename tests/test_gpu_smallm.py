@@ -256,3 +256,30 @@ def test_smallm_swiglu_pair_verify_rounds(T):
         for t in range(T):
             ref, a = oracle.swiglu_pair(gate, up, x[t], "bf16")
             check_f32(to_np64(h[t]), ref, "swiglu T=%d hidden %d t=%d" % (T, hidden, t), a_ref=a)
+
+
+@pytest.mark.parametrize("T", [9, 16])
+def test_smallm_more_tiles_than_workgroups(T):
+    """From 8 tokens on a workgroup takes several 16-row tiles (its staged activation serves
+    them all): the q/k/v set (384 tiles on at most 256 workgroups at T = 16) and a 4160-row
+    gate/up pair at hidden 5120 (260 tiles; blocks of 8 rows, then the rest), every output."""
+    q = lib()
+    rng = np.random.default_rng(900 + T)
+    ws = [synth.draw_matrix(rng, n, 4096, 64, "bf16") for n in (4096, 1024, 1024)]
+    x, xd = _x(rng, T, 4096)
+    ys = [nan_like((T, w.n_out), torch.bfloat16) for w in ws]
+    q.qgemv_int4_smallm([dev_matrix(w) for w in ws], xd, ys)
+    torch.cuda.synchronize()
+    for w, y in zip(ws, ys):
+        for t in range(T):
+            ref, a = oracle.gemv(w, x[t], "bf16", threads=oracle_threads())
+            check(y[t], ref, a, "smallm qkv T=%d n=%d t=%d" % (T, w.n_out, t))
+    gate = synth.draw_matrix(rng, 4160, 5120, 64, "bf16")
+    up = synth.draw_matrix(rng, 4160, 5120, 64, "bf16")
+    x, xd = _x(rng, T, 5120)
+    h = nan_like((T, 4160), torch.float32)
+    q.qgemv_int4_smallm([dev_matrix(gate), dev_matrix(up)], xd, [h], epilogue=q.EPI_SWIGLU_PAIR)
+    torch.cuda.synchronize()
+    for t in range(T):
+        ref, a = oracle.swiglu_pair(gate, up, x[t], "bf16")
+        check_f32(to_np64(h[t]), ref, "swiglu pair 4160 T=%d t=%d" % (T, t), a_ref=a)
