@@ -76,20 +76,20 @@ GEMM_SRC = ("kernels.h", "api.cpp", "qgemm.hip")
 MOEP_SRC = ("kernels.h", "api.cpp", "moe_prefill.hip", "router.hip", "topk_wave.h")
 QUANT_SRC = ("kernels.h", "api.cpp", "quant.hip")
 TRAFFIC = {  # workload: (sources, source hash, FETCH_SIZE KiB, WRITE_SIZE KiB), unscaled
-    "dense_ffn_t1": (GEMV_SRC, "5a99be7ac70382f9", 49304.9, 112.6),
-    "moe_top8_t1": (GEMV_SRC, "5a99be7ac70382f9", 10843.3, 32.1),
-    "qkv_multi_t1": (GEMV_SRC, "5a99be7ac70382f9", 7003.6, 16.0),
-    "rms_qkv_multi_t1": (GEMV_SRC, "5a99be7ac70382f9", 7056.1, 16.0),
-    "qkv_smallm_T4": (SMALLM_SRC, "a99060455c95cd70", 7087.2, 48.0),
-    "qkv_smallm_T16": (SMALLM_SRC, "a99060455c95cd70", 7499.1, 192.0),
-    "prefill_gemm_T32": (STREAM_SRC, "d14b9cce6839ce0f", 36096.5, 7616.0),
-    "prefill_gemm_T256": (GEMM_SRC, "c9b865bd804e8ed7", 34845.6, 8704.0),
-    "prefill_gemm_T1024": (GEMM_SRC, "c9b865bd804e8ed7", 138838.3, 34816.0),
-    "prefill_gemm_T4096": (GEMM_SRC, "c9b865bd804e8ed7", 514743.3, 139858.2),
-    "qkv_prefill_T256": (GEMM_SRC, "c9b865bd804e8ed7", 12470.0, 1849.3),
-    "qkv_prefill_T4096": (GEMM_SRC, "c9b865bd804e8ed7", 73278.5, 29651.0),
-    "moe_prefill_top8_T256": (MOEP_SRC, "cfc7140df3e3865a", 188062.5, 23585.5),
-    "quantize_17408x5120_f32_g64": (QUANT_SRC, "c37b41eaf454e8b1", 174101.4, 48960.0),
+    "dense_ffn_t1": (GEMV_SRC, "25b0ebcb18659e33", 49304.1, 111.8),
+    "moe_top8_t1": (GEMV_SRC, "25b0ebcb18659e33", 10830.3, 32.1),
+    "qkv_multi_t1": (GEMV_SRC, "25b0ebcb18659e33", 6997.1, 16.0),
+    "rms_qkv_multi_t1": (GEMV_SRC, "25b0ebcb18659e33", 7059.1, 16.0),
+    "qkv_smallm_T4": (SMALLM_SRC, "058105c0524fc434", 7086.7, 48.0),
+    "qkv_smallm_T16": (SMALLM_SRC, "058105c0524fc434", 7502.6, 192.0),
+    "prefill_gemm_T32": (STREAM_SRC, "5fdf940d49198b3f", 36098.7, 7616.0),
+    "prefill_gemm_T256": (GEMM_SRC, "91401c9b4e72d7e4", 34846.3, 8704.0),
+    "prefill_gemm_T1024": (GEMM_SRC, "91401c9b4e72d7e4", 138838.3, 34816.0),
+    "prefill_gemm_T4096": (GEMM_SRC, "91401c9b4e72d7e4", 514305.6, 139855.6),
+    "qkv_prefill_T256": (GEMM_SRC, "91401c9b4e72d7e4", 12470.0, 1849.3),
+    "qkv_prefill_T4096": (GEMM_SRC, "91401c9b4e72d7e4", 73310.0, 29651.3),
+    "moe_prefill_top8_T256": (MOEP_SRC, "3f83311d3c1f742d", 188044.9, 23585.5),
+    "quantize_17408x5120_f32_g64": (QUANT_SRC, "63fa58cfbedcc4a2", 174101.4, 48960.0),
 }
 
 
