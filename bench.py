@@ -69,7 +69,7 @@ POOL_BYTES = 1 << 30
 # any change to them makes the figure null until it is measured again.
 TRAFFIC_FETCH_SCALE = 262144.0 / 131084.1
 TRAFFIC_WRITE_SCALE = 1.0
-GEMV_SRC = ("kernels.h", "api.cpp", "qgemv.hip", "topk_wave.h")
+GEMV_SRC = ("kernels.h", "api.cpp", "qgemv.hip", "qgemv_xs.hip", "topk_wave.h")
 SMALLM_SRC = ("kernels.h", "api.cpp", "qgemv_mfma.hip")
 STREAM_SRC = ("kernels.h", "api.cpp", "qgemm_stream.hip")
 GEMM_SRC = ("kernels.h", "api.cpp", "qgemm.hip")
@@ -332,7 +332,7 @@ class Copy(Workload):
 class Dense(Workload):
     name = "dense_ffn_t1"
     launches_per_step = 2
-    dominant = "qgemv_kernel EPI_SWIGLU (gate/up) + EPI_STORE (down)"
+    dominant = "qgemv_kernel EPI_SWIGLU (gate/up) + qgemv_xs_kernel (down)"
 
     def __init__(self, q, synth, torch):
         self.q = q
@@ -376,7 +376,7 @@ class Dense(Workload):
         g, u, d = self.pool[0]
         return [("qgemv_kernel EPI_SWIGLU (gate/up pair, bf16 x, fp32 h)", self.gate_up,
                  g.weight_bytes + u.weight_bytes + 5120 * 2 + 17408 * 4, 0.0, 1),
-                ("qgemv_kernel EPI_STORE (down, fp32 h, bf16 y)", self.down,
+                ("qgemv_xs_kernel (down, fp32 h, bf16 y)", self.down,
                  d.weight_bytes + 17408 * 4 + 5120 * 2, 0.0, 1)]
 
 

@@ -72,12 +72,13 @@ class CGemvForm(ctypes.Structure):
 
     def as_dict(self) -> dict:
         d = {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
-        d["kernel"] = "mfma" if self.kernel == FORM_MFMA else "ring"
+        d["kernel"] = {FORM_RING: "ring", FORM_MFMA: "mfma", FORM_XS: "xs"}[self.kernel]
         return d
 
 
 FORM_RING = 0
 FORM_MFMA = 1
+FORM_XS = 2
 CALL_QGEMV = 0
 CALL_RMS_NORM = 1
 CALL_SMALLM = 2

@@ -24,7 +24,7 @@ CALIB_LIB = os.path.join(PKG, "libqint4_calib.so")
 CALIB_SOURCES = ["calib_read.hip"]
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["api.cpp", "qgemv.hip", "qgemv_mfma.hip", "qgemm.hip", "router.hip", "quant.hip", "moe_prefill.hip",
+SOURCES = ["api.cpp", "qgemv.hip", "qgemv_mfma.hip", "qgemv_xs.hip", "qgemm.hip", "router.hip", "quant.hip", "moe_prefill.hip",
            "qgemm_stream.hip"]
 ARCH = "gfx950"
 

@@ -274,7 +274,9 @@ struct MultiPlan {
   bool mfma = false;  // small-M MFMA tiles of 16 rows
   int blk = 0;        // activation rows per launch
   int64_t tiles = 0;  // MFMA: tiles per launch
-  int64_t grid = 0;   // MFMA: workgroups per launch (each takes tiles i, i + grid, ...)
+  int64_t grid = 0;   // MFMA: workgroups per launch (each takes tiles i, i + grid, ...);
+                      // XS: workgroups (each takes rows b, b + grid, ...)
+  bool xs = false;    // activation-stationary float32 GEMV (one matrix, T = 1)
   GemvPlan plan{};    // otherwise: the persistent GEMV plan
 };
 
@@ -310,6 +312,16 @@ qint4_status plan_multi(int n_outs, const int64_t *n_out, int64_t k_in, int grou
     const int ks = gemv_mfma_waves(k_in);
     const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>((int64_t)(kMaxLds / lds), 16 / ks));
     mp->grid = std::min<int64_t>(tiles, per_cu * n_cu);  // launches of 8 or more tokens
+    return QINT4_OK;
+  }
+  // One matrix with float32 activations over long rows: each wave holds its
+  // slice of x in registers (dense FFN down projection, 17408 -> 5120: 16.3 ->
+  // about 13 us).
+  if (!rms && !swiglu && n_outs == 1 && T == 1 && x_dtype == QINT4_F32 &&
+      gemv_xs_supported(n_out[0], k_in, n_cu)) {
+    mp->xs = true;
+    mp->blk = 1;
+    mp->grid = gemv_xs_grid(n_out[0], n_cu);
     return QINT4_OK;
   }
   const int nc = (int)(k_in / 32);
@@ -544,6 +556,26 @@ qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t
                                       tt <= 4 ? tiles : mp.grid, stream);
       if (e != hipSuccess) return fail(QINT4_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(e));
     }
+    return ok();
+  }
+
+  if (mp.xs) {
+    GemvXsParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.codes = ws[0].codes;
+    p.scales = ws[0].scales;
+    p.biases = ws[0].biases;
+    p.x = reinterpret_cast<const float *>(x);
+    p.y = ys[0];
+    p.n_out = (int32_t)ws[0].n_out;
+    p.ncx = (int32_t)(k_in / 32);
+    p.kwb = (int32_t)(k_in / 2);
+    p.sbrow = (int32_t)sbrow_b;
+    p.log2_group = ilog2(ws[0].group_size);
+    p.waves = gemv_xs_waves(k_in);
+    p.y_bf16 = y_dtype == QINT4_BF16;
+    hipError_t e = launch_gemv_xs(p, mp.grid, sb_bf16, stream);
+    if (e != hipSuccess) return fail(QINT4_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return ok();
   }
 
@@ -1371,6 +1403,19 @@ qint4_status qint4_plan_qgemv(int32_t call, int32_t n, const int64_t *n_outs, in
     form->grid = form->tokens <= 4 ? mp.tiles : mp.grid;  // the first launch
     form->tasks = mp.tiles;
     form->waves = gemv_mfma_waves(k_in);
+  } else if (mp.xs) {
+    std::memset(form, 0, sizeof(*form));
+    form->kernel = QINT4_FORM_XS;
+    form->tokens = 1;
+    form->launches = 1;
+    form->grid = mp.grid;
+    form->tasks = n_outs[0];
+    form->waves = gemv_xs_waves(k_in);
+    form->lanes = 64;
+    form->rows_per_task = 1;
+    form->steps_per_task = 1;
+    form->busiest_wave_steps = (n_outs[0] + mp.grid - 1) / mp.grid;
+    form->ring_depth = gemv_xs_depth();
   } else {
     ring_form(mp.plan, multi_xmode(x_dtype, rms), swiglu ? EPI_SWIGLU : EPI_STORE, launches, form);
   }

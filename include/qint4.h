@@ -503,7 +503,12 @@ qint4_status quantize_int4(const void *w, int32_t w_dtype, int64_t n_rows, int64
  * flight: ring_depth 0 is the streaming ring, refilled while it is consumed;
  * 1, 2 or 4 is a ring filled once, taken when no wave has more steps than
  * that.  The small-M MFMA kernels (QINT4_FORM_MFMA) run one 16-row tile per
- * workgroup, its K range split over `waves` waves.  ([FFAI #9], the note on
+ * workgroup, its K range split over `waves` waves.  The activation-stationary
+ * kernel (QINT4_FORM_XS: one matrix, float32 activations, T = 1, k_in from
+ * 4096 to 32768) gives each of a workgroup's `waves` waves a 2048-wide slice
+ * of k_in whose activations it holds in registers; workgroup b of `grid`
+ * takes rows b, b + grid, ... (busiest_wave_steps: rows of the busiest
+ * workgroup; ring_depth: rows in flight per wave).  ([FFAI #9], the note on
  * T=1 decode negative results, structural conclusion: decode is bound by the
  * bandwidth of the expert weight gather; the plan keeps enough loads in
  * flight on every CU.)
@@ -524,21 +529,22 @@ qint4_status quantize_int4(const void *w, int32_t w_dtype, int64_t n_rows, int64
  * Returns QINT4_ERR_SHAPE / _DTYPE / _VALUE / _NULL for arguments the call
  * itself would reject on these grounds.
  */
-enum { QINT4_FORM_RING = 0, QINT4_FORM_MFMA = 1 };
+enum { QINT4_FORM_RING = 0, QINT4_FORM_MFMA = 1, QINT4_FORM_XS = 2 };
 enum { QINT4_CALL_QGEMV = 0, QINT4_CALL_RMS_NORM = 1, QINT4_CALL_SMALLM = 2 };
 
 typedef struct qint4_gemv_form {
-  int32_t kernel;              /* QINT4_FORM_RING or QINT4_FORM_MFMA                 */
+  int32_t kernel;              /* QINT4_FORM_RING, QINT4_FORM_MFMA or QINT4_FORM_XS  */
   int32_t tokens;              /* token template: most activation rows per launch    */
   int64_t launches;            /* launches the call makes                            */
   int64_t grid;                /* workgroups per launch                              */
-  int64_t tasks;               /* ring: tasks; MFMA: 16-row tiles                    */
+  int64_t tasks;               /* ring: tasks; MFMA: 16-row tiles; XS: rows          */
   int32_t waves;               /* waves per workgroup                                */
-  int32_t lanes;               /* ring: lanes per row                                */
+  int32_t lanes;               /* ring, XS: lanes per row (XS: per wave slice)       */
   int32_t rows_per_task;       /* ring                                               */
   int32_t steps_per_task;      /* ring                                               */
-  int64_t busiest_wave_steps;  /* ring: steps of the wave with the most tasks        */
-  int32_t ring_depth;          /* ring: 0 streaming; 1, 2 or 4 one pass              */
+  int64_t busiest_wave_steps;  /* ring: steps of the busiest wave; XS: its rows      */
+  int32_t ring_depth;          /* ring: 0 streaming; 1, 2 or 4 one pass; XS: rows in */
+                               /* flight per wave                                    */
   int32_t reserved;
 } qint4_gemv_form;
 

@@ -47,7 +47,7 @@ def test_qkv_projection_is_one_task_pair_per_wave():
 
 @pytest.mark.parametrize("n_outs,k_in,x_dt,epi,call,T", [
     ([17408, 17408], 5120, "bf16", q.EPI_SWIGLU_PAIR, q.CALL_QGEMV, 1),
-    ([5120], 17408, "f32", q.EPI_NONE, q.CALL_QGEMV, 1),
+    ([5120], 3584, "f32", q.EPI_NONE, q.CALL_QGEMV, 1),
     ([4096, 1024, 1024], 4096, "bf16", q.EPI_NONE, q.CALL_RMS_NORM, 1),
     ([4096, 1024, 1024], 4096, "f32", q.EPI_NONE, q.CALL_RMS_NORM, 1),
     ([5000], 2304, "bf16", q.EPI_NONE, q.CALL_SMALLM, 13),
@@ -84,6 +84,37 @@ def test_smallm_mfma_form():
     assert (f["kernel"], f["tokens"], f["launches"]) == ("mfma", 1, 1)
     f = q.plan_qgemv([5120], 17408, T=16, call=q.CALL_SMALLM, n_cu=N_CU)
     assert (f["kernel"], f["tokens"], f["launches"]) == ("ring", 4, 4)
+
+
+def test_xs_form_for_long_float32_rows():
+    """One matrix with float32 activations and 4096 <= k_in <= 32768 (the dense down projection
+    17408 -> 5120): the activation-stationary kernel, one workgroup per CU (fewer for short
+    matrices), ceil(k_in / 2048) waves, rows dealt b, b + grid, ..., 4 rows in flight."""
+    f = q.plan_qgemv([5120], 17408, x_dtype="f32", n_cu=N_CU)
+    assert (f["kernel"], f["grid"], f["waves"], f["tasks"], f["busiest_wave_steps"], f["ring_depth"]) == \
+        ("xs", N_CU, 9, 5120, 20, 4)
+    f = q.plan_qgemv([100], 6144, x_dtype="f32", n_cu=N_CU)
+    assert (f["kernel"], f["grid"], f["waves"], f["busiest_wave_steps"]) == ("xs", 100, 3, 1)
+    f = q.plan_qgemv([5000], 4160, group_size=64, x_dtype="f32", n_cu=N_CU)
+    assert (f["kernel"], f["waves"], f["busiest_wave_steps"]) == ("xs", 3, 20)
+    f = q.plan_qgemv([256 * N_CU], 4096, x_dtype="f32", n_cu=N_CU)
+    assert (f["kernel"], f["busiest_wave_steps"]) == ("xs", 256)
+    f = q.plan_qgemv([100], 32768, x_dtype="f32", n_cu=N_CU)
+    assert (f["kernel"], f["waves"]) == ("xs", 16)
+
+
+@pytest.mark.parametrize("n_outs,k_in,x_dt,epi,call", [
+    ([5120], 17408, "bf16", q.EPI_NONE, q.CALL_QGEMV),           # bf16 activations
+    ([5120], 3584, "f32", q.EPI_NONE, q.CALL_QGEMV),             # rows shorter than 4096
+    ([100], 32832, "f32", q.EPI_NONE, q.CALL_QGEMV),             # more than 16 slices
+    ([256 * N_CU + 1], 4096, "f32", q.EPI_NONE, q.CALL_QGEMV),   # more than 256 rows per CU
+    ([5120, 5120], 17408, "f32", q.EPI_NONE, q.CALL_QGEMV),      # two matrices
+    ([5120], 17408, "f32", q.EPI_NONE, q.CALL_RMS_NORM),         # RMSNorm prologue
+    ([5120, 5120], 17408, "f32", q.EPI_SWIGLU_PAIR, q.CALL_QGEMV),
+])
+def test_xs_form_only_where_it_applies(n_outs, k_in, x_dt, epi, call):
+    f = q.plan_qgemv(n_outs, k_in, x_dtype=x_dt, epilogue=epi, call=call, n_cu=N_CU)
+    assert f["kernel"] == "ring"
 
 
 def test_plan_query_rejects_what_the_calls_reject():

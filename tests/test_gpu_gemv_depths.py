@@ -30,7 +30,7 @@ GEMV_CASES = [
     (25000, 512, "bf16", 0, 5),
     (8, 1024, "f32", 1, 1),
     (16000, 1024, "f32", 2, 2),
-    (9000, 4096, "f32", 4, 4),
+    (16000, 2048, "f32", 4, 4),
 ]
 
 
