@@ -314,14 +314,15 @@ qint4_status plan_multi(int n_outs, const int64_t *n_out, int64_t k_in, int grou
     mp->grid = std::min<int64_t>(tiles, per_cu * n_cu);  // launches of 8 or more tokens
     return QINT4_OK;
   }
-  // One matrix with float32 activations over long rows: each wave holds its
-  // slice of x in registers (dense FFN down projection, 17408 -> 5120: 16.3 ->
-  // about 13 us).
-  if (!rms && !swiglu && n_outs == 1 && T == 1 && x_dtype == QINT4_F32 &&
-      gemv_xs_supported(n_out[0], k_in, n_cu)) {
+  // One matrix with float32 activations, or the gate/up pair, over long rows:
+  // each wave holds its slice of x in registers (dense FFN 5120 -> 17408 ->
+  // 5120: gate/up 22.6 -> about 20 us, down 16.3 -> 13.0 us).
+  // (Not for small-M calls, whose rows must not depend on T.)
+  if (!batched && !rms && T == 1 && ((n_outs == 1 && !swiglu && x_dtype == QINT4_F32) || swiglu) &&
+      gemv_xs_supported(n_out[0], k_in, streams, n_cu)) {
     mp->xs = true;
     mp->blk = 1;
-    mp->grid = gemv_xs_grid(n_out[0], n_cu);
+    mp->grid = gemv_xs_grid(n_out[0], streams, n_cu);
     return QINT4_OK;
   }
   const int nc = (int)(k_in / 32);
@@ -562,19 +563,22 @@ qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t
   if (mp.xs) {
     GemvXsParams p;
     std::memset(&p, 0, sizeof(p));
-    p.codes = ws[0].codes;
-    p.scales = ws[0].scales;
-    p.biases = ws[0].biases;
-    p.x = reinterpret_cast<const float *>(x);
+    for (int i = 0; i < n; ++i) {  // n = 1, or 2 for the pair
+      p.codes[i] = ws[i].codes;
+      p.scales[i] = ws[i].scales;
+      p.biases[i] = ws[i].biases;
+    }
+    p.x = x;
     p.y = ys[0];
     p.n_out = (int32_t)ws[0].n_out;
     p.ncx = (int32_t)(k_in / 32);
     p.kwb = (int32_t)(k_in / 2);
     p.sbrow = (int32_t)sbrow_b;
     p.log2_group = ilog2(ws[0].group_size);
+    p.log2_lpr = gemv_xs_log2_lanes(k_in);
     p.waves = gemv_xs_waves(k_in);
     p.y_bf16 = y_dtype == QINT4_BF16;
-    hipError_t e = launch_gemv_xs(p, mp.grid, sb_bf16, stream);
+    hipError_t e = launch_gemv_xs(p, mp.grid, sb_bf16, x_dtype == QINT4_BF16, swiglu ? 2 : 1, stream);
     if (e != hipSuccess) return fail(QINT4_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return ok();
   }
@@ -1411,8 +1415,8 @@ qint4_status qint4_plan_qgemv(int32_t call, int32_t n, const int64_t *n_outs, in
     form->grid = mp.grid;
     form->tasks = n_outs[0];
     form->waves = gemv_xs_waves(k_in);
-    form->lanes = 64;
-    form->rows_per_task = 1;
+    form->lanes = 1 << gemv_xs_log2_lanes(k_in);
+    form->rows_per_task = 64 / form->lanes;
     form->steps_per_task = 1;
     form->busiest_wave_steps = (n_outs[0] + mp.grid - 1) / mp.grid;
     form->ring_depth = gemv_xs_depth();

@@ -172,32 +172,38 @@ size_t gemv_mfma_lds_bytes(int tt, int group_size, int64_t k_in, int streams);
 hipError_t launch_gemv_mfma(const GemvParams &p, int tt, int group_size, int sb_bf16, int swiglu,
                             int64_t grid, hipStream_t stream);
 
-// T=1 GEMVs of one matrix with float32 activations and stored outputs over
-// long rows (qgemv_xs.hip): each wave holds a 2048-wide slice of x in
-// registers, gemv_xs_waves(k_in) waves per workgroup cover k_in, and
-// workgroup b of `grid` takes rows b, b + grid, ...
-constexpr int kXsMaxWaves = 16;   // k_in up to 32768
-constexpr int kXsMaxRows = 256;   // rows per workgroup
+// Activation-stationary T=1 GEMVs (qgemv_xs.hip): one matrix with float32
+// activations and stored outputs, or the gate/up pair with the SwiGLU
+// epilogue, over rows of kXsMinK .. kXsMaxWaves * 2048 columns.  Lane j of a
+// row group of wave w holds chunk L w + j of x in registers (L = 1 <<
+// log2_lpr lanes per row, gemv_xs_waves(k_in) waves per workgroup cover
+// k_in), and workgroup b of `grid` takes rows b, b + grid, ...
+constexpr int kXsMaxWaves = 16;    // k_in up to 32768
+constexpr int kXsMaxRows = 256;    // rows per workgroup
 constexpr int64_t kXsMinK = 4096;  // shorter rows keep the streaming GEMV
+constexpr int64_t kXsMinCodes = (int64_t)1 << 25;  // smaller calls too
 struct GemvXsParams {
-  const uint32_t *codes;
-  const void *scales;
-  const void *biases;
-  const float *x;
-  void *y;
+  const uint32_t *codes[2];  // [0]: the matrix, or the gate; [1]: the up matrix
+  const void *scales[2];
+  const void *biases[2];
+  const void *x;       // float32 or bf16 bits
+  void *y;             // outputs, or h = silu(gate) * up
   int32_t n_out;
   int32_t ncx;         // k_in / 32
   int32_t kwb;         // code bytes of one row
   int32_t sbrow;       // scale (= bias) bytes of one row
   int32_t log2_group;
+  int32_t log2_lpr;    // gemv_xs_log2_lanes(k_in)
   int32_t waves;       // gemv_xs_waves(k_in)
   int32_t y_bf16;
 };
-bool gemv_xs_supported(int64_t n_out, int64_t k_in, int n_cu);
-int64_t gemv_xs_grid(int64_t n_out, int n_cu);
+int gemv_xs_log2_lanes(int64_t k_in);
 int gemv_xs_waves(int64_t k_in);
+bool gemv_xs_supported(int64_t n_out, int64_t k_in, int streams, int n_cu);
+int64_t gemv_xs_grid(int64_t n_out, int streams, int n_cu);
 int gemv_xs_depth();  // rows in flight per wave
-hipError_t launch_gemv_xs(const GemvXsParams &p, int64_t grid, int sb_bf16, hipStream_t stream);
+hipError_t launch_gemv_xs(const GemvXsParams &p, int64_t grid, int sb_bf16, int x_bf16, int streams,
+                          hipStream_t stream);
 
 // LDS bytes a GEMV launch needs: per token, the staged activation (padded to
 // ncx_pad chunks) and its chunk sums; then (MoE down) the float32 residual row

@@ -1,35 +1,44 @@
-// qgemv_xs.hip -- T=1 int4 group-affine GEMV with float32 activations for
-// long rows (the dense FFN down projection), "activation-stationary" on gfx950.
+// qgemv_xs.hip -- T=1 int4 group-affine GEMVs with the activation held in
+// registers ("activation-stationary") on gfx950: one matrix with float32
+// activations over long rows (the dense FFN down projection), and the gate/up
+// pair with the SwiGLU epilogue (the dense FFN gate/up projection).
 //
 // Sources (by page title and passage):
 //   [FFAI #14] thewafflehaus/FFAI pull 14, "feat(everything-bagel): clean
 //              migration of PR #9 + #10 onto updated dev": int4 GEMV wrapper
 //              (weight, scales, biases, in_dim, group_size); the down
 //              projection reads the float32 SwiGLU intermediate.
+//   [FFAI #9]  thewafflehaus/FFAI pull 9, "Everything Bagel": fused swiglu,
+//              h = silu(gate) * up with silu(g) = g / (1 + exp(-g)).
 //
 // Per row and group the product is the affine form of the GEMV family,
 //     sum_k (s q_k + b) x_k = s * sum_k q_k x_k + b * sum_k x_k,
-// with q_k x_k accumulated in float32 (q from v_cvt_f32_ubyte of the masked
-// code bytes, as in the streaming GEMV's float32 path).
+// accumulated in float32: for float32 activations q comes from
+// v_cvt_f32_ubyte of the masked code bytes; for bf16 activations a nibble
+// pair (q_i, q_{i+4}) of a word becomes the exact bf16 pair (128 + q_i,
+// 128 + q_{i+4}) (bits 0x4300 | q) for v_dot2_f32_bf16, and 128 * sum x is
+// removed per chunk, as in the streaming GEMV.
 //
 // Work decomposition (gfx950 specific, not from the pages):
-//   * Each wave owns a 2048-wide slice of k_in: lane l of wave w takes the
-//     32-code chunk c = 64 w + l of every row and keeps its 32 activation
-//     values in registers for the whole launch (nothing is staged in LDS, so
-//     the dot products issue no LDS reads).  A workgroup's waves cover k_in
-//     (ceil(k_in / 2048) of them; lanes past the last chunk load nothing).
+//   * L lanes (32 or 64) cover one row, so a wave takes 64 / L rows per
+//     step.  Lane j of a row group in wave w takes the 32-code chunk
+//     c = L w + j of its rows and keeps that chunk's 32 activation values in
+//     registers for the whole launch: nothing is staged in LDS and the dot
+//     products issue no LDS reads.  A workgroup's ceil(k_in / 32 / L) waves
+//     cover k_in; lanes past the last chunk load nothing.
 //   * Workgroup b of G takes rows b, b + G, b + 2G, ...: at any moment the
-//     grid streams one compact band of the matrix, and every wave reads one
-//     1 KB span of each row (64 lanes x 16 contiguous bytes).
-//   * Each wave keeps D rows of code, scale and bias loads in flight; the
-//     loads sit between scheduling barriers so they are issued where the
-//     ring needs them (the compiler otherwise gathers them at the end of the
-//     loop body and waits for all of them at its top).
-//   * Every 4 rows the 4 per-lane partials are reduced across the wave:
-//     one permlane32 swap per pair of rows, one permlane16 swap, then DPP
-//     within rows of 16 lanes, leaving row r of the block in the 16 lanes
-//     (bit 5, bit 4) = (r >> 1, r & 1).  The wave's row sums go to LDS and,
-//     after one workgroup barrier, are summed in wave order and stored.
+//     grid streams one compact band of each matrix, each row group of a wave
+//     reading L * 16 contiguous bytes of a row per stream.
+//   * Each wave keeps 4 rows of code, scale and bias loads (per stream) in
+//     flight; the loads sit between scheduling barriers, so they are issued
+//     where the ring needs them (the compiler otherwise gathers them at the
+//     end of the loop body and waits for all of them at its top).
+//   * Every 4 rows the per-lane partials are reduced across the wave
+//     (permlane32 / permlane16 swaps, then DPP within rows of 16 lanes),
+//     leaving row r of the block in the 16 lanes whose bits (5, 4) are
+//     (r >> 1, r & 1).  Each wave's row sums go to LDS; after one workgroup
+//     barrier they are summed in wave order, and the epilogue (SwiGLU for the
+//     pair) runs before the store.
 #include <algorithm>
 
 #include "kernels.h"
@@ -38,7 +47,9 @@ namespace qint4 {
 namespace {
 
 constexpr uint32_t kOutOfRange = 0x80000000u;
-constexpr int kXsDepth = 4;  // rows in flight per wave (8 measured slower)
+constexpr int kXsRowsInFlight = 4;  // per wave (8 measured slower on the down projection)
+
+typedef __bf16 xs_bf16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t xs_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
@@ -62,154 +73,298 @@ __device__ __forceinline__ float xs_sb_value(uint32_t bits) {
   return __uint_as_float(SBT == 1 ? bits << 16 : bits);
 }
 
+__device__ __forceinline__ float xs_bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float xs_bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
 template <int CTRL>
 __device__ __forceinline__ float xs_dpp(float v) {
   return __builtin_bit_cast(float,
                             __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
-template <int SBT, int D>
+// Sum within aligned groups of 16 lanes (every lane gets its group's sum).
+__device__ __forceinline__ float xs_sum16(float t) {
+  t += xs_dpp<0xB1>(t);   // quad_perm [1,0,3,2]
+  t += xs_dpp<0x4E>(t);   // quad_perm [2,3,0,1]
+  t += xs_dpp<0x141>(t);  // row_half_mirror
+  t += xs_dpp<0x140>(t);  // row_mirror
+  return t;
+}
+
+// The activation of one chunk in the form the dot product takes: float32
+// values in element order (XB = false) or the 16 bf16 pairs
+// (x[8 jj + i], x[8 jj + i + 4]) of the nibble pairs (XB = true).
+template <bool XB>
+struct XsChunk {
+  uint32_t v[XB ? 16 : 32];
+};
+
+// sum over the chunk of q_k x_k (float32 activations)
+__device__ __forceinline__ float xs_dot_f32(const uint4 q, const XsChunk<false> &x) {
+  const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
+  float a[4];  // one chain per word
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    // bytes of lo: nibbles 0, 2, 4, 6; of hi: nibbles 1, 3, 5, 7
+    uint32_t lo = wd[jj] & 0x0F0F0F0Fu, hi = (wd[jj] >> 4) & 0x0F0F0F0Fu;
+    asm("" : "+v"(lo), "+v"(hi));  // keep the byte split (v_cvt_f32_ubyte{0..3})
+    const uint32_t *xe = x.v + 8 * jj;
+    float t = (float)(lo & 0xFFu) * __uint_as_float(xe[0]);
+    t = fmaf((float)(hi & 0xFFu), __uint_as_float(xe[1]), t);
+    t = fmaf((float)((lo >> 8) & 0xFFu), __uint_as_float(xe[2]), t);
+    t = fmaf((float)((hi >> 8) & 0xFFu), __uint_as_float(xe[3]), t);
+    t = fmaf((float)((lo >> 16) & 0xFFu), __uint_as_float(xe[4]), t);
+    t = fmaf((float)((hi >> 16) & 0xFFu), __uint_as_float(xe[5]), t);
+    t = fmaf((float)(lo >> 24), __uint_as_float(xe[6]), t);
+    t = fmaf((float)(hi >> 24), __uint_as_float(xe[7]), t);
+    a[jj] = t;
+  }
+  return (a[0] + a[1]) + (a[2] + a[3]);
+}
+
+// sum over the chunk of (128 + q_k) x_k (bf16 activations)
+__device__ __forceinline__ float xs_dot_bf16(const uint4 q, const XsChunk<true> &x, uint32_t magic) {
+  const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
+  float a[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t pq = ((wd[jj] >> (4 * i)) & 0x000F000Fu) | magic;
+      t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(xs_bf16x2_t, pq),
+                                          __builtin_bit_cast(xs_bf16x2_t, x.v[4 * jj + i]), t, false);
+    }
+    a[jj] = t;
+  }
+  return (a[0] + a[1]) + (a[2] + a[3]);
+}
+
+// XB: bf16 activations; NS: code streams (1 stored outputs, 2 the gate/up
+// pair); L2: log2 of the lanes per row (5 or 6).
+template <int SBT, bool XB, int NS, int L2>
 __global__ void __launch_bounds__(kXsMaxWaves * 64) qgemv_xs_kernel(const GemvXsParams p) {
-  static_assert(D % 4 == 0, "rows are reduced in blocks of 4");
+  constexpr int L = 1 << L2;
+  constexpr int RPS = 64 / L;                  // rows per step
+  constexpr int D = kXsRowsInFlight / RPS;     // steps in flight
+  constexpr int SPB = 4 / RPS;                 // steps per block of 4 rows
   constexpr uint32_t SBB = SBT == 1 ? 2u : 4u;
-  // per-row sums of each wave; row kXsMaxRows takes the lanes that hold no row
-  __shared__ float part[kXsMaxRows + 1][kXsMaxWaves + 1];
+  constexpr uint32_t XCB = XB ? 64u : 128u;    // activation bytes of one chunk
+  static_assert(L2 == 5 || L2 == 6, "32 or 64 lanes per row");
+  // per-row sums of each wave and stream; row kXsMaxRows takes the lanes that
+  // hold no row
+  __shared__ float part[NS][kXsMaxRows + 1][kXsMaxWaves + 1];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int W = p.waves;
-  const int c = 64 * w + lane;  // this lane's chunk
+  const int sg = lane >> L2;              // row group of the lane inside a step
+  const int c = L * w + (lane & (L - 1));  // this lane's chunk
   const bool active = c < p.ncx;
   const int G = (int)gridDim.x, b = (int)blockIdx.x;
   const int nr = (p.n_out - b + G - 1) / G;  // rows of this workgroup, <= kXsMaxRows
 
-  const __amdgpu_buffer_rsrc_t rx = xs_rsrc(p.x, (uint32_t)p.ncx * 128u);
-  const __amdgpu_buffer_rsrc_t rc = xs_rsrc(p.codes, (uint32_t)p.n_out * (uint32_t)p.kwb);
-  const __amdgpu_buffer_rsrc_t rs = xs_rsrc(p.scales, (uint32_t)p.n_out * (uint32_t)p.sbrow);
-  const __amdgpu_buffer_rsrc_t rb = xs_rsrc(p.biases, (uint32_t)p.n_out * (uint32_t)p.sbrow);
-
-  // the chunk's 32 activation values, element order
-  float xr[32];
-  {
-    const uint32_t xo = active ? (uint32_t)c * 128u : kOutOfRange;
+  const __amdgpu_buffer_rsrc_t rx = xs_rsrc(p.x, (uint32_t)p.ncx * XCB);
+  __amdgpu_buffer_rsrc_t rc[NS], rs[NS], rb[NS];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint4 v = xs_load16(rx, xo + 16u * i);
-      xr[4 * i] = __uint_as_float(v.x);
-      xr[4 * i + 1] = __uint_as_float(v.y);
-      xr[4 * i + 2] = __uint_as_float(v.z);
-      xr[4 * i + 3] = __uint_as_float(v.w);
-    }
+  for (int s = 0; s < NS; ++s) {
+    rc[s] = xs_rsrc(p.codes[s], (uint32_t)p.n_out * (uint32_t)p.kwb);
+    rs[s] = xs_rsrc(p.scales[s], (uint32_t)p.n_out * (uint32_t)p.sbrow);
+    rb[s] = xs_rsrc(p.biases[s], (uint32_t)p.n_out * (uint32_t)p.sbrow);
   }
 
-  const uint32_t lane_c = (uint32_t)c * 16u;
-  const uint32_t lane_s = (((uint32_t)c * 32u) >> p.log2_group) * SBB;
-  uint4 q[D];
-  uint32_t sv[D], bv[D];
-  int issued = 0;  // rows issued by this wave (uniform)
+  // the chunk's activation: loads first, turned into registers after the
+  // first code loads are issued
+  constexpr int XV = XB ? 4 : 8;
+  uint4 xv[XV];
+  {
+    const uint32_t xo = active ? (uint32_t)c * XCB : kOutOfRange;
+#pragma unroll
+    for (int i = 0; i < XV; ++i) xv[i] = xs_load16(rx, xo + 16u * i);
+  }
+
+  // byte offsets of this lane's next row: a running sum, advanced by the
+  // (uniform) distance between a wave's consecutive steps
+  const uint32_t row0 = (uint32_t)(b + G * sg);
+  uint32_t run_c = row0 * (uint32_t)p.kwb + (uint32_t)c * 16u;
+  uint32_t run_s = row0 * (uint32_t)p.sbrow + (((uint32_t)c * 32u) >> p.log2_group) * SBB;
+  const uint32_t step_c = (uint32_t)(RPS * G) * (uint32_t)p.kwb;
+  const uint32_t step_s = (uint32_t)(RPS * G) * (uint32_t)p.sbrow;
+  uint4 q[D][NS];
+  uint32_t sv[D][NS], bv[D][NS];
+  int issued = 0;  // steps issued by this wave (uniform)
   auto issue = [&](int u) {
-    // rows past the workgroup's last are out of range: the load is still
-    // issued, so the number in flight, and every wait, is static
-    const bool ok = active && issued < nr;
-    const uint32_t row = (uint32_t)(b + G * issued);
-    const uint32_t oc = ok ? row * (uint32_t)p.kwb + lane_c : kOutOfRange;
-    const uint32_t os = ok ? row * (uint32_t)p.sbrow + lane_s : kOutOfRange;
+    // rows past the workgroup's last are out of range: the loads are still
+    // issued, so the number in flight, and every wait, is static (the running
+    // offsets may wrap there; they are not used)
+    const bool ok = active && RPS * issued + sg < nr;
+    const uint32_t oc = ok ? run_c : kOutOfRange;
+    const uint32_t os = ok ? run_s : kOutOfRange;
     __builtin_amdgcn_sched_barrier(0);
-    q[u] = xs_load16(rc, oc);
-    sv[u] = xs_load_sb<SBT>(rs, os);
-    bv[u] = xs_load_sb<SBT>(rb, os);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      q[u][s] = xs_load16(rc[s], oc);
+      sv[u][s] = xs_load_sb<SBT>(rs[s], os);
+      bv[u][s] = xs_load_sb<SBT>(rb[s], os);
+    }
     __builtin_amdgcn_sched_barrier(0);
+    run_c += step_c;
+    run_s += step_s;
     ++issued;
   };
 #pragma unroll
   for (int u = 0; u < D; ++u) issue(u);
 
-  float xs = 0.f;
+  XsChunk<XB> xc;
+  float xs = 0.f;  // sum of the chunk's activation values
+  if constexpr (XB) {
 #pragma unroll
-  for (int i = 0; i < 32; ++i) xs += xr[i];
-  // The slice has arrived (xs waited for it).  Redefining the registers here
-  // keeps the compiler from treating the loop below as a consumer of loads
-  // issued before it, for which it would wait on every load at the loop top.
+    for (int jj = 0; jj < 4; ++jj) {
+      const uint32_t w0 = xv[jj].x, w1 = xv[jj].y, w2 = xv[jj].z, w3 = xv[jj].w;  // x[8jj .. 8jj+7]
+      xc.v[4 * jj + 0] = (w0 & 0xFFFFu) | (w2 << 16);
+      xc.v[4 * jj + 1] = (w0 >> 16) | (w2 & 0xFFFF0000u);
+      xc.v[4 * jj + 2] = (w1 & 0xFFFFu) | (w3 << 16);
+      xc.v[4 * jj + 3] = (w1 >> 16) | (w3 & 0xFFFF0000u);
+      xs += ((xs_bf16_lo(w0) + xs_bf16_hi(w0)) + (xs_bf16_lo(w1) + xs_bf16_hi(w1))) +
+            ((xs_bf16_lo(w2) + xs_bf16_hi(w2)) + (xs_bf16_lo(w3) + xs_bf16_hi(w3)));
+    }
+  } else {
 #pragma unroll
-  for (int i = 0; i < 32; ++i) asm volatile("" : "+v"(xr[i]));
+    for (int i = 0; i < 8; ++i) {
+      xc.v[4 * i] = xv[i].x;
+      xc.v[4 * i + 1] = xv[i].y;
+      xc.v[4 * i + 2] = xv[i].z;
+      xc.v[4 * i + 3] = xv[i].w;
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) xs += __uint_as_float(xc.v[i]);
+  }
+  // The chunk has arrived (xs waited for it).  Redefining its registers keeps
+  // the compiler from treating the loop below as a consumer of loads issued
+  // before it, for which it would wait on every load at the loop top.
+#pragma unroll
+  for (int i = 0; i < (XB ? 16 : 32); ++i) asm volatile("" : "+v"(xc.v[i]));
+  asm volatile("" : "+v"(xs));
+  uint32_t magic = 0x43004300u;
+  asm volatile("" : "+v"(magic));  // a VGPR operand, so the AND-OR stays one VOP3
+  const float corr = XB ? -128.f * xs : 0.f;
 
-  for (int base = 0; base < nr; base += D) {
+  const int nsteps = (nr + RPS - 1) / RPS;
+  for (int base = 0; base < nsteps; base += D) {
 #pragma unroll
-    for (int blk = 0; blk < D / 4; ++blk) {
-      float v[4];
+    for (int blk = 0; blk < D / SPB; ++blk) {
+      float v[NS][SPB];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int u = 4 * blk + i;
-        const uint32_t wd[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
-        float a[4];  // one chain per word
+      for (int i = 0; i < SPB; ++i) {
+        const int u = SPB * blk + i;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          // bytes of lo: nibbles 0, 2, 4, 6; of hi: nibbles 1, 3, 5, 7
-          uint32_t lo = wd[jj] & 0x0F0F0F0Fu, hi = (wd[jj] >> 4) & 0x0F0F0F0Fu;
-          asm("" : "+v"(lo), "+v"(hi));  // keep the byte split (v_cvt_f32_ubyte{0..3})
-          const float *xe = xr + 8 * jj;
-          float t = (float)(lo & 0xFFu) * xe[0];
-          t = fmaf((float)(hi & 0xFFu), xe[1], t);
-          t = fmaf((float)((lo >> 8) & 0xFFu), xe[2], t);
-          t = fmaf((float)((hi >> 8) & 0xFFu), xe[3], t);
-          t = fmaf((float)((lo >> 16) & 0xFFu), xe[4], t);
-          t = fmaf((float)((hi >> 16) & 0xFFu), xe[5], t);
-          t = fmaf((float)(lo >> 24), xe[6], t);
-          t = fmaf((float)(hi >> 24), xe[7], t);
-          a[jj] = t;
+        for (int s = 0; s < NS; ++s) {
+          float d;
+          if constexpr (XB)
+            d = xs_dot_bf16(q[u][s], xc, magic) + corr;
+          else
+            d = xs_dot_f32(q[u][s], xc);
+          v[s][i] = fmaf(xs_sb_value<SBT>(sv[u][s]), d, xs_sb_value<SBT>(bv[u][s]) * xs);
         }
-        const float d = (a[0] + a[1]) + (a[2] + a[3]);
-        v[i] = fmaf(xs_sb_value<SBT>(sv[u]), d, xs_sb_value<SBT>(bv[u]) * xs);
         issue(u);
       }
-      // rows base + 4 blk + r, r = 0..3, across the wave
-      auto r0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[0]), __float_as_uint(v[2]), false, false);
-      auto r1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[1]), __float_as_uint(v[3]), false, false);
-      const float s0 = __uint_as_float(r0[0]) + __uint_as_float(r0[1]);  // rows 0 | 2
-      const float s1 = __uint_as_float(r1[0]) + __uint_as_float(r1[1]);  // rows 1 | 3
-      auto r2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(s0), __float_as_uint(s1), false, false);
-      float t = __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
-      t += xs_dpp<0xB1>(t);   // quad_perm [1,0,3,2]
-      t += xs_dpp<0x4E>(t);   // quad_perm [2,3,0,1]
-      t += xs_dpp<0x141>(t);  // row_half_mirror
-      t += xs_dpp<0x140>(t);  // row_mirror
-      const int rr = base + 4 * blk + 2 * ((lane >> 5) & 1) + ((lane >> 4) & 1);
-      part[((lane & 15) == 0 && rr < nr) ? rr : kXsMaxRows][w] = t;
+      // the block's 4 rows across the wave; row r ends in the 16 lanes with
+      // (bit 5, bit 4) = (r >> 1, r & 1)
+      const int step0 = base + SPB * blk;
+      int rr;
+      if constexpr (L2 == 6) {
+        rr = RPS * step0 + 2 * ((lane >> 5) & 1) + ((lane >> 4) & 1);
+      } else {
+        // step step0 + (bit 4), row group (bit 5)
+        rr = RPS * (step0 + ((lane >> 4) & 1)) + ((lane >> 5) & 1);
+      }
+      const int slot = ((lane & 15) == 0 && rr < nr) ? rr : kXsMaxRows;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        float t;
+        if constexpr (L2 == 6) {
+          // steps i = 0..3 hold rows i; pair rows (0, 2) and (1, 3) across the halves
+          auto r0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[s][0]), __float_as_uint(v[s][2]), false, false);
+          auto r1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[s][1]), __float_as_uint(v[s][3]), false, false);
+          const float s0 = __uint_as_float(r0[0]) + __uint_as_float(r0[1]);
+          const float s1 = __uint_as_float(r1[0]) + __uint_as_float(r1[1]);
+          auto r2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(s0), __float_as_uint(s1), false, false);
+          t = __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
+        } else {
+          // steps i = 0, 1 hold rows 2 i + (bit 5)
+          auto r2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[s][0]), __float_as_uint(v[s][1]), false, false);
+          t = __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
+        }
+        part[s][slot][w] = xs_sum16(t);
+      }
     }
   }
   __syncthreads();
   for (int t = (int)threadIdx.x; t < nr; t += W * 64) {
-    float s = 0.f;
-    for (int k = 0; k < W; ++k) s += part[t][k];
+    float acc[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      acc[s] = 0.f;
+      for (int k = 0; k < W; ++k) acc[s] += part[s][t][k];
+    }
+    float out = acc[0];
+    if constexpr (NS == 2) out = (acc[0] / (1.f + __expf(-acc[0]))) * acc[1];  // silu(gate) * up
     const int64_t row = (int64_t)b + (int64_t)G * t;
     if (p.y_bf16)
-      reinterpret_cast<__bf16 *>(p.y)[row] = (__bf16)s;
+      reinterpret_cast<__bf16 *>(p.y)[row] = (__bf16)out;
     else
-      reinterpret_cast<float *>(p.y)[row] = s;
+      reinterpret_cast<float *>(p.y)[row] = out;
   }
+}
+
+template <int SBT, bool XB, int NS>
+hipError_t xs_launch(const GemvXsParams &p, int64_t grid, hipStream_t stream) {
+  auto kern = p.log2_lpr == 5 ? qgemv_xs_kernel<SBT, XB, NS, 5> : qgemv_xs_kernel<SBT, XB, NS, 6>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(p.waves * 64), 0, stream, p);
+  return hipGetLastError();
 }
 
 }  // namespace
 
-bool gemv_xs_supported(int64_t n_out, int64_t k_in, int n_cu) {
+// Lanes per row: 32 while that needs at most kXsMaxWaves waves (k_in up to
+// 16384), else 64.
+int gemv_xs_log2_lanes(int64_t k_in) { return (k_in / 32 + 31) / 32 <= kXsMaxWaves ? 5 : 6; }
+
+int gemv_xs_waves(int64_t k_in) {
+  const int64_t L = (int64_t)1 << gemv_xs_log2_lanes(k_in);
+  return (int)((k_in / 32 + L - 1) / L);
+}
+
+// Rows of kXsMinK or more columns, and at least kXsMinCodes codes in all
+// (the 4096 x 4096 float32 GEMV, 16.8 M codes, stays faster on the
+// streaming GEMV: 4.9 against 5.2 us).
+bool gemv_xs_supported(int64_t n_out, int64_t k_in, int streams, int n_cu) {
   if (k_in < kXsMinK || k_in > (int64_t)kXsMaxWaves * 2048 || k_in % 32 != 0) return false;
-  const int64_t grid = std::min<int64_t>(n_cu, n_out);
+  if (n_out * k_in * streams < kXsMinCodes) return false;
+  const int64_t grid = gemv_xs_grid(n_out, streams, n_cu);
   return grid >= 1 && (n_out + grid - 1) / grid <= kXsMaxRows;
 }
 
-int64_t gemv_xs_grid(int64_t n_out, int n_cu) { return std::min<int64_t>(n_cu, n_out); }
+// One workgroup per CU for stored outputs; four per CU for the gate/up pair
+// (17408 x 5120 pair: 23.2 us at one per CU, 21.2 us at four, measured).
+int64_t gemv_xs_grid(int64_t n_out, int streams, int n_cu) {
+  return std::min<int64_t>((int64_t)n_cu * (streams == 2 ? 4 : 1), n_out);
+}
 
-int gemv_xs_waves(int64_t k_in) { return (int)((k_in / 32 + 63) / 64); }
+int gemv_xs_depth() { return kXsRowsInFlight; }
 
-int gemv_xs_depth() { return kXsDepth; }
-
-hipError_t launch_gemv_xs(const GemvXsParams &p, int64_t grid, int sb_bf16, hipStream_t stream) {
-  if (p.waves != gemv_xs_waves((int64_t)p.ncx * 32) || p.waves < 1 || p.waves > kXsMaxWaves ||
-      grid < 1 || grid > p.n_out || ((int64_t)p.n_out + grid - 1) / grid > kXsMaxRows)
+hipError_t launch_gemv_xs(const GemvXsParams &p, int64_t grid, int sb_bf16, int x_bf16, int streams,
+                          hipStream_t stream) {
+  const int64_t k_in = (int64_t)p.ncx * 32;
+  if (p.log2_lpr != gemv_xs_log2_lanes(k_in) || p.waves != gemv_xs_waves(k_in) || p.waves < 1 ||
+      p.waves > kXsMaxWaves || grid < 1 || grid > p.n_out ||
+      ((int64_t)p.n_out + grid - 1) / grid > kXsMaxRows || (streams != 1 && streams != 2))
     return hipErrorInvalidValue;
-  auto kern = sb_bf16 ? qgemv_xs_kernel<1, kXsDepth> : qgemv_xs_kernel<0, kXsDepth>;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(p.waves * 64), 0, stream, p);
-  return hipGetLastError();
+  if (streams == 2)
+    return x_bf16 ? (sb_bf16 ? xs_launch<1, true, 2>(p, grid, stream) : xs_launch<0, true, 2>(p, grid, stream))
+                  : (sb_bf16 ? xs_launch<1, false, 2>(p, grid, stream) : xs_launch<0, false, 2>(p, grid, stream));
+  return x_bf16 ? (sb_bf16 ? xs_launch<1, true, 1>(p, grid, stream) : xs_launch<0, true, 1>(p, grid, stream))
+                : (sb_bf16 ? xs_launch<1, false, 1>(p, grid, stream) : xs_launch<0, false, 1>(p, grid, stream));
 }
 
 }  // namespace qint4

@@ -46,7 +46,7 @@ def test_qkv_projection_is_one_task_pair_per_wave():
 
 
 @pytest.mark.parametrize("n_outs,k_in,x_dt,epi,call,T", [
-    ([17408, 17408], 5120, "bf16", q.EPI_SWIGLU_PAIR, q.CALL_QGEMV, 1),
+    ([2000, 2000], 1280, "bf16", q.EPI_SWIGLU_PAIR, q.CALL_QGEMV, 1),
     ([5120], 3584, "f32", q.EPI_NONE, q.CALL_QGEMV, 1),
     ([4096, 1024, 1024], 4096, "bf16", q.EPI_NONE, q.CALL_RMS_NORM, 1),
     ([4096, 1024, 1024], 4096, "f32", q.EPI_NONE, q.CALL_RMS_NORM, 1),
@@ -87,34 +87,50 @@ def test_smallm_mfma_form():
 
 
 def test_xs_form_for_long_float32_rows():
-    """One matrix with float32 activations and 4096 <= k_in <= 32768 (the dense down projection
-    17408 -> 5120): the activation-stationary kernel, one workgroup per CU (fewer for short
-    matrices), ceil(k_in / 2048) waves, rows dealt b, b + grid, ..., 4 rows in flight."""
+    """One matrix with float32 activations, 4096 <= k_in <= 32768 and at least 2^25 codes (the
+    dense down projection 17408 -> 5120): the activation-stationary kernel, one workgroup per CU,
+    32 lanes a row (two rows a step) while that takes at most 16 waves, else 64."""
     f = q.plan_qgemv([5120], 17408, x_dtype="f32", n_cu=N_CU)
-    assert (f["kernel"], f["grid"], f["waves"], f["tasks"], f["busiest_wave_steps"], f["ring_depth"]) == \
-        ("xs", N_CU, 9, 5120, 20, 4)
-    f = q.plan_qgemv([100], 6144, x_dtype="f32", n_cu=N_CU)
-    assert (f["kernel"], f["grid"], f["waves"], f["busiest_wave_steps"]) == ("xs", 100, 3, 1)
-    f = q.plan_qgemv([5000], 4160, group_size=64, x_dtype="f32", n_cu=N_CU)
-    assert (f["kernel"], f["waves"], f["busiest_wave_steps"]) == ("xs", 3, 20)
+    assert (f["kernel"], f["grid"], f["waves"], f["lanes"], f["tasks"], f["busiest_wave_steps"],
+            f["ring_depth"]) == ("xs", N_CU, 9, 64, 5120, 20, 4)
+    f = q.plan_qgemv([5000], 8192, x_dtype="f32", n_cu=N_CU)
+    assert (f["kernel"], f["waves"], f["lanes"], f["rows_per_task"], f["busiest_wave_steps"]) == \
+        ("xs", 8, 32, 2, 20)
+    f = q.plan_qgemv([4100], 8320, group_size=32, x_dtype="f32", n_cu=N_CU)
+    assert (f["kernel"], f["waves"], f["lanes"]) == ("xs", 9, 32)
     f = q.plan_qgemv([256 * N_CU], 4096, x_dtype="f32", n_cu=N_CU)
     assert (f["kernel"], f["busiest_wave_steps"]) == ("xs", 256)
-    f = q.plan_qgemv([100], 32768, x_dtype="f32", n_cu=N_CU)
-    assert (f["kernel"], f["waves"]) == ("xs", 16)
+    f = q.plan_qgemv([2049], 32768, x_dtype="f32", n_cu=N_CU)
+    assert (f["kernel"], f["waves"], f["lanes"]) == ("xs", 16, 64)
 
 
 @pytest.mark.parametrize("n_outs,k_in,x_dt,epi,call", [
     ([5120], 17408, "bf16", q.EPI_NONE, q.CALL_QGEMV),           # bf16 activations
-    ([5120], 3584, "f32", q.EPI_NONE, q.CALL_QGEMV),             # rows shorter than 4096
-    ([100], 32832, "f32", q.EPI_NONE, q.CALL_QGEMV),             # more than 16 slices
+    ([9000], 3584, "f32", q.EPI_NONE, q.CALL_QGEMV),             # rows shorter than 4096
+    ([2000], 32832, "f32", q.EPI_NONE, q.CALL_QGEMV),            # more than 16 waves of 64 lanes
+    ([4096], 4096, "f32", q.EPI_NONE, q.CALL_QGEMV),             # fewer than 2^25 codes
     ([256 * N_CU + 1], 4096, "f32", q.EPI_NONE, q.CALL_QGEMV),   # more than 256 rows per CU
     ([5120, 5120], 17408, "f32", q.EPI_NONE, q.CALL_QGEMV),      # two matrices
     ([5120], 17408, "f32", q.EPI_NONE, q.CALL_RMS_NORM),         # RMSNorm prologue
-    ([5120, 5120], 17408, "f32", q.EPI_SWIGLU_PAIR, q.CALL_QGEMV),
+    ([5120, 5120], 3584, "bf16", q.EPI_SWIGLU_PAIR, q.CALL_QGEMV),  # pair, short rows
+    ([5120, 5120], 17408, "bf16", q.EPI_SWIGLU_PAIR, q.CALL_SMALLM),  # small-M call
 ])
 def test_xs_form_only_where_it_applies(n_outs, k_in, x_dt, epi, call):
     f = q.plan_qgemv(n_outs, k_in, x_dtype=x_dt, epilogue=epi, call=call, n_cu=N_CU)
-    assert f["kernel"] == "ring"
+    assert f["kernel"] != "xs"
+
+
+def test_xs_form_for_the_gate_up_pair():
+    """The T=1 gate/up pair with 4096 <= k_in <= 32768 (dense FFN 5120 -> 17408): 32 lanes a
+    row (two rows a step) up to 16384 columns, 64 beyond; four workgroups per CU."""
+    f = q.plan_qgemv([17408, 17408], 5120, epilogue=q.EPI_SWIGLU_PAIR, n_cu=N_CU)
+    assert (f["kernel"], f["grid"], f["waves"], f["lanes"], f["rows_per_task"], f["tasks"],
+            f["busiest_wave_steps"]) == ("xs", 4 * N_CU, 5, 32, 2, 17408, 17)
+    f = q.plan_qgemv([2048, 2048], 17408, x_dtype="f32", epilogue=q.EPI_SWIGLU_PAIR, n_cu=N_CU)
+    assert (f["kernel"], f["waves"], f["lanes"]) == ("xs", 9, 64)
+    f = q.plan_qgemv([1000, 1000], 32768, epilogue=q.EPI_SWIGLU_PAIR, n_cu=N_CU)
+    assert (f["kernel"], f["grid"], f["waves"], f["lanes"], f["busiest_wave_steps"]) == \
+        ("xs", 1000, 16, 64, 1)
 
 
 def test_plan_query_rejects_what_the_calls_reject():

@@ -79,8 +79,8 @@ def test_smallm_ring_forms(T, n_out, k_in, depth, steps):
 SWIGLU_CASES = [
     (8, 2048, 1, 1),
     (8000, 2048, 2, 2),
-    (8, 5120, 4, 3),
-    (1000, 5120, 0, 5),
+    (500, 2112, 4, 3),
+    (2000, 1280, 0, 5),
 ]
 
 

@@ -1,8 +1,9 @@
-"""GPU parity of the activation-stationary GEMV form (float32 activations, one matrix, k_in from
-4096 to 32768) against the fp64 oracle, through the C ABI.  Each case first asserts, through the
-library's plan query, that the call takes that form, so the edges below stay on it: fewer rows
-than CUs (one row per workgroup), rows not a multiple of the grid, a last wave with only a few
-lanes holding a chunk, sixteen waves, and 256 rows per workgroup."""
+"""GPU parity of the activation-stationary GEMV form (qgemv_int4 on one matrix with float32
+activations, qgemv_int4_multi on the gate/up pair; k_in from 4096 to 32768, at least 2^25 codes)
+against the fp64 oracle, through the C ABI.  Each case first asserts, through the library's plan
+query, that the call takes that form, so the edges below stay on it: rows not a multiple of the
+grid, fewer rows than workgroups (one row each), a last wave with few lanes holding a chunk, 32
+and 64 lanes a row, sixteen waves, and 256 rows per workgroup."""
 import numpy as np
 import pytest
 import torch
@@ -25,7 +26,7 @@ def _n_cu():
     return torch.cuda.get_device_properties(0).multi_processor_count
 
 
-def _run(w, x, y_dt):
+def _run_single(w, x, y_dt):
     q = lib()
     f = q.plan_qgemv([w.n_out], w.k_in, group_size=w.group_size, x_dtype="f32")
     assert f["kernel"] == "xs", f
@@ -35,22 +36,22 @@ def _run(w, x, y_dt):
     return y, f
 
 
-# (n_out, k_in, group size): 100 rows < CUs; 333 rows, 1-2 per workgroup; 4160 = 130 chunks, the
-# third wave holding 2; 6144 / g128; 17408 (the dense down projection) with ragged rows;
-# 32768 = 16 waves
-SHAPES = [(100, 6144, 128), (333, 4096, 32), (5000, 4160, 64), (1000, 17408, 64), (257, 32768, 64)]
+# (n_out, k_in, group size): 5000 rows, 19 or 20 per workgroup, 32 lanes a row; 8320 = 260
+# chunks, the ninth wave holding 4 per row group; 16384 / g128, 16 waves of 32 lanes; 17408 (the
+# dense down projection), 64 lanes a row; 32768, 16 waves of 64 lanes
+SINGLE = [(5000, 8192, 64), (4100, 8320, 32), (2100, 16384, 128), (2000, 17408, 64), (2049, 32768, 64)]
 
 
-@pytest.mark.parametrize("n_out,k_in,g", SHAPES)
+@pytest.mark.parametrize("n_out,k_in,g", SINGLE)
 @pytest.mark.parametrize("sb_dt,y_dt", [("bf16", "bf16"), ("f32", "f32"), ("bf16", "f32")])
-def test_xs_shapes_and_dtypes(n_out, k_in, g, sb_dt, y_dt):
+def test_xs_single_shapes_and_dtypes(n_out, k_in, g, sb_dt, y_dt):
     rng = np.random.default_rng(n_out * 17 + k_in + g)
     w = synth.draw_matrix(rng, n_out, k_in, g, sb_dt)
     x = synth.draw_activation(rng, (k_in,), "f32")
-    y, f = _run(w, x, y_dt)
+    y, f = _run_single(w, x, y_dt)
     y_ref, a_ref = oracle.gemv(w, x, "f32", threads=oracle_threads())
-    check(y, y_ref, a_ref, "xs gemv %dx%d g%d %s/%s (grid %d, %d waves)" %
-          (n_out, k_in, g, sb_dt, y_dt, f["grid"], f["waves"]))
+    check(y, y_ref, a_ref, "xs gemv %dx%d g%d %s/%s (grid %d, %d waves of %d lanes)" %
+          (n_out, k_in, g, sb_dt, y_dt, f["grid"], f["waves"], f["lanes"]))
 
 
 def test_xs_most_rows_per_workgroup():
@@ -59,18 +60,43 @@ def test_xs_most_rows_per_workgroup():
     rng = np.random.default_rng(4242)
     w = synth.draw_matrix(rng, n_out, 4096, 64, "bf16")
     x = synth.draw_activation(rng, (4096,), "f32")
-    y, f = _run(w, x, "f32")
+    y, f = _run_single(w, x, "f32")
     assert f["busiest_wave_steps"] == 256
     y_ref, a_ref = oracle.gemv(w, x, "f32", threads=oracle_threads())
     check(y, y_ref, a_ref, "xs gemv %dx4096 (256 rows per workgroup)" % n_out)
 
 
+# (n_out, k_in, x dtype): the dense FFN gate/up pair 17408 x 5120; 6144 columns, 2 or 3 rows per
+# workgroup; 1000 rows < 4 workgroups per CU, 32768 columns (16 waves of 64 lanes); float32
+# activations over 17408 columns
+PAIRS = [(17408, 5120, "bf16"), (3000, 6144, "bf16"), (1000, 32768, "bf16"), (2048, 17408, "f32")]
+
+
+@pytest.mark.parametrize("n_out,k_in,x_dt", PAIRS)
+@pytest.mark.parametrize("sb_dt,h_dt", [("bf16", "f32"), ("f32", "bf16")])
+def test_xs_gate_up_pair(n_out, k_in, x_dt, sb_dt, h_dt):
+    q = lib()
+    f = q.plan_qgemv([n_out, n_out], k_in, x_dtype=x_dt, epilogue=q.EPI_SWIGLU_PAIR)
+    assert f["kernel"] == "xs", f
+    rng = np.random.default_rng(n_out * 5 + k_in)
+    gate = synth.draw_matrix(rng, n_out, k_in, 64, sb_dt)
+    up = synth.draw_matrix(rng, n_out, k_in, 64, sb_dt)
+    x = synth.draw_activation(rng, (k_in,), x_dt)
+    h = nan_like(n_out, TD[h_dt])
+    q.qgemv_int4_multi([dev_matrix(gate), dev_matrix(up)], synth.to_torch(x, x_dt), [h],
+                       epilogue=q.EPI_SWIGLU_PAIR)
+    torch.cuda.synchronize()
+    h_ref, a_ref = oracle.swiglu_pair(gate, up, x, x_dt, threads=oracle_threads())
+    check(h, h_ref, a_ref, "xs gate/up pair %dx%d %s %s/%s (grid %d, %d waves of %d lanes)" %
+          (n_out, k_in, x_dt, sb_dt, h_dt, f["grid"], f["waves"], f["lanes"]))
+
+
 def test_xs_unpack_identity_probe():
-    """s = 1, b = 0 and x = e_k for k at the start, middle and end of every wave's slice: y[o]
+    """s = 1, b = 0 and x = e_k for k at the start, middle and end of the waves' slices: y[o]
     equals code k of row o exactly."""
     q = lib()
     rng = np.random.default_rng(31)
-    n_out, k_in = 300, 4160
+    n_out, k_in = 4100, 8320
     raw = rng.integers(0, 16, size=(n_out, k_in), dtype=np.uint8)
     groups = k_in // 64
     w = synth.QMatrix(codes=synth.pack_codes(raw), scales=np.ones((n_out, groups), np.float32),
@@ -78,7 +104,7 @@ def test_xs_unpack_identity_probe():
                       n_out=n_out, k_in=k_in)
     dw = dev_matrix(w)
     assert q.plan_qgemv([n_out], k_in, x_dtype="f32")["kernel"] == "xs"
-    for k in (0, 1, 7, 31, 32, 2047, 2048, 2049, 4095, 4096, 4127, 4128, 4159):
+    for k in (0, 1, 7, 31, 32, 1023, 1024, 1025, 4095, 4096, 8191, 8192, 8287, 8288, 8319):
         x = np.zeros(k_in, np.float32)
         x[k] = 1.0
         y = nan_like(n_out, torch.float32)
@@ -87,7 +113,7 @@ def test_xs_unpack_identity_probe():
         assert np.array_equal(y.cpu().numpy().astype(np.float64), raw[:, k].astype(np.float64)), k
 
 
-def test_xs_repeatable_and_matches_itself_across_calls():
+def test_xs_repeatable():
     """Two calls on the same inputs give the same bits (fixed reduction order)."""
     q = lib()
     rng = np.random.default_rng(77)
