@@ -76,20 +76,20 @@ GEMM_SRC = ("kernels.h", "api.cpp", "qgemm.hip")
 MOEP_SRC = ("kernels.h", "api.cpp", "moe_prefill.hip", "router.hip", "topk_wave.h")
 QUANT_SRC = ("kernels.h", "api.cpp", "quant.hip")
 TRAFFIC = {  # workload: (sources, source hash, FETCH_SIZE KiB, WRITE_SIZE KiB), unscaled
-    "dense_ffn_t1": (GEMV_SRC, "25b0ebcb18659e33", 49304.1, 111.8),
-    "moe_top8_t1": (GEMV_SRC, "25b0ebcb18659e33", 10830.3, 32.1),
-    "qkv_multi_t1": (GEMV_SRC, "25b0ebcb18659e33", 6997.1, 16.0),
-    "rms_qkv_multi_t1": (GEMV_SRC, "25b0ebcb18659e33", 7059.1, 16.0),
-    "qkv_smallm_T4": (SMALLM_SRC, "058105c0524fc434", 7086.7, 48.0),
-    "qkv_smallm_T16": (SMALLM_SRC, "058105c0524fc434", 7502.6, 192.0),
-    "prefill_gemm_T32": (STREAM_SRC, "5fdf940d49198b3f", 36098.7, 7616.0),
-    "prefill_gemm_T256": (GEMM_SRC, "91401c9b4e72d7e4", 34846.3, 8704.0),
-    "prefill_gemm_T1024": (GEMM_SRC, "91401c9b4e72d7e4", 138838.3, 34816.0),
-    "prefill_gemm_T4096": (GEMM_SRC, "91401c9b4e72d7e4", 514305.6, 139855.6),
-    "qkv_prefill_T256": (GEMM_SRC, "91401c9b4e72d7e4", 12470.0, 1849.3),
-    "qkv_prefill_T4096": (GEMM_SRC, "91401c9b4e72d7e4", 73310.0, 29651.3),
-    "moe_prefill_top8_T256": (MOEP_SRC, "3f83311d3c1f742d", 188044.9, 23585.5),
-    "quantize_17408x5120_f32_g64": (QUANT_SRC, "63fa58cfbedcc4a2", 174101.4, 48960.0),
+    "dense_ffn_t1": (GEMV_SRC, "7dc155591f520df6", 52606.6, 548.9),
+    "moe_top8_t1": (GEMV_SRC, "7dc155591f520df6", 10830.5, 32.1),
+    "qkv_multi_t1": (GEMV_SRC, "7dc155591f520df6", 6997.1, 16.0),
+    "rms_qkv_multi_t1": (GEMV_SRC, "7dc155591f520df6", 7059.1, 16.0),
+    "qkv_smallm_T4": (SMALLM_SRC, "b37944cd34acebaa", 7086.7, 48.0),
+    "qkv_smallm_T16": (SMALLM_SRC, "b37944cd34acebaa", 7502.6, 192.0),
+    "prefill_gemm_T32": (STREAM_SRC, "f4720541ff162c5e", 36105.8, 7616.0),
+    "prefill_gemm_T256": (GEMM_SRC, "531da73ccf42639e", 34844.2, 8704.0),
+    "prefill_gemm_T1024": (GEMM_SRC, "531da73ccf42639e", 138833.1, 34816.0),
+    "prefill_gemm_T4096": (GEMM_SRC, "531da73ccf42639e", 514332.5, 139879.4),
+    "qkv_prefill_T256": (GEMM_SRC, "531da73ccf42639e", 12470.0, 1849.3),
+    "qkv_prefill_T4096": (GEMM_SRC, "531da73ccf42639e", 73538.4, 29651.1),
+    "moe_prefill_top8_T256": (MOEP_SRC, "4ed671db042b1000", 194330.6, 23585.6),
+    "quantize_17408x5120_f32_g64": (QUANT_SRC, "382609fdef2591f3", 174101.4, 48960.0),
 }
 
 
@@ -332,7 +332,7 @@ class Copy(Workload):
 class Dense(Workload):
     name = "dense_ffn_t1"
     launches_per_step = 2
-    dominant = "qgemv_kernel EPI_SWIGLU (gate/up) + qgemv_xs_kernel (down)"
+    dominant = "qgemv_xs_kernel (gate/up pair with SwiGLU, then down)"
 
     def __init__(self, q, synth, torch):
         self.q = q
@@ -374,7 +374,7 @@ class Dense(Workload):
 
     def parts(self):
         g, u, d = self.pool[0]
-        return [("qgemv_kernel EPI_SWIGLU (gate/up pair, bf16 x, fp32 h)", self.gate_up,
+        return [("qgemv_xs_kernel (gate/up pair with SwiGLU, bf16 x, fp32 h)", self.gate_up,
                  g.weight_bytes + u.weight_bytes + 5120 * 2 + 17408 * 4, 0.0, 1),
                 ("qgemv_xs_kernel (down, fp32 h, bf16 y)", self.down,
                  d.weight_bytes + 17408 * 4 + 5120 * 2, 0.0, 1)]
