@@ -197,7 +197,7 @@ constexpr int kMaxWaves = 12;  // waves per workgroup (one persistent workgroup 
 // workgroup's one-pass staging: 4 vectors of 16 bytes per thread.
 template <class TasksFor>
 GemvPlan plan_gemv(int cpr, int n_cu, int xmode, int64_t residual_rows, TasksFor tasks_for,
-                   int tt = 1) {
+                   int tt = 1, int max_rt = 2) {
   GemvPlan best{};
   best.tt = tt;
   double best_cost = 1e300;
@@ -212,7 +212,7 @@ GemvPlan plan_gemv(int cpr, int n_cu, int xmode, int64_t residual_rows, TasksFor
     const int spt = (cpr + L - 1) / L;
     const size_t lds = gemv_lds_bytes(xmode, spt * L, residual_rows, tt);
     if (lds > (size_t)kMaxLds) continue;
-    for (int rt = 1; rt <= 2; ++rt) {
+    for (int rt = 1; rt <= max_rt; ++rt) {
       const int64_t n_tasks = tasks_for(rt * (64 / L));
       for (int w = 1; w <= std::min(kMaxWaves, gemv_max_waves(tt)); ++w) {
         if (residual_rows > (int64_t)w * 64 * 4 * 4) continue;
@@ -360,8 +360,12 @@ qint4_status plan_moe(int64_t hidden, int64_t inter, int32_t top_k, int32_t act_
   // routing in the gate/up launch: 16 floats of LDS hand the ranked ids to every wave
   *gate_up = plan_gemv((int)(hidden / 32), n_cu, xmode_a, routed ? 16 : 0, gu_tasks);
   if (gate_up->waves == 0) return fail(QINT4_ERR_SHAPE, "hidden %lld needs too much LDS", (long long)hidden);
+  // the down projection takes one row group per task: twice the waves of
+  // two-row tasks, so two waves per SIMD overlap their dot products and
+  // reductions (128 experts, top-8, 2048 x 768: 0.2-0.5 us faster per step,
+  // although two-row tasks share their LDS activation reads)
   auto down_tasks = [&](int rpt) { return (hidden + rpt - 1) / rpt; };
-  *down = plan_gemv((int)(inter / 32) * top_k, n_cu, XM_F32, residual ? hidden : 0, down_tasks);
+  *down = plan_gemv((int)(inter / 32) * top_k, n_cu, XM_F32, residual ? hidden : 0, down_tasks, 1, 1);
   if (down->waves == 0)
     return fail(QINT4_ERR_SHAPE, "top_k * inter = %lld needs too much LDS", (long long)(top_k * inter));
   if (gate_up->n_tasks > INT32_MAX || down->n_tasks > INT32_MAX)
