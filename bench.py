@@ -76,20 +76,20 @@ GEMM_SRC = ("kernels.h", "api.cpp", "qgemm.hip")
 MOEP_SRC = ("kernels.h", "api.cpp", "moe_prefill.hip", "router.hip", "topk_wave.h")
 QUANT_SRC = ("kernels.h", "api.cpp", "quant.hip")
 TRAFFIC = {  # workload: (sources, source hash, FETCH_SIZE KiB, WRITE_SIZE KiB), unscaled
-    "dense_ffn_t1": (GEMV_SRC, "7dc155591f520df6", 52606.6, 548.9),
-    "moe_top8_t1": (GEMV_SRC, "7dc155591f520df6", 10830.5, 32.1),
-    "qkv_multi_t1": (GEMV_SRC, "7dc155591f520df6", 6997.1, 16.0),
-    "rms_qkv_multi_t1": (GEMV_SRC, "7dc155591f520df6", 7059.1, 16.0),
-    "qkv_smallm_T4": (SMALLM_SRC, "b37944cd34acebaa", 7086.7, 48.0),
-    "qkv_smallm_T16": (SMALLM_SRC, "b37944cd34acebaa", 7502.6, 192.0),
-    "prefill_gemm_T32": (STREAM_SRC, "f4720541ff162c5e", 36105.8, 7616.0),
-    "prefill_gemm_T256": (GEMM_SRC, "531da73ccf42639e", 34844.2, 8704.0),
-    "prefill_gemm_T1024": (GEMM_SRC, "531da73ccf42639e", 138833.1, 34816.0),
-    "prefill_gemm_T4096": (GEMM_SRC, "531da73ccf42639e", 514332.5, 139879.4),
-    "qkv_prefill_T256": (GEMM_SRC, "531da73ccf42639e", 12470.0, 1849.3),
-    "qkv_prefill_T4096": (GEMM_SRC, "531da73ccf42639e", 73538.4, 29651.1),
-    "moe_prefill_top8_T256": (MOEP_SRC, "4ed671db042b1000", 194330.6, 23585.6),
-    "quantize_17408x5120_f32_g64": (QUANT_SRC, "382609fdef2591f3", 174101.4, 48960.0),
+    "dense_ffn_t1": (GEMV_SRC, "03a54e7c3abe2968", 52604.6, 549.6),
+    "moe_top8_t1": (GEMV_SRC, "03a54e7c3abe2968", 10805.3, 32.1),
+    "qkv_multi_t1": (GEMV_SRC, "03a54e7c3abe2968", 6997.1, 16.0),
+    "rms_qkv_multi_t1": (GEMV_SRC, "03a54e7c3abe2968", 7059.1, 16.0),
+    "qkv_smallm_T4": (SMALLM_SRC, "30401caa647ee234", 7086.7, 48.0),
+    "qkv_smallm_T16": (SMALLM_SRC, "30401caa647ee234", 7502.6, 192.0),
+    "prefill_gemm_T32": (STREAM_SRC, "95ba28ffd103b2d0", 36095.3, 7616.0),
+    "prefill_gemm_T256": (GEMM_SRC, "3f1bcf18866574be", 34844.9, 8704.0),
+    "prefill_gemm_T1024": (GEMM_SRC, "3f1bcf18866574be", 138968.6, 34816.0),
+    "prefill_gemm_T4096": (GEMM_SRC, "3f1bcf18866574be", 514439.0, 139866.8),
+    "qkv_prefill_T256": (GEMM_SRC, "3f1bcf18866574be", 12470.0, 1849.3),
+    "qkv_prefill_T4096": (GEMM_SRC, "3f1bcf18866574be", 73409.8, 29650.6),
+    "moe_prefill_top8_T256": (MOEP_SRC, "34beda4816c26f2e", 188046.9, 23585.5),
+    "quantize_17408x5120_f32_g64": (QUANT_SRC, "780e77792db6bb81", 174101.4, 48960.0),
 }
 
 
