@@ -214,12 +214,29 @@ __device__ __forceinline__ float seg_sum(float v, int l2) {
 
 // The 32 codes of a chunk as 16 bf16 pairs (128 + q_i, 128 + q_{i+4}):
 // pq[4 jj + i] pairs nibbles i and i+4 of word jj.
+// Two words are shifted as one 64-bit value (one v_lshrrev_b64 instead of
+// two 32-bit shifts; the compiler splits a 64-bit shift whose halves are
+// masked); the high word's nibbles that land in the low word's top bits are
+// masked off.
+template <int S>
+__device__ __forceinline__ uint64_t shr64_nibbles(uint64_t w) {
+  uint64_t r;
+  asm("v_lshrrev_b64 %0, %1, %2" : "=v"(r) : "n"(4 * S), "v"(w));
+  return r;
+}
+
 __device__ __forceinline__ void decode_chunk_bf16(const uint4 q, uint32_t magic, uint32_t (&pq)[16]) {
   const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj)
+  for (int h = 0; h < 2; ++h) {
+    const uint64_t w2 = ((uint64_t)w[2 * h + 1] << 32) | w[2 * h];
+    const uint64_t sh[4] = {w2, shr64_nibbles<1>(w2), shr64_nibbles<2>(w2), shr64_nibbles<3>(w2)};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pq[4 * jj + i] = ((w[jj] >> (4 * i)) & 0x000F000Fu) | magic;
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        pq[4 * (2 * h + e) + i] = ((uint32_t)(sh[i] >> (32 * e)) & 0x000F000Fu) | magic;
+  }
 }
 
 // sum over one decoded chunk of (128 + q_k) * x_k, starting from acc.

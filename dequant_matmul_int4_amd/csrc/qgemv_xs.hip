@@ -122,20 +122,38 @@ __device__ __forceinline__ float xs_dot_f32(const uint4 q, const XsChunk<false> 
   return (a[0] + a[1]) + (a[2] + a[3]);
 }
 
+// Two code words shifted right by 4 s bits as one 64-bit value: one
+// v_lshrrev_b64 instead of two 32-bit shifts (the compiler splits a 64-bit
+// shift whose halves are masked).  The high word's low nibbles that move into
+// the top of the low word are masked off by the caller.
+template <int S>
+__device__ __forceinline__ uint64_t xs_shr64(uint64_t w) {
+  uint64_t r;
+  asm("v_lshrrev_b64 %0, %1, %2" : "=v"(r) : "n"(4 * S), "v"(w));
+  return r;
+}
+
 // sum over the chunk of (128 + q_k) x_k (bf16 activations)
 __device__ __forceinline__ float xs_dot_bf16(const uint4 q, const XsChunk<true> &x, uint32_t magic) {
   const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
-  float a[4];
+  float a[4];  // one chain per word
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    float t = 0.f;
+  for (int h = 0; h < 2; ++h) {
+    const uint64_t w2 = ((uint64_t)wd[2 * h + 1] << 32) | wd[2 * h];
+    const uint64_t sh[4] = {w2, xs_shr64<1>(w2), xs_shr64<2>(w2), xs_shr64<3>(w2)};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t pq = ((wd[jj] >> (4 * i)) & 0x000F000Fu) | magic;
-      t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(xs_bf16x2_t, pq),
-                                          __builtin_bit_cast(xs_bf16x2_t, x.v[4 * jj + i]), t, false);
+    for (int e = 0; e < 2; ++e) {
+      const int jj = 2 * h + e;
+      float t = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // nibbles i and i + 4 of word jj
+        const uint32_t pq = ((uint32_t)(sh[i] >> (32 * e)) & 0x000F000Fu) | magic;
+        t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(xs_bf16x2_t, pq),
+                                            __builtin_bit_cast(xs_bf16x2_t, x.v[4 * jj + i]), t, false);
+      }
+      a[jj] = t;
     }
-    a[jj] = t;
   }
   return (a[0] + a[1]) + (a[2] + a[3]);
 }
