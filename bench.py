@@ -76,19 +76,19 @@ GEMM_SRC = ("kernels.h", "api.cpp", "qgemm.hip")
 MOEP_SRC = ("kernels.h", "api.cpp", "moe_prefill.hip", "router.hip", "topk_wave.h")
 QUANT_SRC = ("kernels.h", "api.cpp", "quant.hip")
 TRAFFIC = {  # workload: (sources, source hash, FETCH_SIZE KiB, WRITE_SIZE KiB), unscaled
-    "dense_ffn_t1": (GEMV_SRC, "03a54e7c3abe2968", 52604.6, 549.6),
-    "moe_top8_t1": (GEMV_SRC, "03a54e7c3abe2968", 10805.3, 32.1),
-    "qkv_multi_t1": (GEMV_SRC, "03a54e7c3abe2968", 6997.1, 16.0),
-    "rms_qkv_multi_t1": (GEMV_SRC, "03a54e7c3abe2968", 7059.1, 16.0),
+    "dense_ffn_t1": (GEMV_SRC, "e4fda320485c3ac3", 52624.7, 549.4),
+    "moe_top8_t1": (GEMV_SRC, "e4fda320485c3ac3", 10794.1, 32.1),
+    "qkv_multi_t1": (GEMV_SRC, "e4fda320485c3ac3", 7003.6, 16.0),
+    "rms_qkv_multi_t1": (GEMV_SRC, "e4fda320485c3ac3", 7059.1, 16.0),
     "qkv_smallm_T4": (SMALLM_SRC, "30401caa647ee234", 7086.7, 48.0),
     "qkv_smallm_T16": (SMALLM_SRC, "30401caa647ee234", 7502.6, 192.0),
-    "prefill_gemm_T32": (STREAM_SRC, "95ba28ffd103b2d0", 36095.3, 7616.0),
-    "prefill_gemm_T256": (GEMM_SRC, "3f1bcf18866574be", 34844.9, 8704.0),
-    "prefill_gemm_T1024": (GEMM_SRC, "3f1bcf18866574be", 138968.6, 34816.0),
-    "prefill_gemm_T4096": (GEMM_SRC, "3f1bcf18866574be", 514439.0, 139866.8),
+    "prefill_gemm_T32": (STREAM_SRC, "95ba28ffd103b2d0", 36096.4, 7616.0),
+    "prefill_gemm_T256": (GEMM_SRC, "3f1bcf18866574be", 34845.3, 8704.0),
+    "prefill_gemm_T1024": (GEMM_SRC, "3f1bcf18866574be", 138874.5, 34816.0),
+    "prefill_gemm_T4096": (GEMM_SRC, "3f1bcf18866574be", 514341.4, 139851.5),
     "qkv_prefill_T256": (GEMM_SRC, "3f1bcf18866574be", 12470.0, 1849.3),
-    "qkv_prefill_T4096": (GEMM_SRC, "3f1bcf18866574be", 73409.8, 29650.6),
-    "moe_prefill_top8_T256": (MOEP_SRC, "34beda4816c26f2e", 188046.9, 23585.5),
+    "qkv_prefill_T4096": (GEMM_SRC, "3f1bcf18866574be", 73386.9, 29651.3),
+    "moe_prefill_top8_T256": (MOEP_SRC, "34beda4816c26f2e", 188056.9, 23585.5),
     "quantize_17408x5120_f32_g64": (QUANT_SRC, "780e77792db6bb81", 174101.4, 48960.0),
 }
 
