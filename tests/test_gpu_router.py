@@ -77,6 +77,21 @@ def test_router_ties_go_to_smaller_index():
     np.testing.assert_allclose(wts1[0], [0.7310585786300049, 0.2689414213699951], rtol=W_RTOL)
 
 
+@pytest.mark.parametrize("n_experts", [64, 128, 256])
+def test_router_negative_logits_and_signed_zeros(n_experts):
+    """Integer logits from -3 to 3 with zeros of both signs: -0 and +0 tie (the lower index goes
+    first) and negative logits rank below positive ones in their float order."""
+    rng = np.random.default_rng(n_experts + 8)
+    logits = rng.integers(-3, 4, size=(24, n_experts)).astype(np.float32)
+    zeros = logits == 0
+    logits[zeros & (rng.random(logits.shape) < 0.5)] = -0.0
+    logits[:4] = -np.abs(logits[:4])  # rows with no positive logit
+    ids, wts = _route(logits, 8)
+    ref_ids, ref_wts = _expect(logits.astype(np.float64), 8)
+    assert np.array_equal(ids, ref_ids)
+    np.testing.assert_allclose(wts, ref_wts, rtol=W_RTOL, atol=0)
+
+
 def test_router_nan_and_inf_logits():
     """NaN ranks below every number; -inf logits get weight 0."""
     rng = np.random.default_rng(7)
