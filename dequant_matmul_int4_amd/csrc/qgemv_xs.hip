@@ -50,6 +50,7 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 constexpr int kXsRowsInFlight = 4;  // per wave (8 measured slower on the down projection)
 
 typedef __bf16 xs_bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 xs_f16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t xs_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
@@ -92,35 +93,13 @@ __device__ __forceinline__ float xs_sum16(float t) {
 }
 
 // The activation of one chunk in the form the dot product takes: float32
-// values in element order (XB = false) or the 16 bf16 pairs
-// (x[8 jj + i], x[8 jj + i + 4]) of the nibble pairs (XB = true).
+// values in element order, times 2^24 at even and 2^20 at odd positions
+// (XB = false), or the 16 bf16 pairs (x[8 jj + i], x[8 jj + i + 4]) of the
+// nibble pairs (XB = true).
 template <bool XB>
 struct XsChunk {
   uint32_t v[XB ? 16 : 32];
 };
-
-// sum over the chunk of q_k x_k (float32 activations)
-__device__ __forceinline__ float xs_dot_f32(const uint4 q, const XsChunk<false> &x) {
-  const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
-  float a[4];  // one chain per word
-#pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    // bytes of lo: nibbles 0, 2, 4, 6; of hi: nibbles 1, 3, 5, 7
-    uint32_t lo = wd[jj] & 0x0F0F0F0Fu, hi = (wd[jj] >> 4) & 0x0F0F0F0Fu;
-    asm("" : "+v"(lo), "+v"(hi));  // keep the byte split (v_cvt_f32_ubyte{0..3})
-    const uint32_t *xe = x.v + 8 * jj;
-    float t = (float)(lo & 0xFFu) * __uint_as_float(xe[0]);
-    t = fmaf((float)(hi & 0xFFu), __uint_as_float(xe[1]), t);
-    t = fmaf((float)((lo >> 8) & 0xFFu), __uint_as_float(xe[2]), t);
-    t = fmaf((float)((hi >> 8) & 0xFFu), __uint_as_float(xe[3]), t);
-    t = fmaf((float)((lo >> 16) & 0xFFu), __uint_as_float(xe[4]), t);
-    t = fmaf((float)((hi >> 16) & 0xFFu), __uint_as_float(xe[5]), t);
-    t = fmaf((float)(lo >> 24), __uint_as_float(xe[6]), t);
-    t = fmaf((float)(hi >> 24), __uint_as_float(xe[7]), t);
-    a[jj] = t;
-  }
-  return (a[0] + a[1]) + (a[2] + a[3]);
-}
 
 // Two code words shifted right by 4 s bits as one 64-bit value: one
 // v_lshrrev_b64 instead of two 32-bit shifts (the compiler splits a 64-bit
@@ -131,6 +110,42 @@ __device__ __forceinline__ uint64_t xs_shr64(uint64_t w) {
   uint64_t r;
   asm("v_lshrrev_b64 %0, %1, %2" : "=v"(r) : "n"(4 * S), "v"(w));
   return r;
+}
+
+// sum over the chunk of q_k x_k (float32 activations).  A word masked with
+// 0x000F000F holds nibbles (n, n + 4) as the f16 subnormals q 2^-24, masked
+// with 0x00F000F0 nibbles (n + 1, n + 5) as 16 q 2^-24; v_fma_mix_f32 takes
+// them exactly, against activations stored times 2^24 and 2^20 respectively
+// (XsChunk<false>), so each step is fmaf(q, x, t) with one rounding.  Masks
+// on the word and on the word shifted by 8 give all eight nibbles.
+__device__ __forceinline__ float xs_dot_f32(const uint4 q, const XsChunk<false> &x) {
+  const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
+  float a[2];  // one chain per word pair
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint64_t w2 = ((uint64_t)wd[2 * h + 1] << 32) | wd[2 * h];
+    const uint64_t w8 = xs_shr64<2>(w2);
+    float t = 0.f;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const uint32_t u0 = (uint32_t)(w2 >> (32 * e)), u8 = (uint32_t)(w8 >> (32 * e));
+      const xs_f16x2_t p0 = __builtin_bit_cast(xs_f16x2_t, u0 & 0x000F000Fu);  // nibbles 0, 4
+      const xs_f16x2_t p1 = __builtin_bit_cast(xs_f16x2_t, u0 & 0x00F000F0u);  // 1, 5 (times 16)
+      const xs_f16x2_t p2 = __builtin_bit_cast(xs_f16x2_t, u8 & 0x000F000Fu);  // 2, 6
+      const xs_f16x2_t p3 = __builtin_bit_cast(xs_f16x2_t, u8 & 0x00F000F0u);  // 3, 7 (times 16)
+      const uint32_t *xe = x.v + 8 * (2 * h + e);
+      t = fmaf((float)p0.x, __uint_as_float(xe[0]), t);
+      t = fmaf((float)p1.x, __uint_as_float(xe[1]), t);
+      t = fmaf((float)p2.x, __uint_as_float(xe[2]), t);
+      t = fmaf((float)p3.x, __uint_as_float(xe[3]), t);
+      t = fmaf((float)p0.y, __uint_as_float(xe[4]), t);
+      t = fmaf((float)p1.y, __uint_as_float(xe[5]), t);
+      t = fmaf((float)p2.y, __uint_as_float(xe[6]), t);
+      t = fmaf((float)p3.y, __uint_as_float(xe[7]), t);
+    }
+    a[h] = t;
+  }
+  return a[0] + a[1];
 }
 
 // sum over the chunk of (128 + q_k) x_k (bf16 activations)
@@ -256,6 +271,9 @@ __global__ void __launch_bounds__(kXsMaxWaves * 64) qgemv_xs_kernel(const GemvXs
     }
 #pragma unroll
     for (int i = 0; i < 32; ++i) xs += __uint_as_float(xc.v[i]);
+    // even nibble positions pair with codes q 2^-24, odd ones with 16 q 2^-24
+#pragma unroll
+    for (int i = 0; i < 32; ++i) xc.v[i] = __float_as_uint(__uint_as_float(xc.v[i]) * ((i & 1) ? 0x1p20f : 0x1p24f));
   }
   // The chunk has arrived (xs waited for it).  Redefining its registers keeps
   // the compiler from treating the loop below as a consumer of loads issued
