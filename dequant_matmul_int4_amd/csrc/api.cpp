@@ -314,15 +314,16 @@ qint4_status plan_multi(int n_outs, const int64_t *n_out, int64_t k_in, int grou
     mp->grid = std::min<int64_t>(tiles, per_cu * n_cu);  // launches of 8 or more tokens
     return QINT4_OK;
   }
-  // One matrix with float32 activations, or the gate/up pair, over long rows:
-  // each wave holds its slice of x in registers (dense FFN 5120 -> 17408 ->
-  // 5120: gate/up 22.6 -> about 20 us, down 16.3 -> 13.0 us).
-  // (Not for small-M calls, whose rows must not depend on T.)
-  if (!batched && !rms && T == 1 && ((n_outs == 1 && !swiglu && x_dtype == QINT4_F32) || swiglu) &&
+  // One matrix, or the gate/up pair, over long rows: each wave holds its
+  // slice of x in registers (dense FFN 5120 -> 17408 -> 5120: gate/up 22.6 ->
+  // about 20 us, float32 down 16.3 -> 12.5 us; bf16 activations, one matrix:
+  // 5120 x 17408 14.5 -> 11.1 us, 17408 x 5120 14.1 -> 11.3 us, 2048 x 32768
+  // 12.3 -> 8.0 us).  (Not for small-M calls, whose rows must not depend on T.)
+  if (!batched && !rms && T == 1 && ((n_outs == 1 && !swiglu) || swiglu) &&
       gemv_xs_supported(n_out[0], k_in, streams, n_cu)) {
     mp->xs = true;
     mp->blk = 1;
-    mp->grid = gemv_xs_grid(n_out[0], streams, n_cu);
+    mp->grid = gemv_xs_grid(n_out[0], k_in, streams, n_cu);
     return QINT4_OK;
   }
   const int nc = (int)(k_in / 32);

@@ -172,8 +172,8 @@ size_t gemv_mfma_lds_bytes(int tt, int group_size, int64_t k_in, int streams);
 hipError_t launch_gemv_mfma(const GemvParams &p, int tt, int group_size, int sb_bf16, int swiglu,
                             int64_t grid, hipStream_t stream);
 
-// Activation-stationary T=1 GEMVs (qgemv_xs.hip): one matrix with float32
-// activations and stored outputs, or the gate/up pair with the SwiGLU
+// Activation-stationary T=1 GEMVs (qgemv_xs.hip): one matrix with stored
+// outputs, or the gate/up pair with the SwiGLU
 // epilogue, over rows of kXsMinK .. kXsMaxWaves * 2048 columns.  Lane j of a
 // row group of wave w holds chunk L w + j of x in registers (L = 1 <<
 // log2_lpr lanes per row, gemv_xs_waves(k_in) waves per workgroup cover
@@ -200,7 +200,7 @@ struct GemvXsParams {
 int gemv_xs_log2_lanes(int64_t k_in);
 int gemv_xs_waves(int64_t k_in);
 bool gemv_xs_supported(int64_t n_out, int64_t k_in, int streams, int n_cu);
-int64_t gemv_xs_grid(int64_t n_out, int streams, int n_cu);
+int64_t gemv_xs_grid(int64_t n_out, int64_t k_in, int streams, int n_cu);
 int gemv_xs_depth();  // rows in flight per wave
 hipError_t launch_gemv_xs(const GemvXsParams &p, int64_t grid, int sb_bf16, int x_bf16, int streams,
                           hipStream_t stream);

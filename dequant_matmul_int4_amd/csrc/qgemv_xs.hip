@@ -1,6 +1,6 @@
 // qgemv_xs.hip -- T=1 int4 group-affine GEMVs with the activation held in
-// registers ("activation-stationary") on gfx950: one matrix with float32
-// activations over long rows (the dense FFN down projection), and the gate/up
+// registers ("activation-stationary") on gfx950: one matrix over long rows
+// (the dense FFN down projection, with float32 activations), and the gate/up
 // pair with the SwiGLU epilogue (the dense FFN gate/up projection).
 //
 // Sources (by page title and passage):
@@ -13,11 +13,13 @@
 //
 // Per row and group the product is the affine form of the GEMV family,
 //     sum_k (s q_k + b) x_k = s * sum_k q_k x_k + b * sum_k x_k,
-// accumulated in float32: for float32 activations q comes from
-// v_cvt_f32_ubyte of the masked code bytes; for bf16 activations a nibble
-// pair (q_i, q_{i+4}) of a word becomes the exact bf16 pair (128 + q_i,
-// 128 + q_{i+4}) (bits 0x4300 | q) for v_dot2_f32_bf16, and 128 * sum x is
-// removed per chunk, as in the streaming GEMV.
+// accumulated in float32: for float32 activations a masked nibble pair is
+// the f16 pair (q 2^-24, q' 2^-24) or (16 q 2^-24, 16 q' 2^-24), exact
+// subnormals, which v_fma_mix_f32 multiplies by activations stored times 2^24
+// or 2^20 (activations of magnitude 2^104 or more overflow there); for bf16
+// activations a nibble pair (q_i, q_{i+4}) of a word becomes the exact bf16
+// pair (128 + q_i, 128 + q_{i+4}) (bits 0x4300 | q) for v_dot2_f32_bf16, and
+// 128 * sum x is removed per chunk, as in the streaming GEMV.
 //
 // Work decomposition (gfx950 specific, not from the pages):
 //   * L lanes (32 or 64) cover one row, so a wave takes 64 / L rows per
@@ -377,14 +379,18 @@ int gemv_xs_waves(int64_t k_in) {
 bool gemv_xs_supported(int64_t n_out, int64_t k_in, int streams, int n_cu) {
   if (k_in < kXsMinK || k_in > (int64_t)kXsMaxWaves * 2048 || k_in % 32 != 0) return false;
   if (n_out * k_in * streams < kXsMinCodes) return false;
-  const int64_t grid = gemv_xs_grid(n_out, streams, n_cu);
+  const int64_t grid = gemv_xs_grid(n_out, k_in, streams, n_cu);
   return grid >= 1 && (n_out + grid - 1) / grid <= kXsMaxRows;
 }
 
-// One workgroup per CU for stored outputs; four per CU for the gate/up pair
-// (17408 x 5120 pair: 23.2 us at one per CU, 21.2 us at four, measured).
-int64_t gemv_xs_grid(int64_t n_out, int streams, int n_cu) {
-  return std::min<int64_t>((int64_t)n_cu * (streams == 2 ? 4 : 1), n_out);
+// Workgroups per CU: four for the gate/up pair (17408 x 5120 pair: 23.2 us at
+// one per CU, 21.2 us at four); for one matrix two while a workgroup has at
+// most five waves (k_in up to 5120), else one (measured, bf16 activations:
+// 17408 x 5120 14.4 -> 11.3 us and 14336 x 4096 8.8 -> 7.1 us at two; 6144 x
+// 6144 5.9 -> 6.2 us and 5120 x 17408 11.1 -> 11.5 us at two).
+int64_t gemv_xs_grid(int64_t n_out, int64_t k_in, int streams, int n_cu) {
+  const int per_cu = streams == 2 ? 4 : (gemv_xs_waves(k_in) <= 5 ? 2 : 1);
+  return std::min<int64_t>((int64_t)n_cu * per_cu, n_out);
 }
 
 int gemv_xs_depth() { return kXsRowsInFlight; }

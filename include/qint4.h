@@ -505,8 +505,8 @@ qint4_status quantize_int4(const void *w, int32_t w_dtype, int64_t n_rows, int64
  * that.  The small-M MFMA kernels (QINT4_FORM_MFMA) run one 16-row tile per
  * workgroup, its K range split over `waves` waves.  The activation-stationary
  * kernel (QINT4_FORM_XS: qgemv_int4 / qgemv_int4_multi at T = 1 on one
- * matrix with float32 activations, or on the gate/up pair; k_in from 4096 to
- * 32768 and at least 2^25 codes in all) gives lane j of a row group of wave
+ * matrix or on the gate/up pair; k_in from 4096 to 32768 and at least 2^25
+ * codes in all) gives lane j of a row group of wave
  * w the 32-code chunk lanes * w + j of its rows, whose activations it holds
  * in registers; a workgroup's `waves` waves cover k_in, and workgroup b of
  * `grid` takes rows b, b + grid, ... (rows_per_task: rows per wave step;

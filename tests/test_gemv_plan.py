@@ -86,30 +86,38 @@ def test_smallm_mfma_form():
     assert (f["kernel"], f["tokens"], f["launches"]) == ("ring", 4, 4)
 
 
-def test_xs_form_for_long_float32_rows():
-    """One matrix with float32 activations, 4096 <= k_in <= 32768 and at least 2^25 codes (the
-    dense down projection 17408 -> 5120): the activation-stationary kernel, one workgroup per CU,
-    32 lanes a row (two rows a step) while that takes at most 16 waves, else 64."""
-    f = q.plan_qgemv([5120], 17408, x_dtype="f32", n_cu=N_CU)
-    assert (f["kernel"], f["grid"], f["waves"], f["lanes"], f["tasks"], f["busiest_wave_steps"],
-            f["ring_depth"]) == ("xs", N_CU, 9, 64, 5120, 20, 4)
+def test_xs_form_for_long_rows():
+    """One matrix, 4096 <= k_in <= 32768 and at least 2^25 codes (the dense down projection
+    17408 -> 5120): the activation-stationary kernel, 32 lanes a row (two rows a step) while that
+    takes at most 16 waves, else 64; two workgroups per CU while a workgroup has at most five
+    waves, else one."""
+    for x_dt in ("f32", "bf16"):
+        f = q.plan_qgemv([5120], 17408, x_dtype=x_dt, n_cu=N_CU)
+        assert (f["kernel"], f["grid"], f["waves"], f["lanes"], f["tasks"], f["busiest_wave_steps"],
+                f["ring_depth"]) == ("xs", N_CU, 9, 64, 5120, 20, 4)
+        f = q.plan_qgemv([17408], 5120, x_dtype=x_dt, n_cu=N_CU)
+        assert (f["kernel"], f["grid"], f["waves"], f["lanes"], f["busiest_wave_steps"]) == \
+            ("xs", 2 * N_CU, 5, 32, 34)
     f = q.plan_qgemv([5000], 8192, x_dtype="f32", n_cu=N_CU)
     assert (f["kernel"], f["waves"], f["lanes"], f["rows_per_task"], f["busiest_wave_steps"]) == \
         ("xs", 8, 32, 2, 20)
     f = q.plan_qgemv([4100], 8320, group_size=32, x_dtype="f32", n_cu=N_CU)
     assert (f["kernel"], f["waves"], f["lanes"]) == ("xs", 9, 32)
-    f = q.plan_qgemv([256 * N_CU], 4096, x_dtype="f32", n_cu=N_CU)
-    assert (f["kernel"], f["busiest_wave_steps"]) == ("xs", 256)
+    f = q.plan_qgemv([256 * N_CU], 6144, x_dtype="f32", n_cu=N_CU)
+    assert (f["kernel"], f["grid"], f["busiest_wave_steps"]) == ("xs", N_CU, 256)
+    f = q.plan_qgemv([512 * N_CU], 4096, x_dtype="bf16", n_cu=N_CU)
+    assert (f["kernel"], f["grid"], f["busiest_wave_steps"]) == ("xs", 2 * N_CU, 256)
     f = q.plan_qgemv([2049], 32768, x_dtype="f32", n_cu=N_CU)
     assert (f["kernel"], f["waves"], f["lanes"]) == ("xs", 16, 64)
 
 
 @pytest.mark.parametrize("n_outs,k_in,x_dt,epi,call", [
-    ([5120], 17408, "bf16", q.EPI_NONE, q.CALL_QGEMV),           # bf16 activations
     ([9000], 3584, "f32", q.EPI_NONE, q.CALL_QGEMV),             # rows shorter than 4096
     ([2000], 32832, "f32", q.EPI_NONE, q.CALL_QGEMV),            # more than 16 waves of 64 lanes
     ([4096], 4096, "f32", q.EPI_NONE, q.CALL_QGEMV),             # fewer than 2^25 codes
-    ([256 * N_CU + 1], 4096, "f32", q.EPI_NONE, q.CALL_QGEMV),   # more than 256 rows per CU
+    ([5120], 5120, "bf16", q.EPI_NONE, q.CALL_QGEMV),            # the same
+    ([256 * N_CU + 1], 6144, "f32", q.EPI_NONE, q.CALL_QGEMV),   # over 256 rows a workgroup
+    ([512 * N_CU + 1], 4096, "bf16", q.EPI_NONE, q.CALL_QGEMV),  # the same, two per CU
     ([5120, 5120], 17408, "f32", q.EPI_NONE, q.CALL_QGEMV),      # two matrices
     ([5120], 17408, "f32", q.EPI_NONE, q.CALL_RMS_NORM),         # RMSNorm prologue
     ([5120, 5120], 3584, "bf16", q.EPI_SWIGLU_PAIR, q.CALL_QGEMV),  # pair, short rows

@@ -1,9 +1,9 @@
-"""GPU parity of the activation-stationary GEMV form (qgemv_int4 on one matrix with float32
+"""GPU parity of the activation-stationary GEMV form (qgemv_int4 on one matrix, float32 or bf16
 activations, qgemv_int4_multi on the gate/up pair; k_in from 4096 to 32768, at least 2^25 codes)
 against the fp64 oracle, through the C ABI.  Each case first asserts, through the library's plan
 query, that the call takes that form, so the edges below stay on it: rows not a multiple of the
 grid, fewer rows than workgroups (one row each), a last wave with few lanes holding a chunk, 32
-and 64 lanes a row, sixteen waves, and 256 rows per workgroup."""
+and 64 lanes a row, sixteen waves, one and two workgroups per CU, and 256 rows per workgroup."""
 import numpy as np
 import pytest
 import torch
@@ -26,44 +26,65 @@ def _n_cu():
     return torch.cuda.get_device_properties(0).multi_processor_count
 
 
-def _run_single(w, x, y_dt):
+def _run_single(w, x, x_dt, y_dt):
     q = lib()
-    f = q.plan_qgemv([w.n_out], w.k_in, group_size=w.group_size, x_dtype="f32")
+    f = q.plan_qgemv([w.n_out], w.k_in, group_size=w.group_size, x_dtype=x_dt)
     assert f["kernel"] == "xs", f
     y = nan_like(w.n_out, TD[y_dt])
-    q.qgemv_int4(dev_matrix(w), synth.to_torch(x, "f32"), y)
+    q.qgemv_int4(dev_matrix(w), synth.to_torch(x, x_dt), y)
     torch.cuda.synchronize()
     return y, f
 
 
 # (n_out, k_in, group size): 5000 rows, 19 or 20 per workgroup, 32 lanes a row; 8320 = 260
 # chunks, the ninth wave holding 4 per row group; 16384 / g128, 16 waves of 32 lanes; 17408 (the
-# dense down projection), 64 lanes a row; 32768, 16 waves of 64 lanes
-SINGLE = [(5000, 8192, 64), (4100, 8320, 32), (2100, 16384, 128), (2000, 17408, 64), (2049, 32768, 64)]
+# dense down projection), 64 lanes a row; 32768, 16 waves of 64 lanes; 5120 columns, five waves,
+# two workgroups per CU
+SINGLE = [(5000, 8192, 64), (4100, 8320, 32), (2100, 16384, 128), (2000, 17408, 64), (2049, 32768, 64),
+          (7001, 5120, 64)]
 
 
 @pytest.mark.parametrize("n_out,k_in,g", SINGLE)
 @pytest.mark.parametrize("sb_dt,y_dt", [("bf16", "bf16"), ("f32", "f32"), ("bf16", "f32")])
-def test_xs_single_shapes_and_dtypes(n_out, k_in, g, sb_dt, y_dt):
+@pytest.mark.parametrize("x_dt", ["f32", "bf16"])
+def test_xs_single_shapes_and_dtypes(n_out, k_in, g, sb_dt, y_dt, x_dt):
     rng = np.random.default_rng(n_out * 17 + k_in + g)
     w = synth.draw_matrix(rng, n_out, k_in, g, sb_dt)
-    x = synth.draw_activation(rng, (k_in,), "f32")
-    y, f = _run_single(w, x, y_dt)
-    y_ref, a_ref = oracle.gemv(w, x, "f32", threads=oracle_threads())
-    check(y, y_ref, a_ref, "xs gemv %dx%d g%d %s/%s (grid %d, %d waves of %d lanes)" %
-          (n_out, k_in, g, sb_dt, y_dt, f["grid"], f["waves"], f["lanes"]))
+    x = synth.draw_activation(rng, (k_in,), x_dt)
+    y, f = _run_single(w, x, x_dt, y_dt)
+    if k_in == 5120:
+        assert f["grid"] == 2 * _n_cu()
+    y_ref, a_ref = oracle.gemv(w, x, x_dt, threads=oracle_threads())
+    check(y, y_ref, a_ref, "xs gemv %dx%d g%d x %s, %s/%s (grid %d, %d waves of %d lanes)" %
+          (n_out, k_in, g, x_dt, sb_dt, y_dt, f["grid"], f["waves"], f["lanes"]))
 
 
 def test_xs_most_rows_per_workgroup():
-    """256 rows per workgroup (the form's limit) on a 4096-wide matrix."""
+    """256 rows per workgroup (the form's limit) on a 6144-wide matrix (one workgroup per CU)."""
     n_out = 256 * _n_cu()
     rng = np.random.default_rng(4242)
-    w = synth.draw_matrix(rng, n_out, 4096, 64, "bf16")
-    x = synth.draw_activation(rng, (4096,), "f32")
-    y, f = _run_single(w, x, "f32")
+    w = synth.draw_matrix(rng, n_out, 6144, 64, "bf16")
+    x = synth.draw_activation(rng, (6144,), "f32")
+    y, f = _run_single(w, x, "f32", "f32")
     assert f["busiest_wave_steps"] == 256
     y_ref, a_ref = oracle.gemv(w, x, "f32", threads=oracle_threads())
-    check(y, y_ref, a_ref, "xs gemv %dx4096 (256 rows per workgroup)" % n_out)
+    check(y, y_ref, a_ref, "xs gemv %dx6144 (256 rows per workgroup)" % n_out)
+
+
+@pytest.mark.parametrize("lo,hi", [(-100, -60), (-20, 100)])
+def test_xs_float32_activation_range(lo, hi):
+    """Float32 activations across the exponent range the scaled form keeps exact (codes as f16
+    subnormals times activations scaled by 2^24 / 2^20): each 32-value chunk in its own binade
+    between 2^lo and 2^hi (products stay normal floats), against the oracle."""
+    n_out, k_in = 2048, 16384
+    rng = np.random.default_rng(99 + hi)
+    w = synth.draw_matrix(rng, n_out, k_in, 64, "f32")
+    x = synth.draw_activation(rng, (k_in,), "f32")
+    binade = np.repeat(rng.integers(lo, hi + 1, size=k_in // 32), 32).astype(np.float64)
+    x = (x.astype(np.float64) * np.exp2(binade)).astype(np.float32)
+    y, f = _run_single(w, x, "f32", "f32")
+    y_ref, a_ref = oracle.gemv(w, x, "f32", threads=oracle_threads())
+    check(y, y_ref, a_ref, "xs gemv %dx%d, activations from 2^%d to 2^%d" % (n_out, k_in, lo, hi))
 
 
 # (n_out, k_in, x dtype): the dense FFN gate/up pair 17408 x 5120; 6144 columns, 2 or 3 rows per
@@ -103,14 +124,15 @@ def test_xs_unpack_identity_probe():
                       biases=np.zeros((n_out, groups), np.float32), sb_dtype="f32", group_size=64,
                       n_out=n_out, k_in=k_in)
     dw = dev_matrix(w)
-    assert q.plan_qgemv([n_out], k_in, x_dtype="f32")["kernel"] == "xs"
-    for k in (0, 1, 7, 31, 32, 1023, 1024, 1025, 4095, 4096, 8191, 8192, 8287, 8288, 8319):
-        x = np.zeros(k_in, np.float32)
-        x[k] = 1.0
-        y = nan_like(n_out, torch.float32)
-        q.qgemv_int4(dw, synth.to_torch(x, "f32"), y)
-        torch.cuda.synchronize()
-        assert np.array_equal(y.cpu().numpy().astype(np.float64), raw[:, k].astype(np.float64)), k
+    for x_dt in ("f32", "bf16"):
+        assert q.plan_qgemv([n_out], k_in, x_dtype=x_dt)["kernel"] == "xs"
+        for k in (0, 1, 2, 3, 4, 5, 6, 7, 31, 32, 1023, 1024, 1025, 4095, 4096, 8191, 8192, 8287, 8288, 8319):
+            x = np.zeros(k_in, np.float32)
+            x[k] = 1.0
+            y = nan_like(n_out, torch.float32)
+            q.qgemv_int4(dw, synth.to_torch(x if x_dt == "f32" else synth.f32_to_bf16_bits(x), x_dt), y)
+            torch.cuda.synchronize()
+            assert np.array_equal(y.cpu().numpy().astype(np.float64), raw[:, k].astype(np.float64)), (x_dt, k)
 
 
 def test_xs_repeatable():
