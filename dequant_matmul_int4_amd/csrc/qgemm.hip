@@ -45,6 +45,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int BK = 64;
@@ -76,16 +77,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// 8 codes of one word -> 8 bf16 weights (k order), as a uint4.
-__device__ __forceinline__ uint4 dequant_word(uint32_t w, float s, float b) {
-  uint32_t lo = w & 0x0F0F0F0Fu;         // codes 0, 2, 4, 6 in bytes 0..3
-  uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // codes 1, 3, 5, 7
-  asm("" : "+v"(lo), "+v"(hi));
+// 8 codes of one word -> 8 bf16 weights (k order), as a uint4.  The word
+// masked with 0x000F000F holds codes (n, n + 4) as the f16 subnormals q 2^-24,
+// masked with 0x00F000F0 codes (n + 1, n + 5) as 16 q 2^-24; v_fma_mix_f32
+// against the scale times 2^24 (s24) or 2^20 (s20) gives fmaf(s, q, b)
+// exactly (scales below 2^104 in magnitude), then RNE to bf16.
+__device__ __forceinline__ uint4 dequant_word(uint32_t w, float s24, float s20, float b) {
+  const uint32_t w8 = w >> 8;
+  const f16x2_t p0 = __builtin_bit_cast(f16x2_t, w & 0x000F000Fu);   // codes 0, 4
+  const f16x2_t p1 = __builtin_bit_cast(f16x2_t, w & 0x00F000F0u);   // 1, 5 (times 16)
+  const f16x2_t p2 = __builtin_bit_cast(f16x2_t, w8 & 0x000F000Fu);  // 2, 6
+  const f16x2_t p3 = __builtin_bit_cast(f16x2_t, w8 & 0x00F000F0u);  // 3, 7 (times 16)
   uint4 r;
-  r.x = pack_bf16x2(fmaf(s, (float)(lo & 0xFFu), b), fmaf(s, (float)(hi & 0xFFu), b));
-  r.y = pack_bf16x2(fmaf(s, (float)((lo >> 8) & 0xFFu), b), fmaf(s, (float)((hi >> 8) & 0xFFu), b));
-  r.z = pack_bf16x2(fmaf(s, (float)((lo >> 16) & 0xFFu), b), fmaf(s, (float)((hi >> 16) & 0xFFu), b));
-  r.w = pack_bf16x2(fmaf(s, (float)(lo >> 24), b), fmaf(s, (float)(hi >> 24), b));
+  r.x = pack_bf16x2(fmaf((float)p0.x, s24, b), fmaf((float)p1.x, s20, b));
+  r.y = pack_bf16x2(fmaf((float)p2.x, s24, b), fmaf((float)p3.x, s20, b));
+  r.z = pack_bf16x2(fmaf((float)p0.y, s24, b), fmaf((float)p1.y, s20, b));
+  r.w = pack_bf16x2(fmaf((float)p2.y, s24, b), fmaf((float)p3.y, s20, b));
   return r;
 }
 
@@ -246,9 +253,10 @@ __global__ void __launch_bounds__(WM * WN * 64) qgemm_kernel(const GemmMultiPara
           bi = *reinterpret_cast<const float *>(ts + bytes);
         }
       }
+      const float s24 = sc * 0x1p24f, s20 = sc * 0x1p20f;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
-        *reinterpret_cast<uint4 *>(dst + jj * 8) = dequant_word(w4[jj], sc, bi);
+        *reinterpret_cast<uint4 *>(dst + jj * 8) = dequant_word(w4[jj], s24, s20, bi);
     }
 #pragma unroll
     for (int i = 0; i < XCH; ++i)

@@ -55,6 +55,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int KS = 128;           // k per step
@@ -99,15 +100,21 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 }
 
 // 8 codes of one word -> the 8 bf16 weights s * q + b (code order).
-__device__ __forceinline__ bf16x8_t dequant8(uint32_t w, float s, float b) {
-  uint32_t lo = w & 0x0F0F0F0Fu;         // codes 0, 2, 4, 6 in bytes 0..3
-  uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // codes 1, 3, 5, 7
-  asm("" : "+v"(lo), "+v"(hi));
+// The word masked with 0x000F000F holds codes (n, n + 4) as the f16
+// subnormals q 2^-24, masked with 0x00F000F0 codes (n + 1, n + 5) as
+// 16 q 2^-24; v_fma_mix_f32 against the scale times 2^24 (s24) or 2^20 (s20)
+// gives fmaf(s, q, b) exactly (scales below 2^104 in magnitude).
+__device__ __forceinline__ bf16x8_t dequant8(uint32_t w, float s24, float s20, float b) {
+  const uint32_t w8 = w >> 8;
+  const f16x2_t p0 = __builtin_bit_cast(f16x2_t, w & 0x000F000Fu);   // codes 0, 4
+  const f16x2_t p1 = __builtin_bit_cast(f16x2_t, w & 0x00F000F0u);   // 1, 5 (times 16)
+  const f16x2_t p2 = __builtin_bit_cast(f16x2_t, w8 & 0x000F000Fu);  // 2, 6
+  const f16x2_t p3 = __builtin_bit_cast(f16x2_t, w8 & 0x00F000F0u);  // 3, 7 (times 16)
   uint4 r;
-  r.x = pack2(fmaf(s, (float)(lo & 0xFFu), b), fmaf(s, (float)(hi & 0xFFu), b));
-  r.y = pack2(fmaf(s, (float)((lo >> 8) & 0xFFu), b), fmaf(s, (float)((hi >> 8) & 0xFFu), b));
-  r.z = pack2(fmaf(s, (float)((lo >> 16) & 0xFFu), b), fmaf(s, (float)((hi >> 16) & 0xFFu), b));
-  r.w = pack2(fmaf(s, (float)(lo >> 24), b), fmaf(s, (float)(hi >> 24), b));
+  r.x = pack2(fmaf((float)p0.x, s24, b), fmaf((float)p1.x, s20, b));
+  r.y = pack2(fmaf((float)p2.x, s24, b), fmaf((float)p3.x, s20, b));
+  r.z = pack2(fmaf((float)p0.y, s24, b), fmaf((float)p1.y, s20, b));
+  r.w = pack2(fmaf((float)p2.y, s24, b), fmaf((float)p3.y, s20, b));
   return __builtin_bit_cast(bf16x8_t, r);
 }
 
@@ -311,8 +318,9 @@ __global__ void __launch_bounds__((kW + 1) * 64) qgemm_stream_kernel(const GemmP
       // dequantise this step's weights: B operands of the four sub-steps
       bf16x8_t bw[4];
       const uint32_t wd[4] = {ring[u].q.x, ring[u].q.y, ring[u].q.z, ring[u].q.w};
+      const float s24 = sc * 0x1p24f, s20 = sc * 0x1p20f;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) bw[s] = dequant8(wd[s], sc, bi);
+      for (int s = 0; s < 4; ++s) bw[s] = dequant8(wd[s], s24, s20, bi);
       load_w(j + D, ring[u]);  // refill the slot just consumed
       const uint16_t *xt = xs + (j % NBUF) * TILE;
 #pragma unroll
