@@ -52,8 +52,11 @@
 //     with the matching activation pair.  The 128 * sum(x) excess is removed
 //     per chunk, and the group affine map is applied per chunk:
 //       sum_k (s q_k + b) x_k = s * (sum_k (128+q_k) x_k - 128 sum x) + b sum x.
-//   * float32 activations: the low and high nibbles of a word are split into
-//     bytes and converted with v_cvt_f32_ubyte{0..3}, then FMA'd in float32.
+//   * float32 activations: a word masked with 0x000F000F holds the nibble
+//     pair (q_i, q_{i+4}) as the exact f16 subnormals q 2^-24, masked with
+//     0x00F000F0 the pair (q_{i+1}, q_{i+5}) as 16 q 2^-24; v_fma_mix_f32
+//     multiplies them by activations staged times 2^24 and 2^20, which is
+//     fmaf(q, x, t) exactly (activations below 2^104 in magnitude).
 //   * MoE down projection: the kept experts' rows are one virtual row of
 //     top_k * inter codes; each lane looks up the expert slot of its chunk,
 //     reads that expert's codes, and folds the slot weight into its
@@ -80,6 +83,7 @@ namespace qint4 {
 namespace {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -257,30 +261,40 @@ __device__ __forceinline__ float dot_pq_bf16(const uint32_t (&pq)[16], const uin
 }
 
 // sum over one 32-code chunk of q_k * x_k in float32.  xv: 8 x float4, word jj
-// uses xv[2jj] = (x0, x2, x4, x6) and xv[2jj+1] = (x1, x3, x5, x7).  One
-// accumulator per word (four independent dependency chains).
+// uses xv[2jj] = (x0, x2, x4, x6) * 2^24 and xv[2jj+1] = (x1, x3, x5, x7) *
+// 2^20 (the staged planes).  The word masked with 0x000F000F holds codes
+// (n, n + 4) as the f16 subnormals q 2^-24, masked with 0x00F000F0 codes
+// (n + 1, n + 5) as 16 q 2^-24, so each v_fma_mix_f32 step is fmaf(q, x, t)
+// with one rounding.  One accumulator per pair of words.
 __device__ __forceinline__ float dot_chunk_f32(const uint4 q, const float4 *xv, float acc) {
   const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-  float c[4] = {acc, 0.f, 0.f, 0.f};
+  float c[2] = {acc, 0.f};
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    uint32_t lo = w[jj] & 0x0F0F0F0Fu;
-    uint32_t hi = (w[jj] >> 4) & 0x0F0F0F0Fu;
-    // keep the byte split: lets the compiler use v_cvt_f32_ubyte{0..3}
-    asm("" : "+v"(lo), "+v"(hi));
-    const float4 a = xv[2 * jj], b = xv[2 * jj + 1];
-    float t = c[jj];
-    t = fmaf((float)(lo & 0xFFu), a.x, t);
-    t = fmaf((float)((lo >> 8) & 0xFFu), a.y, t);
-    t = fmaf((float)((lo >> 16) & 0xFFu), a.z, t);
-    t = fmaf((float)(lo >> 24), a.w, t);
-    t = fmaf((float)(hi & 0xFFu), b.x, t);
-    t = fmaf((float)((hi >> 8) & 0xFFu), b.y, t);
-    t = fmaf((float)((hi >> 16) & 0xFFu), b.z, t);
-    t = fmaf((float)(hi >> 24), b.w, t);
-    c[jj] = t;
+  for (int h = 0; h < 2; ++h) {
+    const uint64_t w2 = ((uint64_t)w[2 * h + 1] << 32) | w[2 * h];
+    const uint64_t w8 = shr64_nibbles<2>(w2);
+    float t = c[h];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int jj = 2 * h + e;
+      const uint32_t u0 = (uint32_t)(w2 >> (32 * e)), u8 = (uint32_t)(w8 >> (32 * e));
+      const f16x2_t p0 = __builtin_bit_cast(f16x2_t, u0 & 0x000F000Fu);  // codes 0, 4
+      const f16x2_t p1 = __builtin_bit_cast(f16x2_t, u0 & 0x00F000F0u);  // 1, 5 (times 16)
+      const f16x2_t p2 = __builtin_bit_cast(f16x2_t, u8 & 0x000F000Fu);  // 2, 6
+      const f16x2_t p3 = __builtin_bit_cast(f16x2_t, u8 & 0x00F000F0u);  // 3, 7 (times 16)
+      const float4 ev = xv[2 * jj], od = xv[2 * jj + 1];
+      t = fmaf((float)p0.x, ev.x, t);
+      t = fmaf((float)p1.x, od.x, t);
+      t = fmaf((float)p2.x, ev.y, t);
+      t = fmaf((float)p3.x, od.y, t);
+      t = fmaf((float)p0.y, ev.z, t);
+      t = fmaf((float)p1.y, od.z, t);
+      t = fmaf((float)p2.y, ev.w, t);
+      t = fmaf((float)p3.y, od.w, t);
+    }
+    c[h] = t;
   }
-  return (c[0] + c[1]) + (c[2] + c[3]);
+  return c[0] + c[1];
 }
 
 // Raw buffer resources: a load whose byte offset is >= the resource's
@@ -395,8 +409,13 @@ __device__ __forceinline__ void stage_store(int o, const uint4 *v, int ncx_pad, 
         e[i] = xe[i] * ge[i];
       }
     }
-    reinterpret_cast<float4 *>(xbuf)[(2 * jj) * ncx_pad + c] = make_float4(e[0], e[2], e[4], e[6]);
-    reinterpret_cast<float4 *>(xbuf)[(2 * jj + 1) * ncx_pad + c] = make_float4(e[1], e[3], e[5], e[7]);
+    // even elements times 2^24, odd ones times 2^20 (the scales dot_chunk_f32
+    // takes with its f16-subnormal codes); the chunk sum is of the values
+    constexpr float kE = 0x1p24f, kO = 0x1p20f;
+    reinterpret_cast<float4 *>(xbuf)[(2 * jj) * ncx_pad + c] =
+        make_float4(e[0] * kE, e[2] * kE, e[4] * kE, e[6] * kE);
+    reinterpret_cast<float4 *>(xbuf)[(2 * jj + 1) * ncx_pad + c] =
+        make_float4(e[1] * kO, e[3] * kO, e[5] * kO, e[7] * kO);
     s = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
   }
   s += dpp_mov<0xB1>(s);
