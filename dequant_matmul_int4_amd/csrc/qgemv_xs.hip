@@ -383,13 +383,16 @@ bool gemv_xs_supported(int64_t n_out, int64_t k_in, int streams, int n_cu) {
   return grid >= 1 && (n_out + grid - 1) / grid <= kXsMaxRows;
 }
 
-// Workgroups per CU: four for the gate/up pair (17408 x 5120 pair: 23.2 us at
-// one per CU, 21.2 us at four); for one matrix two while a workgroup has at
-// most five waves (k_in up to 5120), else one (measured, bf16 activations:
-// 17408 x 5120 14.4 -> 11.3 us and 14336 x 4096 8.8 -> 7.1 us at two; 6144 x
-// 6144 5.9 -> 6.2 us and 5120 x 17408 11.1 -> 11.5 us at two).
+// Workgroups per CU: for the gate/up pair 16 / waves, one to four (measured
+// pair times at one per CU -> this rule: 17408 x 5120 23.2 -> 20.6 us at three,
+// 8192 x 8192 14.6 us at four -> 14.2 at two, 3072 x 16384 13.3 us at four ->
+// 10.4 at one); for one matrix two while a workgroup has at most five waves
+// (k_in up to 5120), else one (bf16 activations: 17408 x 5120 14.4 -> 11.3 us
+// and 14336 x 4096 8.8 -> 7.1 us at two; 6144 x 6144 5.9 -> 6.2 us and
+// 5120 x 17408 11.1 -> 11.5 us at two).
 int64_t gemv_xs_grid(int64_t n_out, int64_t k_in, int streams, int n_cu) {
-  const int per_cu = streams == 2 ? 4 : (gemv_xs_waves(k_in) <= 5 ? 2 : 1);
+  const int w = gemv_xs_waves(k_in);
+  const int per_cu = streams == 2 ? std::max(1, std::min(4, 16 / w)) : (w <= 5 ? 2 : 1);
   return std::min<int64_t>((int64_t)n_cu * per_cu, n_out);
 }
 

@@ -130,15 +130,23 @@ def test_xs_form_only_where_it_applies(n_outs, k_in, x_dt, epi, call):
 
 def test_xs_form_for_the_gate_up_pair():
     """The T=1 gate/up pair with 4096 <= k_in <= 32768 (dense FFN 5120 -> 17408): 32 lanes a
-    row (two rows a step) up to 16384 columns, 64 beyond; four workgroups per CU."""
+    row (two rows a step) up to 16384 columns, 64 beyond; 16 / waves workgroups per CU, one to
+    four."""
     f = q.plan_qgemv([17408, 17408], 5120, epilogue=q.EPI_SWIGLU_PAIR, n_cu=N_CU)
     assert (f["kernel"], f["grid"], f["waves"], f["lanes"], f["rows_per_task"], f["tasks"],
-            f["busiest_wave_steps"]) == ("xs", 4 * N_CU, 5, 32, 2, 17408, 17)
+            f["busiest_wave_steps"]) == ("xs", 3 * N_CU, 5, 32, 2, 17408, -(-17408 // (3 * N_CU)))
+    f = q.plan_qgemv([14336, 14336], 4096, epilogue=q.EPI_SWIGLU_PAIR, n_cu=N_CU)
+    assert (f["kernel"], f["grid"], f["waves"]) == ("xs", 4 * N_CU, 4)
+    f = q.plan_qgemv([8192, 8192], 8192, epilogue=q.EPI_SWIGLU_PAIR, n_cu=N_CU)
+    assert (f["kernel"], f["grid"], f["waves"]) == ("xs", 2 * N_CU, 8)
     f = q.plan_qgemv([2048, 2048], 17408, x_dtype="f32", epilogue=q.EPI_SWIGLU_PAIR, n_cu=N_CU)
-    assert (f["kernel"], f["waves"], f["lanes"]) == ("xs", 9, 64)
+    assert (f["kernel"], f["grid"], f["waves"], f["lanes"]) == ("xs", N_CU, 9, 64)
     f = q.plan_qgemv([1000, 1000], 32768, epilogue=q.EPI_SWIGLU_PAIR, n_cu=N_CU)
     assert (f["kernel"], f["grid"], f["waves"], f["lanes"], f["busiest_wave_steps"]) == \
-        ("xs", 1000, 16, 64, 1)
+        ("xs", N_CU, 16, 64, 4)
+    # fewer rows than workgroups (a part with more CUs): one row each
+    f = q.plan_qgemv([1000, 1000], 32768, epilogue=q.EPI_SWIGLU_PAIR, n_cu=2048)
+    assert (f["kernel"], f["grid"], f["busiest_wave_steps"]) == ("xs", 1000, 1)
 
 
 def test_plan_query_rejects_what_the_calls_reject():

@@ -87,10 +87,11 @@ def test_xs_float32_activation_range(lo, hi):
     check(y, y_ref, a_ref, "xs gemv %dx%d, activations from 2^%d to 2^%d" % (n_out, k_in, lo, hi))
 
 
-# (n_out, k_in, x dtype): the dense FFN gate/up pair 17408 x 5120; 6144 columns, 2 or 3 rows per
-# workgroup; 1000 rows < 4 workgroups per CU, 32768 columns (16 waves of 64 lanes); float32
-# activations over 17408 columns
-PAIRS = [(17408, 5120, "bf16"), (3000, 6144, "bf16"), (1000, 32768, "bf16"), (2048, 17408, "f32")]
+# (n_out, k_in, x dtype): the dense FFN gate/up pair 17408 x 5120 (three workgroups per CU);
+# 6144 and 8192 columns (two per CU), 5 or 6 and 4 or 5 rows per workgroup; 1000 rows over 32768
+# columns (16 waves of 64 lanes, one workgroup per CU); float32 activations over 17408 columns
+PAIRS = [(17408, 5120, "bf16"), (3000, 6144, "bf16"), (2100, 8192, "bf16"), (1000, 32768, "bf16"),
+         (2048, 17408, "f32")]
 
 
 @pytest.mark.parametrize("n_out,k_in,x_dt", PAIRS)
