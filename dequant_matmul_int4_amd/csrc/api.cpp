@@ -276,7 +276,8 @@ struct MultiPlan {
   int64_t tiles = 0;  // MFMA: tiles per launch
   int64_t grid = 0;   // MFMA: workgroups per launch (each takes tiles i, i + grid, ...);
                       // XS: workgroups (each takes rows b, b + grid, ...)
-  bool xs = false;    // activation-stationary float32 GEMV (one matrix, T = 1)
+  bool xs = false;    // activation-stationary GEMV (T = 1)
+  int32_t wg0[kXsMaxMats + 1] = {};  // XS: each matrix's workgroups
   GemvPlan plan{};    // otherwise: the persistent GEMV plan
 };
 
@@ -314,16 +315,17 @@ qint4_status plan_multi(int n_outs, const int64_t *n_out, int64_t k_in, int grou
     mp->grid = std::min<int64_t>(tiles, per_cu * n_cu);  // launches of 8 or more tokens
     return QINT4_OK;
   }
-  // One matrix, or the gate/up pair, over long rows: each wave holds its
-  // slice of x in registers (dense FFN 5120 -> 17408 -> 5120: gate/up 22.6 ->
-  // about 20 us, float32 down 16.3 -> 12.5 us; bf16 activations, one matrix:
-  // 5120 x 17408 14.5 -> 11.1 us, 17408 x 5120 14.1 -> 11.3 us, 2048 x 32768
-  // 12.3 -> 8.0 us).  (Not for small-M calls, whose rows must not depend on T.)
-  if (!batched && !rms && T == 1 && ((n_outs == 1 && !swiglu) || swiglu) &&
-      gemv_xs_supported(n_out[0], k_in, streams, n_cu)) {
+  // Matrices with stored outputs, or the gate/up pair, over long rows: each
+  // wave holds its slice of x in registers (dense FFN 5120 -> 17408 -> 5120:
+  // gate/up 22.6 -> 20.6 us, float32 down 16.3 -> 12.5 us; bf16 activations,
+  // one matrix: 5120 x 17408 14.5 -> 11.1 us, 17408 x 5120 14.1 -> 11.3 us,
+  // 2048 x 32768 12.3 -> 8.0 us; where it applies: gemv_xs_plan).  (Not for
+  // small-M calls, whose rows must not depend on T.)
+  if (!batched && !rms && T == 1 && n_outs <= kXsMaxMats &&
+      gemv_xs_plan(n_outs, n_out, k_in, streams, n_cu, mp->wg0)) {
     mp->xs = true;
     mp->blk = 1;
-    mp->grid = gemv_xs_grid(n_out[0], k_in, streams, n_cu);
+    mp->grid = mp->wg0[n_outs];
     return QINT4_OK;
   }
   const int nc = (int)(k_in / 32);
@@ -568,14 +570,18 @@ qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t
   if (mp.xs) {
     GemvXsParams p;
     std::memset(&p, 0, sizeof(p));
-    for (int i = 0; i < n; ++i) {  // n = 1, or 2 for the pair
+    for (int i = 0; i < n; ++i) {  // the matrices, or the pair's gate and up
       p.codes[i] = ws[i].codes;
       p.scales[i] = ws[i].scales;
       p.biases[i] = ws[i].biases;
     }
+    for (int i = 0; i < n_outs; ++i) {
+      p.y[i] = ys[i];
+      p.n_out[i] = (int32_t)ws[i].n_out;
+    }
+    for (int i = 0; i <= n_outs; ++i) p.wg0[i] = mp.wg0[i];
+    p.n_mats = n_outs;
     p.x = x;
-    p.y = ys[0];
-    p.n_out = (int32_t)ws[0].n_out;
     p.ncx = (int32_t)(k_in / 32);
     p.kwb = (int32_t)(k_in / 2);
     p.sbrow = (int32_t)sbrow_b;
@@ -583,7 +589,7 @@ qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t
     p.log2_lpr = gemv_xs_log2_lanes(k_in);
     p.waves = gemv_xs_waves(k_in);
     p.y_bf16 = y_dtype == QINT4_BF16;
-    hipError_t e = launch_gemv_xs(p, mp.grid, sb_bf16, x_dtype == QINT4_BF16, swiglu ? 2 : 1, stream);
+    hipError_t e = launch_gemv_xs(p, sb_bf16, x_dtype == QINT4_BF16, swiglu ? 2 : 1, stream);
     if (e != hipSuccess) return fail(QINT4_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return ok();
   }
@@ -1418,12 +1424,16 @@ qint4_status qint4_plan_qgemv(int32_t call, int32_t n, const int64_t *n_outs, in
     form->tokens = 1;
     form->launches = 1;
     form->grid = mp.grid;
-    form->tasks = n_outs[0];
     form->waves = gemv_xs_waves(k_in);
     form->lanes = 1 << gemv_xs_log2_lanes(k_in);
     form->rows_per_task = 64 / form->lanes;
     form->steps_per_task = 1;
-    form->busiest_wave_steps = (n_outs[0] + mp.grid - 1) / mp.grid;
+    const int nm = swiglu ? 1 : n;
+    for (int i = 0; i < nm; ++i) {
+      const int64_t gi = mp.wg0[i + 1] - mp.wg0[i];
+      form->tasks += n_outs[i];
+      form->busiest_wave_steps = std::max<int64_t>(form->busiest_wave_steps, (n_outs[i] + gi - 1) / gi);
+    }
     form->ring_depth = gemv_xs_depth();
   } else {
     ring_form(mp.plan, multi_xmode(x_dtype, rms), swiglu ? EPI_SWIGLU : EPI_STORE, launches, form);

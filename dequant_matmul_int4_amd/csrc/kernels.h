@@ -172,23 +172,26 @@ size_t gemv_mfma_lds_bytes(int tt, int group_size, int64_t k_in, int streams);
 hipError_t launch_gemv_mfma(const GemvParams &p, int tt, int group_size, int sb_bf16, int swiglu,
                             int64_t grid, hipStream_t stream);
 
-// Activation-stationary T=1 GEMVs (qgemv_xs.hip): one matrix with stored
-// outputs, or the gate/up pair with the SwiGLU
-// epilogue, over rows of kXsMinK .. kXsMaxWaves * 2048 columns.  Lane j of a
-// row group of wave w holds chunk L w + j of x in registers (L = 1 <<
-// log2_lpr lanes per row, gemv_xs_waves(k_in) waves per workgroup cover
-// k_in), and workgroup b of `grid` takes rows b, b + grid, ...
+// Activation-stationary T=1 GEMVs (qgemv_xs.hip): up to kXsMaxMats matrices
+// sharing x with stored outputs, or the gate/up pair with the SwiGLU
+// epilogue.  Lane j of a row group of wave w holds chunk L w + j of x in
+// registers (L = 1 << log2_lpr lanes per row, gemv_xs_waves(k_in) waves per
+// workgroup cover k_in).  Matrix m owns workgroups wg0[m] .. wg0[m+1]-1, and
+// its workgroup b of G = wg0[m+1] - wg0[m] takes rows b, b + G, ...
 constexpr int kXsMaxWaves = 16;    // k_in up to 32768
 constexpr int kXsMaxRows = 256;    // rows per workgroup
-constexpr int64_t kXsMinK = 4096;  // shorter rows keep the streaming GEMV
-constexpr int64_t kXsMinCodes = (int64_t)1 << 25;  // smaller calls too
+constexpr int kXsMaxMats = 8;      // matrices of one call
 struct GemvXsParams {
-  const uint32_t *codes[2];  // [0]: the matrix, or the gate; [1]: the up matrix
-  const void *scales[2];
-  const void *biases[2];
+  // stored outputs: matrix m in codes/scales/biases[m], its outputs in y[m];
+  // the pair: gate in [0], up in [1], h in y[0] (n_mats = 1)
+  const uint32_t *codes[kXsMaxMats];
+  const void *scales[kXsMaxMats];
+  const void *biases[kXsMaxMats];
+  void *y[kXsMaxMats];
+  int32_t n_out[kXsMaxMats];
+  int32_t wg0[kXsMaxMats + 1];
+  int32_t n_mats;
   const void *x;       // float32 or bf16 bits
-  void *y;             // outputs, or h = silu(gate) * up
-  int32_t n_out;
   int32_t ncx;         // k_in / 32
   int32_t kwb;         // code bytes of one row
   int32_t sbrow;       // scale (= bias) bytes of one row
@@ -199,11 +202,11 @@ struct GemvXsParams {
 };
 int gemv_xs_log2_lanes(int64_t k_in);
 int gemv_xs_waves(int64_t k_in);
-bool gemv_xs_supported(int64_t n_out, int64_t k_in, int streams, int n_cu);
-int64_t gemv_xs_grid(int64_t n_out, int64_t k_in, int streams, int n_cu);
+// Splits the rows of n_mats matrices (the pair: n_mats = 1, streams = 2) over
+// workgroups (wg0[0..n_mats]); returns false where the form does not apply.
+bool gemv_xs_plan(int n_mats, const int64_t *n_out, int64_t k_in, int streams, int n_cu, int32_t *wg0);
 int gemv_xs_depth();  // rows in flight per wave
-hipError_t launch_gemv_xs(const GemvXsParams &p, int64_t grid, int sb_bf16, int x_bf16, int streams,
-                          hipStream_t stream);
+hipError_t launch_gemv_xs(const GemvXsParams &p, int sb_bf16, int x_bf16, int streams, hipStream_t stream);
 
 // LDS bytes a GEMV launch needs: per token, the staged activation (padded to
 // ncx_pad chunks) and its chunk sums; then (MoE down) the float32 residual row

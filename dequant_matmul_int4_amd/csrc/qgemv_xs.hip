@@ -94,6 +94,21 @@ __device__ __forceinline__ float xs_sum16(float t) {
   return t;
 }
 
+// a[m] for a uniform m, by selects (no indexed copy of the kernel arguments)
+template <typename T>
+__device__ __forceinline__ T xs_pick(const T (&a)[kXsMaxMats], int m) {
+  T r = a[0];
+#pragma unroll
+  for (int i = 1; i < kXsMaxMats; ++i) r = m == i ? a[i] : r;
+  return r;
+}
+__device__ __forceinline__ int32_t xs_pick(const int32_t (&a)[kXsMaxMats + 1], int m) {
+  int32_t r = a[0];
+#pragma unroll
+  for (int i = 1; i <= kXsMaxMats; ++i) r = m == i ? a[i] : r;
+  return r;
+}
+
 // The activation of one chunk in the form the dot product takes: float32
 // values in element order, times 2^24 at even and 2^20 at odd positions
 // (XB = false), or the 16 bf16 pairs (x[8 jj + i], x[8 jj + i + 4]) of the
@@ -196,16 +211,23 @@ __global__ void __launch_bounds__(kXsMaxWaves * 64) qgemv_xs_kernel(const GemvXs
   const int sg = lane >> L2;              // row group of the lane inside a step
   const int c = L * w + (lane & (L - 1));  // this lane's chunk
   const bool active = c < p.ncx;
-  const int G = (int)gridDim.x, b = (int)blockIdx.x;
-  const int nr = (p.n_out - b + G - 1) / G;  // rows of this workgroup, <= kXsMaxRows
+  // this workgroup's matrix m (uniform) and its place b among matrix m's G
+  const int bid = (int)blockIdx.x;
+  int m = 0;
+#pragma unroll
+  for (int i = 1; i < kXsMaxMats; ++i) m = (i < p.n_mats && bid >= p.wg0[i]) ? i : m;
+  const int G = xs_pick(p.wg0, m + 1) - xs_pick(p.wg0, m), b = bid - xs_pick(p.wg0, m);
+  const int n_out = xs_pick(p.n_out, m);
+  const int nr = (n_out - b + G - 1) / G;  // rows of this workgroup, <= kXsMaxRows
 
   const __amdgpu_buffer_rsrc_t rx = xs_rsrc(p.x, (uint32_t)p.ncx * XCB);
   __amdgpu_buffer_rsrc_t rc[NS], rs[NS], rb[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    rc[s] = xs_rsrc(p.codes[s], (uint32_t)p.n_out * (uint32_t)p.kwb);
-    rs[s] = xs_rsrc(p.scales[s], (uint32_t)p.n_out * (uint32_t)p.sbrow);
-    rb[s] = xs_rsrc(p.biases[s], (uint32_t)p.n_out * (uint32_t)p.sbrow);
+    const int ms = NS == 2 ? s : m;  // the pair's streams, or this matrix
+    rc[s] = xs_rsrc(xs_pick(p.codes, ms), (uint32_t)n_out * (uint32_t)p.kwb);
+    rs[s] = xs_rsrc(xs_pick(p.scales, ms), (uint32_t)n_out * (uint32_t)p.sbrow);
+    rb[s] = xs_rsrc(xs_pick(p.biases, ms), (uint32_t)n_out * (uint32_t)p.sbrow);
   }
 
   // the chunk's activation: loads first, turned into registers after the
@@ -348,10 +370,11 @@ __global__ void __launch_bounds__(kXsMaxWaves * 64) qgemv_xs_kernel(const GemvXs
     float out = acc[0];
     if constexpr (NS == 2) out = (acc[0] / (1.f + __expf(-acc[0]))) * acc[1];  // silu(gate) * up
     const int64_t row = (int64_t)b + (int64_t)G * t;
+    void *y = xs_pick(p.y, m);
     if (p.y_bf16)
-      reinterpret_cast<__bf16 *>(p.y)[row] = (__bf16)out;
+      reinterpret_cast<__bf16 *>(y)[row] = (__bf16)out;
     else
-      reinterpret_cast<float *>(p.y)[row] = out;
+      reinterpret_cast<float *>(y)[row] = out;
   }
 }
 
@@ -373,38 +396,62 @@ int gemv_xs_waves(int64_t k_in) {
   return (int)((k_in / 32 + L - 1) / L);
 }
 
-// Rows of kXsMinK or more columns, and at least kXsMinCodes codes in all
-// (the 4096 x 4096 float32 GEMV, 16.8 M codes, stays faster on the
-// streaming GEMV: 4.9 against 5.2 us).
-bool gemv_xs_supported(int64_t n_out, int64_t k_in, int streams, int n_cu) {
-  if (k_in < kXsMinK || k_in > (int64_t)kXsMaxWaves * 2048 || k_in % 32 != 0) return false;
-  if (n_out * k_in * streams < kXsMinCodes) return false;
-  const int64_t grid = gemv_xs_grid(n_out, k_in, streams, n_cu);
-  return grid >= 1 && (n_out + grid - 1) / grid <= kXsMaxRows;
-}
-
-// Workgroups per CU: for the gate/up pair 16 / waves, one to four (measured
-// pair times at one per CU -> this rule: 17408 x 5120 23.2 -> 20.6 us at three,
-// 8192 x 8192 14.6 us at four -> 14.2 at two, 3072 x 16384 13.3 us at four ->
-// 10.4 at one); for one matrix two while a workgroup has at most five waves
-// (k_in up to 5120), else one (bf16 activations: 17408 x 5120 14.4 -> 11.3 us
-// and 14336 x 4096 8.8 -> 7.1 us at two; 6144 x 6144 5.9 -> 6.2 us and
-// 5120 x 17408 11.1 -> 11.5 us at two).
-int64_t gemv_xs_grid(int64_t n_out, int64_t k_in, int streams, int n_cu) {
+// Where the form applies, from cold-weight timings (a 1.2 GB pool of copies)
+// against the streaming GEMV:
+//   * stored outputs (bf16 or float32 activations): k_in >= 4096 and at least
+//     26,214,400 codes (5120 x 5120) in all (bf16: 5120 x 5120 7.41 -> 6.38 us,
+//     8192 x 8192 11.1 -> 9.6 us, 17408 x 5120 14.6 -> 12.1 us, 2048 x 32768
+//     13.4 -> 9.6 us; 6144 x 4096, q/k/v 4096 -> 4096/1024/1024 and 4096 x 4096
+//     are even or faster on the streaming GEMV: 5.6 against 6.0 us for q/k/v);
+//   * the gate/up pair: k_in >= 4096 and 2^25 codes.
+// Workgroups per CU: for the gate/up pair 16 / waves, one to four (17408 x
+// 5120 23.2 -> 20.6 us at three, 8192 x 8192 14.6 us at four -> 14.2 at two,
+// 3072 x 16384 13.3 us at four -> 10.4 at one); for stored outputs two while
+// a workgroup has at most eight waves, else one (cold, bf16: 6144 x 6144 8.0 ->
+// 7.2 us and 5120 x 5120 6.9 -> 6.4 us at two; 5120 x 17408 11.9 -> 12.4 us
+// and 4096 x 14336 9.0 -> 9.5 us at two).  One matrix takes min(that, n_out)
+// workgroups; several matrices take ceil(n_out / r) each, r = the rows per
+// workgroup of all their rows over that many workgroups.
+bool gemv_xs_plan(int n_mats, const int64_t *n_out, int64_t k_in, int streams, int n_cu, int32_t *wg0) {
+  if (n_mats < 1 || n_mats > kXsMaxMats || (streams == 2 && n_mats != 1) || (streams != 1 && streams != 2))
+    return false;
+  const int64_t min_codes = streams == 2 ? ((int64_t)1 << 25) : (int64_t)5120 * 5120;
+  if (k_in < 4096 || k_in > (int64_t)kXsMaxWaves * 2048 || k_in % 32 != 0) return false;
+  int64_t rows = 0;
+  for (int i = 0; i < n_mats; ++i) {
+    if (n_out[i] < 1) return false;
+    rows += n_out[i];
+  }
+  if (rows * k_in * streams < min_codes || rows > INT32_MAX) return false;
   const int w = gemv_xs_waves(k_in);
-  const int per_cu = streams == 2 ? std::max(1, std::min(4, 16 / w)) : (w <= 5 ? 2 : 1);
-  return std::min<int64_t>((int64_t)n_cu * per_cu, n_out);
+  const int per_cu = streams == 2 ? std::max(1, std::min(4, 16 / w)) : (w <= 8 ? 2 : 1);
+  const int64_t target = (int64_t)n_cu * per_cu;
+  const int64_t r = (rows + target - 1) / target;  // rows per workgroup (several matrices)
+  int64_t g = 0;
+  wg0[0] = 0;
+  for (int i = 0; i < n_mats; ++i) {
+    const int64_t gi = n_mats == 1 ? std::min<int64_t>(target, n_out[0]) : (n_out[i] + r - 1) / r;
+    if (gi < 1 || (n_out[i] + gi - 1) / gi > kXsMaxRows) return false;
+    g += gi;
+    if (g > INT32_MAX) return false;
+    wg0[i + 1] = (int32_t)g;
+  }
+  return true;
 }
 
 int gemv_xs_depth() { return kXsRowsInFlight; }
 
-hipError_t launch_gemv_xs(const GemvXsParams &p, int64_t grid, int sb_bf16, int x_bf16, int streams,
-                          hipStream_t stream) {
+hipError_t launch_gemv_xs(const GemvXsParams &p, int sb_bf16, int x_bf16, int streams, hipStream_t stream) {
   const int64_t k_in = (int64_t)p.ncx * 32;
   if (p.log2_lpr != gemv_xs_log2_lanes(k_in) || p.waves != gemv_xs_waves(k_in) || p.waves < 1 ||
-      p.waves > kXsMaxWaves || grid < 1 || grid > p.n_out ||
-      ((int64_t)p.n_out + grid - 1) / grid > kXsMaxRows || (streams != 1 && streams != 2))
+      p.waves > kXsMaxWaves || (streams != 1 && streams != 2) || p.n_mats < 1 || p.n_mats > kXsMaxMats ||
+      (streams == 2 && p.n_mats != 1) || p.wg0[0] != 0)
     return hipErrorInvalidValue;
+  for (int i = 0; i < p.n_mats; ++i) {
+    const int64_t gi = (int64_t)p.wg0[i + 1] - p.wg0[i];
+    if (gi < 1 || gi > p.n_out[i] || ((int64_t)p.n_out[i] + gi - 1) / gi > kXsMaxRows) return hipErrorInvalidValue;
+  }
+  const int64_t grid = p.wg0[p.n_mats];
   if (streams == 2)
     return x_bf16 ? (sb_bf16 ? xs_launch<1, true, 2>(p, grid, stream) : xs_launch<0, true, 2>(p, grid, stream))
                   : (sb_bf16 ? xs_launch<1, false, 2>(p, grid, stream) : xs_launch<0, false, 2>(p, grid, stream));

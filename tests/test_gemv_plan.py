@@ -41,8 +41,17 @@ def test_qkv_projection_is_one_task_pair_per_wave():
     """q/k/v of a 4096 activation (6144 rows): 12 waves per CU, 64 lanes a row, 2 rows per task,
     one task per wave, so a one-pass ring of depth 2."""
     f = q.plan_qgemv([4096, 1024, 1024], 4096, n_cu=N_CU)
-    assert (f["waves"], f["lanes"], f["rows_per_task"], f["steps_per_task"]) == (12, 64, 2, 2)
+    assert (f["kernel"], f["waves"], f["lanes"], f["rows_per_task"], f["steps_per_task"]) == \
+        ("ring", 12, 64, 2, 2)
     assert f["grid"] == N_CU and f["ring_depth"] == 2 and f["launches"] == 1
+
+
+def test_xs_form_for_several_matrices():
+    """q/k/v of an 8192 activation (10240 rows, 8 waves of 32 lanes): two workgroups per CU
+    shared out by rows, 20 a workgroup (410 + 52 + 52 workgroups)."""
+    f = q.plan_qgemv([8192, 1024, 1024], 8192, x_dtype="bf16", n_cu=N_CU)
+    assert (f["kernel"], f["waves"], f["lanes"], f["grid"], f["tasks"], f["busiest_wave_steps"],
+            f["launches"]) == ("xs", 8, 32, 410 + 52 + 52, 10240, 20, 1)
 
 
 @pytest.mark.parametrize("n_outs,k_in,x_dt,epi,call,T", [
@@ -87,10 +96,10 @@ def test_smallm_mfma_form():
 
 
 def test_xs_form_for_long_rows():
-    """One matrix, 4096 <= k_in <= 32768 and at least 2^25 codes (the dense down projection
-    17408 -> 5120): the activation-stationary kernel, 32 lanes a row (two rows a step) while that
-    takes at most 16 waves, else 64; two workgroups per CU while a workgroup has at most five
-    waves, else one."""
+    """One matrix, 4096 <= k_in <= 32768 and at least 5120 x 5120 codes (the dense down
+    projection 17408 -> 5120): the activation-stationary kernel, 32 lanes a row (two rows a step)
+    while that takes at most 16 waves, else 64; two workgroups per CU while a workgroup has at
+    most eight waves, else one."""
     for x_dt in ("f32", "bf16"):
         f = q.plan_qgemv([5120], 17408, x_dtype=x_dt, n_cu=N_CU)
         assert (f["kernel"], f["grid"], f["waves"], f["lanes"], f["tasks"], f["busiest_wave_steps"],
@@ -98,12 +107,14 @@ def test_xs_form_for_long_rows():
         f = q.plan_qgemv([17408], 5120, x_dtype=x_dt, n_cu=N_CU)
         assert (f["kernel"], f["grid"], f["waves"], f["lanes"], f["busiest_wave_steps"]) == \
             ("xs", 2 * N_CU, 5, 32, 34)
+        f = q.plan_qgemv([5120], 5120, x_dtype=x_dt, n_cu=N_CU)
+        assert (f["kernel"], f["grid"]) == ("xs", 2 * N_CU)
     f = q.plan_qgemv([5000], 8192, x_dtype="f32", n_cu=N_CU)
-    assert (f["kernel"], f["waves"], f["lanes"], f["rows_per_task"], f["busiest_wave_steps"]) == \
-        ("xs", 8, 32, 2, 20)
+    assert (f["kernel"], f["grid"], f["waves"], f["lanes"], f["rows_per_task"], f["busiest_wave_steps"]) == \
+        ("xs", 2 * N_CU, 8, 32, 2, 10)
     f = q.plan_qgemv([4100], 8320, group_size=32, x_dtype="f32", n_cu=N_CU)
     assert (f["kernel"], f["waves"], f["lanes"]) == ("xs", 9, 32)
-    f = q.plan_qgemv([256 * N_CU], 6144, x_dtype="f32", n_cu=N_CU)
+    f = q.plan_qgemv([256 * N_CU], 8320, x_dtype="f32", n_cu=N_CU)
     assert (f["kernel"], f["grid"], f["busiest_wave_steps"]) == ("xs", N_CU, 256)
     f = q.plan_qgemv([512 * N_CU], 4096, x_dtype="bf16", n_cu=N_CU)
     assert (f["kernel"], f["grid"], f["busiest_wave_steps"]) == ("xs", 2 * N_CU, 256)
@@ -112,15 +123,17 @@ def test_xs_form_for_long_rows():
 
 
 @pytest.mark.parametrize("n_outs,k_in,x_dt,epi,call", [
-    ([9000], 3584, "f32", q.EPI_NONE, q.CALL_QGEMV),             # rows shorter than 4096
+    ([9000], 3584, "f32", q.EPI_NONE, q.CALL_QGEMV),             # float32 rows shorter than 4096
+    ([9000], 3584, "bf16", q.EPI_NONE, q.CALL_QGEMV),            # bf16 rows shorter than 4096
     ([2000], 32832, "f32", q.EPI_NONE, q.CALL_QGEMV),            # more than 16 waves of 64 lanes
-    ([4096], 4096, "f32", q.EPI_NONE, q.CALL_QGEMV),             # fewer than 2^25 codes
-    ([5120], 5120, "bf16", q.EPI_NONE, q.CALL_QGEMV),            # the same
-    ([256 * N_CU + 1], 6144, "f32", q.EPI_NONE, q.CALL_QGEMV),   # over 256 rows a workgroup
+    ([4096], 4096, "f32", q.EPI_NONE, q.CALL_QGEMV),             # fewer than 5120 x 5120 codes
+    ([6144], 4096, "bf16", q.EPI_NONE, q.CALL_QGEMV),            # the same
+    ([4096, 1024, 1024], 4096, "bf16", q.EPI_NONE, q.CALL_QGEMV),  # q/k/v of 4096: the same
+    ([256 * N_CU + 1], 8320, "f32", q.EPI_NONE, q.CALL_QGEMV),   # over 256 rows a workgroup
     ([512 * N_CU + 1], 4096, "bf16", q.EPI_NONE, q.CALL_QGEMV),  # the same, two per CU
-    ([5120, 5120], 17408, "f32", q.EPI_NONE, q.CALL_QGEMV),      # two matrices
     ([5120], 17408, "f32", q.EPI_NONE, q.CALL_RMS_NORM),         # RMSNorm prologue
     ([5120, 5120], 3584, "bf16", q.EPI_SWIGLU_PAIR, q.CALL_QGEMV),  # pair, short rows
+    ([2000, 2000], 8192, "bf16", q.EPI_SWIGLU_PAIR, q.CALL_QGEMV),  # pair, fewer than 2^25 codes
     ([5120, 5120], 17408, "bf16", q.EPI_SWIGLU_PAIR, q.CALL_SMALLM),  # small-M call
 ])
 def test_xs_form_only_where_it_applies(n_outs, k_in, x_dt, epi, call):

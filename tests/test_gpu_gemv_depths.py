@@ -24,8 +24,8 @@ def _gpu():
 # (n_out, k_in, x dtype, ring depth, steps of the busiest wave)
 GEMV_CASES = [
     (8, 2048, "bf16", 1, 1),
-    (7000, 2048, "bf16", 2, 2),
-    (20000, 2048, "bf16", 4, 4),
+    (14000, 1024, "bf16", 2, 2),
+    (28250, 1024, "bf16", 4, 4),
     (30000, 512, "bf16", 4, 3),
     (25000, 512, "bf16", 0, 5),
     (8, 1024, "f32", 1, 1),

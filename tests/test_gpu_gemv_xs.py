@@ -60,15 +60,16 @@ def test_xs_single_shapes_and_dtypes(n_out, k_in, g, sb_dt, y_dt, x_dt):
 
 
 def test_xs_most_rows_per_workgroup():
-    """256 rows per workgroup (the form's limit) on a 6144-wide matrix (one workgroup per CU)."""
+    """256 rows per workgroup (the form's limit) on an 8320-wide matrix (nine waves, one
+    workgroup per CU)."""
     n_out = 256 * _n_cu()
     rng = np.random.default_rng(4242)
-    w = synth.draw_matrix(rng, n_out, 6144, 64, "bf16")
-    x = synth.draw_activation(rng, (6144,), "f32")
+    w = synth.draw_matrix(rng, n_out, 8320, 64, "bf16")
+    x = synth.draw_activation(rng, (8320,), "f32")
     y, f = _run_single(w, x, "f32", "f32")
-    assert f["busiest_wave_steps"] == 256
+    assert f["busiest_wave_steps"] == 256 and f["grid"] == _n_cu()
     y_ref, a_ref = oracle.gemv(w, x, "f32", threads=oracle_threads())
-    check(y, y_ref, a_ref, "xs gemv %dx6144 (256 rows per workgroup)" % n_out)
+    check(y, y_ref, a_ref, "xs gemv %dx8320 (256 rows per workgroup)" % n_out)
 
 
 @pytest.mark.parametrize("lo,hi", [(-100, -60), (-20, 100)])
@@ -85,6 +86,32 @@ def test_xs_float32_activation_range(lo, hi):
     y, f = _run_single(w, x, "f32", "f32")
     y_ref, a_ref = oracle.gemv(w, x, "f32", threads=oracle_threads())
     check(y, y_ref, a_ref, "xs gemv %dx%d, activations from 2^%d to 2^%d" % (n_out, k_in, lo, hi))
+
+
+# matrices sharing x with stored outputs, each with its own workgroups: q/k/v of a 5120
+# activation; three odd sizes (37 rows: one workgroup); eight matrices over 4608 columns (five
+# waves, the last half full); single matrices at the threshold (5120 x 5120 codes)
+MULTI = [([5120, 1024, 1024], 5120), ([3001, 37, 1499], 8192), ([800] * 8, 4608), ([5120], 5120),
+         ([2560], 10240)]
+
+
+@pytest.mark.parametrize("n_outs,k_in", MULTI)
+@pytest.mark.parametrize("x_dt,sb_dt,y_dt", [("bf16", "bf16", "bf16"), ("bf16", "f32", "f32"),
+                                             ("f32", "bf16", "f32")])
+def test_xs_multi(n_outs, k_in, x_dt, sb_dt, y_dt):
+    q = lib()
+    f = q.plan_qgemv(n_outs, k_in, x_dtype=x_dt)
+    assert f["kernel"] == "xs", f
+    rng = np.random.default_rng(sum(n_outs) + k_in + len(n_outs))
+    ws = [synth.draw_matrix(rng, n, k_in, 64, sb_dt) for n in n_outs]
+    x = synth.draw_activation(rng, (k_in,), x_dt)
+    ys = [nan_like(n, TD[y_dt]) for n in n_outs]
+    q.qgemv_int4_multi([dev_matrix(w) for w in ws], synth.to_torch(x, x_dt), ys)
+    torch.cuda.synchronize()
+    for i, (w, y) in enumerate(zip(ws, ys)):
+        y_ref, a_ref = oracle.gemv(w, x, x_dt, threads=oracle_threads())
+        check(y, y_ref, a_ref, "xs multi %s x %d, matrix %d, x %s %s/%s (grid %d)" %
+              (n_outs, k_in, i, x_dt, sb_dt, y_dt, f["grid"]))
 
 
 # (n_out, k_in, x dtype): the dense FFN gate/up pair 17408 x 5120 (three workgroups per CU);
