@@ -116,7 +116,10 @@ typedef struct qint4_matrix {
  *   y       device [n_out], dtype y_dtype (QINT4_F32 or QINT4_BF16);
  *           every element is overwritten (bf16: round to nearest even from
  *           the float32 accumulator)
- * Accumulation is float32.  Returns QINT4_OK or an error status.
+ * Accumulation is float32.  Float32 activations enter the products scaled by
+ * up to 2^24 (exactly, by powers of two), so activations of magnitude 2^104
+ * or more overflow to inf; as do scales of that size in the prefill GEMMs'
+ * dequantisation.  Returns QINT4_OK or an error status.
  */
 qint4_status qgemv_int4(const qint4_matrix *w, const void *x, int32_t x_dtype,
                         void *y, int32_t y_dtype, void *stream);
@@ -504,14 +507,15 @@ qint4_status quantize_int4(const void *w, int32_t w_dtype, int64_t n_rows, int64
  * 1, 2 or 4 is a ring filled once, taken when no wave has more steps than
  * that.  The small-M MFMA kernels (QINT4_FORM_MFMA) run one 16-row tile per
  * workgroup, its K range split over `waves` waves.  The activation-stationary
- * kernel (QINT4_FORM_XS: qgemv_int4 / qgemv_int4_multi at T = 1 on one
- * matrix or on the gate/up pair; k_in from 4096 to 32768 and at least 2^25
- * codes in all) gives lane j of a row group of wave
- * w the 32-code chunk lanes * w + j of its rows, whose activations it holds
- * in registers; a workgroup's `waves` waves cover k_in, and workgroup b of
- * `grid` takes rows b, b + grid, ... (rows_per_task: rows per wave step;
- * busiest_wave_steps: rows of the busiest workgroup; ring_depth: rows in
- * flight per wave).  ([FFAI #9], the note on
+ * kernel (QINT4_FORM_XS: qgemv_int4 / qgemv_int4_multi at T = 1 on one to
+ * eight matrices with stored outputs, k_in from 4096 to 32768 and at least
+ * 5120 * 5120 codes in all, or on the gate/up pair with at least 2^25) gives
+ * lane j of a row group of wave w the 32-code chunk lanes * w + j of its
+ * rows, whose activations it holds in registers; a workgroup's `waves` waves
+ * cover k_in.  Each matrix owns a range of the `grid` workgroups, and its
+ * workgroup b of G takes rows b, b + G, ... (tasks: rows of all matrices;
+ * rows_per_task: rows per wave step; busiest_wave_steps: rows of the busiest
+ * workgroup; ring_depth: rows in flight per wave).  ([FFAI #9], the note on
  * T=1 decode negative results, structural conclusion: decode is bound by the
  * bandwidth of the expert weight gather; the plan keeps enough loads in
  * flight on every CU.)
