@@ -403,7 +403,9 @@ int gemv_xs_waves(int64_t k_in) {
 //     8192 x 8192 11.1 -> 9.6 us, 17408 x 5120 14.6 -> 12.1 us, 2048 x 32768
 //     13.4 -> 9.6 us; 6144 x 4096, q/k/v 4096 -> 4096/1024/1024 and 4096 x 4096
 //     are even or faster on the streaming GEMV: 5.6 against 6.0 us for q/k/v);
-//   * the gate/up pair: k_in >= 4096 and 2^25 codes.
+//   * the gate/up pair: k_in >= 2048 and 2^25 codes (8192 x 2048 7.67 ->
+//     6.72 us, 8192 x 3072 9.00 -> 8.57 us, 14336 x 4096 16.1 -> 14.9 us;
+//     5632 x 2048 and smaller pairs are faster on the streaming GEMV).
 // Workgroups per CU: for the gate/up pair 16 / waves, one to four (17408 x
 // 5120 23.2 -> 20.6 us at three, 8192 x 8192 14.6 us at four -> 14.2 at two,
 // 3072 x 16384 13.3 us at four -> 10.4 at one); for stored outputs two while
@@ -416,7 +418,7 @@ bool gemv_xs_plan(int n_mats, const int64_t *n_out, int64_t k_in, int streams, i
   if (n_mats < 1 || n_mats > kXsMaxMats || (streams == 2 && n_mats != 1) || (streams != 1 && streams != 2))
     return false;
   const int64_t min_codes = streams == 2 ? ((int64_t)1 << 25) : (int64_t)5120 * 5120;
-  if (k_in < 4096 || k_in > (int64_t)kXsMaxWaves * 2048 || k_in % 32 != 0) return false;
+  if (k_in < (streams == 2 ? 2048 : 4096) || k_in > (int64_t)kXsMaxWaves * 2048 || k_in % 32 != 0) return false;
   int64_t rows = 0;
   for (int i = 0; i < n_mats; ++i) {
     if (n_out[i] < 1) return false;

@@ -132,7 +132,7 @@ def test_xs_form_for_long_rows():
     ([256 * N_CU + 1], 8320, "f32", q.EPI_NONE, q.CALL_QGEMV),   # over 256 rows a workgroup
     ([512 * N_CU + 1], 4096, "bf16", q.EPI_NONE, q.CALL_QGEMV),  # the same, two per CU
     ([5120], 17408, "f32", q.EPI_NONE, q.CALL_RMS_NORM),         # RMSNorm prologue
-    ([5120, 5120], 3584, "bf16", q.EPI_SWIGLU_PAIR, q.CALL_QGEMV),  # pair, short rows
+    ([9000, 9000], 1984, "bf16", q.EPI_SWIGLU_PAIR, q.CALL_QGEMV),  # pair, rows under 2048
     ([2000, 2000], 8192, "bf16", q.EPI_SWIGLU_PAIR, q.CALL_QGEMV),  # pair, fewer than 2^25 codes
     ([5120, 5120], 17408, "bf16", q.EPI_SWIGLU_PAIR, q.CALL_SMALLM),  # small-M call
 ])
@@ -142,7 +142,7 @@ def test_xs_form_only_where_it_applies(n_outs, k_in, x_dt, epi, call):
 
 
 def test_xs_form_for_the_gate_up_pair():
-    """The T=1 gate/up pair with 4096 <= k_in <= 32768 (dense FFN 5120 -> 17408): 32 lanes a
+    """The T=1 gate/up pair with 2048 <= k_in <= 32768 (dense FFN 5120 -> 17408): 32 lanes a
     row (two rows a step) up to 16384 columns, 64 beyond; 16 / waves workgroups per CU, one to
     four."""
     f = q.plan_qgemv([17408, 17408], 5120, epilogue=q.EPI_SWIGLU_PAIR, n_cu=N_CU)
@@ -154,6 +154,8 @@ def test_xs_form_for_the_gate_up_pair():
     assert (f["kernel"], f["grid"], f["waves"]) == ("xs", 2 * N_CU, 8)
     f = q.plan_qgemv([2048, 2048], 17408, x_dtype="f32", epilogue=q.EPI_SWIGLU_PAIR, n_cu=N_CU)
     assert (f["kernel"], f["grid"], f["waves"], f["lanes"]) == ("xs", N_CU, 9, 64)
+    f = q.plan_qgemv([8192, 8192], 2048, epilogue=q.EPI_SWIGLU_PAIR, n_cu=N_CU)
+    assert (f["kernel"], f["grid"], f["waves"], f["lanes"]) == ("xs", 4 * N_CU, 2, 32)
     f = q.plan_qgemv([1000, 1000], 32768, epilogue=q.EPI_SWIGLU_PAIR, n_cu=N_CU)
     assert (f["kernel"], f["grid"], f["waves"], f["lanes"], f["busiest_wave_steps"]) == \
         ("xs", N_CU, 16, 64, 4)

@@ -116,9 +116,10 @@ def test_xs_multi(n_outs, k_in, x_dt, sb_dt, y_dt):
 
 # (n_out, k_in, x dtype): the dense FFN gate/up pair 17408 x 5120 (three workgroups per CU);
 # 6144 and 8192 columns (two per CU), 5 or 6 and 4 or 5 rows per workgroup; 1000 rows over 32768
-# columns (16 waves of 64 lanes, one workgroup per CU); float32 activations over 17408 columns
+# columns (16 waves of 64 lanes, one workgroup per CU); float32 activations over 17408 columns;
+# 2048 and 3072 columns (two and three waves, four workgroups per CU)
 PAIRS = [(17408, 5120, "bf16"), (3000, 6144, "bf16"), (2100, 8192, "bf16"), (1000, 32768, "bf16"),
-         (2048, 17408, "f32")]
+         (2048, 17408, "f32"), (8192, 2048, "bf16"), (6000, 3072, "f32")]
 
 
 @pytest.mark.parametrize("n_out,k_in,x_dt", PAIRS)
