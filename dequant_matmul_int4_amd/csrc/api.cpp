@@ -195,6 +195,7 @@ constexpr int kMaxWaves = 12;  // waves per workgroup (one persistent workgroup 
 // of a task) add one load's worth per step: taller tasks share those reads.
 // The cheapest wins (ties: larger RT, then more waves).  A residual row (MoE down) must fit the
 // workgroup's one-pass staging: 4 vectors of 16 bytes per thread.
+constexpr double kPlanTie = 0.02;
 template <class TasksFor>
 GemvPlan plan_gemv(int cpr, int n_cu, int xmode, int64_t residual_rows, TasksFor tasks_for,
                    int tt = 1, int max_rt = 2) {
@@ -221,8 +222,8 @@ GemvPlan plan_gemv(int cpr, int n_cu, int xmode, int64_t residual_rows, TasksFor
         const int64_t tpw = (n_tasks + nw - 1) / nw;
         double cost = (double)tpw * w * spt * (rt + x_reads);
         if ((int64_t)cpr * 4 > (int64_t)xq_octets * w) cost *= 1.5;  // staging needs extra rounds
-        const bool better = cost < best_cost * (1 - 1e-9) ||
-                            (cost <= best_cost * (1 + 1e-9) &&
+        const bool better = cost < best_cost * (1 - kPlanTie) ||
+                            (cost <= best_cost * (1 + kPlanTie) &&
                              (rt > best.rt || (rt == best.rt && w > best.waves)));
         if (better) {
           best_cost = cost;

@@ -398,27 +398,30 @@ int gemv_xs_waves(int64_t k_in) {
 
 // Where the form applies, from cold-weight timings (a 1.2 GB pool of copies)
 // against the streaming GEMV:
-//   * stored outputs (bf16 or float32 activations): k_in >= 4096 and at least
+//   * stored outputs (bf16 or float32 activations): k_in >= 2048 and at least
 //     26,214,400 codes (5120 x 5120) in all (bf16: 5120 x 5120 7.41 -> 6.38 us,
 //     8192 x 8192 11.1 -> 9.6 us, 17408 x 5120 14.6 -> 12.1 us, 2048 x 32768
-//     13.4 -> 9.6 us; 6144 x 4096, q/k/v 4096 -> 4096/1024/1024 and 4096 x 4096
-//     are even or faster on the streaming GEMV: 5.6 against 6.0 us for q/k/v);
+//     13.4 -> 9.6 us, 12800 x 2048 9.0 -> 6.3 us, 128256 x 2048 86.7 -> 30.0
+//     us; 6144 x 4096, q/k/v 4096 -> 4096/1024/1024 and 4096 x 4096 are even
+//     or faster on the streaming GEMV: 5.6 against 6.0 us for q/k/v);
 //   * the gate/up pair: k_in >= 2048 and 2^25 codes (8192 x 2048 7.67 ->
 //     6.72 us, 8192 x 3072 9.00 -> 8.57 us, 14336 x 4096 16.1 -> 14.9 us;
 //     5632 x 2048 and smaller pairs are faster on the streaming GEMV).
 // Workgroups per CU: for the gate/up pair 16 / waves, one to four (17408 x
 // 5120 23.2 -> 20.6 us at three, 8192 x 8192 14.6 us at four -> 14.2 at two,
-// 3072 x 16384 13.3 us at four -> 10.4 at one); for stored outputs two while
-// a workgroup has at most eight waves, else one (cold, bf16: 6144 x 6144 8.0 ->
-// 7.2 us and 5120 x 5120 6.9 -> 6.4 us at two; 5120 x 17408 11.9 -> 12.4 us
-// and 4096 x 14336 9.0 -> 9.5 us at two).  One matrix takes min(that, n_out)
-// workgroups; several matrices take ceil(n_out / r) each, r = the rows per
-// workgroup of all their rows over that many workgroups.
+// 3072 x 16384 13.3 us at four -> 10.4 at one; eight for two-wave pairs is
+// 30% slower); for stored outputs four up to three waves, two up to eight,
+// else one (cold, bf16: 128256 x 2048 46.8 -> 30.0 us at four instead of
+// two; 6144 x 6144 8.0 -> 7.2 us and 5120 x 5120 6.9 -> 6.4 us at two;
+// 5120 x 17408 11.9 -> 12.4 us and 4096 x 14336 9.0 -> 9.5 us at two); more
+// where a workgroup would get over kXsMaxRows rows.  One matrix takes
+// min(that, n_out) workgroups; several matrices take ceil(n_out / r) each,
+// r = the rows per workgroup of all their rows over that many workgroups.
 bool gemv_xs_plan(int n_mats, const int64_t *n_out, int64_t k_in, int streams, int n_cu, int32_t *wg0) {
   if (n_mats < 1 || n_mats > kXsMaxMats || (streams == 2 && n_mats != 1) || (streams != 1 && streams != 2))
     return false;
   const int64_t min_codes = streams == 2 ? ((int64_t)1 << 25) : (int64_t)5120 * 5120;
-  if (k_in < (streams == 2 ? 2048 : 4096) || k_in > (int64_t)kXsMaxWaves * 2048 || k_in % 32 != 0) return false;
+  if (k_in < 2048 || k_in > (int64_t)kXsMaxWaves * 2048 || k_in % 32 != 0) return false;
   int64_t rows = 0;
   for (int i = 0; i < n_mats; ++i) {
     if (n_out[i] < 1) return false;
@@ -426,8 +429,9 @@ bool gemv_xs_plan(int n_mats, const int64_t *n_out, int64_t k_in, int streams, i
   }
   if (rows * k_in * streams < min_codes || rows > INT32_MAX) return false;
   const int w = gemv_xs_waves(k_in);
-  const int per_cu = streams == 2 ? std::max(1, std::min(4, 16 / w)) : (w <= 8 ? 2 : 1);
-  const int64_t target = (int64_t)n_cu * per_cu;
+  const int per_cu = streams == 2 ? std::max(1, std::min(4, 16 / w)) : (w <= 3 ? 4 : w <= 8 ? 2 : 1);
+  // more workgroups where that would leave over kXsMaxRows rows to one
+  const int64_t target = std::max<int64_t>((int64_t)n_cu * per_cu, (rows + kXsMaxRows - 1) / kXsMaxRows);
   const int64_t r = (rows + target - 1) / target;  // rows per workgroup (several matrices)
   int64_t g = 0;
   wg0[0] = 0;

@@ -120,17 +120,23 @@ def test_xs_form_for_long_rows():
     assert (f["kernel"], f["grid"], f["busiest_wave_steps"]) == ("xs", 2 * N_CU, 256)
     f = q.plan_qgemv([2049], 32768, x_dtype="f32", n_cu=N_CU)
     assert (f["kernel"], f["waves"], f["lanes"]) == ("xs", 16, 64)
+    # short rows: four workgroups per CU up to three waves (the 128256-row LM head over 2048
+    # columns), and more workgroups where one would get over 256 rows
+    f = q.plan_qgemv([128256], 2048, x_dtype="bf16", n_cu=N_CU)
+    assert (f["kernel"], f["grid"], f["waves"], f["busiest_wave_steps"]) == ("xs", 4 * N_CU, 2, 126)
+    f = q.plan_qgemv([152064], 5120, x_dtype="bf16", n_cu=N_CU)
+    assert (f["kernel"], f["grid"], f["busiest_wave_steps"]) == ("xs", 594, 256)
+    f = q.plan_qgemv([512 * N_CU + 1], 4096, x_dtype="bf16", n_cu=N_CU)
+    assert f["kernel"] == "xs" and f["busiest_wave_steps"] <= 256
 
 
 @pytest.mark.parametrize("n_outs,k_in,x_dt,epi,call", [
-    ([9000], 3584, "f32", q.EPI_NONE, q.CALL_QGEMV),             # float32 rows shorter than 4096
-    ([9000], 3584, "bf16", q.EPI_NONE, q.CALL_QGEMV),            # bf16 rows shorter than 4096
+    ([9000], 1984, "f32", q.EPI_NONE, q.CALL_QGEMV),             # rows shorter than 2048
+    ([14000], 1984, "bf16", q.EPI_NONE, q.CALL_QGEMV),           # the same
     ([2000], 32832, "f32", q.EPI_NONE, q.CALL_QGEMV),            # more than 16 waves of 64 lanes
     ([4096], 4096, "f32", q.EPI_NONE, q.CALL_QGEMV),             # fewer than 5120 x 5120 codes
     ([6144], 4096, "bf16", q.EPI_NONE, q.CALL_QGEMV),            # the same
     ([4096, 1024, 1024], 4096, "bf16", q.EPI_NONE, q.CALL_QGEMV),  # q/k/v of 4096: the same
-    ([256 * N_CU + 1], 8320, "f32", q.EPI_NONE, q.CALL_QGEMV),   # over 256 rows a workgroup
-    ([512 * N_CU + 1], 4096, "bf16", q.EPI_NONE, q.CALL_QGEMV),  # the same, two per CU
     ([5120], 17408, "f32", q.EPI_NONE, q.CALL_RMS_NORM),         # RMSNorm prologue
     ([9000, 9000], 1984, "bf16", q.EPI_SWIGLU_PAIR, q.CALL_QGEMV),  # pair, rows under 2048
     ([2000, 2000], 8192, "bf16", q.EPI_SWIGLU_PAIR, q.CALL_QGEMV),  # pair, fewer than 2^25 codes

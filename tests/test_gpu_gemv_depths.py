@@ -30,7 +30,7 @@ GEMV_CASES = [
     (25000, 512, "bf16", 0, 5),
     (8, 1024, "f32", 1, 1),
     (16000, 1024, "f32", 2, 2),
-    (16000, 2048, "f32", 4, 4),
+    (27750, 1024, "f32", 4, 4),
 ]
 
 

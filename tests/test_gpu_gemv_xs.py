@@ -39,9 +39,9 @@ def _run_single(w, x, x_dt, y_dt):
 # (n_out, k_in, group size): 5000 rows, 19 or 20 per workgroup, 32 lanes a row; 8320 = 260
 # chunks, the ninth wave holding 4 per row group; 16384 / g128, 16 waves of 32 lanes; 17408 (the
 # dense down projection), 64 lanes a row; 32768, 16 waves of 64 lanes; 5120 columns, five waves,
-# two workgroups per CU
+# two workgroups per CU; 2048 columns, two waves, four workgroups per CU
 SINGLE = [(5000, 8192, 64), (4100, 8320, 32), (2100, 16384, 128), (2000, 17408, 64), (2049, 32768, 64),
-          (7001, 5120, 64)]
+          (7001, 5120, 64), (12801, 2048, 64)]
 
 
 @pytest.mark.parametrize("n_out,k_in,g", SINGLE)
