@@ -320,9 +320,10 @@ qint4_status plan_multi(int n_outs, const int64_t *n_out, int64_t k_in, int grou
   // wave holds its slice of x in registers (dense FFN 5120 -> 17408 -> 5120:
   // gate/up 22.6 -> 20.6 us, float32 down 16.3 -> 12.5 us; bf16 activations,
   // one matrix: 5120 x 17408 14.5 -> 11.1 us, 17408 x 5120 14.1 -> 11.3 us,
-  // 2048 x 32768 12.3 -> 8.0 us; where it applies: gemv_xs_plan).  (Not for
-  // small-M calls, whose rows must not depend on T.)
-  if (!batched && !rms && T == 1 && n_outs <= kXsMaxMats &&
+  // 2048 x 32768 12.3 -> 8.0 us; where it applies: gemv_xs_plan), with or
+  // without the RMSNorm prologue.  (Not for small-M calls, whose rows must not
+  // depend on T.)
+  if (!batched && T == 1 && n_outs <= kXsMaxMats &&
       gemv_xs_plan(n_outs, n_out, k_in, streams, n_cu, mp->wg0)) {
     mp->xs = true;
     mp->blk = 1;
@@ -583,6 +584,8 @@ qint4_status run_multi(int32_t n, const qint4_matrix *ws, const void *x, int32_t
     for (int i = 0; i <= n_outs; ++i) p.wg0[i] = mp.wg0[i];
     p.n_mats = n_outs;
     p.x = x;
+    p.gamma = gamma;
+    p.eps = eps;
     p.ncx = (int32_t)(k_in / 32);
     p.kwb = (int32_t)(k_in / 2);
     p.sbrow = (int32_t)sbrow_b;

@@ -192,6 +192,8 @@ struct GemvXsParams {
   int32_t wg0[kXsMaxMats + 1];
   int32_t n_mats;
   const void *x;       // float32 or bf16 bits
+  const void *gamma;   // RMSNorm weight (x's dtype), or NULL: no RMSNorm prologue
+  float eps;           // RMSNorm epsilon
   int32_t ncx;         // k_in / 32
   int32_t kwb;         // code bytes of one row
   int32_t sbrow;       // scale (= bias) bytes of one row
@@ -207,6 +209,8 @@ int gemv_xs_waves(int64_t k_in);
 bool gemv_xs_plan(int n_mats, const int64_t *n_out, int64_t k_in, int streams, int n_cu, int32_t *wg0);
 int gemv_xs_depth();  // rows in flight per wave
 hipError_t launch_gemv_xs(const GemvXsParams &p, int sb_bf16, int x_bf16, int streams, hipStream_t stream);
+// (p.gamma != NULL: x * gamma is the activation and the row sums are scaled by
+// 1 / sqrt(sum(x^2) / k_in + eps), as in the streaming GEMV's RMSNorm form)
 
 // LDS bytes a GEMV launch needs: per token, the staged activation (padded to
 // ncx_pad chunks) and its chunk sums; then (MoE down) the float32 residual row

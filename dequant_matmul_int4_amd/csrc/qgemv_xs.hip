@@ -1,7 +1,9 @@
 // qgemv_xs.hip -- T=1 int4 group-affine GEMVs with the activation held in
-// registers ("activation-stationary") on gfx950: one matrix over long rows
-// (the dense FFN down projection, with float32 activations), and the gate/up
-// pair with the SwiGLU epilogue (the dense FFN gate/up projection).
+// registers ("activation-stationary") on gfx950: matrices over long rows
+// sharing x (the dense FFN down projection, with float32 activations; LM
+// heads; large projections), and the gate/up pair with the SwiGLU epilogue
+// (the dense FFN gate/up projection), each optionally behind the RMSNorm
+// prologue.
 //
 // Sources (by page title and passage):
 //   [FFAI #14] thewafflehaus/FFAI pull 14, "feat(everything-bagel): clean
@@ -190,20 +192,25 @@ __device__ __forceinline__ float xs_dot_bf16(const uint4 q, const XsChunk<true> 
   return (a[0] + a[1]) + (a[2] + a[3]);
 }
 
-// XB: bf16 activations; NS: code streams (1 stored outputs, 2 the gate/up
-// pair); L2: log2 of the lanes per row (5 or 6).
-template <int SBT, bool XB, int NS, int L2>
+// XB: bf16 activations into the bf16 dot product; NS: code streams (1 stored
+// outputs, 2 the gate/up pair); L2: log2 of the lanes per row (5 or 6); RM:
+// RMSNorm prologue, 0 none, 1 with bf16 x and gamma, 2 with float32 (the
+// float32 dot product on x * gamma).
+template <int SBT, bool XB, int NS, int L2, int RM>
 __global__ void __launch_bounds__(kXsMaxWaves * 64) qgemv_xs_kernel(const GemvXsParams p) {
   constexpr int L = 1 << L2;
   constexpr int RPS = 64 / L;                  // rows per step
   constexpr int D = kXsRowsInFlight / RPS;     // steps in flight
   constexpr int SPB = 4 / RPS;                 // steps per block of 4 rows
   constexpr uint32_t SBB = SBT == 1 ? 2u : 4u;
-  constexpr uint32_t XCB = XB ? 64u : 128u;    // activation bytes of one chunk
+  constexpr bool XIN16 = XB || RM == 1;        // activations stored as bf16
+  constexpr uint32_t XCB = XIN16 ? 64u : 128u;  // activation bytes of one chunk
   static_assert(L2 == 5 || L2 == 6, "32 or 64 lanes per row");
+  static_assert(RM == 0 || !XB, "the RMSNorm form takes the float32 dot product");
   // per-row sums of each wave and stream; row kXsMaxRows takes the lanes that
   // hold no row
   __shared__ float part[NS][kXsMaxRows + 1][kXsMaxWaves + 1];
+  __shared__ float ssq_part[kXsMaxWaves];  // RM: each wave's share of sum(x^2)
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -230,14 +237,19 @@ __global__ void __launch_bounds__(kXsMaxWaves * 64) qgemv_xs_kernel(const GemvXs
     rb[s] = xs_rsrc(xs_pick(p.biases, ms), (uint32_t)n_out * (uint32_t)p.sbrow);
   }
 
-  // the chunk's activation: loads first, turned into registers after the
-  // first code loads are issued
-  constexpr int XV = XB ? 4 : 8;
-  uint4 xv[XV];
+  // the chunk's activation (and RMSNorm weight): loads first, turned into
+  // registers after the first code loads are issued
+  constexpr int XV = XIN16 ? 4 : 8;
+  uint4 xv[XV], gv[RM ? XV : 1];
   {
     const uint32_t xo = active ? (uint32_t)c * XCB : kOutOfRange;
 #pragma unroll
     for (int i = 0; i < XV; ++i) xv[i] = xs_load16(rx, xo + 16u * i);
+    if constexpr (RM != 0) {
+      const __amdgpu_buffer_rsrc_t rg = xs_rsrc(p.gamma, (uint32_t)p.ncx * XCB);
+#pragma unroll
+      for (int i = 0; i < XV; ++i) gv[i] = xs_load16(rg, xo + 16u * i);
+    }
   }
 
   // byte offsets of this lane's next row: a running sum, advanced by the
@@ -273,7 +285,8 @@ __global__ void __launch_bounds__(kXsMaxWaves * 64) qgemv_xs_kernel(const GemvXs
   for (int u = 0; u < D; ++u) issue(u);
 
   XsChunk<XB> xc;
-  float xs = 0.f;  // sum of the chunk's activation values
+  float xs = 0.f;   // sum of the chunk's activation values
+  float ssq = 0.f;  // RM: this lane's sum of x^2 over its chunk
   if constexpr (XB) {
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
@@ -286,15 +299,59 @@ __global__ void __launch_bounds__(kXsMaxWaves * 64) qgemv_xs_kernel(const GemvXs
             ((xs_bf16_lo(w2) + xs_bf16_hi(w2)) + (xs_bf16_lo(w3) + xs_bf16_hi(w3)));
     }
   } else {
+    // the chunk's values in element order (RM: x * gamma, with this lane's
+    // share of sum(x^2))
+    float e[32];
+    if constexpr (XIN16) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      xc.v[4 * i] = xv[i].x;
-      xc.v[4 * i + 1] = xv[i].y;
-      xc.v[4 * i + 2] = xv[i].z;
-      xc.v[4 * i + 3] = xv[i].w;
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          e[8 * i + 2 * j] = xs_bf16_lo(w[j]);
+          e[8 * i + 2 * j + 1] = xs_bf16_hi(w[j]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        e[4 * i] = __uint_as_float(xv[i].x);
+        e[4 * i + 1] = __uint_as_float(xv[i].y);
+        e[4 * i + 2] = __uint_as_float(xv[i].z);
+        e[4 * i + 3] = __uint_as_float(xv[i].w);
+      }
+    }
+    if constexpr (RM != 0) {
+      float g[32];
+      if constexpr (RM == 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t w[4] = {gv[i].x, gv[i].y, gv[i].z, gv[i].w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            g[8 * i + 2 * j] = xs_bf16_lo(w[j]);
+            g[8 * i + 2 * j + 1] = xs_bf16_hi(w[j]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          g[4 * i] = __uint_as_float(gv[i].x);
+          g[4 * i + 1] = __uint_as_float(gv[i].y);
+          g[4 * i + 2] = __uint_as_float(gv[i].z);
+          g[4 * i + 3] = __uint_as_float(gv[i].w);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        ssq = fmaf(e[i], e[i], ssq);
+        e[i] *= g[i];
+      }
     }
 #pragma unroll
-    for (int i = 0; i < 32; ++i) xs += __uint_as_float(xc.v[i]);
+    for (int i = 0; i < 32; ++i) xc.v[i] = __float_as_uint(e[i]);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) xs += e[i];
     // even nibble positions pair with codes q 2^-24, odd ones with 16 q 2^-24
 #pragma unroll
     for (int i = 0; i < 32; ++i) xc.v[i] = __float_as_uint(__uint_as_float(xc.v[i]) * ((i & 1) ? 0x1p20f : 0x1p24f));
@@ -305,6 +362,7 @@ __global__ void __launch_bounds__(kXsMaxWaves * 64) qgemv_xs_kernel(const GemvXs
 #pragma unroll
   for (int i = 0; i < (XB ? 16 : 32); ++i) asm volatile("" : "+v"(xc.v[i]));
   asm volatile("" : "+v"(xs));
+  if constexpr (RM != 0) asm volatile("" : "+v"(ssq));
   uint32_t magic = 0x43004300u;
   asm volatile("" : "+v"(magic));  // a VGPR operand, so the AND-OR stays one VOP3
   const float corr = XB ? -128.f * xs : 0.f;
@@ -359,13 +417,31 @@ __global__ void __launch_bounds__(kXsMaxWaves * 64) qgemv_xs_kernel(const GemvXs
       }
     }
   }
+  if constexpr (RM != 0) {
+    // each chunk sits in 64 / L lanes of a wave: count row group 0's
+    const float t16 = xs_sum16(sg == 0 ? ssq : 0.f);
+    const int tb = __float_as_int(t16);
+    const float wsum = (__int_as_float(__builtin_amdgcn_readlane(tb, 0)) +
+                        __int_as_float(__builtin_amdgcn_readlane(tb, 16))) +
+                       (__int_as_float(__builtin_amdgcn_readlane(tb, 32)) +
+                        __int_as_float(__builtin_amdgcn_readlane(tb, 48)));
+    if (lane == 0) ssq_part[w] = wsum;
+  }
   __syncthreads();
+  // RMSNorm: every thread sums the waves' shares in the same order
+  float inv_rms = 1.f;
+  if constexpr (RM != 0) {
+    float tot = 0.f;
+    for (int k = 0; k < W; ++k) tot += ssq_part[k];
+    inv_rms = 1.f / sqrtf(tot / (float)(p.ncx * 32) + p.eps);
+  }
   for (int t = (int)threadIdx.x; t < nr; t += W * 64) {
     float acc[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       acc[s] = 0.f;
       for (int k = 0; k < W; ++k) acc[s] += part[s][t][k];
+      if constexpr (RM != 0) acc[s] *= inv_rms;
     }
     float out = acc[0];
     if constexpr (NS == 2) out = (acc[0] / (1.f + __expf(-acc[0]))) * acc[1];  // silu(gate) * up
@@ -378,9 +454,9 @@ __global__ void __launch_bounds__(kXsMaxWaves * 64) qgemv_xs_kernel(const GemvXs
   }
 }
 
-template <int SBT, bool XB, int NS>
+template <int SBT, bool XB, int NS, int RM = 0>
 hipError_t xs_launch(const GemvXsParams &p, int64_t grid, hipStream_t stream) {
-  auto kern = p.log2_lpr == 5 ? qgemv_xs_kernel<SBT, XB, NS, 5> : qgemv_xs_kernel<SBT, XB, NS, 6>;
+  auto kern = p.log2_lpr == 5 ? qgemv_xs_kernel<SBT, XB, NS, 5, RM> : qgemv_xs_kernel<SBT, XB, NS, 6, RM>;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(p.waves * 64), 0, stream, p);
   return hipGetLastError();
 }
@@ -458,6 +534,13 @@ hipError_t launch_gemv_xs(const GemvXsParams &p, int sb_bf16, int x_bf16, int st
     if (gi < 1 || gi > p.n_out[i] || ((int64_t)p.n_out[i] + gi - 1) / gi > kXsMaxRows) return hipErrorInvalidValue;
   }
   const int64_t grid = p.wg0[p.n_mats];
+  if (p.gamma) {  // RMSNorm prologue: the float32 dot product on x * gamma
+    if (streams == 2)
+      return x_bf16 ? (sb_bf16 ? xs_launch<1, false, 2, 1>(p, grid, stream) : xs_launch<0, false, 2, 1>(p, grid, stream))
+                    : (sb_bf16 ? xs_launch<1, false, 2, 2>(p, grid, stream) : xs_launch<0, false, 2, 2>(p, grid, stream));
+    return x_bf16 ? (sb_bf16 ? xs_launch<1, false, 1, 1>(p, grid, stream) : xs_launch<0, false, 1, 1>(p, grid, stream))
+                  : (sb_bf16 ? xs_launch<1, false, 1, 2>(p, grid, stream) : xs_launch<0, false, 1, 2>(p, grid, stream));
+  }
   if (streams == 2)
     return x_bf16 ? (sb_bf16 ? xs_launch<1, true, 2>(p, grid, stream) : xs_launch<0, true, 2>(p, grid, stream))
                   : (sb_bf16 ? xs_launch<1, false, 2>(p, grid, stream) : xs_launch<0, false, 2>(p, grid, stream));

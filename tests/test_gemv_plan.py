@@ -128,6 +128,11 @@ def test_xs_form_for_long_rows():
     assert (f["kernel"], f["grid"], f["busiest_wave_steps"]) == ("xs", 594, 256)
     f = q.plan_qgemv([512 * N_CU + 1], 4096, x_dtype="bf16", n_cu=N_CU)
     assert f["kernel"] == "xs" and f["busiest_wave_steps"] <= 256
+    # behind the RMSNorm prologue alike (the LM head after the final norm)
+    f = q.plan_qgemv([128256], 2048, x_dtype="bf16", call=q.CALL_RMS_NORM, n_cu=N_CU)
+    assert (f["kernel"], f["grid"]) == ("xs", 4 * N_CU)
+    f = q.plan_qgemv([17408, 17408], 5120, epilogue=q.EPI_SWIGLU_PAIR, call=q.CALL_RMS_NORM, n_cu=N_CU)
+    assert (f["kernel"], f["grid"]) == ("xs", 3 * N_CU)
 
 
 @pytest.mark.parametrize("n_outs,k_in,x_dt,epi,call", [
@@ -137,7 +142,6 @@ def test_xs_form_for_long_rows():
     ([4096], 4096, "f32", q.EPI_NONE, q.CALL_QGEMV),             # fewer than 5120 x 5120 codes
     ([6144], 4096, "bf16", q.EPI_NONE, q.CALL_QGEMV),            # the same
     ([4096, 1024, 1024], 4096, "bf16", q.EPI_NONE, q.CALL_QGEMV),  # q/k/v of 4096: the same
-    ([5120], 17408, "f32", q.EPI_NONE, q.CALL_RMS_NORM),         # RMSNorm prologue
     ([9000, 9000], 1984, "bf16", q.EPI_SWIGLU_PAIR, q.CALL_QGEMV),  # pair, rows under 2048
     ([2000, 2000], 8192, "bf16", q.EPI_SWIGLU_PAIR, q.CALL_QGEMV),  # pair, fewer than 2^25 codes
     ([5120, 5120], 17408, "bf16", q.EPI_SWIGLU_PAIR, q.CALL_SMALLM),  # small-M call

@@ -111,3 +111,52 @@ def test_rms_matches_plain_multi_on_normalised_input():
     for a_, b_ in zip(y_rms, ys):
         a64, b64 = to_np64(a_), to_np64(b_)
         assert np.linalg.norm(a64 - b64) / np.linalg.norm(b64) <= 1e-5
+
+
+# the activation-stationary form behind the RMSNorm prologue (x * gamma and sum(x^2) taken in
+# registers, the row sums scaled at the end): one matrix over 2048, 5120 and 17408 columns,
+# q/k/v of a 5120 activation, and gate/up pairs over 2048 and 6144 columns
+XS_RMS = [([12801], 2048, "bf16", 0), ([5120], 5120, "bf16", 0), ([2000], 17408, "f32", 0),
+          ([5120, 1024, 1024], 5120, "bf16", 0), ([8192, 8192], 2048, "bf16", 1),
+          ([3000, 3000], 6144, "f32", 1)]
+
+
+@pytest.mark.parametrize("n_outs,k_in,x_dt,pair", XS_RMS)
+@pytest.mark.parametrize("sb_dt,y_dt", [("bf16", "bf16"), ("f32", "f32")])
+def test_rms_xs_forms(n_outs, k_in, x_dt, pair, sb_dt, y_dt):
+    q = lib()
+    epi = q.EPI_SWIGLU_PAIR if pair else q.EPI_NONE
+    f = q.plan_qgemv(n_outs, k_in, x_dtype=x_dt, epilogue=epi, call=q.CALL_RMS_NORM)
+    assert f["kernel"] == "xs", f
+    rng = np.random.default_rng(sum(n_outs) + k_in + pair)
+    ws = [synth.draw_matrix(rng, n, k_in, 64, sb_dt) for n in n_outs]
+    x = synth.draw_activation(rng, (k_in,), x_dt)
+    gamma = synth.draw_norm_weight(rng, k_in, x_dt)
+    if pair:
+        (h,) = _run(ws, x, gamma, x_dt, y_dt, epilogue=epi, n_outs=[n_outs[0]])
+        ref, a = oracle.rms_norm_swiglu_pair(ws[0], ws[1], x, x_dt, gamma, EPS, threads=oracle_threads())
+        check(h, ref, a, "xs rms pair %dx%d %s %s/%s" % (n_outs[0], k_in, x_dt, sb_dt, y_dt))
+        return
+    ys = _run(ws, x, gamma, x_dt, y_dt)
+    refs = oracle.rms_norm_multi(ws, x, x_dt, gamma, EPS, threads=oracle_threads())
+    for i, (y, (ref, a)) in enumerate(zip(ys, refs)):
+        check(y, ref, a, "xs rms %s x %d matrix %d %s %s/%s" % (n_outs, k_in, i, x_dt, sb_dt, y_dt))
+
+
+def test_rms_xs_matches_plain_xs_on_normalised_input():
+    """The RMSNorm form of the activation-stationary kernel against its plain form on the
+    host-normalised float32 input (both parity-tested): they agree to 1e-5."""
+    q = lib()
+    rng = np.random.default_rng(404)
+    ws = [synth.draw_matrix(rng, n, 5120, 64, "bf16") for n in (5120, 1024, 1024)]
+    x = synth.draw_activation(rng, (5120,), "bf16")
+    gamma = synth.draw_norm_weight(rng, 5120, "bf16")
+    assert q.plan_qgemv([5120, 1024, 1024], 5120, x_dtype="f32")["kernel"] == "xs"
+    y_rms = _run(ws, x, gamma, "bf16", "f32")
+    xn = oracle.rms_norm(x, "bf16", gamma, EPS).astype(np.float32)
+    ys = [nan_like(w.n_out, torch.float32) for w in ws]
+    q.qgemv_int4_multi([dev_matrix(w) for w in ws], torch.tensor(xn, device="cuda"), ys)
+    torch.cuda.synchronize()
+    for a_, b_ in zip(y_rms, ys):
+        a64, b64 = to_np64(a_), to_np64(b_)
+        assert np.linalg.norm(a64 - b64) / np.linalg.norm(b64) <= 1e-5
