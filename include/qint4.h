@@ -508,9 +508,9 @@ qint4_status quantize_int4(const void *w, int32_t w_dtype, int64_t n_rows, int64
  * that.  The small-M MFMA kernels (QINT4_FORM_MFMA) run one 16-row tile per
  * workgroup, its K range split over `waves` waves.  The activation-stationary
  * kernel (QINT4_FORM_XS: qgemv_int4 / qgemv_int4_multi at T = 1 on one to
- * eight matrices with stored outputs, k_in from 4096 to 32768 and at least
- * 5120 * 5120 codes in all, or on the gate/up pair with k_in from 2048 and at
- * least 2^25 codes) gives
+ * eight matrices with stored outputs, k_in from 2048 to 32768 and at least
+ * 5120 * 5120 codes in all, or on the gate/up pair with at least 2^25 codes;
+ * rms_norm_qgemv_int4 alike) gives
  * lane j of a row group of wave w the 32-code chunk lanes * w + j of its
  * rows, whose activations it holds in registers; a workgroup's `waves` waves
  * cover k_in.  Each matrix owns a range of the `grid` workgroups, and its
