@@ -76,20 +76,20 @@ GEMM_SRC = ("kernels.h", "api.cpp", "qgemm.hip")
 MOEP_SRC = ("kernels.h", "api.cpp", "moe_prefill.hip", "router.hip", "topk_wave.h")
 QUANT_SRC = ("kernels.h", "api.cpp", "quant.hip")
 TRAFFIC = {  # workload: (sources, source hash, FETCH_SIZE KiB, WRITE_SIZE KiB), unscaled
-    "dense_ffn_t1": (GEMV_SRC, "3b6dd4a21a7d1e7a", 52730.5, 545.1),
-    "moe_top8_t1": (GEMV_SRC, "3b6dd4a21a7d1e7a", 10802.8, 32.1),
-    "qkv_multi_t1": (GEMV_SRC, "3b6dd4a21a7d1e7a", 6997.6, 16.0),
-    "rms_qkv_multi_t1": (GEMV_SRC, "3b6dd4a21a7d1e7a", 7057.1, 16.0),
-    "qkv_smallm_T4": (SMALLM_SRC, "e3c6141d9d4eeb06", 7086.7, 48.0),
-    "qkv_smallm_T16": (SMALLM_SRC, "e3c6141d9d4eeb06", 7502.6, 192.0),
-    "prefill_gemm_T32": (STREAM_SRC, "9253a8986c047114", 36101.9, 7616.0),
-    "prefill_gemm_T256": (GEMM_SRC, "1649d149c6f6e6c7", 34850.4, 8704.0),
-    "prefill_gemm_T1024": (GEMM_SRC, "1649d149c6f6e6c7", 139354.1, 34816.0),
-    "prefill_gemm_T4096": (GEMM_SRC, "1649d149c6f6e6c7", 515073.1, 139916.4),
-    "qkv_prefill_T256": (GEMM_SRC, "1649d149c6f6e6c7", 12470.0, 1849.3),
-    "qkv_prefill_T4096": (GEMM_SRC, "1649d149c6f6e6c7", 75236.8, 29650.4),
-    "moe_prefill_top8_T256": (MOEP_SRC, "4ba298957f5e3cf1", 187853.8, 23585.6),
-    "quantize_17408x5120_f32_g64": (QUANT_SRC, "53770553003c863b", 174101.5, 48960.0),
+    "dense_ffn_t1": (GEMV_SRC, "ccdad67c06d00f2c", 52748.4, 545.5),
+    "moe_top8_t1": (GEMV_SRC, "ccdad67c06d00f2c", 10802.8, 32.1),
+    "qkv_multi_t1": (GEMV_SRC, "ccdad67c06d00f2c", 6997.6, 16.0),
+    "rms_qkv_multi_t1": (GEMV_SRC, "ccdad67c06d00f2c", 7057.1, 16.0),
+    "qkv_smallm_T4": (SMALLM_SRC, "1945b2914096cd9e", 7086.6, 48.0),
+    "qkv_smallm_T16": (SMALLM_SRC, "1945b2914096cd9e", 7502.6, 192.0),
+    "prefill_gemm_T32": (STREAM_SRC, "fd3edbcac088e1cd", 36112.7, 7616.0),
+    "prefill_gemm_T256": (GEMM_SRC, "111d8436f4badcf5", 34848.3, 8704.0),
+    "prefill_gemm_T1024": (GEMM_SRC, "111d8436f4badcf5", 139596.3, 34816.0),
+    "prefill_gemm_T4096": (GEMM_SRC, "111d8436f4badcf5", 515714.2, 139848.0),
+    "qkv_prefill_T256": (GEMM_SRC, "111d8436f4badcf5", 12470.0, 1849.3),
+    "qkv_prefill_T4096": (GEMM_SRC, "111d8436f4badcf5", 75757.6, 29650.2),
+    "moe_prefill_top8_T256": (MOEP_SRC, "1fd358bb4ab7069d", 193672.9, 23585.8),
+    "quantize_17408x5120_f32_g64": (QUANT_SRC, "957344c34d8c5002", 174101.4, 48960.1),
 }
 
 
