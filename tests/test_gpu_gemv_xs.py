@@ -72,6 +72,28 @@ def test_xs_most_rows_per_workgroup():
     check(y, y_ref, a_ref, "xs gemv %dx8320 (256 rows per workgroup)" % n_out)
 
 
+def test_xs_grid_grows_past_256_rows_per_workgroup():
+    """A matrix whose rows would give a workgroup more than 256 at two per CU (an LM-head-like
+    2 * 256 * n_cu + 1 rows over 5120 columns): the grid grows to keep every workgroup at 256 or
+    fewer.  Every 61st row, and the last rows, against the oracle on those rows."""
+    q = lib()
+    n_out, k_in = 2 * 256 * _n_cu() + 1, 5120
+    f = q.plan_qgemv([n_out], k_in, x_dtype="bf16")
+    assert f["kernel"] == "xs" and f["grid"] == -(-n_out // 256) and f["busiest_wave_steps"] <= 256, f
+    rng = np.random.default_rng(515)
+    w = synth.draw_matrix(rng, n_out, k_in, 64, "bf16")
+    x = synth.draw_activation(rng, (k_in,), "bf16")
+    y = nan_like(n_out, torch.float32)
+    q.qgemv_int4(dev_matrix(w), synth.to_torch(x, "bf16"), y)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, n_out, 61), np.arange(n_out - 300, n_out)]))
+    sub = synth.QMatrix(codes=w.codes[rows], scales=w.scales[rows], biases=w.biases[rows],
+                        sb_dtype="bf16", group_size=64, n_out=len(rows), k_in=k_in)
+    y_ref, a_ref = oracle.gemv(sub, x, "bf16", threads=oracle_threads())
+    check(y[torch.from_numpy(rows).cuda()], y_ref, a_ref,
+          "xs gemv %dx%d (grid %d), %d sampled rows" % (n_out, k_in, f["grid"], len(rows)))
+
+
 @pytest.mark.parametrize("lo,hi", [(-100, -60), (-20, 100)])
 def test_xs_float32_activation_range(lo, hi):
     """Float32 activations across the exponent range the scaled form keeps exact (codes as f16
