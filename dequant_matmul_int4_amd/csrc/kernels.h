@@ -177,7 +177,8 @@ hipError_t launch_gemv_mfma(const GemvParams &p, int tt, int group_size, int sb_
 // epilogue.  Lane j of a row group of wave w holds chunk L w + j of x in
 // registers (L = 1 << log2_lpr lanes per row, gemv_xs_waves(k_in) waves per
 // workgroup cover k_in).  Matrix m owns workgroups wg0[m] .. wg0[m+1]-1, and
-// its workgroup b of G = wg0[m+1] - wg0[m] takes rows b, b + G, ...
+// its workgroup b of G = wg0[m+1] - wg0[m] takes rows b, b + G, ... (the
+// pair: the block of ceil(n_out / G) rows from b * that)
 constexpr int kXsMaxWaves = 16;    // k_in up to 32768
 constexpr int kXsMaxRows = 256;    // rows per workgroup
 constexpr int kXsMaxMats = 8;      // matrices of one call

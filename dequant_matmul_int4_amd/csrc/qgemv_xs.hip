@@ -32,7 +32,8 @@
 //     cover k_in; lanes past the last chunk load nothing.
 //   * Workgroup b of G takes rows b, b + G, b + 2G, ...: at any moment the
 //     grid streams one compact band of each matrix, each row group of a wave
-//     reading L * 16 contiguous bytes of a row per stream.
+//     reading L * 16 contiguous bytes of a row per stream.  The gate/up pair
+//     takes a contiguous block of rows per workgroup instead.
 //   * Each wave keeps 4 rows of code, scale and bias loads (per stream) in
 //     flight; the loads sit between scheduling barriers, so they are issued
 //     where the ring needs them (the compiler otherwise gathers them at the
@@ -225,7 +226,15 @@ __global__ void __launch_bounds__(kXsMaxWaves * 64) qgemv_xs_kernel(const GemvXs
   for (int i = 1; i < kXsMaxMats; ++i) m = (i < p.n_mats && bid >= p.wg0[i]) ? i : m;
   const int G = xs_pick(p.wg0, m + 1) - xs_pick(p.wg0, m), b = bid - xs_pick(p.wg0, m);
   const int n_out = xs_pick(p.n_out, m);
-  const int nr = (n_out - b + G - 1) / G;  // rows of this workgroup, <= kXsMaxRows
+  // Rows of this workgroup (<= kXsMaxRows): stored outputs take rows b, b + G,
+  // ... (the grid streams one compact band of each matrix); the pair takes the
+  // contiguous block of rows b * RB .. (measured faster for the pair: 17408 x
+  // 5120 21.45 -> 20.86 us, 8192 x 2048 6.73 -> 6.34 us; slower for one
+  // matrix: the float32 down projection 12.51 -> 13.03 us, 128256 x 2048
+  // 29.9 -> 31.1 us).
+  constexpr bool BLOCK = NS == 2;
+  const int RB = (n_out + G - 1) / G;
+  const int nr = BLOCK ? max(0, min(RB, n_out - b * RB)) : (n_out - b + G - 1) / G;
 
   const __amdgpu_buffer_rsrc_t rx = xs_rsrc(p.x, (uint32_t)p.ncx * XCB);
   __amdgpu_buffer_rsrc_t rc[NS], rs[NS], rb[NS];
@@ -254,11 +263,12 @@ __global__ void __launch_bounds__(kXsMaxWaves * 64) qgemv_xs_kernel(const GemvXs
 
   // byte offsets of this lane's next row: a running sum, advanced by the
   // (uniform) distance between a wave's consecutive steps
-  const uint32_t row0 = (uint32_t)(b + G * sg);
+  const uint32_t row0 = (uint32_t)(BLOCK ? b * RB + sg : b + G * sg);
   uint32_t run_c = row0 * (uint32_t)p.kwb + (uint32_t)c * 16u;
   uint32_t run_s = row0 * (uint32_t)p.sbrow + (((uint32_t)c * 32u) >> p.log2_group) * SBB;
-  const uint32_t step_c = (uint32_t)(RPS * G) * (uint32_t)p.kwb;
-  const uint32_t step_s = (uint32_t)(RPS * G) * (uint32_t)p.sbrow;
+  const uint32_t row_step = (uint32_t)(BLOCK ? RPS : RPS * G);  // rows between a wave's steps
+  const uint32_t step_c = row_step * (uint32_t)p.kwb;
+  const uint32_t step_s = row_step * (uint32_t)p.sbrow;
   uint4 q[D][NS];
   uint32_t sv[D][NS], bv[D][NS];
   int issued = 0;  // steps issued by this wave (uniform)
@@ -445,7 +455,7 @@ __global__ void __launch_bounds__(kXsMaxWaves * 64) qgemv_xs_kernel(const GemvXs
     }
     float out = acc[0];
     if constexpr (NS == 2) out = (acc[0] / (1.f + __expf(-acc[0]))) * acc[1];  // silu(gate) * up
-    const int64_t row = (int64_t)b + (int64_t)G * t;
+    const int64_t row = BLOCK ? (int64_t)b * RB + t : (int64_t)b + (int64_t)G * t;
     void *y = xs_pick(p.y, m);
     if (p.y_bf16)
       reinterpret_cast<__bf16 *>(y)[row] = (__bf16)out;

@@ -514,7 +514,8 @@ qint4_status quantize_int4(const void *w, int32_t w_dtype, int64_t n_rows, int64
  * lane j of a row group of wave w the 32-code chunk lanes * w + j of its
  * rows, whose activations it holds in registers; a workgroup's `waves` waves
  * cover k_in.  Each matrix owns a range of the `grid` workgroups, and its
- * workgroup b of G takes rows b, b + G, ... (tasks: rows of all matrices;
+ * workgroup b of G takes rows b, b + G, ... (the pair: a contiguous block
+ * of rows per workgroup) (tasks: rows of all matrices;
  * rows_per_task: rows per wave step; busiest_wave_steps: rows of the busiest
  * workgroup; ring_depth: rows in flight per wave).  ([FFAI #9], the note on
  * T=1 decode negative results, structural conclusion: decode is bound by the
