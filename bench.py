@@ -76,10 +76,10 @@ GEMM_SRC = ("kernels.h", "api.cpp", "qgemm.hip")
 MOEP_SRC = ("kernels.h", "api.cpp", "moe_prefill.hip", "router.hip", "topk_wave.h")
 QUANT_SRC = ("kernels.h", "api.cpp", "quant.hip")
 TRAFFIC = {  # workload: (sources, source hash, FETCH_SIZE KiB, WRITE_SIZE KiB), unscaled
-    "dense_ffn_t1": (GEMV_SRC, "ccdad67c06d00f2c", 52748.4, 545.5),
-    "moe_top8_t1": (GEMV_SRC, "ccdad67c06d00f2c", 10802.8, 32.1),
-    "qkv_multi_t1": (GEMV_SRC, "ccdad67c06d00f2c", 6997.6, 16.0),
-    "rms_qkv_multi_t1": (GEMV_SRC, "ccdad67c06d00f2c", 7057.1, 16.0),
+    "dense_ffn_t1": (GEMV_SRC, "4854a9b2a3d12933", 49668.0, 88.7),
+    "moe_top8_t1": (GEMV_SRC, "4854a9b2a3d12933", 10802.8, 32.1),
+    "qkv_multi_t1": (GEMV_SRC, "4854a9b2a3d12933", 6997.6, 16.0),
+    "rms_qkv_multi_t1": (GEMV_SRC, "4854a9b2a3d12933", 7057.1, 16.0),
     "qkv_smallm_T4": (SMALLM_SRC, "1945b2914096cd9e", 7086.6, 48.0),
     "qkv_smallm_T16": (SMALLM_SRC, "1945b2914096cd9e", 7502.6, 192.0),
     "prefill_gemm_T32": (STREAM_SRC, "fd3edbcac088e1cd", 36112.7, 7616.0),
