@@ -186,6 +186,25 @@ def test_xs_unpack_identity_probe():
             assert np.array_equal(y.cpu().numpy().astype(np.float64), raw[:, k].astype(np.float64)), (x_dt, k)
 
 
+def test_xs_pair_repeatable():
+    """The gate/up pair (a block of rows per workgroup, some workgroups without rows): two calls
+    on the same inputs give the same bits."""
+    q = lib()
+    rng = np.random.default_rng(78)
+    n_out, k_in = 17408, 5120
+    f = q.plan_qgemv([n_out, n_out], k_in, epilogue=q.EPI_SWIGLU_PAIR)
+    assert f["kernel"] == "xs" and -(-n_out // f["busiest_wave_steps"]) < f["grid"], f
+    gate = dev_matrix(synth.draw_matrix(rng, n_out, k_in, 64, "bf16"))
+    up = dev_matrix(synth.draw_matrix(rng, n_out, k_in, 64, "bf16"))
+    x = synth.to_torch(synth.draw_activation(rng, (k_in,), "bf16"), "bf16")
+    h1 = nan_like(n_out, torch.float32)
+    h2 = nan_like(n_out, torch.float32)
+    q.qgemv_int4_multi([gate, up], x, [h1], epilogue=q.EPI_SWIGLU_PAIR)
+    q.qgemv_int4_multi([gate, up], x, [h2], epilogue=q.EPI_SWIGLU_PAIR)
+    torch.cuda.synchronize()
+    assert torch.isfinite(h1).all() and torch.equal(h1, h2)
+
+
 def test_xs_repeatable():
     """Two calls on the same inputs give the same bits (fixed reduction order)."""
     q = lib()
